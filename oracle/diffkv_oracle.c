@@ -1,0 +1,992 @@
+/*
+ * diffkv_oracle.c -- plain serial CPU oracle for the DiffKV hot path.
+ *
+ * TEST INFRASTRUCTURE: only tests/, __graft_entry__.smoke() and the
+ * cpu_baseline leg of bench.py may load this library.  It shares no code
+ * with the HIP library under compressed_paged_attention_amd/.
+ *
+ * Every function follows a passage of the notes page "DiffKV: Differentiated
+ * Memory Management for Large Language Models with Parallel KV Compaction"
+ * (SOSP'25, arXiv 2412.03131); the passage is named at each function.  Where
+ * the page leaves a step open, the reading taken is stated at the function.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -shared -fPIC.
+ * Floating point: fp32 steps use IEEE single arithmetic with round to
+ * nearest even (x86-64 SSE, FLT_EVAL_METHOD 0, no contraction); attention
+ * and softmax are computed in fp64.
+ *
+ * Parity status: every function here is pinned by a -m "not gpu" test
+ * (closed forms, the Fig 6 worked example, invariants, brute force on tiny
+ * inputs, numpy's IEEE fp16 conversion) except the fp32 rounding of the score
+ * sums after a score update, which is compared within a tolerance only.
+ */
+#include "diffkv_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* small helpers                                                             */
+/* ------------------------------------------------------------------------ */
+
+static int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+static int32_t round16(int32_t x) { return (x + 15) / 16 * 16; }
+
+static int cfg_valid(const orc_cfg* c) {
+  if (!c) return 0;
+  if (c->head_dim != 64 && c->head_dim != 128) return 0;
+  if (c->num_kv_heads < 1 || c->gqa_group < 1 || c->gqa_group > 16) return 0;
+  if (c->hi_page_tokens != 16 || c->lo_page_tokens != 2 * c->hi_page_tokens) return 0;
+  if (c->max_seq_len < 1 || c->window < 0) return 0;
+  if (!(c->alpha_l >= 0.0f) || !(c->alpha_h >= 0.0f)) return 0;
+  if (c->lo_enabled && c->alpha_l > c->alpha_h) return 0;
+  return 1;
+}
+
+int32_t orc_table_len(const orc_cfg* c) {
+  /* The page says a row of S_max / T_h entries cannot overflow; one more is
+   * needed (hi and lo pages together can exceed ceil(N/T_h) by one). */
+  return (int32_t)cdiv64(c->max_seq_len, c->hi_page_tokens) + 1;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Unified page layout ("Memory management": unified pages have six segments:
+ * quantized K, K metadata, quantized V, V metadata, token score, position;
+ * tokens per page depend on the precision).  Segment order follows the page;
+ * each segment starts on a 16-byte boundary.                                 */
+/* ------------------------------------------------------------------------ */
+
+int32_t orc_tier_layout(const orc_cfg* c, int32_t tier, int32_t seg[7]) {
+  int32_t d = c->head_dim;
+  int32_t T = (tier == ORC_HI) ? c->hi_page_tokens : c->lo_page_tokens;
+  int32_t kbits = (tier == ORC_HI) ? 8 : 4;
+  int32_t vbits = (tier == ORC_HI) ? 4 : 2;
+  int32_t size[6];
+  size[0] = T * d * kbits / 8; /* K codes */
+  size[1] = 4 * T;             /* K scale + zero, fp16 each */
+  size[2] = T * d * vbits / 8; /* V codes */
+  size[3] = 4 * T;             /* V scale + zero */
+  size[4] = 4 * T;             /* score (fp32) */
+  size[5] = 4 * T;             /* position (int32) */
+  int32_t off = 0;
+  for (int i = 0; i < 6; i++) {
+    seg[i] = off;
+    off += round16(size[i]);
+  }
+  seg[6] = off;
+  return T;
+}
+
+int32_t orc_page_bytes(const orc_cfg* c) {
+  if (!cfg_valid(c)) return -1;
+  int32_t a[7], b[7];
+  orc_tier_layout(c, ORC_HI, a);
+  orc_tier_layout(c, ORC_LO, b);
+  return a[6] > b[6] ? a[6] : b[6];
+}
+
+/* K codes are token-major: token t's d codes are contiguous.  8-bit codes
+ * take one byte each; 4-bit codes pack dims 2i (low nibble) and 2i+1. */
+void orc_k_code_addr(const orc_cfg* c, int32_t tier, int32_t tok, int32_t j,
+                     int32_t* byte, int32_t* shift) {
+  int32_t seg[7];
+  orc_tier_layout(c, tier, seg);
+  int32_t d = c->head_dim;
+  if (tier == ORC_HI) {
+    *byte = seg[0] + tok * d + j;
+    *shift = 0;
+  } else {
+    *byte = seg[0] + tok * (d / 2) + j / 2;
+    *shift = 4 * (j % 2);
+  }
+}
+
+/* V codes use a token-vectorized layout (the page's value-layout idea:
+ * vectorize along tokens, not features) cut into 64 equal lane chunks of
+ * d/8 bytes.  For dim j put i = j mod 16, nb = j div 16, r = t mod 4.
+ *   hi (16 tokens, 4 bits): q = t div 4, M = nb;
+ *   lo (32 tokens, 2 bits): q = (t mod 16) div 4, M = 2 nb + (t div 16).
+ * Chunk L = i + 16 q.  Inside the chunk the code is field h = r mod 2 of pair
+ * P = 2 M + r div 2, where pair P sits in 32-bit word w with its two fields
+ * 16 bits apart:
+ *   hi: w = P div 4, bit = 4 (P mod 4) + 16 h
+ *   lo: w = P div 8, bit = 2 (P mod 8) + 16 h
+ * (little-endian words).  Every (t, j) gets a distinct field. */
+void orc_v_code_addr(const orc_cfg* c, int32_t tier, int32_t tok, int32_t j,
+                     int32_t* byte, int32_t* shift) {
+  int32_t seg[7];
+  orc_tier_layout(c, tier, seg);
+  int32_t chunk = c->head_dim / 8;
+  int32_t i = j % 16, nb = j / 16, r = tok % 4;
+  int32_t q, M, w, bit;
+  int32_t h = r % 2;
+  if (tier == ORC_HI) {
+    q = tok / 4;
+    M = nb;
+    int32_t P = 2 * M + r / 2;
+    w = P / 4;
+    bit = 4 * (P % 4) + 16 * h;
+  } else {
+    q = (tok % 16) / 4;
+    M = 2 * nb + tok / 16;
+    int32_t P = 2 * M + r / 2;
+    w = P / 8;
+    bit = 2 * (P % 8) + 16 * h;
+  }
+  int32_t L = i + 16 * q;
+  *byte = seg[2] + L * chunk + 4 * w + bit / 8;
+  *shift = bit % 8;
+}
+
+static void put_field(uint8_t* page, int32_t byte, int32_t shift, int32_t bits,
+                      uint32_t val) {
+  uint8_t mask = (uint8_t)(((1u << bits) - 1u) << shift);
+  page[byte] = (uint8_t)((page[byte] & ~mask) | ((val << shift) & mask));
+}
+
+static uint32_t get_field(const uint8_t* page, int32_t byte, int32_t shift, int32_t bits) {
+  return (page[byte] >> shift) & ((1u << bits) - 1u);
+}
+
+static void put_u16(uint8_t* p, uint16_t v) { p[0] = (uint8_t)v; p[1] = (uint8_t)(v >> 8); }
+static uint16_t get_u16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+static void put_u32(uint8_t* p, uint32_t v) {
+  for (int i = 0; i < 4; i++) p[i] = (uint8_t)(v >> (8 * i));
+}
+static uint32_t get_u32(const uint8_t* p) {
+  return (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
+}
+static uint32_t f32_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+static float bits_f32(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+
+static void write_slot(const orc_cfg* c, uint8_t* page, int32_t tier, int32_t slot,
+                       const uint8_t* kc, const uint8_t* vc, const uint16_t km[2],
+                       const uint16_t vm[2], float score, int32_t pos) {
+  int32_t seg[7];
+  orc_tier_layout(c, tier, seg);
+  int32_t kbits = tier == ORC_HI ? 8 : 4, vbits = tier == ORC_HI ? 4 : 2;
+  for (int32_t j = 0; j < c->head_dim; j++) {
+    int32_t byte, shift;
+    orc_k_code_addr(c, tier, slot, j, &byte, &shift);
+    put_field(page, byte, shift, kbits, kc[j]);
+    orc_v_code_addr(c, tier, slot, j, &byte, &shift);
+    put_field(page, byte, shift, vbits, vc[j]);
+  }
+  put_u16(page + seg[1] + 4 * slot, km[0]);
+  put_u16(page + seg[1] + 4 * slot + 2, km[1]);
+  put_u16(page + seg[3] + 4 * slot, vm[0]);
+  put_u16(page + seg[3] + 4 * slot + 2, vm[1]);
+  put_u32(page + seg[4] + 4 * slot, f32_bits(score));
+  put_u32(page + seg[5] + 4 * slot, (uint32_t)pos);
+}
+
+void orc_read_slot(const orc_cfg* c, const uint8_t* page, int32_t tier, int32_t slot,
+                   uint8_t* kc, uint8_t* vc, uint16_t* km, uint16_t* vm,
+                   float* score, int32_t* pos) {
+  int32_t seg[7];
+  orc_tier_layout(c, tier, seg);
+  int32_t kbits = tier == ORC_HI ? 8 : 4, vbits = tier == ORC_HI ? 4 : 2;
+  for (int32_t j = 0; j < c->head_dim; j++) {
+    int32_t byte, shift;
+    if (kc) {
+      orc_k_code_addr(c, tier, slot, j, &byte, &shift);
+      kc[j] = (uint8_t)get_field(page, byte, shift, kbits);
+    }
+    if (vc) {
+      orc_v_code_addr(c, tier, slot, j, &byte, &shift);
+      vc[j] = (uint8_t)get_field(page, byte, shift, vbits);
+    }
+  }
+  if (km) { km[0] = get_u16(page + seg[1] + 4 * slot); km[1] = get_u16(page + seg[1] + 4 * slot + 2); }
+  if (vm) { vm[0] = get_u16(page + seg[3] + 4 * slot); vm[1] = get_u16(page + seg[3] + 4 * slot + 2); }
+  if (score) *score = bits_f32(get_u32(page + seg[4] + 4 * slot));
+  if (pos) *pos = (int32_t)get_u32(page + seg[5] + 4 * slot);
+}
+
+/* ------------------------------------------------------------------------ */
+/* IEEE 754 binary16 conversion, written from the format's definition:
+ * 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits; subnormals below
+ * 2^-14 with quantum 2^-24; rounding to nearest, ties to even.             */
+/* ------------------------------------------------------------------------ */
+
+uint16_t orc_f32_to_f16(float f) {
+  uint32_t u = f32_bits(f);
+  uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+  if (isnan(f)) return (uint16_t)(sign | 0x7e00u);
+  double a = fabs((double)f);
+  if (isinf(f)) return (uint16_t)(sign | 0x7c00u);
+  if (a == 0.0) return sign;
+  int e;
+  frexp(a, &e);          /* a = m * 2^e, m in [0.5, 1) -> floor(log2 a) = e - 1 */
+  int ex = e - 1;
+  if (ex < -14) ex = -14; /* subnormal range shares the quantum 2^-24 */
+  double quantum = ldexp(1.0, ex - 10);
+  double n = nearbyint(a / quantum); /* exact division (power of two), RNE */
+  if (n >= 2048.0) {      /* rounding carried into the next binade */
+    n /= 2.0;
+    ex += 1;
+  }
+  if (ex > 15) return (uint16_t)(sign | 0x7c00u); /* overflow to infinity */
+  if (n < 1024.0) return (uint16_t)(sign | (uint16_t)n); /* subnormal (ex == -14) */
+  uint16_t bexp = (uint16_t)(ex + 15);
+  uint16_t frac = (uint16_t)(n - 1024.0);
+  return (uint16_t)(sign | (bexp << 10) | frac);
+}
+
+float orc_f16_to_f32(uint16_t h) {
+  int s = (h >> 15) & 1, e = (h >> 10) & 31, m = h & 1023;
+  double v;
+  if (e == 0) v = ldexp((double)m, -24);
+  else if (e == 31) v = m ? NAN : INFINITY;
+  else v = ldexp((double)(1024 + m), e - 25);
+  return (float)(s ? -v : v);
+}
+
+void orc_f32_to_f16_n(const float* x, uint16_t* h, int64_t n) {
+  for (int64_t i = 0; i < n; i++) h[i] = orc_f32_to_f16(x[i]);
+}
+void orc_f16_to_f32_n(const uint16_t* h, float* x, int64_t n) {
+  for (int64_t i = 0; i < n; i++) x[i] = orc_f16_to_f32(h[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Asymmetric quantization ("Background", KV cache optimization: scale s and
+ * zero z, Q = round((X - z) / s), X^ = s Q + z, applied to each K and each V
+ * vector on its own).  Reading: z = min, s = (max - min)/(2^b - 1), both
+ * stored as fp16 (rounded to nearest even); the code uses the stored fp16
+ * values, fp32 IEEE division and rint (ties to even), clamped to
+ * [0, 2^b - 1]; a zero scale gives code 0.                                 */
+/* ------------------------------------------------------------------------ */
+
+void orc_quantize(const float* x, int32_t n, int32_t bits, uint16_t* s16,
+                  uint16_t* z16, uint8_t* codes) {
+  float mn = x[0], mx = x[0];
+  for (int32_t i = 1; i < n; i++) {
+    if (x[i] < mn) mn = x[i];
+    if (x[i] > mx) mx = x[i];
+  }
+  int32_t qmax = (1 << bits) - 1;
+  float range = mx - mn;
+  float scale = range / (float)qmax;
+  *s16 = orc_f32_to_f16(scale);
+  *z16 = orc_f32_to_f16(mn);
+  float s = orc_f16_to_f32(*s16), z = orc_f16_to_f32(*z16);
+  for (int32_t i = 0; i < n; i++) {
+    if (s == 0.0f) {
+      codes[i] = 0;
+      continue;
+    }
+    float t = (x[i] - z) / s;
+    float r = rintf(t);
+    if (r < 0.0f) r = 0.0f;
+    if (r > (float)qmax) r = (float)qmax;
+    codes[i] = (uint8_t)r;
+  }
+}
+
+float orc_dequant(uint16_t s16, uint16_t z16, int32_t code) {
+  /* The product of an fp16 scale and a code of at most 8 bits is exact in
+   * fp32, so this is one rounding (the add). */
+  float s = orc_f16_to_f32(s16), z = orc_f16_to_f32(z16);
+  float prod = s * (float)code;
+  return prod + z;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Classification ("Approach" and "KV compression policy", prompt phase):
+ * the last W tokens are always high precision; otherwise a token whose mean
+ * score exceeds alpha_h/N is high, one in [alpha_l/N, alpha_h/N] is low, and
+ * one below alpha_l/N is pruned.  N is the request's length (the approach
+ * summary and the generation-phase algorithm use N; the prompt passage's
+ * 1/i variant is not taken).  Comparisons are made without division, as
+ * s*N against alpha in fp64, which is exact for N < 2^29.  With the low tier
+ * closed, a token is high iff s*N >= alpha_l and pruned otherwise.        */
+/* ------------------------------------------------------------------------ */
+
+static int32_t classify_prompt(const orc_cfg* c, float s, int64_t N, int64_t p) {
+  if (c->window > 0 && p >= N - c->window) return ORC_HI;
+  double x = (double)s * (double)N;
+  if (c->lo_enabled) {
+    if (x > (double)c->alpha_h) return ORC_HI;
+    if (x >= (double)c->alpha_l) return ORC_LO;
+    return ORC_PRUNE;
+  }
+  return x >= (double)c->alpha_l ? ORC_HI : ORC_PRUNE;
+}
+
+static int cu_valid(int32_t batch, const int64_t* cu) {
+  if (batch < 0 || !cu || cu[0] != 0) return 0;
+  for (int32_t r = 0; r < batch; r++)
+    if (cu[r + 1] < cu[r]) return 0;
+  return 1;
+}
+
+int orc_classify(const orc_cfg* c, int32_t batch, const int64_t* cu,
+                 const float* scores, uint8_t* tiers, int32_t* counts) {
+  if (!cfg_valid(c) || !cu_valid(batch, cu)) return ORC_E_INVALID;
+  int32_t H = c->num_kv_heads;
+  int64_t total = cu[batch];
+  for (int32_t r = 0; r < batch; r++) {
+    int64_t N = cu[r + 1] - cu[r];
+    for (int32_t h = 0; h < H; h++) {
+      int32_t nh = 0, nl = 0;
+      for (int64_t p = 0; p < N; p++) {
+        int64_t idx = (int64_t)h * total + cu[r] + p;
+        int32_t t = classify_prompt(c, scores[idx], N, p);
+        tiers[idx] = (uint8_t)t;
+        if (t == ORC_HI) nh++;
+        if (t == ORC_LO) nl++;
+      }
+      counts[((int64_t)r * H + h) * 2 + 0] = nh;
+      counts[((int64_t)r * H + h) * 2 + 1] = nl;
+    }
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Circular free page list ("Memory management": one contiguous list of all
+ * page ids with an allocation pointer (start) and a reclamation pointer
+ * (end), both wrapping; allocating advances start, freeing advances end; a
+ * prefix sum over per-head counts gives each head its own region).
+ * Reading: the two pointers are monotonically increasing 64-bit counters,
+ * the list index is counter mod P and the free count is end - start.       */
+/* ------------------------------------------------------------------------ */
+
+int orc_pool_init(orc_pool* p) {
+  if (!p || p->num_pages < 1) return ORC_E_INVALID;
+  for (int64_t i = 0; i < p->num_pages; i++) p->free_list[i] = (int32_t)i;
+  p->ptr[0] = 0;
+  p->ptr[1] = (uint64_t)p->num_pages;
+  p->status[0] = 0;
+  return ORC_OK;
+}
+
+/* Plan + coordination of prompt compaction (Fig 6 workflow).  Per unit
+ * (request r, KV head h; units in r-major, h-minor order):
+ *   1. conservatively take k = ceil(N/T_h) pages (all assumed high), as one
+ *      block from the allocation pointer, block ids in list order;
+ *   2. plan n_hp = ceil(n_hi/T_h) high pages and n_lp = ceil(n_lo/T_l) low
+ *      pages; high pages are block[0..n_hp) placed left to right in the
+ *      table row, low pages are block[k-1], block[k-2], ... placed right to
+ *      left;
+ *   3. the unused middle of the block is appended at the reclamation pointer
+ *      (units in order, each unit's pages in ascending block index);
+ *   4. reading for the case the page misses: when n_hp + n_lp = k + 1 the
+ *      block is one page short; that unit takes one more page from the
+ *      allocation pointer after the frees, and it becomes the innermost low
+ *      page (table index L_max - n_lp).
+ * All or nothing: if the pool cannot supply the pages, or any unit is not
+ * empty, nothing is written except the sticky status bit. */
+static int prompt_allocate_core(int32_t H, int32_t T_h, int32_t T_l, int32_t L_max,
+                                int32_t batch, const int64_t* seqlens,
+                                const int32_t* n_hi, const int32_t* n_lo,
+                                int32_t* free_list, uint64_t* ptr, uint32_t* status,
+                                int64_t P, int32_t* table, int32_t* state,
+                                int64_t S_max) {
+  int64_t U = (int64_t)batch * H;
+  int64_t K = 0, F = 0, E = 0;
+  uint32_t st = 0;
+  for (int64_t u = 0; u < U; u++) {
+    int64_t N = seqlens[u / H];
+    if (N <= 0) continue;
+    const int32_t* s = state + 4 * u;
+    if (s[0] || s[1] || s[2] || s[3]) st |= ORC_ST_BAD_STATE;
+    if (n_hi[u] < 0 || n_lo[u] < 0 || n_hi[u] + n_lo[u] > N) st |= ORC_ST_BAD_STATE;
+    if (S_max > 0 && N > S_max) st |= ORC_ST_TABLE_OVERFLOW;
+    int64_t k = cdiv64(N, T_h), hp = cdiv64(n_hi[u], T_h), lp = cdiv64(n_lo[u], T_l);
+    if (k > L_max || hp + lp > L_max) st |= ORC_ST_TABLE_OVERFLOW;
+    K += k;
+    if (k > hp + lp) F += k - hp - lp;
+    if (hp + lp > k) E += hp + lp - k;
+  }
+  int64_t free0 = (int64_t)(ptr[1] - ptr[0]);
+  if (!st && (K > free0 || K - F + E > free0)) st |= ORC_ST_POOL_EXHAUSTED;
+  if (st) {
+    *status |= st;
+    return 0;
+  }
+  uint64_t start = ptr[0], end = ptr[1];
+  int32_t* freed = (int32_t*)malloc(sizeof(int32_t) * (size_t)(F > 0 ? F : 1));
+  int64_t nf = 0;
+  /* 1-3: conservative block per unit, table placement, middle collected */
+  for (int64_t u = 0; u < U; u++) {
+    int64_t N = seqlens[u / H];
+    if (N <= 0) continue;
+    int64_t k = cdiv64(N, T_h), hp = cdiv64(n_hi[u], T_h), lp = cdiv64(n_lo[u], T_l);
+    int32_t* row = table + u * L_max;
+    for (int64_t i = 0; i < k; i++) {
+      int32_t id = free_list[(start + (uint64_t)i) % (uint64_t)P];
+      if (i < hp) row[i] = id;                      /* high: left to right */
+      else if (i >= k - lp) row[L_max - 1 - (k - 1 - i)] = id; /* low: right to left */
+      else freed[nf++] = id;                        /* unused middle */
+    }
+    start += (uint64_t)k;
+  }
+  /* 3: reclaim at the end pointer */
+  for (int64_t i = 0; i < nf; i++) free_list[(end + (uint64_t)i) % (uint64_t)P] = freed[i];
+  end += (uint64_t)nf;
+  /* 4: extra page for units whose block was one short */
+  for (int64_t u = 0; u < U; u++) {
+    int64_t N = seqlens[u / H];
+    if (N <= 0) continue;
+    int64_t k = cdiv64(N, T_h), hp = cdiv64(n_hi[u], T_h), lp = cdiv64(n_lo[u], T_l);
+    if (hp + lp > k) {
+      table[u * L_max + (L_max - lp)] = free_list[start % (uint64_t)P];
+      start += 1;
+    }
+    state[4 * u + 0] = n_hi[u];
+    state[4 * u + 1] = n_lo[u];
+    state[4 * u + 2] = (int32_t)hp;
+    state[4 * u + 3] = (int32_t)lp;
+  }
+  ptr[0] = start;
+  ptr[1] = end;
+  free(freed);
+  return 1;
+}
+
+int orc_prompt_allocate(int32_t H, int32_t T_h, int32_t T_l, int32_t L_max,
+                        int32_t batch, const int64_t* seqlens,
+                        const int32_t* n_hi, const int32_t* n_lo,
+                        int32_t* free_list, uint64_t* ptr, uint32_t* status,
+                        int64_t num_pages, int32_t* page_table,
+                        int32_t* tier_state) {
+  if (H < 1 || T_h < 1 || T_l < 1 || L_max < 1 || batch < 0 || num_pages < 1) return ORC_E_INVALID;
+  prompt_allocate_core(H, T_h, T_l, L_max, batch, seqlens, n_hi, n_lo, free_list, ptr,
+                       status, num_pages, page_table, tier_state, 0);
+  return ORC_OK;
+}
+
+static uint8_t* page_at(orc_pool* p, int32_t id) {
+  return p->pages + (int64_t)id * p->page_bytes;
+}
+
+/* Quantize one token (fp32 K and V vectors) for a tier and write its slot. */
+static void store_token(const orc_cfg* c, uint8_t* page, int32_t tier, int32_t slot,
+                        const float* xk, const float* xv, float score, int32_t pos) {
+  int32_t d = c->head_dim;
+  uint8_t kc[128], vc[128];
+  uint16_t km[2], vm[2];
+  orc_quantize(xk, d, tier == ORC_HI ? 8 : 4, &km[0], &km[1], kc);
+  orc_quantize(xv, d, tier == ORC_HI ? 4 : 2, &vm[0], &vm[1], vc);
+  write_slot(c, page, tier, slot, kc, vc, km, vm, score, pos);
+}
+
+/* Prompt compaction: classify counts, the Fig 6 plan/coordination above,
+ * then packing.  Packing reading: inside a tier, tokens take slots in
+ * position order; high slot s lives in the page at table index s div T_h,
+ * low slot s in the page at L_max - 1 - (s div T_l); every page handed to a
+ * unit is zero-filled before its tokens are written.  The stored score is
+ * the running sum of received attention, mean * count with
+ * count = N - 1 - p queries so far (one fp32 multiply), so a later mean is
+ * sum / count. */
+int orc_compact_prompt(const orc_cfg* c, orc_pool* p, int32_t batch,
+                       const int64_t* cu, const uint16_t* k, const uint16_t* v,
+                       const float* scores, const uint8_t* tiers,
+                       int32_t* table, int32_t* state) {
+  if (!cfg_valid(c) || !p || !cu_valid(batch, cu)) return ORC_E_INVALID;
+  if (p->page_bytes != orc_page_bytes(c)) return ORC_E_INVALID;
+  int32_t H = c->num_kv_heads, d = c->head_dim, L = orc_table_len(c);
+  int32_t Th = c->hi_page_tokens, Tl = c->lo_page_tokens;
+  int64_t total = cu[batch];
+  int64_t U = (int64_t)batch * H;
+  int64_t* seqlens = (int64_t*)malloc(sizeof(int64_t) * (size_t)(batch > 0 ? batch : 1));
+  int32_t* nh = (int32_t*)calloc((size_t)(U > 0 ? U : 1), sizeof(int32_t));
+  int32_t* nl = (int32_t*)calloc((size_t)(U > 0 ? U : 1), sizeof(int32_t));
+  for (int32_t r = 0; r < batch; r++) seqlens[r] = cu[r + 1] - cu[r];
+  for (int64_t u = 0; u < U; u++) {
+    int32_t r = (int32_t)(u / H), h = (int32_t)(u % H);
+    for (int64_t t = 0; t < seqlens[r]; t++) {
+      uint8_t ti = tiers[(int64_t)h * total + cu[r] + t];
+      if (ti == ORC_HI) nh[u]++;
+      else if (ti == ORC_LO) nl[u]++;
+    }
+  }
+  int ok = prompt_allocate_core(H, Th, Tl, L, batch, seqlens, nh, nl, p->free_list, p->ptr,
+                                p->status, p->num_pages, table, state, c->max_seq_len);
+  if (ok) {
+    float xk[128], xv[128];
+    for (int64_t u = 0; u < U; u++) {
+      int32_t r = (int32_t)(u / H), h = (int32_t)(u % H);
+      int64_t N = seqlens[r];
+      if (N <= 0) continue;
+      int32_t* row = table + u * L;
+      for (int32_t j = 0; j < state[4 * u + 2]; j++) memset(page_at(p, row[j]), 0, (size_t)p->page_bytes);
+      for (int32_t j = 0; j < state[4 * u + 3]; j++) memset(page_at(p, row[L - 1 - j]), 0, (size_t)p->page_bytes);
+      int32_t sh = 0, sl = 0;
+      for (int64_t t = 0; t < N; t++) {
+        int64_t idx = (int64_t)h * total + cu[r] + t;
+        uint8_t ti = tiers[idx];
+        if (ti != ORC_HI && ti != ORC_LO) continue;
+        const uint16_t* kr = k + ((cu[r] + t) * H + h) * d;
+        const uint16_t* vr = v + ((cu[r] + t) * H + h) * d;
+        for (int32_t j = 0; j < d; j++) {
+          xk[j] = orc_f16_to_f32(kr[j]);
+          xv[j] = orc_f16_to_f32(vr[j]);
+        }
+        float sum = scores[idx] * (float)(N - 1 - t);
+        if (ti == ORC_HI) {
+          int32_t s = sh++;
+          store_token(c, page_at(p, row[s / Th]), ORC_HI, s % Th, xk, xv, sum, (int32_t)t);
+        } else {
+          int32_t s = sl++;
+          store_token(c, page_at(p, row[L - 1 - s / Tl]), ORC_LO, s % Tl, xk, xv, sum, (int32_t)t);
+        }
+      }
+    }
+  }
+  free(seqlens);
+  free(nh);
+  free(nl);
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Generation-phase step ("KV compression policy", generation phase and the
+ * algorithm flow; "Memory management", generation workflow; "Implementation":
+ * the compactor runs before the attention kernel).
+ *
+ * Per active unit with current length N (the new token gets position N and
+ * N' = N + 1 is the length the thresholds use):
+ *   - the new token enters the window, i.e. the high tier (8/4 bits);
+ *   - t_c, the token at position N - W, just left the window; its mean is
+ *     sum / (W - 1) and it is classified against alpha/N';
+ *   - t_c high: the least important non-window high token t_v (position
+ *     <= N - W, t_c included) stays if its mean still exceeds alpha_h/N', is
+ *     requantized to the low tier if it lies in [alpha_l/N', alpha_h/N'], and
+ *     is pruned otherwise;
+ *   - t_c low: t_c is requantized into the low tier; the least important low
+ *     token (t_c included) is pruned if its mean is below alpha_l/N';
+ *   - t_c pruned: it is removed.
+ * Readings: means are compared without division (sum_a cnt_b vs
+ * sum_b cnt_a in fp64; ties go to the smaller position); count of a token at
+ * position p is N - 1 - p; requantization starts from the fp32 values
+ * dequantized from the high codes; a removal and an insertion in the same
+ * tier share the slot, otherwise the insertion appends.  Neither tier ever
+ * shrinks, so a unit needs at most one new page per step and never frees
+ * one (pages return only on release).  All or nothing over the call. */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  int32_t active;
+  int32_t new_hi_slot, hi_append;
+  int32_t lo_src_hi_slot; /* hi slot of the token moving to the low tier, -1 */
+  int32_t lo_slot, lo_append;
+  int32_t need_page;      /* 0 none, ORC_HI or ORC_LO */
+  int32_t page_id;
+} step_plan;
+
+static int32_t classify_mean(const orc_cfg* c, float sum, int64_t cnt, int64_t Np) {
+  double x = (double)sum * (double)Np;
+  double ch = (double)c->alpha_h * (double)cnt, cl = (double)c->alpha_l * (double)cnt;
+  if (c->lo_enabled) {
+    if (x > ch) return ORC_HI;
+    if (x >= cl) return ORC_LO;
+    return ORC_PRUNE;
+  }
+  return x >= cl ? ORC_HI : ORC_PRUNE;
+}
+
+/* a strictly less important than b */
+static int less_important(float sa, int64_t ca, int32_t pa, float sb, int64_t cb, int32_t pb) {
+  double l = (double)sa * (double)cb, r = (double)sb * (double)ca;
+  if (l != r) return l < r;
+  return pa < pb;
+}
+
+static uint8_t* slot_page(orc_pool* p, const int32_t* row, int32_t L, int32_t tier,
+                          int32_t slot, const orc_cfg* c) {
+  if (tier == ORC_HI) return page_at(p, row[slot / c->hi_page_tokens]);
+  return page_at(p, row[L - 1 - slot / c->lo_page_tokens]);
+}
+
+int orc_compact_step(const orc_cfg* c, orc_pool* p, int32_t batch,
+                     const int32_t* seq_len, const uint16_t* k_new,
+                     const uint16_t* v_new, int32_t* table, int32_t* state) {
+  if (!cfg_valid(c) || !p || batch < 0 || c->window < 2) return ORC_E_INVALID;
+  if (p->page_bytes != orc_page_bytes(c)) return ORC_E_INVALID;
+  int32_t H = c->num_kv_heads, d = c->head_dim, L = orc_table_len(c), W = c->window;
+  int32_t Th = c->hi_page_tokens, Tl = c->lo_page_tokens;
+  int64_t U = (int64_t)batch * H;
+  step_plan* pl = (step_plan*)calloc((size_t)(U > 0 ? U : 1), sizeof(step_plan));
+  uint32_t st = 0;
+  int64_t demand = 0;
+  for (int64_t u = 0; u < U; u++) {
+    step_plan* P = &pl[u];
+    P->lo_src_hi_slot = -1;
+    int64_t N = seq_len[u / H];
+    if (N <= 0) continue;
+    P->active = 1;
+    int32_t n_hi = state[4 * u], n_lo = state[4 * u + 1], ph = state[4 * u + 2], plo = state[4 * u + 3];
+    if (N + 1 > c->max_seq_len) { st |= ORC_ST_TABLE_OVERFLOW; continue; }
+    if (n_hi < 0 || n_lo < 0 || ph != cdiv64(n_hi, Th) || plo != cdiv64(n_lo, Tl) ||
+        n_hi + n_lo > N || ph + plo > L) {
+      st |= ORC_ST_BAD_STATE;
+      continue;
+    }
+    const int32_t* row = table + u * L;
+    int bad_id = 0;
+    for (int32_t j = 0; j < ph; j++) if (row[j] < 0 || row[j] >= p->num_pages) bad_id = 1;
+    for (int32_t j = 0; j < plo; j++) if (row[L - 1 - j] < 0 || row[L - 1 - j] >= p->num_pages) bad_id = 1;
+    if (bad_id) { st |= ORC_ST_BAD_STATE; continue; }
+    int64_t Np = N + 1;
+    int64_t tc_pos = N - W;
+    P->new_hi_slot = n_hi;
+    P->hi_append = 1;
+    if (tc_pos >= 0) {
+      int32_t tc = -1;
+      float tc_sum = 0;
+      for (int32_t s = 0; s < n_hi; s++) {
+        float sc; int32_t pos;
+        orc_read_slot(c, slot_page(p, row, L, ORC_HI, s, c), ORC_HI, s % Th, 0, 0, 0, 0, &sc, &pos);
+        if (pos == tc_pos) { tc = s; tc_sum = sc; }
+      }
+      if (tc < 0) { st |= ORC_ST_BAD_STATE; continue; }
+      int32_t cls = classify_mean(c, tc_sum, W - 1, Np);
+      if (cls == ORC_HI) {
+        int32_t v = -1; float vs = 0; int32_t vp = 0; int64_t vc = 0;
+        for (int32_t s = 0; s < n_hi; s++) {
+          float sc; int32_t pos;
+          orc_read_slot(c, slot_page(p, row, L, ORC_HI, s, c), ORC_HI, s % Th, 0, 0, 0, 0, &sc, &pos);
+          if (pos > tc_pos) continue; /* window */
+          int64_t cnt = N - 1 - pos;
+          if (v < 0 || less_important(sc, cnt, pos, vs, vc, vp)) { v = s; vs = sc; vp = pos; vc = cnt; }
+        }
+        int32_t vcls = classify_mean(c, vs, vc, Np);
+        if (vcls == ORC_LO) {
+          P->lo_src_hi_slot = v;
+          P->lo_slot = n_lo;
+          P->lo_append = 1;
+          P->new_hi_slot = v;
+          P->hi_append = 0;
+        } else if (vcls == ORC_PRUNE) {
+          P->new_hi_slot = v;
+          P->hi_append = 0;
+        }
+      } else if (cls == ORC_LO) {
+        P->lo_src_hi_slot = tc;
+        P->new_hi_slot = tc;
+        P->hi_append = 0;
+        /* least important among low tokens and t_c */
+        int32_t v = -1; float vs = tc_sum; int32_t vp = (int32_t)tc_pos; int64_t vc = W - 1;
+        for (int32_t s = 0; s < n_lo; s++) {
+          float sc; int32_t pos;
+          orc_read_slot(c, slot_page(p, row, L, ORC_LO, s, c), ORC_LO, s % Tl, 0, 0, 0, 0, &sc, &pos);
+          int64_t cnt = N - 1 - pos;
+          if (less_important(sc, cnt, pos, vs, vc, vp)) { v = s; vs = sc; vp = pos; vc = cnt; }
+        }
+        if (v >= 0 && classify_mean(c, vs, vc, Np) == ORC_PRUNE) {
+          P->lo_slot = v;
+          P->lo_append = 0;
+        } else {
+          P->lo_slot = n_lo;
+          P->lo_append = 1;
+        }
+      } else {
+        P->new_hi_slot = tc;
+        P->hi_append = 0;
+      }
+    }
+    if (P->hi_append && n_hi % Th == 0) P->need_page = ORC_HI;
+    if (P->lo_append && n_lo % Tl == 0) P->need_page = ORC_LO;
+    if (P->need_page && ph + plo + 1 > L) { st |= ORC_ST_TABLE_OVERFLOW; continue; }
+    if (P->need_page) demand++;
+  }
+  if (!st && demand > (int64_t)(p->ptr[1] - p->ptr[0])) st |= ORC_ST_POOL_EXHAUSTED;
+  if (st) {
+    p->status[0] |= st;
+    free(pl);
+    return ORC_OK;
+  }
+  /* coordination: pages in unit order from the allocation pointer */
+  uint64_t start = p->ptr[0];
+  for (int64_t u = 0; u < U; u++) {
+    if (!pl[u].active || !pl[u].need_page) continue;
+    pl[u].page_id = p->free_list[start % (uint64_t)p->num_pages];
+    start++;
+  }
+  p->ptr[0] = start;
+  /* commit */
+  float xk[128], xv[128];
+  for (int64_t u = 0; u < U; u++) {
+    step_plan* P = &pl[u];
+    if (!P->active) continue;
+    int32_t b = (int32_t)(u / H);
+    int32_t* row = table + u * L;
+    int32_t* s4 = state + 4 * u;
+    if (P->need_page == ORC_HI) {
+      row[s4[2]] = P->page_id;
+      s4[2]++;
+      memset(page_at(p, P->page_id), 0, (size_t)p->page_bytes);
+    } else if (P->need_page == ORC_LO) {
+      row[L - 1 - s4[3]] = P->page_id;
+      s4[3]++;
+      memset(page_at(p, P->page_id), 0, (size_t)p->page_bytes);
+    }
+    if (P->lo_src_hi_slot >= 0) {
+      uint8_t kc[128], vc[128];
+      uint16_t km[2], vm[2];
+      float sc; int32_t pos;
+      orc_read_slot(c, slot_page(p, row, L, ORC_HI, P->lo_src_hi_slot, c), ORC_HI,
+                    P->lo_src_hi_slot % Th, kc, vc, km, vm, &sc, &pos);
+      for (int32_t j = 0; j < d; j++) {
+        xk[j] = orc_dequant(km[0], km[1], kc[j]);
+        xv[j] = orc_dequant(vm[0], vm[1], vc[j]);
+      }
+      store_token(c, slot_page(p, row, L, ORC_LO, P->lo_slot, c), ORC_LO, P->lo_slot % Tl,
+                  xk, xv, sc, pos);
+      if (P->lo_append) s4[1]++;
+    }
+    const uint16_t* kr = k_new + ((int64_t)b * H + (u % H)) * d;
+    const uint16_t* vr = v_new + ((int64_t)b * H + (u % H)) * d;
+    for (int32_t j = 0; j < d; j++) {
+      xk[j] = orc_f16_to_f32(kr[j]);
+      xv[j] = orc_f16_to_f32(vr[j]);
+    }
+    store_token(c, slot_page(p, row, L, ORC_HI, P->new_hi_slot, c), ORC_HI, P->new_hi_slot % Th,
+                xk, xv, 0.0f, seq_len[b]);
+    if (P->hi_append) s4[0]++;
+  }
+  free(pl);
+  return ORC_OK;
+}
+
+/* Release ("Memory management", generation workflow: when a request
+ * completes, all its pages are reclaimed).  Units of released requests in
+ * order; each unit's high pages (table left to right) then low pages (table
+ * right to left) are appended at the reclamation pointer; the rows are reset
+ * to -1 and the unit state to zero. */
+int orc_release(const orc_cfg* c, orc_pool* p, int32_t batch, const uint8_t* mask,
+                int32_t* table, int32_t* state) {
+  if (!cfg_valid(c) || !p || batch < 0) return ORC_E_INVALID;
+  int32_t H = c->num_kv_heads, L = orc_table_len(c);
+  int64_t U = (int64_t)batch * H, total = 0;
+  uint32_t st = 0;
+  for (int64_t u = 0; u < U; u++) {
+    if (!mask[u / H]) continue;
+    int32_t ph = state[4 * u + 2], plo = state[4 * u + 3];
+    if (ph < 0 || plo < 0 || ph + plo > L) { st |= ORC_ST_BAD_STATE; continue; }
+    const int32_t* row = table + u * L;
+    for (int32_t j = 0; j < ph; j++) if (row[j] < 0 || row[j] >= p->num_pages) st |= ORC_ST_BAD_STATE;
+    for (int32_t j = 0; j < plo; j++) if (row[L - 1 - j] < 0 || row[L - 1 - j] >= p->num_pages) st |= ORC_ST_BAD_STATE;
+    total += ph + plo;
+  }
+  if (!st && (int64_t)(p->ptr[1] - p->ptr[0]) + total > p->num_pages) st |= ORC_ST_BAD_STATE;
+  if (st) {
+    p->status[0] |= st;
+    return ORC_OK;
+  }
+  uint64_t end = p->ptr[1];
+  for (int64_t u = 0; u < U; u++) {
+    if (!mask[u / H]) continue;
+    int32_t* row = table + u * L;
+    int32_t ph = state[4 * u + 2], plo = state[4 * u + 3];
+    for (int32_t j = 0; j < ph; j++) p->free_list[(end++) % (uint64_t)p->num_pages] = row[j];
+    for (int32_t j = 0; j < plo; j++) p->free_list[(end++) % (uint64_t)p->num_pages] = row[L - 1 - j];
+    for (int32_t j = 0; j < L; j++) row[j] = -1;
+    for (int32_t j = 0; j < 4; j++) state[4 * u + j] = 0;
+  }
+  p->ptr[1] = end;
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Attention ("Background", the attention formula: softmax of q.k/sqrt(d)
+ * over the cached tokens weighting the values; GQA: the q heads of a group
+ * share one KV head).  Over the compressed cache the keys and values are the
+ * dequantized ones and only retained tokens take part.  fp64 throughout.   */
+/* ------------------------------------------------------------------------ */
+
+void orc_attention_dense(const double* q, const double* k, const double* v, int32_t n,
+                         int32_t d, double* out) {
+  double* x = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+  double scale = 1.0 / sqrt((double)d), m = -INFINITY, z = 0.0;
+  for (int32_t t = 0; t < n; t++) {
+    double acc = 0.0;
+    for (int32_t i = 0; i < d; i++) acc += q[i] * k[(int64_t)t * d + i];
+    x[t] = acc * scale;
+    if (x[t] > m) m = x[t];
+  }
+  for (int32_t t = 0; t < n; t++) z += exp(x[t] - m);
+  for (int32_t i = 0; i < d; i++) out[i] = 0.0;
+  for (int32_t t = 0; t < n; t++) {
+    double pr = exp(x[t] - m) / z;
+    for (int32_t i = 0; i < d; i++) out[i] += pr * v[(int64_t)t * d + i];
+  }
+  free(x);
+}
+
+/* The page's decomposition: each token adds coefficient (softmax weight
+ * times |v|) times the unit vector v/|v|; a zero value vector adds nothing. */
+void orc_attention_unit_vectors(const double* q, const double* k, const double* v,
+                                int32_t n, int32_t d, double* out) {
+  double* x = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+  double scale = 1.0 / sqrt((double)d), m = -INFINITY, z = 0.0;
+  for (int32_t t = 0; t < n; t++) {
+    double acc = 0.0;
+    for (int32_t i = 0; i < d; i++) acc += q[i] * k[(int64_t)t * d + i];
+    x[t] = acc * scale;
+    if (x[t] > m) m = x[t];
+  }
+  for (int32_t t = 0; t < n; t++) z += exp(x[t] - m);
+  for (int32_t i = 0; i < d; i++) out[i] = 0.0;
+  for (int32_t t = 0; t < n; t++) {
+    double norm = 0.0;
+    for (int32_t i = 0; i < d; i++) norm += v[(int64_t)t * d + i] * v[(int64_t)t * d + i];
+    norm = sqrt(norm);
+    if (norm == 0.0) continue;
+    double coef = exp(x[t] - m) / z * norm;
+    for (int32_t i = 0; i < d; i++) out[i] += coef * (v[(int64_t)t * d + i] / norm);
+  }
+  free(x);
+}
+
+/* Decode attention over the compressed cache of each active request: one
+ * query per q head, keys/values dequantized from every retained slot (high
+ * pages then low pages; the order does not change the result), softmax in
+ * fp64, output rounded to fp32.  An inactive request (seq_len <= 0) or a unit
+ * without tokens gives zeros.
+ * Score update (reading of the stored token scores, policy section): with
+ * update_scores set, each retained token other than the query's own
+ * (position < seq_len) adds the max over the group's q heads of its softmax
+ * weight to its stored sum (fp32 add of the fp64 value rounded once). */
+int orc_decode_attn(const orc_cfg* c, orc_pool* p, int32_t batch, const uint16_t* q,
+                    const int32_t* table, const int32_t* state, const int32_t* seq_len,
+                    float* out, int32_t update_scores) {
+  if (!cfg_valid(c) || !p || batch < 0) return ORC_E_INVALID;
+  if (p->page_bytes != orc_page_bytes(c)) return ORC_E_INVALID;
+  int32_t H = c->num_kv_heads, G = c->gqa_group, d = c->head_dim, L = orc_table_len(c);
+  int32_t Th = c->hi_page_tokens, Tl = c->lo_page_tokens;
+  memset(out, 0, sizeof(float) * (size_t)batch * H * G * d);
+  uint32_t st = 0;
+  for (int64_t u = 0; u < (int64_t)batch * H; u++) {
+    int32_t b = (int32_t)(u / H), h = (int32_t)(u % H);
+    if (seq_len[b] <= 0) continue;
+    const int32_t* s4 = state + 4 * u;
+    const int32_t* row = table + u * L;
+    int32_t n_hi = s4[0], n_lo = s4[1];
+    int bad = (n_hi < 0 || n_lo < 0 || s4[2] != cdiv64(n_hi, Th) || s4[3] != cdiv64(n_lo, Tl) ||
+               s4[2] + s4[3] > L);
+    if (!bad) {
+      for (int32_t j = 0; j < s4[2]; j++) if (row[j] < 0 || row[j] >= p->num_pages) bad = 1;
+      for (int32_t j = 0; j < s4[3]; j++) if (row[L - 1 - j] < 0 || row[L - 1 - j] >= p->num_pages) bad = 1;
+    }
+    if (bad) { st |= ORC_ST_BAD_STATE; continue; }
+    int32_t n = n_hi + n_lo;
+    if (n == 0) continue;
+    double* kh = (double*)malloc(sizeof(double) * (size_t)n * d);
+    double* vh = (double*)malloc(sizeof(double) * (size_t)n * d);
+    int32_t* tier = (int32_t*)malloc(sizeof(int32_t) * (size_t)n);
+    int32_t* slot = (int32_t*)malloc(sizeof(int32_t) * (size_t)n);
+    int32_t* pos = (int32_t*)malloc(sizeof(int32_t) * (size_t)n);
+    double* pmax = (double*)calloc((size_t)n, sizeof(double));
+    double* x = (double*)malloc(sizeof(double) * (size_t)n);
+    for (int32_t t = 0; t < n; t++) {
+      int32_t tr = t < n_hi ? ORC_HI : ORC_LO;
+      int32_t s = t < n_hi ? t : t - n_hi;
+      uint8_t kc[128], vc[128];
+      uint16_t km[2], vm[2];
+      float sc;
+      const uint8_t* pg = slot_page(p, row, L, tr, s, c);
+      orc_read_slot(c, pg, tr, s % (tr == ORC_HI ? Th : Tl), kc, vc, km, vm, &sc, &pos[t]);
+      tier[t] = tr;
+      slot[t] = s;
+      for (int32_t i = 0; i < d; i++) {
+        kh[(int64_t)t * d + i] = (double)orc_dequant(km[0], km[1], kc[i]);
+        vh[(int64_t)t * d + i] = (double)orc_dequant(vm[0], vm[1], vc[i]);
+      }
+    }
+    double scale = 1.0 / sqrt((double)d);
+    for (int32_t g = 0; g < G; g++) {
+      int32_t jh = h * G + g;
+      const uint16_t* qr = q + ((int64_t)b * H * G + jh) * d;
+      double qd[128];
+      for (int32_t i = 0; i < d; i++) qd[i] = (double)orc_f16_to_f32(qr[i]);
+      double m = -INFINITY, z = 0.0;
+      for (int32_t t = 0; t < n; t++) {
+        double acc = 0.0;
+        for (int32_t i = 0; i < d; i++) acc += qd[i] * kh[(int64_t)t * d + i];
+        x[t] = acc * scale;
+        if (x[t] > m) m = x[t];
+      }
+      for (int32_t t = 0; t < n; t++) z += exp(x[t] - m);
+      float* o = out + ((int64_t)b * H * G + jh) * d;
+      for (int32_t i = 0; i < d; i++) {
+        double acc = 0.0;
+        for (int32_t t = 0; t < n; t++) acc += exp(x[t] - m) / z * vh[(int64_t)t * d + i];
+        o[i] = (float)acc;
+      }
+      for (int32_t t = 0; t < n; t++) {
+        double pr = exp(x[t] - m) / z;
+        if (pr > pmax[t]) pmax[t] = pr;
+      }
+    }
+    if (update_scores) {
+      for (int32_t t = 0; t < n; t++) {
+        if (pos[t] >= seq_len[b]) continue;
+        int32_t tr = tier[t], s = slot[t];
+        uint8_t* pg = slot_page(p, row, L, tr, s, c);
+        int32_t seg[7];
+        orc_tier_layout(c, tr, seg);
+        uint8_t* sp = pg + seg[4] + 4 * (s % (tr == ORC_HI ? Th : Tl));
+        float old = bits_f32(get_u32(sp));
+        float nw = (float)((double)old + pmax[t]);
+        put_u32(sp, f32_bits(nw));
+      }
+    }
+    free(kh); free(vh); free(tier); free(slot); free(pos); free(pmax); free(x);
+  }
+  p->status[0] |= st;
+  return ORC_OK;
+}
+
+/* Prompt importance ("KV compression policy", prompt phase: a token's
+ * importance is the mean of the attention it receives; for GQA the group's
+ * q heads are combined with max).  Here the receiving attention comes from
+ * nq probe queries per request that attend to every token of the request;
+ * per probe query the max over the group's q heads is taken, then the mean
+ * over probes (fp64, rounded to fp32 once). */
+int orc_importance_from_queries(const orc_cfg* c, int32_t batch, const int64_t* cu,
+                                const uint16_t* k, int32_t nq, const uint16_t* qp,
+                                float* scores) {
+  if (!cfg_valid(c) || !cu_valid(batch, cu) || nq < 1) return ORC_E_INVALID;
+  int32_t H = c->num_kv_heads, G = c->gqa_group, d = c->head_dim;
+  int64_t total = cu[batch];
+  double scale = 1.0 / sqrt((double)d);
+  for (int32_t r = 0; r < batch; r++) {
+    int64_t N = cu[r + 1] - cu[r];
+    if (N <= 0) continue;
+    double* acc = (double*)malloc(sizeof(double) * (size_t)N);
+    double* mx = (double*)malloc(sizeof(double) * (size_t)N);
+    double* x = (double*)malloc(sizeof(double) * (size_t)N);
+    for (int32_t h = 0; h < H; h++) {
+      for (int64_t t = 0; t < N; t++) acc[t] = 0.0;
+      for (int32_t qi = 0; qi < nq; qi++) {
+        for (int64_t t = 0; t < N; t++) mx[t] = 0.0;
+        for (int32_t g = 0; g < G; g++) {
+          const uint16_t* qr = qp + (((int64_t)r * nq + qi) * H * G + (h * G + g)) * d;
+          double m = -INFINITY, z = 0.0;
+          for (int64_t t = 0; t < N; t++) {
+            const uint16_t* kr = k + ((cu[r] + t) * H + h) * d;
+            double a = 0.0;
+            for (int32_t i = 0; i < d; i++)
+              a += (double)orc_f16_to_f32(qr[i]) * (double)orc_f16_to_f32(kr[i]);
+            x[t] = a * scale;
+            if (x[t] > m) m = x[t];
+          }
+          for (int64_t t = 0; t < N; t++) z += exp(x[t] - m);
+          for (int64_t t = 0; t < N; t++) {
+            double pr = exp(x[t] - m) / z;
+            if (pr > mx[t]) mx[t] = pr;
+          }
+        }
+        for (int64_t t = 0; t < N; t++) acc[t] += mx[t];
+      }
+      for (int64_t t = 0; t < N; t++) scores[(int64_t)h * total + cu[r] + t] = (float)(acc[t] / nq);
+    }
+    free(acc); free(mx); free(x);
+  }
+  return ORC_OK;
+}

@@ -1,0 +1,132 @@
+/*
+ * diffkv_oracle.h -- plain, slow, serial CPU oracle for the DiffKV hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link
+ * or call this.  Only tests/, __graft_entry__.smoke() and bench.py's
+ * cpu_baseline leg use it.  It shares no code, header, table or helper with
+ * the HIP library; the two agree only through the written specification of
+ * the page layout and the policy readings.
+ *
+ * Source of what is computed: the notes page "DiffKV: Differentiated Memory
+ * Management for Large Language Models with Parallel KV Compaction"
+ * (SOSP'25, arXiv 2412.03131), sections "Background" (attention formula and
+ * asymmetric quantization), "KV compression policy" (prompt- and
+ * generation-phase logic), "Memory management" (unified pages, circular free
+ * page list, bidirectional page table, Fig 6 prompt workflow, generation
+ * workflow) and "Implementation" (compactor before attention).
+ *
+ * All buffers are host memory owned by the caller.  Layouts match the HIP
+ * library's C-ABI so parity tests can compare them byte for byte.
+ */
+#ifndef DIFFKV_ORACLE_H
+#define DIFFKV_ORACLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+  int32_t head_dim;       /* d: 64 or 128 */
+  int32_t num_kv_heads;   /* H */
+  int32_t gqa_group;      /* G: q head j reads KV head j / G */
+  int32_t hi_page_tokens; /* T_h (16) */
+  int32_t lo_page_tokens; /* T_l = 2 T_h */
+  int32_t max_seq_len;    /* S_max; table row length L_max = ceil(S_max/T_h)+1 */
+  int32_t window;         /* W: most recent tokens always high precision */
+  int32_t lo_enabled;     /* 0: high / prune only */
+  float alpha_h, alpha_l; /* thresholds are alpha/N */
+} orc_cfg;
+
+typedef struct {
+  uint8_t* pages;     /* [num_pages * page_bytes] */
+  int32_t* free_list; /* [num_pages] circular list of page ids */
+  uint64_t* ptr;      /* [2]: allocation counter (start), reclaim counter (end) */
+  uint32_t* status;   /* [1] sticky status bits */
+  int64_t num_pages;
+  int32_t page_bytes;
+} orc_pool;
+
+enum { ORC_OK = 0, ORC_E_INVALID = 1 };
+enum { ORC_ST_POOL_EXHAUSTED = 1u, ORC_ST_TABLE_OVERFLOW = 2u, ORC_ST_BAD_STATE = 4u };
+enum { ORC_PRUNE = 0, ORC_LO = 1, ORC_HI = 2 };
+
+/* ---- layout ---------------------------------------------------------- */
+int32_t orc_page_bytes(const orc_cfg* c);
+int32_t orc_table_len(const orc_cfg* c);
+/* seg[0..5] = byte offsets of K codes, K meta, V codes, V meta, score, pos;
+ * seg[6] = bytes used by the tier; returns tokens per page of the tier. */
+int32_t orc_tier_layout(const orc_cfg* c, int32_t tier, int32_t seg[7]);
+/* Byte offset and bit shift of one K or V code inside a page of `tier`. */
+void orc_k_code_addr(const orc_cfg* c, int32_t tier, int32_t tok, int32_t j,
+                     int32_t* byte, int32_t* shift);
+void orc_v_code_addr(const orc_cfg* c, int32_t tier, int32_t tok, int32_t j,
+                     int32_t* byte, int32_t* shift);
+/* Unpack one slot of a page: codes one per byte, metadata, score, pos. */
+void orc_read_slot(const orc_cfg* c, const uint8_t* page, int32_t tier, int32_t slot,
+                   uint8_t* kc, uint8_t* vc, uint16_t* kmeta /*[2]*/,
+                   uint16_t* vmeta /*[2]*/, float* score, int32_t* pos);
+
+/* ---- fp16 and codec ---------------------------------------------------- */
+uint16_t orc_f32_to_f16(float f);
+float orc_f16_to_f32(uint16_t h);
+void orc_f32_to_f16_n(const float* x, uint16_t* h, int64_t n);
+void orc_f16_to_f32_n(const uint16_t* h, float* x, int64_t n);
+/* Per-vector asymmetric min/max quantization to `bits` (8, 4 or 2). */
+void orc_quantize(const float* x, int32_t n, int32_t bits, uint16_t* s16,
+                  uint16_t* z16, uint8_t* codes);
+float orc_dequant(uint16_t s16, uint16_t z16, int32_t code);
+
+/* ---- policy ------------------------------------------------------------ */
+int orc_classify(const orc_cfg* c, int32_t batch, const int64_t* cu_seqlens,
+                 const float* scores, uint8_t* tiers, int32_t* tier_counts);
+
+/* Plan + allocation part of prompt compaction on page counts only (used by
+ * the worked-example test with small pages).  n_hi/n_lo: [batch*H]; seqlens
+ * [batch]; writes tables and state; returns ORC_OK or ORC_E_INVALID. */
+int orc_prompt_allocate(int32_t H, int32_t T_h, int32_t T_l, int32_t L_max,
+                        int32_t batch, const int64_t* seqlens,
+                        const int32_t* n_hi, const int32_t* n_lo,
+                        int32_t* free_list, uint64_t* ptr, uint32_t* status,
+                        int64_t num_pages, int32_t* page_table,
+                        int32_t* tier_state);
+
+int orc_pool_init(orc_pool* p);
+int orc_compact_prompt(const orc_cfg* c, orc_pool* p, int32_t batch,
+                       const int64_t* cu_seqlens, const uint16_t* k,
+                       const uint16_t* v, const float* scores,
+                       const uint8_t* tiers, int32_t* page_table,
+                       int32_t* tier_state);
+int orc_compact_step(const orc_cfg* c, orc_pool* p, int32_t batch,
+                     const int32_t* seq_len, const uint16_t* k_new,
+                     const uint16_t* v_new, int32_t* page_table,
+                     int32_t* tier_state);
+int orc_release(const orc_cfg* c, orc_pool* p, int32_t batch,
+                const uint8_t* release_mask, int32_t* page_table,
+                int32_t* tier_state);
+
+/* ---- attention ----------------------------------------------------------- */
+int orc_decode_attn(const orc_cfg* c, orc_pool* p, int32_t batch,
+                    const uint16_t* q, const int32_t* page_table,
+                    const int32_t* tier_state, const int32_t* seq_len,
+                    float* out, int32_t update_scores);
+/* Full-precision textbook attention of one query over n keys (fp64). */
+void orc_attention_dense(const double* q, const double* k, const double* v,
+                         int32_t n, int32_t d, double* out);
+/* Same output through the coefficient x unit-vector decomposition. */
+void orc_attention_unit_vectors(const double* q, const double* k,
+                                const double* v, int32_t n, int32_t d,
+                                double* out);
+/* Prompt importance from nq probe queries: per token, mean over queries of
+ * the max over the G q heads of a KV head of the softmax weight. */
+int orc_importance_from_queries(const orc_cfg* c, int32_t batch,
+                                const int64_t* cu_seqlens, const uint16_t* k,
+                                int32_t nq, const uint16_t* qprobe,
+                                float* scores);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
