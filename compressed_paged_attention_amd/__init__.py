@@ -1,0 +1,230 @@
+"""Python binding of libdiffkv.so (the MI355X DiffKV hot path).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  torch provides device memory and the current stream.  The C entry
+points keep their names (``diffkv_classify``, ``diffkv_compact``,
+``diffkv_decode_attn`` ...); ``DiffKVState`` only allocates the caller-owned
+device buffers those calls work on.
+
+The library must be built (``python -m compressed_paged_attention_amd.build``
+or ``__graft_entry__.build()``); importing a missing library raises instead of
+falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdiffkv.so")
+
+DIFFKV_OK, DIFFKV_E_INVALID, DIFFKV_E_WORKSPACE, DIFFKV_E_HIP = 0, 1, 2, 3
+ST_POOL_EXHAUSTED, ST_TABLE_OVERFLOW, ST_BAD_STATE = 1, 2, 4
+PROMPT, STEP, RELEASE, ATTN, ATTN_SCORES = 0, 1, 2, 3, 4
+PRUNE, LO, HI = 0, 1, 2
+
+
+class DiffKVError(RuntimeError):
+    pass
+
+
+class diffkv_config(ctypes.Structure):
+    _fields_ = [("head_dim", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("gqa_group", ctypes.c_int32), ("hi_page_tokens", ctypes.c_int32),
+                ("lo_page_tokens", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("lo_enabled", ctypes.c_int32),
+                ("alpha_h", ctypes.c_float), ("alpha_l", ctypes.c_float)]
+
+
+class diffkv_pool(ctypes.Structure):
+    _fields_ = [("pages", ctypes.c_void_p), ("free_list", ctypes.c_void_p),
+                ("ptr", ctypes.c_void_p), ("status", ctypes.c_void_p),
+                ("num_pages", ctypes.c_int64), ("page_bytes", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Loads libdiffkv.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise DiffKVError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m compressed_paged_attention_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        cfgp = ctypes.POINTER(diffkv_config)
+        poolp = ctypes.POINTER(diffkv_pool)
+        L.diffkv_page_bytes.argtypes = [cfgp]
+        L.diffkv_page_bytes.restype = i32
+        L.diffkv_table_len.argtypes = [cfgp]
+        L.diffkv_table_len.restype = i32
+        L.diffkv_attn_splits.argtypes = [cfgp, i32]
+        L.diffkv_attn_splits.restype = i32
+        L.diffkv_workspace_bytes.argtypes = [cfgp, i32, i32, i64]
+        L.diffkv_workspace_bytes.restype = sz
+        L.diffkv_pool_init.argtypes = [cfgp, poolp, vp]
+        L.diffkv_state_init.argtypes = [cfgp, i32, vp, vp, vp]
+        L.diffkv_classify.argtypes = [cfgp, i32, i64, vp, vp, vp, vp, vp]
+        L.diffkv_compact.argtypes = [cfgp, poolp, i32, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                     vp, sz, vp]
+        L.diffkv_decode_attn.argtypes = [cfgp, poolp, i32, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+        for f in ("diffkv_pool_init", "diffkv_state_init", "diffkv_classify", "diffkv_compact",
+                  "diffkv_decode_attn"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def make_config(c: dict) -> diffkv_config:
+    return diffkv_config(int(c["head_dim"]), int(c["num_kv_heads"]), int(c["gqa_group"]),
+                         int(c.get("hi_page_tokens", 16)), int(c.get("lo_page_tokens", 32)),
+                         int(c["max_seq_len"]), int(c["window"]), int(c.get("lo_enabled", 1)),
+                         float(c["alpha_h"]), float(c["alpha_l"]))
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    if t is None:
+        return ctypes.c_void_p(0)
+    if not t.is_cuda:
+        raise DiffKVError("device tensor expected")
+    if not t.is_contiguous():
+        raise DiffKVError("contiguous tensor expected")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(rc: int, what: str):
+    if rc != DIFFKV_OK:
+        raise DiffKVError(f"{what} failed with code {rc}")
+
+
+def diffkv_page_bytes(cfg: dict) -> int:
+    return lib().diffkv_page_bytes(ctypes.byref(make_config(cfg)))
+
+
+def diffkv_table_len(cfg: dict) -> int:
+    return lib().diffkv_table_len(ctypes.byref(make_config(cfg)))
+
+
+def diffkv_attn_splits(cfg: dict, batch: int) -> int:
+    return lib().diffkv_attn_splits(ctypes.byref(make_config(cfg)), batch)
+
+
+def diffkv_workspace_bytes(cfg: dict, op: int, batch: int, total_tokens: int = 0) -> int:
+    return lib().diffkv_workspace_bytes(ctypes.byref(make_config(cfg)), op, batch, total_tokens)
+
+
+class Pool:
+    """Caller-owned device buffers of one page pool (torch allocations)."""
+
+    def __init__(self, cfg: dict, num_pages: int, device="cuda"):
+        self.cfg = dict(cfg)
+        self.num_pages = int(num_pages)
+        self.page_bytes = diffkv_page_bytes(cfg)
+        if self.page_bytes <= 0:
+            raise DiffKVError("invalid config")
+        self.pages = torch.empty(self.num_pages * self.page_bytes, dtype=torch.uint8, device=device)
+        self.free_list = torch.empty(self.num_pages, dtype=torch.int32, device=device)
+        self.ptr = torch.empty(2, dtype=torch.int64, device=device)
+        self.status = torch.empty(1, dtype=torch.int32, device=device)
+
+    def struct(self) -> diffkv_pool:
+        return diffkv_pool(self.pages.data_ptr(), self.free_list.data_ptr(), self.ptr.data_ptr(),
+                           self.status.data_ptr(), self.num_pages, self.page_bytes)
+
+
+def diffkv_pool_init(cfg: dict, pool: Pool, stream=None):
+    _check(lib().diffkv_pool_init(ctypes.byref(make_config(cfg)), ctypes.byref(pool.struct()),
+                                  _stream(stream)), "diffkv_pool_init")
+
+
+def diffkv_state_init(cfg: dict, batch: int, page_table, tier_state, stream=None):
+    _check(lib().diffkv_state_init(ctypes.byref(make_config(cfg)), batch, _ptr(page_table),
+                                   _ptr(tier_state), _stream(stream)), "diffkv_state_init")
+
+
+def diffkv_classify(cfg: dict, cu_seqlens, scores, tiers, tier_counts, total_tokens: int, stream=None):
+    batch = cu_seqlens.numel() - 1
+    _check(lib().diffkv_classify(ctypes.byref(make_config(cfg)), batch, int(total_tokens),
+                                 _ptr(cu_seqlens), _ptr(scores), _ptr(tiers), _ptr(tier_counts),
+                                 _stream(stream)), "diffkv_classify")
+
+
+def diffkv_compact(cfg: dict, pool: Pool, mode: int, batch: int, page_table, tier_state, workspace,
+                   total_tokens: int = 0, cu_seqlens=None, seq_len=None, k=None, v=None, scores=None,
+                   tiers=None, release_mask=None, stream=None):
+    _check(lib().diffkv_compact(ctypes.byref(make_config(cfg)), ctypes.byref(pool.struct()), mode, batch,
+                                int(total_tokens), _ptr(cu_seqlens), _ptr(seq_len), _ptr(k), _ptr(v),
+                                _ptr(scores), _ptr(tiers), _ptr(release_mask), _ptr(page_table),
+                                _ptr(tier_state), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                _stream(stream)), "diffkv_compact")
+
+
+def diffkv_decode_attn(cfg: dict, pool: Pool, batch: int, q, page_table, tier_state, seq_len, out,
+                       update_scores: bool, workspace, stream=None):
+    _check(lib().diffkv_decode_attn(ctypes.byref(make_config(cfg)), ctypes.byref(pool.struct()), batch,
+                                    _ptr(q), _ptr(page_table), _ptr(tier_state), _ptr(seq_len), _ptr(out),
+                                    1 if update_scores else 0, _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream)),
+           "diffkv_decode_attn")
+
+
+class DiffKVState:
+    """All device buffers of one cache (pool, tables, workspaces) for `batch` slots."""
+
+    def __init__(self, cfg: dict, batch: int, num_pages: int, max_total_tokens: int = 0, device="cuda"):
+        self.cfg = dict(cfg)
+        self.batch = batch
+        self.H = int(cfg["num_kv_heads"])
+        self.G = int(cfg["gqa_group"])
+        self.d = int(cfg["head_dim"])
+        self.L = diffkv_table_len(cfg)
+        self.pool = Pool(cfg, num_pages, device)
+        self.page_table = torch.empty(batch, self.H, self.L, dtype=torch.int32, device=device)
+        self.tier_state = torch.empty(batch, self.H, 4, dtype=torch.int32, device=device)
+        cws = max(diffkv_workspace_bytes(cfg, PROMPT, batch, max_total_tokens),
+                  diffkv_workspace_bytes(cfg, STEP, batch), diffkv_workspace_bytes(cfg, RELEASE, batch))
+        self.ws_compact = torch.empty(cws, dtype=torch.uint8, device=device)
+        self.ws_attn = torch.zeros(diffkv_workspace_bytes(cfg, ATTN_SCORES, batch), dtype=torch.uint8,
+                                   device=device)
+        diffkv_pool_init(cfg, self.pool)
+        diffkv_state_init(cfg, batch, self.page_table, self.tier_state)
+
+    def classify(self, cu_seqlens, scores):
+        total = int(scores.shape[1])
+        tiers = torch.empty(self.H, total, dtype=torch.uint8, device=scores.device)
+        counts = torch.empty(cu_seqlens.numel() - 1, self.H, 2, dtype=torch.int32, device=scores.device)
+        diffkv_classify(self.cfg, cu_seqlens, scores, tiers, counts, total)
+        return tiers, counts
+
+    def compact_prompt(self, cu_seqlens, k, v, scores, tiers):
+        total = int(scores.shape[1])
+        need = diffkv_workspace_bytes(self.cfg, PROMPT, self.batch, total)
+        if self.ws_compact.numel() < need:
+            self.ws_compact = torch.empty(need, dtype=torch.uint8, device=self.ws_compact.device)
+        diffkv_compact(self.cfg, self.pool, PROMPT, self.batch, self.page_table, self.tier_state,
+                       self.ws_compact, total_tokens=total, cu_seqlens=cu_seqlens, k=k, v=v,
+                       scores=scores, tiers=tiers)
+
+    def compact_step(self, seq_len, k_new, v_new):
+        diffkv_compact(self.cfg, self.pool, STEP, self.batch, self.page_table, self.tier_state,
+                       self.ws_compact, seq_len=seq_len, k=k_new, v=v_new)
+
+    def release(self, mask):
+        diffkv_compact(self.cfg, self.pool, RELEASE, self.batch, self.page_table, self.tier_state,
+                       self.ws_compact, release_mask=mask)
+
+    def decode_attn(self, q, seq_len, update_scores: bool = False, out=None):
+        if out is None:
+            out = torch.empty(self.batch, self.H * self.G, self.d, dtype=torch.float32, device=q.device)
+        diffkv_decode_attn(self.cfg, self.pool, self.batch, q, self.page_table, self.tier_state, seq_len,
+                           out, update_scores, self.ws_attn)
+        return out

@@ -1,0 +1,151 @@
+// api.hip -- the exported C-ABI of libdiffkv.so (declared in include/diffkv.h):
+// host-side validation, workspace sizing and kernel launches.
+#include <hip/hip_runtime.h>
+
+#include "../../include/diffkv.h"
+#include "dkv_common.hpp"
+#include "dkv_launch.hpp"
+
+using namespace dkv;
+
+namespace {
+
+bool cfg_ok(const diffkv_config* c) {
+  if (!c) return false;
+  if (c->head_dim != 64 && c->head_dim != 128) return false;
+  if (c->num_kv_heads < 1 || c->gqa_group < 1 || c->gqa_group > 16) return false;
+  if (c->hi_page_tokens != kHiTokens || c->lo_page_tokens != kLoTokens) return false;
+  if (c->max_seq_len < 1 || c->window < 0) return false;
+  if (!(c->alpha_l >= 0.0f) || !(c->alpha_h >= 0.0f)) return false;
+  if (c->lo_enabled && c->alpha_l > c->alpha_h) return false;
+  return true;
+}
+
+Cfg to_cfg(const diffkv_config* c) {
+  Cfg r;
+  r.d = c->head_dim;
+  r.H = c->num_kv_heads;
+  r.G = c->gqa_group;
+  r.L = (c->max_seq_len + kHiTokens - 1) / kHiTokens + 1;
+  r.W = c->window;
+  r.lo_en = c->lo_enabled ? 1 : 0;
+  r.S_max = c->max_seq_len;
+  r.ah = c->alpha_h;
+  r.al = c->alpha_l;
+  return r;
+}
+
+bool pool_ok(const diffkv_config* c, const diffkv_pool* p) {
+  return p && p->pages && p->free_list && p->ptr && p->status && p->num_pages >= 1 &&
+         p->num_pages < (int64_t(1) << 31) && p->page_bytes == page_bytes_for(c->head_dim);
+}
+
+Pool to_pool(const diffkv_pool* p) {
+  return Pool{(uint8_t*)p->pages, p->free_list, p->ptr, p->status, p->num_pages, p->page_bytes};
+}
+
+int rc(hipError_t e) { return e == hipSuccess ? DIFFKV_OK : DIFFKV_E_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t diffkv_page_bytes(const diffkv_config* cfg) {
+  if (!cfg_ok(cfg)) return -1;
+  return page_bytes_for(cfg->head_dim);
+}
+
+int32_t diffkv_table_len(const diffkv_config* cfg) {
+  if (!cfg_ok(cfg)) return -1;
+  return to_cfg(cfg).L;
+}
+
+int32_t diffkv_attn_splits(const diffkv_config* cfg, int32_t batch) {
+  if (!cfg_ok(cfg) || batch < 0) return -1;
+  return attn_splits(to_cfg(cfg), batch);
+}
+
+size_t diffkv_workspace_bytes(const diffkv_config* cfg, int32_t op, int32_t batch, int64_t total_tokens) {
+  if (!cfg_ok(cfg) || batch < 0 || total_tokens < 0) return 0;
+  const Cfg c = to_cfg(cfg);
+  switch (op) {
+    case DIFFKV_PROMPT: return prompt_workspace(c, batch, total_tokens);
+    case DIFFKV_STEP: return step_workspace(c, batch);
+    case DIFFKV_RELEASE: return release_workspace(c, batch);
+    case DIFFKV_ATTN: return attn_workspace(c, batch, false);
+    case DIFFKV_ATTN_SCORES: return attn_workspace(c, batch, true);
+    default: return 0;
+  }
+}
+
+int diffkv_pool_init(const diffkv_config* cfg, const diffkv_pool* pool, void* stream) {
+  if (!cfg_ok(cfg) || !pool_ok(cfg, pool)) return DIFFKV_E_INVALID;
+  return rc(launch_pool_init(to_pool(pool), (hipStream_t)stream));
+}
+
+int diffkv_state_init(const diffkv_config* cfg, int32_t batch, int32_t* page_table, int32_t* tier_state,
+                      void* stream) {
+  if (!cfg_ok(cfg) || batch < 0 || (batch > 0 && (!page_table || !tier_state))) return DIFFKV_E_INVALID;
+  return rc(launch_state_init(to_cfg(cfg), batch, page_table, tier_state, (hipStream_t)stream));
+}
+
+int diffkv_classify(const diffkv_config* cfg, int32_t batch, int64_t total_tokens, const int64_t* cu_seqlens,
+                    const float* scores, uint8_t* tiers, int32_t* tier_counts, void* stream) {
+  if (!cfg_ok(cfg) || batch < 0 || total_tokens < 0) return DIFFKV_E_INVALID;
+  if (batch > 0 && (!cu_seqlens || !tier_counts)) return DIFFKV_E_INVALID;
+  if (total_tokens > 0 && (!scores || !tiers)) return DIFFKV_E_INVALID;
+  if (batch > 65535) return DIFFKV_E_INVALID;
+  return rc(launch_classify(to_cfg(cfg), batch, total_tokens, cu_seqlens, scores, tiers, tier_counts,
+                            (hipStream_t)stream));
+}
+
+int diffkv_compact(const diffkv_config* cfg, const diffkv_pool* pool, int32_t mode, int32_t batch,
+                   int64_t total_tokens, const int64_t* cu_seqlens, const int32_t* seq_len, const uint16_t* k,
+                   const uint16_t* v, const float* scores, const uint8_t* tiers, const uint8_t* release_mask,
+                   int32_t* page_table, int32_t* tier_state, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  if (!cfg_ok(cfg) || !pool_ok(cfg, pool) || batch < 0 || total_tokens < 0) return DIFFKV_E_INVALID;
+  if (batch > 0 && (!page_table || !tier_state)) return DIFFKV_E_INVALID;
+  if ((int64_t)batch * cfg->num_kv_heads > 65535) return DIFFKV_E_INVALID;
+  const Cfg c = to_cfg(cfg);
+  const Pool p = to_pool(pool);
+  hipStream_t s = (hipStream_t)stream;
+  size_t need = 0;
+  switch (mode) {
+    case DIFFKV_PROMPT:
+      if (batch > 0 && !cu_seqlens) return DIFFKV_E_INVALID;
+      if (total_tokens > 0 && (!k || !v || !scores || !tiers)) return DIFFKV_E_INVALID;
+      need = prompt_workspace(c, batch, total_tokens);
+      if (!workspace || workspace_bytes < need) return DIFFKV_E_WORKSPACE;
+      return rc(launch_prompt(c, p, batch, total_tokens, cu_seqlens, k, v, scores, tiers, page_table, tier_state,
+                              workspace, s));
+    case DIFFKV_STEP:
+      if (c.W < 2) return DIFFKV_E_INVALID;
+      if (batch > 0 && (!seq_len || !k || !v)) return DIFFKV_E_INVALID;
+      need = step_workspace(c, batch);
+      if (!workspace || workspace_bytes < need) return DIFFKV_E_WORKSPACE;
+      return rc(launch_step(c, p, batch, seq_len, k, v, page_table, tier_state, workspace, s));
+    case DIFFKV_RELEASE:
+      if (batch > 0 && !release_mask) return DIFFKV_E_INVALID;
+      need = release_workspace(c, batch);
+      if (!workspace || workspace_bytes < need) return DIFFKV_E_WORKSPACE;
+      return rc(launch_release(c, p, batch, release_mask, page_table, tier_state, workspace, s));
+    default:
+      return DIFFKV_E_INVALID;
+  }
+}
+
+int diffkv_decode_attn(const diffkv_config* cfg, const diffkv_pool* pool, int32_t batch, const uint16_t* q,
+                       const int32_t* page_table, const int32_t* tier_state, const int32_t* seq_len, float* out,
+                       int32_t update_scores, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!cfg_ok(cfg) || !pool_ok(cfg, pool) || batch < 0) return DIFFKV_E_INVALID;
+  if (batch > 0 && (!q || !page_table || !tier_state || !seq_len || !out)) return DIFFKV_E_INVALID;
+  if ((int64_t)batch * cfg->num_kv_heads > 65535) return DIFFKV_E_INVALID;
+  const Cfg c = to_cfg(cfg);
+  const size_t need = attn_workspace(c, batch, update_scores != 0);
+  if (!workspace || workspace_bytes < need) return DIFFKV_E_WORKSPACE;
+  return rc(launch_attn(c, to_pool(pool), batch, q, page_table, tier_state, seq_len, out, update_scores != 0,
+                        workspace, (hipStream_t)stream));
+}
+
+}  // extern "C"

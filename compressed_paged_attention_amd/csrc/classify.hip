@@ -1,0 +1,108 @@
+// classify.hip -- pool/state initialisation and token classification.
+//
+// Classification follows the "Approach" summary and the prompt-phase logic
+// of "KV compression policy" in the DiffKV notes: the most recent W tokens
+// are high precision; any other token is high if its mean score exceeds
+// alpha_h/N, low if it lies in [alpha_l/N, alpha_h/N], pruned below
+// alpha_l/N (N = the request's length).  The comparison is s*N against alpha
+// in fp64, exact for N < 2^29, so no division rounding decides a tier.
+#include "dkv_common.hpp"
+#include "dkv_launch.hpp"
+
+namespace dkv {
+
+__global__ void pool_init_kernel(int32_t* list, uint64_t* ptr, uint32_t* status, int64_t P) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < P) list[i] = (int32_t)i;
+  if (i == 0) {
+    ptr[0] = 0;
+    ptr[1] = (uint64_t)P;
+    status[0] = 0;
+  }
+}
+
+__global__ void state_init_kernel(int32_t* table, int64_t n_table, int32_t* state, int64_t n_state) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n_table) table[i] = -1;
+  if (i < n_state) state[i] = 0;
+}
+
+hipError_t launch_pool_init(const Pool& p, hipStream_t s) {
+  const int64_t blocks = (p.P + 255) / 256;
+  pool_init_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p.list, p.ptr, p.status, p.P);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_init(const Cfg& c, int batch, int32_t* table, int32_t* state, hipStream_t s) {
+  const int64_t nt = (int64_t)batch * c.H * c.L, ns = (int64_t)batch * c.H * 4;
+  const int64_t n = nt > ns ? nt : ns;
+  if (n == 0) return hipSuccess;
+  state_init_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(table, nt, state, ns);
+  return hipGetLastError();
+}
+
+__device__ inline int tier_of(float s, int64_t N, int64_t p, int W, int lo_en, double ah, double al) {
+  if (W > 0 && p >= N - W) return kTierHi;
+  const double x = (double)s * (double)N;
+  if (lo_en) {
+    if (x > ah) return kTierHi;
+    return x >= al ? kTierLo : kTierPrune;
+  }
+  return x >= al ? kTierHi : kTierPrune;
+}
+
+// grid (H, batch); one workgroup per unit walks its tokens and reduces the
+// two counts.
+__global__ __launch_bounds__(1024) void classify_kernel(int H, int W, int lo_en, float ah, float al,
+                                                        int64_t total, const int64_t* __restrict__ cu,
+                                                        const float* __restrict__ scores,
+                                                        uint8_t* __restrict__ tiers,
+                                                        int32_t* __restrict__ counts) {
+  const int h = blockIdx.x, r = blockIdx.y;
+  const int64_t b0 = cu[r], N = cu[r + 1] - b0;
+  if (b0 < 0 || N < 0 || cu[r + 1] > total) {  // inconsistent offsets: nothing is read
+    if (threadIdx.x == 0) {
+      counts[((int64_t)r * H + h) * 2 + 0] = 0;
+      counts[((int64_t)r * H + h) * 2 + 1] = 0;
+    }
+    return;
+  }
+  const float* s = scores + (int64_t)h * total + b0;
+  uint8_t* t = tiers + (int64_t)h * total + b0;
+  const double dah = (double)ah, dal = (double)al;
+  int nh = 0, nl = 0;
+  for (int64_t p = threadIdx.x; p < N; p += blockDim.x) {
+    const int ti = tier_of(s[p], N, p, W, lo_en, dah, dal);
+    t[p] = (uint8_t)ti;
+    nh += ti == kTierHi;
+    nl += ti == kTierLo;
+  }
+  __shared__ int red[2][16];
+  nh = wave_sum(nh);
+  nl = wave_sum(nl);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  if (lane == 0) {
+    red[0][wid] = nh;
+    red[1][wid] = nl;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int a = 0, b = 0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); w++) {
+      a += red[0][w];
+      b += red[1][w];
+    }
+    counts[((int64_t)r * H + h) * 2 + 0] = a;
+    counts[((int64_t)r * H + h) * 2 + 1] = b;
+  }
+}
+
+hipError_t launch_classify(const Cfg& c, int batch, int64_t total, const int64_t* cu,
+                           const float* scores, uint8_t* tiers, int32_t* counts, hipStream_t s) {
+  if (batch == 0) return hipSuccess;
+  classify_kernel<<<dim3(c.H, batch), dim3(1024), 0, s>>>(c.H, c.W, c.lo_en, c.ah, c.al, total, cu,
+                                                          scores, tiers, counts);
+  return hipGetLastError();
+}
+
+}  // namespace dkv

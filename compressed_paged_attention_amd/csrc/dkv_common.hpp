@@ -1,0 +1,189 @@
+// dkv_common.hpp -- device-side definitions shared by the libdiffkv kernels:
+// unified-page layout, the per-vector codec, and wave/block primitives for
+// gfx950 (wave64).
+//
+// Unified page ("Memory management" section of the DiffKV notes: six
+// segments -- quantized K, K metadata, quantized V, V metadata, token score,
+// position -- with a per-precision token count).  Segment order follows the
+// notes; every segment starts on a 16-byte boundary.
+//   high tier: 16 tokens, K 8 bit token-major [16][d], V 4 bit
+//   low tier : 32 tokens, K 4 bit token-major [32][d/2] (dim 2i low nibble),
+//              V 2 bit
+//   metadata : one 32-bit word per token, fp16 scale in bits 0-15, fp16 zero
+//              in bits 16-31
+//   score    : fp32 running sum of received attention; position: int32
+// V codes are token-vectorized and cut into 64 lane chunks of d/8 bytes so
+// that lane L = i + 16q of a wave reads exactly the operand it feeds to a
+// 16x16x16 matrix instruction: chunk L holds dims i + 16 nb of tokens
+// 4q..4q+3 (high; low: tokens 16 ks + 4q .. +3).  Inside a chunk, field
+// h = r mod 2 of pair P = 2M + r/2 (r = token mod 4; M = nb for high,
+// M = 2 nb + ks for low) sits in 32-bit word w at bit b:
+//   high: w = P / 4, b = 4 (P mod 4) + 16 h
+//   low : w = P / 8, b = 2 (P mod 8) + 16 h
+// so one AND/OR with 0x000F000F (0x00030003) after a shift yields a packed
+// pair of fp16 operands.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dkv {
+
+constexpr int kHiTokens = 16;
+constexpr int kLoTokens = 32;
+constexpr int kTierPrune = 0, kTierLo = 1, kTierHi = 2;
+constexpr uint32_t kStExhausted = 1u, kStOverflow = 2u, kStBadState = 4u;
+
+struct Seg {
+  int T, kbits, vbits, kc, km, vc, vm, sc, ps, bytes;
+};
+
+__host__ __device__ constexpr int r16(int x) { return (x + 15) & ~15; }
+
+__host__ __device__ constexpr Seg tier_seg(int d, bool hi) {
+  const int T = hi ? kHiTokens : kLoTokens;
+  const int kb = hi ? 8 : 4, vb = hi ? 4 : 2;
+  const int kc = 0;
+  const int km = kc + r16(T * d * kb / 8);
+  const int vc = km + r16(4 * T);
+  const int vm = vc + r16(T * d * vb / 8);
+  const int sc = vm + r16(4 * T);
+  const int ps = sc + r16(4 * T);
+  const int end = ps + r16(4 * T);
+  return Seg{T, kb, vb, kc, km, vc, vm, sc, ps, end};
+}
+
+__host__ __device__ constexpr int page_bytes_for(int d) {
+  return tier_seg(d, true).bytes > tier_seg(d, false).bytes ? tier_seg(d, true).bytes
+                                                           : tier_seg(d, false).bytes;
+}
+
+// Byte offset (from the page start) and bit shift of V code (tok, j).
+__host__ __device__ inline void v_field(int d, bool hi, int tok, int j, int& byte, int& shift) {
+  const Seg s = tier_seg(d, hi);
+  const int i = j & 15, nb = j >> 4, r = tok & 3, h = r & 1;
+  int lane, w, bit;
+  if (hi) {
+    const int P = 2 * nb + (r >> 1);
+    lane = i + 16 * (tok >> 2);
+    w = P >> 2;
+    bit = 4 * (P & 3) + 16 * h;
+  } else {
+    const int P = 2 * (2 * nb + (tok >> 4)) + (r >> 1);
+    lane = i + 16 * ((tok & 15) >> 2);
+    w = P >> 3;
+    bit = 2 * (P & 7) + 16 * h;
+  }
+  byte = s.vc + lane * (d / 8) + 4 * w + (bit >> 3);
+  shift = bit & 7;
+}
+
+// Byte offset and shift of K code (tok, j).
+__host__ __device__ inline void k_field(int d, bool hi, int tok, int j, int& byte, int& shift) {
+  if (hi) {
+    byte = tok * d + j;
+    shift = 0;
+  } else {
+    byte = tok * (d / 2) + (j >> 1);
+    shift = 4 * (j & 1);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp16 helpers (IEEE binary16, round to nearest even via v_cvt_f16_f32).
+// ---------------------------------------------------------------------------
+__device__ inline uint16_t f2h_bits(float x) {
+  _Float16 h = (_Float16)x;
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ inline float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+
+// ---------------------------------------------------------------------------
+// Per-vector asymmetric codec ("Background": Q = round((X - z)/s),
+// X^ = s Q + z).  z = fp16(min), s = fp16((max - min) / (2^b - 1)); codes use
+// the stored fp16 values, IEEE fp32 division and round-half-even, clamped to
+// [0, 2^b - 1]; s == 0 gives code 0.  Must match the CPU reference bit for
+// bit, so nothing here may be contracted or approximated.
+// ---------------------------------------------------------------------------
+__device__ inline void codec_params(float mn, float mx, int bits, uint16_t& s16, uint16_t& z16,
+                                    float& s, float& z) {
+  const float qmax = (float)((1 << bits) - 1);
+  const float range = __fsub_rn(mx, mn);
+  const float scale = __fdiv_rn(range, qmax);
+  s16 = f2h_bits(scale);
+  z16 = f2h_bits(mn);
+  s = h2f(s16);
+  z = h2f(z16);
+}
+
+__device__ inline uint32_t codec_code(float x, float s, float z, int bits) {
+  if (s == 0.0f) return 0u;
+  const float t = __fdiv_rn(__fsub_rn(x, z), s);
+  float r = rintf(t);
+  const float qmax = (float)((1 << bits) - 1);
+  r = fminf(fmaxf(r, 0.0f), qmax);
+  return (uint32_t)r;
+}
+
+// Dequantized value; the product of an fp16 scale and a code of <= 8 bits is
+// exact in fp32, so this is a single rounding.
+__device__ inline float dequant(float s, float z, uint32_t code) {
+  return __fadd_rn(__fmul_rn(s, (float)code), z);
+}
+
+// ---------------------------------------------------------------------------
+// wave64 / block primitives
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ inline T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ inline float wave_min(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Inclusive scan across a wave (Hillis-Steele over 64 lanes).
+template <typename T>
+__device__ inline T wave_incl_scan(T v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    T t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// Exclusive block scan of one value per thread; `lds` holds >= blockDim/64
+// elements; returns the exclusive prefix and writes the block total.
+template <typename T>
+__device__ inline T block_excl_scan(T v, T* lds, T& total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+  T inc = wave_incl_scan(v);
+  if (lane == 63) lds[wid] = inc;
+  __syncthreads();
+  if (wid == 0) {
+    T x = lane < nw ? lds[lane] : T(0);
+    T xi = wave_incl_scan(x);
+    if (lane < nw) lds[lane] = xi - x;
+    if (lane == nw - 1) lds[nw] = xi;
+  }
+  __syncthreads();
+  T res = inc - v + lds[wid];
+  total = lds[nw];
+  __syncthreads();
+  return res;
+}
+
+__device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace dkv

@@ -1,0 +1,56 @@
+// dkv_launch.hpp -- host-side launch wrappers of the libdiffkv kernels
+// (internal to the library; the exported C-ABI lives in api.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dkv {
+
+struct Cfg {
+  int d, H, G, L, W, lo_en, S_max;
+  float ah, al;
+};
+
+struct Pool {
+  uint8_t* pages;
+  int32_t* list;
+  uint64_t* ptr;
+  uint32_t* status;
+  int64_t P;
+  int page_bytes;
+};
+
+// classify / init
+hipError_t launch_pool_init(const Pool& p, hipStream_t s);
+hipError_t launch_state_init(const Cfg& c, int batch, int32_t* table, int32_t* state, hipStream_t s);
+hipError_t launch_classify(const Cfg& c, int batch, int64_t total, const int64_t* cu,
+                           const float* scores, uint8_t* tiers, int32_t* counts, hipStream_t s);
+
+// prompt compaction
+size_t prompt_workspace(const Cfg& c, int batch, int64_t total);
+hipError_t launch_prompt(const Cfg& c, const Pool& p, int batch, int64_t total, const int64_t* cu,
+                         const uint16_t* k, const uint16_t* v, const float* scores,
+                         const uint8_t* tiers, int32_t* table, int32_t* state, void* ws,
+                         hipStream_t s);
+
+// generation step and release
+size_t step_workspace(const Cfg& c, int batch);
+hipError_t launch_step(const Cfg& c, const Pool& p, int batch, const int32_t* seq_len,
+                       const uint16_t* k, const uint16_t* v, int32_t* table, int32_t* state,
+                       void* ws, hipStream_t s);
+size_t release_workspace(const Cfg& c, int batch);
+hipError_t launch_release(const Cfg& c, const Pool& p, int batch, const uint8_t* mask,
+                          int32_t* table, int32_t* state, void* ws, hipStream_t s);
+
+// decode attention
+int attn_splits(const Cfg& c, int batch);
+size_t attn_workspace(const Cfg& c, int batch, bool scores);
+hipError_t launch_attn(const Cfg& c, const Pool& p, int batch, const uint16_t* q,
+                       const int32_t* table, const int32_t* state, const int32_t* seq_len,
+                       float* out, bool update_scores, void* ws, hipStream_t s);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace dkv

@@ -1,0 +1,181 @@
+/*
+ * diffkv.h -- C-ABI of libdiffkv.so, the MI355X (gfx950) DiffKV hot path:
+ * differentiated KV compaction and paged decode attention over the
+ * compacted cache.
+ *
+ * What is computed follows the notes page "DiffKV: Differentiated Memory
+ * Management for Large Language Models with Parallel KV Compaction"
+ * (SOSP'25, arXiv 2412.03131).  Each entry point names the section it
+ * implements.
+ *
+ * Conventions (all entry points)
+ *  - Every pointer argument is DEVICE memory unless marked "host".  The
+ *    caller allocates and owns every buffer; the library allocates nothing
+ *    and keeps no global state, so distinct pools can be used concurrently.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *    kernels on it and return without synchronizing.
+ *  - fp16 tensors travel as raw IEEE binary16 bits (uint16_t).
+ *  - Tensors are row-major and contiguous in the shapes given below.
+ *  - Return codes report host-detectable problems only: DIFFKV_E_INVALID
+ *    (null pointer, bad config or sizes), DIFFKV_E_WORKSPACE (workspace
+ *    smaller than diffkv_workspace_bytes), DIFFKV_E_HIP (launch error).  On
+ *    a non-zero return nothing was enqueued.
+ *  - Conditions found on the device (pool exhausted, table row overflow,
+ *    inconsistent state) set sticky bits in pool->status; a compaction call
+ *    that sets one commits nothing (all or nothing over the whole call).
+ *    The caller reads status after synchronizing and clears it itself.
+ *  - Determinism: identical inputs give byte-identical outputs; no result
+ *    depends on the order of atomic operations.
+ *
+ * Units: one (request b, KV head h) pair, u = b*H + h.  Tiers: 2 = high
+ * (K 8 bit, V 4 bit, 16 tokens per page), 1 = low (K 4 bit, V 2 bit, 32
+ * tokens per page), 0 = pruned.
+ */
+#ifndef DIFFKV_H
+#define DIFFKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Host struct.  Thresholds: high if mean score > alpha_h/N, low if in
+ * [alpha_l/N, alpha_h/N], pruned below alpha_l/N ("Approach"; "KV
+ * compression policy").  With lo_enabled = 0: high iff >= alpha_l/N.
+ * Valid: head_dim in {64,128}; 1 <= gqa_group <= 16; hi_page_tokens = 16;
+ * lo_page_tokens = 32; max_seq_len >= 1; window >= 0 (>= 2 for STEP);
+ * 0 <= alpha_l <= alpha_h when lo_enabled. */
+typedef struct {
+  int32_t head_dim;       /* d */
+  int32_t num_kv_heads;   /* H */
+  int32_t gqa_group;      /* G: q head j reads KV head j / G */
+  int32_t hi_page_tokens; /* T_h = 16 */
+  int32_t lo_page_tokens; /* T_l = 32 */
+  int32_t max_seq_len;    /* S_max; table row length L = ceil(S_max/16) + 1 */
+  int32_t window;         /* W: the most recent W tokens stay high precision */
+  int32_t lo_enabled;     /* 0: high / prune only */
+  float alpha_h, alpha_l;
+} diffkv_config;
+
+/* Host struct describing caller-owned device buffers of one page pool
+ * ("Memory management": unified pages, circular free page list). */
+typedef struct {
+  void* pages;        /* [num_pages * page_bytes] unified pages */
+  int32_t* free_list; /* [num_pages] circular list of page ids */
+  uint64_t* ptr;      /* [2]: allocation counter, reclamation counter; list
+                         index = counter mod num_pages, free = ptr[1]-ptr[0] */
+  uint32_t* status;   /* [1] sticky DIFFKV_ST_* bits */
+  int64_t num_pages;  /* 1 <= num_pages < 2^31 */
+  int32_t page_bytes; /* must equal diffkv_page_bytes(cfg) */
+} diffkv_pool;
+
+enum { DIFFKV_OK = 0, DIFFKV_E_INVALID = 1, DIFFKV_E_WORKSPACE = 2, DIFFKV_E_HIP = 3 };
+enum { DIFFKV_ST_POOL_EXHAUSTED = 1u, DIFFKV_ST_TABLE_OVERFLOW = 2u, DIFFKV_ST_BAD_STATE = 4u };
+enum { DIFFKV_PROMPT = 0, DIFFKV_STEP = 1, DIFFKV_RELEASE = 2, DIFFKV_ATTN = 3, DIFFKV_ATTN_SCORES = 4 };
+
+/* Bytes of one unified page (six segments, "Memory management"): 3584 at
+ * d = 128, 2048 at d = 64; -1 for an invalid config. */
+int32_t diffkv_page_bytes(const diffkv_config* cfg);
+
+/* Entries per page-table row, ceil(max_seq_len / 16) + 1; -1 if invalid. */
+int32_t diffkv_table_len(const diffkv_config* cfg);
+
+/* Device scratch needed by one call of `op` (DIFFKV_PROMPT / STEP / RELEASE
+ * for diffkv_compact, DIFFKV_ATTN or DIFFKV_ATTN_SCORES for
+ * diffkv_decode_attn without / with update_scores) on `batch` requests with
+ * `total_tokens` = sum of prompt lengths (PROMPT only).  0 on invalid input.
+ * Compaction workspaces need no initialization.  An attention workspace must
+ * be zero-filled once before its first use; every diffkv_decode_attn call
+ * leaves its split counters at zero again, so it must not be shared with
+ * diffkv_compact.  Calls that share one workspace must not overlap. */
+size_t diffkv_workspace_bytes(const diffkv_config* cfg, int32_t op, int32_t batch,
+                              int64_t total_tokens);
+
+/* Fills free_list with 0..num_pages-1, ptr = {0, num_pages}, status = 0. */
+int diffkv_pool_init(const diffkv_config* cfg, const diffkv_pool* pool, void* stream);
+
+/* Resets `batch` requests to empty: page_table [batch, H, L] = -1,
+ * tier_state [batch, H, 4] = 0. */
+int diffkv_state_init(const diffkv_config* cfg, int32_t batch, int32_t* page_table,
+                      int32_t* tier_state, void* stream);
+
+/* Token classification ("Approach"; "KV compression policy", prompt phase).
+ *  cu_seqlens  int64 [batch+1], cu[0] = 0, non-decreasing; N_r = cu[r+1]-cu[r]
+ *  scores      fp32 [H, cu[batch]]: per token its mean received attention
+ *  tiers       uint8 [H, cu[batch]] out: 2 high, 1 low, 0 pruned.  The last
+ *              W tokens of each request are high; otherwise s*N_r is compared
+ *              with alpha_h and alpha_l exactly (fp64, no division).
+ *  tier_counts int32 [batch, H, 2] out: (high count, low count). */
+int diffkv_classify(const diffkv_config* cfg, int32_t batch, int64_t total_tokens,
+                    const int64_t* cu_seqlens, const float* scores, uint8_t* tiers,
+                    int32_t* tier_counts, void* stream);
+
+/* KV compaction ("Memory management": parallel KV compaction, planning per
+ * head plus a prefix sum over the circular free page list; bidirectional
+ * page table; Fig 6 prompt workflow; generation workflow; "Implementation":
+ * called after K/V are computed, before attention).
+ *
+ * page_table int32 [batch, H, L]: high page ids from the left (index 0 up),
+ *            low page ids from the right (index L-1 down), -1 elsewhere.
+ * tier_state int32 [batch, H, 4]: (high tokens, low tokens, high pages,
+ *            low pages) per unit.
+ * Inside a tier, slot s of a unit lives in page table[s/16] (high) or
+ * table[L-1-s/32] (low) at in-page index s mod 16 (32).
+ *
+ * mode DIFFKV_PROMPT: admits requests with N_r > 0 (others untouched; their
+ *   rows must be empty).  Uses cu_seqlens, k/v fp16 [cu[batch], H, d]
+ *   (token-major), scores (mean per token, [H, total]) and tiers from
+ *   diffkv_classify.  Per unit: a conservative block of ceil(N/16) pages
+ *   from the allocation pointer (units in order); high pages take the block
+ *   from the left, low pages from the right; the middle is reclaimed at the
+ *   reclamation pointer (units in order, ascending block index); a unit
+ *   that needs one page more than its block takes it after the frees as its
+ *   innermost low page.  Tokens are quantized per vector (min/max
+ *   asymmetric, fp16 scale/zero; "Background") and packed in position
+ *   order; the stored score is mean * (N - 1 - pos) (a running sum).
+ * mode DIFFKV_STEP: one generation step for every request with
+ *   seq_len[b] > 0 (seq_len = length before this step's token).  Uses
+ *   k/v fp16 [batch, H, d] (the new token per unit).  The new token enters
+ *   the high tier; the token that leaves the window is classified against
+ *   alpha/(N+1); a least-important token of the receiving tier may be
+ *   requantized to low or pruned ("KV compression policy", generation
+ *   phase).  At most one new page per unit, no reclamation.
+ * mode DIFFKV_RELEASE: for requests with release_mask[b] != 0, appends the
+ *   unit's high pages (left to right) then low pages (right to left) at the
+ *   reclamation pointer, units in order, and resets the rows.
+ * Unused pointer arguments of a mode may be NULL. */
+int diffkv_compact(const diffkv_config* cfg, const diffkv_pool* pool, int32_t mode,
+                   int32_t batch, int64_t total_tokens, const int64_t* cu_seqlens,
+                   const int32_t* seq_len, const uint16_t* k, const uint16_t* v,
+                   const float* scores, const uint8_t* tiers, const uint8_t* release_mask,
+                   int32_t* page_table, int32_t* tier_state, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* Paged decode attention over the compacted cache ("Background": softmax of
+ * q.k/sqrt(d) weighting v; "Implementation": custom attention kernel, high
+ * pages before low pages, sequence split with a merge).
+ *  q       fp16 [batch, H*G, d]; q head j uses KV head j / G
+ *  seq_len int32 [batch]: position of the query token (its K/V was appended
+ *          by the preceding STEP); <= 0 marks an inactive request (output 0)
+ *  out     fp32 [batch, H*G, d]
+ * Keys and values are dequantized on the fly (x = s*code + z per token);
+ * softmax is fp32 online with a split-sequence merge; only retained tokens
+ * take part.  With update_scores != 0 each retained token with position <
+ * seq_len[b] adds the max over the group's q heads of its softmax weight to
+ * its stored score sum (pool->pages are written). */
+int diffkv_decode_attn(const diffkv_config* cfg, const diffkv_pool* pool, int32_t batch,
+                       const uint16_t* q, const int32_t* page_table,
+                       const int32_t* tier_state, const int32_t* seq_len, float* out,
+                       int32_t update_scores, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Number of sequence splits diffkv_decode_attn uses for this config and
+ * batch (host-side heuristic; the workspace size depends on it). */
+int32_t diffkv_attn_splits(const diffkv_config* cfg, int32_t batch);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

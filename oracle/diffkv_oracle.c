@@ -768,9 +768,6 @@ int orc_release(const orc_cfg* c, orc_pool* p, int32_t batch, const uint8_t* mas
     if (!mask[u / H]) continue;
     int32_t ph = state[4 * u + 2], plo = state[4 * u + 3];
     if (ph < 0 || plo < 0 || ph + plo > L) { st |= ORC_ST_BAD_STATE; continue; }
-    const int32_t* row = table + u * L;
-    for (int32_t j = 0; j < ph; j++) if (row[j] < 0 || row[j] >= p->num_pages) st |= ORC_ST_BAD_STATE;
-    for (int32_t j = 0; j < plo; j++) if (row[L - 1 - j] < 0 || row[L - 1 - j] >= p->num_pages) st |= ORC_ST_BAD_STATE;
     total += ph + plo;
   }
   if (!st && (int64_t)(p->ptr[1] - p->ptr[0]) + total > p->num_pages) st |= ORC_ST_BAD_STATE;

@@ -1,0 +1,221 @@
+"""GPU parity of the C-ABI library against the oracle (small and medium sizes
+that span several pages, splits and ragged tails).
+
+Bit-exact: tiers, tier counts, page tables, tier state, free list, both
+pointers, status, and every byte of every live page after compaction.
+Tolerance: attention outputs |gpu - ref| <= 2e-3 + 1e-3 |ref|; score sums
+after the update 1e-5 + 1e-4 |ref| (then re-synced to the oracle's bytes).
+"""
+import numpy as np
+import pytest
+import torch
+
+from tests.invariants import check_pool_invariants
+from tests.parity import (assert_attn_close, assert_scores_close, assert_state_equal, np_,
+                          resync_scores)
+
+pytestmark = pytest.mark.gpu
+
+dev = torch.device("cuda:0")
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dk():
+    import compressed_paged_attention_amd as dk
+    dk.lib()
+    return dk
+
+
+@pytest.fixture(scope="module")
+def orc():
+    import oracle
+    oracle.lib()
+    return oracle
+
+
+def _scores_for(cfg, pr, orc):
+    from workloads import synth
+    if cfg["score"] == "probe":
+        return orc.importance_from_queries(cfg, pr["cu_seqlens"].numpy(), pr["k"].numpy(),
+                                           synth.probe_queries(cfg).numpy())
+    return pr["scores"].numpy()
+
+
+class Pair:
+    """The same cache on the device (library) and on the host (oracle)."""
+
+    def __init__(self, dk, orc, cfg, batch, num_pages, max_total):
+        self.cfg, self.batch = cfg, batch
+        self.g = dk.DiffKVState(cfg, batch, num_pages, max_total_tokens=max_total, device=dev)
+        self.o = orc.State(cfg, batch, num_pages)
+        self.orc = orc
+
+    def prompt(self, cu, k, v, scores, check=True, what="prompt"):
+        tiers_o, counts_o = self.orc.classify(self.cfg, cu, scores)
+        sc = torch.from_numpy(np.ascontiguousarray(scores)).to(dev)
+        cu_d = torch.from_numpy(np.ascontiguousarray(cu, dtype=np.int64)).to(dev)
+        tiers, counts = self.g.classify(cu_d, sc)
+        assert np.array_equal(np_(tiers), tiers_o), f"{what}: tiers differ"
+        assert np.array_equal(np_(counts), counts_o), f"{what}: counts differ"
+        self.o.compact_prompt(cu, k, v, scores, tiers_o)
+        self.g.compact_prompt(cu_d, torch.from_numpy(np.ascontiguousarray(k)).to(dev),
+                              torch.from_numpy(np.ascontiguousarray(v)).to(dev), sc, tiers)
+        torch.cuda.synchronize()
+        if check:
+            assert_state_equal(self.g, self.o, what=what)
+
+    def step(self, seq, kn, vn, what="step"):
+        self.o.compact_step(seq, kn, vn)
+        self.g.compact_step(torch.from_numpy(seq).to(dev), torch.from_numpy(kn).to(dev),
+                            torch.from_numpy(vn).to(dev))
+        torch.cuda.synchronize()
+        assert_state_equal(self.g, self.o, what=what)
+
+    def attend(self, q, seq, update, what="attn"):
+        out_o = self.o.decode_attn(q, seq, update_scores=update)
+        out_g = self.g.decode_attn(torch.from_numpy(q).to(dev), torch.from_numpy(seq).to(dev),
+                                   update_scores=update)
+        torch.cuda.synchronize()
+        err = assert_attn_close(out_g, out_o, what)
+        if update:
+            assert_scores_close(self.g, self.o, what)
+            resync_scores(self.g, self.o)
+        return err
+
+    def release(self, mask, what="release"):
+        self.o.release(mask)
+        self.g.release(torch.from_numpy(np.asarray(mask, np.uint8)).to(dev))
+        torch.cuda.synchronize()
+        assert_state_equal(self.g, self.o, pages=False, what=what)
+
+
+def test_smoke_entry():
+    import __graft_entry__
+    __graft_entry__.smoke()
+
+
+@pytest.mark.parametrize("window", [64, 0])
+def test_tiny_prompt_and_attention(dk, orc, window):
+    from workloads import synth
+    cfg = synth.config("tiny", window=window)
+    pr = synth.make_prompt(cfg)
+    sc = _scores_for(cfg, pr, orc)
+    p = Pair(dk, orc, cfg, 1, 64, int(pr["cu_seqlens"][-1]))
+    _say("tiny prompt, W =", window)
+    p.prompt(pr["cu_seqlens"].numpy(), pr["k"].numpy(), pr["v"].numpy(), sc)
+    check_pool_invariants(orc, p.o)
+    dec = synth.make_decode(cfg, 0)
+    seq = pr["lens"].numpy().astype(np.int32)
+    err = p.attend(dec["q"].numpy(), seq - 1, False, "tiny attn")
+    _say("tiny attention max err", err)
+
+
+def _medium_cfg(name, **over):
+    from workloads import synth
+    c = synth.config(name, **over)
+    return c
+
+
+@pytest.mark.parametrize("d,G,lo", [(128, 4, 1), (64, 5, 1), (128, 7, 0), (128, 8, 1)])
+def test_ragged_prompt_step_attention(dk, orc, d, G, lo):
+    """Ragged batch (tails inside pages, a prompt shorter than the window),
+    prompt compaction, 6 steps with score updates, release of half the batch,
+    re-admission into the freed slots."""
+    from workloads import synth
+    cfg = _medium_cfg("llama3_8b", head_dim=d, gqa_group=G, lo_enabled=lo, num_kv_heads=3,
+                      batch=5, max_seq_len=3000, window=64)
+    lens = torch.tensor([1500, 37, 700, 1201, 64], dtype=torch.int64)
+    pr = synth.make_prompt(cfg, lens=lens)
+    sc = pr["scores"].numpy()
+    cu = pr["cu_seqlens"].numpy()
+    P = int(sum(-(-int(n) // 16) for n in lens) * 3 * 1.1) + 8
+    p = Pair(dk, orc, cfg, 5, P, int(cu[-1]))
+    _say(f"ragged d={d} G={G} lo={lo}: prompt")
+    p.prompt(cu, pr["k"].numpy(), pr["v"].numpy(), sc)
+    check_pool_invariants(orc, p.o)
+    seq = lens.numpy().astype(np.int32)
+    for step in range(6):
+        dec = synth.make_decode(cfg, step)
+        _say("  step", step)
+        p.step(seq, dec["k_new"].numpy(), dec["v_new"].numpy(), f"step {step}")
+        p.attend(dec["q"].numpy(), seq, True, f"attn {step}")
+        seq = seq + 1
+    check_pool_invariants(orc, p.o)
+    mask = np.array([1, 0, 1, 0, 1], np.uint8)
+    p.release(mask)
+    check_pool_invariants(orc, p.o)
+    lens2 = torch.tensor([900, 0, 65, 0, 333], dtype=torch.int64)
+    pr2 = synth.make_prompt(cfg, lens=lens2, salt=7)
+    _say("  re-admit")
+    p.prompt(pr2["cu_seqlens"].numpy(), pr2["k"].numpy(), pr2["v"].numpy(), pr2["scores"].numpy(),
+             what="re-admit")
+    check_pool_invariants(orc, p.o)
+    seq = np.where(mask == 1, lens2.numpy(), seq).astype(np.int32)
+    dec = synth.make_decode(cfg, 99)
+    p.step(seq, dec["k_new"].numpy(), dec["v_new"].numpy(), "step after re-admit")
+    p.attend(dec["q"].numpy(), seq, True, "attn after re-admit")
+
+
+def test_fig6_scaled_on_gpu(dk, orc):
+    """The Fig 6 worked example at 16/32-token pages: pages 5-8 to head A,
+    9-12 to head B, pointer to 13, pages 6, 7, 11 reclaimed."""
+    cfg = dict(head_dim=128, num_kv_heads=2, gqa_group=1, max_seq_len=64, window=0,
+               alpha_h=1.0, alpha_l=0.2)
+    N = 64
+    tiers = np.zeros((2, N), np.uint8)
+    tiers[0, :16] = 2
+    tiers[0, 16:40] = 1
+    tiers[1, 0:17] = 2
+    tiers[1, 30:50] = 1
+    rng = np.random.default_rng(3)
+    k = rng.standard_normal((N, 2, 128)).astype(np.float16).view(np.uint16)
+    v = rng.standard_normal((N, 2, 128)).astype(np.float16).view(np.uint16)
+    scores = rng.random((2, N)).astype(np.float32) / N
+    g = dk.DiffKVState(cfg, 1, 16, max_total_tokens=N, device=dev)
+    g.pool.ptr[0] = 5                                  # pages 0-4 in use
+    g.compact_prompt(torch.tensor([0, N], device=dev), torch.from_numpy(k).to(dev),
+                     torch.from_numpy(v).to(dev), torch.from_numpy(scores).to(dev),
+                     torch.from_numpy(tiers).to(dev))
+    torch.cuda.synchronize()
+    pt = np_(g.page_table)
+    assert pt[0, 0].tolist() == [5, -1, -1, -1, 8]
+    assert pt[0, 1].tolist() == [9, 10, -1, -1, 12]
+    assert np_(g.pool.ptr).tolist() == [13, 19]
+    assert np_(g.pool.free_list)[:3].tolist() == [6, 7, 11]
+
+
+def test_exhaustion_and_overflow_commit_nothing(dk, orc):
+    from workloads import synth
+    cfg = _medium_cfg("llama3_8b", num_kv_heads=2, batch=2, max_seq_len=600)
+    lens = torch.tensor([500, 300], dtype=torch.int64)
+    pr = synth.make_prompt(cfg, lens=lens)
+    cu = pr["cu_seqlens"].numpy()
+    need = 2 * (-(-500 // 16) - 0) + 2 * (-(-300 // 16))
+    p = Pair(dk, orc, cfg, 2, need - 1, int(cu[-1]))
+    before = np_(p.g.page_table).copy()
+    p.prompt(cu, pr["k"].numpy(), pr["v"].numpy(), pr["scores"].numpy(), what="exhausted")
+    assert int(p.o.status[0]) == orc.ST_POOL_EXHAUSTED
+    assert np.array_equal(np_(p.g.page_table), before)
+    # table overflow: a prompt longer than max_seq_len
+    cfg2 = dict(cfg, max_seq_len=400)
+    p2 = Pair(dk, orc, cfg2, 2, 4 * need, int(cu[-1]))
+    p2.prompt(cu, pr["k"].numpy(), pr["v"].numpy(), pr["scores"].numpy(), what="overflow")
+    assert int(p2.o.status[0]) & orc.ST_TABLE_OVERFLOW
+
+
+def test_step_exhaustion(dk, orc):
+    cfg = dict(head_dim=64, num_kv_heads=1, gqa_group=2, max_seq_len=100, window=64,
+               alpha_h=1.0, alpha_l=0.2)
+    rng = np.random.default_rng(5)
+    N = 32
+    k = rng.standard_normal((N, 1, 64)).astype(np.float16).view(np.uint16)
+    sc = np.zeros((1, N), np.float32)
+    p = Pair(dk, orc, cfg, 1, 2, N)
+    p.prompt(np.array([0, N]), k, k, sc)
+    kn = k[:1].reshape(1, 1, 64).copy()
+    p.step(np.array([N], np.int32), kn, kn, "step exhausted")
+    assert int(p.o.status[0]) == orc.ST_POOL_EXHAUSTED

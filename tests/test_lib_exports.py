@@ -1,0 +1,56 @@
+"""The C-ABI library loads and exports every entry point include/diffkv.h
+declares; host-only queries and argument validation work without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "diffkv.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(diffkv_\w+)\s*\(", src)))
+
+
+def test_header_declares_entry_points():
+    names = _declared()
+    for n in ("diffkv_classify", "diffkv_compact", "diffkv_decode_attn", "diffkv_page_bytes",
+              "diffkv_workspace_bytes", "diffkv_pool_init"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    import compressed_paged_attention_amd as dk
+    L = dk.lib()
+    missing = [n for n in _declared() if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_host_queries_and_validation():
+    import compressed_paged_attention_amd as dk
+    from workloads import synth
+    c = synth.config("llama3_8b")
+    assert dk.diffkv_page_bytes(c) == 3584
+    assert dk.diffkv_page_bytes(dict(c, head_dim=64)) == 2048
+    assert dk.diffkv_table_len(c) == -(-c["max_seq_len"] // 16) + 1
+    assert dk.diffkv_page_bytes(dict(c, head_dim=96)) == -1
+    assert dk.diffkv_page_bytes(dict(c, alpha_l=2.0)) == -1
+    assert dk.diffkv_page_bytes(dict(c, hi_page_tokens=8)) == -1
+    for op in (dk.PROMPT, dk.STEP, dk.RELEASE, dk.ATTN, dk.ATTN_SCORES):
+        assert dk.diffkv_workspace_bytes(c, op, 32, 131072) > 0
+    assert dk.diffkv_workspace_bytes(c, 99, 32, 0) == 0
+    assert dk.diffkv_workspace_bytes(c, dk.ATTN_SCORES, 32) > dk.diffkv_workspace_bytes(c, dk.ATTN, 32)
+    assert 1 <= dk.diffkv_attn_splits(c, 32) <= 64
+    # invalid arguments are rejected on the host, before any launch
+    L = dk.lib()
+    bad = dk.make_config(dict(c, head_dim=96))
+    assert L.diffkv_classify(ctypes.byref(bad), 1, 0, None, None, None, None, None) == dk.DIFFKV_E_INVALID
+    good = dk.make_config(c)
+    pool = dk.diffkv_pool(None, None, None, None, 10, 3584)
+    assert L.diffkv_compact(ctypes.byref(good), ctypes.byref(pool), dk.PROMPT, 1, 0, None, None, None, None,
+                            None, None, None, None, None, None, 0, None) == dk.DIFFKV_E_INVALID
+    assert L.diffkv_decode_attn(ctypes.byref(good), ctypes.byref(pool), 1, None, None, None, None, None, 0,
+                                None, 0, None) == dk.DIFFKV_E_INVALID
