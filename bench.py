@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Benchmark of the DiffKV hot path on one MI355X.
+
+Workload: one Llama3-8B-shaped attention layer -- 32 q / 8 KV heads, d = 128,
+batch 32, 4096-token contexts, fp16 K/V ~ N(0,1) with 4 outlier channels x8
+per KV head, importance scores Zipf(1.1) with a per-unit random permutation,
+alpha_h = 1.0, alpha_l = 0.2, W = 64, a pool of 1.25x the conservative need.
+
+A timed step is one decode step of the whole batch on the compacted cache:
+generation-step compaction (diffkv_compact STEP), then decode attention with
+the score update (diffkv_decode_attn, update_scores = 1; one kernel when each
+unit fits one workgroup).  The
+prompt side of the path (classification and prompt compaction) and the
+release are timed in the same run on the same caches and reported beside it.
+Caches rotate over several independent replicas (one per simulated layer) so
+that the 256 MB Infinity Cache cannot hold the working set.
+
+value = batch * steps / (time of the timed region): request-tokens per second
+of complete decode steps.  Every per-call duration comes from HIP events on
+the stream the library launches on.  The roofline object describes the
+attention kernel: algorithmic bytes per launch (codes + metadata of every
+retained token, q, out, table entries, and the 8-byte read-modify-write of
+each retained token's score) over its mean event-timed duration.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "compressed decode-attn tokens/s + compaction µs/step; % peak HBM GB/s"
+PEAK_HBM_GBS = 8000.0
+
+
+def algorithmic_attn_bytes(tier_state, B, H, G, d):
+    """Bytes the attention with score update must move: per retained hi token
+    1.5d + 8 (codes + K/V scale/zero), per lo token 0.75d + 8, q (fp16) and out
+    (fp32) rows, 4 bytes per page-table entry read, and 8 bytes per retained
+    token for the score read-modify-write."""
+    ts = tier_state.reshape(-1, 4).astype("int64")
+    n_hi, n_lo, ph, pl = ts[:, 0].sum(), ts[:, 1].sum(), ts[:, 2].sum(), ts[:, 3].sum()
+    return int(n_hi * (1.5 * d + 8) + n_lo * (0.75 * d + 8) + B * H * G * d * (2 + 4) + 4 * (ph + pl)
+               + 8 * (n_hi + n_lo))
+
+
+def cpu_baseline(cfg, n_req, n_steps):
+    """The oracle timed on this host on a bounded sample of the same workload."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from workloads import synth
+    c = dict(cfg, batch=n_req)
+    lens = synth.seq_lens(c)
+    pr = synth.make_prompt(c, lens=lens)
+    P = synth.pool_pages(c, lens, oracle.page_bytes(c))
+    st = oracle.State(c, n_req, P)
+    cu = pr["cu_seqlens"].numpy()
+    t0 = time.perf_counter()
+    tiers, _ = oracle.classify(c, cu, pr["scores"].numpy())
+    st.compact_prompt(cu, pr["k"].numpy(), pr["v"].numpy(), pr["scores"].numpy(), tiers)
+    t_prompt = time.perf_counter() - t0
+    seq = lens.numpy().astype(np.int32)
+    t0 = time.perf_counter()
+    for s in range(n_steps):
+        dec = synth.make_decode(c, s, batch=n_req)
+        st.compact_step(seq, dec["k_new"].numpy(), dec["v_new"].numpy())
+        st.decode_attn(dec["q"].numpy(), seq, update_scores=True)
+        seq += 1
+    t_step = (time.perf_counter() - t0) / n_steps
+    del torch
+    return dict(value=n_req / t_step, unit="request-tokens/s", cores=1, kind="oracle",
+                sample=f"{n_req} of {cfg['batch']} requests ({n_req * cfg['num_kv_heads']} units, "
+                       f"{cfg['seq'][0]} tokens each): prompt compaction once "
+                       f"({t_prompt:.2f} s, not in value), then {n_steps} decode steps "
+                       f"(step compaction + fp64 attention + score update), "
+                       f"{t_step * 1e3:.1f} ms per step; single thread",
+                cpu=platform.processor() or platform.machine(), prompt_s=t_prompt, step_s=t_step)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--workload", default="llama3_8b")
+    ap.add_argument("--cpu-requests", type=int, default=8)
+    ap.add_argument("--cpu-steps", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only; the path has no cross-GPU exchange "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import compressed_paged_attention_amd as dk
+    from workloads import synth
+
+    dev = torch.device("cuda:0")
+    cfg = synth.config(args.workload)
+    B, H, G, d = cfg["batch"], cfg["num_kv_heads"], cfg["gqa_group"], cfg["head_dim"]
+    R = args.replicas
+    lens = synth.seq_lens(cfg)
+    P = synth.pool_pages(cfg, lens, dk.diffkv_page_bytes(cfg))
+    total = int(lens.sum())
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    # ---- prompt side on every replica: classify + prompt compaction ----
+    reps, seqs0, prompt_ms = [], [], []
+    for r in range(R):
+        pr = synth.make_prompt(cfg, device=dev, salt=r, lens=lens)
+        st = dk.DiffKVState(cfg, B, P, max_total_tokens=total, device=dev)
+        cu = pr["cu_seqlens"].to(dev)
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record()
+        tiers, counts = st.classify(cu, pr["scores"])
+        st.compact_prompt(cu, pr["k"], pr["v"], pr["scores"], tiers)
+        e1.record()
+        torch.cuda.synchronize()
+        prompt_ms.append(e0.elapsed_time(e1))
+        assert int(st.pool.status.item()) == 0, "prompt compaction reported a status bit"
+        reps.append(st)
+        del pr, tiers, counts
+        print(f"[bench] replica {r}: prompt compaction {prompt_ms[-1] * 1e3:.0f} us", file=sys.stderr,
+              flush=True)
+    torch.cuda.empty_cache()
+
+    nsteps = args.warmup + args.steps
+    dec = [synth.make_decode(cfg, s, device=dev) for s in range(nsteps)]
+    seq_per_step = [(lens + s // R).to(torch.int32).to(dev) for s in range(nsteps)]
+    out = torch.empty(B, H * G, d, dtype=torch.float32, device=dev)
+    ts_before = [st.tier_state.cpu().numpy() for st in reps]
+
+    def one_step(s, evs=None):
+        st = reps[s % R]
+        sq = seq_per_step[s]
+        if evs:
+            evs[0].record()
+        st.compact_step(sq, dec[s]["k_new"], dec[s]["v_new"])
+        if evs:
+            evs[1].record()
+        st.decode_attn(dec[s]["q"], sq, update_scores=1, out=out)
+        if evs:
+            evs[2].record()
+
+    for s in range(args.warmup):
+        one_step(s)
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+    evs = [[ev() for _ in range(3)] for _ in range(args.steps)]
+    t0, t1 = ev(), ev()
+    torch.cuda.synchronize()
+    t0.record()
+    for k in range(args.steps):
+        one_step(args.warmup + k, evs[k])
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    comp = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    attn = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    status = [int(st.pool.status.item()) for st in reps]
+    assert all(x == 0 for x in status), f"status bits set during the run: {status}"
+    ts_after = [st.tier_state.cpu().numpy() for st in reps]
+    print("[bench] timed steps done", file=sys.stderr, flush=True)
+
+    # ---- release (every replica) ----
+    rel_ms = []
+    mask = torch.ones(B, dtype=torch.uint8, device=dev)
+    for st in reps:
+        e0, e1 = ev(), ev()
+        e0.record()
+        st.release(mask)
+        e1.record()
+        torch.cuda.synchronize()
+        rel_ms.append(e0.elapsed_time(e1))
+
+    attn_bytes = np.mean([0.5 * (algorithmic_attn_bytes(a, B, H, G, d) + algorithmic_attn_bytes(b, B, H, G, d))
+                          for a, b in zip(ts_before, ts_after)])
+    t_attn_s = float(attn.mean()) * 1e-3
+    achieved = attn_bytes / t_attn_s / 1e9
+    ts = np.stack(ts_before).reshape(-1, 4).astype(np.int64)
+    n_hi, n_lo = int(ts[:, 0].sum()), int(ts[:, 1].sum())
+    ctx = R * total * H
+    step_ms = total_ms / args.steps
+    res = {
+        "metric": METRIC,
+        "value": B * args.steps / (total_ms * 1e-3),
+        "unit": "request-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16-mfma/f32",
+        "data": "synthetic",
+        "config": {"workload": "llama3_8b_layer", "q_heads": H * G, "kv_heads": H, "head_dim": d,
+                   "batch": B, "context": int(lens[0]), "score": "zipf(1.1)", "alpha_h": cfg["alpha_h"],
+                   "alpha_l": cfg["alpha_l"], "window": cfg["window"], "replicas": R,
+                   "pool_pages": P, "page_bytes": dk.diffkv_page_bytes(cfg),
+                   "attn_splits": dk.diffkv_attn_splits(cfg, B)},
+        "attn_tokens_per_s": B / t_attn_s,
+        "attn_us": float(attn.mean()) * 1e3,
+        "attn_us_p10_p90": [float(np.percentile(attn, 10)) * 1e3, float(np.percentile(attn, 90)) * 1e3],
+        "compaction_us_per_step": float(comp.mean()) * 1e3,
+        "compaction_share": float(comp.mean() / (comp.mean() + attn.mean())),
+        "prompt_compaction_us": float(np.mean(prompt_ms)) * 1e3,
+        "prompt_input_GBps": (total * H * d * 4 + total * H * 4) / (np.mean(prompt_ms) * 1e-3) / 1e9,
+        "release_us": float(np.mean(rel_ms)) * 1e3,
+        "retained": {"hi_frac": n_hi / ctx, "lo_frac": n_lo / ctx,
+                     "kv_compression_vs_fp16": (ctx * 4 * d) / (n_hi * (1.5 * d + 16) + n_lo * (0.75 * d + 16))},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                     "kernel": "attn_kernel<128,1>", "bytes_per_launch": int(attn_bytes)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_requests, args.cpu_steps)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

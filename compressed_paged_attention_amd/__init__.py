@@ -72,8 +72,9 @@ def lib() -> ctypes.CDLL:
         L.diffkv_compact.argtypes = [cfgp, poolp, i32, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                      vp, sz, vp]
         L.diffkv_decode_attn.argtypes = [cfgp, poolp, i32, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+        L.diffkv_update_scores.argtypes = [cfgp, poolp, i32, vp, vp, vp, vp, sz, vp]
         for f in ("diffkv_pool_init", "diffkv_state_init", "diffkv_classify", "diffkv_compact",
-                  "diffkv_decode_attn"):
+                  "diffkv_decode_attn", "diffkv_update_scores"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -169,12 +170,20 @@ def diffkv_compact(cfg: dict, pool: Pool, mode: int, batch: int, page_table, tie
 
 
 def diffkv_decode_attn(cfg: dict, pool: Pool, batch: int, q, page_table, tier_state, seq_len, out,
-                       update_scores: bool, workspace, stream=None):
+                       update_scores: int, workspace, stream=None):
     _check(lib().diffkv_decode_attn(ctypes.byref(make_config(cfg)), ctypes.byref(pool.struct()), batch,
                                     _ptr(q), _ptr(page_table), _ptr(tier_state), _ptr(seq_len), _ptr(out),
-                                    1 if update_scores else 0, _ptr(workspace),
+                                    int(update_scores), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(stream)),
            "diffkv_decode_attn")
+
+
+def diffkv_update_scores(cfg: dict, pool: Pool, batch: int, page_table, tier_state, seq_len, workspace,
+                         stream=None):
+    _check(lib().diffkv_update_scores(ctypes.byref(make_config(cfg)), ctypes.byref(pool.struct()), batch,
+                                      _ptr(page_table), _ptr(tier_state), _ptr(seq_len), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream(stream)),
+           "diffkv_update_scores")
 
 
 class DiffKVState:
@@ -222,9 +231,13 @@ class DiffKVState:
         diffkv_compact(self.cfg, self.pool, RELEASE, self.batch, self.page_table, self.tier_state,
                        self.ws_compact, release_mask=mask)
 
-    def decode_attn(self, q, seq_len, update_scores: bool = False, out=None):
+    def decode_attn(self, q, seq_len, update_scores: int = 0, out=None):
         if out is None:
             out = torch.empty(self.batch, self.H * self.G, self.d, dtype=torch.float32, device=q.device)
         diffkv_decode_attn(self.cfg, self.pool, self.batch, q, self.page_table, self.tier_state, seq_len,
-                           out, update_scores, self.ws_attn)
+                           out, int(update_scores), self.ws_attn)
         return out
+
+    def update_scores(self, seq_len):
+        diffkv_update_scores(self.cfg, self.pool, self.batch, self.page_table, self.tier_state, seq_len,
+                             self.ws_attn)

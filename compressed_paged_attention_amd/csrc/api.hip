@@ -141,11 +141,24 @@ int diffkv_decode_attn(const diffkv_config* cfg, const diffkv_pool* pool, int32_
   if (!cfg_ok(cfg) || !pool_ok(cfg, pool) || batch < 0) return DIFFKV_E_INVALID;
   if (batch > 0 && (!q || !page_table || !tier_state || !seq_len || !out)) return DIFFKV_E_INVALID;
   if ((int64_t)batch * cfg->num_kv_heads > 65535) return DIFFKV_E_INVALID;
+  if (update_scores < 0 || update_scores > 2) return DIFFKV_E_INVALID;
   const Cfg c = to_cfg(cfg);
   const size_t need = attn_workspace(c, batch, update_scores != 0);
   if (!workspace || workspace_bytes < need) return DIFFKV_E_WORKSPACE;
-  return rc(launch_attn(c, to_pool(pool), batch, q, page_table, tier_state, seq_len, out, update_scores != 0,
+  return rc(launch_attn(c, to_pool(pool), batch, q, page_table, tier_state, seq_len, out, update_scores,
                         workspace, (hipStream_t)stream));
+}
+
+int diffkv_update_scores(const diffkv_config* cfg, const diffkv_pool* pool, int32_t batch, const int32_t* page_table,
+                         const int32_t* tier_state, const int32_t* seq_len, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  if (!cfg_ok(cfg) || !pool_ok(cfg, pool) || batch < 0) return DIFFKV_E_INVALID;
+  if (batch > 0 && (!page_table || !tier_state || !seq_len)) return DIFFKV_E_INVALID;
+  if ((int64_t)batch * cfg->num_kv_heads > 65535) return DIFFKV_E_INVALID;
+  const Cfg c = to_cfg(cfg);
+  if (!workspace || workspace_bytes < attn_workspace(c, batch, true)) return DIFFKV_E_WORKSPACE;
+  return rc(launch_scores(c, to_pool(pool), batch, page_table, tier_state, seq_len, workspace,
+                          (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -9,9 +9,10 @@
 // tokens of q_j . k^ / sqrt(d) weighting v^, with k^ = s_k c + z_k and
 // v^ = s_v c + z_v dequantized per token on the fly.
 //
-// MI355X mapping.  One workgroup = (unit, split) with 4 waves; wave w takes
-// the split's pages w, w+4, ...  Per page a wave uses 16x16x16 fp16 matrix
-// instructions:
+// MI355X mapping.  One workgroup = (unit, split) with 8 waves; wave w takes
+// the split's pages w, w+8, ... and keeps the next page's loads in flight
+// while it computes the current one.  Per page a wave uses 16x16x16 fp16
+// matrix instructions:
 //   S (16 tokens x 16 heads)   = codes_K (16 x d) * Q^T (d x 16)
 //   O^T (16 dims x 16 heads)  += codes_V^T (16 x 16 tokens) * P'^T (16 x 16)
 // with P' = softmax weight * s_v.  The dequantization is algebraic:
@@ -20,12 +21,14 @@
 // so only integer codes (exact in fp16) enter the matrix units.  P' is split
 // into an fp16 head and an fp16 tail (two instructions) so the PV product
 // keeps ~22 bits.  The S accumulator layout equals the P'^T operand layout,
-// so softmax needs no data movement between the two products.  The codes of
-// K are read token-major (lane: token l%16, a quarter of d); the codes of V
-// are stored in 64 lane chunks so each lane issues one 16-byte load per page.
-// The online softmax is fp32 in base 2.  Splits write (m, l, O) partials; the
-// last workgroup of a unit (device-scope fences + one atomic counter) merges
-// them and resets the counter.
+// so softmax needs no data movement between the two products.  K codes are
+// read token-major (lane: token l%16, a quarter of d); V codes are stored in
+// 64 lane chunks so each lane issues one 16-byte load per page.  The online
+// softmax is fp32 in base 2.  The 8 waves are merged in LDS by a fixed-order
+// tree (deterministic).  With one split per unit the same workgroup then runs
+// the score update over the unit's saved logits; with several splits the
+// partials go through a merge kernel.  No device-scope fence is used: on a
+// multi-XCD part those write back and invalidate whole L2 caches.
 #include "dkv_common.hpp"
 #include "dkv_launch.hpp"
 
@@ -34,6 +37,11 @@ namespace dkv {
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 8;              // waves per attention workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kIdCap = 2048;           // page ids of a split staged in LDS
+constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ inline float4_t mfma16(half4_t a, half4_t b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
@@ -58,31 +66,24 @@ __device__ inline half2_t pair(uint32_t w, int s, uint32_t mask) {
   return unbias(((w >> s) & mask) | 0x64006400u);
 }
 
-constexpr float kLog2e = 1.4426950408889634f;
-
-struct Split {
-  int S;
-};
-
-size_t attn_parts_offset(int64_t U) { return align_up((size_t)U * sizeof(int32_t), 256); }
-
 int attn_splits(const Cfg& c, int batch) {
   const int64_t U = (int64_t)batch * c.H;
   if (U <= 0) return 1;
-  int64_t S = (2048 + U - 1) / U;
-  int64_t cap = c.L / 8;
+  int64_t S = (256 + U - 1) / U;  // about one 8-wave workgroup per compute unit
+  int64_t cap = c.L / 16;
   if (cap < 1) cap = 1;
   if (S > cap) S = cap;
   if (S > 64) S = 64;
+  const int64_t need = (c.L + kIdCap - 1) / kIdCap;  // a split's page ids must fit in LDS
+  if (S < need) S = need;
   if (S < 1) S = 1;
   return (int)S;
 }
 
 struct AttnWs {
-  int32_t* counters;  // [U] zero between calls
-  float* part;        // [U][S][G][D + 2]
-  float* ml;          // [U][G][2] final (max, sum) for the score update
-  float* logits;      // [U][L][32][G] base-2 logits of every retained slot
+  float* part;    // [U][S][G][D + 2] split partials (unnormalized O, max, sum)
+  float* ml;      // [U][G][2] final (max, sum) in base 2, for the score update
+  float* logits;  // [U][L][32][G] base-2 logits of every retained slot
 };
 
 static AttnWs attn_carve(const Cfg& c, int batch, bool scores, void* ws, size_t* bytes) {
@@ -91,15 +92,13 @@ static AttnWs attn_carve(const Cfg& c, int batch, bool scores, void* ws, size_t*
   uint8_t* b = (uint8_t*)ws;
   size_t off = 0;
   AttnWs w;
-  w.counters = (int32_t*)(b + off);
-  off = align_up(off + (size_t)U * sizeof(int32_t), 256);
   w.part = (float*)(b + off);
-  off = align_up(off + (size_t)U * S * c.G * (c.d + 2) * sizeof(float), 256);
+  if (S > 1) off = align_up(off + (size_t)U * S * c.G * (c.d + 2) * sizeof(float), 256);
   w.ml = (float*)(b + off);
   off = align_up(off + (size_t)U * c.G * 2 * sizeof(float), 256);
   w.logits = (float*)(b + off);
   if (scores) off = align_up(off + (size_t)U * c.L * 32 * c.G * sizeof(float), 256);
-  if (bytes) *bytes = off;
+  if (bytes) *bytes = off < 256 ? 256 : off;
   return w;
 }
 
@@ -109,29 +108,203 @@ size_t attn_workspace(const Cfg& c, int batch, bool scores) {
   return n;
 }
 
-// Unit validity, identical in every workgroup of the unit.
-__device__ inline bool unit_ok(int nh, int nl, int ph, int pl, int L, int64_t P, const int32_t* row) {
-  bool ok = nh >= 0 && nl >= 0 && ph == (int)cdiv(nh, kHiTokens) && pl == (int)cdiv(nl, kLoTokens) &&
-            ph + pl <= L;
+__device__ inline bool state_ok(int nh, int nl, int ph, int pl, int L) {
+  return nh >= 0 && nl >= 0 && ph == (int)cdiv(nh, kHiTokens) && pl == (int)cdiv(nl, kLoTokens) && ph + pl <= L;
+}
+
+// Validates every page id of the unit (same answer in every workgroup of the
+// unit) and stages the ids of logical pages [p0, p0 + kIdCap) in LDS.
+__device__ inline bool unit_ids(int ph, int pl, int L, int64_t P, const int32_t* row, int p0, int32_t* ids) {
   int bad = 0;
-  if (ok) {
-    for (int j = threadIdx.x; j < ph + pl; j += blockDim.x) {
-      const int32_t id = j < ph ? row[j] : row[L - 1 - (j - ph)];
-      bad |= (id < 0 || id >= P);
-    }
+  for (int j = threadIdx.x; j < ph + pl; j += blockDim.x) {
+    const int32_t id = j < ph ? row[j] : row[L - 1 - (j - ph)];
+    bad |= (id < 0 || id >= P);
+    if (ids && j >= p0 && j - p0 < kIdCap) ids[j - p0] = id;
   }
-  return __syncthreads_or(bad) == 0 && ok;
+  return __syncthreads_or(bad) == 0;
+}
+
+// Per-lane byte offsets of one page's loads for the two tiers.  A page is
+// read with the same loads whatever its tier (offsets are selected, not
+// branched on), so the next page's loads can stay in flight while the
+// current page is computed.
+struct LaneOffs {
+  int k0[2], k1[2], km0[2], km1[2], vm0[2], vm1[2], v[2], ps0[2], ps1[2];
+};
+
+template <int D>
+__device__ inline LaneOffs lane_offsets(int i, int qg, int lane) {
+  constexpr Seg sh = tier_seg(D, true), sl = tier_seg(D, false);
+  constexpr int KB = D / 8;  // bytes per K load
+  LaneOffs o;
+  o.k0[0] = sh.kc + i * D + qg * (D / 4);  // high: token i, dims qg*D/4 ..
+  o.k1[0] = o.k0[0] + KB;
+  o.k0[1] = sl.kc + i * (D / 2) + qg * (D / 8);  // low: tokens i and i + 16
+  o.k1[1] = sl.kc + (i + 16) * (D / 2) + qg * (D / 8);
+  o.km0[0] = o.km1[0] = sh.km + 16 * qg;
+  o.km0[1] = sl.km + 16 * qg;
+  o.km1[1] = sl.km + 64 + 16 * qg;
+  o.vm0[0] = o.vm1[0] = sh.vm + 16 * qg;
+  o.vm0[1] = sl.vm + 16 * qg;
+  o.vm1[1] = sl.vm + 64 + 16 * qg;
+  o.ps0[0] = o.ps1[0] = sh.ps + 16 * qg;
+  o.ps0[1] = sl.ps + 16 * qg;
+  o.ps1[1] = sl.ps + 64 + 16 * qg;
+  o.v[0] = sh.vc + lane * (D / 8);
+  o.v[1] = sl.vc + lane * (D / 8);
+  return o;
+}
+
+// Registers of one page for one lane.
+template <int D>
+struct PageRegs {
+  static constexpr int KW = D / 32;  // dwords per K load
+  uint32_t k[2 * KW];  // high: 2*KW dwords of token i; low: KW of token i, KW of i+16
+  uint32_t km[8];      // K (scale, zero) words: tokens 4qg.. (low: and 16+4qg..)
+  uint32_t vm[8];      // V (scale, zero) words
+  uint32_t v[KW];      // the lane's V chunk
+  int32_t pos[8];      // positions (only when logits are kept)
+};
+
+template <int N>
+__device__ inline void ldw(uint32_t* r, const uint8_t* p) {
+  if constexpr (N == 4) {
+    const uint4 a = *(const uint4*)p;
+    r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
+  } else {
+    const uint2 a = *(const uint2*)p;
+    r[0] = a.x; r[1] = a.y;
+  }
 }
 
 template <int D, bool SAVE>
-__global__ __launch_bounds__(256) void attn_kernel(int H, int G, int L, int S, int64_t P, int page_bytes,
-                                                   float scale_log2, const uint16_t* __restrict__ q,
-                                                   const int32_t* __restrict__ table,
-                                                   const int32_t* __restrict__ state,
-                                                   const int32_t* __restrict__ seq_len,
-                                                   const uint8_t* __restrict__ pages, float* __restrict__ out,
-                                                   int32_t* counters, float* part, float* ml,
-                                                   float* __restrict__ logits, uint32_t* status) {
+__device__ inline void load_page(PageRegs<D>& R, const uint8_t* pg, bool lo, const LaneOffs& o) {
+  constexpr int KW = PageRegs<D>::KW;
+  ldw<KW>(R.k, pg + (lo ? o.k0[1] : o.k0[0]));
+  ldw<KW>(R.k + KW, pg + (lo ? o.k1[1] : o.k1[0]));
+  ldw<4>(R.km, pg + (lo ? o.km0[1] : o.km0[0]));
+  ldw<4>(R.km + 4, pg + (lo ? o.km1[1] : o.km1[0]));
+  ldw<4>(R.vm, pg + (lo ? o.vm0[1] : o.vm0[0]));
+  ldw<4>(R.vm + 4, pg + (lo ? o.vm1[1] : o.vm1[0]));
+  ldw<KW>(R.v, pg + (lo ? o.v[1] : o.v[0]));
+  if (SAVE) {
+    ldw<4>((uint32_t*)R.pos, pg + (lo ? o.ps0[1] : o.ps0[0]));
+    ldw<4>((uint32_t*)R.pos + 4, pg + (lo ? o.ps1[1] : o.ps1[0]));
+  }
+}
+
+struct Softmax {
+  float m, lsum, zsum;
+};
+
+// One 16-token block: logits (masked), online-softmax update, PV products.
+// `s` holds q.c for tokens first..first+3 of the page; `kmw`/`vmw`/`pos` the
+// words of those tokens; `vpair(nb)` the fp16 V operand of 16-dim block nb;
+// `keep(r, x)` stores the logit of token first + r.
+template <int D, typename VOp, typename Keep>
+__device__ inline void block_update(const float4_t& s, const uint32_t* kmw, const uint32_t* vmw, int first,
+                                    int nval, float sumq, float scale_log2, Softmax& sm, float4_t* acc,
+                                    VOp vpair, Keep keep) {
+  constexpr int NB = D / 16;
+  float x[4];
+  float pm = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 4; r++) {
+    const float ks = h2f((uint16_t)kmw[r]), kz = h2f((uint16_t)(kmw[r] >> 16));
+    x[r] = (ks * s[r] + kz * sumq) * scale_log2;
+    if (first + r >= nval) x[r] = -INFINITY;
+    pm = fmaxf(pm, x[r]);
+  }
+  keep(x);
+  pm = fmaxf(pm, __shfl_xor(pm, 16, 64));
+  pm = fmaxf(pm, __shfl_xor(pm, 32, 64));
+  const float mn = fmaxf(sm.m, pm);
+  const float alpha = __builtin_amdgcn_exp2f(sm.m - mn);
+  float p[4], ps = 0.0f, pz = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 4; r++) {
+    p[r] = __builtin_amdgcn_exp2f(x[r] - mn);
+    ps += p[r];
+    pz += p[r] * h2f((uint16_t)(vmw[r] >> 16));
+  }
+  sm.lsum = sm.lsum * alpha + ps;
+  sm.zsum = sm.zsum * alpha + pz;
+  if (__any(alpha != 1.0f)) {
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) acc[nb] *= alpha;
+  }
+  sm.m = mn;
+  _Float16 ph16[4], pl16[4];
+#pragma unroll
+  for (int r = 0; r < 4; r++) {
+    const float pp = p[r] * h2f((uint16_t)vmw[r]);
+    ph16[r] = (_Float16)pp;
+    pl16[r] = (_Float16)(pp - (float)ph16[r]);
+  }
+  const half4_t bh = {ph16[0], ph16[1], ph16[2], ph16[3]};
+  const half4_t bl = {pl16[0], pl16[1], pl16[2], pl16[3]};
+#pragma unroll
+  for (int nb = 0; nb < NB; nb++) {
+    const half4_t a = vpair(nb);
+    acc[nb] = mfma16(a, bh, acc[nb]);
+    acc[nb] = mfma16(a, bl, acc[nb]);
+  }
+}
+
+// keep(mb, x): stores the 4 logits of 16-token block mb of the page
+template <int D, typename Keep>
+__device__ inline void compute_page(const PageRegs<D>& R, bool hi, int nval, const half4_t* qhi,
+                                    const half4_t* qlo, float sumq, float scale_log2, int qg, Softmax& sm,
+                                    float4_t* acc, Keep keep) {
+  constexpr int NB = D / 16, KW = PageRegs<D>::KW;
+  if (hi) {
+    float4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kb = 0; kb < NB; kb++) s = mfma16(u8x4_to_h4(R.k[kb]), qhi[kb], s);
+    block_update<D>(
+        s, R.km, R.vm, 4 * qg, nval, sumq, scale_log2, sm, acc,
+        [&](int nb) {
+          const uint32_t w = R.v[nb >> 1];
+          const int s0 = 8 * (nb & 1);
+          return cat(pair(w, s0, 0x000F000Fu), pair(w, s0 + 4, 0x000F000Fu));
+        },
+        [&](const float* x) { keep(0, x); });
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < 2; mb++) {
+      float4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kb = 0; kb < NB; kb++) {
+        const uint32_t w = R.k[KW * mb + (kb >> 1)];
+        const int s0 = 8 * (kb & 1);
+        s = mfma16(cat(pair(w, s0, 0x000F000Fu), pair(w, s0 + 4, 0x000F000Fu)), qlo[kb], s);
+      }
+      block_update<D>(
+          s, R.km + 4 * mb, R.vm + 4 * mb, 16 * mb + 4 * qg, nval, sumq, scale_log2, sm, acc,
+          [&](int nb) {
+            const int M = 2 * nb + mb;
+            const int P0 = 2 * M, P1 = 2 * M + 1;
+            return cat(pair(R.v[P0 >> 3], 2 * (P0 & 7), 0x00030003u),
+                       pair(R.v[P1 >> 3], 2 * (P1 & 7), 0x00030003u));
+          },
+          [&](const float* x) { keep(mb, x); });
+    }
+  }
+}
+
+constexpr int kLgCap = 16384;  // logits kept in LDS when a unit needs at most this many
+
+// MODE 0: attention; 1: attention + score update in the same workgroup (one
+// split only); 2: attention keeping logits (score update later).
+template <int D, int MODE>
+__global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int S, int64_t P, int page_bytes,
+                                                        float scale_log2, const uint16_t* __restrict__ q,
+                                                        const int32_t* __restrict__ table,
+                                                        const int32_t* __restrict__ state,
+                                                        const int32_t* __restrict__ seq_len, uint8_t* pages,
+                                                        float* __restrict__ out, float* __restrict__ part,
+                                                        float* __restrict__ ml, float* logits, uint32_t* status) {
+  constexpr bool SAVE = MODE != 0;
   constexpr int NB = D / 16;  // 16-dim blocks (K-steps of QK, N-blocks of PV)
   constexpr int QD = D / 4;   // dims per lane group
   const int split = blockIdx.x;
@@ -143,10 +316,21 @@ __global__ __launch_bounds__(256) void attn_kernel(int H, int G, int L, int S, i
   const int32_t* s4 = state + 4 * u;
   const int nh = s4[0], nl = s4[1], ph = s4[2], pl = s4[3];
   const int N = seq_len[b];
-  const bool ok = unit_ok(nh, nl, ph, pl, L, P, row);
+  const bool sok = state_ok(nh, nl, ph, pl, L);
+  const int TPg = sok ? ph + pl : 0;
+  const int pps = (TPg + S - 1) / S;
+  const int p0 = split * pps;
+  const int p1 = min(TPg, p0 + pps);
+
+  __shared__ int32_t ids[kIdCap];
+  __shared__ float wm[kWaves][16], wl[kWaves][16], sM[16], sL[16];
+  __shared__ float4_t buf[kWaves / 2][16 * D / 4];
+  __shared__ float lg_s[MODE == 1 ? kLgCap : 1];
+
+  const bool ok = sok && pps <= kIdCap && unit_ids(ph, pl, L, P, row, p0, ids);
   float* orow = out + ((int64_t)b * H * G + (int64_t)h * G) * D;
   if (N <= 0 || !ok || nh + nl == 0) {
-    if (split == 0) {
+    if (S == 1 || split == 0) {
       for (int x = tid; x < G * D; x += blockDim.x) orow[x] = 0.0f;
       if (SAVE)
         for (int x = tid; x < G; x += blockDim.x) {
@@ -154,6 +338,13 @@ __global__ __launch_bounds__(256) void attn_kernel(int H, int G, int L, int S, i
           ml[(u * G + x) * 2 + 1] = 0.0f;
         }
       if (N > 0 && !ok && tid == 0) atomicOr(status, kStBadState);
+    }
+    if (S > 1) {
+      float* mp = part + (((int64_t)u * S + split) * G) * (D + 2);
+      for (int x = tid; x < G; x += blockDim.x) {
+        mp[x * (D + 2) + D] = -INFINITY;
+        mp[x * (D + 2) + D + 1] = 0.0f;
+      }
     }
     return;
   }
@@ -192,295 +383,186 @@ __global__ __launch_bounds__(256) void attn_kernel(int H, int G, int L, int S, i
     sumq += __shfl_xor(sumq, 32, 64);
   }
 
-  // ---- page range of this split: hi pages first, then lo pages ----
-  const int TPg = ph + pl;
-  const int pps = (TPg + S - 1) / S;
-  const int p0 = split * pps;
-  const int p1 = min(TPg, p0 + pps);
-  const Seg sh = tier_seg(D, true), sl = tier_seg(D, false);
-
-  float m = -INFINITY, lsum = 0.0f, zsum = 0.0f;
+  Softmax sm{-INFINITY, 0.0f, 0.0f};
   float4_t acc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; nb++) acc[nb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  for (int j = p0 + wid; j < p1; j += 4) {
-    const bool is_hi = j < ph;
-    const int jt = is_hi ? j : j - ph;
-    const int tidx = is_hi ? jt : L - 1 - jt;
-    const uint8_t* pg = pages + (int64_t)row[tidx] * page_bytes;
-    if (is_hi) {
-      const int nval = min(kHiTokens, nh - kHiTokens * jt);
-      // loads
-      uint32_t kw[NB];
-      const uint4* kp = (const uint4*)(pg + sh.kc + i * D + qg * QD);
+  auto table_idx = [&](int j) { return j < ph ? j : L - 1 - (j - ph); };
+  auto valid = [&](int j) {
+    return j < ph ? min(kHiTokens, nh - kHiTokens * j) : min(kLoTokens, nl - kLoTokens * (j - ph));
+  };
+  // logits go to LDS when the whole unit's fit (fused score update), else to
+  // the workspace (indexed by table slot)
+  const bool lg_lds = MODE == 1 && TPg * 32 * G <= kLgCap;
+  const LaneOffs offs = lane_offsets<D>(i, qg, lane);
+
+  // ---- page loop: the next page's loads are in flight during each compute ----
+  if (p0 + wid < p1) {
+    auto fetch = [&](PageRegs<D>& R, int jj) {
+      jj = min(jj, p1 - 1);  // past the end: reload the last page (unused)
+      load_page<D, SAVE>(R, pages + (int64_t)ids[jj - p0] * page_bytes, jj >= ph, offs);
+    };
+    auto run = [&](const PageRegs<D>& R, int j) {
+      const int lgl = j * 32 * G, lgg = table_idx(j) * 32 * G;
+      compute_page<D>(R, j < ph, valid(j), qhi, qlo, sumq, scale_log2, qg, sm, acc,
+                      [&](int mb, const float* x) {
+                        if (!SAVE || i >= G) return;
+                        const int t0 = 16 * mb + 4 * qg;
 #pragma unroll
-      for (int c = 0; c < NB / 4; c++) {
-        const uint4 w = kp[c];
-        kw[4 * c] = w.x;
-        kw[4 * c + 1] = w.y;
-        kw[4 * c + 2] = w.z;
-        kw[4 * c + 3] = w.w;
-      }
-      const uint4 kmeta = *(const uint4*)(pg + sh.km + 16 * qg);
-      const uint4 vmeta = *(const uint4*)(pg + sh.vm + 16 * qg);
-      uint32_t vw[D / 32];
-      if constexpr (D == 128) {
-        const uint4 w = *(const uint4*)(pg + sh.vc + lane * 16);
-        vw[0] = w.x;
-        vw[1] = w.y;
-        vw[2] = w.z;
-        vw[3] = w.w;
-      } else {
-        const uint2 w = *(const uint2*)(pg + sh.vc + lane * 8);
-        vw[0] = w.x;
-        vw[1] = w.y;
-      }
-      // S = codes_K * Q^T
-      float4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int kb = 0; kb < NB; kb++) s = mfma16(u8x4_to_h4(kw[kb]), qhi[kb], s);
-      const uint32_t km[4] = {kmeta.x, kmeta.y, kmeta.z, kmeta.w};
-      const uint32_t vm[4] = {vmeta.x, vmeta.y, vmeta.z, vmeta.w};
-      float x[4];
-      float pm = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        const float ks = h2f((uint16_t)km[r]), kz = h2f((uint16_t)(km[r] >> 16));
-        x[r] = (ks * s[r] + kz * sumq) * scale_log2;
-        if (4 * qg + r >= nval) x[r] = -INFINITY;
-        pm = fmaxf(pm, x[r]);
-      }
-      if (SAVE && i < G) {
-        float* lg = logits + (((int64_t)u * L + tidx) * 32 + 4 * qg) * G + i;
-#pragma unroll
-        for (int r = 0; r < 4; r++) lg[r * G] = x[r];
-      }
-      pm = fmaxf(pm, __shfl_xor(pm, 16, 64));
-      pm = fmaxf(pm, __shfl_xor(pm, 32, 64));
-      const float mn = fmaxf(m, pm);
-      const float alpha = __builtin_amdgcn_exp2f(m - mn);
-      float p[4], ps = 0.0f, pz = 0.0f;
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        p[r] = __builtin_amdgcn_exp2f(x[r] - mn);
-        ps += p[r];
-        pz += p[r] * h2f((uint16_t)(vm[r] >> 16));
-      }
-      lsum = lsum * alpha + ps;
-      zsum = zsum * alpha + pz;
-      if (__any(alpha != 1.0f)) {
-#pragma unroll
-        for (int nb = 0; nb < NB; nb++) acc[nb] *= alpha;
-      }
-      m = mn;
-      _Float16 ph16[4], pl16[4];
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        const float pp = p[r] * h2f((uint16_t)vm[r]);
-        ph16[r] = (_Float16)pp;
-        pl16[r] = (_Float16)(pp - (float)ph16[r]);
-      }
-      const half4_t bh = {ph16[0], ph16[1], ph16[2], ph16[3]};
-      const half4_t bl = {pl16[0], pl16[1], pl16[2], pl16[3]};
-#pragma unroll
-      for (int nb = 0; nb < NB; nb++) {
-        const uint32_t w = vw[nb >> 1];
-        const int s0 = 8 * (nb & 1);
-        const half4_t a = cat(pair(w, s0, 0x000F000Fu), pair(w, s0 + 4, 0x000F000Fu));
-        acc[nb] = mfma16(a, bh, acc[nb]);
-        acc[nb] = mfma16(a, bl, acc[nb]);
-      }
-    } else {
-      const int nval = min(kLoTokens, nl - kLoTokens * jt);
-      uint32_t kw[2][NB / 2];
-#pragma unroll
-      for (int mb = 0; mb < 2; mb++) {
-        if constexpr (D == 128) {
-          const uint4 w = *(const uint4*)(pg + sl.kc + (i + 16 * mb) * (D / 2) + qg * (QD / 2));
-          kw[mb][0] = w.x;
-          kw[mb][1] = w.y;
-          kw[mb][2] = w.z;
-          kw[mb][3] = w.w;
-        } else {
-          const uint2 w = *(const uint2*)(pg + sl.kc + (i + 16 * mb) * (D / 2) + qg * (QD / 2));
-          kw[mb][0] = w.x;
-          kw[mb][1] = w.y;
-        }
-      }
-      uint4 kmeta[2], vmeta[2];
-#pragma unroll
-      for (int mb = 0; mb < 2; mb++) {
-        kmeta[mb] = *(const uint4*)(pg + sl.km + 64 * mb + 16 * qg);
-        vmeta[mb] = *(const uint4*)(pg + sl.vm + 64 * mb + 16 * qg);
-      }
-      uint32_t vw[D / 32];
-      if constexpr (D == 128) {
-        const uint4 w = *(const uint4*)(pg + sl.vc + lane * 16);
-        vw[0] = w.x;
-        vw[1] = w.y;
-        vw[2] = w.z;
-        vw[3] = w.w;
-      } else {
-        const uint2 w = *(const uint2*)(pg + sl.vc + lane * 8);
-        vw[0] = w.x;
-        vw[1] = w.y;
-      }
-      float x[2][4];
-      float pm = -INFINITY;
-#pragma unroll
-      for (int mb = 0; mb < 2; mb++) {
-        float4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int kb = 0; kb < NB; kb++) {
-          const uint32_t w = kw[mb][kb >> 1];
-          const int s0 = 8 * (kb & 1);
-          s = mfma16(cat(pair(w, s0, 0x000F000Fu), pair(w, s0 + 4, 0x000F000Fu)), qlo[kb], s);
-        }
-        const uint32_t km[4] = {kmeta[mb].x, kmeta[mb].y, kmeta[mb].z, kmeta[mb].w};
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-          const float ks = h2f((uint16_t)km[r]), kz = h2f((uint16_t)(km[r] >> 16));
-          float xv = (ks * s[r] + kz * sumq) * scale_log2;
-          if (16 * mb + 4 * qg + r >= nval) xv = -INFINITY;
-          x[mb][r] = xv;
-          pm = fmaxf(pm, xv);
-        }
-      }
-      if (SAVE && i < G) {
-#pragma unroll
-        for (int mb = 0; mb < 2; mb++) {
-          float* lg = logits + (((int64_t)u * L + tidx) * 32 + 16 * mb + 4 * qg) * G + i;
-#pragma unroll
-          for (int r = 0; r < 4; r++) lg[r * G] = x[mb][r];
-        }
-      }
-      pm = fmaxf(pm, __shfl_xor(pm, 16, 64));
-      pm = fmaxf(pm, __shfl_xor(pm, 32, 64));
-      const float mn = fmaxf(m, pm);
-      const float alpha = __builtin_amdgcn_exp2f(m - mn);
-      float p[2][4], ps = 0.0f, pz = 0.0f;
-#pragma unroll
-      for (int mb = 0; mb < 2; mb++) {
-        const uint32_t vm[4] = {vmeta[mb].x, vmeta[mb].y, vmeta[mb].z, vmeta[mb].w};
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-          p[mb][r] = __builtin_amdgcn_exp2f(x[mb][r] - mn);
-          ps += p[mb][r];
-          pz += p[mb][r] * h2f((uint16_t)(vm[r] >> 16));
-        }
-      }
-      lsum = lsum * alpha + ps;
-      zsum = zsum * alpha + pz;
-      if (__any(alpha != 1.0f)) {
-#pragma unroll
-        for (int nb = 0; nb < NB; nb++) acc[nb] *= alpha;
-      }
-      m = mn;
-#pragma unroll
-      for (int ks = 0; ks < 2; ks++) {
-        const uint32_t vm[4] = {vmeta[ks].x, vmeta[ks].y, vmeta[ks].z, vmeta[ks].w};
-        _Float16 ph16[4], pl16[4];
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-          const float pp = p[ks][r] * h2f((uint16_t)vm[r]);
-          ph16[r] = (_Float16)pp;
-          pl16[r] = (_Float16)(pp - (float)ph16[r]);
-        }
-        const half4_t bh = {ph16[0], ph16[1], ph16[2], ph16[3]};
-        const half4_t bl = {pl16[0], pl16[1], pl16[2], pl16[3]};
-#pragma unroll
-        for (int nb = 0; nb < NB; nb++) {
-          const int M = 2 * nb + ks;
-          const int P0 = 2 * M, P1 = 2 * M + 1;
-          const half4_t a = cat(pair(vw[P0 >> 3], 2 * (P0 & 7), 0x00030003u),
-                                pair(vw[P1 >> 3], 2 * (P1 & 7), 0x00030003u));
-          acc[nb] = mfma16(a, bh, acc[nb]);
-          acc[nb] = mfma16(a, bl, acc[nb]);
-        }
-      }
+                        for (int r = 0; r < 4; r++) {
+                          const float val = R.pos[4 * mb + r] == N ? -INFINITY : x[r];
+                          if (MODE == 1 && lg_lds) lg_s[lgl + (t0 + r) * G + i] = val;
+                          else logits[(int64_t)u * L * 32 * G + lgg + (t0 + r) * G + i] = val;
+                        }
+                      });
+    };
+    PageRegs<D> A, B;
+    int j = p0 + wid;
+    fetch(A, j);
+    while (true) {
+      fetch(B, j + kWaves);
+      run(A, j);
+      j += kWaves;
+      if (j >= p1) break;
+      fetch(A, j + kWaves);
+      run(B, j);
+      j += kWaves;
+      if (j >= p1) break;
     }
   }
 
-  // ---- combine the 4 waves of the workgroup ----
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
-  zsum += __shfl_xor(zsum, 16, 64);
-  zsum += __shfl_xor(zsum, 32, 64);
-  __shared__ float wm[4][16], wl[4][16];
-  __shared__ float wo[4][16][D + 1];
+  // ---- merge the 8 waves: maxima, rescale, fixed-order tree in LDS ----
+  sm.lsum += __shfl_xor(sm.lsum, 16, 64);
+  sm.lsum += __shfl_xor(sm.lsum, 32, 64);
+  sm.zsum += __shfl_xor(sm.zsum, 16, 64);
+  sm.zsum += __shfl_xor(sm.zsum, 32, 64);
   if (qg == 0) {
-    wm[wid][i] = m;
-    wl[wid][i] = lsum;
+    wm[wid][i] = sm.m;
+    wl[wid][i] = sm.lsum;
   }
-#pragma unroll
-  for (int nb = 0; nb < NB; nb++)
-#pragma unroll
-    for (int r = 0; r < 4; r++) wo[wid][i][16 * nb + 4 * qg + r] = acc[nb][r] + zsum;
   __syncthreads();
-  // per (head, dim) combination; the partial of this workgroup
-  float* mypart = part + (((int64_t)u * S + split) * G) * (D + 2);
-  for (int x = tid; x < G * D; x += blockDim.x) {
-    const int g = x / D, dd = x % D;
-    float M = fmaxf(fmaxf(wm[0][g], wm[1][g]), fmaxf(wm[2][g], wm[3][g]));
-    float o = 0.0f, l = 0.0f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < 4; w++) {
-        const float f = __builtin_amdgcn_exp2f(wm[w][g] - M);
-        o += wo[w][g][dd] * f;
-        l += wl[w][g] * f;
-      }
-    }
-    if (S == 1) {
-      orow[x] = o / l;
-      if (SAVE && dd == 0) {
-        ml[(u * G + g) * 2 + 0] = M;
-        ml[(u * G + g) * 2 + 1] = l;
-      }
-    } else {
-      mypart[g * (D + 2) + dd] = o;
-      if (dd == 0) {
-        mypart[g * (D + 2) + D] = M;
-        mypart[g * (D + 2) + D + 1] = l;
-      }
-    }
+  if (tid < 16) {
+    float M = -INFINITY;
+    for (int w = 0; w < kWaves; w++) M = fmaxf(M, wm[w][tid]);
+    float l = 0.0f;
+    if (M != -INFINITY)
+      for (int w = 0; w < kWaves; w++) l += wl[w][tid] * __builtin_amdgcn_exp2f(wm[w][tid] - M);
+    sM[tid] = M;
+    sL[tid] = l;
   }
-  if (S == 1) return;
+  __syncthreads();
+  {
+    const float M = sM[i];
+    const float f = (M == -INFINITY || sm.m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sm.m - M);
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) acc[nb] = (acc[nb] + sm.zsum) * f;
+  }
+  // lane (i, qg), block nb holds dims 16nb + 4qg .. +3 of head i -> float4 slot
+#pragma unroll
+  for (int half = kWaves / 2; half >= 1; half >>= 1) {
+    if (wid >= half && wid < 2 * half) {
+#pragma unroll
+      for (int nb = 0; nb < NB; nb++) buf[wid - half][i * (D / 4) + 4 * nb + qg] = acc[nb];
+    }
+    __syncthreads();
+    if (wid < half) {
+#pragma unroll
+      for (int nb = 0; nb < NB; nb++) acc[nb] += buf[wid][i * (D / 4) + 4 * nb + qg];
+    }
+    __syncthreads();
+  }
 
-  // ---- the last workgroup of the unit merges the split partials ----
-  __shared__ int s_last;
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = atomicAdd(&counters[u], 1) == S - 1;
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const float* up = part + ((int64_t)u * S * G) * (D + 2);
-  for (int x = tid; x < G * D; x += blockDim.x) {
+  if (S == 1) {
+    if (wid == 0 && i < G) {
+      const float inv = sL[i] > 0.0f ? 1.0f / sL[i] : 0.0f;
+#pragma unroll
+      for (int nb = 0; nb < NB; nb++) *(float4_t*)(orow + i * D + 16 * nb + 4 * qg) = acc[nb] * inv;
+    }
+    if (SAVE && tid < G) {
+      ml[(u * G + tid) * 2 + 0] = sM[tid];
+      ml[(u * G + tid) * 2 + 1] = sL[tid];
+    }
+    if (MODE == 1) {
+      // score update: every retained token other than the query's own (its
+      // logit was kept as -inf) adds max over the group of its softmax weight
+      if (tid < 16) sL[tid] = sL[tid] > 0.0f ? 1.0f / sL[tid] : 0.0f;
+      __syncthreads();
+      const Seg sh = tier_seg(D, true), sl = tier_seg(D, false);
+      const float* lgg = logits + (int64_t)u * L * 32 * G;
+      constexpr int kU = 4;
+      for (int x0 = tid; x0 < TPg * 32; x0 += kU * blockDim.x) {
+        float* sc[kU];
+        float old[kU], add[kU];
+#pragma unroll
+        for (int e = 0; e < kU; e++) {
+          const int x = x0 + e * blockDim.x;
+          const int j = x >> 5, t = x & 31;
+          sc[e] = nullptr;
+          add[e] = 0.0f;
+          if (x < TPg * 32 && t < valid(j)) {
+            const float* lg = lg_lds ? lg_s + (j * 32 + t) * G : lgg + (table_idx(j) * 32 + t) * G;
+            float mx = 0.0f;
+            for (int g = 0; g < G; g++) mx = fmaxf(mx, __builtin_amdgcn_exp2f(lg[g] - sM[g]) * sL[g]);
+            add[e] = mx;
+            sc[e] = (float*)(pages + (int64_t)ids[j] * page_bytes + (j < ph ? sh.sc : sl.sc) + 4 * t);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < kU; e++) old[e] = sc[e] ? *sc[e] : 0.0f;
+#pragma unroll
+        for (int e = 0; e < kU; e++)
+          if (sc[e]) *sc[e] = old[e] + add[e];
+      }
+    }
+  } else {
+    float* mp = part + (((int64_t)u * S + split) * G) * (D + 2);
+    if (wid == 0 && i < G) {
+#pragma unroll
+      for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) mp[i * (D + 2) + 16 * nb + 4 * qg + r] = acc[nb][r];
+    }
+    if (tid < G) {
+      mp[tid * (D + 2) + D] = sM[tid];
+      mp[tid * (D + 2) + D + 1] = sL[tid];
+    }
+  }
+}
+
+// Split merge (several workgroups per unit): out = sum_s O_s 2^(m_s - M) /
+// sum_s l_s 2^(m_s - M); also the final (M, L) for the score update.
+template <int D>
+__global__ __launch_bounds__(256) void attn_merge_kernel(int H, int G, int S, const int32_t* __restrict__ seq_len,
+                                                         const float* __restrict__ part, float* __restrict__ out,
+                                                         float* __restrict__ ml, int save) {
+  const int64_t u = blockIdx.x;
+  const int b = (int)(u / H), h = (int)(u % H);
+  if (seq_len[b] <= 0) return;  // the attention kernel already wrote zeros
+  const float* up = part + (u * S * G) * (D + 2);
+  float* orow = out + ((int64_t)b * H * G + (int64_t)h * G) * D;
+  for (int x = threadIdx.x; x < G * D; x += blockDim.x) {
     const int g = x / D, dd = x % D;
     float M = -INFINITY;
-    for (int sp = 0; sp < S; sp++) M = fmaxf(M, __builtin_nontemporal_load(&up[(sp * G + g) * (D + 2) + D]));
+    for (int sp = 0; sp < S; sp++) M = fmaxf(M, up[(sp * G + g) * (D + 2) + D]);
     float o = 0.0f, l = 0.0f;
-    for (int sp = 0; sp < S; sp++) {
-      const float* pp = up + (sp * G + g) * (D + 2);
-      const float ms = __builtin_nontemporal_load(&pp[D]);
-      if (ms == -INFINITY) continue;
-      const float f = __builtin_amdgcn_exp2f(ms - M);
-      o += __builtin_nontemporal_load(&pp[dd]) * f;
-      l += __builtin_nontemporal_load(&pp[D + 1]) * f;
-    }
-    orow[x] = o / l;
-    if (SAVE && dd == 0) {
+    if (M != -INFINITY)
+      for (int sp = 0; sp < S; sp++) {
+        const float* pp = up + (sp * G + g) * (D + 2);
+        if (pp[D] == -INFINITY) continue;
+        const float f = __builtin_amdgcn_exp2f(pp[D] - M);
+        o += pp[dd] * f;
+        l += pp[D + 1] * f;
+      }
+    orow[x] = l > 0.0f ? o / l : 0.0f;
+    if (save && dd == 0) {
       ml[(u * G + g) * 2 + 0] = M;
       ml[(u * G + g) * 2 + 1] = l;
     }
   }
-  if (tid == 0) counters[u] = 0;
 }
 
-// Score update: each retained token other than the query's own adds the max
-// over the group's q heads of its softmax weight to its stored sum.
+// Score update from saved logits (several splits, or a deferred update).
 template <int D>
 __global__ __launch_bounds__(256) void score_kernel(int H, int G, int L, int S, int64_t P, int page_bytes,
                                                     const int32_t* __restrict__ table,
@@ -496,12 +578,13 @@ __global__ __launch_bounds__(256) void score_kernel(int H, int G, int L, int S, 
   const int32_t* s4 = state + 4 * u;
   const int nh = s4[0], nl = s4[1], ph = s4[2], pl = s4[3];
   const int N = seq_len[b];
-  if (N <= 0 || nh + nl == 0) return;
-  if (!unit_ok(nh, nl, ph, pl, L, P, row)) return;
-  __shared__ float sM[16], sL[16];
+  if (N <= 0 || nh + nl == 0 || !state_ok(nh, nl, ph, pl, L)) return;
+  if (!unit_ids(ph, pl, L, P, row, 0, nullptr)) return;
+  __shared__ float sM[16], sI[16];
   if (tid < G) {
     sM[tid] = ml[(u * G + tid) * 2 + 0];
-    sL[tid] = 1.0f / ml[(u * G + tid) * 2 + 1];
+    const float l = ml[(u * G + tid) * 2 + 1];
+    sI[tid] = l > 0.0f ? 1.0f / l : 0.0f;
   }
   __syncthreads();
   const int TPg = ph + pl;
@@ -516,48 +599,68 @@ __global__ __launch_bounds__(256) void score_kernel(int H, int G, int L, int S, 
     const int nval = is_hi ? min(kHiTokens, nh - kHiTokens * jt) : min(kLoTokens, nl - kLoTokens * jt);
     if (t >= nval) continue;
     const int tidx = is_hi ? jt : L - 1 - jt;
-    uint8_t* pg = pages + (int64_t)row[tidx] * page_bytes;
-    const Seg& sg = is_hi ? sh : sl;
-    const int32_t pos = *(const int32_t*)(pg + sg.ps + 4 * t);
-    if (pos >= N) continue;
     const float* lg = logits + (((int64_t)u * L + tidx) * 32 + t) * G;
     float mx = 0.0f;
-    for (int g = 0; g < G; g++) mx = fmaxf(mx, __builtin_amdgcn_exp2f(lg[g] - sM[g]) * sL[g]);
-    float* sc = (float*)(pg + sg.sc + 4 * t);
+    for (int g = 0; g < G; g++) mx = fmaxf(mx, __builtin_amdgcn_exp2f(lg[g] - sM[g]) * sI[g]);
+    float* sc = (float*)(pages + (int64_t)row[tidx] * page_bytes + (is_hi ? sh.sc : sl.sc) + 4 * t);
     *sc = *sc + mx;
   }
 }
 
+hipError_t launch_scores(const Cfg& c, const Pool& p, int batch, const int32_t* table, const int32_t* state,
+                         const int32_t* seq_len, void* ws, hipStream_t s) {
+  const int64_t U = (int64_t)batch * c.H;
+  if (U == 0) return hipSuccess;
+  const int S = attn_splits(c, batch);
+  AttnWs w = attn_carve(c, batch, true, ws, nullptr);
+  const dim3 grid(S, (unsigned)U), block(256);
+  if (c.d == 128)
+    score_kernel<128><<<grid, block, 0, s>>>(c.H, c.G, c.L, S, p.P, p.page_bytes, table, state, seq_len, w.ml,
+                                             w.logits, p.pages);
+  else
+    score_kernel<64><<<grid, block, 0, s>>>(c.H, c.G, c.L, S, p.P, p.page_bytes, table, state, seq_len, w.ml,
+                                            w.logits, p.pages);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn(const Cfg& c, const Pool& p, int batch, const uint16_t* q, const int32_t* table,
-                       const int32_t* state, const int32_t* seq_len, float* out, bool update_scores, void* ws,
+                       const int32_t* state, const int32_t* seq_len, float* out, int mode, void* ws,
                        hipStream_t s) {
   const int64_t U = (int64_t)batch * c.H;
   if (U == 0) return hipSuccess;
   const int S = attn_splits(c, batch);
-  AttnWs w = attn_carve(c, batch, update_scores, ws, nullptr);
+  AttnWs w = attn_carve(c, batch, mode != 0, ws, nullptr);
   const float scale_log2 = (1.0f / sqrtf((float)c.d)) * kLog2e;
-  const dim3 grid(S, (unsigned)U), block(256);
-#define DKV_ATTN(D, SV)                                                                                   \
-  attn_kernel<D, SV><<<grid, block, 0, s>>>(c.H, c.G, c.L, S, p.P, p.page_bytes, scale_log2, q, table, \
-                                            state, seq_len, p.pages, out, w.counters, w.part, w.ml,      \
-                                            w.logits, p.status)
+  const dim3 grid(S, (unsigned)U), block(kThreads);
+  // a single split runs the score update inside the attention workgroup
+  const int kmode = mode == 1 && S > 1 ? 2 : mode;
+#define DKV_ATTN(D, M)                                                                                     \
+  attn_kernel<D, M><<<grid, block, 0, s>>>(c.H, c.G, c.L, S, p.P, p.page_bytes, scale_log2, q, table,   \
+                                           state, seq_len, p.pages, out, w.part, w.ml, w.logits, p.status)
   if (c.d == 128) {
-    if (update_scores) DKV_ATTN(128, true);
-    else DKV_ATTN(128, false);
+    if (kmode == 0) DKV_ATTN(128, 0);
+    else if (kmode == 1) DKV_ATTN(128, 1);
+    else DKV_ATTN(128, 2);
   } else {
-    if (update_scores) DKV_ATTN(64, true);
-    else DKV_ATTN(64, false);
+    if (kmode == 0) DKV_ATTN(64, 0);
+    else if (kmode == 1) DKV_ATTN(64, 1);
+    else DKV_ATTN(64, 2);
   }
 #undef DKV_ATTN
-  if (update_scores) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (S > 1) {
     if (c.d == 128)
-      score_kernel<128><<<grid, block, 0, s>>>(c.H, c.G, c.L, S, p.P, p.page_bytes, table, state, seq_len, w.ml,
-                                               w.logits, p.pages);
+      attn_merge_kernel<128><<<dim3((unsigned)U), dim3(256), 0, s>>>(c.H, c.G, S, seq_len, w.part, out, w.ml,
+                                                                     mode != 0);
     else
-      score_kernel<64><<<grid, block, 0, s>>>(c.H, c.G, c.L, S, p.P, p.page_bytes, table, state, seq_len, w.ml,
-                                              w.logits, p.pages);
+      attn_merge_kernel<64><<<dim3((unsigned)U), dim3(256), 0, s>>>(c.H, c.G, S, seq_len, w.part, out, w.ml,
+                                                                    mode != 0);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (mode == 1) return launch_scores(c, p, batch, table, state, seq_len, ws, s);
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace dkv

@@ -47,9 +47,12 @@ hipError_t launch_release(const Cfg& c, const Pool& p, int batch, const uint8_t*
 // decode attention
 int attn_splits(const Cfg& c, int batch);
 size_t attn_workspace(const Cfg& c, int batch, bool scores);
+// mode 0: attention; 1: attention + score update; 2: attention keeping logits
 hipError_t launch_attn(const Cfg& c, const Pool& p, int batch, const uint16_t* q,
                        const int32_t* table, const int32_t* state, const int32_t* seq_len,
-                       float* out, bool update_scores, void* ws, hipStream_t s);
+                       float* out, int mode, void* ws, hipStream_t s);
+hipError_t launch_scores(const Cfg& c, const Pool& p, int batch, const int32_t* table,
+                         const int32_t* state, const int32_t* seq_len, void* ws, hipStream_t s);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

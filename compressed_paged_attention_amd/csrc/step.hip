@@ -390,8 +390,7 @@ __global__ __launch_bounds__(256) void step_commit_kernel(int H, int L, int64_t 
       else row[L - 1 - pl] = id;
     }
   }
-  __threadfence();
-  __syncthreads();
+  __syncthreads();  // workgroup scope suffices: no device-scope fence (it flushes L2)
   const Seg sh = tier_seg(D, true);
   const int lo_src = R[S_LOSRC];
   if (lo_src >= 0) {
@@ -414,8 +413,7 @@ __global__ __launch_bounds__(256) void step_commit_kernel(int H, int L, int64_t 
     uint8_t* dstp = pages + (int64_t)row[L - 1 - (lo_slot >> 5)] * page_bytes;
     store_token<D>(dstp, false, lo_slot & 31, xk, xv, red, sc, pos);
   }
-  __threadfence();
-  __syncthreads();
+  __syncthreads();  // workgroup scope suffices: no device-scope fence (it flushes L2)
   {
     const int64_t rowi = ((int64_t)b * H + h) * D + tid;
     const float xk = tid < D ? h2f(k_new[rowi]) : 0.0f;

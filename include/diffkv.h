@@ -86,10 +86,10 @@ int32_t diffkv_table_len(const diffkv_config* cfg);
  * for diffkv_compact, DIFFKV_ATTN or DIFFKV_ATTN_SCORES for
  * diffkv_decode_attn without / with update_scores) on `batch` requests with
  * `total_tokens` = sum of prompt lengths (PROMPT only).  0 on invalid input.
- * Compaction workspaces need no initialization.  An attention workspace must
- * be zero-filled once before its first use; every diffkv_decode_attn call
- * leaves its split counters at zero again, so it must not be shared with
- * diffkv_compact.  Calls that share one workspace must not overlap. */
+ * Workspaces need no initialization.  A DIFFKV_ATTN_SCORES workspace carries
+ * the logits from diffkv_decode_attn(update_scores = 2) to
+ * diffkv_update_scores, so nothing else may use it in between.  Calls that
+ * share one workspace must not overlap. */
 size_t diffkv_workspace_bytes(const diffkv_config* cfg, int32_t op, int32_t batch,
                               int64_t total_tokens);
 
@@ -162,14 +162,26 @@ int diffkv_compact(const diffkv_config* cfg, const diffkv_pool* pool, int32_t mo
  *  out     fp32 [batch, H*G, d]
  * Keys and values are dequantized on the fly (x = s*code + z per token);
  * softmax is fp32 online with a split-sequence merge; only retained tokens
- * take part.  With update_scores != 0 each retained token with position <
- * seq_len[b] adds the max over the group's q heads of its softmax weight to
- * its stored score sum (pool->pages are written). */
+ * take part.
+ * update_scores: 0 = attention only; 1 = attention, then the score update
+ * (each retained token with position < seq_len[b] adds the max over the
+ * group's q heads of its softmax weight to its stored score sum; pages are
+ * written); 2 = attention that keeps its logits in `workspace` for a later
+ * diffkv_update_scores call (needs the DIFFKV_ATTN_SCORES workspace size). */
 int diffkv_decode_attn(const diffkv_config* cfg, const diffkv_pool* pool, int32_t batch,
                        const uint16_t* q, const int32_t* page_table,
                        const int32_t* tier_state, const int32_t* seq_len, float* out,
                        int32_t update_scores, void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/* The score update of a preceding diffkv_decode_attn(update_scores = 2) call
+ * with the same arguments and workspace (policy reading of the notes' stored
+ * token scores: a running sum of received attention, max over the group's q
+ * heads).  Writes the score segment of pool->pages. */
+int diffkv_update_scores(const diffkv_config* cfg, const diffkv_pool* pool, int32_t batch,
+                         const int32_t* page_table, const int32_t* tier_state,
+                         const int32_t* seq_len, void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 /* Number of sequence splits diffkv_decode_attn uses for this config and
  * batch (host-side heuristic; the workspace size depends on it). */

@@ -219,3 +219,64 @@ def test_step_exhaustion(dk, orc):
     kn = k[:1].reshape(1, 1, 64).copy()
     p.step(np.array([N], np.int32), kn, kn, "step exhausted")
     assert int(p.o.status[0]) == orc.ST_POOL_EXHAUSTED
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_single_split_fused_scores(dk, orc, mode):
+    """256 units -> one workgroup per unit: attention and score update in one
+    kernel (mode 1), or attention keeping logits + diffkv_update_scores (2)."""
+    from workloads import synth
+    cfg = _medium_cfg("llama3_8b", batch=32, max_seq_len=1200)
+    assert dk.diffkv_attn_splits(cfg, 32) == 1
+    g = torch.Generator().manual_seed(11)
+    lens = torch.randint(40, 900, (32,), generator=g, dtype=torch.int64)
+    pr = synth.make_prompt(cfg, lens=lens)
+    cu = pr["cu_seqlens"].numpy()
+    P = int(sum(-(-int(n) // 16) for n in lens) * 8 * 1.1) + 8
+    p = Pair(dk, orc, cfg, 32, P, int(cu[-1]))
+    _say("single split: prompt")
+    p.prompt(cu, pr["k"].numpy(), pr["v"].numpy(), pr["scores"].numpy())
+    seq = lens.numpy().astype(np.int32)
+    for step in range(3):
+        dec = synth.make_decode(cfg, step)
+        p.step(seq, dec["k_new"].numpy(), dec["v_new"].numpy(), f"step {step}")
+        if mode == 1:
+            p.attend(dec["q"].numpy(), seq, True, f"attn {step}")
+        else:
+            out_o = p.o.decode_attn(dec["q"].numpy(), seq, update_scores=True)
+            sq = torch.from_numpy(seq).to(dev)
+            out_g = p.g.decode_attn(torch.from_numpy(dec["q"].numpy()).to(dev), sq, update_scores=2)
+            p.g.update_scores(sq)
+            torch.cuda.synchronize()
+            assert_attn_close(out_g, out_o, f"attn {step}")
+            assert_scores_close(p.g, p.o, f"scores {step}")
+            resync_scores(p.g, p.o)
+        seq = seq + 1
+
+
+def test_deterministic_replay(dk, orc):
+    """Same inputs twice -> byte-identical state and outputs."""
+    from workloads import synth
+    cfg = _medium_cfg("llama3_8b", num_kv_heads=4, batch=3, max_seq_len=2000)
+    lens = torch.tensor([1800, 333, 1024], dtype=torch.int64)
+    pr = synth.make_prompt(cfg, lens=lens)
+    res = []
+    for _ in range(2):
+        gst = dk.DiffKVState(cfg, 3, 2000, max_total_tokens=int(lens.sum()), device=dev)
+        cu = pr["cu_seqlens"].to(dev)
+        sc = pr["scores"].to(dev)
+        tiers, _ = gst.classify(cu, sc)
+        gst.compact_prompt(cu, pr["k"].to(dev), pr["v"].to(dev), sc, tiers)
+        seq = lens.to(torch.int32).to(dev)
+        outs = []
+        for step in range(3):
+            dec = synth.make_decode(cfg, step)
+            gst.compact_step(seq, dec["k_new"].to(dev), dec["v_new"].to(dev))
+            outs.append(np_(gst.decode_attn(dec["q"].to(dev), seq, update_scores=1)))
+            seq = seq + 1
+        torch.cuda.synchronize()
+        live = sorted({int(x) for x in np_(gst.page_table).ravel() if x >= 0})
+        res.append((np_(gst.page_table), np_(gst.pool.free_list), np_(gst.pool.pages.view(2000, -1))[live],
+                    np.stack(outs)))
+    for a, b in zip(res[0], res[1]):
+        assert np.array_equal(a, b)
