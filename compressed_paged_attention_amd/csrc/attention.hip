@@ -11,20 +11,23 @@
 //
 // MI355X mapping.  One workgroup = (unit, split) with 8 waves; wave w takes
 // the split's pages w, w+8, ... and keeps the next page's loads in flight
-// while it computes the current one.  Per page a wave uses 16x16x16 fp16
+// while it computes the current one.  The first page's loads are issued
+// before anything else; page ids are checked as they are used (a load never
+// leaves the pool; a bad id zeroes the unit's output).  Per page a wave uses 16x16x16 fp16
 // matrix instructions:
 //   S (16 tokens x 16 heads)   = codes_K (16 x d) * Q^T (d x 16)
 //   O^T (16 dims x 16 heads)  += codes_V^T (16 x 16 tokens) * P'^T (16 x 16)
 // with P' = softmax weight * s_v.  The dequantization is algebraic:
 //   q . k^ = s_k (q . c_k) + z_k sum(q)
 //   sum_t p_t v^_t = sum_t (p_t s_v,t) c_t + (sum_t p_t z_v,t) * 1
-// so only integer codes (exact in fp16) enter the matrix units.  P' is split
+// so only integer codes (exact fp16 subnormals) enter the matrix units.  P' is split
 // into an fp16 head and an fp16 tail (two instructions) so the PV product
-// keeps ~22 bits.  The S accumulator layout equals the P'^T operand layout,
+// keeps ~22 bits.  The online softmax rescales lazily (reference max moves
+// by more than 2^4 at a time).  The S accumulator layout equals the P'^T operand layout,
 // so softmax needs no data movement between the two products.  K codes are
 // read token-major (lane: token l%16, a quarter of d); V codes are stored in
 // 64 lane chunks so each lane issues one 16-byte load per page.  The online
-// softmax is fp32 in base 2.  The 8 waves are merged in LDS by a fixed-order
+// softmax is fp32 in base 2.  The waves are merged in LDS by a fixed-order
 // tree (deterministic).  With one split per unit the same workgroup then runs
 // the score update over the unit's saved logits; with several splits the
 // partials go through a merge kernel.  No device-scope fence is used: on a
@@ -40,31 +43,28 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 8;              // waves per attention workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kIdCap = 2048;           // page ids of a split staged in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ inline float4_t mfma16(half4_t a, half4_t b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 
-// two packed fp16 values (1024 + x) -> exact x
-__device__ inline half2_t unbias(uint32_t w) {
-  half2_t h = __builtin_bit_cast(half2_t, w);
-  const half2_t k = {(_Float16)1024.0f, (_Float16)1024.0f};
-  return h - k;
+// Codes enter the matrix units as fp16 subnormals: the 16-bit pattern c is
+// the fp16 value c * 2^-24 (exact), so unpacking is a mask or a byte permute
+// and the 2^24 is restored in fp32 (K: folded into the scale; V: at the
+// merge).  The matrix instruction keeps fp16 subnormal inputs exactly.
+__device__ inline half4_t cat(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(half4_t, (uint64_t)a | ((uint64_t)b << 32));
 }
-__device__ inline half4_t cat(half2_t a, half2_t b) { return half4_t{a.x, a.y, b.x, b.y}; }
-
-// 4 u8 codes of one dword -> 4 fp16 values in order
-__device__ inline half4_t u8x4_to_h4(uint32_t w) {
-  const uint32_t a = (w & 0x000000FFu) | ((w & 0x0000FF00u) << 8) | 0x64006400u;
-  const uint32_t b = ((w & 0x00FF0000u) >> 16) | ((w & 0xFF000000u) >> 8) | 0x64006400u;
-  return cat(unbias(a), unbias(b));
+// 4 u8 codes of one dword -> 4 subnormal fp16 codes in order (byte permutes
+// with zero bytes: selector 0x0C gives 0x00)
+__device__ inline half4_t u8x4(uint32_t w) {
+  return cat(__builtin_amdgcn_perm(0u, w, 0x0C010C00u), __builtin_amdgcn_perm(0u, w, 0x0C030C02u));
 }
-// fields at bit s and s+16 of a dword, `mask` = field mask replicated at 0/16
-__device__ inline half2_t pair(uint32_t w, int s, uint32_t mask) {
-  return unbias(((w >> s) & mask) | 0x64006400u);
-}
+// the fields at bits s and s+16 of a dword -> subnormal fp16 pair
+__device__ inline uint32_t nib2(uint32_t w, int s) { return (w >> s) & 0x000F000Fu; }
+__device__ inline uint32_t crumb2(uint32_t w, int s) { return (w >> s) & 0x00030003u; }
+constexpr float kTwo24 = 16777216.0f;
 
 int attn_splits(const Cfg& c, int batch) {
   const int64_t U = (int64_t)batch * c.H;
@@ -74,8 +74,6 @@ int attn_splits(const Cfg& c, int batch) {
   if (cap < 1) cap = 1;
   if (S > cap) S = cap;
   if (S > 64) S = 64;
-  const int64_t need = (c.L + kIdCap - 1) / kIdCap;  // a split's page ids must fit in LDS
-  if (S < need) S = need;
   if (S < 1) S = 1;
   return (int)S;
 }
@@ -113,49 +111,19 @@ __device__ inline bool state_ok(int nh, int nl, int ph, int pl, int L) {
 }
 
 // Validates every page id of the unit (same answer in every workgroup of the
-// unit) and stages the ids of logical pages [p0, p0 + kIdCap) in LDS.
-__device__ inline bool unit_ids(int ph, int pl, int L, int64_t P, const int32_t* row, int p0, int32_t* ids) {
+// unit; the row is then cache-resident for the page loop's scalar loads).
+__device__ inline bool unit_ids(int ph, int pl, int L, int64_t P, const int32_t* row) {
   int bad = 0;
   for (int j = threadIdx.x; j < ph + pl; j += blockDim.x) {
     const int32_t id = j < ph ? row[j] : row[L - 1 - (j - ph)];
     bad |= (id < 0 || id >= P);
-    if (ids && j >= p0 && j - p0 < kIdCap) ids[j - p0] = id;
   }
   return __syncthreads_or(bad) == 0;
 }
 
-// Per-lane byte offsets of one page's loads for the two tiers.  A page is
-// read with the same loads whatever its tier (offsets are selected, not
-// branched on), so the next page's loads can stay in flight while the
-// current page is computed.
-struct LaneOffs {
-  int k0[2], k1[2], km0[2], km1[2], vm0[2], vm1[2], v[2], ps0[2], ps1[2];
-};
-
-template <int D>
-__device__ inline LaneOffs lane_offsets(int i, int qg, int lane) {
-  constexpr Seg sh = tier_seg(D, true), sl = tier_seg(D, false);
-  constexpr int KB = D / 8;  // bytes per K load
-  LaneOffs o;
-  o.k0[0] = sh.kc + i * D + qg * (D / 4);  // high: token i, dims qg*D/4 ..
-  o.k1[0] = o.k0[0] + KB;
-  o.k0[1] = sl.kc + i * (D / 2) + qg * (D / 8);  // low: tokens i and i + 16
-  o.k1[1] = sl.kc + (i + 16) * (D / 2) + qg * (D / 8);
-  o.km0[0] = o.km1[0] = sh.km + 16 * qg;
-  o.km0[1] = sl.km + 16 * qg;
-  o.km1[1] = sl.km + 64 + 16 * qg;
-  o.vm0[0] = o.vm1[0] = sh.vm + 16 * qg;
-  o.vm0[1] = sl.vm + 16 * qg;
-  o.vm1[1] = sl.vm + 64 + 16 * qg;
-  o.ps0[0] = o.ps1[0] = sh.ps + 16 * qg;
-  o.ps0[1] = sl.ps + 16 * qg;
-  o.ps1[1] = sl.ps + 64 + 16 * qg;
-  o.v[0] = sh.vc + lane * (D / 8);
-  o.v[1] = sl.vc + lane * (D / 8);
-  return o;
-}
-
-// Registers of one page for one lane.
+// Registers of one page for one lane.  A page is read with the same loads
+// whatever its tier (tier offsets are scalar selects, not branches), so the
+// compiler keeps the following pages' loads in flight during a compute.
 template <int D>
 struct PageRegs {
   static constexpr int KW = D / 32;  // dwords per K load
@@ -163,7 +131,6 @@ struct PageRegs {
   uint32_t km[8];      // K (scale, zero) words: tokens 4qg.. (low: and 16+4qg..)
   uint32_t vm[8];      // V (scale, zero) words
   uint32_t v[KW];      // the lane's V chunk
-  int32_t pos[8];      // positions (only when logits are kept)
 };
 
 template <int N>
@@ -177,30 +144,41 @@ __device__ inline void ldw(uint32_t* r, const uint8_t* p) {
   }
 }
 
-template <int D, bool SAVE>
-__device__ inline void load_page(PageRegs<D>& R, const uint8_t* pg, bool lo, const LaneOffs& o) {
+// kb: lane K offset of the high tier (token i, dims qg*D/4); the low tier's
+// is kb/2 (token i) and kb/2 + 16*D/2 (token i + 16).  mq = 16 qg, vl = lane
+// chunk offset.  Metadata segments start at the same offset in both tiers.
+template <int D>
+__device__ inline void load_page(PageRegs<D>& R, const uint8_t* pg, bool lo, int kb, int mq, int vl) {
   constexpr int KW = PageRegs<D>::KW;
-  ldw<KW>(R.k, pg + (lo ? o.k0[1] : o.k0[0]));
-  ldw<KW>(R.k + KW, pg + (lo ? o.k1[1] : o.k1[0]));
-  ldw<4>(R.km, pg + (lo ? o.km0[1] : o.km0[0]));
-  ldw<4>(R.km + 4, pg + (lo ? o.km1[1] : o.km1[0]));
-  ldw<4>(R.vm, pg + (lo ? o.vm0[1] : o.vm0[0]));
-  ldw<4>(R.vm + 4, pg + (lo ? o.vm1[1] : o.vm1[0]));
-  ldw<KW>(R.v, pg + (lo ? o.v[1] : o.v[0]));
-  if (SAVE) {
-    ldw<4>((uint32_t*)R.pos, pg + (lo ? o.ps0[1] : o.ps0[0]));
-    ldw<4>((uint32_t*)R.pos + 4, pg + (lo ? o.ps1[1] : o.ps1[0]));
-  }
+  constexpr Seg sh = tier_seg(D, true), sl = tier_seg(D, false);
+  static_assert(sh.km == sl.km, "K metadata offsets differ between tiers");
+  const int k0 = lo ? (kb >> 1) : kb;
+  const int k1 = lo ? (kb >> 1) + 16 * (D / 2) : kb + 4 * KW;
+  ldw<KW>(R.k, pg + k0);
+  ldw<KW>(R.k + KW, pg + k1);
+  ldw<4>(R.km, pg + sh.km + mq);
+  ldw<4>(R.km + 4, pg + sh.km + mq + (lo ? 64 : 0));
+  const int vm = lo ? sl.vm : sh.vm;
+  ldw<4>(R.vm, pg + vm + mq);
+  ldw<4>(R.vm + 4, pg + vm + mq + (lo ? 64 : 0));
+  ldw<KW>(R.v, pg + (lo ? sl.vc : sh.vc) + vl);
 }
 
 struct Softmax {
-  float m, lsum, zsum;
+  float m, lsum, zsum;  // reference max (base 2), sum of weights, sum of weight * z_v
 };
 
+// The reference max moves only when a block's max exceeds it by more than
+// kLazy (base 2), so weights stay <= 2^kLazy and the accumulators are
+// rescaled rarely.  P' = p s_v is carried at 2^-kLazy so its fp16 head can
+// never overflow (|P'| 2^-kLazy <= s_v); the scale is restored at the merge.
+constexpr float kLazy = 4.0f;
+constexpr float kPScale = 1.0f / 16.0f;  // 2^-kLazy
+
 // One 16-token block: logits (masked), online-softmax update, PV products.
-// `s` holds q.c for tokens first..first+3 of the page; `kmw`/`vmw`/`pos` the
-// words of those tokens; `vpair(nb)` the fp16 V operand of 16-dim block nb;
-// `keep(r, x)` stores the logit of token first + r.
+// `s` holds q.c * 2^-24 for tokens first..first+3 of the page; `kmw`/`vmw`
+// the metadata words of those tokens; `vpair(nb)` the fp16 V operand of
+// 16-dim block nb; `keep(x)` stores the block's logits.
 template <int D, typename VOp, typename Keep>
 __device__ inline void block_update(const float4_t& s, const uint32_t* kmw, const uint32_t* vmw, int first,
                                     int nval, float sumq, float scale_log2, Softmax& sm, float4_t* acc,
@@ -210,7 +188,8 @@ __device__ inline void block_update(const float4_t& s, const uint32_t* kmw, cons
   float pm = -INFINITY;
 #pragma unroll
   for (int r = 0; r < 4; r++) {
-    const float ks = h2f((uint16_t)kmw[r]), kz = h2f((uint16_t)(kmw[r] >> 16));
+    // q.k^ = s_k q.c + z_k sum(q); s holds q.c * 2^-24
+    const float ks = h2f((uint16_t)kmw[r]) * kTwo24, kz = h2f((uint16_t)(kmw[r] >> 16));
     x[r] = (ks * s[r] + kz * sumq) * scale_log2;
     if (first + r >= nval) x[r] = -INFINITY;
     pm = fmaxf(pm, x[r]);
@@ -218,26 +197,23 @@ __device__ inline void block_update(const float4_t& s, const uint32_t* kmw, cons
   keep(x);
   pm = fmaxf(pm, __shfl_xor(pm, 16, 64));
   pm = fmaxf(pm, __shfl_xor(pm, 32, 64));
-  const float mn = fmaxf(sm.m, pm);
-  const float alpha = __builtin_amdgcn_exp2f(sm.m - mn);
-  float p[4], ps = 0.0f, pz = 0.0f;
-#pragma unroll
-  for (int r = 0; r < 4; r++) {
-    p[r] = __builtin_amdgcn_exp2f(x[r] - mn);
-    ps += p[r];
-    pz += p[r] * h2f((uint16_t)(vmw[r] >> 16));
-  }
-  sm.lsum = sm.lsum * alpha + ps;
-  sm.zsum = sm.zsum * alpha + pz;
-  if (__any(alpha != 1.0f)) {
+  if (__any(pm > sm.m + kLazy)) {
+    const float mn = pm > sm.m + kLazy ? pm : sm.m;
+    const float alpha = __builtin_amdgcn_exp2f(sm.m - mn);
+    sm.lsum *= alpha;
+    sm.zsum *= alpha;
 #pragma unroll
     for (int nb = 0; nb < NB; nb++) acc[nb] *= alpha;
+    sm.m = mn;
   }
-  sm.m = mn;
+  float p[4];
   _Float16 ph16[4], pl16[4];
 #pragma unroll
   for (int r = 0; r < 4; r++) {
-    const float pp = p[r] * h2f((uint16_t)vmw[r]);
+    p[r] = __builtin_amdgcn_exp2f(x[r] - sm.m);
+    sm.lsum += p[r];
+    sm.zsum += p[r] * h2f((uint16_t)(vmw[r] >> 16));
+    const float pp = p[r] * h2f((uint16_t)vmw[r]) * kPScale;
     ph16[r] = (_Float16)pp;
     pl16[r] = (_Float16)(pp - (float)ph16[r]);
   }
@@ -253,39 +229,43 @@ __device__ inline void block_update(const float4_t& s, const uint32_t* kmw, cons
 
 // keep(mb, x): stores the 4 logits of 16-token block mb of the page
 template <int D, typename Keep>
-__device__ inline void compute_page(const PageRegs<D>& R, bool hi, int nval, const half4_t* qhi,
-                                    const half4_t* qlo, float sumq, float scale_log2, int qg, Softmax& sm,
-                                    float4_t* acc, Keep keep) {
+__device__ inline void compute_page(const PageRegs<D>& R, bool hi, int nval, const half4_t* qop, float sumq,
+                                    float scale_log2, int qg, Softmax& sm, float4_t* acc, Keep keep) {
   constexpr int NB = D / 16, KW = PageRegs<D>::KW;
   if (hi) {
-    float4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
+    // two accumulators halve the dependent chain of the q.c products
+    float4_t s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = s0;
 #pragma unroll
-    for (int kb = 0; kb < NB; kb++) s = mfma16(u8x4_to_h4(R.k[kb]), qhi[kb], s);
+    for (int kb = 0; kb < NB; kb += 2) {
+      s0 = mfma16(u8x4(R.k[kb]), qop[kb], s0);
+      s1 = mfma16(u8x4(R.k[kb + 1]), qop[kb + 1], s1);
+    }
     block_update<D>(
-        s, R.km, R.vm, 4 * qg, nval, sumq, scale_log2, sm, acc,
+        s0 + s1, R.km, R.vm, 4 * qg, nval, sumq, scale_log2, sm, acc,
         [&](int nb) {
+          // block nb: pairs 2nb (tokens 0, 1) and 2nb + 1 (tokens 2, 3)
           const uint32_t w = R.v[nb >> 1];
-          const int s0 = 8 * (nb & 1);
-          return cat(pair(w, s0, 0x000F000Fu), pair(w, s0 + 4, 0x000F000Fu));
+          const int sft = 8 * (nb & 1);
+          return cat(nib2(w, sft), nib2(w, sft + 4));
         },
         [&](const float* x) { keep(0, x); });
   } else {
 #pragma unroll
     for (int mb = 0; mb < 2; mb++) {
-      float4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
+      float4_t s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = s0;
 #pragma unroll
-      for (int kb = 0; kb < NB; kb++) {
+      for (int kb = 0; kb < NB; kb += 2) {
         const uint32_t w = R.k[KW * mb + (kb >> 1)];
-        const int s0 = 8 * (kb & 1);
-        s = mfma16(cat(pair(w, s0, 0x000F000Fu), pair(w, s0 + 4, 0x000F000Fu)), qlo[kb], s);
+        s0 = mfma16(cat(nib2(w, 0), nib2(w, 4)), qop[kb], s0);
+        s1 = mfma16(cat(nib2(w, 8), nib2(w, 12)), qop[kb + 1], s1);
       }
       block_update<D>(
-          s, R.km + 4 * mb, R.vm + 4 * mb, 16 * mb + 4 * qg, nval, sumq, scale_log2, sm, acc,
+          s0 + s1, R.km + 4 * mb, R.vm + 4 * mb, 16 * mb + 4 * qg, nval, sumq, scale_log2, sm, acc,
           [&](int nb) {
+            // block (nb, mb): pairs P = 2M, 2M + 1 with M = 2nb + mb, in word P / 8
             const int M = 2 * nb + mb;
             const int P0 = 2 * M, P1 = 2 * M + 1;
-            return cat(pair(R.v[P0 >> 3], 2 * (P0 & 7), 0x00030003u),
-                       pair(R.v[P1 >> 3], 2 * (P1 & 7), 0x00030003u));
+            return cat(crumb2(R.v[P0 >> 3], 2 * (P0 & 7)), crumb2(R.v[P1 >> 3], 2 * (P1 & 7)));
           },
           [&](const float* x) { keep(mb, x); });
     }
@@ -310,7 +290,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
   const int split = blockIdx.x;
   const int64_t u = blockIdx.y;
   const int b = (int)(u / H), h = (int)(u % H);
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar loop control
   const int i = lane & 15, qg = lane >> 4;
   const int32_t* row = table + u * L;
   const int32_t* s4 = state + 4 * u;
@@ -322,14 +303,12 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
   const int p0 = split * pps;
   const int p1 = min(TPg, p0 + pps);
 
-  __shared__ int32_t ids[kIdCap];
   __shared__ float wm[kWaves][16], wl[kWaves][16], sM[16], sL[16];
-  __shared__ float4_t buf[kWaves / 2][16 * D / 4];
+  __shared__ float4_t buf[kWaves / 2][16 * D / 4];  // kWaves even
   __shared__ float lg_s[MODE == 1 ? kLgCap : 1];
 
-  const bool ok = sok && pps <= kIdCap && unit_ids(ph, pl, L, P, row, p0, ids);
   float* orow = out + ((int64_t)b * H * G + (int64_t)h * G) * D;
-  if (N <= 0 || !ok || nh + nl == 0) {
+  if (N <= 0 || !sok || nh + nl == 0) {
     if (S == 1 || split == 0) {
       for (int x = tid; x < G * D; x += blockDim.x) orow[x] = 0.0f;
       if (SAVE)
@@ -337,7 +316,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
           ml[(u * G + x) * 2 + 0] = -INFINITY;
           ml[(u * G + x) * 2 + 1] = 0.0f;
         }
-      if (N > 0 && !ok && tid == 0) atomicOr(status, kStBadState);
+      if (N > 0 && !sok && tid == 0) atomicOr(status, kStBadState);
     }
     if (S > 1) {
       float* mp = part + (((int64_t)u * S + split) * G) * (D + 2);
@@ -349,8 +328,27 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
     return;
   }
 
-  // ---- Q operands: lane (i, qg) holds head i, dims qg*QD .. qg*QD+QD-1 ----
-  half4_t qhi[NB], qlo[NB];
+  auto table_idx = [&](int j) { return j < ph ? j : L - 1 - (j - ph); };
+  auto valid = [&](int j) {
+    return j < ph ? min(kHiTokens, nh - kHiTokens * j) : min(kLoTokens, nl - kLoTokens * (j - ph));
+  };
+  const int kbase = i * D + qg * (D / 4), mq = 16 * qg, vl = lane * (D / 8);
+  uint32_t badid = 0;
+  // page ids are checked where they are used; a bad id is clamped into the
+  // pool (the load stays in bounds) and zeroes the unit's result
+  auto fetch = [&](PageRegs<D>& R, int jj) {
+    jj = min(jj, p1 - 1);  // past the end: reload the last page (unused)
+    int32_t id = row[table_idx(jj)];  // uniform index: scalar load
+    badid |= (uint32_t)(id < 0 || id >= P);
+    id = min(max(id, 0), (int32_t)(P - 1));
+    load_page<D>(R, pages + (int64_t)id * page_bytes, jj >= ph, kbase, mq, vl);
+  };
+  PageRegs<D> A, B;
+  const bool busy = p0 + wid < p1;
+  if (busy) fetch(A, p0 + wid);
+
+  // ---- Q operand: lane (i, qg) holds head i, dims qg*QD .. qg*QD+QD-1 ----
+  half4_t qop[NB];
   float sumq = 0.0f;
   {
     uint16_t qv[QD];
@@ -374,11 +372,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
     for (int e = 0; e < QD; e++) sumq += h2f(qv[e]);
     auto H16 = [&](int e) { return __builtin_bit_cast(_Float16, qv[e]); };
 #pragma unroll
-    for (int kb = 0; kb < NB; kb++) {
-      qhi[kb] = half4_t{H16(4 * kb), H16(4 * kb + 1), H16(4 * kb + 2), H16(4 * kb + 3)};
-      const int w = kb >> 1, v = kb & 1, o = 8 * w + 2 * v;
-      qlo[kb] = half4_t{H16(o), H16(o + 4), H16(o + 1), H16(o + 5)};
-    }
+    for (int kb = 0; kb < NB; kb++)
+      qop[kb] = half4_t{H16(4 * kb), H16(4 * kb + 1), H16(4 * kb + 2), H16(4 * kb + 3)};
     sumq += __shfl_xor(sumq, 16, 64);
     sumq += __shfl_xor(sumq, 32, 64);
   }
@@ -388,38 +383,27 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
 #pragma unroll
   for (int nb = 0; nb < NB; nb++) acc[nb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  auto table_idx = [&](int j) { return j < ph ? j : L - 1 - (j - ph); };
-  auto valid = [&](int j) {
-    return j < ph ? min(kHiTokens, nh - kHiTokens * j) : min(kLoTokens, nl - kLoTokens * (j - ph));
-  };
   // logits go to LDS when the whole unit's fit (fused score update), else to
   // the workspace (indexed by table slot)
   const bool lg_lds = MODE == 1 && TPg * 32 * G <= kLgCap;
-  const LaneOffs offs = lane_offsets<D>(i, qg, lane);
 
-  // ---- page loop: the next page's loads are in flight during each compute ----
-  if (p0 + wid < p1) {
-    auto fetch = [&](PageRegs<D>& R, int jj) {
-      jj = min(jj, p1 - 1);  // past the end: reload the last page (unused)
-      load_page<D, SAVE>(R, pages + (int64_t)ids[jj - p0] * page_bytes, jj >= ph, offs);
-    };
+  // ---- page loop: the next page's loads in flight during each compute ----
+  if (busy) {
     auto run = [&](const PageRegs<D>& R, int j) {
       const int lgl = j * 32 * G, lgg = table_idx(j) * 32 * G;
-      compute_page<D>(R, j < ph, valid(j), qhi, qlo, sumq, scale_log2, qg, sm, acc,
-                      [&](int mb, const float* x) {
-                        if (!SAVE || i >= G) return;
-                        const int t0 = 16 * mb + 4 * qg;
+      compute_page<D>(R, j < ph, valid(j), qop, sumq, scale_log2, qg, sm, acc, [&](int mb, const float* x) {
+        if (!SAVE || i >= G) return;
+        const int t0 = 16 * mb + 4 * qg;
+        if (MODE == 1 && lg_lds) {
 #pragma unroll
-                        for (int r = 0; r < 4; r++) {
-                          const float val = R.pos[4 * mb + r] == N ? -INFINITY : x[r];
-                          if (MODE == 1 && lg_lds) lg_s[lgl + (t0 + r) * G + i] = val;
-                          else logits[(int64_t)u * L * 32 * G + lgg + (t0 + r) * G + i] = val;
-                        }
-                      });
+          for (int r = 0; r < 4; r++) lg_s[lgl + (t0 + r) * G + i] = x[r];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; r++) logits[(int64_t)u * L * 32 * G + lgg + (t0 + r) * G + i] = x[r];
+        }
+      });
     };
-    PageRegs<D> A, B;
     int j = p0 + wid;
-    fetch(A, j);
     while (true) {
       fetch(B, j + kWaves);
       run(A, j);
@@ -432,16 +416,21 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
     }
   }
 
-  // ---- merge the 8 waves: maxima, rescale, fixed-order tree in LDS ----
+  // ---- merge the waves: maxima, rescale, fixed-order tree in LDS ----
   sm.lsum += __shfl_xor(sm.lsum, 16, 64);
   sm.lsum += __shfl_xor(sm.lsum, 32, 64);
   sm.zsum += __shfl_xor(sm.zsum, 16, 64);
   sm.zsum += __shfl_xor(sm.zsum, 32, 64);
+  __shared__ uint32_t s_bad;
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  if (badid) s_bad = 1;
   if (qg == 0) {
     wm[wid][i] = sm.m;
     wl[wid][i] = sm.lsum;
   }
   __syncthreads();
+  const bool bad = s_bad != 0;
   if (tid < 16) {
     float M = -INFINITY;
     for (int w = 0; w < kWaves; w++) M = fmaxf(M, wm[w][tid]);
@@ -456,24 +445,35 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
     const float M = sM[i];
     const float f = (M == -INFINITY || sm.m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sm.m - M);
 #pragma unroll
-    for (int nb = 0; nb < NB; nb++) acc[nb] = (acc[nb] + sm.zsum) * f;
+    for (int nb = 0; nb < NB; nb++) acc[nb] = (acc[nb] * (kTwo24 / kPScale) + sm.zsum) * f;
   }
-  // lane (i, qg), block nb holds dims 16nb + 4qg .. +3 of head i -> float4 slot
+  // lane (i, qg), block nb holds dims 16nb + 4qg .. +3 of head i -> float4
+  // slot; waves [half, active) fold into [0, active - half), fixed order
 #pragma unroll
-  for (int half = kWaves / 2; half >= 1; half >>= 1) {
-    if (wid >= half && wid < 2 * half) {
+  for (int active = kWaves; active > 1; active = (active + 1) >> 1) {
+    const int half = (active + 1) >> 1;
+    if (wid >= half && wid < active) {
 #pragma unroll
       for (int nb = 0; nb < NB; nb++) buf[wid - half][i * (D / 4) + 4 * nb + qg] = acc[nb];
     }
     __syncthreads();
-    if (wid < half) {
+    if (wid < active - half) {
 #pragma unroll
       for (int nb = 0; nb < NB; nb++) acc[nb] += buf[wid][i * (D / 4) + 4 * nb + qg];
     }
     __syncthreads();
   }
 
+  if (bad && tid == 0) atomicOr(status, kStBadState);
   if (S == 1) {
+    if (bad) {
+      for (int x = tid; x < G * D; x += blockDim.x) orow[x] = 0.0f;
+      if (SAVE && tid < G) {
+        ml[(u * G + tid) * 2 + 0] = -INFINITY;
+        ml[(u * G + tid) * 2 + 1] = 0.0f;
+      }
+      return;
+    }
     if (wid == 0 && i < G) {
       const float inv = sL[i] > 0.0f ? 1.0f / sL[i] : 0.0f;
 #pragma unroll
@@ -484,8 +484,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
       ml[(u * G + tid) * 2 + 1] = sL[tid];
     }
     if (MODE == 1) {
-      // score update: every retained token other than the query's own (its
-      // logit was kept as -inf) adds max over the group of its softmax weight
+      // score update: every retained token other than the query's own
+      // (position seq_len) adds max over the group of its softmax weight
       if (tid < 16) sL[tid] = sL[tid] > 0.0f ? 1.0f / sL[tid] : 0.0f;
       __syncthreads();
       const Seg sh = tier_seg(D, true), sl = tier_seg(D, false);
@@ -493,6 +493,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
       constexpr int kU = 4;
       for (int x0 = tid; x0 < TPg * 32; x0 += kU * blockDim.x) {
         float* sc[kU];
+        const int32_t* pp[kU];
         float old[kU], add[kU];
 #pragma unroll
         for (int e = 0; e < kU; e++) {
@@ -505,14 +506,20 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
             float mx = 0.0f;
             for (int g = 0; g < G; g++) mx = fmaxf(mx, __builtin_amdgcn_exp2f(lg[g] - sM[g]) * sL[g]);
             add[e] = mx;
-            sc[e] = (float*)(pages + (int64_t)ids[j] * page_bytes + (j < ph ? sh.sc : sl.sc) + 4 * t);
+            const uint8_t* pg = pages + (int64_t)row[table_idx(j)] * page_bytes;
+            sc[e] = (float*)(pg + (j < ph ? sh.sc : sl.sc) + 4 * t);
+            pp[e] = (const int32_t*)(pg + (j < ph ? sh.ps : sl.ps) + 4 * t);
           }
         }
+        int32_t pos[kU];
 #pragma unroll
-        for (int e = 0; e < kU; e++) old[e] = sc[e] ? *sc[e] : 0.0f;
+        for (int e = 0; e < kU; e++) {
+          old[e] = sc[e] ? *sc[e] : 0.0f;
+          pos[e] = sc[e] ? *pp[e] : N;
+        }
 #pragma unroll
         for (int e = 0; e < kU; e++)
-          if (sc[e]) *sc[e] = old[e] + add[e];
+          if (sc[e] && pos[e] < N) *sc[e] = old[e] + add[e];
       }
     }
   } else {
@@ -524,7 +531,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
         for (int r = 0; r < 4; r++) mp[i * (D + 2) + 16 * nb + 4 * qg + r] = acc[nb][r];
     }
     if (tid < G) {
-      mp[tid * (D + 2) + D] = sM[tid];
+      mp[tid * (D + 2) + D] = bad ? NAN : sM[tid];  // NaN marks a bad unit for the merge
       mp[tid * (D + 2) + D + 1] = sL[tid];
     }
   }
@@ -544,9 +551,15 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(int H, int G, int S, co
   for (int x = threadIdx.x; x < G * D; x += blockDim.x) {
     const int g = x / D, dd = x % D;
     float M = -INFINITY;
-    for (int sp = 0; sp < S; sp++) M = fmaxf(M, up[(sp * G + g) * (D + 2) + D]);
+    bool bad = false;
+    for (int sp = 0; sp < S; sp++) {
+      const float ms = up[(sp * G + g) * (D + 2) + D];
+      bad |= ms != ms;
+      M = fmaxf(M, ms);
+    }
     float o = 0.0f, l = 0.0f;
-    if (M != -INFINITY)
+    if (bad) M = -INFINITY;
+    else if (M != -INFINITY)
       for (int sp = 0; sp < S; sp++) {
         const float* pp = up + (sp * G + g) * (D + 2);
         if (pp[D] == -INFINITY) continue;
@@ -579,7 +592,7 @@ __global__ __launch_bounds__(256) void score_kernel(int H, int G, int L, int S, 
   const int nh = s4[0], nl = s4[1], ph = s4[2], pl = s4[3];
   const int N = seq_len[b];
   if (N <= 0 || nh + nl == 0 || !state_ok(nh, nl, ph, pl, L)) return;
-  if (!unit_ids(ph, pl, L, P, row, 0, nullptr)) return;
+  if (!unit_ids(ph, pl, L, P, row)) return;
   __shared__ float sM[16], sI[16];
   if (tid < G) {
     sM[tid] = ml[(u * G + tid) * 2 + 0];
@@ -599,10 +612,12 @@ __global__ __launch_bounds__(256) void score_kernel(int H, int G, int L, int S, 
     const int nval = is_hi ? min(kHiTokens, nh - kHiTokens * jt) : min(kLoTokens, nl - kLoTokens * jt);
     if (t >= nval) continue;
     const int tidx = is_hi ? jt : L - 1 - jt;
+    const uint8_t* pg = pages + (int64_t)row[tidx] * page_bytes;
+    if (*(const int32_t*)(pg + (is_hi ? sh.ps : sl.ps) + 4 * t) >= N) continue;
     const float* lg = logits + (((int64_t)u * L + tidx) * 32 + t) * G;
     float mx = 0.0f;
     for (int g = 0; g < G; g++) mx = fmaxf(mx, __builtin_amdgcn_exp2f(lg[g] - sM[g]) * sI[g]);
-    float* sc = (float*)(pages + (int64_t)row[tidx] * page_bytes + (is_hi ? sh.sc : sl.sc) + 4 * t);
+    float* sc = (float*)(pg + (is_hi ? sh.sc : sl.sc) + 4 * t);
     *sc = *sc + mx;
   }
 }

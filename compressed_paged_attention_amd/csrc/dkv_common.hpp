@@ -7,8 +7,8 @@
 // position -- with a per-precision token count).  Segment order follows the
 // notes; every segment starts on a 16-byte boundary.
 //   high tier: 16 tokens, K 8 bit token-major [16][d], V 4 bit
-//   low tier : 32 tokens, K 4 bit token-major [32][d/2] (dim 2i low nibble),
-//              V 2 bit
+//   low tier : 32 tokens, K 4 bit token-major [32][d/2] (dims 8w..8w+7 in
+//              word w, even dims in the low half-word), V 2 bit
 //   metadata : one 32-bit word per token, fp16 scale in bits 0-15, fp16 zero
 //              in bits 16-31
 //   score    : fp32 running sum of received attention; position: int32
@@ -78,14 +78,17 @@ __host__ __device__ inline void v_field(int d, bool hi, int tok, int j, int& byt
   shift = bit & 7;
 }
 
-// Byte offset and shift of K code (tok, j).
+// Byte offset and shift of K code (tok, j).  4-bit: dim 8w+e of a token is
+// nibble e/2 + 4(e&1) of the token's word w, so one shift-and-mask yields an
+// fp16 pair of consecutive dims.
 __host__ __device__ inline void k_field(int d, bool hi, int tok, int j, int& byte, int& shift) {
   if (hi) {
     byte = tok * d + j;
     shift = 0;
   } else {
-    byte = tok * (d / 2) + (j >> 1);
-    shift = 4 * (j & 1);
+    const int e = j & 7, n = (e >> 1) + 4 * (e & 1);
+    byte = tok * (d / 2) + 4 * (j >> 3) + (n >> 1);
+    shift = 4 * (n & 1);
   }
 }
 

@@ -87,7 +87,9 @@ int32_t orc_page_bytes(const orc_cfg* c) {
 }
 
 /* K codes are token-major: token t's d codes are contiguous.  8-bit codes
- * take one byte each; 4-bit codes pack dims 2i (low nibble) and 2i+1. */
+ * take one byte each.  4-bit codes: dims 8w..8w+7 of a token share 32-bit
+ * word w; dim 8w+e sits in nibble n(e) = e/2 + 4 (e mod 2) (bits 4n..4n+3),
+ * so even dims fill the low half-word and odd dims the high half-word. */
 void orc_k_code_addr(const orc_cfg* c, int32_t tier, int32_t tok, int32_t j,
                      int32_t* byte, int32_t* shift) {
   int32_t seg[7];
@@ -97,8 +99,10 @@ void orc_k_code_addr(const orc_cfg* c, int32_t tier, int32_t tok, int32_t j,
     *byte = seg[0] + tok * d + j;
     *shift = 0;
   } else {
-    *byte = seg[0] + tok * (d / 2) + j / 2;
-    *shift = 4 * (j % 2);
+    int32_t e = j % 8;
+    int32_t n = e / 2 + 4 * (e % 2);
+    *byte = seg[0] + tok * (d / 2) + 4 * (j / 8) + n / 2;
+    *shift = 4 * (n % 2);
   }
 }
 
