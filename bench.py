@@ -49,6 +49,54 @@ def algorithmic_attn_bytes(tier_state, B, H, G, d):
                + 8 * (n_hi + n_lo))
 
 
+KERNEL_SOURCES = ("compressed_paged_attention_amd/csrc/attention.hip",
+                  "compressed_paged_attention_amd/csrc/dkv_common.hpp",
+                  "compressed_paged_attention_amd/csrc/dkv_launch.hpp")
+TRAFFIC_FILE = "profiles/attn_kernel_llama3_8b_traffic.txt"
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), or None
+    when the summary is missing or the kernel sources changed since."""
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            parts = line.split()
+            if len(parts) == 2 and not line.startswith((" ", "#", "|")):
+                kv[parts[0]] = parts[1]
+    if kv.get("source_sha256") != kernel_source_hash() or "traffic_bytes_per_launch" not in kv:
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+def copy_probe(mib):
+    """One elementwise copy of a known size (reads and writes `mib` MiB):
+    the calibration point for the HBM byte counters."""
+    import torch
+    n = mib * (1 << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    del x, y
+    torch.cuda.empty_cache()
+    print(f"[bench] copy probe: {mib} MiB read + {mib} MiB written", file=sys.stderr, flush=True)
+
+
 def cpu_baseline(cfg, n_req, n_steps):
     """The oracle timed on this host on a bounded sample of the same workload."""
     import numpy as np
@@ -94,6 +142,8 @@ def main():
     ap.add_argument("--cpu-requests", type=int, default=8)
     ap.add_argument("--cpu-steps", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one elementwise copy of this size first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only; the path has no cross-GPU exchange "
@@ -107,6 +157,8 @@ def main():
     from workloads import synth
 
     dev = torch.device("cuda:0")
+    if args.copy_probe_mib > 0:
+        copy_probe(args.copy_probe_mib)
     cfg = synth.config(args.workload)
     B, H, G, d = cfg["batch"], cfg["num_kv_heads"], cfg["gqa_group"], cfg["head_dim"]
     R = args.replicas
@@ -224,8 +276,9 @@ def main():
         "retained": {"hi_frac": n_hi / ctx, "lo_frac": n_lo / ctx,
                      "kv_compression_vs_fp16": (ctx * 4 * d) / (n_hi * (1.5 * d + 16) + n_lo * (0.75 * d + 16))},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": None,
-                     "kernel": "attn_kernel<128,1>", "bytes_per_launch": int(attn_bytes)},
+                     "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": measured_traffic() if args.workload == "llama3_8b" else None,
+                     "kernel": "attn_kernel<128, 1, true>", "bytes_per_launch": int(attn_bytes)},
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)

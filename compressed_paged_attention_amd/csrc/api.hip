@@ -2,7 +2,7 @@
 // host-side validation, workspace sizing and kernel launches.
 #include <hip/hip_runtime.h>
 
-#include "../../include/diffkv.h"
+#include "diffkv.h"
 #include "dkv_common.hpp"
 #include "dkv_launch.hpp"
 

@@ -32,6 +32,8 @@
 // the score update over the unit's saved logits; with several splits the
 // partials go through a merge kernel.  No device-scope fence is used: on a
 // multi-XCD part those write back and invalidate whole L2 caches.
+#include <type_traits>
+
 #include "dkv_common.hpp"
 #include "dkv_launch.hpp"
 
@@ -39,6 +41,7 @@ namespace dkv {
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 8;              // waves per attention workgroup
@@ -47,6 +50,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ inline float4_t mfma16(half4_t a, half4_t b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ inline float4_t mfma32(half8_t a, half8_t b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 // Codes enter the matrix units as fp16 subnormals: the 16-bit pattern c is
@@ -60,6 +66,9 @@ __device__ inline half4_t cat(uint32_t a, uint32_t b) {
 // with zero bytes: selector 0x0C gives 0x00)
 __device__ inline half4_t u8x4(uint32_t w) {
   return cat(__builtin_amdgcn_perm(0u, w, 0x0C010C00u), __builtin_amdgcn_perm(0u, w, 0x0C030C02u));
+}
+__device__ inline half8_t cat8(half4_t a, half4_t b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 // the fields at bits s and s+16 of a dword -> subnormal fp16 pair
 __device__ inline uint32_t nib2(uint32_t w, int s) { return (w >> s) & 0x000F000Fu; }
@@ -131,6 +140,8 @@ struct PageRegs {
   uint32_t km[8];      // K (scale, zero) words: tokens 4qg.. (low: and 16+4qg..)
   uint32_t vm[8];      // V (scale, zero) words
   uint32_t v[KW];      // the lane's V chunk
+  uint32_t sp;         // fused score update: lane < 32 score slot lane, else position slot lane - 32
+  int32_t id;          // page id (wave-uniform)
 };
 
 template <int N>
@@ -164,41 +175,76 @@ __device__ inline void load_page(PageRegs<D>& R, const uint8_t* pg, bool lo, int
   ldw<KW>(R.v, pg + (lo ? sl.vc : sh.vc) + vl);
 }
 
+// Score and position words of the page's 32 slots (high pages: slots 16..31
+// are other in-page bytes, never used).
+template <int D>
+__device__ inline void load_page_sp(PageRegs<D>& R, const uint8_t* pg, bool lo, int lane) {
+  constexpr Seg sh = tier_seg(D, true), sl = tier_seg(D, false);
+  const int off = lane < 32 ? (lo ? sl.sc : sh.sc) + 4 * lane : (lo ? sl.ps : sh.ps) + 4 * (lane - 32);
+  R.sp = *(const uint32_t*)(pg + off);
+}
+
 struct Softmax {
-  float m, lsum, zsum;  // reference max (base 2), sum of weights, sum of weight * z_v
+  // reference max (base 2) raised by kLazy, sum of weights, sum of weight * z_v
+  // (both sums carry the factor 2^-kLazy of the weights)
+  float m, lsum, zsum;
 };
 
-// The reference max moves only when a block's max exceeds it by more than
-// kLazy (base 2), so weights stay <= 2^kLazy and the accumulators are
-// rescaled rarely.  P' = p s_v is carried at 2^-kLazy so its fp16 head can
-// never overflow (|P'| 2^-kLazy <= s_v); the scale is restored at the merge.
-constexpr float kLazy = 4.0f;
-constexpr float kPScale = 1.0f / 16.0f;  // 2^-kLazy
+// max over the lanes i, i+16, i+32, i+48 (the four token rows of a head):
+// two lane swaps (rows 0<->1, 2<->3, then halves), no LDS round trip
+__device__ inline float rows_max(float v) {
+  uint32_t u = __float_as_uint(v);
+  auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  u = __float_as_uint(v);
+  auto c = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
 
-// One 16-token block: logits (masked), online-softmax update, PV products.
-// `s` holds q.c * 2^-24 for tokens first..first+3 of the page; `kmw`/`vmw`
-// the metadata words of those tokens; `vpair(nb)` the fp16 V operand of
-// 16-dim block nb; `keep(x)` stores the block's logits.
-template <int D, typename VOp, typename Keep>
+__device__ inline float rows_sum(float v) {
+  uint32_t u = __float_as_uint(v);
+  auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  u = __float_as_uint(v);
+  auto c = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// The reference max moves only when a block's max exceeds it by more than
+// kLazy (base 2), so weights stay <= 2^kLazy.  Weights are formed directly at
+// 2^-kLazy (p' = 2^(x - m - kLazy) <= 1) so the fp16 head of p' s_v can never
+// overflow; every sum carries that factor, which the merge removes exactly.
+constexpr float kLazy = 4.0f;
+
+// One 16-token block: logits (masked on a partial page), online-softmax
+// update, PV products.  `s` holds q.c * 2^-24 for tokens first..first+3 of the
+// page; `kmw`/`vmw` the metadata words of those tokens; `vpair(nb)` the fp16 V
+// operand of 16-dim block nb; `keep(x)` stores the block's logits.
+// c24 = 2^24 scale_log2 (uniform), sq2 = sum(q) scale_log2 (per head).
+// PACK: column i + G carries the fp16 tail of head i's weights (one matrix
+// instruction per block instead of two); `tail` marks those lanes.
+template <int D, bool PACK, typename VOp, typename Keep>
 __device__ inline void block_update(const float4_t& s, const uint32_t* kmw, const uint32_t* vmw, int first,
-                                    int nval, float sumq, float scale_log2, Softmax& sm, float4_t* acc,
-                                    VOp vpair, Keep keep) {
+                                    int nval, bool partial, float sq2, float c24, bool tail, Softmax& sm,
+                                    float4_t* acc, VOp vpair, Keep keep) {
   constexpr int NB = D / 16;
   float x[4];
-  float pm = -INFINITY;
 #pragma unroll
   for (int r = 0; r < 4; r++) {
-    // q.k^ = s_k q.c + z_k sum(q); s holds q.c * 2^-24
-    const float ks = h2f((uint16_t)kmw[r]) * kTwo24, kz = h2f((uint16_t)(kmw[r] >> 16));
-    x[r] = (ks * s[r] + kz * sumq) * scale_log2;
-    if (first + r >= nval) x[r] = -INFINITY;
-    pm = fmaxf(pm, x[r]);
+    // log2e/sqrt(d) (s_k q.c + z_k sum(q)), with s holding q.c * 2^-24
+    const _Float16 ks = __builtin_bit_cast(_Float16, (uint16_t)kmw[r]);
+    const _Float16 kz = __builtin_bit_cast(_Float16, (uint16_t)(kmw[r] >> 16));
+    x[r] = (float)ks * (s[r] * c24) + (float)kz * sq2;
+  }
+  if (partial) {
+#pragma unroll
+    for (int r = 0; r < 4; r++)
+      if (first + r >= nval) x[r] = -INFINITY;
   }
   keep(x);
-  pm = fmaxf(pm, __shfl_xor(pm, 16, 64));
-  pm = fmaxf(pm, __shfl_xor(pm, 32, 64));
-  if (__any(pm > sm.m + kLazy)) {
-    const float mn = pm > sm.m + kLazy ? pm : sm.m;
+  const float pm = rows_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+  if (__any(pm > sm.m)) {
+    const float mn = pm > sm.m ? pm + kLazy : sm.m;
     const float alpha = __builtin_amdgcn_exp2f(sm.m - mn);
     sm.lsum *= alpha;
     sm.zsum *= alpha;
@@ -206,42 +252,52 @@ __device__ inline void block_update(const float4_t& s, const uint32_t* kmw, cons
     for (int nb = 0; nb < NB; nb++) acc[nb] *= alpha;
     sm.m = mn;
   }
-  float p[4];
   _Float16 ph16[4], pl16[4];
 #pragma unroll
   for (int r = 0; r < 4; r++) {
-    p[r] = __builtin_amdgcn_exp2f(x[r] - sm.m);
-    sm.lsum += p[r];
-    sm.zsum += p[r] * h2f((uint16_t)(vmw[r] >> 16));
-    const float pp = p[r] * h2f((uint16_t)vmw[r]) * kPScale;
+    const float p = __builtin_amdgcn_exp2f(x[r] - sm.m);
+    const _Float16 vs = __builtin_bit_cast(_Float16, (uint16_t)vmw[r]);
+    const _Float16 vz = __builtin_bit_cast(_Float16, (uint16_t)(vmw[r] >> 16));
+    sm.lsum += p;
+    sm.zsum += p * (float)vz;
+    const float pp = p * (float)vs;
     ph16[r] = (_Float16)pp;
     pl16[r] = (_Float16)(pp - (float)ph16[r]);
   }
-  const half4_t bh = {ph16[0], ph16[1], ph16[2], ph16[3]};
-  const half4_t bl = {pl16[0], pl16[1], pl16[2], pl16[3]};
+  if constexpr (PACK) {
+    const half4_t bt = tail ? half4_t{pl16[0], pl16[1], pl16[2], pl16[3]}
+                            : half4_t{ph16[0], ph16[1], ph16[2], ph16[3]};
 #pragma unroll
-  for (int nb = 0; nb < NB; nb++) {
-    const half4_t a = vpair(nb);
-    acc[nb] = mfma16(a, bh, acc[nb]);
-    acc[nb] = mfma16(a, bl, acc[nb]);
+    for (int nb = 0; nb < NB; nb++) acc[nb] = mfma16(vpair(nb), bt, acc[nb]);
+  } else {
+    const half4_t bh = {ph16[0], ph16[1], ph16[2], ph16[3]};
+    const half4_t bl = {pl16[0], pl16[1], pl16[2], pl16[3]};
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) {
+      const half4_t a = vpair(nb);
+      acc[nb] = mfma16(a, bh, acc[nb]);
+      acc[nb] = mfma16(a, bl, acc[nb]);
+    }
   }
 }
 
-// keep(mb, x): stores the 4 logits of 16-token block mb of the page
-template <int D, typename Keep>
-__device__ inline void compute_page(const PageRegs<D>& R, bool hi, int nval, const half4_t* qop, float sumq,
-                                    float scale_log2, int qg, Softmax& sm, float4_t* acc, Keep keep) {
-  constexpr int NB = D / 16, KW = PageRegs<D>::KW;
+// keep(mb, x): stores the 4 logits of 16-token block mb of the page.  The
+// q.c products use the K = 32 instruction: lane (i, qg) holds 8 dims of
+// token i per step, the same 8 dims of q as its Q operand.
+template <int D, bool PACK, typename Keep>
+__device__ inline void compute_page(const PageRegs<D>& R, bool hi, int nval, const half8_t* qop, float sq2,
+                                    float c24, bool tail, int qg, Softmax& sm, float4_t* acc, Keep keep) {
+  constexpr int NS = D / 32, KW = PageRegs<D>::KW;
   if (hi) {
     // two accumulators halve the dependent chain of the q.c products
     float4_t s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = s0;
 #pragma unroll
-    for (int kb = 0; kb < NB; kb += 2) {
-      s0 = mfma16(u8x4(R.k[kb]), qop[kb], s0);
-      s1 = mfma16(u8x4(R.k[kb + 1]), qop[kb + 1], s1);
+    for (int ks = 0; ks < NS; ks += 2) {
+      s0 = mfma32(cat8(u8x4(R.k[2 * ks]), u8x4(R.k[2 * ks + 1])), qop[ks], s0);
+      s1 = mfma32(cat8(u8x4(R.k[2 * ks + 2]), u8x4(R.k[2 * ks + 3])), qop[ks + 1], s1);
     }
-    block_update<D>(
-        s0 + s1, R.km, R.vm, 4 * qg, nval, sumq, scale_log2, sm, acc,
+    block_update<D, PACK>(
+        s0 + s1, R.km, R.vm, 4 * qg, nval, nval < kHiTokens, sq2, c24, tail, sm, acc,
         [&](int nb) {
           // block nb: pairs 2nb (tokens 0, 1) and 2nb + 1 (tokens 2, 3)
           const uint32_t w = R.v[nb >> 1];
@@ -254,13 +310,15 @@ __device__ inline void compute_page(const PageRegs<D>& R, bool hi, int nval, con
     for (int mb = 0; mb < 2; mb++) {
       float4_t s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = s0;
 #pragma unroll
-      for (int kb = 0; kb < NB; kb += 2) {
-        const uint32_t w = R.k[KW * mb + (kb >> 1)];
-        s0 = mfma16(cat(nib2(w, 0), nib2(w, 4)), qop[kb], s0);
-        s1 = mfma16(cat(nib2(w, 8), nib2(w, 12)), qop[kb + 1], s1);
+      for (int ks = 0; ks < NS; ks += 2) {
+        // word w: dims 8w .. 8w + 7 as nibble pairs (0, 4), (1, 5), (2, 6), (3, 7)
+        const uint32_t w0 = R.k[KW * mb + ks], w1 = R.k[KW * mb + ks + 1];
+        s0 = mfma32(cat8(cat(nib2(w0, 0), nib2(w0, 4)), cat(nib2(w0, 8), nib2(w0, 12))), qop[ks], s0);
+        s1 = mfma32(cat8(cat(nib2(w1, 0), nib2(w1, 4)), cat(nib2(w1, 8), nib2(w1, 12))), qop[ks + 1], s1);
       }
-      block_update<D>(
-          s0 + s1, R.km + 4 * mb, R.vm + 4 * mb, 16 * mb + 4 * qg, nval, sumq, scale_log2, sm, acc,
+      block_update<D, PACK>(
+          s0 + s1, R.km + 4 * mb, R.vm + 4 * mb, 16 * mb + 4 * qg, nval, nval < 16 * (mb + 1), sq2, c24, tail,
+          sm, acc,
           [&](int nb) {
             // block (nb, mb): pairs P = 2M, 2M + 1 with M = 2nb + mb, in word P / 8
             const int M = 2 * nb + mb;
@@ -272,11 +330,13 @@ __device__ inline void compute_page(const PageRegs<D>& R, bool hi, int nval, con
   }
 }
 
-constexpr int kLgCap = 16384;  // logits kept in LDS when a unit needs at most this many
+// fused score update: a unit's logits, old scores, positions and page ids
+// are kept in LDS when they fit in this many 32-bit words
+constexpr int kLdsWords = 16384;
 
 // MODE 0: attention; 1: attention + score update in the same workgroup (one
 // split only); 2: attention keeping logits (score update later).
-template <int D, int MODE>
+template <int D, int MODE, bool PACK>
 __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int S, int64_t P, int page_bytes,
                                                         float scale_log2, const uint16_t* __restrict__ q,
                                                         const int32_t* __restrict__ table,
@@ -285,7 +345,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
                                                         float* __restrict__ out, float* __restrict__ part,
                                                         float* __restrict__ ml, float* logits, uint32_t* status) {
   constexpr bool SAVE = MODE != 0;
-  constexpr int NB = D / 16;  // 16-dim blocks (K-steps of QK, N-blocks of PV)
+  constexpr int NB = D / 16;  // 16-dim blocks (N-blocks of PV)
+  constexpr int NS = D / 32;  // 32-dim K-steps of QK
   constexpr int QD = D / 4;   // dims per lane group
   const int split = blockIdx.x;
   const int64_t u = blockIdx.y;
@@ -303,9 +364,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
   const int p0 = split * pps;
   const int p1 = min(TPg, p0 + pps);
 
-  __shared__ float wm[kWaves][16], wl[kWaves][16], sM[16], sL[16];
-  __shared__ float4_t buf[kWaves / 2][16 * D / 4];  // kWaves even
-  __shared__ float lg_s[MODE == 1 ? kLgCap : 1];
+  __shared__ float wm[kWaves][16], wl[kWaves][16], sM[16], sL[16], sI[16];
+  __shared__ float4_t buf[kWaves][16 * D / 4];  // every wave's O columns, for the merge
+  // fused score update: [TPg*32*G] logits, [TPg*32] old scores, [TPg*32]
+  // positions, [TPg] page ids
+  __shared__ uint32_t lds_w[MODE == 1 ? kLdsWords : 1];
 
   float* orow = out + ((int64_t)b * H * G + (int64_t)h * G) * D;
   if (N <= 0 || !sok || nh + nl == 0) {
@@ -341,19 +404,25 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
     int32_t id = row[table_idx(jj)];  // uniform index: scalar load
     badid |= (uint32_t)(id < 0 || id >= P);
     id = min(max(id, 0), (int32_t)(P - 1));
-    load_page<D>(R, pages + (int64_t)id * page_bytes, jj >= ph, kbase, mq, vl);
+    R.id = id;
+    const uint8_t* pg = pages + (int64_t)id * page_bytes;
+    load_page<D>(R, pg, jj >= ph, kbase, mq, vl);
+    if (MODE == 1) load_page_sp<D>(R, pg, jj >= ph, lane);
   };
   PageRegs<D> A, B;
   const bool busy = p0 + wid < p1;
   if (busy) fetch(A, p0 + wid);
 
-  // ---- Q operand: lane (i, qg) holds head i, dims qg*QD .. qg*QD+QD-1 ----
-  half4_t qop[NB];
+  // ---- Q operand: lane (i, qg) holds column i's head, dims qg*QD .. +QD-1;
+  // with PACK, columns G .. 2G-1 repeat heads 0 .. G-1 (their tails) ----
+  const int qhead = i < G ? i : (PACK && i < 2 * G ? i - G : -1);
+  const bool tail = PACK && i >= G;
+  half8_t qop[NS];
   float sumq = 0.0f;
   {
     uint16_t qv[QD];
-    if (i < G) {
-      const uint4* src = (const uint4*)(q + ((int64_t)b * H * G + (int64_t)h * G + i) * D + qg * QD);
+    if (qhead >= 0) {
+      const uint4* src = (const uint4*)(q + ((int64_t)b * H * G + (int64_t)h * G + qhead) * D + qg * QD);
 #pragma unroll
       for (int c = 0; c < QD / 8; c++) {
         const uint4 w = src[c];
@@ -372,11 +441,13 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
     for (int e = 0; e < QD; e++) sumq += h2f(qv[e]);
     auto H16 = [&](int e) { return __builtin_bit_cast(_Float16, qv[e]); };
 #pragma unroll
-    for (int kb = 0; kb < NB; kb++)
-      qop[kb] = half4_t{H16(4 * kb), H16(4 * kb + 1), H16(4 * kb + 2), H16(4 * kb + 3)};
+    for (int ks = 0; ks < NS; ks++)
+      qop[ks] = half8_t{H16(8 * ks), H16(8 * ks + 1), H16(8 * ks + 2), H16(8 * ks + 3),
+                        H16(8 * ks + 4), H16(8 * ks + 5), H16(8 * ks + 6), H16(8 * ks + 7)};
     sumq += __shfl_xor(sumq, 16, 64);
     sumq += __shfl_xor(sumq, 32, 64);
   }
+  const float sq2 = sumq * scale_log2, c24 = kTwo24 * scale_log2;
 
   Softmax sm{-INFINITY, 0.0f, 0.0f};
   float4_t acc[NB];
@@ -385,42 +456,64 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
 
   // logits go to LDS when the whole unit's fit (fused score update), else to
   // the workspace (indexed by table slot)
-  const bool lg_lds = MODE == 1 && TPg * 32 * G <= kLgCap;
+  const bool lg_lds = MODE == 1 && TPg * 32 * (G + 2) + TPg <= kLdsWords;
+  float* lg_s = (float*)lds_w;
+  float* osc_s = (float*)lds_w + TPg * 32 * G;
+  int32_t* pos_s = (int32_t*)lds_w + TPg * 32 * (G + 1);
+  int32_t* id_s = (int32_t*)lds_w + TPg * 32 * (G + 2);
 
   // ---- page loop: the next page's loads in flight during each compute ----
-  if (busy) {
+  // Instantiated once per logits destination (LDS or workspace) so that the
+  // per-block stores need no branch.
+  auto page_loop = [&](auto lds_tag) {
+    constexpr bool kLds = decltype(lds_tag)::value;
     auto run = [&](const PageRegs<D>& R, int j) {
-      const int lgl = j * 32 * G, lgg = table_idx(j) * 32 * G;
-      compute_page<D>(R, j < ph, valid(j), qop, sumq, scale_log2, qg, sm, acc, [&](int mb, const float* x) {
+      if (kLds) {
+        if (lane < 32) osc_s[j * 32 + lane] = __uint_as_float(R.sp);
+        else pos_s[j * 32 + lane - 32] = (int32_t)R.sp;
+        if (lane == 0) id_s[j] = R.id;
+      }
+      float* lgp = kLds ? lg_s + j * 32 * G : logits + ((int64_t)u * L + table_idx(j)) * 32 * G;
+      compute_page<D, PACK>(R, j < ph, valid(j), qop, sq2, c24, tail, qg, sm, acc, [&](int mb, const float* x) {
         if (!SAVE || i >= G) return;
         const int t0 = 16 * mb + 4 * qg;
-        if (MODE == 1 && lg_lds) {
 #pragma unroll
-          for (int r = 0; r < 4; r++) lg_s[lgl + (t0 + r) * G + i] = x[r];
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; r++) logits[(int64_t)u * L * 32 * G + lgg + (t0 + r) * G + i] = x[r];
-        }
+        for (int r = 0; r < 4; r++) lgp[(t0 + r) * G + i] = x[r];
       });
     };
+    // n_w pages for this wave; the last one is peeled so that no load is
+    // still in flight when the wave reaches the merge
     int j = p0 + wid;
-    while (true) {
+    const int n_w = (p1 - 1 - j) / kWaves + 1;
+    int k = 1;
+    for (; k + 2 <= n_w; k += 2) {
       fetch(B, j + kWaves);
       run(A, j);
       j += kWaves;
-      if (j >= p1) break;
       fetch(A, j + kWaves);
       run(B, j);
       j += kWaves;
-      if (j >= p1) break;
+    }
+    if (k < n_w) {
+      fetch(B, j + kWaves);
+      run(A, j);
+      run(B, j + kWaves);
+    } else {
+      run(A, j);
+    }
+  };
+  if (busy) {
+    if constexpr (MODE == 1) {
+      if (lg_lds) page_loop(std::true_type{});
+      else page_loop(std::false_type{});
+    } else {
+      page_loop(std::false_type{});
     }
   }
 
-  // ---- merge the waves: maxima, rescale, fixed-order tree in LDS ----
-  sm.lsum += __shfl_xor(sm.lsum, 16, 64);
-  sm.lsum += __shfl_xor(sm.lsum, 32, 64);
-  sm.zsum += __shfl_xor(sm.zsum, 16, 64);
-  sm.zsum += __shfl_xor(sm.zsum, 32, 64);
+  // ---- merge the waves: maxima, rescale, fixed-order sums in LDS ----
+  sm.lsum = rows_sum(sm.lsum);
+  sm.zsum = rows_sum(sm.zsum);
   __shared__ uint32_t s_bad;
   if (tid == 0) s_bad = 0;
   __syncthreads();
@@ -439,30 +532,30 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
       for (int w = 0; w < kWaves; w++) l += wl[w][tid] * __builtin_amdgcn_exp2f(wm[w][tid] - M);
     sM[tid] = M;
     sL[tid] = l;
+    sI[tid] = l > 0.0f ? 1.0f / l : 0.0f;
   }
   __syncthreads();
-  {
+  const int ncol = PACK ? 2 * G : G;  // columns that carry data
+  if (i < ncol) {
+    // O = 2^24 acc + sum(p z_v) (the z_v term once per head: not in tail columns)
     const float M = sM[i];
     const float f = (M == -INFINITY || sm.m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sm.m - M);
+    const float z = tail ? 0.0f : sm.zsum;
+    // lane (i, qg), block nb: dims 16nb + 4qg .. +3 of column i
 #pragma unroll
-    for (int nb = 0; nb < NB; nb++) acc[nb] = (acc[nb] * (kTwo24 / kPScale) + sm.zsum) * f;
+    for (int nb = 0; nb < NB; nb++) buf[wid][i * (D / 4) + 4 * nb + qg] = (acc[nb] * kTwo24 + z) * f;
   }
-  // lane (i, qg), block nb holds dims 16nb + 4qg .. +3 of head i -> float4
-  // slot; waves [half, active) fold into [0, active - half), fixed order
+  __syncthreads();
+  const float* ob = (const float*)&buf[0][0];
+  auto ocol = [&](int x) {  // x = g * D + dim: sum over waves (fixed order) of column g (+ its tail)
+    float o = 0.0f;
 #pragma unroll
-  for (int active = kWaves; active > 1; active = (active + 1) >> 1) {
-    const int half = (active + 1) >> 1;
-    if (wid >= half && wid < active) {
-#pragma unroll
-      for (int nb = 0; nb < NB; nb++) buf[wid - half][i * (D / 4) + 4 * nb + qg] = acc[nb];
+    for (int w = 0; w < kWaves; w++) {
+      o += ob[w * 16 * D + x];
+      if (PACK) o += ob[w * 16 * D + x + G * D];
     }
-    __syncthreads();
-    if (wid < active - half) {
-#pragma unroll
-      for (int nb = 0; nb < NB; nb++) acc[nb] += buf[wid][i * (D / 4) + 4 * nb + qg];
-    }
-    __syncthreads();
-  }
+    return o;
+  };
 
   if (bad && tid == 0) atomicOr(status, kStBadState);
   if (S == 1) {
@@ -474,11 +567,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
       }
       return;
     }
-    if (wid == 0 && i < G) {
-      const float inv = sL[i] > 0.0f ? 1.0f / sL[i] : 0.0f;
-#pragma unroll
-      for (int nb = 0; nb < NB; nb++) *(float4_t*)(orow + i * D + 16 * nb + 4 * qg) = acc[nb] * inv;
-    }
+    for (int x = tid; x < G * D; x += blockDim.x) orow[x] = ocol(x) * sI[x / D];
     if (SAVE && tid < G) {
       ml[(u * G + tid) * 2 + 0] = sM[tid];
       ml[(u * G + tid) * 2 + 1] = sL[tid];
@@ -486,50 +575,70 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
     if (MODE == 1) {
       // score update: every retained token other than the query's own
       // (position seq_len) adds max over the group of its softmax weight
-      if (tid < 16) sL[tid] = sL[tid] > 0.0f ? 1.0f / sL[tid] : 0.0f;
-      __syncthreads();
       const Seg sh = tier_seg(D, true), sl = tier_seg(D, false);
-      const float* lgg = logits + (int64_t)u * L * 32 * G;
-      constexpr int kU = 4;
-      for (int x0 = tid; x0 < TPg * 32; x0 += kU * blockDim.x) {
-        float* sc[kU];
-        const int32_t* pp[kU];
-        float old[kU], add[kU];
+      if (lg_lds) {
+        // everything is in LDS: the pass only stores
+        float mg[16], ig[16];
 #pragma unroll
-        for (int e = 0; e < kU; e++) {
-          const int x = x0 + e * blockDim.x;
-          const int j = x >> 5, t = x & 31;
-          sc[e] = nullptr;
-          add[e] = 0.0f;
-          if (x < TPg * 32 && t < valid(j)) {
-            const float* lg = lg_lds ? lg_s + (j * 32 + t) * G : lgg + (table_idx(j) * 32 + t) * G;
+        for (int g = 0; g < 16; g++) {
+          mg[g] = g < G ? sM[g] : 0.0f;
+          ig[g] = g < G ? sI[g] : 0.0f;
+        }
+        constexpr int kU = 4;  // independent slots per thread per round
+        for (int x0 = tid; x0 < TPg * 32; x0 += kU * kThreads) {
+#pragma unroll
+          for (int e = 0; e < kU; e++) {
+            const int x = x0 + e * kThreads;
+            if (x >= TPg * 32) break;
+            const int j = x >> 5, t = x & 31;
+            if (t >= valid(j) || pos_s[x] >= N) continue;
+            const float* lg = lg_s + x * G;
             float mx = 0.0f;
-            for (int g = 0; g < G; g++) mx = fmaxf(mx, __builtin_amdgcn_exp2f(lg[g] - sM[g]) * sL[g]);
-            add[e] = mx;
-            const uint8_t* pg = pages + (int64_t)row[table_idx(j)] * page_bytes;
-            sc[e] = (float*)(pg + (j < ph ? sh.sc : sl.sc) + 4 * t);
-            pp[e] = (const int32_t*)(pg + (j < ph ? sh.ps : sl.ps) + 4 * t);
+#pragma unroll
+            for (int g = 0; g < 16; g++)
+              if (g < G) mx = fmaxf(mx, __builtin_amdgcn_exp2f(lg[g] - mg[g]) * ig[g]);
+            uint8_t* pg = pages + (int64_t)id_s[j] * page_bytes;
+            *(float*)(pg + (j < ph ? sh.sc : sl.sc) + 4 * t) = osc_s[x] + mx;
           }
         }
-        int32_t pos[kU];
+      } else {
+        const float* lgg = logits + (int64_t)u * L * 32 * G;
+        constexpr int kU = 4;
+        for (int x0 = tid; x0 < TPg * 32; x0 += kU * blockDim.x) {
+          float* sc[kU];
+          const int32_t* pp[kU];
+          float old[kU], add[kU];
 #pragma unroll
-        for (int e = 0; e < kU; e++) {
-          old[e] = sc[e] ? *sc[e] : 0.0f;
-          pos[e] = sc[e] ? *pp[e] : N;
+          for (int e = 0; e < kU; e++) {
+            const int x = x0 + e * blockDim.x;
+            const int j = x >> 5, t = x & 31;
+            sc[e] = nullptr;
+            add[e] = 0.0f;
+            if (x < TPg * 32 && t < valid(j)) {
+              const float* lg = lgg + (table_idx(j) * 32 + t) * G;
+              float mx = 0.0f;
+              for (int g = 0; g < G; g++) mx = fmaxf(mx, __builtin_amdgcn_exp2f(lg[g] - sM[g]) * sI[g]);
+              add[e] = mx;
+              uint8_t* pg = pages + (int64_t)row[table_idx(j)] * page_bytes;
+              sc[e] = (float*)(pg + (j < ph ? sh.sc : sl.sc) + 4 * t);
+              pp[e] = (const int32_t*)(pg + (j < ph ? sh.ps : sl.ps) + 4 * t);
+            }
+          }
+          int32_t pos[kU];
+#pragma unroll
+          for (int e = 0; e < kU; e++) {
+            old[e] = sc[e] ? *sc[e] : 0.0f;
+            pos[e] = sc[e] ? *pp[e] : N;
+          }
+#pragma unroll
+          for (int e = 0; e < kU; e++)
+            if (sc[e] && pos[e] < N) *sc[e] = old[e] + add[e];
         }
-#pragma unroll
-        for (int e = 0; e < kU; e++)
-          if (sc[e] && pos[e] < N) *sc[e] = old[e] + add[e];
       }
     }
   } else {
     float* mp = part + (((int64_t)u * S + split) * G) * (D + 2);
-    if (wid == 0 && i < G) {
-#pragma unroll
-      for (int nb = 0; nb < NB; nb++)
-#pragma unroll
-        for (int r = 0; r < 4; r++) mp[i * (D + 2) + 16 * nb + 4 * qg + r] = acc[nb][r];
-    }
+    for (int x = tid; x < G * D; x += blockDim.x) mp[(x / D) * (D + 2) + x % D] = ocol(x);
     if (tid < G) {
       mp[tid * (D + 2) + D] = bad ? NAN : sM[tid];  // NaN marks a bad unit for the merge
       mp[tid * (D + 2) + D + 1] = sL[tid];
@@ -649,18 +758,27 @@ hipError_t launch_attn(const Cfg& c, const Pool& p, int batch, const uint16_t* q
   const dim3 grid(S, (unsigned)U), block(kThreads);
   // a single split runs the score update inside the attention workgroup
   const int kmode = mode == 1 && S > 1 ? 2 : mode;
-#define DKV_ATTN(D, M)                                                                                     \
-  attn_kernel<D, M><<<grid, block, 0, s>>>(c.H, c.G, c.L, S, p.P, p.page_bytes, scale_log2, q, table,   \
-                                           state, seq_len, p.pages, out, w.part, w.ml, w.logits, p.status)
-  if (c.d == 128) {
-    if (kmode == 0) DKV_ATTN(128, 0);
-    else if (kmode == 1) DKV_ATTN(128, 1);
-    else DKV_ATTN(128, 2);
-  } else {
-    if (kmode == 0) DKV_ATTN(64, 0);
-    else if (kmode == 1) DKV_ATTN(64, 1);
-    else DKV_ATTN(64, 2);
+  // head and tail of the weights share one matrix instruction when 2G <= 16
+  const bool pack = 2 * c.G <= 16;
+#define DKV_ATTN(D, M, PK)                                                                             \
+  attn_kernel<D, M, PK><<<grid, block, 0, s>>>(c.H, c.G, c.L, S, p.P, p.page_bytes, scale_log2, q, table, \
+                                               state, seq_len, p.pages, out, w.part, w.ml, w.logits, p.status)
+#define DKV_ATTN_D(D)                                    \
+  if (pack) {                                            \
+    if (kmode == 0) DKV_ATTN(D, 0, true);                \
+    else if (kmode == 1) DKV_ATTN(D, 1, true);           \
+    else DKV_ATTN(D, 2, true);                           \
+  } else {                                               \
+    if (kmode == 0) DKV_ATTN(D, 0, false);               \
+    else if (kmode == 1) DKV_ATTN(D, 1, false);          \
+    else DKV_ATTN(D, 2, false);                          \
   }
+  if (c.d == 128) {
+    DKV_ATTN_D(128)
+  } else {
+    DKV_ATTN_D(64)
+  }
+#undef DKV_ATTN_D
 #undef DKV_ATTN
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
