@@ -167,7 +167,10 @@ int diffkv_compact(const diffkv_config* cfg, const diffkv_pool* pool, int32_t mo
  * (each retained token with position < seq_len[b] adds the max over the
  * group's q heads of its softmax weight to its stored score sum; pages are
  * written); 2 = attention that keeps its logits in `workspace` for a later
- * diffkv_update_scores call (needs the DIFFKV_ATTN_SCORES workspace size). */
+ * diffkv_update_scores call (needs the DIFFKV_ATTN_SCORES workspace size).
+ * A unit whose tier_state is inconsistent, or whose table row holds a page
+ * id outside [0, num_pages), gets output 0, no score update, and sets
+ * DIFFKV_ST_BAD_STATE; no load leaves the pool. */
 int diffkv_decode_attn(const diffkv_config* cfg, const diffkv_pool* pool, int32_t batch,
                        const uint16_t* q, const int32_t* page_table,
                        const int32_t* tier_state, const int32_t* seq_len, float* out,

@@ -9,30 +9,46 @@ ids grow left to right, lo ids right to left), Fig 6 prompt workflow
 6, 7 and 11 reclaimed), generation workflow (at most one new page per head
 per step, no reclamation until the request completes).
 """
+import os
+
 import numpy as np
 import pytest
 
 from tests.invariants import check_pool_invariants
 
 
+def _golden(name):
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", name)
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if line.strip() and not line.startswith("#"):
+                key, *rest = line.split()
+                vals[key] = [int(x) for x in rest]
+    return vals
+
+
 def test_fig6_worked_example_literal(orc):
-    # Small pages exactly as in the figure: T_h = 2, T_l = 4, N = 8.
-    # Pages 0-4 are already in use (allocation pointer at 5).
-    P, L = 16, 8 // 2 + 1
+    # Small pages exactly as in the figure (tests/golden/fig6_prompt_allocation.txt).
+    g = _golden("fig6_prompt_allocation.txt")
+    P, th, tl, N = g["pool_pages"][0], g["hi_page_tokens"][0], g["lo_page_tokens"][0], g["seq_len"][0]
+    L = -(-N // th) + 1
     free_list = np.arange(P, dtype=np.int32)
-    ptr = np.array([5, P], np.uint64)
+    ptr = np.array([g["alloc_start"][0], P], np.uint64)
     status = np.zeros(1, np.uint32)
     table = np.full((1, 2, L), -1, np.int32)
     state = np.zeros((1, 2, 4), np.int32)
-    # head A: 2 hi tokens (1 page) + 3 lo tokens (1 page); head B: 3 hi (2) + 2 lo (1)
-    orc.prompt_allocate(2, 2, 4, L, [8], [2, 3], [3, 2], free_list, ptr, status, table, state)
+    n_hi = [g["head_A_tokens"][0], g["head_B_tokens"][0]]
+    n_lo = [g["head_A_tokens"][1], g["head_B_tokens"][1]]
+    orc.prompt_allocate(2, th, tl, L, [N], n_hi, n_lo, free_list, ptr, status, table, state)
     assert status[0] == 0
-    assert table[0, 0].tolist() == [5, -1, -1, -1, 8]
-    assert table[0, 1].tolist() == [9, 10, -1, -1, 12]
-    assert int(ptr[0]) == 13                      # "pointer advances to 13"
-    assert int(ptr[1]) == P + 3                   # three pages reclaimed
-    assert free_list[[P % P, (P + 1) % P, (P + 2) % P]].tolist() == [6, 7, 11]
-    assert state.tolist() == [[[2, 3, 1, 1], [3, 2, 2, 1]]]
+    assert table[0, 0].tolist() == g["table_A"]
+    assert table[0, 1].tolist() == g["table_B"]
+    assert int(ptr[0]) == g["alloc_pointer_after"][0]
+    freed = g["reclaimed_in_order"]
+    assert int(ptr[1]) == P + len(freed)
+    assert free_list[[(P + i) % P for i in range(len(freed))]].tolist() == freed
+    assert state.tolist() == [[[n_hi[0], n_lo[0], 1, 1], [n_hi[1], n_lo[1], 2, 1]]]
 
 
 def _fig6_scaled_inputs(orc, d=128):
