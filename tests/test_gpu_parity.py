@@ -120,7 +120,7 @@ def _medium_cfg(name, **over):
     return c
 
 
-@pytest.mark.parametrize("d,G,lo", [(128, 4, 1), (64, 5, 1), (128, 7, 0), (128, 8, 1)])
+@pytest.mark.parametrize("d,G,lo", [(128, 4, 1), (64, 5, 1), (128, 7, 0), (128, 8, 1), (64, 16, 1)])
 def test_ragged_prompt_step_attention(dk, orc, d, G, lo):
     """Ragged batch (tails inside pages, a prompt shorter than the window),
     prompt compaction, 6 steps with score updates, release of half the batch,
@@ -251,6 +251,60 @@ def test_single_split_fused_scores(dk, orc, mode):
             assert_attn_close(out_g, out_o, f"attn {step}")
             assert_scores_close(p.g, p.o, f"scores {step}")
             resync_scores(p.g, p.o)
+        seq = seq + 1
+
+
+def test_many_units_coordination_kernel(dk, orc):
+    """More units than the commit kernels' own prefix sum covers (2048): the
+    step takes the single-block coordination path; one split per unit."""
+    from workloads import synth
+    cfg = _medium_cfg("llama3_8b", head_dim=64, num_kv_heads=8, gqa_group=2, batch=264, max_seq_len=400)
+    B = 264
+    assert B * 8 > 2048 and dk.diffkv_attn_splits(cfg, B) == 1
+    g = torch.Generator().manual_seed(21)
+    # lengths just below page boundaries so the steps allocate pages
+    lens = (torch.randint(5, 12, (B,), generator=g) * 16 - torch.randint(0, 3, (B,), generator=g)).to(torch.int64)
+    pr = synth.make_prompt(cfg, lens=lens)
+    cu = pr["cu_seqlens"].numpy()
+    P = int(sum(-(-int(n) // 16) for n in lens) * 8 * 1.2) + 64
+    p = Pair(dk, orc, cfg, B, P, int(cu[-1]))
+    _say("many units: prompt")
+    p.prompt(cu, pr["k"].numpy(), pr["v"].numpy(), pr["scores"].numpy())
+    seq = lens.numpy().astype(np.int32)
+    for step in range(4):
+        dec = synth.make_decode(cfg, step)
+        _say("  step", step)
+        p.step(seq, dec["k_new"].numpy(), dec["v_new"].numpy(), f"step {step}")
+        p.attend(dec["q"].numpy(), seq, True, f"attn {step}")
+        seq = seq + 1
+    check_pool_invariants(orc, p.o)
+
+
+def test_fused_scores_large_units(dk, orc):
+    """One split per unit, with units too large to keep their logits in LDS
+    (the fused score update then goes through the workspace) next to small
+    ones that fit."""
+    from workloads import synth
+    cfg = _medium_cfg("llama3_8b", head_dim=64, batch=32, max_seq_len=6400)
+    assert dk.diffkv_attn_splits(cfg, 32) == 1
+    g = torch.Generator().manual_seed(31)
+    lens = torch.where(torch.arange(32) % 2 == 0, torch.randint(5500, 6200, (32,), generator=g),
+                       torch.randint(100, 600, (32,), generator=g)).to(torch.int64)
+    pr = synth.make_prompt(cfg, lens=lens)
+    cu = pr["cu_seqlens"].numpy()
+    P = int(sum(-(-int(n) // 16) for n in lens) * 8 * 1.05) + 64
+    p = Pair(dk, orc, cfg, 32, P, int(cu[-1]))
+    _say("large units: prompt")
+    p.prompt(cu, pr["k"].numpy(), pr["v"].numpy(), pr["scores"].numpy())
+    ts = np_(p.g.tier_state).reshape(-1, 4)
+    pages = ts[:, 2] + ts[:, 3]
+    G = cfg["gqa_group"]
+    assert (pages * 32 * (G + 2) + pages > 16384).any() and (pages * 32 * (G + 2) + pages <= 16384).any()
+    seq = lens.numpy().astype(np.int32)
+    for step in range(2):
+        dec = synth.make_decode(cfg, step)
+        p.step(seq, dec["k_new"].numpy(), dec["v_new"].numpy(), f"step {step}")
+        p.attend(dec["q"].numpy(), seq, True, f"attn {step}")
         seq = seq + 1
 
 
