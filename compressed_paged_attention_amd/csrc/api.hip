@@ -15,7 +15,8 @@ bool cfg_ok(const diffkv_config* c) {
   if (c->head_dim != 64 && c->head_dim != 128) return false;
   if (c->num_kv_heads < 1 || c->gqa_group < 1 || c->gqa_group > 16) return false;
   if (c->hi_page_tokens != kHiTokens || c->lo_page_tokens != kLoTokens) return false;
-  if (c->max_seq_len < 1 || c->window < 0) return false;
+  // max_seq_len < 2^29: a fp32 score sum times a token count is exact in fp64
+  if (c->max_seq_len < 1 || c->max_seq_len >= (1 << 29) || c->window < 0) return false;
   if (!(c->alpha_l >= 0.0f) || !(c->alpha_h >= 0.0f)) return false;
   if (c->lo_enabled && c->alpha_l > c->alpha_h) return false;
   return true;

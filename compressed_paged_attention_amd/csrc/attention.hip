@@ -350,7 +350,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
   constexpr int QD = D / 4;   // dims per lane group
   const int split = blockIdx.x;
   const int64_t u = blockIdx.y;
-  const int b = (int)(u / H), h = (int)(u % H);
+  const int b = (int)u / H, h = (int)u % H;  // u < 2^31: 32-bit division
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar loop control
   const int i = lane & 15, qg = lane >> 4;
@@ -653,7 +653,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(int H, int G, int S, co
                                                          const float* __restrict__ part, float* __restrict__ out,
                                                          float* __restrict__ ml, int save) {
   const int64_t u = blockIdx.x;
-  const int b = (int)(u / H), h = (int)(u % H);
+  const int b = (int)u / H, h = (int)u % H;  // u < 2^31: 32-bit division
   if (seq_len[b] <= 0) return;  // the attention kernel already wrote zeros
   const float* up = part + (u * S * G) * (D + 2);
   float* orow = out + ((int64_t)b * H * G + (int64_t)h * G) * D;
@@ -694,7 +694,7 @@ __global__ __launch_bounds__(256) void score_kernel(int H, int G, int L, int S, 
                                                     const float* __restrict__ logits, uint8_t* pages) {
   const int split = blockIdx.x;
   const int64_t u = blockIdx.y;
-  const int b = (int)(u / H);
+  const int b = (int)u / H;
   const int tid = threadIdx.x;
   const int32_t* row = table + u * L;
   const int32_t* s4 = state + 4 * u;

@@ -137,21 +137,86 @@ __device__ inline float dequant(float s, float z, uint32_t code) {
 // ---------------------------------------------------------------------------
 // wave64 / block primitives
 // ---------------------------------------------------------------------------
+// Butterfly partner of level LVL across a 64-lane wave, without LDS: levels
+// 0-3 by DPP inside rows of 16 lanes (xor 1, xor 2, half-row mirror, row
+// mirror), levels 4-5 by row swaps (xor 16, xor 32).  Combining a value with
+// its partner at levels 0..5 under an associative, commutative operation
+// leaves the reduction of all 64 lanes in every lane.
+template <int LVL>
+__device__ inline uint32_t lane_xchg(uint32_t v) {
+  if constexpr (LVL == 0) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+  } else if constexpr (LVL == 1) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+  } else if constexpr (LVL == 2) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  } else if constexpr (LVL == 3) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false);  // row_mirror
+  } else if constexpr (LVL == 4) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (threadIdx.x & 16) ? r[0] : r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (threadIdx.x & 32) ? r[0] : r[1];
+  }
+}
+
+template <int LVL, typename T>
+__device__ inline T lane_xchg_t(T v) {
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, lane_xchg<LVL>(__builtin_bit_cast(uint32_t, v)));
+  } else {
+    static_assert(sizeof(T) == 8, "32- or 64-bit values");
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint64_t lo = lane_xchg<LVL>((uint32_t)u), hi = lane_xchg<LVL>((uint32_t)(u >> 32));
+    return __builtin_bit_cast(T, lo | (hi << 32));
+  }
+}
+
+template <typename T, typename Op>
+__device__ inline T wave_reduce(T v, Op op) {
+  v = op(v, lane_xchg_t<0>(v));
+  v = op(v, lane_xchg_t<1>(v));
+  v = op(v, lane_xchg_t<2>(v));
+  v = op(v, lane_xchg_t<3>(v));
+  v = op(v, lane_xchg_t<4>(v));
+  v = op(v, lane_xchg_t<5>(v));
+  return v;
+}
+
+// Reduction inside aligned groups of N lanes (N a power of two <= 64).
+template <int N, typename T, typename Op>
+__device__ inline T group_reduce(T v, Op op) {
+  if constexpr (N > 1) v = op(v, lane_xchg_t<0>(v));
+  if constexpr (N > 2) v = op(v, lane_xchg_t<1>(v));
+  if constexpr (N > 4) v = op(v, lane_xchg_t<2>(v));
+  if constexpr (N > 8) v = op(v, lane_xchg_t<3>(v));
+  if constexpr (N > 16) v = op(v, lane_xchg_t<4>(v));
+  if constexpr (N > 32) v = op(v, lane_xchg_t<5>(v));
+  return v;
+}
+
+// Same with a wave-uniform group size n.
+template <typename T, typename Op>
+__device__ inline T group_reduce(T v, int n, Op op) {
+  if (n > 1) v = op(v, lane_xchg_t<0>(v));
+  if (n > 2) v = op(v, lane_xchg_t<1>(v));
+  if (n > 4) v = op(v, lane_xchg_t<2>(v));
+  if (n > 8) v = op(v, lane_xchg_t<3>(v));
+  if (n > 16) v = op(v, lane_xchg_t<4>(v));
+  if (n > 32) v = op(v, lane_xchg_t<5>(v));
+  return v;
+}
+
 template <typename T>
 __device__ inline T wave_sum(T v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  return wave_reduce(v, [](T a, T b) { return a + b; });
 }
 __device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  return wave_reduce(v, [](float a, float b) { return fmaxf(a, b); });
 }
 __device__ inline float wave_min(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
-  return v;
+  return wave_reduce(v, [](float a, float b) { return fminf(a, b); });
 }
 
 // Inclusive scan across a wave (Hillis-Steele over 64 lanes).
@@ -185,6 +250,26 @@ __device__ inline T block_excl_scan(T v, T* lds, T& total) {
   total = lds[nw];
   __syncthreads();
   return res;
+}
+
+// Exclusive block-wide count of a predicate (ballot + lane mask count per
+// wave, then the wave totals); `lds` holds >= blockDim/64 ints.  Returns the
+// number of threads below this one with pred set and the block total.
+__device__ inline int block_excl_count(bool pred, int* lds, int& total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+  const uint64_t m = __ballot(pred);
+  const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+  if (lane == 0) lds[wid] = __popcll(m);
+  __syncthreads();
+  int before = 0, tot = 0;
+  for (int w = 0; w < nw; w++) {
+    const int c = lds[w];
+    before += w < wid ? c : 0;
+    tot += c;
+  }
+  __syncthreads();
+  total = tot;
+  return before + below;
 }
 
 __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -359,12 +359,12 @@ __global__ __launch_bounds__(256) void prompt_pack_kernel(int H, int L, int64_t 
         vmn = fminf(vmn, xv[i]);
         vmx = fmaxf(vmx, xv[i]);
       }
-      for (int o = 1; o < TPT; o <<= 1) {
-        kmn = fminf(kmn, __shfl_xor(kmn, o, 64));
-        kmx = fmaxf(kmx, __shfl_xor(kmx, o, 64));
-        vmn = fminf(vmn, __shfl_xor(vmn, o, 64));
-        vmx = fmaxf(vmx, __shfl_xor(vmx, o, 64));
-      }
+      auto fmn = [](float a, float b) { return fminf(a, b); };
+      auto fmx = [](float a, float b) { return fmaxf(a, b); };
+      kmn = group_reduce(kmn, TPT, fmn);
+      kmx = group_reduce(kmx, TPT, fmx);
+      vmn = group_reduce(vmn, TPT, fmn);
+      vmx = group_reduce(vmx, TPT, fmx);
       uint16_t ks16, kz16, vs16, vz16;
       float ks, kz, vs, vz;
       codec_params(kmn, kmx, sg.kbits, ks16, kz16, ks, kz);

@@ -68,54 +68,42 @@ static StepWs step_carve(const Cfg& c, int batch, void* ws) {
   return w;
 }
 
+// A candidate token: running score sum, position, slot; pos == kNoPos: none.
+// Its observation count is N - 1 - pos.
+constexpr int32_t kNoPos = 0x7FFFFFFF;
 struct Cand {
   float sum;
-  int cnt, pos, slot;
-  bool has;
+  int32_t pos, slot;
 };
 
-__device__ inline bool less_imp(const Cand& a, const Cand& b) {
-  if (!a.has) return false;
-  if (!b.has) return true;
-  const double l = (double)a.sum * (double)b.cnt, r = (double)b.sum * (double)a.cnt;
-  if (l != r) return l < r;
-  return a.pos < b.pos;
+// Strictly less important: sum_a * cnt_b < sum_b * cnt_a (exact in fp64),
+// ties to the smaller position.
+// Counts are below 2^31 (N <= max_seq_len), so both products are exact.
+__device__ inline bool less_imp(const Cand& a, const Cand& b, int64_t N) {
+  if (a.pos == kNoPos) return false;
+  if (b.pos == kNoPos) return true;
+  const int32_t n1 = (int32_t)(N - 1);
+  const double l = (double)a.sum * (double)(n1 - b.pos), r = (double)b.sum * (double)(n1 - a.pos);
+  return l < r || (l == r && a.pos < b.pos);
 }
 
-__device__ inline Cand shfl_cand(const Cand& c, int o) {
-  Cand r;
-  r.sum = __shfl_xor(c.sum, o, 64);
-  r.cnt = __shfl_xor(c.cnt, o, 64);
-  r.pos = __shfl_xor(c.pos, o, 64);
-  r.slot = __shfl_xor(c.slot, o, 64);
-  r.has = __shfl_xor((int)c.has, o, 64) != 0;
-  return r;
+template <int LVL>
+__device__ inline void argmin_step(Cand& c, int64_t N) {
+  const Cand t{lane_xchg_t<LVL>(c.sum), lane_xchg_t<LVL>(c.pos), lane_xchg_t<LVL>(c.slot)};
+  if (less_imp(t, c, N)) c = t;
 }
 
-// Block argmin of two independent candidates (one pair of barriers).
+__device__ inline Cand wave_argmin(Cand c, int64_t N) {
+  argmin_step<0>(c, N);
+  argmin_step<1>(c, N);
+  argmin_step<2>(c, N);
+  argmin_step<3>(c, N);
+  argmin_step<4>(c, N);
+  argmin_step<5>(c, N);
+  return c;
+}
+
 constexpr int kPlanThreads = 512;
-
-__device__ void block_argmin2(Cand& a, Cand& b, Cand (*lds)[kPlanThreads / 64]) {
-  for (int o = 32; o >= 1; o >>= 1) {
-    Cand t = shfl_cand(a, o);
-    if (less_imp(t, a)) a = t;
-    t = shfl_cand(b, o);
-    if (less_imp(t, b)) b = t;
-  }
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  if (lane == 0) {
-    lds[0][wid] = a;
-    lds[1][wid] = b;
-  }
-  __syncthreads();
-  a = lds[0][0];
-  b = lds[1][0];
-  for (int w = 1; w < nw; w++) {
-    if (less_imp(lds[0][w], a)) a = lds[0][w];
-    if (less_imp(lds[1][w], b)) b = lds[1][w];
-  }
-  __syncthreads();
-}
 
 __device__ inline int classify_mean(float sum, int64_t cnt, int64_t Np, int lo_en, double ah, double al) {
   const double x = (double)sum * (double)Np;
@@ -140,7 +128,7 @@ __global__ __launch_bounds__(kPlanThreads) void step_plan_kernel(int H, int L, i
                                                         const uint64_t* __restrict__ ptr, int64_t* __restrict__ hdr,
                                                         int32_t* __restrict__ rec, int32_t* __restrict__ nf) {
   const int64_t u = blockIdx.x;
-  const int b = (int)(u / H);
+  const int b = (int)u / H;
   const int tid = threadIdx.x;
   if (u == 0 && tid == 0) {  // pointer snapshot for the commit kernel
     hdr[SH_START] = (int64_t)ptr[0];
@@ -171,52 +159,56 @@ __global__ __launch_bounds__(kPlanThreads) void step_plan_kernel(int H, int L, i
   __shared__ float s_tcsum;
   __shared__ uint32_t s_bad;
   __shared__ Cand lds[2][kPlanThreads / 64];
+  const Cand none{0.0f, kNoPos, 0};
   if (tid == 0) {
     s_tc = -1;
     s_bad = 0;
   }
   __syncthreads();
-  Cand bh{0.0f, 0, 0, 0, false}, bl{0.0f, 0, 0, 0, false};
+  Cand bh = none, bl = none;
   if (tc_pos >= 0) {
     // every slot of both tiers (this also checks every page id of the row);
     // kPer slots per thread per round, their loads issued together
     constexpr int kPer = 4;
     const int n = nh + nl;
     for (int base = 0; base < n; base += kPer * kPlanThreads) {
+      // branch-free loads (indices clamped into the unit) so that each
+      // round costs two dependent trips to memory
       int32_t id[kPer];
 #pragma unroll
       for (int e = 0; e < kPer; e++) {
-        const int s = base + e * kPlanThreads + tid;
-        const int ls = s < nh ? s : s - nh;
-        id[e] = s < n ? (s < nh ? row[ls >> 4] : row[L - 1 - (ls >> 5)]) : 0;
+        const int s = min(base + e * kPlanThreads + tid, n - 1);
+        const bool hi = s < nh;
+        const int ls = hi ? s : s - nh;
+        id[e] = row[hi ? (ls >> 4) : L - 1 - (ls >> 5)];
       }
       int32_t pos[kPer];
       float sum[kPer];
 #pragma unroll
       for (int e = 0; e < kPer; e++) {
-        const int s = base + e * kPlanThreads + tid;
+        const int s = min(base + e * kPlanThreads + tid, n - 1);
         const bool hi = s < nh;
         const int ls = hi ? s : s - nh;
-        if (s < n && (id[e] < 0 || id[e] >= P)) s_bad = 1;
         const uint8_t* pg = pages + (int64_t)min(max(id[e], 0), (int32_t)(P - 1)) * page_bytes;
         const int idx = hi ? (ls & 15) : (ls & 31);
-        pos[e] = s < n ? *(const int32_t*)(pg + (hi ? sh.ps : sl.ps) + 4 * idx) : 0;
-        sum[e] = s < n ? *(const float*)(pg + (hi ? sh.sc : sl.sc) + 4 * idx) : 0.0f;
+        pos[e] = *(const int32_t*)(pg + (hi ? sh.ps : sl.ps) + 4 * idx);
+        sum[e] = *(const float*)(pg + (hi ? sh.sc : sl.sc) + 4 * idx);
       }
 #pragma unroll
       for (int e = 0; e < kPer; e++) {
         const int s = base + e * kPlanThreads + tid;
         if (s >= n) continue;
+        if (id[e] < 0 || id[e] >= P) s_bad = 1;
         const bool hi = s < nh;
         const int ls = hi ? s : s - nh;
-        const Cand c{sum[e], (int)(N - 1 - pos[e]), pos[e], ls, true};
+        const Cand c{sum[e], pos[e], ls};
         if (hi) {
           if (pos[e] == tc_pos) {  // positions are unique: one writer
             s_tc = ls;
             s_tcsum = sum[e];
           }
-          if (pos[e] <= tc_pos && less_imp(c, bh)) bh = c;
-        } else if (less_imp(c, bl)) {
+          if (pos[e] <= tc_pos && less_imp(c, bh, N)) bh = c;
+        } else if (less_imp(c, bl, N)) {
           bl = c;
         }
       }
@@ -227,7 +219,19 @@ __global__ __launch_bounds__(kPlanThreads) void step_plan_kernel(int H, int L, i
       if (id < 0 || id >= P) s_bad = 1;
     }
   }
-  block_argmin2(bh, bl, lds);  // its barriers publish s_tc and s_bad
+  bh = wave_argmin(bh, N);
+  bl = wave_argmin(bl, N);
+  if ((tid & 63) == 0) {
+    lds[0][tid >> 6] = bh;
+    lds[1][tid >> 6] = bl;
+  }
+  __syncthreads();  // also publishes s_tc and s_bad
+  if (tid == 0) {
+    for (int w = 1; w < kPlanThreads / 64; w++) {
+      if (less_imp(lds[0][w], bh, N)) bh = lds[0][w];
+      if (less_imp(lds[1][w], bl, N)) bl = lds[1][w];
+    }
+  }
   const int tcs = s_tc;
   const float tcsum = s_tcsum;
   // t_c is in the high tier by construction; a missing t_c is bad state
@@ -240,7 +244,7 @@ __global__ __launch_bounds__(kPlanThreads) void step_plan_kernel(int H, int L, i
   if (tc_pos >= 0) {
     const int cls = classify_mean(tcsum, W - 1, Np, lo_en, dah, dal);
     if (cls == kTierHi) {
-      const int vcls = classify_mean(bh.sum, bh.cnt, Np, lo_en, dah, dal);
+      const int vcls = classify_mean(bh.sum, N - 1 - bh.pos, Np, lo_en, dah, dal);
       if (vcls == kTierLo) {
         lo_src = bh.slot;
         lo_slot = nl;
@@ -257,9 +261,9 @@ __global__ __launch_bounds__(kPlanThreads) void step_plan_kernel(int H, int L, i
       lo_src = tcs;
       new_hi = tcs;
       hi_app = 0;
-      const Cand tcc{tcsum, W - 1, (int)tc_pos, -1, true};
-      const Cand lv = less_imp(tcc, bl) ? tcc : bl;
-      if (lv.slot >= 0 && classify_mean(lv.sum, lv.cnt, Np, lo_en, dah, dal) == kTierPrune) {
+      const Cand tcc{tcsum, (int32_t)tc_pos, -1};
+      const Cand lv = less_imp(tcc, bl, N) ? tcc : bl;
+      if (lv.slot >= 0 && classify_mean(lv.sum, N - 1 - lv.pos, Np, lo_en, dah, dal) == kTierPrune) {
         lo_slot = lv.slot;
         lo_app = 0;
       } else {
@@ -476,7 +480,7 @@ __global__ __launch_bounds__(256) void step_commit_kernel(int H, int L, int64_t 
   constexpr int kPageWords = page_bytes_for(D) / 4;
   const int64_t u = blockIdx.x;
   const int tid = threadIdx.x;
-  const int b = (int)(u / H), h = (int)(u % H);
+  const int b = (int)u / H, h = (int)u % H;  // u < 2^31: 32-bit division
   // ---- phase 1: loads ----
   const int32_t wu = nf[u];
   const int32_t* R = rec + u * kSRec;
@@ -487,19 +491,18 @@ __global__ __launch_bounds__(256) void step_commit_kernel(int H, int L, int64_t 
   float xv_new = tid < D ? h2f(v_new[rowi]) : 0.0f;
   int32_t page = -1;
   if constexpr (DIRECT) {
-    __shared__ int64_t lds[20];
+    __shared__ int lds[16];
     __shared__ int64_t s_off;
     __shared__ uint32_t s_fl;
     if (tid == 0) s_fl = 0;
-    __syncthreads();
     int64_t total = 0;
     uint32_t fl = 0;
     for (int64_t base = 0; base < U; base += blockDim.x) {
       const int64_t x = base + tid;
       const int32_t w = x < U ? nf[x] : 0;
       fl |= (uint32_t)w >> 8;
-      int64_t t;
-      const int64_t excl = block_excl_scan((int64_t)((w & 3) != 0), lds, t);
+      int t;
+      const int excl = block_excl_count((w & 3) != 0, lds, t);
       if (x == u) s_off = total + excl;
       total += t;
     }

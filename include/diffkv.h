@@ -45,7 +45,8 @@ extern "C" {
  * [alpha_l/N, alpha_h/N], pruned below alpha_l/N ("Approach"; "KV
  * compression policy").  With lo_enabled = 0: high iff >= alpha_l/N.
  * Valid: head_dim in {64,128}; 1 <= gqa_group <= 16; hi_page_tokens = 16;
- * lo_page_tokens = 32; max_seq_len >= 1; window >= 0 (>= 2 for STEP);
+ * 1 <= max_seq_len < 2^29 (score sums times token counts stay exact in fp64);
+ * lo_page_tokens = 32; window >= 0 (>= 2 for STEP);
  * 0 <= alpha_l <= alpha_h when lo_enabled. */
 typedef struct {
   int32_t head_dim;       /* d */

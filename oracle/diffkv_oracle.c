@@ -38,7 +38,8 @@ static int cfg_valid(const orc_cfg* c) {
   if (c->head_dim != 64 && c->head_dim != 128) return 0;
   if (c->num_kv_heads < 1 || c->gqa_group < 1 || c->gqa_group > 16) return 0;
   if (c->hi_page_tokens != 16 || c->lo_page_tokens != 2 * c->hi_page_tokens) return 0;
-  if (c->max_seq_len < 1 || c->window < 0) return 0;
+  /* N < 2^29 keeps fp32 score sums times counts exact in fp64 (exact threshold compares) */
+  if (c->max_seq_len < 1 || c->max_seq_len >= (1 << 29) || c->window < 0) return 0;
   if (!(c->alpha_l >= 0.0f) || !(c->alpha_h >= 0.0f)) return 0;
   if (c->lo_enabled && c->alpha_l > c->alpha_h) return 0;
   return 1;
