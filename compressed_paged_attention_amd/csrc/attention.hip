@@ -20,11 +20,14 @@
 // with P' = softmax weight * s_v.  The dequantization is algebraic:
 //   q . k^ = s_k (q . c_k) + z_k sum(q)
 //   sum_t p_t v^_t = sum_t (p_t s_v,t) c_t + (sum_t p_t z_v,t) * 1
-// so only integer codes (exact fp16 subnormals) enter the matrix units.  P' is split
-// into an fp16 head and an fp16 tail (two instructions) so the PV product
-// keeps ~22 bits.  The online softmax rescales lazily (reference max moves
-// by more than 2^4 at a time).  The S accumulator layout equals the P'^T operand layout,
-// so softmax needs no data movement between the two products.  K codes are
+// so only codes enter the matrix units, as exact fp16 values (8-bit codes as
+// subnormals c 2^-24, 4- and 2-bit codes as 1 + c/2^b; the offsets are
+// removed in fp32 with sum(q) and sum(p s_v), see block_update).  P' is
+// split into an fp16 head and an fp16 tail (with 2G <= 16 the tail rides in
+// columns G..2G-1 of the same instruction) so the PV product keeps ~22 bits.
+// The S accumulator layout equals the
+// P'^T operand layout, so softmax needs no data movement between the two
+// products.  K codes are
 // read token-major (lane: token l%16, a quarter of d); V codes are stored in
 // 64 lane chunks so each lane issues one 16-byte load per page.  The online
 // softmax is fp32 in base 2.  The waves are merged in LDS by a fixed-order
@@ -55,25 +58,34 @@ __device__ inline float4_t mfma32(half8_t a, half8_t b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// Codes enter the matrix units as fp16 subnormals: the 16-bit pattern c is
-// the fp16 value c * 2^-24 (exact), so unpacking is a mask or a byte permute
-// and the 2^24 is restored in fp32 (K: folded into the scale; V: at the
-// merge).  The matrix instruction keeps fp16 subnormal inputs exactly.
 __device__ inline half4_t cat(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(half4_t, (uint64_t)a | ((uint64_t)b << 32));
 }
-// 4 u8 codes of one dword -> 4 subnormal fp16 codes in order (byte permutes
-// with zero bytes: selector 0x0C gives 0x00)
+// 8-bit codes enter as fp16 subnormals: the 16-bit pattern c is the value
+// c 2^-24 (exact; measured on the matrix unit to keep fp32-level accuracy for
+// codes of this size), so unpacking 4 codes of a dword is two byte permutes
+// with zero bytes (selector 0x0C gives 0x00); the 2^24 is folded into the
+// logit scale.
 __device__ inline half4_t u8x4(uint32_t w) {
   return cat(__builtin_amdgcn_perm(0u, w, 0x0C010C00u), __builtin_amdgcn_perm(0u, w, 0x0C030C02u));
 }
 __device__ inline half8_t cat8(half4_t a, half4_t b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
-// the fields at bits s and s+16 of a dword -> subnormal fp16 pair
-__device__ inline uint32_t nib2(uint32_t w, int s) { return (w >> s) & 0x000F000Fu; }
-__device__ inline uint32_t crumb2(uint32_t w, int s) { return (w >> s) & 0x00030003u; }
 constexpr float kTwo24 = 16777216.0f;
+// 4- and 2-bit codes enter as the normal fp16 values 1 + c/16 and 1 + c/4:
+// the code goes to the top of the mantissa under the exponent of 1.0 (as
+// subnormals these small codes lose precision in the matrix unit).  The
+// fields at bits s and s+16 of a dword give a packed fp16 pair: one shift
+// and one and-or.
+__device__ inline uint32_t nib2(uint32_t w, int s) {
+  const uint32_t t = s >= 6 ? w >> (s - 6) : w << (6 - s);
+  return (t & 0x03C003C0u) | 0x3C003C00u;
+}
+__device__ inline uint32_t crumb2(uint32_t w, int s) {
+  const uint32_t t = s >= 8 ? w >> (s - 8) : w << (8 - s);
+  return (t & 0x03000300u) | 0x3C003C00u;
+}
 
 int attn_splits(const Cfg& c, int batch) {
   const int64_t U = (int64_t)batch * c.H;
@@ -185,9 +197,7 @@ __device__ inline void load_page_sp(PageRegs<D>& R, const uint8_t* pg, bool lo, 
 }
 
 struct Softmax {
-  // reference max (base 2) raised by kLazy, sum of weights, sum of weight * z_v
-  // (both sums carry the factor 2^-kLazy of the weights)
-  float m, lsum, zsum;
+  float m, lsum, zsum;  // reference (base 2), sum of weights, sum of weight * z_v
 };
 
 // max over the lanes i, i+16, i+32, i+48 (the four token rows of a head):
@@ -210,22 +220,34 @@ __device__ inline float rows_sum(float v) {
   return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
-// The reference max moves only when a block's max exceeds it by more than
-// kLazy (base 2), so weights stay <= 2^kLazy.  Weights are formed directly at
-// 2^-kLazy (p' = 2^(x - m - kLazy) <= 1) so the fp16 head of p' s_v can never
-// overflow; every sum carries that factor, which the merge removes exactly.
+// Reference of the online softmax.  Weights are p = 2^(x - m) for a
+// reference m the wave chooses; every sum (weights, the z term, the PV
+// accumulator) carries the same 2^-m, which the normalization removes, so m
+// is free.  It is kept at least kHead above the largest logit seen, so
+// p <= 1/4 and the fp16 operand p s_v kv stays below 4 s_v (high, kv = 16)
+// or s_v (low, kv = 4): finite for the scale of any vector of fp16 values
+// (range <= 131008, so s_v <= 8734 high, 43670 low).  It moves (to the block
+// max + kHead + kLazy) only when a block breaks that bound, so the
+// accumulators are rescaled rarely.
+constexpr float kHead = 2.0f;
 constexpr float kLazy = 4.0f;
 
 // One 16-token block: logits (masked on a partial page), online-softmax
 // update, PV products.  `s` holds q.c * 2^-24 for tokens first..first+3 of the
 // page; `kmw`/`vmw` the metadata words of those tokens; `vpair(nb)` the fp16 V
 // operand of 16-dim block nb; `keep(x)` stores the block's logits.
-// c24 = 2^24 scale_log2 (uniform), sq2 = sum(q) scale_log2 (per head).
+// sq2 = sum(q) scale_log2 (per head).  K: s = q.c'' with c'' = c 2^-24 (high)
+// or 1 + c/16 (low), so q.c = s * 2^24 or 16 (s - sum q) and
+//   x = ks * s * kmul + (kz - kk ks) sq2,  kmul = 2^24 sl or 16 sl, kk = 0 or 16.
+// V: codes c'' = 1 + c/kv (kv = 16 high, 4 low) with operand p s_v kv, so
+//   sum p s_v kv c'' = sum p s_v c + sum p s_v kv, and the z term collects
+//   p (z_v - kv s_v).
 // PACK: column i + G carries the fp16 tail of head i's weights (one matrix
 // instruction per block instead of two); `tail` marks those lanes.
 template <int D, bool PACK, typename VOp, typename Keep>
 __device__ inline void block_update(const float4_t& s, const uint32_t* kmw, const uint32_t* vmw, int first,
-                                    int nval, bool partial, float sq2, float c24, bool tail, Softmax& sm,
+                                    int nval, bool partial, float sq2, float kmul, float kk, float kv,
+                                    bool tail, Softmax& sm,
                                     float4_t* acc, VOp vpair, Keep keep) {
   constexpr int NB = D / 16;
   float x[4];
@@ -234,7 +256,7 @@ __device__ inline void block_update(const float4_t& s, const uint32_t* kmw, cons
     // log2e/sqrt(d) (s_k q.c + z_k sum(q)), with s holding q.c * 2^-24
     const _Float16 ks = __builtin_bit_cast(_Float16, (uint16_t)kmw[r]);
     const _Float16 kz = __builtin_bit_cast(_Float16, (uint16_t)(kmw[r] >> 16));
-    x[r] = (float)ks * (s[r] * c24) + (float)kz * sq2;
+    x[r] = (float)ks * (s[r] * kmul) + ((float)kz - kk * (float)ks) * sq2;
   }
   if (partial) {
 #pragma unroll
@@ -242,7 +264,7 @@ __device__ inline void block_update(const float4_t& s, const uint32_t* kmw, cons
       if (first + r >= nval) x[r] = -INFINITY;
   }
   keep(x);
-  const float pm = rows_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+  const float pm = rows_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]))) + kHead;
   if (__any(pm > sm.m)) {
     const float mn = pm > sm.m ? pm + kLazy : sm.m;
     const float alpha = __builtin_amdgcn_exp2f(sm.m - mn);
@@ -259,8 +281,8 @@ __device__ inline void block_update(const float4_t& s, const uint32_t* kmw, cons
     const _Float16 vs = __builtin_bit_cast(_Float16, (uint16_t)vmw[r]);
     const _Float16 vz = __builtin_bit_cast(_Float16, (uint16_t)(vmw[r] >> 16));
     sm.lsum += p;
-    sm.zsum += p * (float)vz;
-    const float pp = p * (float)vs;
+    sm.zsum += p * ((float)vz - kv * (float)vs);
+    const float pp = p * ((float)vs * kv);
     ph16[r] = (_Float16)pp;
     pl16[r] = (_Float16)(pp - (float)ph16[r]);
   }
@@ -286,7 +308,7 @@ __device__ inline void block_update(const float4_t& s, const uint32_t* kmw, cons
 // token i per step, the same 8 dims of q as its Q operand.
 template <int D, bool PACK, typename Keep>
 __device__ inline void compute_page(const PageRegs<D>& R, bool hi, int nval, const half8_t* qop, float sq2,
-                                    float c24, bool tail, int qg, Softmax& sm, float4_t* acc, Keep keep) {
+                                    float sl, bool tail, int qg, Softmax& sm, float4_t* acc, Keep keep) {
   constexpr int NS = D / 32, KW = PageRegs<D>::KW;
   if (hi) {
     // two accumulators halve the dependent chain of the q.c products
@@ -297,7 +319,7 @@ __device__ inline void compute_page(const PageRegs<D>& R, bool hi, int nval, con
       s1 = mfma32(cat8(u8x4(R.k[2 * ks + 2]), u8x4(R.k[2 * ks + 3])), qop[ks + 1], s1);
     }
     block_update<D, PACK>(
-        s0 + s1, R.km, R.vm, 4 * qg, nval, nval < kHiTokens, sq2, c24, tail, sm, acc,
+        s0 + s1, R.km, R.vm, 4 * qg, nval, nval < kHiTokens, sq2, kTwo24 * sl, 0.0f, 16.0f, tail, sm, acc,
         [&](int nb) {
           // block nb: pairs 2nb (tokens 0, 1) and 2nb + 1 (tokens 2, 3)
           const uint32_t w = R.v[nb >> 1];
@@ -317,7 +339,8 @@ __device__ inline void compute_page(const PageRegs<D>& R, bool hi, int nval, con
         s1 = mfma32(cat8(cat(nib2(w1, 0), nib2(w1, 4)), cat(nib2(w1, 8), nib2(w1, 12))), qop[ks + 1], s1);
       }
       block_update<D, PACK>(
-          s0 + s1, R.km + 4 * mb, R.vm + 4 * mb, 16 * mb + 4 * qg, nval, nval < 16 * (mb + 1), sq2, c24, tail,
+          s0 + s1, R.km + 4 * mb, R.vm + 4 * mb, 16 * mb + 4 * qg, nval, nval < 16 * (mb + 1), sq2, 16.0f * sl,
+          16.0f, 4.0f, tail,
           sm, acc,
           [&](int nb) {
             // block (nb, mb): pairs P = 2M, 2M + 1 with M = 2nb + mb, in word P / 8
@@ -447,7 +470,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
     sumq += __shfl_xor(sumq, 16, 64);
     sumq += __shfl_xor(sumq, 32, 64);
   }
-  const float sq2 = sumq * scale_log2, c24 = kTwo24 * scale_log2;
+  const float sq2 = sumq * scale_log2;
 
   Softmax sm{-INFINITY, 0.0f, 0.0f};
   float4_t acc[NB];
@@ -474,7 +497,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
         if (lane == 0) id_s[j] = R.id;
       }
       float* lgp = kLds ? lg_s + j * 32 * G : logits + ((int64_t)u * L + table_idx(j)) * 32 * G;
-      compute_page<D, PACK>(R, j < ph, valid(j), qop, sq2, c24, tail, qg, sm, acc, [&](int mb, const float* x) {
+      compute_page<D, PACK>(R, j < ph, valid(j), qop, sq2, scale_log2, tail, qg, sm, acc, [&](int mb, const float* x) {
         if (!SAVE || i >= G) return;
         const int t0 = 16 * mb + 4 * qg;
 #pragma unroll
@@ -537,13 +560,13 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
   __syncthreads();
   const int ncol = PACK ? 2 * G : G;  // columns that carry data
   if (i < ncol) {
-    // O = 2^24 acc + sum(p z_v) (the z_v term once per head: not in tail columns)
+    // O = acc + sum p (z_v - kv s_v) (the z term once per head: not in tail columns)
     const float M = sM[i];
     const float f = (M == -INFINITY || sm.m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sm.m - M);
     const float z = tail ? 0.0f : sm.zsum;
     // lane (i, qg), block nb: dims 16nb + 4qg .. +3 of column i
 #pragma unroll
-    for (int nb = 0; nb < NB; nb++) buf[wid][i * (D / 4) + 4 * nb + qg] = (acc[nb] * kTwo24 + z) * f;
+    for (int nb = 0; nb < NB; nb++) buf[wid][i * (D / 4) + 4 * nb + qg] = (acc[nb] + z) * f;
   }
   __syncthreads();
   const float* ob = (const float*)&buf[0][0];
