@@ -7,9 +7,9 @@ per KV head, importance scores Zipf(1.1) with a per-unit random permutation,
 alpha_h = 1.0, alpha_l = 0.2, W = 64, a pool of 1.25x the conservative need.
 
 A timed step is one decode step of the whole batch on the compacted cache:
-generation-step compaction (diffkv_compact STEP), then decode attention with
-the score update (diffkv_decode_attn, update_scores = 1; one kernel when each
-unit fits one workgroup).  The
+generation-step compaction, then decode attention with the score update, as
+one diffkv_decode_step call (plan kernel, then one kernel that commits each
+unit's step and attends over it when every unit is one workgroup).  The
 prompt side of the path (classification and prompt compaction) and the
 release are timed in the same run on the same caches and reported beside it.
 Caches rotate over several independent replicas (one per simulated layer) so
@@ -230,8 +230,9 @@ def main():
     print("[bench] warmup done", file=sys.stderr, flush=True)
 
     def full_step(s):
-        step_compact(s)
-        step_attn(s)
+        # compaction then attention with the score update, one library call
+        reps[s % R].decode_step(dec[s]["q"], seq_per_step[s], dec[s]["k_new"], dec[s]["v_new"],
+                                update_scores=1, out=out)
 
     # headline: K complete decode steps (compaction + attention with score update)
     total_ms = timed(full_step, args.warmup, args.steps)

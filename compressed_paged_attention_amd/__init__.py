@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libdiffkv.so")
 
 DIFFKV_OK, DIFFKV_E_INVALID, DIFFKV_E_WORKSPACE, DIFFKV_E_HIP = 0, 1, 2, 3
 ST_POOL_EXHAUSTED, ST_TABLE_OVERFLOW, ST_BAD_STATE = 1, 2, 4
-PROMPT, STEP, RELEASE, ATTN, ATTN_SCORES = 0, 1, 2, 3, 4
+PROMPT, STEP, RELEASE, ATTN, ATTN_SCORES, DECODE_STEP, DECODE_STEP_SCORES = 0, 1, 2, 3, 4, 5, 6
 PRUNE, LO, HI = 0, 1, 2
 
 
@@ -73,8 +73,9 @@ def lib() -> ctypes.CDLL:
                                      vp, sz, vp]
         L.diffkv_decode_attn.argtypes = [cfgp, poolp, i32, vp, vp, vp, vp, vp, i32, vp, sz, vp]
         L.diffkv_update_scores.argtypes = [cfgp, poolp, i32, vp, vp, vp, vp, sz, vp]
+        L.diffkv_decode_step.argtypes = [cfgp, poolp, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
         for f in ("diffkv_pool_init", "diffkv_state_init", "diffkv_classify", "diffkv_compact",
-                  "diffkv_decode_attn", "diffkv_update_scores"):
+                  "diffkv_decode_attn", "diffkv_update_scores", "diffkv_decode_step"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -186,6 +187,15 @@ def diffkv_update_scores(cfg: dict, pool: Pool, batch: int, page_table, tier_sta
            "diffkv_update_scores")
 
 
+def diffkv_decode_step(cfg: dict, pool: Pool, batch: int, seq_len, k_new, v_new, q, page_table, tier_state,
+                       out, update_scores: int, workspace, stream=None):
+    _check(lib().diffkv_decode_step(ctypes.byref(make_config(cfg)), ctypes.byref(pool.struct()), batch,
+                                    _ptr(seq_len), _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(page_table),
+                                    _ptr(tier_state), _ptr(out), int(update_scores), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream)),
+           "diffkv_decode_step")
+
+
 class DiffKVState:
     """All device buffers of one cache (pool, tables, workspaces) for `batch` slots."""
 
@@ -204,6 +214,8 @@ class DiffKVState:
         self.ws_compact = torch.empty(cws, dtype=torch.uint8, device=device)
         self.ws_attn = torch.zeros(diffkv_workspace_bytes(cfg, ATTN_SCORES, batch), dtype=torch.uint8,
                                    device=device)
+        self.ws_decode = torch.zeros(diffkv_workspace_bytes(cfg, DECODE_STEP_SCORES, batch), dtype=torch.uint8,
+                                     device=device)
         diffkv_pool_init(cfg, self.pool)
         diffkv_state_init(cfg, batch, self.page_table, self.tier_state)
 
@@ -236,6 +248,14 @@ class DiffKVState:
             out = torch.empty(self.batch, self.H * self.G, self.d, dtype=torch.float32, device=q.device)
         diffkv_decode_attn(self.cfg, self.pool, self.batch, q, self.page_table, self.tier_state, seq_len,
                            out, int(update_scores), self.ws_attn)
+        return out
+
+    def decode_step(self, q, seq_len, k_new, v_new, update_scores: int = 1, out=None):
+        """compact_step(seq_len, k_new, v_new) then decode_attn(q, seq_len), as one call."""
+        if out is None:
+            out = torch.empty(self.batch, self.H * self.G, self.d, dtype=torch.float32, device=q.device)
+        diffkv_decode_step(self.cfg, self.pool, self.batch, seq_len, k_new, v_new, q, self.page_table,
+                           self.tier_state, out, int(update_scores), self.ws_decode)
         return out
 
     def update_scores(self, seq_len):

@@ -75,6 +75,8 @@ size_t diffkv_workspace_bytes(const diffkv_config* cfg, int32_t op, int32_t batc
     case DIFFKV_RELEASE: return release_workspace(c, batch);
     case DIFFKV_ATTN: return attn_workspace(c, batch, false);
     case DIFFKV_ATTN_SCORES: return attn_workspace(c, batch, true);
+    case DIFFKV_DECODE_STEP: return align_up(step_workspace(c, batch), 256) + attn_workspace(c, batch, false);
+    case DIFFKV_DECODE_STEP_SCORES: return align_up(step_workspace(c, batch), 256) + attn_workspace(c, batch, true);
     default: return 0;
   }
 }
@@ -148,6 +150,24 @@ int diffkv_decode_attn(const diffkv_config* cfg, const diffkv_pool* pool, int32_
   if (!workspace || workspace_bytes < need) return DIFFKV_E_WORKSPACE;
   return rc(launch_attn(c, to_pool(pool), batch, q, page_table, tier_state, seq_len, out, update_scores,
                         workspace, (hipStream_t)stream));
+}
+
+int diffkv_decode_step(const diffkv_config* cfg, const diffkv_pool* pool, int32_t batch, const int32_t* seq_len,
+                       const uint16_t* k_new, const uint16_t* v_new, const uint16_t* q, int32_t* page_table,
+                       int32_t* tier_state, float* out, int32_t update_scores, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (!cfg_ok(cfg) || !pool_ok(cfg, pool) || batch < 0) return DIFFKV_E_INVALID;
+  if (batch > 0 && (!seq_len || !k_new || !v_new || !q || !page_table || !tier_state || !out))
+    return DIFFKV_E_INVALID;
+  if ((int64_t)batch * cfg->num_kv_heads > 65535) return DIFFKV_E_INVALID;
+  if (update_scores < 0 || update_scores > 2) return DIFFKV_E_INVALID;
+  const Cfg c = to_cfg(cfg);
+  if (c.W < 2) return DIFFKV_E_INVALID;
+  const size_t ws_step = align_up(step_workspace(c, batch), 256);
+  const size_t need = ws_step + attn_workspace(c, batch, update_scores != 0);
+  if (!workspace || workspace_bytes < need) return DIFFKV_E_WORKSPACE;
+  return rc(launch_decode_step(c, to_pool(pool), batch, seq_len, k_new, v_new, q, page_table, tier_state, out,
+                               update_scores, workspace, (uint8_t*)workspace + ws_step, (hipStream_t)stream));
 }
 
 int diffkv_update_scores(const diffkv_config* cfg, const diffkv_pool* pool, int32_t batch, const int32_t* page_table,

@@ -415,6 +415,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
   }
 
   auto table_idx = [&](int j) { return j < ph ? j : L - 1 - (j - ph); };
+  auto page_id = [&](int tix) { return row[tix]; };
   auto valid = [&](int j) {
     return j < ph ? min(kHiTokens, nh - kHiTokens * j) : min(kLoTokens, nl - kLoTokens * (j - ph));
   };
@@ -424,7 +425,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
   // pool (the load stays in bounds) and zeroes the unit's result
   auto fetch = [&](PageRegs<D>& R, int jj) {
     jj = min(jj, p1 - 1);  // past the end: reload the last page (unused)
-    int32_t id = row[table_idx(jj)];  // uniform index: scalar load
+    int32_t id = page_id(table_idx(jj));  // uniform index: scalar load
     badid |= (uint32_t)(id < 0 || id >= P);
     id = min(max(id, 0), (int32_t)(P - 1));
     R.id = id;
@@ -642,7 +643,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
               float mx = 0.0f;
               for (int g = 0; g < G; g++) mx = fmaxf(mx, __builtin_amdgcn_exp2f(lg[g] - sM[g]) * sI[g]);
               add[e] = mx;
-              uint8_t* pg = pages + (int64_t)row[table_idx(j)] * page_bytes;
+              uint8_t* pg = pages + (int64_t)page_id(table_idx(j)) * page_bytes;
               sc[e] = (float*)(pg + (j < ph ? sh.sc : sl.sc) + 4 * t);
               pp[e] = (const int32_t*)(pg + (j < ph ? sh.ps : sl.ps) + 4 * t);
             }
@@ -783,7 +784,7 @@ hipError_t launch_attn(const Cfg& c, const Pool& p, int batch, const uint16_t* q
   const int kmode = mode == 1 && S > 1 ? 2 : mode;
   // head and tail of the weights share one matrix instruction when 2G <= 16
   const bool pack = 2 * c.G <= 16;
-#define DKV_ATTN(D, M, PK)                                                                             \
+#define DKV_ATTN(D, M, PK)                                                                              \
   attn_kernel<D, M, PK><<<grid, block, 0, s>>>(c.H, c.G, c.L, S, p.P, p.page_bytes, scale_log2, q, table, \
                                                state, seq_len, p.pages, out, w.part, w.ml, w.logits, p.status)
 #define DKV_ATTN_D(D)                                    \
@@ -817,6 +818,14 @@ hipError_t launch_attn(const Cfg& c, const Pool& p, int batch, const uint16_t* q
     if (mode == 1) return launch_scores(c, p, batch, table, state, seq_len, ws, s);
   }
   return hipSuccess;
+}
+
+hipError_t launch_decode_step(const Cfg& c, const Pool& p, int batch, const int32_t* seq_len, const uint16_t* k,
+                              const uint16_t* v, const uint16_t* q, int32_t* table, int32_t* state, float* out,
+                              int mode, void* ws_step, void* ws_attn, hipStream_t s) {
+  hipError_t e = launch_step(c, p, batch, seq_len, k, v, table, state, ws_step, s);
+  if (e != hipSuccess) return e;
+  return launch_attn(c, p, batch, q, table, state, seq_len, out, mode, ws_attn, s);
 }
 
 }  // namespace dkv

@@ -40,6 +40,12 @@ size_t step_workspace(const Cfg& c, int batch);
 hipError_t launch_step(const Cfg& c, const Pool& p, int batch, const int32_t* seq_len,
                        const uint16_t* k, const uint16_t* v, int32_t* table, int32_t* state,
                        void* ws, hipStream_t s);
+// the two halves of launch_step
+hipError_t launch_step_plan(const Cfg& c, const Pool& p, int batch, const int32_t* seq_len,
+                            const int32_t* table, const int32_t* state, void* ws, hipStream_t s);
+hipError_t launch_step_commit(const Cfg& c, const Pool& p, int batch, const int32_t* seq_len,
+                              const uint16_t* k, const uint16_t* v, int32_t* table, int32_t* state,
+                              void* ws, hipStream_t s);
 size_t release_workspace(const Cfg& c, int batch);
 hipError_t launch_release(const Cfg& c, const Pool& p, int batch, const uint8_t* mask,
                           int32_t* table, int32_t* state, void* ws, hipStream_t s);
@@ -53,6 +59,11 @@ hipError_t launch_attn(const Cfg& c, const Pool& p, int batch, const uint16_t* q
                        float* out, int mode, void* ws, hipStream_t s);
 hipError_t launch_scores(const Cfg& c, const Pool& p, int batch, const int32_t* table,
                          const int32_t* state, const int32_t* seq_len, void* ws, hipStream_t s);
+// generation step then attention for the same step
+hipError_t launch_decode_step(const Cfg& c, const Pool& p, int batch, const int32_t* seq_len,
+                              const uint16_t* k, const uint16_t* v, const uint16_t* q, int32_t* table,
+                              int32_t* state, float* out, int mode, void* ws_step, void* ws_attn,
+                              hipStream_t s);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

@@ -1,0 +1,314 @@
+// dkv_step.hpp -- generation-step commit of one unit, shared by the step
+// commit kernel and the fused step + attention kernel.
+//
+// Step workspace: a header (pointer snapshot, commit flag), per-unit plan
+// records and one demand word per unit (see step.hip for the plan).
+#pragma once
+
+#include "dkv_common.hpp"
+#include "dkv_launch.hpp"
+
+namespace dkv {
+
+// Per-unit plan record and a compact demand word per unit:
+//   nf[u] = need tier (bits 0-1: 0 none, 1 low, 2 high) | kActive | status flags << 8
+constexpr int kSRec = 8;
+enum { S_NEWHI = 0, S_HIAPP, S_LOSRC, S_LOSLOT, S_LOAPP, S_PAGE };
+enum { SH_COMMIT = 0, SH_START, SH_END, SH_D };
+constexpr int32_t kActive = 4;
+// Up to this many units every commit workgroup redoes the unit-order prefix
+// sum over the demand words itself (no coordination kernel in between).
+constexpr int64_t kDirectUnits = 2048;
+
+struct StepWs {
+  int64_t* hdr;
+  int32_t* rec;
+  int32_t* nf;
+};
+
+inline StepWs step_carve(const Cfg& c, int batch, void* ws) {
+  const size_t U = (size_t)batch * c.H;
+  uint8_t* p = (uint8_t*)ws;
+  StepWs w;
+  w.hdr = (int64_t*)p;
+  p += align_up(16 * sizeof(int64_t), 256);
+  w.rec = (int32_t*)p;
+  p += align_up(U * kSRec * sizeof(int32_t), 256);
+  w.nf = (int32_t*)p;
+  return w;
+}
+
+// ---------------------------------------------------------------------------
+// commit: phase 1 loads everything the unit needs, phase 2 quantizes and
+// edits LDS images of the destination pages, phase 3 stores.  No barrier
+// waits on an outstanding global store.
+// ---------------------------------------------------------------------------
+
+// LDS field update (other fields of the word may be edited concurrently)
+__device__ inline void lds_put(uint32_t* img, int byte, int shift, int bits, uint32_t val) {
+  const int sh = 8 * (byte & 3) + shift;
+  const uint32_t mask = ((1u << bits) - 1u) << sh;
+  atomicAnd(&img[byte >> 2], ~mask);
+  atomicOr(&img[byte >> 2], (val << sh) & mask);
+}
+
+// One token written into one page through an LDS image of that page.
+struct TokWrite {
+  bool on;     // this token is written
+  bool hi;     // destination tier
+  bool fresh;  // the page is new: the whole page is written (zeros elsewhere)
+  int idx;     // slot inside the page
+  int32_t id;  // page id
+};
+
+// Phase 1: a fresh page's image is zeroed; an existing page's image gets the
+// V segment (the only one shared between tokens at byte level) and a zeroed
+// K range for the token.
+template <int D>
+__device__ void img_load(uint32_t* img, const TokWrite& t, const uint8_t* pages, int page_bytes) {
+  if (!t.on) return;
+  const Seg sg = tier_seg(D, t.hi);
+  if (t.fresh) {
+    for (int w = threadIdx.x; w < page_bytes / 4; w += blockDim.x) img[w] = 0u;
+  } else {
+    const uint4* src = (const uint4*)(pages + (int64_t)t.id * page_bytes + sg.vc);
+    uint4* dst = (uint4*)(img + sg.vc / 4);
+    for (int c = threadIdx.x; c < (sg.vm - sg.vc) / 16; c += blockDim.x) dst[c] = src[c];
+    const int kb = t.idx * D * sg.kbits / 8;
+    for (int w = threadIdx.x; w < D * sg.kbits / 32; w += blockDim.x) img[kb / 4 + w] = 0u;
+  }
+}
+
+// Phase 2: the token's codes (dim threadIdx.x < D), metadata, score, position.
+template <int D>
+__device__ void img_token(uint32_t* img, const TokWrite& t, uint32_t ck, uint32_t cv, uint32_t kmeta,
+                          uint32_t vmeta, float score, int32_t pos) {
+  if (!t.on) return;
+  const Seg sg = tier_seg(D, t.hi);
+  if (threadIdx.x < D) {
+    int byte, shift;
+    k_field(D, t.hi, t.idx, threadIdx.x, byte, shift);
+    lds_put(img, byte, shift, sg.kbits, ck);
+    v_field(D, t.hi, t.idx, threadIdx.x, byte, shift);
+    lds_put(img, byte, shift, sg.vbits, cv);
+  }
+  if (threadIdx.x == 0) {
+    img[sg.km / 4 + t.idx] = kmeta;
+    img[sg.vm / 4 + t.idx] = vmeta;
+    img[sg.sc / 4 + t.idx] = __float_as_uint(score);
+    img[sg.ps / 4 + t.idx] = (uint32_t)pos;
+  }
+}
+
+// Phase 3: a fresh page is written whole; otherwise the token's K range, the
+// V segment and the token's four words.
+template <int D>
+__device__ void img_store(const uint32_t* img, const TokWrite& t, uint8_t* pages, int page_bytes) {
+  if (!t.on) return;
+  const Seg sg = tier_seg(D, t.hi);
+  uint8_t* pg = pages + (int64_t)t.id * page_bytes;
+  if (t.fresh) {
+    for (int c = threadIdx.x; c < page_bytes / 16; c += blockDim.x) ((uint4*)pg)[c] = ((const uint4*)img)[c];
+    return;
+  }
+  const int kb = t.idx * D * sg.kbits / 8, kn = D * sg.kbits / 128;  // 16-byte chunks
+  const int vn = (sg.vm - sg.vc) / 16;
+  for (int c = threadIdx.x; c < kn + vn + 4; c += blockDim.x) {
+    if (c < kn) {
+      ((uint4*)(pg + kb))[c] = ((const uint4*)(img + kb / 4))[c];
+    } else if (c < kn + vn) {
+      ((uint4*)(pg + sg.vc))[c - kn] = ((const uint4*)(img + sg.vc / 4))[c - kn];
+    } else {
+      const int seg = c - kn - vn;
+      const int off = (seg == 0 ? sg.km : seg == 1 ? sg.vm : seg == 2 ? sg.sc : sg.ps) + 4 * t.idx;
+      *(uint32_t*)(pg + off) = img[off / 4];
+    }
+  }
+}
+
+// min and max of the D values held by threads 0..D-1, for n vectors at once
+template <int D, int NV>
+__device__ void block_minmax(float (&mn)[NV], float (&mx)[NV], float* red) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  constexpr int nw = (D + 63) / 64;
+#pragma unroll
+  for (int v = 0; v < NV; v++) {
+    if (tid >= D) {
+      mn[v] = INFINITY;
+      mx[v] = -INFINITY;
+    }
+    mn[v] = wave_min(mn[v]);
+    mx[v] = wave_max(mx[v]);
+  }
+  if (lane == 0 && wid < nw) {
+#pragma unroll
+    for (int v = 0; v < NV; v++) {
+      red[(2 * v) * nw + wid] = mn[v];
+      red[(2 * v + 1) * nw + wid] = mx[v];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int v = 0; v < NV; v++) {
+    mn[v] = red[(2 * v) * nw];
+    mx[v] = red[(2 * v + 1) * nw];
+    for (int w = 1; w < nw; w++) {
+      mn[v] = fminf(mn[v], red[(2 * v) * nw + w]);
+      mx[v] = fmaxf(mx[v], red[(2 * v + 1) * nw + w]);
+    }
+  }
+}
+
+// LDS scratch of commit_unit, in 32-bit words: two page images plus misc.
+template <int D>
+constexpr int commit_lds_words() {
+  return 2 * (page_bytes_for(D) / 4) + 64;
+}
+
+// Result of commit_unit: whether this unit's step was committed, and its
+// tier state afterwards (as written to tier_state).
+struct UnitState {
+  bool committed;
+  int nh, nl, ph, pl;
+  int new_tix;   // table index of a page this step added (-1: none)
+  int new_page;  // its id
+};
+
+// The commit of unit u (one workgroup, any size >= D threads).  DIRECT: the
+// workgroup recomputes the unit-order prefix sum of page demand from the
+// demand words (all-or-nothing check included) and workgroup 0 advances the
+// allocation pointer; otherwise the coordination kernel's result is read.
+// `sm` is LDS scratch of commit_lds_words<D>() words, 16-byte aligned.
+template <int D, bool DIRECT>
+__device__ UnitState commit_unit(int64_t u, int H, int L, int64_t U, int64_t P, int page_bytes,
+                                 const int32_t* __restrict__ seq_len, const uint16_t* __restrict__ k_new,
+                                 const uint16_t* __restrict__ v_new, const int64_t* __restrict__ hdr,
+                                 const int32_t* __restrict__ rec, const int32_t* __restrict__ nf,
+                                 const int32_t* __restrict__ list, int32_t* __restrict__ table,
+                                 int32_t* __restrict__ state, uint8_t* pages, uint64_t* ptr, uint32_t* status,
+                                 uint32_t* sm) {
+  constexpr Seg sh = tier_seg(D, true);
+  constexpr int kPageWords = page_bytes_for(D) / 4;
+  const int tid = threadIdx.x;
+  const int b = (int)u / H, h = (int)u % H;  // u < 2^31: 32-bit division
+  const int32_t* s4c = state + 4 * u;
+  UnitState res{false, s4c[0], s4c[1], s4c[2], s4c[3], -1, -1};
+  // ---- phase 1: loads ----
+  const int32_t wu = nf[u];
+  const int32_t* R = rec + u * kSRec;
+  int32_t* row = table + u * L;
+  int32_t* s4 = state + 4 * u;
+  const int64_t rowi = ((int64_t)b * H + h) * D + tid;
+  float xk_new = tid < D ? h2f(k_new[rowi]) : 0.0f;
+  float xv_new = tid < D ? h2f(v_new[rowi]) : 0.0f;
+  int32_t page = -1;
+  if constexpr (DIRECT) {
+    int* lds = (int*)(sm + 2 * (page_bytes_for(D) / 4));  // 16 ints
+    int64_t& s_off = *(int64_t*)(lds + 16);
+    uint32_t& s_fl = *(uint32_t*)(lds + 18);
+    if (tid == 0) s_fl = 0;
+    int64_t total = 0;
+    uint32_t fl = 0;
+    for (int64_t base = 0; base < U; base += blockDim.x) {
+      const int64_t x = base + tid;
+      const int32_t w = x < U ? nf[x] : 0;
+      fl |= (uint32_t)w >> 8;
+      int t;
+      const int excl = block_excl_count((w & 3) != 0, lds, t);
+      if (x == u) s_off = total + excl;
+      total += t;
+    }
+    if (fl) atomicOr(&s_fl, fl);
+    __syncthreads();
+    const int64_t start = hdr[SH_START], end = hdr[SH_END];
+    uint32_t st = s_fl;
+    if (!st && total > end - start) st = kStExhausted;
+    if (u == 0 && tid == 0) {
+      if (st) atomicOr(status, st);
+      else ptr[0] = (uint64_t)(start + total);
+    }
+    if (st || !(wu & kActive)) return res;
+    if (wu & 3) page = list[(uint64_t)(start + s_off) % (uint64_t)P];
+  } else {
+    if (!hdr[SH_COMMIT] || !(wu & kActive)) return res;
+    page = R[S_PAGE];
+  }
+  const int need = wu & 3;
+  const int nh = s4[0], nl = s4[1], ph = s4[2], pl = s4[3];
+  const int new_hi = R[S_NEWHI], lo_src = R[S_LOSRC], lo_slot = R[S_LOSLOT];
+  const int hi_app = R[S_HIAPP], lo_app = R[S_LOAPP];
+  if (need && (page < 0 || page >= P)) {
+    if (tid == 0) atomicOr(status, kStBadState);
+    return res;
+  }
+  // destinations: the new token's high slot; the requantized token's low slot
+  TokWrite th{true, true, need == kTierHi, new_hi & 15,
+              need == kTierHi ? page : row[new_hi >> 4]};
+  TokWrite tl{lo_src >= 0, false, need == kTierLo, lo_slot & 31,
+              lo_src < 0 ? 0 : (need == kTierLo ? page : row[L - 1 - (lo_slot >> 5)])};
+  uint32_t* img_h = sm;
+  uint32_t* img_l = sm + kPageWords;
+  float* red = (float*)(sm + 2 * kPageWords + 20);  // 16 floats
+  img_load<D>(img_h, th, pages, page_bytes);
+  img_load<D>(img_l, tl, pages, page_bytes);
+  // the requantized token's dequantized values (read before anything is
+  // written: its high slot may be the new token's)
+  float xk_rq = 0.0f, xv_rq = 0.0f, sc_rq = 0.0f;
+  int32_t pos_rq = 0;
+  if (tl.on) {
+    const uint8_t* src = pages + (int64_t)row[lo_src >> 4] * page_bytes;
+    const int si = lo_src & 15;
+    const uint32_t km = *(const uint32_t*)(src + sh.km + 4 * si);
+    const uint32_t vm = *(const uint32_t*)(src + sh.vm + 4 * si);
+    sc_rq = *(const float*)(src + sh.sc + 4 * si);
+    pos_rq = *(const int32_t*)(src + sh.ps + 4 * si);
+    if (tid < D) {
+      int byte, shift;
+      k_field(D, true, si, tid, byte, shift);
+      xk_rq = dequant(h2f((uint16_t)km), h2f((uint16_t)(km >> 16)), ((uint32_t)src[byte] >> shift) & 0xFFu);
+      v_field(D, true, si, tid, byte, shift);
+      xv_rq = dequant(h2f((uint16_t)vm), h2f((uint16_t)(vm >> 16)), ((uint32_t)src[byte] >> shift) & 0xFu);
+    }
+  }
+  const int32_t N = seq_len[b];
+  __syncthreads();  // LDS images loaded (no global store is outstanding)
+  // ---- phase 2: quantize, edit the images ----
+  float mn[4] = {xk_new, xv_new, xk_rq, xv_rq}, mx[4] = {xk_new, xv_new, xk_rq, xv_rq};
+  block_minmax<D, 4>(mn, mx, red);
+  {
+    const Seg sg = tier_seg(D, true);
+    uint16_t ks16, kz16, vs16, vz16;
+    float ks, kz, vs, vz;
+    codec_params(mn[0], mx[0], sg.kbits, ks16, kz16, ks, kz);
+    codec_params(mn[1], mx[1], sg.vbits, vs16, vz16, vs, vz);
+    img_token<D>(img_h, th, codec_code(xk_new, ks, kz, sg.kbits), codec_code(xv_new, vs, vz, sg.vbits),
+                 (uint32_t)ks16 | ((uint32_t)kz16 << 16), (uint32_t)vs16 | ((uint32_t)vz16 << 16), 0.0f, N);
+  }
+  if (tl.on) {
+    const Seg sg = tier_seg(D, false);
+    uint16_t ks16, kz16, vs16, vz16;
+    float ks, kz, vs, vz;
+    codec_params(mn[2], mx[2], sg.kbits, ks16, kz16, ks, kz);
+    codec_params(mn[3], mx[3], sg.vbits, vs16, vz16, vs, vz);
+    img_token<D>(img_l, tl, codec_code(xk_rq, ks, kz, sg.kbits), codec_code(xv_rq, vs, vz, sg.vbits),
+                 (uint32_t)ks16 | ((uint32_t)kz16 << 16), (uint32_t)vs16 | ((uint32_t)vz16 << 16), sc_rq,
+                 pos_rq);
+  }
+  __syncthreads();
+  // ---- phase 3: stores ----
+  img_store<D>(img_h, th, pages, page_bytes);
+  img_store<D>(img_l, tl, pages, page_bytes);
+  res = UnitState{true, nh + hi_app, nl + lo_app, ph + (need == kTierHi), pl + (need == kTierLo),
+                  need == kTierHi ? ph : (need == kTierLo ? L - 1 - pl : -1), page};
+  if (tid == 0) {
+    if (need == kTierHi) row[ph] = page;
+    if (need == kTierLo) row[L - 1 - pl] = page;
+    s4[0] = res.nh;
+    s4[1] = res.nl;
+    s4[2] = res.ph;
+    s4[3] = res.pl;
+  }
+  return res;
+}
+
+}  // namespace dkv

@@ -74,7 +74,15 @@ typedef struct {
 
 enum { DIFFKV_OK = 0, DIFFKV_E_INVALID = 1, DIFFKV_E_WORKSPACE = 2, DIFFKV_E_HIP = 3 };
 enum { DIFFKV_ST_POOL_EXHAUSTED = 1u, DIFFKV_ST_TABLE_OVERFLOW = 2u, DIFFKV_ST_BAD_STATE = 4u };
-enum { DIFFKV_PROMPT = 0, DIFFKV_STEP = 1, DIFFKV_RELEASE = 2, DIFFKV_ATTN = 3, DIFFKV_ATTN_SCORES = 4 };
+enum {
+  DIFFKV_PROMPT = 0,
+  DIFFKV_STEP = 1,
+  DIFFKV_RELEASE = 2,
+  DIFFKV_ATTN = 3,
+  DIFFKV_ATTN_SCORES = 4,
+  DIFFKV_DECODE_STEP = 5,        /* diffkv_decode_step, update_scores = 0 */
+  DIFFKV_DECODE_STEP_SCORES = 6  /* diffkv_decode_step, update_scores = 1 or 2 */
+};
 
 /* Bytes of one unified page (six segments, "Memory management"): 3584 at
  * d = 128, 2048 at d = 64; -1 for an invalid config. */
@@ -177,6 +185,24 @@ int diffkv_decode_attn(const diffkv_config* cfg, const diffkv_pool* pool, int32_
                        const int32_t* tier_state, const int32_t* seq_len, float* out,
                        int32_t update_scores, void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/* One decode step: diffkv_compact(DIFFKV_STEP) followed by
+ * diffkv_decode_attn on the updated cache with the same seq_len, as one call
+ * ("Implementation": the compactor runs after K/V are computed and before the
+ * attention kernel).  Results, status bits and all-or-nothing behaviour are
+ * those of the two calls in sequence (an aborted step leaves the cache as it
+ * was and the attention runs on it).
+ *  seq_len  int32 [batch]: length before this step's token (= position of
+ *           the query token); <= 0 marks an inactive request
+ *  k_new, v_new fp16 [batch, H, d]; q fp16 [batch, H*G, d]; out fp32
+ *  workspace: diffkv_workspace_bytes(DIFFKV_DECODE_STEP[_SCORES]); with
+ *           update_scores = 2 it carries the logits to diffkv_update_scores
+ *           at byte offset diffkv_workspace_bytes(DIFFKV_STEP) rounded up to
+ *           256 (pass that sub-buffer). */
+int diffkv_decode_step(const diffkv_config* cfg, const diffkv_pool* pool, int32_t batch,
+                       const int32_t* seq_len, const uint16_t* k_new, const uint16_t* v_new,
+                       const uint16_t* q, int32_t* page_table, int32_t* tier_state, float* out,
+                       int32_t update_scores, void* workspace, size_t workspace_bytes, void* stream);
 
 /* The score update of a preceding diffkv_decode_attn(update_scores = 2) call
  * with the same arguments and workspace (policy reading of the notes' stored

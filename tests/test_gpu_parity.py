@@ -86,6 +86,21 @@ class Pair:
             resync_scores(self.g, self.o)
         return err
 
+    def decode_step(self, seq, kn, vn, q, update, what="decode step"):
+        """diffkv_decode_step against the oracle's STEP followed by attention."""
+        self.o.compact_step(seq, kn, vn)
+        out_o = self.o.decode_attn(q, seq, update_scores=update)
+        out_g = self.g.decode_step(torch.from_numpy(q).to(dev), torch.from_numpy(seq).to(dev),
+                                   torch.from_numpy(kn).to(dev), torch.from_numpy(vn).to(dev),
+                                   update_scores=1 if update else 0)
+        torch.cuda.synchronize()
+        assert_state_equal(self.g, self.o, pages=not update, what=what)
+        err = assert_attn_close(out_g, out_o, what)
+        if update:
+            assert_scores_close(self.g, self.o, what)
+            resync_scores(self.g, self.o)
+        return err
+
     def release(self, mask, what="release"):
         self.o.release(mask)
         self.g.release(torch.from_numpy(np.asarray(mask, np.uint8)).to(dev))
@@ -306,6 +321,49 @@ def test_fused_scores_large_units(dk, orc):
         p.step(seq, dec["k_new"].numpy(), dec["v_new"].numpy(), f"step {step}")
         p.attend(dec["q"].numpy(), seq, True, f"attn {step}")
         seq = seq + 1
+
+
+@pytest.mark.parametrize("batch,H,update", [(32, 8, True), (32, 8, False), (3, 4, True)])
+def test_decode_step_entry(dk, orc, batch, H, update):
+    """diffkv_decode_step (STEP then attention in one call): the fused kernel
+    when every unit is one split (32 x 8 units), the separate kernels when
+    not (3 x 4 units); lengths put steps on page boundaries."""
+    from workloads import synth
+    cfg = _medium_cfg("llama3_8b", num_kv_heads=H, batch=batch, max_seq_len=1300)
+    assert (dk.diffkv_attn_splits(cfg, batch) == 1) == (batch * H >= 256)
+    g = torch.Generator().manual_seed(41)
+    lens = (torch.randint(4, 70, (batch,), generator=g) * 16 - torch.randint(0, 2, (batch,), generator=g))
+    lens = lens.to(torch.int64)
+    pr = synth.make_prompt(cfg, lens=lens)
+    cu = pr["cu_seqlens"].numpy()
+    P = int(sum(-(-int(n) // 16) for n in lens) * H * 1.1) + 64
+    p = Pair(dk, orc, cfg, batch, P, int(cu[-1]))
+    p.prompt(cu, pr["k"].numpy(), pr["v"].numpy(), pr["scores"].numpy())
+    seq = lens.numpy().astype(np.int32)
+    for step in range(4):
+        dec = synth.make_decode(cfg, step)
+        _say("  decode step", step)
+        p.decode_step(seq, dec["k_new"].numpy(), dec["v_new"].numpy(), dec["q"].numpy(), update,
+                      f"decode step {step}")
+        seq = seq + 1
+    check_pool_invariants(orc, p.o)
+
+
+def test_decode_step_exhausted_pool(dk, orc):
+    """A step that cannot get its page commits nothing; the attention still
+    runs on the unchanged cache (as the two separate calls would)."""
+    cfg = dict(head_dim=64, num_kv_heads=1, gqa_group=2, max_seq_len=100, window=64,
+               alpha_h=1.0, alpha_l=0.2)
+    rng = np.random.default_rng(6)
+    N = 32
+    k = rng.standard_normal((N, 1, 64)).astype(np.float16).view(np.uint16)
+    sc = np.zeros((1, N), np.float32)
+    p = Pair(dk, orc, cfg, 1, 2, N)
+    p.prompt(np.array([0, N]), k, k, sc)
+    kn = k[:1].reshape(1, 1, 64).copy()
+    q = rng.standard_normal((1, 2, 64)).astype(np.float16).view(np.uint16)
+    p.decode_step(np.array([N], np.int32), kn, kn, q, True, "exhausted decode step")
+    assert int(p.o.status[0]) == orc.ST_POOL_EXHAUSTED
 
 
 def test_deterministic_replay(dk, orc):
