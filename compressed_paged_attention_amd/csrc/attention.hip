@@ -39,6 +39,7 @@
 
 #include "dkv_common.hpp"
 #include "dkv_launch.hpp"
+#include "dkv_step.hpp"
 
 namespace dkv {
 
@@ -359,9 +360,15 @@ constexpr int kLdsWords = 16384;
 
 // MODE 0: attention; 1: attention + score update in the same workgroup (one
 // split only); 2: attention keeping logits (score update later).
+// Policy parameters for the next step's plan (made by the fused score update).
+struct PolicyArgs {
+  int W, S_max, lo_en;
+  float ah, al;
+};
+
 template <int D, int MODE, bool PACK>
 __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int S, int64_t P, int page_bytes,
-                                                        float scale_log2, const uint16_t* __restrict__ q,
+                                                        PolicyArgs pa, float scale_log2, const uint16_t* __restrict__ q,
                                                         const int32_t* __restrict__ table,
                                                         const int32_t* __restrict__ state,
                                                         const int32_t* __restrict__ seq_len, uint8_t* pages,
@@ -598,8 +605,30 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
     }
     if (MODE == 1) {
       // score update: every retained token other than the query's own
-      // (position seq_len) adds max over the group of its softmax weight
+      // (position seq_len) adds max over the group of its softmax weight.
+      // With every score sum of the unit in hand, the pass also plans the
+      // next generation step (length N + 1) and leaves the plan in the
+      // unit's first high page, so that step needs no scan.
       const Seg sh = tier_seg(D, true), sl = tier_seg(D, false);
+      const int64_t N1 = (int64_t)N + 1, tc1 = N1 - pa.W;
+      __shared__ int s_tc;
+      __shared__ float s_tcsum;
+      __shared__ Cand cw[2][kWaves];
+      if (tid == 0) s_tc = -1;
+      __syncthreads();
+      Cand bh{0.0f, kNoPos, 0}, bl{0.0f, kNoPos, 0};
+      auto consider = [&](int j, int t, int32_t pos, float score) {
+        if (j < ph) {
+          const int ls = 16 * j + t;
+          if (pos == tc1) {  // positions are unique: one writer
+            s_tc = ls;
+            s_tcsum = score;
+          }
+          if (pos <= tc1) bh = min_imp(bh, Cand{score, pos, ls}, N1);
+        } else {
+          bl = min_imp(bl, Cand{score, pos, 32 * (j - ph) + t}, N1);
+        }
+      };
       if (lg_lds) {
         // everything is in LDS: the pass only stores
         float mg[16], ig[16];
@@ -622,7 +651,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
             for (int g = 0; g < 16; g++)
               if (g < G) mx = fmaxf(mx, __builtin_amdgcn_exp2f(lg[g] - mg[g]) * ig[g]);
             uint8_t* pg = pages + (int64_t)id_s[j] * page_bytes;
-            *(float*)(pg + (j < ph ? sh.sc : sl.sc) + 4 * t) = osc_s[x] + mx;
+            const float ns = osc_s[x] + mx;
+            *(float*)(pg + (j < ph ? sh.sc : sl.sc) + 4 * t) = ns;
+            consider(j, t, pos_s[x], ns);
           }
         }
       } else {
@@ -656,7 +687,42 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
           }
 #pragma unroll
           for (int e = 0; e < kU; e++)
-            if (sc[e] && pos[e] < N) *sc[e] = old[e] + add[e];
+            if (sc[e] && pos[e] < N) {
+              const int x = x0 + e * blockDim.x;
+              *sc[e] = old[e] + add[e];
+              consider(x >> 5, x & 31, pos[e], old[e] + add[e]);
+            }
+        }
+      }
+      // the unit's least important candidates: wave butterflies, then the
+      // waves' results in lanes 0..7 of wave 0
+      bh = wave_argmin(bh, N1);
+      bl = wave_argmin(bl, N1);
+      if (lane == 0) {
+        cw[0][wid] = bh;
+        cw[1][wid] = bl;
+      }
+      __syncthreads();
+      static_assert(kWaves == 8, "eight wave candidates");
+      if (wid == 0) {
+        bh = cw[0][lane & 7];
+        bl = cw[1][lane & 7];
+        argmin_step<0>(bh, N1);
+        argmin_step<1>(bh, N1);
+        argmin_step<2>(bh, N1);
+        argmin_step<0>(bl, N1);
+        argmin_step<1>(bl, N1);
+        argmin_step<2>(bl, N1);
+        const int tcs = s_tc;
+        // a record only where the next step's plan kernel would accept the state
+        if (lane == 0 && ph >= 1 && nh + nl <= N1 && !(tc1 >= 0 && tcs < 0)) {
+          const Plan pn = plan_decide(N1, pa.W, pa.S_max, pa.lo_en, (double)pa.ah, (double)pa.al, nh, nl, ph, pl,
+                                      L, tcs, s_tcsum, bh, bl);
+          uint32_t rw[kRecWords];
+          plan_rec_fill(rw, N1, nh, nl, ph, pl, pn);
+          uint32_t* dst = (uint32_t*)(pages + (int64_t)page_id(0) * page_bytes + plan_rec_off<D>());
+#pragma unroll
+          for (int k = 0; k < kRecWords; k++) dst[k] = rw[k];
         }
       }
     }
@@ -726,6 +792,8 @@ __global__ __launch_bounds__(256) void score_kernel(int H, int G, int L, int S, 
   const int N = seq_len[b];
   if (N <= 0 || nh + nl == 0 || !state_ok(nh, nl, ph, pl, L)) return;
   if (!unit_ids(ph, pl, L, P, row)) return;
+  // the unit's scores change here: a plan record no longer applies
+  if (split == 0 && tid == 0 && ph >= 1) *(uint32_t*)(pages + (int64_t)row[0] * page_bytes + plan_rec_off<D>()) = 0u;
   __shared__ float sM[16], sI[16];
   if (tid < G) {
     sM[tid] = ml[(u * G + tid) * 2 + 0];
@@ -784,9 +852,11 @@ hipError_t launch_attn(const Cfg& c, const Pool& p, int batch, const uint16_t* q
   const int kmode = mode == 1 && S > 1 ? 2 : mode;
   // head and tail of the weights share one matrix instruction when 2G <= 16
   const bool pack = 2 * c.G <= 16;
+  const PolicyArgs pa{c.W, c.S_max, c.lo_en, c.ah, c.al};
 #define DKV_ATTN(D, M, PK)                                                                              \
-  attn_kernel<D, M, PK><<<grid, block, 0, s>>>(c.H, c.G, c.L, S, p.P, p.page_bytes, scale_log2, q, table, \
-                                               state, seq_len, p.pages, out, w.part, w.ml, w.logits, p.status)
+  attn_kernel<D, M, PK><<<grid, block, 0, s>>>(c.H, c.G, c.L, S, p.P, p.page_bytes, pa, scale_log2, q,     \
+                                               table, state, seq_len, p.pages, out, w.part, w.ml, w.logits,  \
+                                               p.status)
 #define DKV_ATTN_D(D)                                    \
   if (pack) {                                            \
     if (kmode == 0) DKV_ATTN(D, 0, true);                \

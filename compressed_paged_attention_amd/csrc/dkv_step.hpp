@@ -159,6 +159,156 @@ __device__ void block_minmax(float (&mn)[NV], float (&mx)[NV], float* red) {
   }
 }
 
+// A candidate token: running score sum, position, slot; pos == kNoPos: none.
+// Its observation count is N - 1 - pos.
+constexpr int32_t kNoPos = 0x7FFFFFFF;
+struct Cand {
+  float sum;
+  int32_t pos, slot;
+};
+
+// Strictly less important: sum_a * cnt_b < sum_b * cnt_a (exact in fp64),
+// ties to the smaller position.
+// Counts are below 2^29 (max_seq_len), so both products are exact.  Written
+// without branches: it sits on the critical path of every reduction.
+__device__ inline bool less_imp(const Cand& a, const Cand& b, int64_t N) {
+  const int32_t n1 = (int32_t)(N - 1);
+  const double l = (double)a.sum * (double)(n1 - b.pos), r = (double)b.sum * (double)(n1 - a.pos);
+  const bool lt = (l < r) | ((l == r) & (a.pos < b.pos));
+  return (a.pos != kNoPos) & ((b.pos == kNoPos) | lt);
+}
+
+__device__ inline Cand min_imp(const Cand& a, const Cand& b, int64_t N) { return less_imp(b, a, N) ? b : a; }
+
+template <int LVL>
+__device__ inline void argmin_step(Cand& c, int64_t N) {
+  const Cand t{lane_xchg_t<LVL>(c.sum), lane_xchg_t<LVL>(c.pos), lane_xchg_t<LVL>(c.slot)};
+  c = min_imp(c, t, N);
+}
+
+__device__ inline Cand wave_argmin(Cand c, int64_t N) {
+  argmin_step<0>(c, N);
+  argmin_step<1>(c, N);
+  argmin_step<2>(c, N);
+  argmin_step<3>(c, N);
+  argmin_step<4>(c, N);
+  argmin_step<5>(c, N);
+  return c;
+}
+
+__device__ inline int classify_mean(float sum, int64_t cnt, int64_t Np, int lo_en, double ah, double al) {
+  const double x = (double)sum * (double)Np;
+  const double ch = ah * (double)cnt, cl = al * (double)cnt;
+  if (lo_en) {
+    if (x > ch) return kTierHi;
+    return x >= cl ? kTierLo : kTierPrune;
+  }
+  return x >= cl ? kTierHi : kTierPrune;
+}
+
+// The step's decision for one unit (DiffKV notes, "KV compression policy",
+// generation phase), from t_c (slot tcs, sum tcsum; tcs < 0: none, N < W),
+// the least important non-window high token bh and low token bl, at length N
+// (the new token's position; thresholds use N + 1).
+struct Plan {
+  int32_t new_hi, hi_app, lo_src, lo_slot, lo_app;
+  int32_t nfw;  // demand word: need tier | kActive | status flags << 8
+};
+
+__device__ inline Plan plan_decide(int64_t N, int W, int S_max, int lo_en, double dah, double dal, int nh, int nl,
+                                   int ph, int pl, int L, int tcs, float tcsum, const Cand& bh, const Cand& bl) {
+  Plan r{nh, 1, -1, 0, 0, kActive};
+  if (N + 1 > S_max) {
+    r.nfw = kActive | (int32_t)(kStOverflow << 8);
+    return r;
+  }
+  const int64_t Np = N + 1, tc_pos = N - W;
+  if (tc_pos >= 0) {
+    const int cls = classify_mean(tcsum, W - 1, Np, lo_en, dah, dal);
+    if (cls == kTierHi) {
+      const int vcls = classify_mean(bh.sum, N - 1 - bh.pos, Np, lo_en, dah, dal);
+      if (vcls == kTierLo) {
+        r.lo_src = bh.slot;
+        r.lo_slot = nl;
+        r.lo_app = 1;
+        r.new_hi = bh.slot;
+        r.hi_app = 0;
+      } else if (vcls == kTierPrune) {
+        r.new_hi = bh.slot;
+        r.hi_app = 0;
+      }
+    } else if (cls == kTierLo) {
+      // t_c moves to the low tier; the least important low token, t_c
+      // included, is pruned below alpha_l / N'
+      r.lo_src = tcs;
+      r.new_hi = tcs;
+      r.hi_app = 0;
+      const Cand tcc{tcsum, (int32_t)tc_pos, -1};
+      const Cand lv = less_imp(tcc, bl, N) ? tcc : bl;
+      if (lv.slot >= 0 && classify_mean(lv.sum, N - 1 - lv.pos, Np, lo_en, dah, dal) == kTierPrune) {
+        r.lo_slot = lv.slot;
+        r.lo_app = 0;
+      } else {
+        r.lo_slot = nl;
+        r.lo_app = 1;
+      }
+    } else {
+      r.new_hi = tcs;
+      r.hi_app = 0;
+    }
+  }
+  int need = 0;
+  if (r.hi_app && nh % kHiTokens == 0) need = kTierHi;
+  if (r.lo_app && nl % kLoTokens == 0) need = kTierLo;
+  const uint32_t fl = (need && ph + pl + 1 > L) ? kStOverflow : 0u;
+  r.nfw = kActive | (fl ? 0 : need) | (int32_t)(fl << 8);
+  return r;
+}
+
+// Plan record of the next step, kept in the spare bytes after the last
+// segment of a unit's first high page (table entry 0): written by a
+// workgroup that has just updated all of the unit's score sums, read by the
+// next step's plan kernel instead of a scan, and invalidated by every other
+// write to the unit's slots or scores (zeroed magic).  Prompt pages start
+// with these bytes zero.
+constexpr uint32_t kPlanMagic = 0x4E414C50u;
+constexpr int kRecWords = 13;  // magic, seq, nh, nl, ph, pl, 5 plan fields, demand word, check
+template <int D>
+constexpr int plan_rec_off() {
+  return tier_seg(D, true).bytes;
+}
+static_assert(page_bytes_for(64) - tier_seg(64, true).bytes >= 4 * kRecWords, "plan record space");
+static_assert(page_bytes_for(128) - tier_seg(128, true).bytes >= 4 * kRecWords, "plan record space");
+
+__device__ inline void plan_rec_fill(uint32_t* w, int64_t seq, int nh, int nl, int ph, int pl, const Plan& p) {
+  w[0] = kPlanMagic;
+  w[1] = (uint32_t)seq;
+  w[2] = (uint32_t)nh;
+  w[3] = (uint32_t)nl;
+  w[4] = (uint32_t)ph;
+  w[5] = (uint32_t)pl;
+  w[6] = (uint32_t)p.new_hi;
+  w[7] = (uint32_t)p.hi_app;
+  w[8] = (uint32_t)p.lo_src;
+  w[9] = (uint32_t)p.lo_slot;
+  w[10] = (uint32_t)p.lo_app;
+  w[11] = (uint32_t)p.nfw;
+  uint32_t x = 0x9E3779B9u;
+  for (int k = 0; k < 12; k++) x = (x ^ w[k]) * 0x01000193u;
+  w[12] = x;
+}
+
+// true when the record is intact and was made for this length and state
+__device__ inline bool plan_rec_check(const uint32_t* w, int64_t seq, int nh, int nl, int ph, int pl, Plan& p) {
+  uint32_t x = 0x9E3779B9u;
+  for (int k = 0; k < 12; k++) x = (x ^ w[k]) * 0x01000193u;
+  if (w[0] != kPlanMagic || x != w[12] || w[1] != (uint32_t)seq || w[2] != (uint32_t)nh ||
+      w[3] != (uint32_t)nl || w[4] != (uint32_t)ph || w[5] != (uint32_t)pl)
+    return false;
+  p = Plan{(int32_t)w[6], (int32_t)w[7], (int32_t)w[8], (int32_t)w[9], (int32_t)w[10], (int32_t)w[11]};
+  return true;
+}
+
 // LDS scratch of commit_unit, in 32-bit words: two page images plus misc.
 template <int D>
 constexpr int commit_lds_words() {
@@ -201,6 +351,22 @@ __device__ UnitState commit_unit(int64_t u, int H, int L, int64_t U, int64_t P, 
   const int64_t rowi = ((int64_t)b * H + h) * D + tid;
   float xk_new = tid < D ? h2f(k_new[rowi]) : 0.0f;
   float xv_new = tid < D ? h2f(v_new[rowi]) : 0.0f;
+  // the plan record and the page ids it names, read before any barrier
+  // (indices clamped into the row: a unit without a record reads, but does
+  // not use, some entry)
+  const int nh = res.nh, nl = res.nl, ph = res.ph, pl = res.pl;
+  const int new_hi = R[S_NEWHI], lo_src = R[S_LOSRC], lo_slot = R[S_LOSLOT];
+  const int hi_app = R[S_HIAPP], lo_app = R[S_LOAPP];
+  auto clampL = [&](int t) { return min(max(t, 0), L - 1); };
+  const int32_t id_hrow = row[clampL(new_hi >> 4)];
+  const int32_t id_lrow = row[clampL(L - 1 - (lo_slot >> 5))];
+  const int32_t id_src = row[clampL(lo_src >> 4)];
+  const int32_t id_first = row[0];
+  int64_t start = 0, end = 0;
+  if constexpr (DIRECT) {
+    start = hdr[SH_START];
+    end = hdr[SH_END];
+  }
   int32_t page = -1;
   if constexpr (DIRECT) {
     int* lds = (int*)(sm + 2 * (page_bytes_for(D) / 4));  // 16 ints
@@ -220,7 +386,6 @@ __device__ UnitState commit_unit(int64_t u, int H, int L, int64_t U, int64_t P, 
     }
     if (fl) atomicOr(&s_fl, fl);
     __syncthreads();
-    const int64_t start = hdr[SH_START], end = hdr[SH_END];
     uint32_t st = s_fl;
     if (!st && total > end - start) st = kStExhausted;
     if (u == 0 && tid == 0) {
@@ -234,18 +399,14 @@ __device__ UnitState commit_unit(int64_t u, int H, int L, int64_t U, int64_t P, 
     page = R[S_PAGE];
   }
   const int need = wu & 3;
-  const int nh = s4[0], nl = s4[1], ph = s4[2], pl = s4[3];
-  const int new_hi = R[S_NEWHI], lo_src = R[S_LOSRC], lo_slot = R[S_LOSLOT];
-  const int hi_app = R[S_HIAPP], lo_app = R[S_LOAPP];
   if (need && (page < 0 || page >= P)) {
     if (tid == 0) atomicOr(status, kStBadState);
     return res;
   }
   // destinations: the new token's high slot; the requantized token's low slot
-  TokWrite th{true, true, need == kTierHi, new_hi & 15,
-              need == kTierHi ? page : row[new_hi >> 4]};
+  TokWrite th{true, true, need == kTierHi, new_hi & 15, need == kTierHi ? page : id_hrow};
   TokWrite tl{lo_src >= 0, false, need == kTierLo, lo_slot & 31,
-              lo_src < 0 ? 0 : (need == kTierLo ? page : row[L - 1 - (lo_slot >> 5)])};
+              lo_src < 0 ? 0 : (need == kTierLo ? page : id_lrow)};
   uint32_t* img_h = sm;
   uint32_t* img_l = sm + kPageWords;
   float* red = (float*)(sm + 2 * kPageWords + 20);  // 16 floats
@@ -256,7 +417,7 @@ __device__ UnitState commit_unit(int64_t u, int H, int L, int64_t U, int64_t P, 
   float xk_rq = 0.0f, xv_rq = 0.0f, sc_rq = 0.0f;
   int32_t pos_rq = 0;
   if (tl.on) {
-    const uint8_t* src = pages + (int64_t)row[lo_src >> 4] * page_bytes;
+    const uint8_t* src = pages + (int64_t)id_src * page_bytes;
     const int si = lo_src & 15;
     const uint32_t km = *(const uint32_t*)(src + sh.km + 4 * si);
     const uint32_t vm = *(const uint32_t*)(src + sh.vm + 4 * si);
@@ -298,6 +459,9 @@ __device__ UnitState commit_unit(int64_t u, int H, int L, int64_t U, int64_t P, 
   // ---- phase 3: stores ----
   img_store<D>(img_h, th, pages, page_bytes);
   img_store<D>(img_l, tl, pages, page_bytes);
+  // the unit changed: its plan record (first high page) no longer applies
+  if (tid == 0 && ph >= 1 && id_first >= 0 && id_first < P)
+    *(uint32_t*)(pages + (int64_t)id_first * page_bytes + plan_rec_off<D>()) = 0u;
   res = UnitState{true, nh + hi_app, nl + lo_app, ph + (need == kTierHi), pl + (need == kTierLo),
                   need == kTierHi ? ph : (need == kTierLo ? L - 1 - pl : -1), page};
   if (tid == 0) {

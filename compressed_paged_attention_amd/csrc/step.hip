@@ -41,81 +41,56 @@ size_t step_workspace(const Cfg& c, int batch) {
          align_up(U * sizeof(int32_t), 256);
 }
 
-// A candidate token: running score sum, position, slot; pos == kNoPos: none.
-// Its observation count is N - 1 - pos.
-constexpr int32_t kNoPos = 0x7FFFFFFF;
-struct Cand {
-  float sum;
-  int32_t pos, slot;
-};
+constexpr int kPlanThreads = 256;
+constexpr int kPlanPer = 8;       // slots per thread per round, loads issued together
+constexpr int kRowCache = 4096;   // table rows up to this long are read once into LDS
 
-// Strictly less important: sum_a * cnt_b < sum_b * cnt_a (exact in fp64),
-// ties to the smaller position.
-// Counts are below 2^31 (N <= max_seq_len), so both products are exact.
-__device__ inline bool less_imp(const Cand& a, const Cand& b, int64_t N) {
-  if (a.pos == kNoPos) return false;
-  if (b.pos == kNoPos) return true;
-  const int32_t n1 = (int32_t)(N - 1);
-  const double l = (double)a.sum * (double)(n1 - b.pos), r = (double)b.sum * (double)(n1 - a.pos);
-  return l < r || (l == r && a.pos < b.pos);
-}
 
-template <int LVL>
-__device__ inline void argmin_step(Cand& c, int64_t N) {
-  const Cand t{lane_xchg_t<LVL>(c.sum), lane_xchg_t<LVL>(c.pos), lane_xchg_t<LVL>(c.slot)};
-  if (less_imp(t, c, N)) c = t;
-}
-
-__device__ inline Cand wave_argmin(Cand c, int64_t N) {
-  argmin_step<0>(c, N);
-  argmin_step<1>(c, N);
-  argmin_step<2>(c, N);
-  argmin_step<3>(c, N);
-  argmin_step<4>(c, N);
-  argmin_step<5>(c, N);
-  return c;
-}
-
-constexpr int kPlanThreads = 512;
-
-__device__ inline int classify_mean(float sum, int64_t cnt, int64_t Np, int lo_en, double ah, double al) {
-  const double x = (double)sum * (double)Np;
-  const double ch = ah * (double)cnt, cl = al * (double)cnt;
-  if (lo_en) {
-    if (x > ch) return kTierHi;
-    return x >= cl ? kTierLo : kTierPrune;
-  }
-  return x >= cl ? kTierHi : kTierPrune;
-}
-
-// One block per unit.  A single pass over both tiers' score and position
-// words finds t_c, the least important non-window high token and the least
-// important low token; the decision needs no second pass.
+// One block per unit.  The unit's length, tier state and table row are read
+// in one round; then one pass over both tiers' score and position words finds
+// t_c, the least important non-window high token and the least important low
+// token (wave butterflies, then the four waves' candidates in one quad).
 template <int D>
 __global__ __launch_bounds__(kPlanThreads) void step_plan_kernel(int H, int L, int W, int S_max, int lo_en, float ah,
-                                                        float al, int64_t P, int page_bytes,
-                                                        const int32_t* __restrict__ seq_len,
-                                                        const int32_t* __restrict__ table,
-                                                        const int32_t* __restrict__ state,
-                                                        const uint8_t* __restrict__ pages,
-                                                        const uint64_t* __restrict__ ptr, int64_t* __restrict__ hdr,
-                                                        int32_t* __restrict__ rec, int32_t* __restrict__ nf) {
-  const int64_t u = blockIdx.x;
-  const int b = (int)u / H;
-  const int tid = threadIdx.x;
+                                                                 float al, int64_t P, int page_bytes,
+                                                                 const int32_t* __restrict__ seq_len,
+                                                                 const int32_t* __restrict__ table,
+                                                                 const int32_t* __restrict__ state,
+                                                                 const uint8_t* __restrict__ pages,
+                                                                 const uint64_t* __restrict__ ptr,
+                                                                 int64_t* __restrict__ hdr, int32_t* __restrict__ rec,
+                                                                 int32_t* __restrict__ nf) {
+  const int u = blockIdx.x;
+  const int b = u / H;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int32_t* row = table + (int64_t)u * L;
+  __shared__ int32_t row_s[kRowCache];
+  __shared__ int s_tc;
+  __shared__ float s_tcsum;
+  __shared__ uint32_t s_bad;
+  __shared__ Cand lds[2][kPlanThreads / 64];
+  __shared__ int s_rec;
+  // ---- round 1: length, tier state, the table row ----
+  const bool cached = L <= kRowCache;
+  if (cached)
+    for (int j = tid; j < L; j += kPlanThreads) row_s[j] = row[j];
   if (u == 0 && tid == 0) {  // pointer snapshot for the commit kernel
     hdr[SH_START] = (int64_t)ptr[0];
     hdr[SH_END] = (int64_t)ptr[1];
   }
   const int64_t N = seq_len[b];
+  const int32_t* s4 = state + 4 * (int64_t)u;
+  const int nh = s4[0], nl = s4[1], ph = s4[2], pl = s4[3];
+  if (tid == 0) {
+    s_tc = -1;
+    s_bad = 0;
+  }
+  __syncthreads();
   if (N <= 0) {
     if (tid == 0) nf[u] = 0;
     return;
   }
-  int32_t* R = rec + u * kSRec;
-  const int32_t* s4 = state + 4 * u;
-  const int nh = s4[0], nl = s4[1], ph = s4[2], pl = s4[3];
-  const int32_t* row = table + u * L;
+  int32_t* R = rec + (int64_t)u * kSRec;
   uint32_t flags = 0;
   if (N + 1 > S_max) flags = kStOverflow;
   else if (nh < 0 || nl < 0 || ph != cdiv(nh, kHiTokens) || pl != cdiv(nl, kLoTokens) || nh + nl > N ||
@@ -125,141 +100,118 @@ __global__ __launch_bounds__(kPlanThreads) void step_plan_kernel(int H, int L, i
     if (tid == 0) nf[u] = kActive | (int32_t)(flags << 8);
     return;
   }
+  auto page_of = [&](int tix) { return cached ? row_s[tix] : row[tix]; };
+  // ---- a plan record left by the previous attention: no scan needed ----
+  if (tid == 0) {
+    s_rec = 0;
+    const int32_t p0 = ph >= 1 ? page_of(0) : -1;
+    if (p0 >= 0 && p0 < P) {
+      const uint32_t* w = (const uint32_t*)(pages + (int64_t)p0 * page_bytes + plan_rec_off<D>());
+      uint32_t rw[kRecWords];
+#pragma unroll
+      for (int k = 0; k < kRecWords; k++) rw[k] = w[k];
+      Plan pr;
+      if (plan_rec_check(rw, N, nh, nl, ph, pl, pr)) {
+        s_rec = 1;
+        R[S_NEWHI] = pr.new_hi;
+        R[S_HIAPP] = pr.hi_app;
+        R[S_LOSRC] = pr.lo_src;
+        R[S_LOSLOT] = pr.lo_slot;
+        R[S_LOAPP] = pr.lo_app;
+        R[S_PAGE] = -1;
+        nf[u] = pr.nfw;
+      }
+    }
+  }
+  __syncthreads();
+  if (s_rec) return;
   const Seg sh = tier_seg(D, true), sl = tier_seg(D, false);
   const int64_t Np = N + 1, tc_pos = N - W;
   const double dah = (double)ah, dal = (double)al;
-  __shared__ int s_tc;
-  __shared__ float s_tcsum;
-  __shared__ uint32_t s_bad;
-  __shared__ Cand lds[2][kPlanThreads / 64];
   const Cand none{0.0f, kNoPos, 0};
-  if (tid == 0) {
-    s_tc = -1;
-    s_bad = 0;
-  }
-  __syncthreads();
   Cand bh = none, bl = none;
   if (tc_pos >= 0) {
-    // every slot of both tiers (this also checks every page id of the row);
-    // kPer slots per thread per round, their loads issued together
-    constexpr int kPer = 4;
+    // every slot of both tiers (this also checks every page id of the row)
     const int n = nh + nl;
-    for (int base = 0; base < n; base += kPer * kPlanThreads) {
-      // branch-free loads (indices clamped into the unit) so that each
-      // round costs two dependent trips to memory
-      int32_t id[kPer];
+    for (int base = 0; base < n; base += kPlanPer * kPlanThreads) {
+      int32_t pos[kPlanPer];
+      float sum[kPlanPer];
+      int32_t id[kPlanPer];
 #pragma unroll
-      for (int e = 0; e < kPer; e++) {
+      for (int e = 0; e < kPlanPer; e++) {
+        // branch-free loads (indices clamped into the unit)
         const int s = min(base + e * kPlanThreads + tid, n - 1);
         const bool hi = s < nh;
         const int ls = hi ? s : s - nh;
-        id[e] = row[hi ? (ls >> 4) : L - 1 - (ls >> 5)];
-      }
-      int32_t pos[kPer];
-      float sum[kPer];
-#pragma unroll
-      for (int e = 0; e < kPer; e++) {
-        const int s = min(base + e * kPlanThreads + tid, n - 1);
-        const bool hi = s < nh;
-        const int ls = hi ? s : s - nh;
+        id[e] = page_of(hi ? (ls >> 4) : L - 1 - (ls >> 5));
         const uint8_t* pg = pages + (int64_t)min(max(id[e], 0), (int32_t)(P - 1)) * page_bytes;
         const int idx = hi ? (ls & 15) : (ls & 31);
         pos[e] = *(const int32_t*)(pg + (hi ? sh.ps : sl.ps) + 4 * idx);
         sum[e] = *(const float*)(pg + (hi ? sh.sc : sl.sc) + 4 * idx);
       }
+      // this round's candidates, then a pairwise tree (short dependent chain)
+      Cand ch[kPlanPer], cl[kPlanPer];
 #pragma unroll
-      for (int e = 0; e < kPer; e++) {
+      for (int e = 0; e < kPlanPer; e++) {
         const int s = base + e * kPlanThreads + tid;
-        if (s >= n) continue;
-        if (id[e] < 0 || id[e] >= P) s_bad = 1;
-        const bool hi = s < nh;
+        const bool in = s < n, hi = s < nh;
         const int ls = hi ? s : s - nh;
-        const Cand c{sum[e], pos[e], ls};
-        if (hi) {
-          if (pos[e] == tc_pos) {  // positions are unique: one writer
-            s_tc = ls;
-            s_tcsum = sum[e];
-          }
-          if (pos[e] <= tc_pos && less_imp(c, bh, N)) bh = c;
-        } else if (less_imp(c, bl, N)) {
-          bl = c;
+        if (in && (id[e] < 0 || id[e] >= P)) s_bad = 1;
+        if (in && hi && pos[e] == tc_pos) {  // positions are unique: one writer
+          s_tc = ls;
+          s_tcsum = sum[e];
         }
+        ch[e] = Cand{sum[e], (in && hi && pos[e] <= tc_pos) ? pos[e] : kNoPos, ls};
+        cl[e] = Cand{sum[e], (in && !hi) ? pos[e] : kNoPos, ls};
       }
+#pragma unroll
+      for (int w = kPlanPer / 2; w >= 1; w >>= 1)
+#pragma unroll
+        for (int e = 0; e < w; e++) {
+          ch[e] = min_imp(ch[e], ch[e + w], N);
+          cl[e] = min_imp(cl[e], cl[e + w], N);
+        }
+      bh = min_imp(bh, ch[0], N);
+      bl = min_imp(bl, cl[0], N);
     }
   } else {
-    for (int j = tid; j < ph + pl; j += blockDim.x) {
-      const int32_t id = j < ph ? row[j] : row[L - 1 - (j - ph)];
+    for (int j = tid; j < ph + pl; j += kPlanThreads) {
+      const int32_t id = page_of(j < ph ? j : L - 1 - (j - ph));
       if (id < 0 || id >= P) s_bad = 1;
     }
   }
   bh = wave_argmin(bh, N);
   bl = wave_argmin(bl, N);
-  if ((tid & 63) == 0) {
-    lds[0][tid >> 6] = bh;
-    lds[1][tid >> 6] = bl;
+  if (lane == 0) {
+    lds[0][wid] = bh;
+    lds[1][wid] = bl;
   }
   __syncthreads();  // also publishes s_tc and s_bad
-  if (tid == 0) {
-    for (int w = 1; w < kPlanThreads / 64; w++) {
-      if (less_imp(lds[0][w], bh, N)) bh = lds[0][w];
-      if (less_imp(lds[1][w], bl, N)) bl = lds[1][w];
-    }
-  }
+  if (wid != 0) return;
+  // the waves' candidates: lane q of each quad holds wave q's, two butterfly levels
+  static_assert(kPlanThreads / 64 == 4, "one quad of candidates");
+  bh = lds[0][lane & 3];
+  bl = lds[1][lane & 3];
+  argmin_step<0>(bh, N);
+  argmin_step<1>(bh, N);
+  argmin_step<0>(bl, N);
+  argmin_step<1>(bl, N);
+  if (lane != 0) return;
   const int tcs = s_tc;
   const float tcsum = s_tcsum;
   // t_c is in the high tier by construction; a missing t_c is bad state
   if (s_bad || (tc_pos >= 0 && tcs < 0)) {
-    if (tid == 0) nf[u] = kActive | (int32_t)(kStBadState << 8);
+    nf[u] = kActive | (int32_t)(kStBadState << 8);
     return;
   }
-  if (tid != 0) return;
-  int new_hi = nh, hi_app = 1, lo_src = -1, lo_slot = 0, lo_app = 0;
-  if (tc_pos >= 0) {
-    const int cls = classify_mean(tcsum, W - 1, Np, lo_en, dah, dal);
-    if (cls == kTierHi) {
-      const int vcls = classify_mean(bh.sum, N - 1 - bh.pos, Np, lo_en, dah, dal);
-      if (vcls == kTierLo) {
-        lo_src = bh.slot;
-        lo_slot = nl;
-        lo_app = 1;
-        new_hi = bh.slot;
-        hi_app = 0;
-      } else if (vcls == kTierPrune) {
-        new_hi = bh.slot;
-        hi_app = 0;
-      }
-    } else if (cls == kTierLo) {
-      // t_c moves to the low tier; the least important low token, t_c
-      // included, is pruned below alpha_l / N'
-      lo_src = tcs;
-      new_hi = tcs;
-      hi_app = 0;
-      const Cand tcc{tcsum, (int32_t)tc_pos, -1};
-      const Cand lv = less_imp(tcc, bl, N) ? tcc : bl;
-      if (lv.slot >= 0 && classify_mean(lv.sum, N - 1 - lv.pos, Np, lo_en, dah, dal) == kTierPrune) {
-        lo_slot = lv.slot;
-        lo_app = 0;
-      } else {
-        lo_slot = nl;
-        lo_app = 1;
-      }
-    } else {
-      new_hi = tcs;
-      hi_app = 0;
-    }
-  }
-  int need = 0;
-  if (hi_app && nh % kHiTokens == 0) need = kTierHi;
-  if (lo_app && nl % kLoTokens == 0) need = kTierLo;
-  uint32_t fl = 0;
-  if (need && ph + pl + 1 > L) fl = kStOverflow;
-  R[S_NEWHI] = new_hi;
-  R[S_HIAPP] = hi_app;
-  R[S_LOSRC] = lo_src;
-  R[S_LOSLOT] = lo_slot;
-  R[S_LOAPP] = lo_app;
+  const Plan pl_ = plan_decide(N, W, S_max, lo_en, dah, dal, nh, nl, ph, pl, L, tcs, tcsum, bh, bl);
+  R[S_NEWHI] = pl_.new_hi;
+  R[S_HIAPP] = pl_.hi_app;
+  R[S_LOSRC] = pl_.lo_src;
+  R[S_LOSLOT] = pl_.lo_slot;
+  R[S_LOAPP] = pl_.lo_app;
   R[S_PAGE] = -1;
-  nf[u] = kActive | (fl ? 0 : need) | (int32_t)(fl << 8);
+  nf[u] = pl_.nfw;
 }
 
 // Coordination for large batches: prefix sum over the demand words, capacity

@@ -17,7 +17,7 @@ import numpy as np
 import pytest
 import torch
 
-from tests.parity import (SCORE_ATOL, SCORE_RTOL, assert_attn_close, assert_state_equal, np_,
+from tests.parity import (SCORE_ATOL, SCORE_RTOL, assert_attn_close, assert_state_equal, masked, np_,
                           resync_scores)
 
 pytestmark = pytest.mark.gpu
@@ -77,16 +77,16 @@ def check_device_pool(g, T_h=16, T_l=32):
 
 
 def unit_page_pairs(g_pt, g_ts, o_pt, o_ts, gb, ob, H, L):
-    """(device page id, oracle page id, is_hi) for every page of the sampled
+    """(device page id, oracle page id, is_hi, is_first) for every page of the sampled
     request's units, in table order; tier state must match."""
     pairs = []
     for h in range(H):
         assert np.array_equal(g_ts[gb, h], o_ts[ob, h]), f"request {gb} head {h}: tier state differs"
         ph, pl = int(o_ts[ob, h, 2]), int(o_ts[ob, h, 3])
         for j in range(ph):
-            pairs.append((int(g_pt[gb, h, j]), int(o_pt[ob, h, j]), True))
+            pairs.append((int(g_pt[gb, h, j]), int(o_pt[ob, h, j]), True, j == 0))
         for j in range(pl):
-            pairs.append((int(g_pt[gb, h, L - 1 - j]), int(o_pt[ob, h, L - 1 - j]), False))
+            pairs.append((int(g_pt[gb, h, L - 1 - j]), int(o_pt[ob, h, L - 1 - j]), False, False))
     return pairs
 
 
@@ -106,9 +106,9 @@ def compare_sampled(g, o, orc, cfg, sample, scores_exact, what):
     op = o.pages[[p[1] for p in pairs]]
     _, seg_h = orc.tier_layout(cfg, orc.HI)
     _, seg_l = orc.tier_layout(cfg, orc.LO)
-    for i, (_, _, hi) in enumerate(pairs):
+    for i, (_, _, hi, first) in enumerate(pairs):
         seg = seg_h if hi else seg_l
-        a, b = gp[i], op[i]
+        a, b = (masked(gp[i], cfg) if first else gp[i]), op[i]
         if np.array_equal(a, b):
             continue
         assert not scores_exact, f"{what}: page pair {i} differs"

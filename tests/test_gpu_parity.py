@@ -366,6 +366,66 @@ def test_decode_step_exhausted_pool(dk, orc):
     assert int(p.o.status[0]) == orc.ST_POOL_EXHAUSTED
 
 
+def _plan_record_words(g, cfg):
+    """The plan-record magic of every unit's first page (0 where none)."""
+    from tests.parity import plan_record_span
+    off, _ = plan_record_span(cfg)
+    first = g.page_table[..., 0].reshape(-1).to(torch.int64)
+    pages = g.pool.pages.view(g.pool.num_pages, -1)
+    ok = first >= 0
+    idx = first.clamp(min=0)
+    w = pages[idx][:, off:off + 4].contiguous().view(torch.int32).reshape(-1)
+    return torch.where(ok, w, torch.zeros_like(w))
+
+
+def test_plan_record_matches_scan(dk, orc):
+    """The next step's plan that the fused score update leaves in each unit's
+    first page gives exactly the state a fresh scan gives: two identical
+    caches, one stepping from the records, one with every record erased
+    before each step, stay byte-identical."""
+    from tests.parity import plan_record_span, first_pages, masked
+    from workloads import synth
+    cfg = _medium_cfg("llama3_8b", batch=32, max_seq_len=1500)
+    assert dk.diffkv_attn_splits(cfg, 32) == 1
+    g = torch.Generator().manual_seed(51)
+    lens = (torch.randint(5, 80, (32,), generator=g) * 16 - torch.randint(0, 3, (32,), generator=g)).to(torch.int64)
+    pr = synth.make_prompt(cfg, lens=lens)
+    P = int(sum(-(-int(n) // 16) for n in lens) * 8 * 1.2) + 64
+    st = []
+    for _ in range(2):
+        s_ = dk.DiffKVState(cfg, 32, P, max_total_tokens=int(lens.sum()), device=dev)
+        cu = pr["cu_seqlens"].to(dev)
+        tiers, _ = s_.classify(cu, pr["scores"].to(dev))
+        s_.compact_prompt(cu, pr["k"].to(dev), pr["v"].to(dev), pr["scores"].to(dev), tiers)
+        st.append(s_)
+    off, n = plan_record_span(cfg)
+    seq = lens.to(torch.int32).to(dev)
+    used = 0
+    for step in range(8):
+        dec = synth.make_decode(cfg, step, device=dev)
+        # cache B: erase every record, so its plan kernel scans
+        b = st[1]
+        first = b.page_table[..., 0].reshape(-1)
+        first = first[first >= 0].to(torch.int64)
+        b.pool.pages.view(b.pool.num_pages, -1)[first, off:off + n] = 0
+        used += int((_plan_record_words(st[0], cfg) != 0).sum())
+        outs = [s_.decode_step(dec["q"], seq, dec["k_new"], dec["v_new"], update_scores=1) for s_ in st]
+        torch.cuda.synchronize()
+        a_, b_ = st
+        assert torch.equal(outs[0], outs[1]), f"step {step}: outputs differ"
+        for name in ("page_table", "tier_state"):
+            assert torch.equal(getattr(a_, name), getattr(b_, name)), f"step {step}: {name} differs"
+        assert torch.equal(a_.pool.free_list, b_.pool.free_list) and torch.equal(a_.pool.ptr, b_.pool.ptr)
+        pa, pb = np_(a_.pool.pages.view(P, -1)), np_(b_.pool.pages.view(P, -1))
+        fp = first_pages(np_(a_.page_table))
+        for p_ in sorted({int(x) for x in np_(a_.page_table).ravel() if x >= 0}):
+            x, y = (masked(pa[p_], cfg), masked(pb[p_], cfg)) if p_ in fp else (pa[p_], pb[p_])
+            assert np.array_equal(x, y), f"step {step}: page {p_} differs"
+        seq = seq + 1
+    assert used > 0, "no plan record was used"
+    assert int(st[0].pool.status.item()) == 0
+
+
 def test_deterministic_replay(dk, orc):
     """Same inputs twice -> byte-identical state and outputs."""
     from workloads import synth
