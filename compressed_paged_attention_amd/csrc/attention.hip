@@ -385,6 +385,18 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar loop control
   const int i = lane & 15, qg = lane >> 4;
   const int32_t* row = table + u * L;
+  // the query and the table entry of this wave's first page (a guess that
+  // holds when the unit has more than wid high pages) go out first: neither
+  // waits for the unit's state
+  const int qhead = i < G ? i : (PACK && i < 2 * G ? i - G : -1);
+  uint4 qraw[QD / 8];
+  {
+    const uint4* src =
+        (const uint4*)(q + ((int64_t)b * H * G + (int64_t)h * G + max(qhead, 0)) * D + qg * QD);
+#pragma unroll
+    for (int c = 0; c < QD / 8; c++) qraw[c] = src[c];
+  }
+  const int32_t id_guess = row[min(wid, L - 1)];
   const int32_t* s4 = state + 4 * u;
   const int nh = s4[0], nl = s4[1], ph = s4[2], pl = s4[3];
   const int N = seq_len[b];
@@ -430,9 +442,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
   uint32_t badid = 0;
   // page ids are checked where they are used; a bad id is clamped into the
   // pool (the load stays in bounds) and zeroes the unit's result
-  auto fetch = [&](PageRegs<D>& R, int jj) {
-    jj = min(jj, p1 - 1);  // past the end: reload the last page (unused)
-    int32_t id = page_id(table_idx(jj));  // uniform index: scalar load
+  auto fetch_id = [&](PageRegs<D>& R, int jj, int32_t id) {
     badid |= (uint32_t)(id < 0 || id >= P);
     id = min(max(id, 0), (int32_t)(P - 1));
     R.id = id;
@@ -440,33 +450,33 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
     load_page<D>(R, pg, jj >= ph, kbase, mq, vl);
     if (MODE == 1) load_page_sp<D>(R, pg, jj >= ph, lane);
   };
+  auto fetch = [&](PageRegs<D>& R, int jj) {
+    jj = min(jj, p1 - 1);  // past the end: reload the last page (unused)
+    fetch_id(R, jj, page_id(table_idx(jj)));  // uniform index: scalar load
+  };
   PageRegs<D> A, B;
   const bool busy = p0 + wid < p1;
-  if (busy) fetch(A, p0 + wid);
+  if (busy) {
+    const int j0 = p0 + wid;
+    fetch_id(A, j0, (j0 == wid && j0 < ph) ? id_guess : page_id(table_idx(j0)));
+  }
 
   // ---- Q operand: lane (i, qg) holds column i's head, dims qg*QD .. +QD-1;
   // with PACK, columns G .. 2G-1 repeat heads 0 .. G-1 (their tails) ----
-  const int qhead = i < G ? i : (PACK && i < 2 * G ? i - G : -1);
   const bool tail = PACK && i >= G;
   half8_t qop[NS];
   float sumq = 0.0f;
   {
     uint16_t qv[QD];
-    if (qhead >= 0) {
-      const uint4* src = (const uint4*)(q + ((int64_t)b * H * G + (int64_t)h * G + qhead) * D + qg * QD);
 #pragma unroll
-      for (int c = 0; c < QD / 8; c++) {
-        const uint4 w = src[c];
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    for (int c = 0; c < QD / 8; c++) {
+      const uint4 w = qraw[c];
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-          qv[8 * c + 2 * e] = (uint16_t)(ws[e] & 0xFFFFu);
-          qv[8 * c + 2 * e + 1] = (uint16_t)(ws[e] >> 16);
-        }
+      for (int e = 0; e < 4; e++) {
+        qv[8 * c + 2 * e] = qhead >= 0 ? (uint16_t)(ws[e] & 0xFFFFu) : (uint16_t)0;
+        qv[8 * c + 2 * e + 1] = qhead >= 0 ? (uint16_t)(ws[e] >> 16) : (uint16_t)0;
       }
-    } else {
-#pragma unroll
-      for (int e = 0; e < QD; e++) qv[e] = 0;
     }
 #pragma unroll
     for (int e = 0; e < QD; e++) sumq += h2f(qv[e]);
@@ -504,12 +514,16 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
         else pos_s[j * 32 + lane - 32] = (int32_t)R.sp;
         if (lane == 0) id_s[j] = R.id;
       }
-      float* lgp = kLds ? lg_s + j * 32 * G : logits + ((int64_t)u * L + table_idx(j)) * 32 * G;
+      // logits: LDS g-major [G][TPg * 32]; workspace [L][32][G] by table slot
+      float* lgp = kLds ? lg_s + i * (TPg * 32) + j * 32 : logits + ((int64_t)u * L + table_idx(j)) * 32 * G;
       compute_page<D, PACK>(R, j < ph, valid(j), qop, sq2, scale_log2, tail, qg, sm, acc, [&](int mb, const float* x) {
         if (!SAVE || i >= G) return;
         const int t0 = 16 * mb + 4 * qg;
 #pragma unroll
-        for (int r = 0; r < 4; r++) lgp[(t0 + r) * G + i] = x[r];
+        for (int r = 0; r < 4; r++) {
+          if (kLds) lgp[t0 + r] = x[r];
+          else lgp[(t0 + r) * G + i] = x[r];
+        }
       });
     };
     // n_w pages for this wave; the last one is peeled so that no load is
@@ -543,47 +557,59 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
   }
 
   // ---- merge the waves: maxima, rescale, fixed-order sums in LDS ----
+  // Two barriers: after the first every lane derives its column's maximum
+  // and sum from the waves' values itself (same order in every lane).
   sm.lsum = rows_sum(sm.lsum);
   sm.zsum = rows_sum(sm.zsum);
-  __shared__ uint32_t s_bad;
-  if (tid == 0) s_bad = 0;
-  __syncthreads();
-  if (badid) s_bad = 1;
+  __shared__ uint32_t wbad[kWaves];
+  __shared__ int s_tc;
+  __shared__ float s_tcsum;
   if (qg == 0) {
     wm[wid][i] = sm.m;
     wl[wid][i] = sm.lsum;
   }
+  if (lane == 0) wbad[wid] = 0;
+  if (badid) wbad[wid] = 1;
+  if (MODE == 1 && tid == 0) s_tc = -1;
   __syncthreads();
-  const bool bad = s_bad != 0;
-  if (tid < 16) {
+  bool bad = false;
+#pragma unroll
+  for (int w = 0; w < kWaves; w++) bad |= wbad[w] != 0;
+  {
     float M = -INFINITY;
-    for (int w = 0; w < kWaves; w++) M = fmaxf(M, wm[w][tid]);
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) M = fmaxf(M, wm[w][i]);
     float l = 0.0f;
     if (M != -INFINITY)
-      for (int w = 0; w < kWaves; w++) l += wl[w][tid] * __builtin_amdgcn_exp2f(wm[w][tid] - M);
-    sM[tid] = M;
-    sL[tid] = l;
-    sI[tid] = l > 0.0f ? 1.0f / l : 0.0f;
-  }
-  __syncthreads();
-  const int ncol = PACK ? 2 * G : G;  // columns that carry data
-  if (i < ncol) {
-    // O = acc + sum p (z_v - kv s_v) (the z term once per head: not in tail columns)
-    const float M = sM[i];
-    const float f = (M == -INFINITY || sm.m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sm.m - M);
-    const float z = tail ? 0.0f : sm.zsum;
-    // lane (i, qg), block nb: dims 16nb + 4qg .. +3 of column i
 #pragma unroll
-    for (int nb = 0; nb < NB; nb++) buf[wid][i * (D / 4) + 4 * nb + qg] = (acc[nb] + z) * f;
+      for (int w = 0; w < kWaves; w++) l += wl[w][i] * __builtin_amdgcn_exp2f(wm[w][i] - M);
+    if (wid == 0 && qg == 0) {
+      sM[i] = M;
+      sL[i] = l;
+      sI[i] = l > 0.0f ? 1.0f / l : 0.0f;
+    }
+    const int ncol = PACK ? 2 * G : G;  // columns that carry data
+    if (i < ncol) {
+      // O = acc + sum p (z_v - kv s_v) (the z term once per head: not in tail columns)
+      const float f = (M == -INFINITY || sm.m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sm.m - M);
+      const float z = tail ? 0.0f : sm.zsum;
+      // lane (i, qg), block nb: dims 16nb + 4qg .. +3 of column i; the 16-byte
+      // slot index is xor-swizzled with the column so that the 16 columns of
+      // one store land in different banks
+#pragma unroll
+      for (int nb = 0; nb < NB; nb++) buf[wid][i * (D / 4) + ((4 * nb + qg) ^ (i & 15))] = (acc[nb] + z) * f;
+    }
   }
   __syncthreads();
   const float* ob = (const float*)&buf[0][0];
-  auto ocol = [&](int x) {  // x = g * D + dim: sum over waves (fixed order) of column g (+ its tail)
+  auto ocol = [&](int g, int dim) {  // sum over waves (fixed order) of column g (+ its tail)
+    const int o0 = (g * (D / 4) + ((dim >> 2) ^ (g & 15))) * 4 + (dim & 3);
+    const int o1 = ((g + G) * (D / 4) + ((dim >> 2) ^ ((g + G) & 15))) * 4 + (dim & 3);
     float o = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWaves; w++) {
-      o += ob[w * 16 * D + x];
-      if (PACK) o += ob[w * 16 * D + x + G * D];
+      o += ob[w * 16 * D + o0];
+      if (PACK) o += ob[w * 16 * D + o1];
     }
     return o;
   };
@@ -598,7 +624,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
       }
       return;
     }
-    for (int x = tid; x < G * D; x += blockDim.x) orow[x] = ocol(x) * sI[x / D];
+    for (int x = tid; x < G * D; x += blockDim.x) orow[x] = ocol(x / D, x % D) * sI[x / D];
     if (SAVE && tid < G) {
       ml[(u * G + tid) * 2 + 0] = sM[tid];
       ml[(u * G + tid) * 2 + 1] = sL[tid];
@@ -611,88 +637,85 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
       // unit's first high page, so that step needs no scan.
       const Seg sh = tier_seg(D, true), sl = tier_seg(D, false);
       const int64_t N1 = (int64_t)N + 1, tc1 = N1 - pa.W;
-      __shared__ int s_tc;
-      __shared__ float s_tcsum;
       __shared__ Cand cw[2][kWaves];
-      if (tid == 0) s_tc = -1;
-      __syncthreads();
       Cand bh{0.0f, kNoPos, 0}, bl{0.0f, kNoPos, 0};
-      auto consider = [&](int j, int t, int32_t pos, float score) {
-        if (j < ph) {
-          const int ls = 16 * j + t;
-          if (pos == tc1) {  // positions are unique: one writer
-            s_tc = ls;
-            s_tcsum = score;
-          }
-          if (pos <= tc1) bh = min_imp(bh, Cand{score, pos, ls}, N1);
-        } else {
-          bl = min_imp(bl, Cand{score, pos, 32 * (j - ph) + t}, N1);
-        }
-      };
-      if (lg_lds) {
-        // everything is in LDS: the pass only stores
-        float mg[16], ig[16];
+      const int NSL = TPg * 32;  // slots, 32 per page (high pages use 16)
+      // kU slots per thread per round: all loads of a round are issued
+      // before any use; GB >= G logits per slot (indices clamped to G - 1:
+      // repeats do not change a maximum)
+      auto pass = [&](auto lds_tag, auto gb_tag) {
+        constexpr bool kLds = decltype(lds_tag)::value;
+        constexpr int GB = decltype(gb_tag)::value;
+        constexpr int kU = kLds ? 1 : 4;  // LDS reads need no batching
+        float mg[GB], ig[GB];
 #pragma unroll
-        for (int g = 0; g < 16; g++) {
-          mg[g] = g < G ? sM[g] : 0.0f;
-          ig[g] = g < G ? sI[g] : 0.0f;
+        for (int g = 0; g < GB; g++) {
+          mg[g] = sM[min(g, G - 1)];
+          ig[g] = sI[min(g, G - 1)];
         }
-        constexpr int kU = 4;  // independent slots per thread per round
-        for (int x0 = tid; x0 < TPg * 32; x0 += kU * kThreads) {
+        const float* lgg = logits + (int64_t)u * L * 32 * G;
+        // wave-uniform trip count: a wave runs while its first slot is in range
+        for (int x0 = tid; x0 - lane < NSL; x0 += kU * kThreads) {
+          float lv[kU][GB], osv[kU];
+          int32_t psv[kU];
+          uint8_t* pgv[kU];
+#pragma unroll
+          for (int e = 0; e < kU; e++) {
+            const int x = min(x0 + e * kThreads, NSL - 1);
+            const int j = x >> 5, t = x & 31;
+            const bool hi = j < ph;
+            if (kLds) {
+#pragma unroll
+              for (int g = 0; g < GB; g++) lv[e][g] = lg_s[min(g, G - 1) * NSL + x];
+              osv[e] = osc_s[x];
+              psv[e] = pos_s[x];
+              pgv[e] = pages + (int64_t)id_s[j] * page_bytes;
+            } else {
+              const int tx = table_idx(j);
+#pragma unroll
+              for (int g = 0; g < GB; g++) lv[e][g] = lgg[(tx * 32 + t) * G + min(g, G - 1)];
+              pgv[e] = pages + (int64_t)page_id(tx) * page_bytes;
+              const int tt = min(t, hi ? kHiTokens - 1 : kLoTokens - 1);
+              osv[e] = *(const float*)(pgv[e] + (hi ? sh.sc : sl.sc) + 4 * tt);
+              psv[e] = *(const int32_t*)(pgv[e] + (hi ? sh.ps : sl.ps) + 4 * tt);
+            }
+          }
 #pragma unroll
           for (int e = 0; e < kU; e++) {
             const int x = x0 + e * kThreads;
-            if (x >= TPg * 32) break;
             const int j = x >> 5, t = x & 31;
-            if (t >= valid(j) || pos_s[x] >= N) continue;
-            const float* lg = lg_s + x * G;
+            const bool hi = j < ph;
+            const bool ok = x < NSL && t < valid(j) && psv[e] < N;
             float mx = 0.0f;
 #pragma unroll
-            for (int g = 0; g < 16; g++)
-              if (g < G) mx = fmaxf(mx, __builtin_amdgcn_exp2f(lg[g] - mg[g]) * ig[g]);
-            uint8_t* pg = pages + (int64_t)id_s[j] * page_bytes;
-            const float ns = osc_s[x] + mx;
-            *(float*)(pg + (j < ph ? sh.sc : sl.sc) + 4 * t) = ns;
-            consider(j, t, pos_s[x], ns);
+            for (int g = 0; g < GB; g++) mx = fmaxf(mx, __builtin_amdgcn_exp2f(lv[e][g] - mg[g]) * ig[g]);
+            const float ns = osv[e] + mx;
+            const int ls = hi ? 16 * j + t : 32 * (j - ph) + t;
+            if (ok) *(float*)(pgv[e] + (hi ? sh.sc : sl.sc) + 4 * t) = ns;
+            if (ok && hi && psv[e] == tc1) {  // positions are unique: one writer
+              s_tc = ls;
+              s_tcsum = ns;
+            }
+            // one comparison per slot, against the running candidate of its tier
+            const Cand c{ns, (ok && (!hi || psv[e] <= tc1)) ? psv[e] : kNoPos, ls};
+            const Cand a{hi ? bh.sum : bl.sum, hi ? bh.pos : bl.pos, hi ? bh.slot : bl.slot};
+            const bool win = less_imp(c, a, N1);
+            if (win && hi) bh = c;
+            if (win && !hi) bl = c;
           }
         }
+      };
+      using I4 = std::integral_constant<int, 4>;
+      using I8 = std::integral_constant<int, 8>;
+      using I16 = std::integral_constant<int, 16>;
+      if (lg_lds) {
+        if (G <= 4) pass(std::true_type{}, I4{});
+        else if (G <= 8) pass(std::true_type{}, I8{});
+        else pass(std::true_type{}, I16{});
       } else {
-        const float* lgg = logits + (int64_t)u * L * 32 * G;
-        constexpr int kU = 4;
-        for (int x0 = tid; x0 < TPg * 32; x0 += kU * blockDim.x) {
-          float* sc[kU];
-          const int32_t* pp[kU];
-          float old[kU], add[kU];
-#pragma unroll
-          for (int e = 0; e < kU; e++) {
-            const int x = x0 + e * blockDim.x;
-            const int j = x >> 5, t = x & 31;
-            sc[e] = nullptr;
-            add[e] = 0.0f;
-            if (x < TPg * 32 && t < valid(j)) {
-              const float* lg = lgg + (table_idx(j) * 32 + t) * G;
-              float mx = 0.0f;
-              for (int g = 0; g < G; g++) mx = fmaxf(mx, __builtin_amdgcn_exp2f(lg[g] - sM[g]) * sI[g]);
-              add[e] = mx;
-              uint8_t* pg = pages + (int64_t)page_id(table_idx(j)) * page_bytes;
-              sc[e] = (float*)(pg + (j < ph ? sh.sc : sl.sc) + 4 * t);
-              pp[e] = (const int32_t*)(pg + (j < ph ? sh.ps : sl.ps) + 4 * t);
-            }
-          }
-          int32_t pos[kU];
-#pragma unroll
-          for (int e = 0; e < kU; e++) {
-            old[e] = sc[e] ? *sc[e] : 0.0f;
-            pos[e] = sc[e] ? *pp[e] : N;
-          }
-#pragma unroll
-          for (int e = 0; e < kU; e++)
-            if (sc[e] && pos[e] < N) {
-              const int x = x0 + e * blockDim.x;
-              *sc[e] = old[e] + add[e];
-              consider(x >> 5, x & 31, pos[e], old[e] + add[e]);
-            }
-        }
+        if (G <= 4) pass(std::false_type{}, I4{});
+        else if (G <= 8) pass(std::false_type{}, I8{});
+        else pass(std::false_type{}, I16{});
       }
       // the unit's least important candidates: wave butterflies, then the
       // waves' results in lanes 0..7 of wave 0
@@ -728,7 +751,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
     }
   } else {
     float* mp = part + (((int64_t)u * S + split) * G) * (D + 2);
-    for (int x = tid; x < G * D; x += blockDim.x) mp[(x / D) * (D + 2) + x % D] = ocol(x);
+    for (int x = tid; x < G * D; x += blockDim.x) mp[(x / D) * (D + 2) + x % D] = ocol(x / D, x % D);
     if (tid < G) {
       mp[tid * (D + 2) + D] = bad ? NAN : sM[tid];  // NaN marks a bad unit for the merge
       mp[tid * (D + 2) + D + 1] = sL[tid];

@@ -280,6 +280,15 @@ constexpr int plan_rec_off() {
 static_assert(page_bytes_for(64) - tier_seg(64, true).bytes >= 4 * kRecWords, "plan record space");
 static_assert(page_bytes_for(128) - tier_seg(128, true).bytes >= 4 * kRecWords, "plan record space");
 
+// integrity word over the first 12 words (rotate-xor: no multiplies on the
+// single-lane tail that writes a record)
+__device__ inline uint32_t plan_rec_hash(const uint32_t* w) {
+  uint32_t x = 0x9E3779B9u;
+#pragma unroll
+  for (int k = 0; k < 12; k++) x = __builtin_rotateleft32(x, 7) ^ (w[k] + (uint32_t)k);
+  return ~x;
+}
+
 __device__ inline void plan_rec_fill(uint32_t* w, int64_t seq, int nh, int nl, int ph, int pl, const Plan& p) {
   w[0] = kPlanMagic;
   w[1] = (uint32_t)seq;
@@ -293,16 +302,12 @@ __device__ inline void plan_rec_fill(uint32_t* w, int64_t seq, int nh, int nl, i
   w[9] = (uint32_t)p.lo_slot;
   w[10] = (uint32_t)p.lo_app;
   w[11] = (uint32_t)p.nfw;
-  uint32_t x = 0x9E3779B9u;
-  for (int k = 0; k < 12; k++) x = (x ^ w[k]) * 0x01000193u;
-  w[12] = x;
+  w[12] = plan_rec_hash(w);
 }
 
 // true when the record is intact and was made for this length and state
 __device__ inline bool plan_rec_check(const uint32_t* w, int64_t seq, int nh, int nl, int ph, int pl, Plan& p) {
-  uint32_t x = 0x9E3779B9u;
-  for (int k = 0; k < 12; k++) x = (x ^ w[k]) * 0x01000193u;
-  if (w[0] != kPlanMagic || x != w[12] || w[1] != (uint32_t)seq || w[2] != (uint32_t)nh ||
+  if (w[0] != kPlanMagic || plan_rec_hash(w) != w[12] || w[1] != (uint32_t)seq || w[2] != (uint32_t)nh ||
       w[3] != (uint32_t)nl || w[4] != (uint32_t)ph || w[5] != (uint32_t)pl)
     return false;
   p = Plan{(int32_t)w[6], (int32_t)w[7], (int32_t)w[8], (int32_t)w[9], (int32_t)w[10], (int32_t)w[11]};

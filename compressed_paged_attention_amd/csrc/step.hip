@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kPlanThreads) void step_plan_kernel(int H, int L, i
   __syncthreads();
   if (s_rec) return;
   const Seg sh = tier_seg(D, true), sl = tier_seg(D, false);
-  const int64_t Np = N + 1, tc_pos = N - W;
+  const int64_t tc_pos = N - W;
   const double dah = (double)ah, dal = (double)al;
   const Cand none{0.0f, kNoPos, 0};
   Cand bh = none, bl = none;
