@@ -366,14 +366,30 @@ struct PolicyArgs {
   float ah, al;
 };
 
-template <int D, int MODE, bool PACK>
+// The generation step's commit, run in front of the attention (STEP): the
+// step workspace made by the plan kernel, the new tokens and the pool lists.
+struct StepArgs {
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const int64_t* hdr;
+  const int32_t* rec;
+  const int32_t* nf;
+  const int32_t* list;
+  int32_t* table;
+  int32_t* state;
+  uint64_t* ptr;
+  int64_t U;
+  int direct;  // every workgroup redoes the demand prefix sum (no coordination kernel)
+};
+
+template <int D, int MODE, bool PACK, bool STEP>
 __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int S, int64_t P, int page_bytes,
                                                         PolicyArgs pa, float scale_log2, const uint16_t* __restrict__ q,
-                                                        const int32_t* __restrict__ table,
-                                                        const int32_t* __restrict__ state,
+                                                        const int32_t* table, const int32_t* state,
                                                         const int32_t* __restrict__ seq_len, uint8_t* pages,
                                                         float* __restrict__ out, float* __restrict__ part,
-                                                        float* __restrict__ ml, float* logits, uint32_t* status) {
+                                                        float* __restrict__ ml, float* logits, uint32_t* status,
+                                                        StepArgs sa) {
   constexpr bool SAVE = MODE != 0;
   constexpr int NB = D / 16;  // 16-dim blocks (N-blocks of PV)
   constexpr int NS = D / 32;  // 32-dim K-steps of QK
@@ -398,22 +414,117 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
   }
   const int32_t id_guess = row[min(wid, L - 1)];
   const int32_t* s4 = state + 4 * u;
-  const int nh = s4[0], nl = s4[1], ph = s4[2], pl = s4[3];
+  int nh = s4[0], nl = s4[1], ph = s4[2], pl = s4[3];
   const int N = seq_len[b];
+
+  __shared__ float wm[kWaves][16], wl[kWaves][16], sM[16], sL[16], sI[16];
+  // every wave's O columns, for the merge; before that (STEP) the commit's
+  // scratch, whose two page images the page loop reads
+  __shared__ float4_t buf[kWaves][16 * D / 4];
+  static_assert(sizeof(buf) >= 4 * commit_lds_words<D>(), "commit scratch");
+  // fused score update: [TPg*32*G] logits, [TPg*32] old scores, [TPg*32]
+  // positions, [TPg] page ids
+  __shared__ uint32_t lds_w[MODE == 1 ? kLdsWords : 1];
+
+  // ---- generation step fused in front (STEP; one split per unit) ----
+  // Every wave learns the step's decision for the unit (the verdict over all
+  // units' demand words, the unit's plan words), hence the tier state after
+  // the step.  The last wave commits, building the written pages whole in
+  // LDS (over the merge buffer), while the others attend to the pages the
+  // step leaves alone; it then takes a smaller share of those, and the
+  // written pages from their images.
+  constexpr int kCW = kWaves - 1;     // the committing wave
+  constexpr int kCommitPages = 4;     // its commit, in page computes (share)
+  static_assert(sizeof(buf) >= 2 * page_bytes_for(D), "two page images in the merge buffer");
+  __shared__ int s_vd[3 * kWaves];
+  __shared__ int32_t s_idt[2];        // ids of the written high and low pages
+  const uint32_t* img_h = (const uint32_t*)&buf[0][0];
+  const uint32_t* img_l = img_h + page_bytes_for(D) / 4;
+  bool go = false;
+  int jh = -1, jl = -1;               // written pages: page-loop index
+  int tix_h = -1, tix_l = -1;         // ... and table index
+  const int nh0 = nh, nl0 = nl, ph0 = ph, pl0 = pl;  // before the step
+  int need = 0, new_hi = 0, hi_app = 0, lo_src = -1, lo_slot = 0, lo_app = 0, rank = 0;
+  int32_t id_hrow = 0, id_lrow = 0, id_src = 0, id_first = 0;
+  int64_t start = 0;
+  const int kbase = i * D + qg * (D / 4), mq = 16 * qg, vl = lane * (D / 8);
+  uint32_t badid = 0;
+  // page ids are checked where they are used (check: the id names a page of
+  // the unit); a bad id is clamped into the pool (the load stays in bounds)
+  // and zeroes the unit's result
+  auto fetch_id = [&](PageRegs<D>& R, int jj, int32_t id, bool check) {
+    badid |= (uint32_t)(check && (id < 0 || id >= P));
+    id = min(max(id, 0), (int32_t)(P - 1));
+    R.id = id;
+    const uint8_t* pg = pages + (int64_t)id * page_bytes;
+    load_page<D>(R, pg, jj >= ph, kbase, mq, vl);
+    if (MODE == 1) load_page_sp<D>(R, pg, jj >= ph, lane);
+  };
+  PageRegs<D> A, B;
+  bool spec = false;  // A already holds page wid (loads issued before the verdict)
+  if constexpr (STEP) {
+    const int32_t wu = sa.nf[u];
+    const int32_t* R = sa.rec + u * kSRec;
+    new_hi = R[S_NEWHI];
+    hi_app = R[S_HIAPP];
+    lo_src = R[S_LOSRC];
+    lo_slot = R[S_LOSLOT];
+    lo_app = R[S_LOAPP];
+    id_hrow = R[S_IDH];
+    id_lrow = R[S_IDL];
+    id_src = R[S_IDS];
+    id_first = R[S_IDF];
+    need = wu & 3;
+    // a non-committing wave's first page is page wid whatever the verdict,
+    // unless the step writes it: its loads need not wait for the verdict
+    spec = wid < kCW && wid < ph && wid != (new_hi >> 4) && state_ok(nh, nl, ph, pl, L);
+    if (spec) fetch_id(A, wid, id_guess, true);
+    if (sa.direct) {
+      start = sa.hdr[SH_START];
+      const int64_t end = sa.hdr[SH_END];
+      uint32_t fl;
+      int total;
+      step_verdict(u, sa.U, sa.nf, s_vd, fl, total, rank);
+      const uint32_t st = fl ? fl : (total > end - start ? (uint32_t)kStExhausted : 0u);
+      if (u == 0 && tid == 64 * kCW) {
+        if (st) atomicOr(status, st);
+        else sa.ptr[0] = (uint64_t)(start + total);
+      }
+      go = st == 0 && (wu & kActive) != 0;
+    } else {
+      go = sa.hdr[SH_COMMIT] != 0 && (wu & kActive) != 0;
+    }
+    if (go) {
+      nh += hi_app;
+      nl += lo_app;
+      ph += need == kTierHi;
+      pl += need == kTierLo;
+      tix_h = new_hi >> 4;
+      tix_l = lo_src >= 0 ? L - 1 - (lo_slot >> 5) : -1;
+      jh = tix_h;
+      jl = lo_src >= 0 ? ph + (lo_slot >> 5) : -1;
+    }
+  }
+  auto table_idx = [&](int j) { return j < ph ? j : L - 1 - (j - ph); };
+  // page id by table index, the written pages' from LDS (read only after
+  // the commit wave has published them); values, not pointers, are selected
+  auto id_tix = [&](int tix) -> int32_t {
+    const int32_t g = row[tix];
+    if (!STEP) return g;
+    const int32_t a = s_idt[0], c = s_idt[1];
+    return tix == tix_h ? a : (tix == tix_l ? c : g);
+  };
+  auto valid = [&](int j) {
+    return j < ph ? min(kHiTokens, nh - kHiTokens * j) : min(kLoTokens, nl - kLoTokens * (j - ph));
+  };
   const bool sok = state_ok(nh, nl, ph, pl, L);
   const int TPg = sok ? ph + pl : 0;
   const int pps = (TPg + S - 1) / S;
   const int p0 = split * pps;
   const int p1 = min(TPg, p0 + pps);
 
-  __shared__ float wm[kWaves][16], wl[kWaves][16], sM[16], sL[16], sI[16];
-  __shared__ float4_t buf[kWaves][16 * D / 4];  // every wave's O columns, for the merge
-  // fused score update: [TPg*32*G] logits, [TPg*32] old scores, [TPg*32]
-  // positions, [TPg] page ids
-  __shared__ uint32_t lds_w[MODE == 1 ? kLdsWords : 1];
-
   float* orow = out + ((int64_t)b * H * G + (int64_t)h * G) * D;
-  if (N <= 0 || !sok || nh + nl == 0) {
+  if (N <= 0 || !sok || nh + nl == 0) {  // (a committing unit never ends here)
     if (S == 1 || split == 0) {
       for (int x = tid; x < G * D; x += blockDim.x) orow[x] = 0.0f;
       if (SAVE)
@@ -433,32 +544,66 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
     return;
   }
 
-  auto table_idx = [&](int j) { return j < ph ? j : L - 1 - (j - ph); };
-  auto page_id = [&](int tix) { return row[tix]; };
-  auto valid = [&](int j) {
-    return j < ph ? min(kHiTokens, nh - kHiTokens * j) : min(kLoTokens, nl - kLoTokens * (j - ph));
-  };
-  const int kbase = i * D + qg * (D / 4), mq = 16 * qg, vl = lane * (D / 8);
-  uint32_t badid = 0;
-  // page ids are checked where they are used; a bad id is clamped into the
-  // pool (the load stays in bounds) and zeroes the unit's result
-  auto fetch_id = [&](PageRegs<D>& R, int jj, int32_t id) {
-    badid |= (uint32_t)(id < 0 || id >= P);
-    id = min(max(id, 0), (int32_t)(P - 1));
-    R.id = id;
-    const uint8_t* pg = pages + (int64_t)id * page_bytes;
-    load_page<D>(R, pg, jj >= ph, kbase, mq, vl);
-    if (MODE == 1) load_page_sp<D>(R, pg, jj >= ph, lane);
+  // ---- page order (wave-uniform).  Without a step wave w takes p0 + w,
+  // p0 + w + 8, ...; with one, waves 0..6 take the pages below `cut`
+  // round-robin and the commit wave those from `cut` up, then the written
+  // pages, which everyone else skips.
+  const int n_cw = go ? max(0, (TPg - kCommitPages * kCW) / kWaves) : 0;
+  const int cut = TPg - n_cw;
+  auto nextj = [&](int j) -> int {
+    if (!go) {
+      j = j < 0 ? p0 + wid : j + kWaves;
+      return j < p1 ? j : -1;
+    }
+    if (wid < kCW) {
+      j = j < 0 ? wid : j + kCW;
+      while (j < cut && (j == jh || j == jl)) j += kCW;
+      return j < cut ? j : -1;
+    }
+    j = j < 0 ? cut : j + 1;
+    while (j < TPg && (j == jh || j == jl)) j++;
+    return j < TPg ? j : -1;
   };
   auto fetch = [&](PageRegs<D>& R, int jj) {
-    jj = min(jj, p1 - 1);  // past the end: reload the last page (unused)
-    fetch_id(R, jj, page_id(table_idx(jj)));  // uniform index: scalar load
+    fetch_id(R, jj, row[table_idx(jj)], true);  // uniform index: scalar load
   };
-  PageRegs<D> A, B;
-  const bool busy = p0 + wid < p1;
-  if (busy) {
-    const int j0 = p0 + wid;
-    fetch_id(A, j0, (j0 == wid && j0 < ph) ? id_guess : page_id(table_idx(j0)));
+  const int ja0 = nextj(-1);
+  const bool committer = STEP && go && wid == kCW;
+  int n_w;  // this wave's page count
+  if (!go) {
+    n_w = ja0 >= 0 ? (p1 - 1 - ja0) / kWaves + 1 : 0;
+  } else if (wid < kCW) {
+    n_w = wid < cut ? (cut - 1 - wid) / kCW + 1 : 0;
+    n_w -= (jh < cut && jh % kCW == wid) + (jl >= 0 && jl < cut && jl % kCW == wid);
+  } else {
+    n_w = (TPg - cut) - (jh >= cut) - (jl >= cut);  // then the written pages, from LDS
+  }
+  if (ja0 >= 0 && !committer && !(spec && ja0 == wid))
+    fetch_id(A, ja0, (ja0 == wid && ja0 < ph0) ? id_guess : row[table_idx(ja0)], true);
+  if constexpr (STEP) {
+    if (committer) {
+      int32_t page = -1;
+      if (need) page = sa.direct ? sa.list[(uint64_t)(start + rank) % (uint64_t)P] : sa.rec[u * kSRec + S_PAGE];
+      if (need && (page < 0 || page >= P)) {
+        // a corrupt free list: nothing is committed and the unit's result is zeroed
+        if (lane == 0) {
+          atomicOr(status, kStBadState);
+          s_idt[0] = 0;
+          s_idt[1] = 0;
+        }
+        badid = 1;
+      } else {
+        int32_t idh, idl;
+        commit_wave<D>(u, L, page_bytes, P, N, sa.k_new, sa.v_new, nh0, nl0, ph0, pl0, need, page, new_hi,
+                       hi_app, lo_src, lo_slot, lo_app, id_hrow, id_lrow, id_src, id_first, sa.table + u * L,
+                       sa.state + 4 * u, pages, (uint32_t*)img_h, (uint32_t*)img_l, idh, idl);
+        if (lane == 0) {
+          s_idt[0] = min(max(idh, 0), (int32_t)(P - 1));
+          s_idt[1] = min(max(idl, 0), (int32_t)(P - 1));
+        }
+      }
+      if (ja0 >= 0) fetch(A, ja0);
+    }
   }
 
   // ---- Q operand: lane (i, qg) holds column i's head, dims qg*QD .. +QD-1;
@@ -508,7 +653,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
   // per-block stores need no branch.
   auto page_loop = [&](auto lds_tag) {
     constexpr bool kLds = decltype(lds_tag)::value;
-    auto run = [&](const PageRegs<D>& R, int j) {
+    auto run = [&](PageRegs<D>& R, int j) {
       if (kLds) {
         if (lane < 32) osc_s[j * 32 + lane] = __uint_as_float(R.sp);
         else pos_s[j * 32 + lane - 32] = (int32_t)R.sp;
@@ -526,28 +671,48 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
         }
       });
     };
-    // n_w pages for this wave; the last one is peeled so that no load is
-    // still in flight when the wave reaches the merge
-    int j = p0 + wid;
-    const int n_w = (p1 - 1 - j) / kWaves + 1;
+    // A and B alternate over the wave's n_w pages; the last one is peeled
+    // so that no load is in flight when the wave reaches the merge (the
+    // loads of each iteration are unconditional: nothing for the compiler
+    // to wait on at a join)
+    int ja = ja0;
     int k = 1;
+    if (n_w > 0) {
     for (; k + 2 <= n_w; k += 2) {
-      fetch(B, j + kWaves);
-      run(A, j);
-      j += kWaves;
-      fetch(A, j + kWaves);
-      run(B, j);
-      j += kWaves;
+      const int jb = nextj(ja);
+      fetch(B, jb);
+      run(A, ja);
+      ja = nextj(jb);
+      fetch(A, ja);
+      run(B, jb);
     }
     if (k < n_w) {
-      fetch(B, j + kWaves);
-      run(A, j);
-      run(B, j + kWaves);
+      const int jb = nextj(ja);
+      fetch(B, jb);
+      run(A, ja);
+      run(B, jb);
     } else {
-      run(A, j);
+      run(A, ja);
+    }
+    }
+    if constexpr (STEP) {
+      // the commit wave: the pages the step wrote, from their LDS images
+      // (after the regular loop, so that no join in it mixes LDS and memory
+      // loads of a page)
+      if (committer) {
+        for (int t = 0; t < 2; t++) {
+          const int j = t == 0 ? jh : jl;
+          if (j < 0) continue;
+          const uint8_t* img = (const uint8_t*)(t == 0 ? img_h : img_l);
+          load_page<D>(A, img, j >= ph, kbase, mq, vl);
+          if (MODE == 1) load_page_sp<D>(A, img, j >= ph, lane);
+          A.id = s_idt[t];
+          run(A, j);
+        }
+      }
     }
   };
-  if (busy) {
+  if (n_w > 0 || committer) {
     if constexpr (MODE == 1) {
       if (lg_lds) page_loop(std::true_type{});
       else page_loop(std::false_type{});
@@ -674,7 +839,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
               const int tx = table_idx(j);
 #pragma unroll
               for (int g = 0; g < GB; g++) lv[e][g] = lgg[(tx * 32 + t) * G + min(g, G - 1)];
-              pgv[e] = pages + (int64_t)page_id(tx) * page_bytes;
+              pgv[e] = pages + (int64_t)id_tix(tx) * page_bytes;
               const int tt = min(t, hi ? kHiTokens - 1 : kLoTokens - 1);
               osv[e] = *(const float*)(pgv[e] + (hi ? sh.sc : sl.sc) + 4 * tt);
               psv[e] = *(const int32_t*)(pgv[e] + (hi ? sh.ps : sl.ps) + 4 * tt);
@@ -743,7 +908,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
                                       L, tcs, s_tcsum, bh, bl);
           uint32_t rw[kRecWords];
           plan_rec_fill(rw, N1, nh, nl, ph, pl, pn);
-          uint32_t* dst = (uint32_t*)(pages + (int64_t)page_id(0) * page_bytes + plan_rec_off<D>());
+          uint32_t* dst = (uint32_t*)(pages + (int64_t)id_tix(0) * page_bytes + plan_rec_off<D>());
 #pragma unroll
           for (int k = 0; k < kRecWords; k++) dst[k] = rw[k];
         }
@@ -876,10 +1041,11 @@ hipError_t launch_attn(const Cfg& c, const Pool& p, int batch, const uint16_t* q
   // head and tail of the weights share one matrix instruction when 2G <= 16
   const bool pack = 2 * c.G <= 16;
   const PolicyArgs pa{c.W, c.S_max, c.lo_en, c.ah, c.al};
-#define DKV_ATTN(D, M, PK)                                                                              \
-  attn_kernel<D, M, PK><<<grid, block, 0, s>>>(c.H, c.G, c.L, S, p.P, p.page_bytes, pa, scale_log2, q,     \
-                                               table, state, seq_len, p.pages, out, w.part, w.ml, w.logits,  \
-                                               p.status)
+  const StepArgs none{};
+#define DKV_ATTN(D, M, PK)                                                                                 \
+  attn_kernel<D, M, PK, false><<<grid, block, 0, s>>>(c.H, c.G, c.L, S, p.P, p.page_bytes, pa, scale_log2, q, \
+                                                      table, state, seq_len, p.pages, out, w.part, w.ml,      \
+                                                      w.logits, p.status, none)
 #define DKV_ATTN_D(D)                                    \
   if (pack) {                                            \
     if (kmode == 0) DKV_ATTN(D, 0, true);                \
@@ -913,12 +1079,54 @@ hipError_t launch_attn(const Cfg& c, const Pool& p, int batch, const uint16_t* q
   return hipSuccess;
 }
 
+// With one split per unit the step's commit runs inside the attention
+// workgroup (plan kernel, then one kernel); otherwise plan, commit and
+// attention kernels in turn.
 hipError_t launch_decode_step(const Cfg& c, const Pool& p, int batch, const int32_t* seq_len, const uint16_t* k,
                               const uint16_t* v, const uint16_t* q, int32_t* table, int32_t* state, float* out,
                               int mode, void* ws_step, void* ws_attn, hipStream_t s) {
-  hipError_t e = launch_step(c, p, batch, seq_len, k, v, table, state, ws_step, s);
+  const int64_t U = (int64_t)batch * c.H;
+  if (U == 0) return hipSuccess;
+  const int S = attn_splits(c, batch);
+  if (S != 1) {
+    hipError_t e = launch_step(c, p, batch, seq_len, k, v, table, state, ws_step, s);
+    if (e != hipSuccess) return e;
+    return launch_attn(c, p, batch, q, table, state, seq_len, out, mode, ws_attn, s);
+  }
+  hipError_t e = launch_step_plan(c, p, batch, seq_len, table, state, ws_step, s);
   if (e != hipSuccess) return e;
-  return launch_attn(c, p, batch, q, table, state, seq_len, out, mode, ws_attn, s);
+  const bool direct = U <= kDirectUnits;
+  if (!direct) {
+    e = launch_step_coord(c, p, batch, ws_step, s);
+    if (e != hipSuccess) return e;
+  }
+  const StepWs sw = step_carve(c, batch, ws_step);
+  AttnWs w = attn_carve(c, batch, mode != 0, ws_attn, nullptr);
+  const float scale_log2 = (1.0f / sqrtf((float)c.d)) * kLog2e;
+  const dim3 grid(1, (unsigned)U), block(kThreads);
+  const bool pack = 2 * c.G <= 16;
+  const PolicyArgs pa{c.W, c.S_max, c.lo_en, c.ah, c.al};
+  const StepArgs sa{k, v, sw.hdr, sw.rec, sw.nf, p.list, table, state, p.ptr, U, direct ? 1 : 0};
+#define DKV_STEP(D, M, PK)                                                                                \
+  attn_kernel<D, M, PK, true><<<grid, block, 0, s>>>(c.H, c.G, c.L, 1, p.P, p.page_bytes, pa, scale_log2, q, \
+                                                     table, state, seq_len, p.pages, out, w.part, w.ml,      \
+                                                     w.logits, p.status, sa)
+#define DKV_STEP_D(D)                           \
+  if (pack) {                                   \
+    if (mode == 0) DKV_STEP(D, 0, true);        \
+    else DKV_STEP(D, 1, true);                  \
+  } else {                                      \
+    if (mode == 0) DKV_STEP(D, 0, false);       \
+    else DKV_STEP(D, 1, false);                 \
+  }
+  if (c.d == 128) {
+    DKV_STEP_D(128)
+  } else {
+    DKV_STEP_D(64)
+  }
+#undef DKV_STEP_D
+#undef DKV_STEP
+  return hipGetLastError();
 }
 
 }  // namespace dkv

@@ -43,6 +43,8 @@ hipError_t launch_step(const Cfg& c, const Pool& p, int batch, const int32_t* se
 // the two halves of launch_step
 hipError_t launch_step_plan(const Cfg& c, const Pool& p, int batch, const int32_t* seq_len,
                             const int32_t* table, const int32_t* state, void* ws, hipStream_t s);
+// prefix sum of page demand in one workgroup (past the direct-commit size)
+hipError_t launch_step_coord(const Cfg& c, const Pool& p, int batch, void* ws, hipStream_t s);
 hipError_t launch_step_commit(const Cfg& c, const Pool& p, int batch, const int32_t* seq_len,
                               const uint16_t* k, const uint16_t* v, int32_t* table, int32_t* state,
                               void* ws, hipStream_t s);

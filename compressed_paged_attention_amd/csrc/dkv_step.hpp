@@ -1,5 +1,6 @@
-// dkv_step.hpp -- generation-step commit of one unit, shared by the step
-// commit kernel and the fused step + attention kernel.
+// dkv_step.hpp -- generation-step commit of one unit: by a workgroup (the
+// step commit kernel) or by one wave of the attention workgroup (the decode
+// step), with the plan and plan-record helpers both use.
 //
 // Step workspace: a header (pointer snapshot, commit flag), per-unit plan
 // records and one demand word per unit (see step.hip for the plan).
@@ -12,8 +13,11 @@ namespace dkv {
 
 // Per-unit plan record and a compact demand word per unit:
 //   nf[u] = need tier (bits 0-1: 0 none, 1 low, 2 high) | kActive | status flags << 8
-constexpr int kSRec = 8;
-enum { S_NEWHI = 0, S_HIAPP, S_LOSRC, S_LOSLOT, S_LOAPP, S_PAGE };
+// The record also carries the ids of the pages the commit reads (the high
+// page of slot new_hi, the low page of slot lo_slot, the high page of
+// lo_src, the first high page), so the commit needs no table lookup.
+constexpr int kSRec = 12;
+enum { S_NEWHI = 0, S_HIAPP, S_LOSRC, S_LOSLOT, S_LOAPP, S_PAGE, S_IDH, S_IDL, S_IDS, S_IDF };
 enum { SH_COMMIT = 0, SH_START, SH_END, SH_D };
 constexpr int32_t kActive = 4;
 // Up to this many units every commit workgroup redoes the unit-order prefix
@@ -265,6 +269,25 @@ __device__ inline Plan plan_decide(int64_t N, int W, int S_max, int lo_en, doubl
   return r;
 }
 
+// The step workspace's record of unit u: the plan and the page ids it
+// names (row: the unit's table row, any readable copy; indices clamped into
+// it, as a unit without a commit reads but does not use some entry).
+template <typename RowAt>
+__device__ inline void step_rec_put(int32_t* R, int32_t* nfu, const Plan& x, int L, RowAt row_at) {
+  auto cl = [&](int t) { return min(max(t, 0), L - 1); };
+  R[S_NEWHI] = x.new_hi;
+  R[S_HIAPP] = x.hi_app;
+  R[S_LOSRC] = x.lo_src;
+  R[S_LOSLOT] = x.lo_slot;
+  R[S_LOAPP] = x.lo_app;
+  R[S_PAGE] = -1;
+  R[S_IDH] = row_at(cl(x.new_hi >> 4));
+  R[S_IDL] = row_at(cl(L - 1 - (x.lo_slot >> 5)));
+  R[S_IDS] = row_at(cl(x.lo_src >> 4));
+  R[S_IDF] = row_at(0);
+  *nfu = x.nfw;
+}
+
 // Plan record of the next step, kept in the spare bytes after the last
 // segment of a unit's first high page (table entry 0): written by a
 // workgroup that has just updated all of the unit's score sums, read by the
@@ -362,11 +385,7 @@ __device__ UnitState commit_unit(int64_t u, int H, int L, int64_t U, int64_t P, 
   const int nh = res.nh, nl = res.nl, ph = res.ph, pl = res.pl;
   const int new_hi = R[S_NEWHI], lo_src = R[S_LOSRC], lo_slot = R[S_LOSLOT];
   const int hi_app = R[S_HIAPP], lo_app = R[S_LOAPP];
-  auto clampL = [&](int t) { return min(max(t, 0), L - 1); };
-  const int32_t id_hrow = row[clampL(new_hi >> 4)];
-  const int32_t id_lrow = row[clampL(L - 1 - (lo_slot >> 5))];
-  const int32_t id_src = row[clampL(lo_src >> 4)];
-  const int32_t id_first = row[0];
+  const int32_t id_hrow = R[S_IDH], id_lrow = R[S_IDL], id_src = R[S_IDS], id_first = R[S_IDF];
   int64_t start = 0, end = 0;
   if constexpr (DIRECT) {
     start = hdr[SH_START];
@@ -478,6 +497,201 @@ __device__ UnitState commit_unit(int64_t u, int H, int L, int64_t U, int64_t P, 
     s4[3] = res.pl;
   }
   return res;
+}
+
+// ---------------------------------------------------------------------------
+// The step's commit inside the attention workgroup: every thread takes part
+// in the verdict; one wave then commits while the others attend.
+// ---------------------------------------------------------------------------
+
+// All threads of the workgroup: status flags of any unit, the total page
+// demand and the number of units before u that need a page, from the demand
+// words in one pass (no barrier inside it); lds holds 3 ints per wave.
+__device__ inline void step_verdict(int64_t u, int64_t U, const int32_t* nf, int* lds, uint32_t& flags, int& total,
+                                    int& rank) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int tot = 0, rk = 0;
+  uint32_t fl = 0;
+#pragma unroll 4
+  for (int64_t base = 0; base < U; base += blockDim.x) {
+    const int64_t x = base + threadIdx.x;
+    const int32_t w = x < U ? nf[x] : 0;
+    fl |= (uint32_t)w >> 8;
+    const bool need = (w & 3) != 0;
+    tot += __popcll(__ballot(need));
+    rk += __popcll(__ballot(need && x < u));
+  }
+  fl = wave_reduce(fl, [](uint32_t a, uint32_t b) { return a | b; });
+  if (lane == 0) {
+    lds[wid] = tot;
+    lds[nw + wid] = rk;
+    lds[2 * nw + wid] = (int)fl;
+  }
+  __syncthreads();
+  total = 0;
+  rank = 0;
+  flags = 0;
+  for (int w = 0; w < nw; w++) {
+    total += lds[w];
+    rank += lds[nw + w];
+    flags |= (uint32_t)lds[2 * nw + w];
+  }
+}
+
+// The commit of unit u by one wave, after a positive verdict (need, page:
+// the new page's tier and id).  The written pages are built whole in LDS
+// (img_h, img_l: the high page of the new token, the low page of the
+// requantized token), their changed bytes stored, then the table and the
+// tier state.  The wave's LDS operations complete in program order, so no
+// barrier is needed between the phases.  id_h, id_l: the written pages' ids.
+template <int D>
+__device__ __forceinline__ void commit_wave(int64_t u, int L, int page_bytes, int64_t P, int N, const uint16_t* k_new,
+                                   const uint16_t* v_new, int nh, int nl, int ph, int pl, int need, int32_t page,
+                                   int new_hi, int hi_app, int lo_src, int lo_slot, int lo_app, int32_t id_hrow,
+                                   int32_t id_lrow, int32_t id_src, int32_t id_first, int32_t* row, int32_t* s4,
+                                   uint8_t* pages, uint32_t* img_h, uint32_t* img_l, int32_t& id_h,
+                                   int32_t& id_l) {
+  constexpr Seg sh = tier_seg(D, true);
+  constexpr int PD = D / 64;  // dims per lane
+  const int lane = threadIdx.x & 63;
+  float xk[PD], xv[PD];
+#pragma unroll
+  for (int e = 0; e < PD; e++) {
+    xk[e] = h2f(k_new[u * D + lane + 64 * e]);
+    xv[e] = h2f(v_new[u * D + lane + 64 * e]);
+  }
+  const TokWrite th{true, true, need == kTierHi, new_hi & 15, need == kTierHi ? page : id_hrow};
+  const TokWrite tl{lo_src >= 0, false, need == kTierLo, lo_slot & 31,
+                    lo_src < 0 ? 0 : (need == kTierLo ? page : id_lrow)};
+  id_h = th.id;
+  id_l = tl.id;
+  // an existing page goes straight from memory into its LDS image (16 bytes
+  // per lane and instruction, every chunk in flight at once, no registers);
+  // a fresh one is zeroed
+  constexpr int kPB = page_bytes_for(D);
+  auto img_full = [&](uint32_t* img, const TokWrite& t) {
+    if (!t.on) return;
+    if (t.fresh) {
+      for (int c = lane; c < kPB / 16; c += 64) ((uint4*)img)[c] = make_uint4(0u, 0u, 0u, 0u);
+    } else {
+      const uint8_t* src = pages + (int64_t)t.id * page_bytes;
+#pragma unroll
+      for (int c = 0; c < (kPB + 1023) / 1024; c++)
+        if (c * 1024 + lane * 16 < kPB)
+          __builtin_amdgcn_global_load_lds((const void*)(src + c * 1024 + lane * 16),
+                                           (__attribute__((address_space(3))) void*)((uint8_t*)img + c * 1024),
+                                           16, 0, 0);
+    }
+  };
+  img_full(img_h, th);
+  img_full(img_l, tl);
+  // the requantized token's dequantized values (its high slot may be the
+  // new token's: read before anything is written)
+  float xk_rq[PD], xv_rq[PD], sc_rq = 0.0f;
+  int32_t pos_rq = 0;
+#pragma unroll
+  for (int e = 0; e < PD; e++) xk_rq[e] = xv_rq[e] = 0.0f;
+  if (tl.on) {
+    const uint8_t* src = pages + (int64_t)id_src * page_bytes;
+    const int si = lo_src & 15;
+    const uint32_t km = *(const uint32_t*)(src + sh.km + 4 * si);
+    const uint32_t vm = *(const uint32_t*)(src + sh.vm + 4 * si);
+    sc_rq = *(const float*)(src + sh.sc + 4 * si);
+    pos_rq = *(const int32_t*)(src + sh.ps + 4 * si);
+#pragma unroll
+    for (int e = 0; e < PD; e++) {
+      int byte, shift;
+      k_field(D, true, si, lane + 64 * e, byte, shift);
+      xk_rq[e] = dequant(h2f((uint16_t)km), h2f((uint16_t)(km >> 16)), ((uint32_t)src[byte] >> shift) & 0xFFu);
+      v_field(D, true, si, lane + 64 * e, byte, shift);
+      xv_rq[e] = dequant(h2f((uint16_t)vm), h2f((uint16_t)(vm >> 16)), ((uint32_t)src[byte] >> shift) & 0xFu);
+    }
+  }
+  float mn[4], mx[4];
+  mn[0] = mx[0] = xk[0];
+  mn[1] = mx[1] = xv[0];
+  mn[2] = mx[2] = xk_rq[0];
+  mn[3] = mx[3] = xv_rq[0];
+#pragma unroll
+  for (int e = 1; e < PD; e++) {
+    mn[0] = fminf(mn[0], xk[e]);
+    mx[0] = fmaxf(mx[0], xk[e]);
+    mn[1] = fminf(mn[1], xv[e]);
+    mx[1] = fmaxf(mx[1], xv[e]);
+    mn[2] = fminf(mn[2], xk_rq[e]);
+    mx[2] = fmaxf(mx[2], xk_rq[e]);
+    mn[3] = fminf(mn[3], xv_rq[e]);
+    mx[3] = fmaxf(mx[3], xv_rq[e]);
+  }
+#pragma unroll
+  for (int v = 0; v < 4; v++) {
+    mn[v] = wave_min(mn[v]);
+    mx[v] = wave_max(mx[v]);
+  }
+  // the images have landed (their loads count as vector memory reads)
+  // before any field edit: s_waitcnt vmcnt(0)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  asm volatile("" ::: "memory");
+  auto put = [&](uint32_t* img, const TokWrite& t, const float* xkv, const float* xvv, float kmn, float kmx,
+                 float vmn, float vmx, float score, int32_t pos) {
+    const Seg sg = tier_seg(D, t.hi);
+    uint16_t ks16, kz16, vs16, vz16;
+    float ks, kz, vs, vz;
+    codec_params(kmn, kmx, sg.kbits, ks16, kz16, ks, kz);
+    codec_params(vmn, vmx, sg.vbits, vs16, vz16, vs, vz);
+#pragma unroll
+    for (int e = 0; e < PD; e++) {
+      int byte, shift;
+      k_field(D, t.hi, t.idx, lane + 64 * e, byte, shift);
+      lds_put(img, byte, shift, sg.kbits, codec_code(xkv[e], ks, kz, sg.kbits));
+      v_field(D, t.hi, t.idx, lane + 64 * e, byte, shift);
+      lds_put(img, byte, shift, sg.vbits, codec_code(xvv[e], vs, vz, sg.vbits));
+    }
+    if (lane == 0) {
+      img[sg.km / 4 + t.idx] = (uint32_t)ks16 | ((uint32_t)kz16 << 16);
+      img[sg.vm / 4 + t.idx] = (uint32_t)vs16 | ((uint32_t)vz16 << 16);
+      img[sg.sc / 4 + t.idx] = __float_as_uint(score);
+      img[sg.ps / 4 + t.idx] = (uint32_t)pos;
+    }
+  };
+  put(img_h, th, xk, xv, mn[0], mx[0], mn[1], mx[1], 0.0f, N);
+  if (tl.on) put(img_l, tl, xk_rq, xv_rq, mn[2], mx[2], mn[3], mx[3], sc_rq, pos_rq);
+  asm volatile("" ::: "memory");  // every field is written before the stores read the images
+  auto store = [&](const uint32_t* img, const TokWrite& t) {
+    if (!t.on) return;
+    const Seg sg = tier_seg(D, t.hi);
+    uint8_t* pg = pages + (int64_t)t.id * page_bytes;
+    if (t.fresh) {
+      for (int c = lane; c < page_bytes / 16; c += 64) ((uint4*)pg)[c] = ((const uint4*)img)[c];
+      return;
+    }
+    const int kb = t.idx * D * sg.kbits / 8, kn = D * sg.kbits / 128;  // 16-byte chunks
+    const int vn = (sg.vm - sg.vc) / 16;
+    for (int c = lane; c < kn + vn + 4; c += 64) {
+      if (c < kn) {
+        ((uint4*)(pg + kb))[c] = ((const uint4*)(img + kb / 4))[c];
+      } else if (c < kn + vn) {
+        ((uint4*)(pg + sg.vc))[c - kn] = ((const uint4*)(img + sg.vc / 4))[c - kn];
+      } else {
+        const int seg = c - kn - vn;
+        const int off = (seg == 0 ? sg.km : seg == 1 ? sg.vm : seg == 2 ? sg.sc : sg.ps) + 4 * t.idx;
+        *(uint32_t*)(pg + off) = img[off / 4];
+      }
+    }
+  };
+  store(img_h, th);
+  store(img_l, tl);
+  if (lane == 0) {
+    // the unit changed: its plan record (first high page) no longer applies
+    if (ph >= 1 && id_first >= 0 && id_first < P)
+      *(uint32_t*)(pages + (int64_t)id_first * page_bytes + plan_rec_off<D>()) = 0u;
+    if (need == kTierHi) row[ph] = page;
+    if (need == kTierLo) row[L - 1 - pl] = page;
+    s4[0] = nh + hi_app;
+    s4[1] = nl + lo_app;
+    s4[2] = ph + (need == kTierHi);
+    s4[3] = pl + (need == kTierLo);
+  }
 }
 
 }  // namespace dkv

@@ -113,13 +113,7 @@ __global__ __launch_bounds__(kPlanThreads) void step_plan_kernel(int H, int L, i
       Plan pr;
       if (plan_rec_check(rw, N, nh, nl, ph, pl, pr)) {
         s_rec = 1;
-        R[S_NEWHI] = pr.new_hi;
-        R[S_HIAPP] = pr.hi_app;
-        R[S_LOSRC] = pr.lo_src;
-        R[S_LOSLOT] = pr.lo_slot;
-        R[S_LOAPP] = pr.lo_app;
-        R[S_PAGE] = -1;
-        nf[u] = pr.nfw;
+        step_rec_put(R, nf + u, pr, L, page_of);
       }
     }
   }
@@ -205,13 +199,7 @@ __global__ __launch_bounds__(kPlanThreads) void step_plan_kernel(int H, int L, i
     return;
   }
   const Plan pl_ = plan_decide(N, W, S_max, lo_en, dah, dal, nh, nl, ph, pl, L, tcs, tcsum, bh, bl);
-  R[S_NEWHI] = pl_.new_hi;
-  R[S_HIAPP] = pl_.hi_app;
-  R[S_LOSRC] = pl_.lo_src;
-  R[S_LOSLOT] = pl_.lo_slot;
-  R[S_LOAPP] = pl_.lo_app;
-  R[S_PAGE] = -1;
-  nf[u] = pl_.nfw;
+  step_rec_put(R, nf + u, pl_, L, page_of);
 }
 
 // Coordination for large batches: prefix sum over the demand words, capacity
@@ -294,6 +282,14 @@ hipError_t launch_step_plan(const Cfg& c, const Pool& p, int batch, const int32_
   if (c.d == 128) DKV_PLAN(128);
   else DKV_PLAN(64);
 #undef DKV_PLAN
+  return hipGetLastError();
+}
+
+hipError_t launch_step_coord(const Cfg& c, const Pool& p, int batch, void* ws, hipStream_t s) {
+  const int64_t U = (int64_t)batch * c.H;
+  if (U == 0) return hipSuccess;
+  const StepWs w = step_carve(c, batch, ws);
+  step_coord_kernel<<<dim3(1), dim3(1024), 0, s>>>(U, p.P, w.nf, w.rec, p.list, w.hdr, p.ptr, p.status);
   return hipGetLastError();
 }
 

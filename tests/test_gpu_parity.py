@@ -289,8 +289,12 @@ def test_many_units_coordination_kernel(dk, orc):
     for step in range(4):
         dec = synth.make_decode(cfg, step)
         _say("  step", step)
-        p.step(seq, dec["k_new"].numpy(), dec["v_new"].numpy(), f"step {step}")
-        p.attend(dec["q"].numpy(), seq, True, f"attn {step}")
+        if step % 2:  # the decode-step entry: commit inside the attention workgroups
+            p.decode_step(seq, dec["k_new"].numpy(), dec["v_new"].numpy(), dec["q"].numpy(), True,
+                          f"decode step {step}")
+        else:
+            p.step(seq, dec["k_new"].numpy(), dec["v_new"].numpy(), f"step {step}")
+            p.attend(dec["q"].numpy(), seq, True, f"attn {step}")
         seq = seq + 1
     check_pool_invariants(orc, p.o)
 
@@ -316,10 +320,14 @@ def test_fused_scores_large_units(dk, orc):
     G = cfg["gqa_group"]
     assert (pages * 32 * (G + 2) + pages > 16384).any() and (pages * 32 * (G + 2) + pages <= 16384).any()
     seq = lens.numpy().astype(np.int32)
-    for step in range(2):
+    for step in range(3):
         dec = synth.make_decode(cfg, step)
-        p.step(seq, dec["k_new"].numpy(), dec["v_new"].numpy(), f"step {step}")
-        p.attend(dec["q"].numpy(), seq, True, f"attn {step}")
+        if step == 2:  # the decode-step entry (commit inside the attention workgroups)
+            p.decode_step(seq, dec["k_new"].numpy(), dec["v_new"].numpy(), dec["q"].numpy(), True,
+                          f"decode step {step}")
+        else:
+            p.step(seq, dec["k_new"].numpy(), dec["v_new"].numpy(), f"step {step}")
+            p.attend(dec["q"].numpy(), seq, True, f"attn {step}")
         seq = seq + 1
 
 
