@@ -21,7 +21,9 @@ stream the library launches on, each over back-to-back launches while a spin
 kernel issued before the start event holds the stream (so the events measure
 the device, not the host's launch rate): the K complete steps (value), K
 attention launches alone on the final caches (attn_us, roofline), and K more
-compaction steps alone (compaction_us_per_step).  The roofline object
+compaction steps alone through the separate kernels (compaction_us_per_step).
+The compaction's share of a step is (step - attention alone) / step.  The
+roofline object
 describes the attention kernel: algorithmic bytes per launch (codes +
 metadata of every retained token, q, out, table entries, and the 8-byte
 read-modify-write of each retained token's score) over its mean duration.
@@ -55,6 +57,7 @@ def algorithmic_attn_bytes(tier_state, B, H, G, d):
 
 KERNEL_SOURCES = ("compressed_paged_attention_amd/csrc/attention.hip",
                   "compressed_paged_attention_amd/csrc/dkv_common.hpp",
+                  "compressed_paged_attention_amd/csrc/dkv_step.hpp",
                   "compressed_paged_attention_amd/csrc/dkv_launch.hpp")
 TRAFFIC_FILE = "profiles/attn_kernel_llama3_8b_traffic.txt"
 
@@ -288,7 +291,9 @@ def main():
         "attn_tokens_per_s": B / t_attn_s,
         "attn_us": float(attn.mean()) * 1e3,
         "compaction_us_per_step": float(comp.mean()) * 1e3,
-        "compaction_share": float(comp.mean() / (comp.mean() + attn.mean())),
+        # the compaction's cost inside a step: the step minus attention alone
+        "step_minus_attention_us": step_ms * 1e3 - float(attn.mean()) * 1e3,
+        "compaction_share": float((step_ms - attn.mean()) / step_ms),
         "prompt_compaction_us": float(np.mean(prompt_ms)) * 1e3,
         "prompt_input_GBps": (total * H * d * 4 + total * H * 4) / (np.mean(prompt_ms) * 1e-3) / 1e9,
         "release_us": float(np.mean(rel_ms)) * 1e3,

@@ -368,6 +368,11 @@ struct PolicyArgs {
 
 // The generation step's commit, run in front of the attention (STEP): the
 // step workspace made by the plan kernel, the new tokens and the pool lists.
+// The kernel reads the table and tier state through its read-only (and
+// restrict) parameters and writes them only through these: the one table
+// entry a step writes (a new page's) is never read back in the kernel, whose
+// page loop and score pass take that id from LDS, and the tier state is read
+// before the commit.
 struct StepArgs {
   const uint16_t* k_new;
   const uint16_t* v_new;
@@ -385,7 +390,8 @@ struct StepArgs {
 template <int D, int MODE, bool PACK, bool STEP>
 __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int S, int64_t P, int page_bytes,
                                                         PolicyArgs pa, float scale_log2, const uint16_t* __restrict__ q,
-                                                        const int32_t* table, const int32_t* state,
+                                                        const int32_t* __restrict__ table,
+                                                        const int32_t* __restrict__ state,
                                                         const int32_t* __restrict__ seq_len, uint8_t* pages,
                                                         float* __restrict__ out, float* __restrict__ part,
                                                         float* __restrict__ ml, float* logits, uint32_t* status,
@@ -812,11 +818,13 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
         constexpr bool kLds = decltype(lds_tag)::value;
         constexpr int GB = decltype(gb_tag)::value;
         constexpr int kU = kLds ? 1 : 4;  // LDS reads need no batching
-        float mg[GB], ig[GB];
+        // max_g 2^(x_g - M_g) / L_g = 2^(max_g (x_g + c_g)), c_g = -M_g - log2 L_g:
+        // one exponential per slot
+        float cg[GB];
 #pragma unroll
         for (int g = 0; g < GB; g++) {
-          mg[g] = sM[min(g, G - 1)];
-          ig[g] = sI[min(g, G - 1)];
+          const float M = sM[min(g, G - 1)], I = sI[min(g, G - 1)];
+          cg[g] = (M == -INFINITY || I == 0.0f) ? -INFINITY : __builtin_amdgcn_logf(I) - M;
         }
         const float* lgg = logits + (int64_t)u * L * 32 * G;
         // wave-uniform trip count: a wave runs while its first slot is in range
@@ -851,10 +859,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
             const int j = x >> 5, t = x & 31;
             const bool hi = j < ph;
             const bool ok = x < NSL && t < valid(j) && psv[e] < N;
-            float mx = 0.0f;
+            float xm = -INFINITY;
 #pragma unroll
-            for (int g = 0; g < GB; g++) mx = fmaxf(mx, __builtin_amdgcn_exp2f(lv[e][g] - mg[g]) * ig[g]);
-            const float ns = osv[e] + mx;
+            for (int g = 0; g < GB; g++) xm = fmaxf(xm, lv[e][g] + cg[g]);
+            const float ns = osv[e] + __builtin_amdgcn_exp2f(xm);
             const int ls = hi ? 16 * j + t : 32 * (j - ph) + t;
             if (ok) *(float*)(pgv[e] + (hi ? sh.sc : sl.sc) + 4 * t) = ns;
             if (ok && hi && psv[e] == tc1) {  // positions are unique: one writer

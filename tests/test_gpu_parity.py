@@ -175,6 +175,46 @@ def test_ragged_prompt_step_attention(dk, orc, d, G, lo):
     p.attend(dec["q"].numpy(), seq, True, "attn after re-admit")
 
 
+@pytest.mark.parametrize("d,G,lo", [(128, 4, 1), (64, 5, 1), (128, 7, 0), (128, 8, 1), (64, 16, 1)])
+def test_decode_step_fused_variants(dk, orc, d, G, lo):
+    """diffkv_decode_step through the fused kernel (short rows: one split per
+    unit) for both head sizes, both weight-column layouts (2G <= 16 or not)
+    and the low tier off; ragged lengths with tails inside pages, steps that
+    cross page boundaries, then release and re-admission."""
+    from workloads import synth
+    cfg = _medium_cfg("llama3_8b", head_dim=d, gqa_group=G, lo_enabled=lo, num_kv_heads=3,
+                      batch=5, max_seq_len=420, window=64)
+    assert dk.diffkv_attn_splits(cfg, 5) == 1
+    lens = torch.tensor([383, 37, 200, 127, 64], dtype=torch.int64)
+    pr = synth.make_prompt(cfg, lens=lens)
+    cu = pr["cu_seqlens"].numpy()
+    P = int(sum(-(-int(n) // 16) + 2 for n in lens) * 3 * 1.2) + 8
+    p = Pair(dk, orc, cfg, 5, P, int(cu[-1]))
+    _say(f"fused decode step d={d} G={G} lo={lo}: prompt")
+    p.prompt(cu, pr["k"].numpy(), pr["v"].numpy(), pr["scores"].numpy())
+    seq = lens.numpy().astype(np.int32)
+    for step in range(8):
+        dec = synth.make_decode(cfg, step)
+        _say("  decode step", step)
+        p.decode_step(seq, dec["k_new"].numpy(), dec["v_new"].numpy(), dec["q"].numpy(), True,
+                      f"decode step {step}")
+        seq = seq + 1
+    check_pool_invariants(orc, p.o)
+    mask = np.array([1, 0, 0, 1, 0], np.uint8)
+    p.release(mask)
+    lens2 = torch.tensor([95, 0, 0, 300, 0], dtype=torch.int64)
+    pr2 = synth.make_prompt(cfg, lens=lens2, salt=5)
+    p.prompt(pr2["cu_seqlens"].numpy(), pr2["k"].numpy(), pr2["v"].numpy(), pr2["scores"].numpy(),
+             what="re-admit")
+    seq = np.where(mask == 1, lens2.numpy(), seq).astype(np.int32)
+    for step in range(3):
+        dec = synth.make_decode(cfg, 50 + step)
+        p.decode_step(seq, dec["k_new"].numpy(), dec["v_new"].numpy(), dec["q"].numpy(), step != 1,
+                      f"decode step after re-admit {step}")
+        seq = seq + 1
+    check_pool_invariants(orc, p.o)
+
+
 def test_fig6_scaled_on_gpu(dk, orc):
     """The Fig 6 worked example at 16/32-token pages: pages 5-8 to head A,
     9-12 to head B, pointer to 13, pages 6, 7, 11 reclaimed."""
