@@ -78,14 +78,28 @@ constexpr float kTwo24 = 16777216.0f;
 // the code goes to the top of the mantissa under the exponent of 1.0 (as
 // subnormals these small codes lose precision in the matrix unit).  The
 // fields at bits s and s+16 of a dword give a packed fp16 pair: one shift
-// and one and-or.
+// and one v_and_or_b32.  (The mask and the exponent bits are kept in a
+// scalar and a vector register: with both as literals the compiler emits an
+// and and an or, since a three-operand instruction takes no literal here.)
+template <uint32_t V>
+__device__ inline uint32_t sreg_const() {
+  uint32_t r;
+  asm("s_mov_b32 %0, %1" : "=s"(r) : "i"(V));
+  return r;
+}
+template <uint32_t V>
+__device__ inline uint32_t vreg_const() {
+  uint32_t r;
+  asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(V));
+  return r;
+}
 __device__ inline uint32_t nib2(uint32_t w, int s) {
   const uint32_t t = s >= 6 ? w >> (s - 6) : w << (6 - s);
-  return (t & 0x03C003C0u) | 0x3C003C00u;
+  return (t & sreg_const<0x03C003C0u>()) | vreg_const<0x3C003C00u>();
 }
 __device__ inline uint32_t crumb2(uint32_t w, int s) {
   const uint32_t t = s >= 8 ? w >> (s - 8) : w << (8 - s);
-  return (t & 0x03000300u) | 0x3C003C00u;
+  return (t & sreg_const<0x03000300u>()) | vreg_const<0x3C003C00u>();
 }
 
 int attn_splits(const Cfg& c, int batch) {
