@@ -482,6 +482,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
   };
   PageRegs<D> A, B;
   bool spec = false;  // A already holds page wid (loads issued before the verdict)
+  WaveCommit<D> wc;
   if constexpr (STEP) {
     const int32_t wu = sa.nf[u];
     const int32_t* R = sa.rec + u * kSRec;
@@ -499,6 +500,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
     // unless the step writes it: its loads need not wait for the verdict
     spec = wid < kCW && wid < ph && wid != (new_hi >> 4) && state_ok(nh, nl, ph, pl, L);
     if (spec) fetch_id(A, wid, id_guess, true);
+    // the committing wave's loads, before the verdict (its unit asks for a
+    // commit; the verdict may still refuse it)
+    if (wid == kCW && (wu & kActive) && ((uint32_t)wu >> 8) == 0)
+      wc.begin(u, page_bytes, P, sa.k_new, sa.v_new, need, lo_src, id_hrow, id_lrow, id_src, pages,
+               (uint32_t*)img_h, (uint32_t*)img_l);
     if (sa.direct) {
       start = sa.hdr[SH_START];
       const int64_t end = sa.hdr[SH_END];
@@ -614,9 +620,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
         badid = 1;
       } else {
         int32_t idh, idl;
-        commit_wave<D>(u, L, page_bytes, P, N, sa.k_new, sa.v_new, nh0, nl0, ph0, pl0, need, page, new_hi,
-                       hi_app, lo_src, lo_slot, lo_app, id_hrow, id_lrow, id_src, id_first, sa.table + u * L,
-                       sa.state + 4 * u, pages, (uint32_t*)img_h, (uint32_t*)img_l, idh, idl);
+        wc.finish(L, page_bytes, P, N, nh0, nl0, ph0, pl0, need, page, new_hi, hi_app, lo_src, lo_slot, lo_app,
+                  id_hrow, id_lrow, id_first, sa.table + u * L, sa.state + 4 * u, pages, (uint32_t*)img_h,
+                  (uint32_t*)img_l, idh, idl);
         if (lane == 0) {
           s_idt[0] = min(max(idh, 0), (int32_t)(P - 1));
           s_idt[1] = min(max(idl, 0), (int32_t)(P - 1));

@@ -538,160 +538,178 @@ __device__ inline void step_verdict(int64_t u, int64_t U, const int32_t* nf, int
   }
 }
 
-// The commit of unit u by one wave, after a positive verdict (need, page:
-// the new page's tier and id).  The written pages are built whole in LDS
-// (img_h, img_l: the high page of the new token, the low page of the
-// requantized token), their changed bytes stored, then the table and the
-// tier state.  The wave's LDS operations complete in program order, so no
-// barrier is needed between the phases.  id_h, id_l: the written pages' ids.
+// The commit of unit u by one wave, in two phases around the verdict.
+// begin (before it; loads only): the new token, the existing pages the step
+// writes (straight into their LDS images img_h, img_l: the high page of the
+// new token, the low page of the requantized token) and the token it
+// requantizes; ids are clamped into the pool, since a unit that will not
+// commit may carry a stale plan.  finish (committing units, page: the new
+// page when need): fresh images zeroed, fields edited, changed bytes stored,
+// then the table entry and the tier state.  The wave's LDS operations
+// complete in program order, so no barrier is needed between the phases.
 template <int D>
-__device__ __forceinline__ void commit_wave(int64_t u, int L, int page_bytes, int64_t P, int N, const uint16_t* k_new,
-                                   const uint16_t* v_new, int nh, int nl, int ph, int pl, int need, int32_t page,
-                                   int new_hi, int hi_app, int lo_src, int lo_slot, int lo_app, int32_t id_hrow,
-                                   int32_t id_lrow, int32_t id_src, int32_t id_first, int32_t* row, int32_t* s4,
-                                   uint8_t* pages, uint32_t* img_h, uint32_t* img_l, int32_t& id_h,
-                                   int32_t& id_l) {
-  constexpr Seg sh = tier_seg(D, true);
-  constexpr int PD = D / 64;  // dims per lane
-  const int lane = threadIdx.x & 63;
+struct WaveCommit {
+  static constexpr int PD = D / 64;  // dims per lane
+  static constexpr int kPB = page_bytes_for(D);
   float xk[PD], xv[PD];
+  uint32_t km_rq = 0, vm_rq = 0, kc_rq[PD], vc_rq[PD];
+  float sc_rq = 0.0f;
+  int32_t pos_rq = 0;
+
+  __device__ __forceinline__ void begin(int64_t u, int page_bytes, int64_t P, const uint16_t* k_new,
+                                        const uint16_t* v_new, int need, int lo_src, int32_t id_hrow,
+                                        int32_t id_lrow, int32_t id_src, const uint8_t* pages, uint32_t* img_h,
+                                        uint32_t* img_l) {
+    constexpr Seg sh = tier_seg(D, true);
+    const int lane = threadIdx.x & 63;
+    auto clampP = [&](int32_t id) { return min(max(id, 0), (int32_t)(P - 1)); };
 #pragma unroll
-  for (int e = 0; e < PD; e++) {
-    xk[e] = h2f(k_new[u * D + lane + 64 * e]);
-    xv[e] = h2f(v_new[u * D + lane + 64 * e]);
-  }
-  const TokWrite th{true, true, need == kTierHi, new_hi & 15, need == kTierHi ? page : id_hrow};
-  const TokWrite tl{lo_src >= 0, false, need == kTierLo, lo_slot & 31,
-                    lo_src < 0 ? 0 : (need == kTierLo ? page : id_lrow)};
-  id_h = th.id;
-  id_l = tl.id;
-  // an existing page goes straight from memory into its LDS image (16 bytes
-  // per lane and instruction, every chunk in flight at once, no registers);
-  // a fresh one is zeroed
-  constexpr int kPB = page_bytes_for(D);
-  auto img_full = [&](uint32_t* img, const TokWrite& t) {
-    if (!t.on) return;
-    if (t.fresh) {
-      for (int c = lane; c < kPB / 16; c += 64) ((uint4*)img)[c] = make_uint4(0u, 0u, 0u, 0u);
-    } else {
-      const uint8_t* src = pages + (int64_t)t.id * page_bytes;
+    for (int e = 0; e < PD; e++) {
+      xk[e] = h2f(k_new[u * D + lane + 64 * e]);
+      xv[e] = h2f(v_new[u * D + lane + 64 * e]);
+      kc_rq[e] = vc_rq[e] = 0u;
+    }
+    // an existing page goes straight from memory into its image (16 bytes
+    // per lane and instruction, every chunk in flight at once)
+    auto img_load = [&](uint32_t* img, int32_t id) {
+      const uint8_t* src = pages + (int64_t)clampP(id) * page_bytes;
 #pragma unroll
       for (int c = 0; c < (kPB + 1023) / 1024; c++)
         if (c * 1024 + lane * 16 < kPB)
           __builtin_amdgcn_global_load_lds((const void*)(src + c * 1024 + lane * 16),
                                            (__attribute__((address_space(3))) void*)((uint8_t*)img + c * 1024),
                                            16, 0, 0);
-    }
-  };
-  img_full(img_h, th);
-  img_full(img_l, tl);
-  // the requantized token's dequantized values (its high slot may be the
-  // new token's: read before anything is written)
-  float xk_rq[PD], xv_rq[PD], sc_rq = 0.0f;
-  int32_t pos_rq = 0;
+    };
+    if (need != kTierHi) img_load(img_h, id_hrow);
+    if (lo_src >= 0 && need != kTierLo) img_load(img_l, id_lrow);
+    if (lo_src >= 0) {
+      const uint8_t* src = pages + (int64_t)clampP(id_src) * page_bytes;
+      const int si = lo_src & 15;
+      km_rq = *(const uint32_t*)(src + sh.km + 4 * si);
+      vm_rq = *(const uint32_t*)(src + sh.vm + 4 * si);
+      sc_rq = *(const float*)(src + sh.sc + 4 * si);
+      pos_rq = *(const int32_t*)(src + sh.ps + 4 * si);
 #pragma unroll
-  for (int e = 0; e < PD; e++) xk_rq[e] = xv_rq[e] = 0.0f;
-  if (tl.on) {
-    const uint8_t* src = pages + (int64_t)id_src * page_bytes;
-    const int si = lo_src & 15;
-    const uint32_t km = *(const uint32_t*)(src + sh.km + 4 * si);
-    const uint32_t vm = *(const uint32_t*)(src + sh.vm + 4 * si);
-    sc_rq = *(const float*)(src + sh.sc + 4 * si);
-    pos_rq = *(const int32_t*)(src + sh.ps + 4 * si);
-#pragma unroll
-    for (int e = 0; e < PD; e++) {
-      int byte, shift;
-      k_field(D, true, si, lane + 64 * e, byte, shift);
-      xk_rq[e] = dequant(h2f((uint16_t)km), h2f((uint16_t)(km >> 16)), ((uint32_t)src[byte] >> shift) & 0xFFu);
-      v_field(D, true, si, lane + 64 * e, byte, shift);
-      xv_rq[e] = dequant(h2f((uint16_t)vm), h2f((uint16_t)(vm >> 16)), ((uint32_t)src[byte] >> shift) & 0xFu);
-    }
-  }
-  float mn[4], mx[4];
-  mn[0] = mx[0] = xk[0];
-  mn[1] = mx[1] = xv[0];
-  mn[2] = mx[2] = xk_rq[0];
-  mn[3] = mx[3] = xv_rq[0];
-#pragma unroll
-  for (int e = 1; e < PD; e++) {
-    mn[0] = fminf(mn[0], xk[e]);
-    mx[0] = fmaxf(mx[0], xk[e]);
-    mn[1] = fminf(mn[1], xv[e]);
-    mx[1] = fmaxf(mx[1], xv[e]);
-    mn[2] = fminf(mn[2], xk_rq[e]);
-    mx[2] = fmaxf(mx[2], xk_rq[e]);
-    mn[3] = fminf(mn[3], xv_rq[e]);
-    mx[3] = fmaxf(mx[3], xv_rq[e]);
-  }
-#pragma unroll
-  for (int v = 0; v < 4; v++) {
-    mn[v] = wave_min(mn[v]);
-    mx[v] = wave_max(mx[v]);
-  }
-  // the images have landed (their loads count as vector memory reads)
-  // before any field edit: s_waitcnt vmcnt(0)
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  asm volatile("" ::: "memory");
-  auto put = [&](uint32_t* img, const TokWrite& t, const float* xkv, const float* xvv, float kmn, float kmx,
-                 float vmn, float vmx, float score, int32_t pos) {
-    const Seg sg = tier_seg(D, t.hi);
-    uint16_t ks16, kz16, vs16, vz16;
-    float ks, kz, vs, vz;
-    codec_params(kmn, kmx, sg.kbits, ks16, kz16, ks, kz);
-    codec_params(vmn, vmx, sg.vbits, vs16, vz16, vs, vz);
-#pragma unroll
-    for (int e = 0; e < PD; e++) {
-      int byte, shift;
-      k_field(D, t.hi, t.idx, lane + 64 * e, byte, shift);
-      lds_put(img, byte, shift, sg.kbits, codec_code(xkv[e], ks, kz, sg.kbits));
-      v_field(D, t.hi, t.idx, lane + 64 * e, byte, shift);
-      lds_put(img, byte, shift, sg.vbits, codec_code(xvv[e], vs, vz, sg.vbits));
-    }
-    if (lane == 0) {
-      img[sg.km / 4 + t.idx] = (uint32_t)ks16 | ((uint32_t)kz16 << 16);
-      img[sg.vm / 4 + t.idx] = (uint32_t)vs16 | ((uint32_t)vz16 << 16);
-      img[sg.sc / 4 + t.idx] = __float_as_uint(score);
-      img[sg.ps / 4 + t.idx] = (uint32_t)pos;
-    }
-  };
-  put(img_h, th, xk, xv, mn[0], mx[0], mn[1], mx[1], 0.0f, N);
-  if (tl.on) put(img_l, tl, xk_rq, xv_rq, mn[2], mx[2], mn[3], mx[3], sc_rq, pos_rq);
-  asm volatile("" ::: "memory");  // every field is written before the stores read the images
-  auto store = [&](const uint32_t* img, const TokWrite& t) {
-    if (!t.on) return;
-    const Seg sg = tier_seg(D, t.hi);
-    uint8_t* pg = pages + (int64_t)t.id * page_bytes;
-    if (t.fresh) {
-      for (int c = lane; c < page_bytes / 16; c += 64) ((uint4*)pg)[c] = ((const uint4*)img)[c];
-      return;
-    }
-    const int kb = t.idx * D * sg.kbits / 8, kn = D * sg.kbits / 128;  // 16-byte chunks
-    const int vn = (sg.vm - sg.vc) / 16;
-    for (int c = lane; c < kn + vn + 4; c += 64) {
-      if (c < kn) {
-        ((uint4*)(pg + kb))[c] = ((const uint4*)(img + kb / 4))[c];
-      } else if (c < kn + vn) {
-        ((uint4*)(pg + sg.vc))[c - kn] = ((const uint4*)(img + sg.vc / 4))[c - kn];
-      } else {
-        const int seg = c - kn - vn;
-        const int off = (seg == 0 ? sg.km : seg == 1 ? sg.vm : seg == 2 ? sg.sc : sg.ps) + 4 * t.idx;
-        *(uint32_t*)(pg + off) = img[off / 4];
+      for (int e = 0; e < PD; e++) {
+        int byte, shift;
+        k_field(D, true, si, lane + 64 * e, byte, shift);
+        kc_rq[e] = ((uint32_t)src[byte] >> shift) & 0xFFu;
+        v_field(D, true, si, lane + 64 * e, byte, shift);
+        vc_rq[e] = ((uint32_t)src[byte] >> shift) & 0xFu;
       }
     }
-  };
-  store(img_h, th);
-  store(img_l, tl);
-  if (lane == 0) {
-    // the unit changed: its plan record (first high page) no longer applies
-    if (ph >= 1 && id_first >= 0 && id_first < P)
-      *(uint32_t*)(pages + (int64_t)id_first * page_bytes + plan_rec_off<D>()) = 0u;
-    if (need == kTierHi) row[ph] = page;
-    if (need == kTierLo) row[L - 1 - pl] = page;
-    s4[0] = nh + hi_app;
-    s4[1] = nl + lo_app;
-    s4[2] = ph + (need == kTierHi);
-    s4[3] = pl + (need == kTierLo);
   }
-}
+
+  __device__ __forceinline__ void finish(int L, int page_bytes, int64_t P, int N, int nh, int nl, int ph, int pl,
+                                         int need, int32_t page, int new_hi, int hi_app, int lo_src, int lo_slot,
+                                         int lo_app, int32_t id_hrow, int32_t id_lrow, int32_t id_first,
+                                         int32_t* row, int32_t* s4, uint8_t* pages, uint32_t* img_h,
+                                         uint32_t* img_l, int32_t& id_h, int32_t& id_l) {
+    const int lane = threadIdx.x & 63;
+    const TokWrite th{true, true, need == kTierHi, new_hi & 15, need == kTierHi ? page : id_hrow};
+    const TokWrite tl{lo_src >= 0, false, need == kTierLo, lo_slot & 31,
+                      lo_src < 0 ? 0 : (need == kTierLo ? page : id_lrow)};
+    id_h = th.id;
+    id_l = tl.id;
+    // a fresh page's image starts zeroed
+    if (th.fresh)
+      for (int c = lane; c < kPB / 16; c += 64) ((uint4*)img_h)[c] = make_uint4(0u, 0u, 0u, 0u);
+    if (tl.on && tl.fresh)
+      for (int c = lane; c < kPB / 16; c += 64) ((uint4*)img_l)[c] = make_uint4(0u, 0u, 0u, 0u);
+    // the requantized token's dequantized values (its high slot may be the
+    // new token's: read in begin, before anything is written)
+    float xk_rq[PD], xv_rq[PD];
+#pragma unroll
+    for (int e = 0; e < PD; e++) {
+      xk_rq[e] = tl.on ? dequant(h2f((uint16_t)km_rq), h2f((uint16_t)(km_rq >> 16)), kc_rq[e]) : 0.0f;
+      xv_rq[e] = tl.on ? dequant(h2f((uint16_t)vm_rq), h2f((uint16_t)(vm_rq >> 16)), vc_rq[e]) : 0.0f;
+    }
+    float mn[4], mx[4];
+    mn[0] = mx[0] = xk[0];
+    mn[1] = mx[1] = xv[0];
+    mn[2] = mx[2] = xk_rq[0];
+    mn[3] = mx[3] = xv_rq[0];
+#pragma unroll
+    for (int e = 1; e < PD; e++) {
+      mn[0] = fminf(mn[0], xk[e]);
+      mx[0] = fmaxf(mx[0], xk[e]);
+      mn[1] = fminf(mn[1], xv[e]);
+      mx[1] = fmaxf(mx[1], xv[e]);
+      mn[2] = fminf(mn[2], xk_rq[e]);
+      mx[2] = fmaxf(mx[2], xk_rq[e]);
+      mn[3] = fminf(mn[3], xv_rq[e]);
+      mx[3] = fmaxf(mx[3], xv_rq[e]);
+    }
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+      mn[v] = wave_min(mn[v]);
+      mx[v] = wave_max(mx[v]);
+    }
+    // the images have landed (their loads count as vector memory reads)
+    // before any field edit: s_waitcnt vmcnt(0)
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    asm volatile("" ::: "memory");
+    auto put = [&](uint32_t* img, const TokWrite& t, const float* xkv, const float* xvv, float kmn, float kmx,
+                   float vmn, float vmx, float score, int32_t pos) {
+      const Seg sg = tier_seg(D, t.hi);
+      uint16_t ks16, kz16, vs16, vz16;
+      float ks, kz, vs, vz;
+      codec_params(kmn, kmx, sg.kbits, ks16, kz16, ks, kz);
+      codec_params(vmn, vmx, sg.vbits, vs16, vz16, vs, vz);
+#pragma unroll
+      for (int e = 0; e < PD; e++) {
+        int byte, shift;
+        k_field(D, t.hi, t.idx, lane + 64 * e, byte, shift);
+        lds_put(img, byte, shift, sg.kbits, codec_code(xkv[e], ks, kz, sg.kbits));
+        v_field(D, t.hi, t.idx, lane + 64 * e, byte, shift);
+        lds_put(img, byte, shift, sg.vbits, codec_code(xvv[e], vs, vz, sg.vbits));
+      }
+      if (lane == 0) {
+        img[sg.km / 4 + t.idx] = (uint32_t)ks16 | ((uint32_t)kz16 << 16);
+        img[sg.vm / 4 + t.idx] = (uint32_t)vs16 | ((uint32_t)vz16 << 16);
+        img[sg.sc / 4 + t.idx] = __float_as_uint(score);
+        img[sg.ps / 4 + t.idx] = (uint32_t)pos;
+      }
+    };
+    put(img_h, th, xk, xv, mn[0], mx[0], mn[1], mx[1], 0.0f, N);
+    if (tl.on) put(img_l, tl, xk_rq, xv_rq, mn[2], mx[2], mn[3], mx[3], sc_rq, pos_rq);
+    asm volatile("" ::: "memory");  // every field is written before the stores read the images
+    auto store = [&](const uint32_t* img, const TokWrite& t) {
+      if (!t.on) return;
+      const Seg sg = tier_seg(D, t.hi);
+      uint8_t* pg = pages + (int64_t)t.id * page_bytes;
+      if (t.fresh) {
+        for (int c = lane; c < page_bytes / 16; c += 64) ((uint4*)pg)[c] = ((const uint4*)img)[c];
+        return;
+      }
+      const int kb = t.idx * D * sg.kbits / 8, kn = D * sg.kbits / 128;  // 16-byte chunks
+      const int vn = (sg.vm - sg.vc) / 16;
+      for (int c = lane; c < kn + vn + 4; c += 64) {
+        if (c < kn) {
+          ((uint4*)(pg + kb))[c] = ((const uint4*)(img + kb / 4))[c];
+        } else if (c < kn + vn) {
+          ((uint4*)(pg + sg.vc))[c - kn] = ((const uint4*)(img + sg.vc / 4))[c - kn];
+        } else {
+          const int seg = c - kn - vn;
+          const int off = (seg == 0 ? sg.km : seg == 1 ? sg.vm : seg == 2 ? sg.sc : sg.ps) + 4 * t.idx;
+          *(uint32_t*)(pg + off) = img[off / 4];
+        }
+      }
+    };
+    store(img_h, th);
+    store(img_l, tl);
+    if (lane == 0) {
+      // the unit changed: its plan record (first high page) no longer applies
+      if (ph >= 1 && id_first >= 0 && id_first < P)
+        *(uint32_t*)(pages + (int64_t)id_first * page_bytes + plan_rec_off<D>()) = 0u;
+      if (need == kTierHi) row[ph] = page;
+      if (need == kTierLo) row[L - 1 - pl] = page;
+      s4[0] = nh + hi_app;
+      s4[1] = nl + lo_app;
+      s4[2] = ph + (need == kTierHi);
+      s4[3] = pl + (need == kTierLo);
+    }
+  }
+};
 
 }  // namespace dkv
