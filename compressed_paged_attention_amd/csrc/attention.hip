@@ -343,6 +343,9 @@ __device__ inline void compute_page(const PageRegs<D>& R, bool hi, int nval, con
         },
         [&](const float* x) { keep(0, x); });
   } else {
+    // both blocks' q.c products first: the matrix unit works on the second
+    // while the first block's softmax runs
+    float4_t sb[2];
 #pragma unroll
     for (int mb = 0; mb < 2; mb++) {
       float4_t s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = s0;
@@ -353,8 +356,12 @@ __device__ inline void compute_page(const PageRegs<D>& R, bool hi, int nval, con
         s0 = mfma32(cat8(cat(nib2(w0, 0), nib2(w0, 4)), cat(nib2(w0, 8), nib2(w0, 12))), qop[ks], s0);
         s1 = mfma32(cat8(cat(nib2(w1, 0), nib2(w1, 4)), cat(nib2(w1, 8), nib2(w1, 12))), qop[ks + 1], s1);
       }
+      sb[mb] = s0 + s1;
+    }
+#pragma unroll
+    for (int mb = 0; mb < 2; mb++) {
       block_update<D, PACK>(
-          s0 + s1, R.km + 4 * mb, R.vm + 4 * mb, 16 * mb + 4 * qg, nval, nval < 16 * (mb + 1), sq2, 16.0f * sl,
+          sb[mb], R.km + 4 * mb, R.vm + 4 * mb, 16 * mb + 4 * qg, nval, nval < 16 * (mb + 1), sq2, 16.0f * sl,
           16.0f, 4.0f, tail,
           sm, acc,
           [&](int nb) {
