@@ -1115,15 +1115,16 @@ hipError_t launch_attn(const Cfg& c, const Pool& p, int batch, const uint16_t* q
 }
 
 // With one split per unit the step's commit runs inside the attention
-// workgroup (plan kernel, then one kernel); otherwise plan, commit and
-// attention kernels in turn.
+// workgroup (plan kernel, then one kernel); otherwise, and when the score
+// update is deferred (mode 2: the logits go to the workspace for a later
+// diffkv_update_scores), plan, commit and attention kernels in turn.
 hipError_t launch_decode_step(const Cfg& c, const Pool& p, int batch, const int32_t* seq_len, const uint16_t* k,
                               const uint16_t* v, const uint16_t* q, int32_t* table, int32_t* state, float* out,
                               int mode, void* ws_step, void* ws_attn, hipStream_t s) {
   const int64_t U = (int64_t)batch * c.H;
   if (U == 0) return hipSuccess;
   const int S = attn_splits(c, batch);
-  if (S != 1) {
+  if (S != 1 || mode == 2) {
     hipError_t e = launch_step(c, p, batch, seq_len, k, v, table, state, ws_step, s);
     if (e != hipSuccess) return e;
     return launch_attn(c, p, batch, q, table, state, seq_len, out, mode, ws_attn, s);

@@ -191,7 +191,12 @@ int diffkv_decode_attn(const diffkv_config* cfg, const diffkv_pool* pool, int32_
  * ("Implementation": the compactor runs after K/V are computed and before the
  * attention kernel).  Results, status bits and all-or-nothing behaviour are
  * those of the two calls in sequence (an aborted step leaves the cache as it
- * was and the attention runs on it).
+ * was and the attention runs on it).  When every unit is one split
+ * (diffkv_attn_splits == 1) and update_scores != 2, the commit runs inside
+ * the attention kernel; one difference remains there: a free-list entry
+ * outside the pool (a corrupt pool) leaves that unit uncommitted, sets
+ * BAD_STATE and zeroes its output, where the two calls would attend to the
+ * uncommitted unit.
  *  seq_len  int32 [batch]: length before this step's token (= position of
  *           the query token); <= 0 marks an inactive request
  *  k_new, v_new fp16 [batch, H, d]; q fp16 [batch, H*G, d]; out fp32

@@ -397,6 +397,40 @@ def test_decode_step_entry(dk, orc, batch, H, update):
     check_pool_invariants(orc, p.o)
 
 
+def test_decode_step_deferred_scores(dk, orc):
+    """diffkv_decode_step(update_scores = 2) keeps the logits for a later
+    diffkv_update_scores (one split per unit, where the step otherwise runs
+    fused with the score update): the pair equals the oracle's step and
+    attention with the score update, and the second call adds nothing twice."""
+    from workloads import synth
+    cfg = _medium_cfg("llama3_8b", num_kv_heads=3, batch=5, max_seq_len=420, window=64)
+    assert dk.diffkv_attn_splits(cfg, 5) == 1
+    lens = torch.tensor([300, 41, 129, 77, 64], dtype=torch.int64)
+    pr = synth.make_prompt(cfg, lens=lens)
+    cu = pr["cu_seqlens"].numpy()
+    P = int(sum(-(-int(n) // 16) + 2 for n in lens) * 3 * 1.2) + 8
+    p = Pair(dk, orc, cfg, 5, P, int(cu[-1]))
+    p.prompt(cu, pr["k"].numpy(), pr["v"].numpy(), pr["scores"].numpy())
+    seq = lens.numpy().astype(np.int32)
+    off = -(-dk.diffkv_workspace_bytes(cfg, dk.STEP, 5) // 256) * 256
+    for step in range(3):
+        dec = synth.make_decode(cfg, step)
+        kn, vn, q = dec["k_new"].numpy(), dec["v_new"].numpy(), dec["q"].numpy()
+        p.o.compact_step(seq, kn, vn)
+        out_o = p.o.decode_attn(q, seq, update_scores=True)
+        seq_d = torch.from_numpy(seq).to(dev)
+        out_g = p.g.decode_step(torch.from_numpy(q).to(dev), seq_d, torch.from_numpy(kn).to(dev),
+                                torch.from_numpy(vn).to(dev), update_scores=2)
+        dk.diffkv_update_scores(cfg, p.g.pool, 5, p.g.page_table, p.g.tier_state, seq_d, p.g.ws_decode[off:])
+        torch.cuda.synchronize()
+        what = f"deferred decode step {step}"
+        assert_state_equal(p.g, p.o, pages=False, what=what)
+        assert_attn_close(out_g, out_o, what)
+        assert_scores_close(p.g, p.o, what)
+        resync_scores(p.g, p.o)
+        seq = seq + 1
+
+
 def test_decode_step_exhausted_pool(dk, orc):
     """A step that cannot get its page commits nothing; the attention still
     runs on the unchanged cache (as the two separate calls would)."""
