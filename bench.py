@@ -16,7 +16,8 @@ Caches rotate over several independent replicas (one per simulated layer) so
 that the 256 MB Infinity Cache cannot hold the working set.
 
 value = batch * steps / (time of the timed region): request-tokens per second
-of complete decode steps.  Three segments are timed with HIP events on the
+of complete decode steps (timed as 8 back-to-back segments; their spread is
+reported as p10/p50/p90 per step).  Three kinds of segments are timed with HIP events on the
 stream the library launches on, each over back-to-back launches while a spin
 kernel issued before the start event holds the stream (so the events measure
 the device, not the host's launch rate): the K complete steps (value), K
@@ -26,7 +27,10 @@ The compaction's share of a step is (step - attention alone) / step.  The
 roofline object
 describes the attention kernel: algorithmic bytes per launch (codes +
 metadata of every retained token, q, out, table entries, and the 8-byte
-read-modify-write of each retained token's score) over its mean duration.
+read-modify-write of each retained token's score) over its mean duration;
+stream_read_GBps is the box's achievable read rate (a reduction over 4 GiB),
+the practical ceiling beside the 8 TB/s peak.  The oracle baseline runs first
+(before the process touches the GPU), on one thread and as several processes.
 """
 from __future__ import annotations
 
@@ -89,6 +93,27 @@ def measured_traffic():
     return float(kv["traffic_bytes_per_launch"])
 
 
+def stream_read_gbps(gib=4, reps=10):
+    """Achievable HBM read rate on this machine: row sums over a `gib` GiB
+    buffer viewed as 4096-float rows (torch's own kernel; the fastest
+    torch reduction measured here, 6.2 TB/s against 3.8 for a full sum),
+    best of `reps`."""
+    import torch
+    x = torch.ones(gib << 28, dtype=torch.float32, device="cuda:0")
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        x.view(-1, 4096).sum(dim=1)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3
+        best = t if best is None else min(best, t)
+    del x
+    torch.cuda.empty_cache()
+    return (gib << 30) / best / 1e9
+
+
 def copy_probe(mib):
     """One elementwise copy of a known size (reads and writes `mib` MiB):
     the calibration point for the HBM byte counters."""
@@ -104,10 +129,10 @@ def copy_probe(mib):
     print(f"[bench] copy probe: {mib} MiB read + {mib} MiB written", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(cfg, n_req, n_steps):
-    """The oracle timed on this host on a bounded sample of the same workload."""
+def _oracle_steps(cfg, n_req, n_steps, barrier=None):
+    """Prompt compaction, then n_steps decode steps of the oracle on n_req
+    requests of the workload; returns (prompt s, step s)."""
     import numpy as np
-    import torch
 
     import oracle
     from workloads import synth
@@ -122,21 +147,60 @@ def cpu_baseline(cfg, n_req, n_steps):
     st.compact_prompt(cu, pr["k"].numpy(), pr["v"].numpy(), pr["scores"].numpy(), tiers)
     t_prompt = time.perf_counter() - t0
     seq = lens.numpy().astype(np.int32)
+    decs = [synth.make_decode(c, s, batch=n_req) for s in range(n_steps)]
+    if barrier is not None:
+        barrier.wait()
     t0 = time.perf_counter()
     for s in range(n_steps):
-        dec = synth.make_decode(c, s, batch=n_req)
+        dec = decs[s]
         st.compact_step(seq, dec["k_new"].numpy(), dec["v_new"].numpy())
         st.decode_attn(dec["q"].numpy(), seq, update_scores=True)
         seq += 1
     t_step = (time.perf_counter() - t0) / n_steps
-    del torch
-    return dict(value=n_req / t_step, unit="request-tokens/s", cores=1, kind="oracle",
-                sample=f"{n_req} of {cfg['batch']} requests ({n_req * cfg['num_kv_heads']} units, "
-                       f"{cfg['seq'][0]} tokens each): prompt compaction once "
-                       f"({t_prompt:.2f} s, not in value), then {n_steps} decode steps "
-                       f"(step compaction + fp64 attention + score update), "
-                       f"{t_step * 1e3:.1f} ms per step; single thread",
-                cpu=platform.processor() or platform.machine(), prompt_s=t_prompt, step_s=t_step)
+    return t_prompt, t_step
+
+
+_BARRIER = None
+
+
+def _pool_init(b):
+    global _BARRIER
+    _BARRIER = b
+
+
+def _oracle_worker_b(args):
+    import torch
+    torch.set_num_threads(1)
+    cfg, n_req, n_steps = args
+    return _oracle_steps(cfg, n_req, n_steps, _BARRIER)
+
+
+def cpu_baseline(cfg, n_req, n_steps, workers):
+    """The oracle timed on this host on a bounded sample of the same workload:
+    once on one thread, once as `workers` processes (each n_req / 4 requests
+    of its own, steps started together).  Runs before the process touches
+    the GPU (the workers are forked)."""
+    import multiprocessing as mp
+    t_prompt, t_step = _oracle_steps(cfg, n_req, n_steps)
+    single = dict(value=n_req / t_step, cores=1,
+                  sample=f"{n_req} of {cfg['batch']} requests ({n_req * cfg['num_kv_heads']} units, "
+                         f"{cfg['seq'][0]} tokens each): prompt compaction once "
+                         f"({t_prompt:.2f} s, not in value), then {n_steps} decode steps "
+                         f"(step compaction + fp64 attention + score update), "
+                         f"{t_step * 1e3:.1f} ms per step")
+    per = max(1, n_req // 4)
+    ctx = mp.get_context("fork")
+    barrier = ctx.Barrier(workers)
+    with ctx.Pool(workers, initializer=_pool_init, initargs=(barrier,)) as pool:
+        res = pool.map(_oracle_worker_b, [(cfg, per, n_steps)] * workers)
+    value = sum(per / ts for _, ts in res)
+    return dict(value=value, unit="request-tokens/s", cores=workers, kind="oracle",
+                sample=f"{workers} processes, each {per} requests ({per * cfg['num_kv_heads']} units, "
+                       f"{cfg['seq'][0]} tokens each) through prompt compaction, then {n_steps} decode "
+                       f"steps (step compaction + fp64 attention + score update) started together; "
+                       f"value = sum of the processes' request-tokens/s",
+                single_thread=single, cpu=platform.processor() or platform.machine(),
+                nproc=os.cpu_count())
 
 
 def main():
@@ -149,6 +213,8 @@ def main():
     ap.add_argument("--cpu-requests", type=int, default=8)
     ap.add_argument("--cpu-steps", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-workers", type=int, default=min(16, os.cpu_count() or 1),
+                    help="oracle processes for the all-cores baseline")
     ap.add_argument("--hold-cycles", type=int, default=100_000_000,
                     help="spin-kernel length that holds the stream while a timed segment is enqueued")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -162,8 +228,17 @@ def main():
     import numpy as np
     import torch
 
-    import compressed_paged_attention_amd as dk
     from workloads import synth
+
+    # the oracle baseline first: its worker processes fork from a process
+    # that has not touched the GPU
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(synth.config(args.workload), args.cpu_requests, args.cpu_steps, args.cpu_workers)
+        print("[bench] cpu baseline done", file=sys.stderr, flush=True)
+
+    import compressed_paged_attention_amd as dk
 
     dev = torch.device("cuda:0")
     if args.copy_probe_mib > 0:
@@ -237,8 +312,11 @@ def main():
         reps[s % R].decode_step(dec[s]["q"], seq_per_step[s], dec[s]["k_new"], dec[s]["v_new"],
                                 update_scores=1, out=out)
 
-    # headline: K complete decode steps (compaction + attention with score update)
-    total_ms = timed(full_step, args.warmup, args.steps)
+    # headline: K complete decode steps (compaction + attention with score
+    # update), timed as 8 back-to-back segments (their spread: p10/p50/p90)
+    nseg = 8 if args.steps % 8 == 0 else 1
+    seg_ms = [timed(full_step, args.warmup + k * (args.steps // nseg), args.steps // nseg) for k in range(nseg)]
+    total_ms = float(sum(seg_ms))
     ts_after = [st.tier_state.cpu().numpy() for st in reps]
     # attention alone: the same K launches again on the final caches
     last = args.warmup + args.steps - R
@@ -278,6 +356,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": step_ms,
+        "step_us_p10_p50_p90": [float(np.percentile(np.array(seg_ms) * 1e3 / (args.steps // nseg), x))
+                                for x in (10, 50, 90)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -302,11 +382,11 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS,
                      "traffic": measured_traffic() if args.workload == "llama3_8b" else None,
-                     "kernel": "attn_kernel<128, 1, true>", "bytes_per_launch": int(attn_bytes)},
+                     "kernel": "attn_kernel<128, 1, true, false>", "bytes_per_launch": int(attn_bytes),
+                     "stream_read_GBps": stream_read_gbps()},
     }
-    if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_requests, args.cpu_steps)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 
 
