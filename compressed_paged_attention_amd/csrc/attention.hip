@@ -891,7 +891,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
             for (int g = 0; g < GB; g++) xm = fmaxf(xm, lv[e][g] + cg[g]);
             const float ns = osv[e] + __builtin_amdgcn_exp2f(xm);
             const int ls = hi ? 16 * j + t : 32 * (j - ph) + t;
-            if (ok) *(float*)(pgv[e] + (hi ? sh.sc : sl.sc) + 4 * t) = ns;
+            // non-temporal: these words are read again only by a later
+            // step, and the launch then ends with fewer dirty lines to write back
+            if (ok) __builtin_nontemporal_store(ns, (float*)(pgv[e] + (hi ? sh.sc : sl.sc) + 4 * t));
             if (ok && hi && psv[e] == tc1) {  // positions are unique: one writer
               s_tc = ls;
               s_tcsum = ns;
