@@ -919,10 +919,21 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
         else if (G <= 8) pass(std::false_type{}, I8{});
         else pass(std::false_type{}, I16{});
       }
-      // the unit's least important candidates: wave butterflies, then the
-      // waves' results in lanes 0..7 of wave 0
-      bh = wave_argmin(bh, N1);
-      bl = wave_argmin(bl, N1);
+      // The next step's plan needs at most one of the two candidates: the
+      // class of the token leaving the window decides (high: the least
+      // important high token; low: the least important low token; pruned:
+      // neither), and it is known once the pass has published t_c.
+      __syncthreads();
+      const int tcs = s_tc;
+      const float tcsum = s_tcsum;
+      int cls = -1;
+      if (tc1 >= 0 && tcs >= 0)
+        cls = classify_mean(tcsum, pa.W - 1, N1 + 1, pa.lo_en, (double)pa.ah, (double)pa.al);
+      const bool needH = cls == kTierHi, needL = cls == kTierLo;
+      // the needed candidate: wave butterflies, then the waves' results in
+      // lanes 0..7 of wave 0
+      if (needH) bh = wave_argmin(bh, N1);
+      if (needL) bl = wave_argmin(bl, N1);
       if (lane == 0) {
         cw[0][wid] = bh;
         cw[1][wid] = bl;
@@ -930,19 +941,22 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
       __syncthreads();
       static_assert(kWaves == 8, "eight wave candidates");
       if (wid == 0) {
-        bh = cw[0][lane & 7];
-        bl = cw[1][lane & 7];
-        argmin_step<0>(bh, N1);
-        argmin_step<1>(bh, N1);
-        argmin_step<2>(bh, N1);
-        argmin_step<0>(bl, N1);
-        argmin_step<1>(bl, N1);
-        argmin_step<2>(bl, N1);
-        const int tcs = s_tc;
+        if (needH) {
+          bh = cw[0][lane & 7];
+          argmin_step<0>(bh, N1);
+          argmin_step<1>(bh, N1);
+          argmin_step<2>(bh, N1);
+        }
+        if (needL) {
+          bl = cw[1][lane & 7];
+          argmin_step<0>(bl, N1);
+          argmin_step<1>(bl, N1);
+          argmin_step<2>(bl, N1);
+        }
         // a record only where the next step's plan kernel would accept the state
         if (lane == 0 && ph >= 1 && nh + nl <= N1 && !(tc1 >= 0 && tcs < 0)) {
           const Plan pn = plan_decide(N1, pa.W, pa.S_max, pa.lo_en, (double)pa.ah, (double)pa.al, nh, nl, ph, pl,
-                                      L, tcs, s_tcsum, bh, bl);
+                                      L, tcs, tcsum, bh, bl);
           uint32_t rw[kRecWords];
           plan_rec_fill(rw, N1, nh, nl, ph, pl, pn);
           uint32_t* dst = (uint32_t*)(pages + (int64_t)id_tix(0) * page_bytes + plan_rec_off<D>());
