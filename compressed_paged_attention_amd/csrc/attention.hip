@@ -171,14 +171,18 @@ struct PageRegs {
   int32_t id;          // page id (wave-uniform)
 };
 
+// Page words are read once per launch: non-temporal loads (measured: the
+// plain attention 4 % faster; they keep the caches for the rest)
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 template <int N>
 __device__ inline void ldw(uint32_t* r, const uint8_t* p) {
   if constexpr (N == 4) {
-    const uint4 a = *(const uint4*)p;
-    r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
+    const u32x4_t a = __builtin_nontemporal_load((const u32x4_t*)p);
+    r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
   } else {
-    const uint2 a = *(const uint2*)p;
-    r[0] = a.x; r[1] = a.y;
+    const u32x2_t a = __builtin_nontemporal_load((const u32x2_t*)p);
+    r[0] = a[0]; r[1] = a[1];
   }
 }
 
@@ -208,7 +212,7 @@ template <int D>
 __device__ inline void load_page_sp(PageRegs<D>& R, const uint8_t* pg, bool lo, int lane) {
   constexpr Seg sh = tier_seg(D, true), sl = tier_seg(D, false);
   const int off = lane < 32 ? (lo ? sl.sc : sh.sc) + 4 * lane : (lo ? sl.ps : sh.ps) + 4 * (lane - 32);
-  R.sp = *(const uint32_t*)(pg + off);
+  R.sp = __builtin_nontemporal_load((const uint32_t*)(pg + off));
 }
 
 struct Softmax {
