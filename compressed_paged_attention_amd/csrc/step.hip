@@ -140,8 +140,8 @@ __global__ __launch_bounds__(kPlanThreads) void step_plan_kernel(int H, int L, i
         id[e] = page_of(hi ? (ls >> 4) : L - 1 - (ls >> 5));
         const uint8_t* pg = pages + (int64_t)min(max(id[e], 0), (int32_t)(P - 1)) * page_bytes;
         const int idx = hi ? (ls & 15) : (ls & 31);
-        pos[e] = *(const int32_t*)(pg + (hi ? sh.ps : sl.ps) + 4 * idx);
-        sum[e] = *(const float*)(pg + (hi ? sh.sc : sl.sc) + 4 * idx);
+        pos[e] = __builtin_nontemporal_load((const int32_t*)(pg + (hi ? sh.ps : sl.ps) + 4 * idx));
+        sum[e] = __builtin_nontemporal_load((const float*)(pg + (hi ? sh.sc : sl.sc) + 4 * idx));
       }
       // this round's candidates, then a pairwise tree (short dependent chain)
       Cand ch[kPlanPer], cl[kPlanPer];
