@@ -301,16 +301,22 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1)
 
-    for s in range(args.warmup):
-        step_compact(s)
-        step_attn(s)
-    torch.cuda.synchronize()
-    print("[bench] warmup done", file=sys.stderr, flush=True)
-
     def full_step(s):
         # compaction then attention with the score update, one library call
+        # (chained: the replica's previous step planned this one)
         reps[s % R].decode_step(dec[s]["q"], seq_per_step[s], dec[s]["k_new"], dec[s]["v_new"],
                                 update_scores=1, out=out)
+
+    # warmup: the separate kernels, then one full step per replica (which
+    # starts each replica's chain of planned steps)
+    for s in range(args.warmup):
+        if s < args.warmup - R:
+            step_compact(s)
+            step_attn(s)
+        else:
+            full_step(s)
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
 
     # headline: K complete decode steps (compaction + attention with score
     # update), timed as 8 back-to-back segments (their spread: p10/p50/p90)

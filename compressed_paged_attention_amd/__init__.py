@@ -21,7 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdiffkv.so")
 
 DIFFKV_OK, DIFFKV_E_INVALID, DIFFKV_E_WORKSPACE, DIFFKV_E_HIP = 0, 1, 2, 3
-ST_POOL_EXHAUSTED, ST_TABLE_OVERFLOW, ST_BAD_STATE = 1, 2, 4
+ST_POOL_EXHAUSTED, ST_TABLE_OVERFLOW, ST_BAD_STATE, ST_STALE_CHAIN = 1, 2, 4, 8
 PROMPT, STEP, RELEASE, ATTN, ATTN_SCORES, DECODE_STEP, DECODE_STEP_SCORES = 0, 1, 2, 3, 4, 5, 6
 PRUNE, LO, HI = 0, 1, 2
 
@@ -73,7 +73,7 @@ def lib() -> ctypes.CDLL:
                                      vp, sz, vp]
         L.diffkv_decode_attn.argtypes = [cfgp, poolp, i32, vp, vp, vp, vp, vp, i32, vp, sz, vp]
         L.diffkv_update_scores.argtypes = [cfgp, poolp, i32, vp, vp, vp, vp, sz, vp]
-        L.diffkv_decode_step.argtypes = [cfgp, poolp, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+        L.diffkv_decode_step.argtypes = [cfgp, poolp, i32, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, sz, vp]
         for f in ("diffkv_pool_init", "diffkv_state_init", "diffkv_classify", "diffkv_compact",
                   "diffkv_decode_attn", "diffkv_update_scores", "diffkv_decode_step"):
             getattr(L, f).restype = ctypes.c_int
@@ -188,10 +188,10 @@ def diffkv_update_scores(cfg: dict, pool: Pool, batch: int, page_table, tier_sta
 
 
 def diffkv_decode_step(cfg: dict, pool: Pool, batch: int, seq_len, k_new, v_new, q, page_table, tier_state,
-                       out, update_scores: int, workspace, stream=None):
+                       out, update_scores: int, workspace, chain: int = 0, stream=None):
     _check(lib().diffkv_decode_step(ctypes.byref(make_config(cfg)), ctypes.byref(pool.struct()), batch,
                                     _ptr(seq_len), _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(page_table),
-                                    _ptr(tier_state), _ptr(out), int(update_scores), _ptr(workspace),
+                                    _ptr(tier_state), _ptr(out), int(update_scores), int(chain), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(stream)),
            "diffkv_decode_step")
 
@@ -218,6 +218,10 @@ class DiffKVState:
                                      device=device)
         diffkv_pool_init(cfg, self.pool)
         diffkv_state_init(cfg, batch, self.page_table, self.tier_state)
+        # decode_step(update_scores=1) calls made in a row (their attention
+        # leaves the next step's plans in ws_decode); any other call that
+        # writes the cache ends the chain
+        self.chain = 0
 
     def classify(self, cu_seqlens, scores):
         total = int(scores.shape[1])
@@ -231,33 +235,47 @@ class DiffKVState:
         need = diffkv_workspace_bytes(self.cfg, PROMPT, self.batch, total)
         if self.ws_compact.numel() < need:
             self.ws_compact = torch.empty(need, dtype=torch.uint8, device=self.ws_compact.device)
+        self.chain = 0
         diffkv_compact(self.cfg, self.pool, PROMPT, self.batch, self.page_table, self.tier_state,
                        self.ws_compact, total_tokens=total, cu_seqlens=cu_seqlens, k=k, v=v,
                        scores=scores, tiers=tiers)
 
     def compact_step(self, seq_len, k_new, v_new):
+        self.chain = 0
         diffkv_compact(self.cfg, self.pool, STEP, self.batch, self.page_table, self.tier_state,
                        self.ws_compact, seq_len=seq_len, k=k_new, v=v_new)
 
     def release(self, mask):
+        self.chain = 0
         diffkv_compact(self.cfg, self.pool, RELEASE, self.batch, self.page_table, self.tier_state,
                        self.ws_compact, release_mask=mask)
 
     def decode_attn(self, q, seq_len, update_scores: int = 0, out=None):
         if out is None:
             out = torch.empty(self.batch, self.H * self.G, self.d, dtype=torch.float32, device=q.device)
+        if update_scores:
+            self.chain = 0
         diffkv_decode_attn(self.cfg, self.pool, self.batch, q, self.page_table, self.tier_state, seq_len,
                            out, int(update_scores), self.ws_attn)
         return out
 
-    def decode_step(self, q, seq_len, k_new, v_new, update_scores: int = 1, out=None):
-        """compact_step(seq_len, k_new, v_new) then decode_attn(q, seq_len), as one call."""
+    def decode_step(self, q, seq_len, k_new, v_new, update_scores: int = 1, out=None, chain=None):
+        """compact_step(seq_len, k_new, v_new) then decode_attn(q, seq_len), as one call.
+
+        chain: None follows this object's own count of decode_step calls
+        made in a row (0 forces the plan kernel)."""
         if out is None:
             out = torch.empty(self.batch, self.H * self.G, self.d, dtype=torch.float32, device=q.device)
+        c = self.chain if chain is None else int(chain)
+        self.chain = 0
         diffkv_decode_step(self.cfg, self.pool, self.batch, seq_len, k_new, v_new, q, self.page_table,
-                           self.tier_state, out, int(update_scores), self.ws_decode)
+                           self.tier_state, out, int(update_scores), self.ws_decode,
+                           chain=c if update_scores == 1 else 0)
+        if update_scores == 1:
+            self.chain = c + 1
         return out
 
     def update_scores(self, seq_len):
+        self.chain = 0
         diffkv_update_scores(self.cfg, self.pool, self.batch, self.page_table, self.tier_state, seq_len,
                              self.ws_attn)

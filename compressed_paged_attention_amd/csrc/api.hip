@@ -10,6 +10,9 @@ using namespace dkv;
 
 namespace {
 
+// workspaces hold 8- and 16-byte words at 256-byte offsets
+bool ws_ok(const void* ws) { return ws && ((uintptr_t)ws & 255) == 0; }
+
 bool cfg_ok(const diffkv_config* c) {
   if (!c) return false;
   if (c->head_dim != 64 && c->head_dim != 128) return false;
@@ -75,8 +78,12 @@ size_t diffkv_workspace_bytes(const diffkv_config* cfg, int32_t op, int32_t batc
     case DIFFKV_RELEASE: return release_workspace(c, batch);
     case DIFFKV_ATTN: return attn_workspace(c, batch, false);
     case DIFFKV_ATTN_SCORES: return attn_workspace(c, batch, true);
-    case DIFFKV_DECODE_STEP: return align_up(step_workspace(c, batch), 256) + attn_workspace(c, batch, false);
-    case DIFFKV_DECODE_STEP_SCORES: return align_up(step_workspace(c, batch), 256) + attn_workspace(c, batch, true);
+    case DIFFKV_DECODE_STEP:
+      return align_up(step_workspace(c, batch), 256) + align_up(attn_workspace(c, batch, false), 256) +
+             step_workspace(c, batch);
+    case DIFFKV_DECODE_STEP_SCORES:
+      return align_up(step_workspace(c, batch), 256) + align_up(attn_workspace(c, batch, true), 256) +
+             step_workspace(c, batch);
     default: return 0;
   }
 }
@@ -119,19 +126,19 @@ int diffkv_compact(const diffkv_config* cfg, const diffkv_pool* pool, int32_t mo
       if (batch > 0 && !cu_seqlens) return DIFFKV_E_INVALID;
       if (total_tokens > 0 && (!k || !v || !scores || !tiers)) return DIFFKV_E_INVALID;
       need = prompt_workspace(c, batch, total_tokens);
-      if (!workspace || workspace_bytes < need) return DIFFKV_E_WORKSPACE;
+      if (!ws_ok(workspace) || workspace_bytes < need) return DIFFKV_E_WORKSPACE;
       return rc(launch_prompt(c, p, batch, total_tokens, cu_seqlens, k, v, scores, tiers, page_table, tier_state,
                               workspace, s));
     case DIFFKV_STEP:
       if (c.W < 2) return DIFFKV_E_INVALID;
       if (batch > 0 && (!seq_len || !k || !v)) return DIFFKV_E_INVALID;
       need = step_workspace(c, batch);
-      if (!workspace || workspace_bytes < need) return DIFFKV_E_WORKSPACE;
+      if (!ws_ok(workspace) || workspace_bytes < need) return DIFFKV_E_WORKSPACE;
       return rc(launch_step(c, p, batch, seq_len, k, v, page_table, tier_state, workspace, s));
     case DIFFKV_RELEASE:
       if (batch > 0 && !release_mask) return DIFFKV_E_INVALID;
       need = release_workspace(c, batch);
-      if (!workspace || workspace_bytes < need) return DIFFKV_E_WORKSPACE;
+      if (!ws_ok(workspace) || workspace_bytes < need) return DIFFKV_E_WORKSPACE;
       return rc(launch_release(c, p, batch, release_mask, page_table, tier_state, workspace, s));
     default:
       return DIFFKV_E_INVALID;
@@ -147,27 +154,29 @@ int diffkv_decode_attn(const diffkv_config* cfg, const diffkv_pool* pool, int32_
   if (update_scores < 0 || update_scores > 2) return DIFFKV_E_INVALID;
   const Cfg c = to_cfg(cfg);
   const size_t need = attn_workspace(c, batch, update_scores != 0);
-  if (!workspace || workspace_bytes < need) return DIFFKV_E_WORKSPACE;
+  if (!ws_ok(workspace) || workspace_bytes < need) return DIFFKV_E_WORKSPACE;
   return rc(launch_attn(c, to_pool(pool), batch, q, page_table, tier_state, seq_len, out, update_scores,
                         workspace, (hipStream_t)stream));
 }
 
 int diffkv_decode_step(const diffkv_config* cfg, const diffkv_pool* pool, int32_t batch, const int32_t* seq_len,
                        const uint16_t* k_new, const uint16_t* v_new, const uint16_t* q, int32_t* page_table,
-                       int32_t* tier_state, float* out, int32_t update_scores, void* workspace,
+                       int32_t* tier_state, float* out, int32_t update_scores, int32_t chain, void* workspace,
                        size_t workspace_bytes, void* stream) {
   if (!cfg_ok(cfg) || !pool_ok(cfg, pool) || batch < 0) return DIFFKV_E_INVALID;
   if (batch > 0 && (!seq_len || !k_new || !v_new || !q || !page_table || !tier_state || !out))
     return DIFFKV_E_INVALID;
   if ((int64_t)batch * cfg->num_kv_heads > 65535) return DIFFKV_E_INVALID;
-  if (update_scores < 0 || update_scores > 2) return DIFFKV_E_INVALID;
+  if (update_scores < 0 || update_scores > 2 || chain < 0) return DIFFKV_E_INVALID;
   const Cfg c = to_cfg(cfg);
   if (c.W < 2) return DIFFKV_E_INVALID;
   const size_t ws_step = align_up(step_workspace(c, batch), 256);
-  const size_t need = ws_step + attn_workspace(c, batch, update_scores != 0);
-  if (!workspace || workspace_bytes < need) return DIFFKV_E_WORKSPACE;
+  const size_t ws_attn = align_up(attn_workspace(c, batch, update_scores != 0), 256);
+  const size_t need = ws_step + ws_attn + step_workspace(c, batch);
+  if (!ws_ok(workspace) || workspace_bytes < need) return DIFFKV_E_WORKSPACE;
+  uint8_t* w = (uint8_t*)workspace;
   return rc(launch_decode_step(c, to_pool(pool), batch, seq_len, k_new, v_new, q, page_table, tier_state, out,
-                               update_scores, workspace, (uint8_t*)workspace + ws_step, (hipStream_t)stream));
+                               update_scores, chain, w, w + ws_step, w + ws_step + ws_attn, (hipStream_t)stream));
 }
 
 int diffkv_update_scores(const diffkv_config* cfg, const diffkv_pool* pool, int32_t batch, const int32_t* page_table,
@@ -177,7 +186,7 @@ int diffkv_update_scores(const diffkv_config* cfg, const diffkv_pool* pool, int3
   if (batch > 0 && (!page_table || !tier_state || !seq_len)) return DIFFKV_E_INVALID;
   if ((int64_t)batch * cfg->num_kv_heads > 65535) return DIFFKV_E_INVALID;
   const Cfg c = to_cfg(cfg);
-  if (!workspace || workspace_bytes < attn_workspace(c, batch, true)) return DIFFKV_E_WORKSPACE;
+  if (!ws_ok(workspace) || workspace_bytes < attn_workspace(c, batch, true)) return DIFFKV_E_WORKSPACE;
   return rc(launch_scores(c, to_pool(pool), batch, page_table, tier_state, seq_len, workspace,
                           (hipStream_t)stream));
 }

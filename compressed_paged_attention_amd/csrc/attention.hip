@@ -410,6 +410,16 @@ struct StepArgs {
   uint64_t* ptr;
   int64_t U;
   int direct;  // every workgroup redoes the demand prefix sum (no coordination kernel)
+  // chained: hdr/rec/nf are the slot the previous step's attention left
+  // (its chain words checked by every workgroup, pointer start from it),
+  // not the plan kernel's
+  int chained;
+  const int32_t* cw;
+  // the other slot, for the next step (written with the score update; null: none)
+  int64_t* hdr_n;
+  int32_t* rec_n;
+  int32_t* nf_n;
+  int32_t* cw_n;
 };
 
 template <int D, int MODE, bool PACK, bool STEP>
@@ -518,14 +528,25 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
                (uint32_t*)img_h, (uint32_t*)img_l);
     if (sa.direct) {
       start = sa.hdr[SH_START];
-      const int64_t end = sa.hdr[SH_END];
+      int64_t end;
       uint32_t fl;
       int total;
-      step_verdict(u, sa.U, sa.nf, s_vd, fl, total, rank);
+      if (sa.chained) {
+        // the pool's end pointer moves only between steps; its start is
+        // read live as a check (workgroup 0 may already have advanced it)
+        end = (int64_t)sa.ptr[1];
+        const int64_t live = (int64_t)sa.ptr[0];
+        step_verdict_chain(u, sa.U, H, sa.cw, seq_len, state, s_vd, fl, total, rank);
+        if (live != start && live != start + total) fl |= kStStale;
+      } else {
+        end = sa.hdr[SH_END];
+        step_verdict(u, sa.U, sa.nf, s_vd, fl, total, rank);
+      }
       const uint32_t st = fl ? fl : (total > end - start ? (uint32_t)kStExhausted : 0u);
       if (u == 0 && tid == 64 * kCW) {
         if (st) atomicOr(status, st);
         else sa.ptr[0] = (uint64_t)(start + total);
+        if (sa.hdr_n) sa.hdr_n[SH_START] = st ? start : start + total;
       }
       go = st == 0 && (wu & kActive) != 0;
     } else {
@@ -571,6 +592,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
         }
       if (N > 0 && !sok && tid == 0) atomicOr(status, kStBadState);
     }
+    if constexpr (STEP)
+      if (sa.cw_n && tid == 0) sa.cw_n[kChainWords * u] = -1;  // no plan for the next step
     if (S > 1) {
       float* mp = part + (((int64_t)u * S + split) * G) * (D + 2);
       for (int x = tid; x < G; x += blockDim.x) {
@@ -824,6 +847,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
         ml[(u * G + tid) * 2 + 0] = -INFINITY;
         ml[(u * G + tid) * 2 + 1] = 0.0f;
       }
+      if constexpr (STEP)
+        if (sa.cw_n && tid == 0) sa.cw_n[kChainWords * u] = -1;
       return;
     }
     for (int x = tid; x < G * D; x += blockDim.x) orow[x] = ocol(x / D, x % D) * sI[x / D];
@@ -957,15 +982,59 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
           argmin_step<1>(bl, N1);
           argmin_step<2>(bl, N1);
         }
-        // a record only where the next step's plan kernel would accept the state
-        if (lane == 0 && ph >= 1 && nh + nl <= N1 && !(tc1 >= 0 && tcs < 0)) {
+        // a record only where the next step's plan kernel would accept the
+        // state.  Every lane holds the candidates and takes the decision;
+        // lane k writes word k of each record (one store instruction per
+        // record, one round of id lookups).
+        const bool rec_ok = ph >= 1 && nh + nl <= N1 && !(tc1 >= 0 && tcs < 0);
+        if (rec_ok) {
           const Plan pn = plan_decide(N1, pa.W, pa.S_max, pa.lo_en, (double)pa.ah, (double)pa.al, nh, nl, ph, pl,
                                       L, tcs, tcsum, bh, bl);
           uint32_t rw[kRecWords];
           plan_rec_fill(rw, N1, nh, nl, ph, pl, pn);
-          uint32_t* dst = (uint32_t*)(pages + (int64_t)id_tix(0) * page_bytes + plan_rec_off<D>());
+          uint32_t wv = rw[0];
 #pragma unroll
-          for (int k = 0; k < kRecWords; k++) dst[k] = rw[k];
+          for (int k = 1; k < kRecWords; k++) wv = lane == k ? rw[k] : wv;
+          uint32_t* dst = (uint32_t*)(pages + (int64_t)id_tix(0) * page_bytes + plan_rec_off<D>());
+          if (lane < kRecWords) dst[lane] = wv;
+          if constexpr (STEP) {
+            if (sa.cw_n) {
+              // the same plan in the next step's slot: the step record
+              // (plan fields, then the ids of the pages the commit reads,
+              // from the table after this step: the page list in LDS when it
+              // is there; entries past the unit's pages are -1), the chain
+              // words and the demand word
+              auto cl = [&](int t) { return min(max(t, 0), L - 1); };
+              const int tix = lane == S_IDH   ? cl(pn.new_hi >> 4)
+                              : lane == S_IDL ? cl(L - 1 - (pn.lo_slot >> 5))
+                              : lane == S_IDS ? cl(pn.lo_src >> 4)
+                                              : 0;
+              int32_t id;
+              if (lg_lds) {
+                const int j = tix < ph ? tix : ph + (L - 1 - tix);
+                id = id_s[min(j, TPg - 1)];
+                id = j < TPg ? id : -1;
+              } else {
+                id = id_tix(tix);
+              }
+              const int32_t rv = lane == S_NEWHI   ? pn.new_hi
+                                 : lane == S_HIAPP  ? pn.hi_app
+                                 : lane == S_LOSRC  ? pn.lo_src
+                                 : lane == S_LOSLOT ? pn.lo_slot
+                                 : lane == S_LOAPP  ? pn.lo_app
+                                 : lane == S_PAGE   ? -1
+                                                    : id;
+              if (lane <= S_IDF) sa.rec_n[u * kSRec + lane] = rv;
+              const int32_t c4[kChainWords] = {(int32_t)N1, nh, nl, ph, pl, pn.nfw, pn.hi_app, pn.lo_app};
+              int32_t cv = c4[0];
+#pragma unroll
+              for (int k = 1; k < kChainWords; k++) cv = lane == k ? c4[k] : cv;
+              if (lane < kChainWords) sa.cw_n[kChainWords * u + lane] = cv;
+              if (lane == 0) sa.nf_n[u] = pn.nfw;
+            }
+          }
+        } else if (STEP && lane == 0 && sa.cw_n) {
+          sa.cw_n[kChainWords * u] = -1;
         }
       }
     }
@@ -1140,7 +1209,7 @@ hipError_t launch_attn(const Cfg& c, const Pool& p, int batch, const uint16_t* q
 // diffkv_update_scores), plan, commit and attention kernels in turn.
 hipError_t launch_decode_step(const Cfg& c, const Pool& p, int batch, const int32_t* seq_len, const uint16_t* k,
                               const uint16_t* v, const uint16_t* q, int32_t* table, int32_t* state, float* out,
-                              int mode, void* ws_step, void* ws_attn, hipStream_t s) {
+                              int mode, int chain, void* ws_step, void* ws_attn, void* ws_next, hipStream_t s) {
   const int64_t U = (int64_t)batch * c.H;
   if (U == 0) return hipSuccess;
   const int S = attn_splits(c, batch);
@@ -1149,20 +1218,46 @@ hipError_t launch_decode_step(const Cfg& c, const Pool& p, int batch, const int3
     if (e != hipSuccess) return e;
     return launch_attn(c, p, batch, q, table, state, seq_len, out, mode, ws_attn, s);
   }
-  hipError_t e = launch_step_plan(c, p, batch, seq_len, table, state, ws_step, s);
-  if (e != hipSuccess) return e;
   const bool direct = U <= kDirectUnits;
-  if (!direct) {
-    e = launch_step_coord(c, p, batch, ws_step, s);
+  // chained steps: the attention with the score update plans the next step
+  // into the other slot; a chained call reads slot (chain & 1) and runs no
+  // plan kernel
+  const bool can_chain = direct && mode == 1;
+  const bool chained = can_chain && chain > 0;
+  void* cur = chained && (chain & 1) ? ws_next : ws_step;
+  void* nxt = cur == ws_step ? ws_next : ws_step;
+  hipError_t e;
+  if (!chained) {
+    e = launch_step_plan(c, p, batch, seq_len, table, state, ws_step, s);
     if (e != hipSuccess) return e;
+    if (!direct) {
+      e = launch_step_coord(c, p, batch, ws_step, s);
+      if (e != hipSuccess) return e;
+    }
   }
-  const StepWs sw = step_carve(c, batch, ws_step);
+  const StepWs sw = step_carve(c, batch, cur), sn = step_carve(c, batch, nxt);
   AttnWs w = attn_carve(c, batch, mode != 0, ws_attn, nullptr);
   const float scale_log2 = (1.0f / sqrtf((float)c.d)) * kLog2e;
   const dim3 grid(1, (unsigned)U), block(kThreads);
   const bool pack = 2 * c.G <= 16;
   const PolicyArgs pa{c.W, c.S_max, c.lo_en, c.ah, c.al};
-  const StepArgs sa{k, v, sw.hdr, sw.rec, sw.nf, p.list, table, state, p.ptr, U, direct ? 1 : 0};
+  const StepArgs sa{k,
+                    v,
+                    sw.hdr,
+                    sw.rec,
+                    sw.nf,
+                    p.list,
+                    table,
+                    state,
+                    p.ptr,
+                    U,
+                    direct ? 1 : 0,
+                    chained ? 1 : 0,
+                    sw.cw,
+                    can_chain ? sn.hdr : nullptr,
+                    can_chain ? sn.rec : nullptr,
+                    can_chain ? sn.nf : nullptr,
+                    can_chain ? sn.cw : nullptr};
 #define DKV_STEP(D, M, PK)                                                                                \
   attn_kernel<D, M, PK, true><<<grid, block, 0, s>>>(c.H, c.G, c.L, 1, p.P, p.page_bytes, pa, scale_log2, q, \
                                                      table, state, seq_len, p.pages, out, w.part, w.ml,      \

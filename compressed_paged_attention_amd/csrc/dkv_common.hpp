@@ -32,7 +32,7 @@ namespace dkv {
 constexpr int kHiTokens = 16;
 constexpr int kLoTokens = 32;
 constexpr int kTierPrune = 0, kTierLo = 1, kTierHi = 2;
-constexpr uint32_t kStExhausted = 1u, kStOverflow = 2u, kStBadState = 4u;
+constexpr uint32_t kStExhausted = 1u, kStOverflow = 2u, kStBadState = 4u, kStStale = 8u;
 
 struct Seg {
   int T, kbits, vbits, kc, km, vc, vm, sc, ps, bytes;

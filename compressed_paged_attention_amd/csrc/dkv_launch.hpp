@@ -61,11 +61,12 @@ hipError_t launch_attn(const Cfg& c, const Pool& p, int batch, const uint16_t* q
                        float* out, int mode, void* ws, hipStream_t s);
 hipError_t launch_scores(const Cfg& c, const Pool& p, int batch, const int32_t* table,
                          const int32_t* state, const int32_t* seq_len, void* ws, hipStream_t s);
-// generation step then attention for the same step
+// generation step then attention for the same step; ws_step and ws_next are
+// the two step slots (chain: consecutive chained calls before this one)
 hipError_t launch_decode_step(const Cfg& c, const Pool& p, int batch, const int32_t* seq_len,
                               const uint16_t* k, const uint16_t* v, const uint16_t* q, int32_t* table,
-                              int32_t* state, float* out, int mode, void* ws_step, void* ws_attn,
-                              hipStream_t s);
+                              int32_t* state, float* out, int mode, int chain, void* ws_step, void* ws_attn,
+                              void* ws_next, hipStream_t s);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

@@ -24,10 +24,13 @@ constexpr int32_t kActive = 4;
 // sum over the demand words itself (no coordination kernel in between).
 constexpr int64_t kDirectUnits = 2048;
 
+// One step workspace (slot): pointer snapshot, per-unit records and demand
+// words, and per-unit chain words (see kChainWords).
 struct StepWs {
   int64_t* hdr;
   int32_t* rec;
   int32_t* nf;
+  int32_t* cw;
 };
 
 inline StepWs step_carve(const Cfg& c, int batch, void* ws) {
@@ -39,8 +42,20 @@ inline StepWs step_carve(const Cfg& c, int batch, void* ws) {
   w.rec = (int32_t*)p;
   p += align_up(U * kSRec * sizeof(int32_t), 256);
   w.nf = (int32_t*)p;
+  p += align_up(U * sizeof(int32_t), 256);
+  w.cw = (int32_t*)p;
   return w;
 }
+
+// Chained decode steps: a step whose attention updates every score sum of a
+// unit also plans the unit's next step (length N + 1, the tier state after
+// this step's commit) and leaves record, demand word and these chain words
+// in the other workspace slot, so the next step needs no plan kernel:
+//   {N the plan is for (-1: no plan), nh, nl, ph, pl, demand word, hi_app, lo_app}
+// The consumer checks every active unit's words against its length and tier
+// state (a tier state word may also read as its value after the unit's own
+// commit in the same launch).
+constexpr int kChainWords = 8;
 
 // ---------------------------------------------------------------------------
 // commit: phase 1 loads everything the unit needs, phase 2 quantizes and
@@ -516,6 +531,58 @@ __device__ inline void step_verdict(int64_t u, int64_t U, const int32_t* nf, int
   for (int64_t base = 0; base < U; base += blockDim.x) {
     const int64_t x = base + threadIdx.x;
     const int32_t w = x < U ? nf[x] : 0;
+    fl |= (uint32_t)w >> 8;
+    const bool need = (w & 3) != 0;
+    tot += __popcll(__ballot(need));
+    rk += __popcll(__ballot(need && x < u));
+  }
+  fl = wave_reduce(fl, [](uint32_t a, uint32_t b) { return a | b; });
+  if (lane == 0) {
+    lds[wid] = tot;
+    lds[nw + wid] = rk;
+    lds[2 * nw + wid] = (int)fl;
+  }
+  __syncthreads();
+  total = 0;
+  rank = 0;
+  flags = 0;
+  for (int w = 0; w < nw; w++) {
+    total += lds[w];
+    rank += lds[nw + w];
+    flags |= (uint32_t)lds[2 * nw + w];
+  }
+}
+
+// step_verdict over a chained slot: a unit whose batch slot is inactive
+// (seq_len <= 0) demands nothing; an active unit whose chain words were not
+// made for its length and tier state (the caller broke the chain) sets
+// kStStale.  Other workgroups may commit while this one reads: each tier
+// state word passes as its value before the step or after the unit's commit
+// (a word may be read before its store and its neighbour after).
+__device__ inline void step_verdict_chain(int64_t u, int64_t U, int H, const int32_t* cw, const int32_t* seq_len,
+                                          const int32_t* state, int* lds, uint32_t& flags, int& total, int& rank) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int tot = 0, rk = 0;
+  uint32_t fl = 0;
+#pragma unroll 2
+  for (int64_t base = 0; base < U; base += blockDim.x) {
+    const int64_t x = base + threadIdx.x;
+    const bool in = x < U;
+    const int64_t xc = in ? x : 0;
+    const int32_t N = seq_len[(int)xc / H];
+    const int4 c0 = ((const int4*)cw)[2 * xc], c1 = ((const int4*)cw)[2 * xc + 1];
+    const int32_t* s4 = state + 4 * xc;
+    const int32_t snh = s4[0], snl = s4[1], sph = s4[2], spl = s4[3];
+    int32_t w = c1.y;
+    if (!in || N <= 0) {
+      w = 0;
+    } else {
+      const int need = w & 3;
+      const bool ok = c0.x == N && (snh == c0.y || snh == c0.y + c1.z) && (snl == c0.z || snl == c0.z + c1.w) &&
+                      (sph == c0.w || sph == c0.w + (need == kTierHi)) &&
+                      (spl == c1.x || spl == c1.x + (need == kTierLo));
+      if (!ok) fl |= kStStale;
+    }
     fl |= (uint32_t)w >> 8;
     const bool need = (w & 3) != 0;
     tot += __popcll(__ballot(need));

@@ -38,7 +38,7 @@ namespace dkv {
 size_t step_workspace(const Cfg& c, int batch) {
   const size_t U = (size_t)batch * c.H;
   return align_up(16 * sizeof(int64_t), 256) + align_up(U * kSRec * sizeof(int32_t), 256) +
-         align_up(U * sizeof(int32_t), 256);
+         align_up(U * sizeof(int32_t), 256) + align_up(U * kChainWords * sizeof(int32_t), 256);
 }
 
 constexpr int kPlanThreads = 256;
@@ -70,10 +70,34 @@ __global__ __launch_bounds__(kPlanThreads) void step_plan_kernel(int H, int L, i
   __shared__ uint32_t s_bad;
   __shared__ Cand lds[2][kPlanThreads / 64];
   __shared__ int s_rec;
-  // ---- round 1: length, tier state, the table row ----
+  // ---- round 1: length, tier state, the table row (every load of a
+  // thread issued before any is used: one round trip) ----
   const bool cached = L <= kRowCache;
-  if (cached)
-    for (int j = tid; j < L; j += kPlanThreads) row_s[j] = row[j];
+  if (cached) {
+    constexpr int kPer = kRowCache / kPlanThreads;
+    int32_t v[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; k++) {
+      const int j = tid + k * kPlanThreads;
+      v[k] = j < L ? row[j] : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; k++) {
+      const int j = tid + k * kPlanThreads;
+      if (j < L) row_s[j] = v[k];
+    }
+  }
+  // the plan record in the unit's first page: its loads go out before the
+  // barrier (the id is clamped into the pool; used only if it is the
+  // unit's first high page)
+  const int32_t first_id = row[0];
+  uint32_t rw[kRecWords];
+  if (tid == 0) {
+    const uint32_t* w = (const uint32_t*)(pages + (int64_t)min(max(first_id, 0), (int32_t)(P - 1)) * page_bytes +
+                                          plan_rec_off<D>());
+#pragma unroll
+    for (int k = 0; k < kRecWords; k++) rw[k] = w[k];
+  }
   if (u == 0 && tid == 0) {  // pointer snapshot for the commit kernel
     hdr[SH_START] = (int64_t)ptr[0];
     hdr[SH_END] = (int64_t)ptr[1];
@@ -104,12 +128,8 @@ __global__ __launch_bounds__(kPlanThreads) void step_plan_kernel(int H, int L, i
   // ---- a plan record left by the previous attention: no scan needed ----
   if (tid == 0) {
     s_rec = 0;
-    const int32_t p0 = ph >= 1 ? page_of(0) : -1;
+    const int32_t p0 = ph >= 1 ? first_id : -1;
     if (p0 >= 0 && p0 < P) {
-      const uint32_t* w = (const uint32_t*)(pages + (int64_t)p0 * page_bytes + plan_rec_off<D>());
-      uint32_t rw[kRecWords];
-#pragma unroll
-      for (int k = 0; k < kRecWords; k++) rw[k] = w[k];
       Plan pr;
       if (plan_rec_check(rw, N, nh, nl, ph, pl, pr)) {
         s_rec = 1;

@@ -18,7 +18,8 @@
  *  - Tensors are row-major and contiguous in the shapes given below.
  *  - Return codes report host-detectable problems only: DIFFKV_E_INVALID
  *    (null pointer, bad config or sizes), DIFFKV_E_WORKSPACE (workspace
- *    smaller than diffkv_workspace_bytes), DIFFKV_E_HIP (launch error).  On
+ *    smaller than diffkv_workspace_bytes, or not 256-byte aligned as
+ *    hipMalloc returns it), DIFFKV_E_HIP (launch error).  On
  *    a non-zero return nothing was enqueued.
  *  - Conditions found on the device (pool exhausted, table row overflow,
  *    inconsistent state) set sticky bits in pool->status; a compaction call
@@ -73,7 +74,12 @@ typedef struct {
 } diffkv_pool;
 
 enum { DIFFKV_OK = 0, DIFFKV_E_INVALID = 1, DIFFKV_E_WORKSPACE = 2, DIFFKV_E_HIP = 3 };
-enum { DIFFKV_ST_POOL_EXHAUSTED = 1u, DIFFKV_ST_TABLE_OVERFLOW = 2u, DIFFKV_ST_BAD_STATE = 4u };
+enum {
+  DIFFKV_ST_POOL_EXHAUSTED = 1u,
+  DIFFKV_ST_TABLE_OVERFLOW = 2u,
+  DIFFKV_ST_BAD_STATE = 4u,
+  DIFFKV_ST_STALE_CHAIN = 8u /* diffkv_decode_step: chain > 0 on a cache changed since its plans */
+};
 enum {
   DIFFKV_PROMPT = 0,
   DIFFKV_STEP = 1,
@@ -200,14 +206,30 @@ int diffkv_decode_attn(const diffkv_config* cfg, const diffkv_pool* pool, int32_
  *  seq_len  int32 [batch]: length before this step's token (= position of
  *           the query token); <= 0 marks an inactive request
  *  k_new, v_new fp16 [batch, H, d]; q fp16 [batch, H*G, d]; out fp32
- *  workspace: diffkv_workspace_bytes(DIFFKV_DECODE_STEP[_SCORES]); with
+ *  chain    0, or the number of diffkv_decode_step(update_scores = 1) calls
+ *           made just before this one on the same pool, page_table,
+ *           tier_state and workspace, with nothing else writing them in
+ *           between (seq_len one higher at each call).  The attention of
+ *           such a step updates every score sum of a unit and, from them,
+ *           plans the unit's next step (the generation-phase decision at
+ *           length seq_len + 1) into the workspace; a chained call
+ *           (chain > 0, update_scores = 1, one split per unit,
+ *           batch * H <= 2048) takes those plans and runs no plan kernel.
+ *           Each plan carries a tag of the length and tier state it was
+ *           made for, and the pool's start pointer is checked against the
+ *           previous step's: on any mismatch the whole step is aborted
+ *           (nothing committed, DIFFKV_ST_STALE_CHAIN set; repeat it with
+ *           chain = 0).  Ignored where a chained call does not apply.
+ *  workspace: diffkv_workspace_bytes(DIFFKV_DECODE_STEP[_SCORES]); it
+ *           carries the plans from one chained call to the next; with
  *           update_scores = 2 it carries the logits to diffkv_update_scores
  *           at byte offset diffkv_workspace_bytes(DIFFKV_STEP) rounded up to
  *           256 (pass that sub-buffer). */
 int diffkv_decode_step(const diffkv_config* cfg, const diffkv_pool* pool, int32_t batch,
                        const int32_t* seq_len, const uint16_t* k_new, const uint16_t* v_new,
                        const uint16_t* q, int32_t* page_table, int32_t* tier_state, float* out,
-                       int32_t update_scores, void* workspace, size_t workspace_bytes, void* stream);
+                       int32_t update_scores, int32_t chain, void* workspace, size_t workspace_bytes,
+                       void* stream);
 
 /* The score update of a preceding diffkv_decode_attn(update_scores = 2) call
  * with the same arguments and workspace (policy reading of the notes' stored

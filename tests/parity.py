@@ -103,4 +103,7 @@ def resync_scores(g, st):
     pages = g.pool.pages.view(g.pool.num_pages, -1)
     idx = torch.tensor(live, dtype=torch.int64, device=pages.device)
     pages[idx] = torch.from_numpy(st.pages[live]).to(pages.device)
+    # pages written from outside the library: plans made from the old scores
+    # no longer apply (the next decode step runs the plan kernel)
+    g.chain = 0
     torch.cuda.synchronize()

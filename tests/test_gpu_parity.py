@@ -460,52 +460,169 @@ def _plan_record_words(g, cfg):
     return torch.where(ok, w, torch.zeros_like(w))
 
 
+def _assert_caches_equal(a_, b_, P, what):
+    """Two caches byte-identical: table, tier state, pool lists and pointer, pages."""
+    for name in ("page_table", "tier_state"):
+        assert torch.equal(getattr(a_, name), getattr(b_, name)), f"{what}: {name} differs"
+    assert torch.equal(a_.pool.free_list, b_.pool.free_list), f"{what}: free lists differ"
+    assert torch.equal(a_.pool.ptr, b_.pool.ptr), f"{what}: pointers differ"
+    pa, pb = np_(a_.pool.pages.view(P, -1)), np_(b_.pool.pages.view(P, -1))
+    live = sorted({int(x) for x in np_(a_.page_table).ravel() if x >= 0})
+    bad = [p_ for p_ in live if not np.array_equal(pa[p_], pb[p_])]
+    assert not bad, f"{what}: {len(bad)} of {len(live)} live pages differ, first {bad[:5]}"
+
+
+def _twin_caches(dk, cfg, batch, lens, P, n):
+    from workloads import synth
+    pr = synth.make_prompt(cfg, lens=lens)
+    st = []
+    for _ in range(n):
+        s_ = dk.DiffKVState(cfg, batch, P, max_total_tokens=int(lens.sum()), device=dev)
+        cu = pr["cu_seqlens"].to(dev)
+        tiers, _ = s_.classify(cu, pr["scores"].to(dev))
+        s_.compact_prompt(cu, pr["k"].to(dev), pr["v"].to(dev), pr["scores"].to(dev), tiers)
+        st.append(s_)
+    return st
+
+
 def test_plan_record_matches_scan(dk, orc):
-    """The next step's plan that the fused score update leaves in each unit's
-    first page gives exactly the state a fresh scan gives: two identical
-    caches, one stepping from the records, one with every record erased
-    before each step, stay byte-identical."""
+    """The next step's plan that the fused score update leaves behind gives
+    exactly the state a fresh scan gives: three identical caches -- A steps
+    chained (plans from the previous step's workspace slot, no plan kernel),
+    B through the plan kernel reading the records in each unit's first page,
+    C through the plan kernel with every record erased before each step (a
+    scan) -- stay byte-identical."""
     from tests.parity import plan_record_span, first_pages, masked
     from workloads import synth
     cfg = _medium_cfg("llama3_8b", batch=32, max_seq_len=1500)
     assert dk.diffkv_attn_splits(cfg, 32) == 1
     g = torch.Generator().manual_seed(51)
     lens = (torch.randint(5, 80, (32,), generator=g) * 16 - torch.randint(0, 3, (32,), generator=g)).to(torch.int64)
-    pr = synth.make_prompt(cfg, lens=lens)
     P = int(sum(-(-int(n) // 16) for n in lens) * 8 * 1.2) + 64
-    st = []
-    for _ in range(2):
-        s_ = dk.DiffKVState(cfg, 32, P, max_total_tokens=int(lens.sum()), device=dev)
-        cu = pr["cu_seqlens"].to(dev)
-        tiers, _ = s_.classify(cu, pr["scores"].to(dev))
-        s_.compact_prompt(cu, pr["k"].to(dev), pr["v"].to(dev), pr["scores"].to(dev), tiers)
-        st.append(s_)
+    st = _twin_caches(dk, cfg, 32, lens, P, 3)
     off, n = plan_record_span(cfg)
     seq = lens.to(torch.int32).to(dev)
     used = 0
     for step in range(8):
         dec = synth.make_decode(cfg, step, device=dev)
-        # cache B: erase every record, so its plan kernel scans
-        b = st[1]
-        first = b.page_table[..., 0].reshape(-1)
+        # cache C: erase every record, so its plan kernel scans
+        c_ = st[2]
+        first = c_.page_table[..., 0].reshape(-1)
         first = first[first >= 0].to(torch.int64)
-        b.pool.pages.view(b.pool.num_pages, -1)[first, off:off + n] = 0
-        used += int((_plan_record_words(st[0], cfg) != 0).sum())
-        outs = [s_.decode_step(dec["q"], seq, dec["k_new"], dec["v_new"], update_scores=1) for s_ in st]
+        c_.pool.pages.view(c_.pool.num_pages, -1)[first, off:off + n] = 0
+        used += int((_plan_record_words(st[1], cfg) != 0).sum())
+        chains = (None, 0, 0)
+        outs = [s_.decode_step(dec["q"], seq, dec["k_new"], dec["v_new"], update_scores=1, chain=c)
+                for s_, c in zip(st, chains)]
         torch.cuda.synchronize()
-        a_, b_ = st
-        assert torch.equal(outs[0], outs[1]), f"step {step}: outputs differ"
+        assert st[0].chain == step + 1
+        assert torch.equal(outs[0], outs[1]), f"step {step}: outputs of A and B differ"
+        assert torch.equal(outs[1], outs[2]), f"step {step}: outputs of B and C differ"
+        _assert_caches_equal(st[0], st[1], P, f"step {step}: chained vs records")
+        b_, c2 = st[1], st[2]
         for name in ("page_table", "tier_state"):
-            assert torch.equal(getattr(a_, name), getattr(b_, name)), f"step {step}: {name} differs"
-        assert torch.equal(a_.pool.free_list, b_.pool.free_list) and torch.equal(a_.pool.ptr, b_.pool.ptr)
-        pa, pb = np_(a_.pool.pages.view(P, -1)), np_(b_.pool.pages.view(P, -1))
-        fp = first_pages(np_(a_.page_table))
-        for p_ in sorted({int(x) for x in np_(a_.page_table).ravel() if x >= 0}):
-            x, y = (masked(pa[p_], cfg), masked(pb[p_], cfg)) if p_ in fp else (pa[p_], pb[p_])
+            assert torch.equal(getattr(b_, name), getattr(c2, name)), f"step {step}: {name} differs"
+        assert torch.equal(b_.pool.free_list, c2.pool.free_list) and torch.equal(b_.pool.ptr, c2.pool.ptr)
+        pb, pc = np_(b_.pool.pages.view(P, -1)), np_(c2.pool.pages.view(P, -1))
+        fp = first_pages(np_(b_.page_table))
+        for p_ in sorted({int(x) for x in np_(b_.page_table).ravel() if x >= 0}):
+            x, y = (masked(pb[p_], cfg), masked(pc[p_], cfg)) if p_ in fp else (pb[p_], pc[p_])
             assert np.array_equal(x, y), f"step {step}: page {p_} differs"
         seq = seq + 1
     assert used > 0, "no plan record was used"
-    assert int(st[0].pool.status.item()) == 0
+    for s_ in st:
+        assert int(s_.pool.status.item()) == 0
+
+
+@pytest.mark.parametrize("d,G,lo", [(128, 4, 1), (64, 5, 1), (128, 7, 0), (64, 16, 1)])
+def test_chained_steps_match_plan_kernel(dk, orc, d, G, lo):
+    """Chained decode steps (each planned by the previous step's attention)
+    against the same steps through the plan kernel, for both head sizes,
+    both weight-column layouts and the low tier off: outputs and caches
+    byte-identical over steps that cross page boundaries, a release with
+    re-admission in the middle (the chain restarts) and a step without the
+    score update (which ends the chain)."""
+    from workloads import synth
+    cfg = _medium_cfg("llama3_8b", head_dim=d, gqa_group=G, lo_enabled=lo, num_kv_heads=3,
+                      batch=5, max_seq_len=420, window=64)
+    assert dk.diffkv_attn_splits(cfg, 5) == 1
+    lens = torch.tensor([383, 37, 200, 127, 64], dtype=torch.int64)
+    P = int(sum(-(-int(n) // 16) + 2 for n in lens) * 3 * 1.2) + 8
+    a_, b_ = _twin_caches(dk, cfg, 5, lens, P, 2)
+    seq = lens.to(torch.int32)
+
+    def both(step, upd=1):
+        dec = synth.make_decode(cfg, step, device=dev)
+        sd = seq.to(dev)
+        oa = a_.decode_step(dec["q"], sd, dec["k_new"], dec["v_new"], update_scores=upd)
+        ob = b_.decode_step(dec["q"], sd, dec["k_new"], dec["v_new"], update_scores=upd, chain=0)
+        torch.cuda.synchronize()
+        assert torch.equal(oa, ob), f"step {step}: outputs differ"
+        _assert_caches_equal(a_, b_, P, f"step {step}")
+
+    _say(f"chained steps d={d} G={G} lo={lo}")
+    for step in range(12):
+        both(step)
+        seq = seq + 1
+    assert a_.chain == 12
+    mask = torch.tensor([1, 0, 0, 1, 0], dtype=torch.uint8, device=dev)
+    a_.release(mask)
+    b_.release(mask)
+    lens2 = torch.tensor([95, 0, 0, 300, 0], dtype=torch.int64)
+    pr2 = synth.make_prompt(cfg, lens=lens2, salt=5)
+    for s_ in (a_, b_):
+        cu = pr2["cu_seqlens"].to(dev)
+        tiers, _ = s_.classify(cu, pr2["scores"].to(dev))
+        s_.compact_prompt(cu, pr2["k"].to(dev), pr2["v"].to(dev), pr2["scores"].to(dev), tiers)
+    assert a_.chain == 0
+    seq = torch.where(mask.cpu() == 1, lens2.to(torch.int32), seq)
+    for step in range(6):
+        both(50 + step, upd=0 if step == 3 else 1)
+        seq = seq + 1
+    assert a_.chain == 2
+    for s_ in (a_, b_):
+        assert int(s_.pool.status.item()) == 0
+
+
+def test_chain_broken_aborts_step(dk, orc):
+    """A chained call on a cache that does not match the plans (here: the
+    length not advanced) aborts the whole step with STALE_CHAIN: nothing is
+    committed and the attention runs on the unchanged cache, as an
+    attention call alone would; repeated with chain = 0 the step commits
+    and matches the plan kernel's."""
+    from workloads import synth
+    cfg = _medium_cfg("llama3_8b", batch=32, max_seq_len=1500)
+    g = torch.Generator().manual_seed(52)
+    lens = (torch.randint(5, 80, (32,), generator=g) * 16 - torch.randint(0, 3, (32,), generator=g)).to(torch.int64)
+    P = int(sum(-(-int(n) // 16) for n in lens) * 8 * 1.2) + 64
+    a_, b_ = _twin_caches(dk, cfg, 32, lens, P, 2)
+    seq = lens.to(torch.int32).to(dev)
+    for step in range(3):
+        dec = synth.make_decode(cfg, step, device=dev)
+        for s_ in (a_, b_):
+            s_.decode_step(dec["q"], seq, dec["k_new"], dec["v_new"], update_scores=1)
+        seq = seq + 1
+    torch.cuda.synchronize()
+    _assert_caches_equal(a_, b_, P, "before the broken chain")
+    # A: a chained call with the previous step's length; B: the attention alone
+    dec = synth.make_decode(cfg, 3, device=dev)
+    stale = seq - 1
+    oa = a_.decode_step(dec["q"], stale, dec["k_new"], dec["v_new"], update_scores=1)
+    ob = b_.decode_attn(dec["q"], stale, update_scores=1)
+    torch.cuda.synchronize()
+    assert int(a_.pool.status.item()) == dk.ST_STALE_CHAIN
+    assert int(b_.pool.status.item()) == 0
+    # (with no unit committing, the fused kernel's page order and arithmetic
+    # are the attention kernel's)
+    assert torch.equal(oa, ob), "broken chain: attention differs"
+    _assert_caches_equal(a_, b_, P, "broken chain")
+    # recovery: the status cleared, the step repeated without the chain
+    a_.pool.status.zero_()
+    for s_ in (a_, b_):
+        s_.decode_step(dec["q"], seq, dec["k_new"], dec["v_new"], update_scores=1, chain=0)
+    torch.cuda.synchronize()
+    assert int(a_.pool.status.item()) == 0
+    _assert_caches_equal(a_, b_, P, "recovered step")
 
 
 def test_deterministic_replay(dk, orc):

@@ -54,3 +54,27 @@ def test_host_queries_and_validation():
                             None, None, None, None, None, None, 0, None) == dk.DIFFKV_E_INVALID
     assert L.diffkv_decode_attn(ctypes.byref(good), ctypes.byref(pool), 1, None, None, None, None, None, 0,
                                 None, 0, None) == dk.DIFFKV_E_INVALID
+
+
+def test_decode_step_host_validation():
+    """diffkv_decode_step refuses a negative chain count and a workspace off
+    256-byte alignment on the host (batch 0: no kernel could run either way);
+    its workspace holds two step slots around the attention's."""
+    import compressed_paged_attention_amd as dk
+    from workloads import synth
+    c = synth.config("llama3_8b")
+    L = dk.lib()
+    cfg = dk.make_config(c)
+    fake = 1 << 20  # never dereferenced on the host
+    pool = dk.diffkv_pool(fake, fake, fake, fake, 10, 3584)
+    need = dk.diffkv_workspace_bytes(c, dk.DECODE_STEP_SCORES, 0)
+    args = [ctypes.byref(cfg), ctypes.byref(pool), 0] + [fake] * 7
+    assert L.diffkv_decode_step(*args, 1, -1, fake, need, None) == dk.DIFFKV_E_INVALID
+    assert L.diffkv_decode_step(*args, 1, 0, fake + 16, need, None) == dk.DIFFKV_E_WORKSPACE
+    assert L.diffkv_decode_step(*args, 1, 0, fake, need - 1, None) == dk.DIFFKV_E_WORKSPACE
+    assert L.diffkv_decode_step(*args, 1, 3, fake, need, None) == dk.DIFFKV_OK
+    for b in (1, 32, 300):
+        step = dk.diffkv_workspace_bytes(c, dk.STEP, b)
+        att = dk.diffkv_workspace_bytes(c, dk.ATTN_SCORES, b)
+        r = lambda x: -(-x // 256) * 256
+        assert dk.diffkv_workspace_bytes(c, dk.DECODE_STEP_SCORES, b) == r(step) + r(att) + step
