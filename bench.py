@@ -8,8 +8,10 @@ alpha_h = 1.0, alpha_l = 0.2, W = 64, a pool of 1.25x the conservative need.
 
 A timed step is one decode step of the whole batch on the compacted cache:
 generation-step compaction, then decode attention with the score update, as
-one diffkv_decode_step call (plan kernel, then one kernel that commits each
-unit's step and attends over it when every unit is one workgroup).  The
+one diffkv_decode_step call: one kernel that commits each unit's step and
+attends over it when every unit is one workgroup.  Each replica's steps are
+chained (a step's score update plans the next one into the workspace; the
+first step of a chain runs a plan kernel first, done in the warmup).  The
 prompt side of the path (classification and prompt compaction) and the
 release are timed in the same run on the same caches and reported beside it.
 Caches rotate over several independent replicas (one per simulated layer) so
