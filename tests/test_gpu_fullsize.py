@@ -244,9 +244,25 @@ def run_sampled(dk, orc, cfg, sample, steps, what, ptr_offset=0, events=None):
 # --------------------------------------------------------------------------
 # tests
 # --------------------------------------------------------------------------
+def _clone_state(dk, g, cfg, B, P, total):
+    """A second device cache with g's tables, tier state and pool bytes."""
+    c = dk.DiffKVState(cfg, B, P, max_total_tokens=total, device=dev)
+    for name in ("page_table", "tier_state"):
+        getattr(c, name).copy_(getattr(g, name))
+    for name in ("pages", "free_list", "ptr", "status"):
+        getattr(c.pool, name).copy_(getattr(g.pool, name))
+    torch.cuda.synchronize()
+    return c
+
+
 def test_llama3_8b_full_batch(dk, orc):
     """Whole Llama3-8B-shaped batch on both sides: bit-exact state and pages,
-    attention and scores within tolerance, two decode steps."""
+    attention and scores within tolerance, for two decode steps through the
+    separate calls and one through diffkv_decode_step (the fused kernel, plan
+    kernel first).  Then the launch configuration the benchmark times --
+    chained decode steps, planned by the previous step's attention -- for
+    three steps against a copy of the cache stepping through the plan kernel:
+    outputs and caches byte-identical."""
     from workloads import synth
     from tests.test_gpu_parity import Pair
     cfg = synth.config("llama3_8b")
@@ -269,8 +285,31 @@ def test_llama3_8b_full_batch(dk, orc):
         err = p.attend(dec["q"].numpy(), seq, True, f"attn {step}")
         _say(f"  step {step}: attention max err {err:.2e}")
         seq = seq + 1
+    dec = synth.make_decode(cfg, 2)
+    err = p.decode_step(seq, dec["k_new"].numpy(), dec["v_new"].numpy(), dec["q"].numpy(), True,
+                        "fused decode step 2")
+    _say(f"  fused decode step 2: attention max err {err:.2e}")
+    seq = seq + 1
     check_device_pool(p.g)
-    del p
+    a_ = p.g
+    del p.o
+    b_ = _clone_state(dk, a_, cfg, B, P, int(lens.sum()))
+    sd = torch.from_numpy(seq).to(dev)
+    for step in range(3, 6):
+        dec = synth.make_decode(cfg, step, device=dev)
+        oa = a_.decode_step(dec["q"], sd, dec["k_new"], dec["v_new"], update_scores=1)
+        ob = b_.decode_step(dec["q"], sd, dec["k_new"], dec["v_new"], update_scores=1, chain=0)
+        torch.cuda.synchronize()
+        assert torch.equal(oa, ob), f"chained step {step}: outputs differ"
+        for name in ("page_table", "tier_state"):
+            assert torch.equal(getattr(a_, name), getattr(b_, name)), f"chained step {step}: {name} differs"
+        assert torch.equal(a_.pool.free_list, b_.pool.free_list) and torch.equal(a_.pool.ptr, b_.pool.ptr)
+        assert torch.equal(a_.pool.pages, b_.pool.pages), f"chained step {step}: pages differ"
+        _say(f"  chained step {step}: identical (chain {a_.chain})")
+        sd = sd + 1
+    assert a_.chain == 3 and int(a_.pool.status.item()) == 0
+    check_device_pool(a_)
+    del p, a_, b_
     _free_gpu()
 
 
