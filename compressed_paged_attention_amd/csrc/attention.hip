@@ -505,6 +505,20 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
   bool spec = false;  // A already holds page wid (loads issued before the verdict)
   WaveCommit<D> wc;
   if constexpr (STEP) {
+    // with at most kWaveVerdictUnits units the committing wave takes the
+    // verdict alone, its loads (and the pool pointers) issued before
+    // anything else; the other waves' first page loads do not wait for them
+    const bool wv = sa.direct && sa.U <= kWaveVerdictUnits;
+    WaveVerdict vd;
+    int64_t h_start = 0, h_end = 0, p_live = 0;
+    if (sa.direct) {
+      h_start = sa.hdr[SH_START];
+      // chained: the pool's end pointer moves only between steps; its start
+      // is read live as a check (workgroup 0 may already have advanced it)
+      h_end = sa.chained ? (int64_t)sa.ptr[1] : sa.hdr[SH_END];
+      p_live = (int64_t)sa.ptr[0];
+    }
+    if (wv && wid == kCW) vd.load(sa.chained, sa.U, H, sa.nf, sa.cw, seq_len, state);
     const int32_t wu = sa.nf[u];
     const int32_t* R = sa.rec + u * kSRec;
     new_hi = R[S_NEWHI];
@@ -527,19 +541,28 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
       wc.begin(u, page_bytes, P, sa.k_new, sa.v_new, need, lo_src, id_hrow, id_lrow, id_src, pages,
                (uint32_t*)img_h, (uint32_t*)img_l);
     if (sa.direct) {
-      start = sa.hdr[SH_START];
-      int64_t end;
+      start = h_start;
+      const int64_t end = h_end;
       uint32_t fl;
       int total;
-      if (sa.chained) {
-        // the pool's end pointer moves only between steps; its start is
-        // read live as a check (workgroup 0 may already have advanced it)
-        end = (int64_t)sa.ptr[1];
-        const int64_t live = (int64_t)sa.ptr[0];
+      if (wv) {
+        if (wid == kCW) {
+          vd.eval(sa.chained, u, sa.U, fl, total, rank);
+          if (sa.chained && p_live != start && p_live != start + total) fl |= kStStale;
+          if (lane == 0) {
+            s_vd[0] = total;
+            s_vd[1] = rank;
+            s_vd[2] = (int)fl;
+          }
+        }
+        __syncthreads();
+        total = s_vd[0];
+        rank = s_vd[1];
+        fl = (uint32_t)s_vd[2];
+      } else if (sa.chained) {
         step_verdict_chain(u, sa.U, H, sa.cw, seq_len, state, s_vd, fl, total, rank);
-        if (live != start && live != start + total) fl |= kStStale;
+        if (p_live != start && p_live != start + total) fl |= kStStale;
       } else {
-        end = sa.hdr[SH_END];
         step_verdict(u, sa.U, sa.nf, s_vd, fl, total, rank);
       }
       const uint32_t st = fl ? fl : (total > end - start ? (uint32_t)kStExhausted : 0u);

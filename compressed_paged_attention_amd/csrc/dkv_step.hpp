@@ -605,6 +605,86 @@ __device__ inline void step_verdict_chain(int64_t u, int64_t U, int H, const int
   }
 }
 
+// One unit's inputs to a chained verdict: its chain words, batch length and
+// tier state (loads clamped into the arrays; chain_eval decides as
+// step_verdict_chain does).
+struct ChainIn {
+  int4 c0, c1;
+  int32_t N, snh, snl, sph, spl;
+};
+
+__device__ __forceinline__ ChainIn chain_load(int64_t x, int64_t U, int H, const int32_t* cw,
+                                              const int32_t* seq_len, const int32_t* state) {
+  const int64_t xc = x < U ? x : 0;
+  ChainIn c;
+  c.N = seq_len[(int)xc / H];
+  c.c0 = ((const int4*)cw)[2 * xc];
+  c.c1 = ((const int4*)cw)[2 * xc + 1];
+  const int32_t* s4 = state + 4 * xc;
+  c.snh = s4[0];
+  c.snl = s4[1];
+  c.sph = s4[2];
+  c.spl = s4[3];
+  return c;
+}
+
+// The unit's demand word (0 when out of range or inactive), kStStale into fl
+// when its chain words were not made for its length and tier state.
+__device__ __forceinline__ int32_t chain_eval(const ChainIn& c, bool in, uint32_t& fl) {
+  if (!in || c.N <= 0) return 0;
+  const int32_t w = c.c1.y;
+  const int need = w & 3;
+  const bool ok = c.c0.x == c.N && (c.snh == c.c0.y || c.snh == c.c0.y + c.c1.z) &&
+                  (c.snl == c.c0.z || c.snl == c.c0.z + c.c1.w) &&
+                  (c.sph == c.c0.w || c.sph == c.c0.w + (need == kTierHi)) &&
+                  (c.spl == c.c1.x || c.spl == c.c1.x + (need == kTierLo));
+  if (!ok) fl |= kStStale;
+  return w;
+}
+
+// The step verdict taken by one wave, for up to kWaveVerdictUnits units:
+// load issues every unit's inputs at once (first thing in the kernel, so
+// they do not queue behind the wave's page loads); eval reduces them with
+// ballots to the status flags, the total page demand and the number of units
+// before u that need a page.
+constexpr int kWaveVerdictUnits = 256;
+struct WaveVerdict {
+  static constexpr int NC = kWaveVerdictUnits / 64;
+  ChainIn c[NC];
+  int32_t w[NC];
+
+  __device__ __forceinline__ void load(bool chained, int64_t U, int H, const int32_t* nf, const int32_t* cw,
+                                       const int32_t* seq_len, const int32_t* state) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int k = 0; k < NC; k++) {
+      const int64_t x = lane + 64 * k;
+      if (chained) c[k] = chain_load(x, U, H, cw, seq_len, state);
+      else w[k] = nf[x < U ? x : 0];
+    }
+  }
+
+  __device__ __forceinline__ void eval(bool chained, int64_t u, int64_t U, uint32_t& flags, int& total,
+                                       int& rank) const {
+    const int lane = threadIdx.x & 63;
+    uint32_t fl = 0;
+    int tot = 0, rk = 0;
+#pragma unroll
+    for (int k = 0; k < NC; k++) {
+      const int64_t x = lane + 64 * k;
+      const bool in = x < U;
+      const int32_t wk = chained ? chain_eval(c[k], in, fl) : (in ? w[k] : 0);
+      fl |= (uint32_t)wk >> 8;
+      const bool need = (wk & 3) != 0;
+      tot += __popcll(__ballot(need));
+      rk += __popcll(__ballot(need && x < u));
+    }
+    flags = wave_reduce(fl, [](uint32_t a, uint32_t b) { return a | b; });
+    total = tot;
+    rank = rk;
+  }
+};
+
 // The commit of unit u by one wave, in two phases around the verdict.
 // begin (before it; loads only): the new token, the existing pages the step
 // writes (straight into their LDS images img_h, img_l: the high page of the

@@ -371,11 +371,12 @@ def test_fused_scores_large_units(dk, orc):
         seq = seq + 1
 
 
-@pytest.mark.parametrize("batch,H,update", [(32, 8, True), (32, 8, False), (3, 4, True)])
+@pytest.mark.parametrize("batch,H,update", [(32, 8, True), (32, 8, False), (64, 8, True), (3, 4, True)])
 def test_decode_step_entry(dk, orc, batch, H, update):
     """diffkv_decode_step (STEP then attention in one call): the fused kernel
-    when every unit is one split (32 x 8 units), the separate kernels when
-    not (3 x 4 units); lengths put steps on page boundaries."""
+    when every unit is one split (32 x 8 units: one wave takes the verdict;
+    64 x 8: every thread takes part), the separate kernels when not (3 x 4
+    units); lengths put steps on page boundaries."""
     from workloads import synth
     cfg = _medium_cfg("llama3_8b", num_kv_heads=H, batch=batch, max_seq_len=1300)
     assert (dk.diffkv_attn_splits(cfg, batch) == 1) == (batch * H >= 256)
@@ -485,7 +486,8 @@ def _twin_caches(dk, cfg, batch, lens, P, n):
     return st
 
 
-def test_plan_record_matches_scan(dk, orc):
+@pytest.mark.parametrize("batch", [32, 64])
+def test_plan_record_matches_scan(dk, orc, batch):
     """The next step's plan that the fused score update leaves behind gives
     exactly the state a fresh scan gives: three identical caches -- A steps
     chained (plans from the previous step's workspace slot, no plan kernel),
@@ -494,12 +496,13 @@ def test_plan_record_matches_scan(dk, orc):
     scan) -- stay byte-identical."""
     from tests.parity import plan_record_span, first_pages, masked
     from workloads import synth
-    cfg = _medium_cfg("llama3_8b", batch=32, max_seq_len=1500)
-    assert dk.diffkv_attn_splits(cfg, 32) == 1
+    cfg = _medium_cfg("llama3_8b", batch=batch, max_seq_len=1500)
+    assert dk.diffkv_attn_splits(cfg, batch) == 1
     g = torch.Generator().manual_seed(51)
-    lens = (torch.randint(5, 80, (32,), generator=g) * 16 - torch.randint(0, 3, (32,), generator=g)).to(torch.int64)
+    lens = (torch.randint(5, 80, (batch,), generator=g) * 16 -
+            torch.randint(0, 3, (batch,), generator=g)).to(torch.int64)
     P = int(sum(-(-int(n) // 16) for n in lens) * 8 * 1.2) + 64
-    st = _twin_caches(dk, cfg, 32, lens, P, 3)
+    st = _twin_caches(dk, cfg, batch, lens, P, 3)
     off, n = plan_record_span(cfg)
     seq = lens.to(torch.int32).to(dev)
     used = 0
