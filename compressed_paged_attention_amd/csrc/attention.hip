@@ -22,7 +22,7 @@
 //   sum_t p_t v^_t = sum_t (p_t s_v,t) c_t + (sum_t p_t z_v,t) * 1
 // so only codes enter the matrix units, as exact fp16 values (8-bit codes as
 // subnormals c 2^-24, 4- and 2-bit codes as 1 + c/2^b; the offsets are
-// removed in fp32 with sum(q) and sum(p s_v), see block_update).  P' is
+// removed in fp32 with sum(q) and sum(p s_v), see block_logits/block_pv).  P' is
 // split into an fp16 head and an fp16 tail (with 2G <= 16 the tail rides in
 // columns G..2G-1 of the same instruction) so the PV product keeps ~22 bits.
 // The S accumulator layout equals the
@@ -245,31 +245,20 @@ __device__ inline float rows_sum(float v) {
 // is free.  It is kept at least kHead above the largest logit seen, so
 // p <= 1/4 and the fp16 operand p s_v kv stays below 4 s_v (high, kv = 16)
 // or s_v (low, kv = 4): finite for the scale of any vector of fp16 values
-// (range <= 131008, so s_v <= 8734 high, 43670 low).  It moves (to the block
-// max + kHead + kLazy) only when a block breaks that bound, so the
+// (range <= 131008, so s_v <= 8734 high, 43670 low).  It moves (to the page's
+// column max + kHead + kLazy) only when a page breaks that bound, so the
 // accumulators are rescaled rarely.
 constexpr float kHead = 2.0f;
 constexpr float kLazy = 4.0f;
 
-// One 16-token block: logits (masked on a partial page), online-softmax
-// update, PV products.  `s` holds q.c * 2^-24 for tokens first..first+3 of the
-// page; `kmw`/`vmw` the metadata words of those tokens; `vpair(nb)` the fp16 V
-// operand of 16-dim block nb; `keep(x)` stores the block's logits.
+// One 16-token block in two halves.  block_logits: the block's logits
+// (masked on a partial page).  `s` holds q.c * 2^-24 for tokens
+// first..first+3 of the page; `kmw` the K metadata words of those tokens.
 // sq2 = sum(q) scale_log2 (per head).  K: s = q.c'' with c'' = c 2^-24 (high)
 // or 1 + c/16 (low), so q.c = s * 2^24 or 16 (s - sum q) and
 //   x = ks * s * kmul + (kz - kk ks) sq2,  kmul = 2^24 sl or 16 sl, kk = 0 or 16.
-// V: codes c'' = 1 + c/kv (kv = 16 high, 4 low) with operand p s_v kv, so
-//   sum p s_v kv c'' = sum p s_v c + sum p s_v kv, and the z term collects
-//   p (z_v - kv s_v).
-// PACK: column i + G carries the fp16 tail of head i's weights (one matrix
-// instruction per block instead of two); `tail` marks those lanes.
-template <int D, bool PACK, typename VOp, typename Keep>
-__device__ inline void block_update(const float4_t& s, const uint32_t* kmw, const uint32_t* vmw, int first,
-                                    int nval, bool partial, float sq2, float kmul, float kk, float kv,
-                                    bool tail, Softmax& sm,
-                                    float4_t* acc, VOp vpair, Keep keep) {
-  constexpr int NB = D / 16;
-  float x[4];
+__device__ inline void block_logits(const float4_t& s, const uint32_t* kmw, int first, int nval, bool partial,
+                                    float sq2, float kmul, float kk, float* x) {
 #pragma unroll
   for (int r = 0; r < 4; r++) {
     // log2e/sqrt(d) (s_k q.c + z_k sum(q)), with s holding q.c * 2^-24
@@ -282,9 +271,18 @@ __device__ inline void block_update(const float4_t& s, const uint32_t* kmw, cons
     for (int r = 0; r < 4; r++)
       if (first + r >= nval) x[r] = -INFINITY;
   }
-  keep(x);
-  const float pm = rows_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]))) + kHead;
-  if (__any(pm > sm.m)) {
+}
+
+// The reference check, once per page: lm is the lane's largest logit of the
+// page.  A column's maximum breaks the bound exactly when one of its lanes'
+// does, so the common case needs no cross-lane step; when some column breaks
+// it (rare), every column's reference moves to its maximum + kHead + kLazy
+// if that is higher, and the sums are rescaled.
+template <int D>
+__device__ inline void ref_check(float lm, Softmax& sm, float4_t* acc) {
+  constexpr int NB = D / 16;
+  if (__any(lm + kHead > sm.m)) {
+    const float pm = rows_max(lm) + kHead;
     const float mn = pm > sm.m ? pm + kLazy : sm.m;
     const float alpha = __builtin_amdgcn_exp2f(sm.m - mn);
     sm.lsum *= alpha;
@@ -293,6 +291,20 @@ __device__ inline void block_update(const float4_t& s, const uint32_t* kmw, cons
     for (int nb = 0; nb < NB; nb++) acc[nb] *= alpha;
     sm.m = mn;
   }
+}
+
+// block_pv: weights of the block's logits under the reference, their sums,
+// and the PV products.  `vmw` the V metadata words of the lane's tokens;
+// `vpair(nb)` the fp16 V operand of 16-dim block nb.
+// V: codes c'' = 1 + c/kv (kv = 16 high, 4 low) with operand p s_v kv, so
+//   sum p s_v kv c'' = sum p s_v c + sum p s_v kv, and the z term collects
+//   p (z_v - kv s_v).
+// PACK: column i + G carries the fp16 tail of head i's weights (one matrix
+// instruction per block instead of two); `tail` marks those lanes.
+template <int D, bool PACK, typename VOp>
+__device__ inline void block_pv(const float* x, const uint32_t* vmw, float kv, bool tail, Softmax& sm,
+                                float4_t* acc, VOp vpair) {
+  constexpr int NB = D / 16;
   _Float16 ph16[4], pl16[4];
 #pragma unroll
   for (int r = 0; r < 4; r++) {
@@ -322,9 +334,13 @@ __device__ inline void block_update(const float4_t& s, const uint32_t* kmw, cons
   }
 }
 
+__device__ inline float max4(const float* x) { return fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])); }
+
 // keep(mb, x): stores the 4 logits of 16-token block mb of the page.  The
 // q.c products use the K = 32 instruction: lane (i, qg) holds 8 dims of
-// token i per step, the same 8 dims of q as its Q operand.
+// token i per step, the same 8 dims of q as its Q operand.  One reference
+// check per page (a low page's two blocks share it, so nothing branches
+// between their weights).
 template <int D, bool PACK, typename Keep>
 __device__ inline void compute_page(const PageRegs<D>& R, bool hi, int nval, const half8_t* qop, float sq2,
                                     float sl, bool tail, int qg, Softmax& sm, float4_t* acc, Keep keep) {
@@ -337,19 +353,19 @@ __device__ inline void compute_page(const PageRegs<D>& R, bool hi, int nval, con
       s0 = mfma32(cat8(u8x4(R.k[2 * ks]), u8x4(R.k[2 * ks + 1])), qop[ks], s0);
       s1 = mfma32(cat8(u8x4(R.k[2 * ks + 2]), u8x4(R.k[2 * ks + 3])), qop[ks + 1], s1);
     }
-    block_update<D, PACK>(
-        s0 + s1, R.km, R.vm, 4 * qg, nval, nval < kHiTokens, sq2, kTwo24 * sl, 0.0f, 16.0f, tail, sm, acc,
-        [&](int nb) {
-          // block nb: pairs 2nb (tokens 0, 1) and 2nb + 1 (tokens 2, 3)
-          const uint32_t w = R.v[nb >> 1];
-          const int sft = 8 * (nb & 1);
-          return cat(nib2(w, sft), nib2(w, sft + 4));
-        },
-        [&](const float* x) { keep(0, x); });
+    float x[4];
+    block_logits(s0 + s1, R.km, 4 * qg, nval, nval < kHiTokens, sq2, kTwo24 * sl, 0.0f, x);
+    keep(0, x);
+    ref_check<D>(max4(x), sm, acc);
+    block_pv<D, PACK>(x, R.vm, 16.0f, tail, sm, acc, [&](int nb) {
+      // block nb: pairs 2nb (tokens 0, 1) and 2nb + 1 (tokens 2, 3)
+      const uint32_t w = R.v[nb >> 1];
+      const int sft = 8 * (nb & 1);
+      return cat(nib2(w, sft), nib2(w, sft + 4));
+    });
   } else {
-    // both blocks' q.c products first: the matrix unit works on the second
-    // while the first block's softmax runs
-    float4_t sb[2];
+    // both blocks' q.c products and logits first, then one reference check
+    float x[2][4];
 #pragma unroll
     for (int mb = 0; mb < 2; mb++) {
       float4_t s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = s0;
@@ -360,21 +376,19 @@ __device__ inline void compute_page(const PageRegs<D>& R, bool hi, int nval, con
         s0 = mfma32(cat8(cat(nib2(w0, 0), nib2(w0, 4)), cat(nib2(w0, 8), nib2(w0, 12))), qop[ks], s0);
         s1 = mfma32(cat8(cat(nib2(w1, 0), nib2(w1, 4)), cat(nib2(w1, 8), nib2(w1, 12))), qop[ks + 1], s1);
       }
-      sb[mb] = s0 + s1;
+      block_logits(s0 + s1, R.km + 4 * mb, 16 * mb + 4 * qg, nval, nval < 16 * (mb + 1), sq2, 16.0f * sl, 16.0f,
+                   x[mb]);
+      keep(mb, x[mb]);
     }
+    ref_check<D>(fmaxf(max4(x[0]), max4(x[1])), sm, acc);
 #pragma unroll
     for (int mb = 0; mb < 2; mb++) {
-      block_update<D, PACK>(
-          sb[mb], R.km + 4 * mb, R.vm + 4 * mb, 16 * mb + 4 * qg, nval, nval < 16 * (mb + 1), sq2, 16.0f * sl,
-          16.0f, 4.0f, tail,
-          sm, acc,
-          [&](int nb) {
-            // block (nb, mb): pairs P = 2M, 2M + 1 with M = 2nb + mb, in word P / 8
-            const int M = 2 * nb + mb;
-            const int P0 = 2 * M, P1 = 2 * M + 1;
-            return cat(crumb2(R.v[P0 >> 3], 2 * (P0 & 7)), crumb2(R.v[P1 >> 3], 2 * (P1 & 7)));
-          },
-          [&](const float* x) { keep(mb, x); });
+      block_pv<D, PACK>(x[mb], R.vm + 4 * mb, 4.0f, tail, sm, acc, [&](int nb) {
+        // block (nb, mb): pairs P = 2M, 2M + 1 with M = 2nb + mb, in word P / 8
+        const int M = 2 * nb + mb;
+        const int P0 = 2 * M, P1 = 2 * M + 1;
+        return cat(crumb2(R.v[P0 >> 3], 2 * (P0 & 7)), crumb2(R.v[P1 >> 3], 2 * (P1 & 7)));
+      });
     }
   }
 }
