@@ -489,7 +489,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
   // step leaves alone; it then takes a smaller share of those, and the
   // written pages from their images.
   constexpr int kCW = kWaves - 1;     // the committing wave
-  constexpr int kCommitPages = 4;     // its commit, in page computes (share)
+  constexpr int kCommitPages = 6;     // its commit, in page computes (share)
   static_assert(sizeof(buf) >= 2 * page_bytes_for(D), "two page images in the merge buffer");
   __shared__ int s_vd[3 * kWaves];
   __shared__ int32_t s_idt[2];        // ids of the written high and low pages

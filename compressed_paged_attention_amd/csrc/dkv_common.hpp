@@ -33,6 +33,7 @@ constexpr int kHiTokens = 16;
 constexpr int kLoTokens = 32;
 constexpr int kTierPrune = 0, kTierLo = 1, kTierHi = 2;
 constexpr uint32_t kStExhausted = 1u, kStOverflow = 2u, kStBadState = 4u, kStStale = 8u;
+constexpr uint32_t kStAll = 15u;  // every status bit
 
 struct Seg {
   int T, kbits, vbits, kc, km, vc, vm, sc, ps, bytes;

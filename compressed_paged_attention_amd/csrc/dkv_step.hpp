@@ -581,9 +581,14 @@ __device__ inline void step_verdict_chain(int64_t u, int64_t U, int H, const int
       const bool ok = c0.x == N && (snh == c0.y || snh == c0.y + c1.z) && (snl == c0.z || snl == c0.z + c1.w) &&
                       (sph == c0.w || sph == c0.w + (need == kTierHi)) &&
                       (spl == c1.x || spl == c1.x + (need == kTierLo));
-      if (!ok) fl |= kStStale;
+      // a unit that fails the check contributes only the stale bit (its
+      // words may be anything)
+      if (!ok) {
+        fl |= kStStale;
+        w = 0;
+      }
     }
-    fl |= (uint32_t)w >> 8;
+    fl |= ((uint32_t)w >> 8) & kStAll;
     const bool need = (w & 3) != 0;
     tot += __popcll(__ballot(need));
     rk += __popcll(__ballot(need && x < u));
@@ -628,8 +633,9 @@ __device__ __forceinline__ ChainIn chain_load(int64_t x, int64_t U, int H, const
   return c;
 }
 
-// The unit's demand word (0 when out of range or inactive), kStStale into fl
-// when its chain words were not made for its length and tier state.
+// The unit's demand word (0 when out of range or inactive); when its chain
+// words were not made for its length and tier state, kStStale into fl and 0
+// (the words may be anything).
 __device__ __forceinline__ int32_t chain_eval(const ChainIn& c, bool in, uint32_t& fl) {
   if (!in || c.N <= 0) return 0;
   const int32_t w = c.c1.y;
@@ -638,7 +644,10 @@ __device__ __forceinline__ int32_t chain_eval(const ChainIn& c, bool in, uint32_
                   (c.snl == c.c0.z || c.snl == c.c0.z + c.c1.w) &&
                   (c.sph == c.c0.w || c.sph == c.c0.w + (need == kTierHi)) &&
                   (c.spl == c.c1.x || c.spl == c.c1.x + (need == kTierLo));
-  if (!ok) fl |= kStStale;
+  if (!ok) {
+    fl |= kStStale;
+    return 0;
+  }
   return w;
 }
 
@@ -674,7 +683,7 @@ struct WaveVerdict {
       const int64_t x = lane + 64 * k;
       const bool in = x < U;
       const int32_t wk = chained ? chain_eval(c[k], in, fl) : (in ? w[k] : 0);
-      fl |= (uint32_t)wk >> 8;
+      fl |= ((uint32_t)wk >> 8) & kStAll;
       const bool need = (wk & 3) != 0;
       tot += __popcll(__ballot(need));
       rk += __popcll(__ballot(need && x < u));

@@ -78,7 +78,9 @@ enum {
   DIFFKV_ST_POOL_EXHAUSTED = 1u,
   DIFFKV_ST_TABLE_OVERFLOW = 2u,
   DIFFKV_ST_BAD_STATE = 4u,
-  DIFFKV_ST_STALE_CHAIN = 8u /* diffkv_decode_step: chain > 0 on a cache changed since its plans */
+  DIFFKV_ST_STALE_CHAIN = 8u /* diffkv_decode_step: chain > 0 on a cache changed since its plans,
+                                or one whose previous step left no plan (a state the plan
+                                kernel rejects, e.g. after aborted steps) */
 };
 enum {
   DIFFKV_PROMPT = 0,
