@@ -588,11 +588,11 @@ def test_chained_steps_match_plan_kernel(dk, orc, d, G, lo):
 
 
 def test_chain_broken_aborts_step(dk, orc):
-    """A chained call on a cache that does not match the plans (here: the
-    length not advanced) aborts the whole step with STALE_CHAIN: nothing is
-    committed and the attention runs on the unchanged cache, as an
-    attention call alone would; repeated with chain = 0 the step commits
-    and matches the plan kernel's."""
+    """A chained call on a cache that does not match the plans (the length
+    not advanced; then a workspace overwritten with arbitrary words) aborts
+    the whole step with STALE_CHAIN alone: nothing is committed and the
+    attention runs on the unchanged cache, as an attention call alone would;
+    repeated with chain = 0 the step commits and matches the plan kernel's."""
     from workloads import synth
     cfg = _medium_cfg("llama3_8b", batch=32, max_seq_len=1500)
     g = torch.Generator().manual_seed(52)
@@ -626,6 +626,24 @@ def test_chain_broken_aborts_step(dk, orc):
     torch.cuda.synchronize()
     assert int(a_.pool.status.item()) == 0
     _assert_caches_equal(a_, b_, P, "recovered step")
+    # a workspace overwritten with arbitrary words: the same abort, and no
+    # other status bit (the words' own flag bits are not taken)
+    seq = seq + 1
+    dec = synth.make_decode(cfg, 4, device=dev)
+    a_.ws_decode.fill_(0xFF)
+    assert a_.chain > 0
+    oa = a_.decode_step(dec["q"], seq, dec["k_new"], dec["v_new"], update_scores=1)
+    ob = b_.decode_attn(dec["q"], seq, update_scores=1)
+    torch.cuda.synchronize()
+    assert int(a_.pool.status.item()) == dk.ST_STALE_CHAIN, hex(int(a_.pool.status.item()))
+    assert torch.equal(oa, ob), "overwritten workspace: attention differs"
+    _assert_caches_equal(a_, b_, P, "overwritten workspace")
+    a_.pool.status.zero_()
+    for s_ in (a_, b_):
+        s_.decode_step(dec["q"], seq, dec["k_new"], dec["v_new"], update_scores=1, chain=0)
+    torch.cuda.synchronize()
+    assert int(a_.pool.status.item()) == 0
+    _assert_caches_equal(a_, b_, P, "recovered after the overwrite")
 
 
 def test_deterministic_replay(dk, orc):
