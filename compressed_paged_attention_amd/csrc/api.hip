@@ -125,6 +125,8 @@ int diffkv_compact(const diffkv_config* cfg, const diffkv_pool* pool, int32_t mo
     case DIFFKV_PROMPT:
       if (batch > 0 && !cu_seqlens) return DIFFKV_E_INVALID;
       if (total_tokens > 0 && (!k || !v || !scores || !tiers)) return DIFFKV_E_INVALID;
+      // token rows are read with 16-byte loads
+      if (((uintptr_t)k | (uintptr_t)v) & 15u) return DIFFKV_E_INVALID;
       need = prompt_workspace(c, batch, total_tokens);
       if (!ws_ok(workspace) || workspace_bytes < need) return DIFFKV_E_WORKSPACE;
       return rc(launch_prompt(c, p, batch, total_tokens, cu_seqlens, k, v, scores, tiers, page_table, tier_state,

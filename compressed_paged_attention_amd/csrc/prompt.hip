@@ -40,6 +40,7 @@ struct PromptWs {
   int32_t* chunks;
   int32_t* pos;
   int32_t* freed;
+  int32_t* pmap;  // [U*L] owning unit of each page of the call, in page order
 };
 
 static inline int num_chunks(const Cfg& c) { return (c.S_max + kChunk - 1) / kChunk; }
@@ -59,6 +60,8 @@ static PromptWs carve(const Cfg& c, int batch, int64_t total, void* ws, size_t* 
   w.pos = (int32_t*)(b + off);
   off = align_up(off + (size_t)c.H * total * sizeof(int32_t), 256);
   w.freed = (int32_t*)(b + off);
+  off = align_up(off + (size_t)U * c.L * sizeof(int32_t), 256);
+  w.pmap = (int32_t*)(b + off);
   off = align_up(off + (size_t)U * c.L * sizeof(int32_t), 256);
   if (bytes) *bytes = off;
   return w;
@@ -281,18 +284,20 @@ __global__ __launch_bounds__(256) void prompt_scatter_kernel(int H, int L, int C
 }
 
 // Frees appended at the old reclamation pointer; extra pages taken after
-// them.  A list slot read here (logical index below the old end) is never
+// them; the page map (owner of each page the pack kernel writes).  A list slot read here (logical index below the old end) is never
 // one of the slots written here: the written logical indices sit exactly P
 // above indices this call already consumed.
 __global__ __launch_bounds__(256) void prompt_list_kernel(int L, int64_t P, const int64_t* __restrict__ hdr,
                                                           const int64_t* __restrict__ rec,
                                                           const int32_t* __restrict__ freed,
-                                                          int32_t* list, int32_t* __restrict__ table) {
+                                                          int32_t* list, int32_t* __restrict__ table,
+                                                          int32_t* __restrict__ pmap) {
   if (!hdr[H_COMMIT]) return;
   const int64_t u = blockIdx.x;
   const int64_t* R = rec + u * kRec;
   if (R[R_N] <= 0) return;
   const int64_t k = R[R_K], hp = R[R_HP], lp = R[R_LP];
+  for (int64_t i = threadIdx.x; i < hp + lp; i += blockDim.x) pmap[R[R_POFF] + i] = (int32_t)u;
   const int64_t f = k > hp + lp ? k - hp - lp : 0;
   const uint64_t end0 = (uint64_t)hdr[H_END];
   for (int64_t i = threadIdx.x; i < f; i += blockDim.x)
@@ -304,10 +309,194 @@ __global__ __launch_bounds__(256) void prompt_list_kernel(int L, int64_t P, cons
   }
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // K/V rows: 16-byte non-temporal loads
+
+// Codes of the per-vector codec without a division: t = fl(x - z) * (1/s)
+// with the hardware reciprocal is within 2^-14 of the quotient for every
+// quotient up to 2^9 in magnitude, so rounding t gives the code unless t
+// lies within 2^-11 of a half-integer; then the caller redoes the codes with
+// the IEEE division.  Quotients beyond the code range clamp the same either
+// way; a zero scale comes in as rs = 0 and gives code 0.
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+
+__device__ inline float lo_h(uint32_t w) { return h2f((uint16_t)(w & 0xFFFFu)); }
+__device__ inline float hi_h(uint32_t w) { return h2f((uint16_t)(w >> 16)); }
+
+// min and max of the 8 fp16 values in 4 words (pairwise in fp16: exact)
+// (the words go through scalars: a bit cast of a vector element expression
+// was measured to read element 0 with this compiler)
+__device__ inline void minmax8(const u32x4& w, float& mn, float& mx) {
+  const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
+  const h2v a = __builtin_bit_cast(h2v, w0), b = __builtin_bit_cast(h2v, w1);
+  const h2v c = __builtin_bit_cast(h2v, w2), d = __builtin_bit_cast(h2v, w3);
+  const h2v m0 = __builtin_elementwise_min(__builtin_elementwise_min(a, b), __builtin_elementwise_min(c, d));
+  const h2v m1 = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
+  mn = fminf((float)m0[0], (float)m0[1]);
+  mx = fmaxf((float)m1[0], (float)m1[1]);
+}
+
+// The 8 codes of one lane's dims of a token: element e of `w` (dim 8a+e).
+// Returns the codes packed one per byte (code e in byte e of the pair).
+template <int BITS>
+__device__ inline uint2 codes8(const u32x4& w, float s, float z) {
+  constexpr float qmax = (float)((1 << BITS) - 1);
+  const float rs = s == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(s);
+  bool near = false;
+  uint32_t out[2] = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 8; e++) {
+    const float x = (e & 1) ? hi_h(w[e >> 1]) : lo_h(w[e >> 1]);
+    const float t = __fmul_rn(__fsub_rn(x, z), rs);
+    const float rt = __builtin_rintf(t);
+    near |= !(__builtin_fabsf(t - rt) < 0.5f - 0x1p-11f);
+    // clamped integer value to byte e mod 4 (an exact conversion)
+    out[e >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_amdgcn_fmed3f(rt, 0.0f, qmax), e & 3, out[e >> 2]);
+  }
+  if (near) {
+    out[0] = out[1] = 0u;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      const float x = (e & 1) ? hi_h(w[e >> 1]) : lo_h(w[e >> 1]);
+      out[e >> 2] |= codec_code(x, s, z, BITS) << (8 * (e & 3));
+    }
+  }
+  return make_uint2(out[0], out[1]);
+}
+
+// Page packing ("Memory management": a unified page holds its tokens'
+// quantized K and V with their metadata, score and position).  One wave per
+// page, no LDS: lane (g, a), a = lane mod d/8, holds dims 8a..8a+7 of the
+// tokens 4g..4g+3 (and, in a low page, 16+4g..16+4g+3): one 16-byte load
+// per token row for K and V.  Per token the min/max come from a reduction
+// over the d/8 lanes of the group; K codes leave as whole words, V codes are
+// assembled into the lane-chunk layout: a V word holds the 4 (low: 8) tokens
+// of a group at one in-chunk dim and two 16-dim blocks, the second block
+// from lane a^2.  Lanes a = 0..3 store the group's metadata, score and
+// position words.  Slots past the tier's count are written as zeros, as is
+// the page's tail after the last segment.
+template <int D, bool HI>
+__device__ inline void pack_page(uint8_t* pg, int lane, int valid, const int32_t* pl, int64_t slot0, int64_t N,
+                                 int64_t b0, int H, int h, const uint16_t* __restrict__ k,
+                                 const uint16_t* __restrict__ v, const float* __restrict__ sc_in) {
+  constexpr int NA = D / 8;             // lanes per token group
+  constexpr int NT = HI ? 1 : 2;        // token quads per lane
+  constexpr Seg sg = tier_seg(D, HI);
+  const int a = lane % NA, g = lane / NA;
+  const bool act = g < 4;
+  // Loads in three batches, none behind a branch (the memory counters wait
+  // in order, so a load issued after another cannot be waited for alone):
+  // positions, then K/V rows and scores.  Slots past the tier's count read
+  // the page's first slot and are masked to zero afterwards.
+  int32_t pos[NT][4];
+#pragma unroll
+  for (int th = 0; th < NT; th++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int t = 16 * th + 4 * g + r;
+      const int64_t slot = slot0 + ((act && t < valid) ? t : 0);
+      pos[th][r] = HI ? pl[slot] : pl[N - 1 - slot];
+    }
+  u32x4 kr[NT][4], vr[NT][4];
+  float mean[NT][4];
+#pragma unroll
+  for (int th = 0; th < NT; th++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int64_t row = ((b0 + pos[th][r]) * H + h) * D + 8 * a;
+      kr[th][r] = __builtin_nontemporal_load((const u32x4*)(k + row));
+      vr[th][r] = __builtin_nontemporal_load((const u32x4*)(v + row));
+      mean[th][r] = sc_in[b0 + pos[th][r]];
+    }
+#pragma unroll
+  for (int th = 0; th < NT; th++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int t = 16 * th + 4 * g + r;
+      const bool ok = act && t < valid;
+      if (!ok) {
+        kr[th][r] = u32x4{0u, 0u, 0u, 0u};
+        vr[th][r] = u32x4{0u, 0u, 0u, 0u};
+      }
+      // score (mean * (N - 1 - pos), a running sum over the tokens after
+      // pos) and position words, by lanes a == 2 and a == 3
+      if (act && (a == 2 || a == 3)) {
+        uint32_t wd = 0u;
+        if (ok)
+          wd = a == 3 ? (uint32_t)pos[th][r] : __float_as_uint(__fmul_rn(mean[th][r], (float)(N - 1 - pos[th][r])));
+        *(uint32_t*)(pg + (a == 2 ? sg.sc : sg.ps) + 4 * t) = wd;
+      }
+    }
+  const int nbp = (a >> 1) & 1;  // parity of the lane's 16-dim block
+  uint32_t vw[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};  // V word per in-chunk dim 8(a&1)+e
+  uint8_t* kc = pg + sg.kc;
+  auto fmn = [](float p, float q) { return fminf(p, q); };
+  auto fmx = [](float p, float q) { return fmaxf(p, q); };
+#pragma unroll
+  for (int th = 0; th < NT; th++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int t = 16 * th + 4 * g + r;
+      float kmn, kmx, vmn, vmx;
+      minmax8(kr[th][r], kmn, kmx);
+      minmax8(vr[th][r], vmn, vmx);
+      kmn = group_reduce<NA>(kmn, fmn);
+      kmx = group_reduce<NA>(kmx, fmx);
+      vmn = group_reduce<NA>(vmn, fmn);
+      vmx = group_reduce<NA>(vmx, fmx);
+      uint16_t ks16, kz16, vs16, vz16;
+      float ks, kz, vs, vz;
+      codec_params(kmn, kmx, sg.kbits, ks16, kz16, ks, kz);
+      codec_params(vmn, vmx, sg.vbits, vs16, vz16, vs, vz);
+      const uint2 ck = codes8<sg.kbits>(kr[th][r], ks, kz);
+      const uint2 cv = codes8<sg.vbits>(vr[th][r], vs, vz);
+      if (act) {
+        if (HI) {
+          // 8-bit K, token-major: bytes t*D + 8a .. +7
+          *(uint2*)(kc + t * D + 8 * a) = ck;
+        } else {
+          // 4-bit K: dim 8a+e in nibble e/2 + 4(e&1) of word a; bytes of
+          // ck hold dims (0,1,2,3) and (4,5,6,7)
+          const uint32_t ev = (ck.x & 0x00FF00FFu) | ((ck.y & 0x00FF00FFu) << 8);  // dims 0,4,2,6
+          const uint32_t od = ((ck.x >> 8) & 0x00FF00FFu) | (((ck.y >> 8) & 0x00FF00FFu) << 8);  // 1,5,3,7
+          // nibbles: dim e -> e/2 + 4(e&1): 0->0, 2->1, 4->2, 6->3, 1->4, 3->5, 5->6, 7->7
+          const uint32_t lo4 = (ev & 0xFu) | ((ev >> 12) & 0xF0u) | ((ev >> 0) & 0xF00u) | ((ev >> 12) & 0xF000u);
+          const uint32_t hi4 = (od & 0xFu) | ((od >> 12) & 0xF0u) | ((od >> 0) & 0xF00u) | ((od >> 12) & 0xF000u);
+          *(uint32_t*)(kc + t * (D / 2) + 4 * a) = lo4 | (hi4 << 16);
+        }
+        if (a < 2) *(uint32_t*)(pg + (a == 0 ? sg.km : sg.vm) + 4 * t) =
+            a == 0 ? ((uint32_t)ks16 | ((uint32_t)kz16 << 16)) : ((uint32_t)vs16 | ((uint32_t)vz16 << 16));
+      }
+      // V field of (token t, dim 8a+e): bit 8 nbp + 4(r>>1) + 16(r&1)
+      // (high), 8 nbp + 4 th + 2(r>>1) + 16(r&1) (low)
+      const int sh = HI ? 8 * nbp + 4 * (r >> 1) + 16 * (r & 1) : 8 * nbp + 4 * th + 2 * (r >> 1) + 16 * (r & 1);
+#pragma unroll
+      for (int e = 0; e < 8; e++) vw[e] |= ((e < 4 ? cv.x : cv.y) >> (8 * (e & 3)) & 0xFFu) << sh;
+    }
+  // the other 16-dim block of each word comes from lane a^2
+#pragma unroll
+  for (int e = 0; e < 8; e++) vw[e] |= lane_xchg<1>(vw[e]);
+  if (act) {
+    // lane keeps in-chunk dims 8(a&1) + 4 nbp .. +3: chunk L = i + 16 g, word a>>2
+    uint8_t* vc = pg + sg.vc;
+#pragma unroll
+    for (int e4 = 0; e4 < 4; e4++) {
+      const int L = 8 * (a & 1) + 4 * nbp + e4 + 16 * g;
+      *(uint32_t*)(vc + L * (D / 8) + 4 * (a >> 2)) = nbp ? vw[4 + e4] : vw[e4];
+    }
+  }
+  // bytes after the last segment (high pages are shorter than the page)
+  for (int off = sg.bytes + 16 * lane; off < page_bytes_for(D); off += 16 * 64)
+    *(uint4*)(pg + off) = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Persistent: wave w of the grid packs pages item = w, w + #waves, ... of the
+// call's TP pages (items in unit order, each unit's high pages then low
+// pages); the owning unit comes from the page map the list kernel wrote.
 template <int D>
-__global__ __launch_bounds__(256) void prompt_pack_kernel(int H, int L, int64_t total, int64_t U, int64_t P,
-                                                          int page_bytes, const int64_t* __restrict__ hdr,
+__global__ __launch_bounds__(256) void prompt_pack_kernel(int H, int L, int64_t total, int64_t P, int page_bytes,
+                                                          const int64_t* __restrict__ hdr,
                                                           const int64_t* __restrict__ rec,
+                                                          const int32_t* __restrict__ pmap,
                                                           const int32_t* __restrict__ pos_list,
                                                           const int32_t* __restrict__ table,
                                                           const uint16_t* __restrict__ k,
@@ -316,17 +505,11 @@ __global__ __launch_bounds__(256) void prompt_pack_kernel(int H, int L, int64_t 
                                                           uint8_t* __restrict__ pages, uint32_t* status) {
   if (!hdr[H_COMMIT]) return;
   const int64_t TP = hdr[H_PAGES];
-  __shared__ uint32_t img[page_bytes_for(D) / 4];
-  const int tid = threadIdx.x;
-  for (int64_t item = blockIdx.x; item < TP; item += gridDim.x) {
-    // the unit owning this page: the largest u with Poff[u] <= item
-    int64_t lo = 0, hi = U - 1;
-    while (lo < hi) {
-      const int64_t mid = (lo + hi + 1) >> 1;
-      if (rec[mid * kRec + R_POFF] <= item) lo = mid;
-      else hi = mid - 1;
-    }
-    const int64_t u = lo;
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = (int64_t)gridDim.x * (blockDim.x >> 6);
+  for (int64_t item = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+       item < TP; item += nw) {
+    const int64_t u = __builtin_amdgcn_readfirstlane(pmap[item]);
     const int64_t* R = rec + u * kRec;
     const int h = (int)(u % H);
     const int64_t j = item - R[R_POFF];
@@ -338,64 +521,15 @@ __global__ __launch_bounds__(256) void prompt_pack_kernel(int H, int L, int64_t 
     const int64_t slot0 = jt * T;
     const int valid = (int)(n_tier - slot0 < T ? n_tier - slot0 : T);
     const int64_t N = R[R_N], b0 = R[R_BASE];
-    for (int w = tid; w < page_bytes / 4; w += blockDim.x) img[w] = 0u;
-    __syncthreads();
-    const Seg sg = tier_seg(D, is_hi);
-    const int TPT = 256 / T;          // threads per token
-    const int DPT = D / TPT;          // dims per thread
-    const int t = tid / TPT, sub = tid % TPT;
-    if (t < valid) {
-      const int64_t slot = slot0 + t;
-      const int32_t* pl = pos_list + (int64_t)h * total + b0;
-      const int64_t pos = is_hi ? pl[slot] : pl[N - 1 - slot];
-      const int64_t rowi = ((b0 + pos) * H + h) * D + (int64_t)sub * DPT;
-      float xk[16], xv[16];
-      float kmn = INFINITY, kmx = -INFINITY, vmn = INFINITY, vmx = -INFINITY;
-      for (int i = 0; i < DPT; i++) {
-        xk[i] = h2f(k[rowi + i]);
-        xv[i] = h2f(v[rowi + i]);
-        kmn = fminf(kmn, xk[i]);
-        kmx = fmaxf(kmx, xk[i]);
-        vmn = fminf(vmn, xv[i]);
-        vmx = fmaxf(vmx, xv[i]);
-      }
-      auto fmn = [](float a, float b) { return fminf(a, b); };
-      auto fmx = [](float a, float b) { return fmaxf(a, b); };
-      kmn = group_reduce(kmn, TPT, fmn);
-      kmx = group_reduce(kmx, TPT, fmx);
-      vmn = group_reduce(vmn, TPT, fmn);
-      vmx = group_reduce(vmx, TPT, fmx);
-      uint16_t ks16, kz16, vs16, vz16;
-      float ks, kz, vs, vz;
-      codec_params(kmn, kmx, sg.kbits, ks16, kz16, ks, kz);
-      codec_params(vmn, vmx, sg.vbits, vs16, vz16, vs, vz);
-      for (int i = 0; i < DPT; i++) {
-        const int jd = sub * DPT + i;
-        int byte, shift;
-        k_field(D, is_hi, t, jd, byte, shift);
-        const uint32_t kc = codec_code(xk[i], ks, kz, sg.kbits);
-        atomicOr(&img[byte >> 2], kc << (8 * (byte & 3) + shift));
-        v_field(D, is_hi, t, jd, byte, shift);
-        const uint32_t vc = codec_code(xv[i], vs, vz, sg.vbits);
-        atomicOr(&img[byte >> 2], vc << (8 * (byte & 3) + shift));
-      }
-      if (sub == 0) {
-        img[(sg.km >> 2) + t] = (uint32_t)ks16 | ((uint32_t)kz16 << 16);
-        img[(sg.vm >> 2) + t] = (uint32_t)vs16 | ((uint32_t)vz16 << 16);
-        const float mean = scores[(int64_t)h * total + b0 + pos];
-        img[(sg.sc >> 2) + t] = __float_as_uint(__fmul_rn(mean, (float)(N - 1 - pos)));
-        img[(sg.ps >> 2) + t] = (uint32_t)pos;
-      }
+    if (id < 0 || id >= P) {
+      if (lane == 0) atomicOr(status, kStBadState);
+      continue;
     }
-    __syncthreads();
-    if (id >= 0 && id < P) {
-      uint4* dst = (uint4*)(pages + (int64_t)id * page_bytes);
-      const uint4* src = (const uint4*)img;
-      for (int c = tid; c < page_bytes / 16; c += blockDim.x) dst[c] = src[c];
-    } else if (tid == 0) {
-      atomicOr(status, kStBadState);
-    }
-    __syncthreads();
+    uint8_t* pg = pages + (int64_t)id * page_bytes;
+    const int32_t* pl = pos_list + (int64_t)h * total + b0;
+    const float* sc = scores + (int64_t)h * total;
+    if (is_hi) pack_page<D, true>(pg, lane, valid, pl, slot0, N, b0, H, h, k, v, sc);
+    else pack_page<D, false>(pg, lane, valid, pl, slot0, N, b0, H, h, k, v, sc);
   }
 }
 
@@ -414,15 +548,16 @@ hipError_t launch_prompt(const Cfg& c, const Pool& p, int batch, int64_t total, 
                                                                    w.rec, w.chunks, p.list, w.pos,
                                                                    w.freed, table, state);
   prompt_list_kernel<<<dim3((unsigned)U), dim3(256), 0, s>>>(c.L, p.P, w.hdr, w.rec, w.freed, p.list,
-                                                             table);
-  int64_t grid = U * c.L;
+                                                             table, w.pmap);
+  // four waves (pages in flight) per workgroup
+  int64_t grid = (U * c.L + 3) / 4;
   if (grid > 4096) grid = 4096;
   if (c.d == 128)
     prompt_pack_kernel<128><<<dim3((unsigned)grid), dim3(256), 0, s>>>(
-        c.H, c.L, total, U, p.P, p.page_bytes, w.hdr, w.rec, w.pos, table, k, v, scores, p.pages, p.status);
+        c.H, c.L, total, p.P, p.page_bytes, w.hdr, w.rec, w.pmap, w.pos, table, k, v, scores, p.pages, p.status);
   else
     prompt_pack_kernel<64><<<dim3((unsigned)grid), dim3(256), 0, s>>>(
-        c.H, c.L, total, U, p.P, p.page_bytes, w.hdr, w.rec, w.pos, table, k, v, scores, p.pages, p.status);
+        c.H, c.L, total, p.P, p.page_bytes, w.hdr, w.rec, w.pmap, w.pos, table, k, v, scores, p.pages, p.status);
   return hipGetLastError();
 }
 

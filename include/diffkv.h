@@ -143,7 +143,7 @@ int diffkv_classify(const diffkv_config* cfg, int32_t batch, int64_t total_token
  *
  * mode DIFFKV_PROMPT: admits requests with N_r > 0 (others untouched; their
  *   rows must be empty).  Uses cu_seqlens, k/v fp16 [cu[batch], H, d]
- *   (token-major), scores (mean per token, [H, total]) and tiers from
+ *   (token-major; both 16-byte aligned, else DIFFKV_E_INVALID), scores (mean per token, [H, total]) and tiers from
  *   diffkv_classify.  Per unit: a conservative block of ceil(N/16) pages
  *   from the allocation pointer (units in order); high pages take the block
  *   from the left, low pages from the right; the middle is reclaimed at the
