@@ -312,101 +312,119 @@ __global__ __launch_bounds__(256) void prompt_list_kernel(int L, int64_t P, cons
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // K/V rows: 16-byte non-temporal loads
 
 // Codes of the per-vector codec without a division: t = fl(x - z) * (1/s)
-// with the hardware reciprocal is within 2^-14 of the quotient for every
-// quotient up to 2^9 in magnitude, so rounding t gives the code unless t
-// lies within 2^-11 of a half-integer; then the caller redoes the codes with
-// the IEEE division.  Quotients beyond the code range clamp the same either
-// way; a zero scale comes in as rs = 0 and gives code 0.
+// with the hardware reciprocal (1 ulp; 2 ulp still suffice) is within 8e-5
+// of the quotient q wherever |q| <= 257, so rounding t gives the code unless
+// t lies within 2^-13 of a half-integer; then the codes are redone with the
+// IEEE division.  Quotients beyond the code range clamp the same either
+// way; a zero scale comes in as rs = 0 and gives code 0.  (K and V are
+// finite fp16 values.)
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 
 __device__ inline float lo_h(uint32_t w) { return h2f((uint16_t)(w & 0xFFFFu)); }
 __device__ inline float hi_h(uint32_t w) { return h2f((uint16_t)(w >> 16)); }
 
-// min and max of the 8 fp16 values in 4 words (pairwise in fp16: exact)
-// (the words go through scalars: a bit cast of a vector element expression
-// was measured to read element 0 with this compiler)
-__device__ inline void minmax8(const u32x4& w, float& mn, float& mx) {
-  const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
-  const h2v a = __builtin_bit_cast(h2v, w0), b = __builtin_bit_cast(h2v, w1);
-  const h2v c = __builtin_bit_cast(h2v, w2), d = __builtin_bit_cast(h2v, w3);
-  const h2v m0 = __builtin_elementwise_min(__builtin_elementwise_min(a, b), __builtin_elementwise_min(c, d));
-  const h2v m1 = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
-  mn = fminf((float)m0[0], (float)m0[1]);
-  mx = fmaxf((float)m1[0], (float)m1[1]);
+// fp16 pairs: elementwise min / max (exact; the 3-input packed forms)
+__device__ inline uint32_t pmin(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_minimum(__builtin_bit_cast(h2v, a), __builtin_bit_cast(h2v, b)));
+}
+__device__ inline uint32_t pmax(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_maximum(__builtin_bit_cast(h2v, a), __builtin_bit_cast(h2v, b)));
 }
 
-// The 8 codes of one lane's dims of a token: element e of `w` (dim 8a+e).
-// Returns the codes packed one per byte (code e in byte e of the pair).
+// fl(x - z) for the fp16 half SEL of w: one mixed-precision fma (x * 1 - z,
+// a single rounding, the same value as converting x and subtracting)
+template <int SEL>
+__device__ inline float sub_h(uint32_t w, float z) {
+  float r;
+  if constexpr (SEL == 0)
+    asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(z));
+  else
+    asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(z));
+  return r;
+}
+
+// The 8 codes of a lane's dims 8a..8a+7 of one token (element e in half
+// e&1 of word e>>1), as integers.
 template <int BITS>
-__device__ inline uint2 codes8(const u32x4& w, float s, float z) {
+__device__ inline void codes8(const uint32_t* w, float s, float z, uint32_t* c) {
   constexpr float qmax = (float)((1 << BITS) - 1);
   const float rs = s == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(s);
-  bool near = false;
-  uint32_t out[2] = {0u, 0u};
+  float dmax = 0.0f;
 #pragma unroll
   for (int e = 0; e < 8; e++) {
-    const float x = (e & 1) ? hi_h(w[e >> 1]) : lo_h(w[e >> 1]);
-    const float t = __fmul_rn(__fsub_rn(x, z), rs);
+    const float d = (e & 1) ? sub_h<1>(w[e >> 1], z) : sub_h<0>(w[e >> 1], z);
+    const float t = __fmul_rn(d, rs);
     const float rt = __builtin_rintf(t);
-    near |= !(__builtin_fabsf(t - rt) < 0.5f - 0x1p-11f);
-    // clamped integer value to byte e mod 4 (an exact conversion)
-    out[e >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_amdgcn_fmed3f(rt, 0.0f, qmax), e & 3, out[e >> 2]);
+    dmax = fmaxf(dmax, __builtin_fabsf(t - rt));
+    c[e] = (uint32_t)__builtin_amdgcn_fmed3f(rt, 0.0f, qmax);
   }
-  if (near) {
-    out[0] = out[1] = 0u;
+  if (!(dmax < 0.5f - 0x1p-13f)) {
 #pragma unroll
-    for (int e = 0; e < 8; e++) {
-      const float x = (e & 1) ? hi_h(w[e >> 1]) : lo_h(w[e >> 1]);
-      out[e >> 2] |= codec_code(x, s, z, BITS) << (8 * (e & 3));
-    }
+    for (int e = 0; e < 8; e++) c[e] = codec_code((e & 1) ? hi_h(w[e >> 1]) : lo_h(w[e >> 1]), s, z, BITS);
   }
-  return make_uint2(out[0], out[1]);
+}
+
+// Where a page comes from (wave-uniform).
+struct PackMeta {
+  int32_t id;
+  int hi, valid, h;
+  int64_t slot0, N, b0;
+};
+
+__device__ inline PackMeta pack_meta(int64_t item, int H, int L, const int64_t* __restrict__ rec,
+                                     const int32_t* __restrict__ pmap, const int32_t* __restrict__ table) {
+  PackMeta m;
+  const int u = __builtin_amdgcn_readfirstlane(pmap[item]);
+  const int64_t* R = rec + (int64_t)u * kRec;
+  m.h = u % H;
+  const int64_t j = item - R[R_POFF], hp = R[R_HP];
+  m.hi = j < hp;
+  const int64_t jt = m.hi ? j : j - hp;
+  m.id = table[(int64_t)u * L + (m.hi ? jt : L - 1 - jt)];
+  const int T = m.hi ? kHiTokens : kLoTokens;
+  const int64_t n_tier = m.hi ? R[R_NH] : R[R_NL];
+  m.slot0 = jt * T;
+  m.valid = (int)(n_tier - m.slot0 < T ? n_tier - m.slot0 : T);
+  m.N = R[R_N];
+  m.b0 = R[R_BASE];
+  return m;
+}
+
+// Positions of the lane's tokens 16 th + 4 g + r (high pages: th = 0 only);
+// slots past the tier's count read the page's first slot.
+__device__ inline void pack_pos(const PackMeta& m, int g, bool act, const int32_t* __restrict__ pos_list,
+                                int64_t total, int32_t (&pos)[2][4]) {
+  const int32_t* pl = pos_list + (int64_t)m.h * total + m.b0;
+#pragma unroll
+  for (int th = 0; th < 2; th++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int t = 16 * th + 4 * g + r;
+      const int64_t slot = m.slot0 + ((act && t < m.valid) ? t : 0);
+      pos[th][r] = m.hi ? pl[slot] : pl[m.N - 1 - slot];
+    }
 }
 
 // Page packing ("Memory management": a unified page holds its tokens'
 // quantized K and V with their metadata, score and position).  One wave per
 // page, no LDS: lane (g, a), a = lane mod d/8, holds dims 8a..8a+7 of the
-// tokens 4g..4g+3 (and, in a low page, 16+4g..16+4g+3): one 16-byte load
-// per token row for K and V.  Per token the min/max come from a reduction
-// over the d/8 lanes of the group; K codes leave as whole words, V codes are
-// assembled into the lane-chunk layout: a V word holds the 4 (low: 8) tokens
-// of a group at one in-chunk dim and two 16-dim blocks, the second block
-// from lane a^2.  Lanes a = 0..3 store the group's metadata, score and
-// position words.  Slots past the tier's count are written as zeros, as is
-// the page's tail after the last segment.
+// tokens 4g..4g+3 (and, in a low page, 16+4g..16+4g+3), one 16-byte row
+// load each for K and V.  Per token the min/max come from a reduction over
+// the d/8 lanes of the group (fp16 pairs: K and V minima in one word, maxima
+// in another); K codes leave as whole words, V codes are assembled into the
+// lane-chunk layout: a V word holds the 4 (low: 8) tokens of a group at one
+// in-chunk dim and two 16-dim blocks, the second block from lane a^2.  Lanes
+// a = 0..3 store the metadata, score and position words.  Slots past the
+// tier's count are written as zeros, as is the page's tail after the last
+// segment.
 template <int D, bool HI>
-__device__ inline void pack_page(uint8_t* pg, int lane, int valid, const int32_t* pl, int64_t slot0, int64_t N,
-                                 int64_t b0, int H, int h, const uint16_t* __restrict__ k,
-                                 const uint16_t* __restrict__ v, const float* __restrict__ sc_in) {
+__device__ inline void pack_compute(uint8_t* pg, int lane, int valid, int64_t N, const int32_t (&pos)[2][4],
+                                    u32x4 (&kr)[2][4], u32x4 (&vr)[2][4], const float (&mean)[2][4]) {
   constexpr int NA = D / 8;             // lanes per token group
   constexpr int NT = HI ? 1 : 2;        // token quads per lane
   constexpr Seg sg = tier_seg(D, HI);
   const int a = lane % NA, g = lane / NA;
   const bool act = g < 4;
-  // Loads in three batches, none behind a branch (the memory counters wait
-  // in order, so a load issued after another cannot be waited for alone):
-  // positions, then K/V rows and scores.  Slots past the tier's count read
-  // the page's first slot and are masked to zero afterwards.
-  int32_t pos[NT][4];
-#pragma unroll
-  for (int th = 0; th < NT; th++)
-#pragma unroll
-    for (int r = 0; r < 4; r++) {
-      const int t = 16 * th + 4 * g + r;
-      const int64_t slot = slot0 + ((act && t < valid) ? t : 0);
-      pos[th][r] = HI ? pl[slot] : pl[N - 1 - slot];
-    }
-  u32x4 kr[NT][4], vr[NT][4];
-  float mean[NT][4];
-#pragma unroll
-  for (int th = 0; th < NT; th++)
-#pragma unroll
-    for (int r = 0; r < 4; r++) {
-      const int64_t row = ((b0 + pos[th][r]) * H + h) * D + 8 * a;
-      kr[th][r] = __builtin_nontemporal_load((const u32x4*)(k + row));
-      vr[th][r] = __builtin_nontemporal_load((const u32x4*)(v + row));
-      mean[th][r] = sc_in[b0 + pos[th][r]];
-    }
 #pragma unroll
   for (int th = 0; th < NT; th++)
 #pragma unroll
@@ -429,59 +447,73 @@ __device__ inline void pack_page(uint8_t* pg, int lane, int valid, const int32_t
   const int nbp = (a >> 1) & 1;  // parity of the lane's 16-dim block
   uint32_t vw[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};  // V word per in-chunk dim 8(a&1)+e
   uint8_t* kc = pg + sg.kc;
-  auto fmn = [](float p, float q) { return fminf(p, q); };
-  auto fmx = [](float p, float q) { return fmaxf(p, q); };
 #pragma unroll
   for (int th = 0; th < NT; th++)
 #pragma unroll
     for (int r = 0; r < 4; r++) {
       const int t = 16 * th + 4 * g + r;
-      float kmn, kmx, vmn, vmx;
-      minmax8(kr[th][r], kmn, kmx);
-      minmax8(vr[th][r], vmn, vmx);
-      kmn = group_reduce<NA>(kmn, fmn);
-      kmx = group_reduce<NA>(kmx, fmx);
-      vmn = group_reduce<NA>(vmn, fmn);
-      vmx = group_reduce<NA>(vmx, fmx);
+      const uint32_t kw[4] = {kr[th][r][0], kr[th][r][1], kr[th][r][2], kr[th][r][3]};
+      const uint32_t vwr[4] = {vr[th][r][0], vr[th][r][1], vr[th][r][2], vr[th][r][3]};
+      // per-lane pair minima / maxima, then (K, V) words reduced over the group
+      const uint32_t kn = pmin(pmin(kw[0], kw[1]), pmin(kw[2], kw[3]));
+      const uint32_t kx = pmax(pmax(kw[0], kw[1]), pmax(kw[2], kw[3]));
+      const uint32_t vn = pmin(pmin(vwr[0], vwr[1]), pmin(vwr[2], vwr[3]));
+      const uint32_t vx = pmax(pmax(vwr[0], vwr[1]), pmax(vwr[2], vwr[3]));
+      uint32_t mn = pmin(__builtin_amdgcn_perm(vn, kn, 0x05040100u), __builtin_amdgcn_perm(vn, kn, 0x07060302u));
+      uint32_t mx = pmax(__builtin_amdgcn_perm(vx, kx, 0x05040100u), __builtin_amdgcn_perm(vx, kx, 0x07060302u));
+      mn = pmin(mn, lane_xchg<0>(mn));
+      mx = pmax(mx, lane_xchg<0>(mx));
+      mn = pmin(mn, lane_xchg<1>(mn));
+      mx = pmax(mx, lane_xchg<1>(mx));
+      mn = pmin(mn, lane_xchg<2>(mn));
+      mx = pmax(mx, lane_xchg<2>(mx));
+      if constexpr (NA > 8) {
+        mn = pmin(mn, lane_xchg<3>(mn));
+        mx = pmax(mx, lane_xchg<3>(mx));
+      }
       uint16_t ks16, kz16, vs16, vz16;
       float ks, kz, vs, vz;
-      codec_params(kmn, kmx, sg.kbits, ks16, kz16, ks, kz);
-      codec_params(vmn, vmx, sg.vbits, vs16, vz16, vs, vz);
-      const uint2 ck = codes8<sg.kbits>(kr[th][r], ks, kz);
-      const uint2 cv = codes8<sg.vbits>(vr[th][r], vs, vz);
+      codec_params(lo_h(mn), lo_h(mx), sg.kbits, ks16, kz16, ks, kz);
+      codec_params(hi_h(mn), hi_h(mx), sg.vbits, vs16, vz16, vs, vz);
+      uint32_t c[8];
+      codes8<sg.kbits>(kw, ks, kz, c);
       if (act) {
         if (HI) {
           // 8-bit K, token-major: bytes t*D + 8a .. +7
-          *(uint2*)(kc + t * D + 8 * a) = ck;
+          const uint32_t w0 = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+          const uint32_t w1 = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+          *(uint2*)(kc + t * D + 8 * a) = make_uint2(w0, w1);
         } else {
-          // 4-bit K: dim 8a+e in nibble e/2 + 4(e&1) of word a; bytes of
-          // ck hold dims (0,1,2,3) and (4,5,6,7)
-          const uint32_t ev = (ck.x & 0x00FF00FFu) | ((ck.y & 0x00FF00FFu) << 8);  // dims 0,4,2,6
-          const uint32_t od = ((ck.x >> 8) & 0x00FF00FFu) | (((ck.y >> 8) & 0x00FF00FFu) << 8);  // 1,5,3,7
-          // nibbles: dim e -> e/2 + 4(e&1): 0->0, 2->1, 4->2, 6->3, 1->4, 3->5, 5->6, 7->7
-          const uint32_t lo4 = (ev & 0xFu) | ((ev >> 12) & 0xF0u) | ((ev >> 0) & 0xF00u) | ((ev >> 12) & 0xF000u);
-          const uint32_t hi4 = (od & 0xFu) | ((od >> 12) & 0xF0u) | ((od >> 0) & 0xF00u) | ((od >> 12) & 0xF000u);
-          *(uint32_t*)(kc + t * (D / 2) + 4 * a) = lo4 | (hi4 << 16);
+          // 4-bit K: dim 8a+e in nibble e/2 + 4(e&1) of word a
+          uint32_t w = 0;
+#pragma unroll
+          for (int e = 0; e < 8; e++) w |= c[e] << (4 * ((e >> 1) + 4 * (e & 1)));
+          *(uint32_t*)(kc + t * (D / 2) + 4 * a) = w;
         }
-        if (a < 2) *(uint32_t*)(pg + (a == 0 ? sg.km : sg.vm) + 4 * t) =
-            a == 0 ? ((uint32_t)ks16 | ((uint32_t)kz16 << 16)) : ((uint32_t)vs16 | ((uint32_t)vz16 << 16));
+        if (a < 2)
+          *(uint32_t*)(pg + (a == 0 ? sg.km : sg.vm) + 4 * t) =
+              a == 0 ? ((uint32_t)ks16 | ((uint32_t)kz16 << 16)) : ((uint32_t)vs16 | ((uint32_t)vz16 << 16));
       }
+      codes8<sg.vbits>(vwr, vs, vz, c);
       // V field of (token t, dim 8a+e): bit 8 nbp + 4(r>>1) + 16(r&1)
       // (high), 8 nbp + 4 th + 2(r>>1) + 16(r&1) (low)
       const int sh = HI ? 8 * nbp + 4 * (r >> 1) + 16 * (r & 1) : 8 * nbp + 4 * th + 2 * (r >> 1) + 16 * (r & 1);
 #pragma unroll
-      for (int e = 0; e < 8; e++) vw[e] |= ((e < 4 ? cv.x : cv.y) >> (8 * (e & 3)) & 0xFFu) << sh;
+      for (int e = 0; e < 8; e++) vw[e] |= c[e] << sh;
     }
   // the other 16-dim block of each word comes from lane a^2
 #pragma unroll
   for (int e = 0; e < 8; e++) vw[e] |= lane_xchg<1>(vw[e]);
   if (act) {
     // lane keeps in-chunk dims 8(a&1) + 4 nbp .. +3: chunk L = i + 16 g, word a>>2
+    // (a bitwise select: an index that depends on the lane would move the
+    // array out of registers)
     uint8_t* vc = pg + sg.vc;
+    const uint32_t msk = 0u - (uint32_t)nbp;
 #pragma unroll
     for (int e4 = 0; e4 < 4; e4++) {
       const int L = 8 * (a & 1) + 4 * nbp + e4 + 16 * g;
-      *(uint32_t*)(vc + L * (D / 8) + 4 * (a >> 2)) = nbp ? vw[4 + e4] : vw[e4];
+      *(uint32_t*)(vc + L * (D / 8) + 4 * (a >> 2)) = vw[e4] ^ ((vw[e4] ^ vw[4 + e4]) & msk);
     }
   }
   // bytes after the last segment (high pages are shorter than the page)
@@ -489,9 +521,11 @@ __device__ inline void pack_page(uint8_t* pg, int lane, int valid, const int32_t
     *(uint4*)(pg + off) = make_uint4(0u, 0u, 0u, 0u);
 }
 
-// Persistent: wave w of the grid packs pages item = w, w + #waves, ... of the
-// call's TP pages (items in unit order, each unit's high pages then low
-// pages); the owning unit comes from the page map the list kernel wrote.
+// Persistent: each wave packs a contiguous range of the call's TP pages
+// (items in unit order, each unit's high pages then its low pages; the
+// owner of an item comes from the page map the list kernel wrote).  While a
+// page's rows are in flight the wave looks up the next page and loads its
+// positions, so a page waits for one round trip.
 template <int D>
 __global__ __launch_bounds__(256) void prompt_pack_kernel(int H, int L, int64_t total, int64_t P, int page_bytes,
                                                           const int64_t* __restrict__ hdr,
@@ -505,31 +539,53 @@ __global__ __launch_bounds__(256) void prompt_pack_kernel(int H, int L, int64_t 
                                                           uint8_t* __restrict__ pages, uint32_t* status) {
   if (!hdr[H_COMMIT]) return;
   const int64_t TP = hdr[H_PAGES];
+  constexpr int NA = D / 8;
   const int lane = threadIdx.x & 63;
+  const int a = lane % NA, g = lane / NA;
+  const bool act = g < 4;
   const int64_t nw = (int64_t)gridDim.x * (blockDim.x >> 6);
-  for (int64_t item = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-       item < TP; item += nw) {
-    const int64_t u = __builtin_amdgcn_readfirstlane(pmap[item]);
-    const int64_t* R = rec + u * kRec;
-    const int h = (int)(u % H);
-    const int64_t j = item - R[R_POFF];
-    const bool is_hi = j < R[R_HP];
-    const int64_t jt = is_hi ? j : j - R[R_HP];
-    const int32_t id = is_hi ? table[u * L + jt] : table[u * L + L - 1 - jt];
-    const int T = is_hi ? kHiTokens : kLoTokens;
-    const int64_t n_tier = is_hi ? R[R_NH] : R[R_NL];
-    const int64_t slot0 = jt * T;
-    const int valid = (int)(n_tier - slot0 < T ? n_tier - slot0 : T);
-    const int64_t N = R[R_N], b0 = R[R_BASE];
-    if (id < 0 || id >= P) {
-      if (lane == 0) atomicOr(status, kStBadState);
-      continue;
+  const int64_t w = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t per = (TP + nw - 1) / nw;
+  const int64_t i0 = w * per, i1 = TP < i0 + per ? TP : i0 + per;
+  if (i0 >= i1) return;
+  PackMeta m = pack_meta(i0, H, L, rec, pmap, table);
+  int32_t pos[2][4];
+  pack_pos(m, g, act, pos_list, total, pos);
+  for (int64_t item = i0; item < i1; item++) {
+    // this page's rows and mean scores
+    u32x4 kr[2][4], vr[2][4];
+    float mean[2][4];
+    const float* sc = scores + (int64_t)m.h * total + m.b0;
+#pragma unroll
+    for (int th = 0; th < 2; th++) {
+      if (th == 1 && m.hi) break;
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const int64_t row = ((m.b0 + pos[th][r]) * H + m.h) * D + 8 * a;
+        kr[th][r] = __builtin_nontemporal_load((const u32x4*)(k + row));
+        vr[th][r] = __builtin_nontemporal_load((const u32x4*)(v + row));
+        mean[th][r] = sc[pos[th][r]];
+      }
     }
-    uint8_t* pg = pages + (int64_t)id * page_bytes;
-    const int32_t* pl = pos_list + (int64_t)h * total + b0;
-    const float* sc = scores + (int64_t)h * total;
-    if (is_hi) pack_page<D, true>(pg, lane, valid, pl, slot0, N, b0, H, h, k, v, sc);
-    else pack_page<D, false>(pg, lane, valid, pl, slot0, N, b0, H, h, k, v, sc);
+    // the next page's metadata and positions meanwhile
+    PackMeta mn = m;
+    int32_t posn[2][4];
+    if (item + 1 < i1) {
+      mn = pack_meta(item + 1, H, L, rec, pmap, table);
+      pack_pos(mn, g, act, pos_list, total, posn);
+    }
+    if (m.id < 0 || m.id >= P) {
+      if (lane == 0) atomicOr(status, kStBadState);
+    } else {
+      uint8_t* pg = pages + (int64_t)m.id * page_bytes;
+      if (m.hi) pack_compute<D, true>(pg, lane, m.valid, m.N, pos, kr, vr, mean);
+      else pack_compute<D, false>(pg, lane, m.valid, m.N, pos, kr, vr, mean);
+    }
+    m = mn;
+#pragma unroll
+    for (int th = 0; th < 2; th++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) pos[th][r] = posn[th][r];
   }
 }
 
@@ -549,9 +605,15 @@ hipError_t launch_prompt(const Cfg& c, const Pool& p, int batch, int64_t total, 
                                                                    w.freed, table, state);
   prompt_list_kernel<<<dim3((unsigned)U), dim3(256), 0, s>>>(c.L, p.P, w.hdr, w.rec, w.freed, p.list,
                                                              table, w.pmap);
-  // four waves (pages in flight) per workgroup
-  int64_t grid = (U * c.L + 3) / 4;
-  if (grid > 4096) grid = 4096;
+  // persistent: as many 4-wave workgroups as fit on the device at once
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess)
+    e = c.d == 128 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prompt_pack_kernel<128>, 256, 0)
+                   : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prompt_pack_kernel<64>, 256, 0);
+  if (e != hipSuccess) return e;
+  int64_t grid = (int64_t)(cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
   if (c.d == 128)
     prompt_pack_kernel<128><<<dim3((unsigned)grid), dim3(256), 0, s>>>(
         c.H, c.L, total, p.P, p.page_bytes, w.hdr, w.rec, w.pmap, w.pos, table, k, v, scores, p.pages, p.status);
