@@ -47,6 +47,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "compressed decode-attn tokens/s + compaction µs/step; % peak HBM GB/s"
+WORKLOAD_NAMES = {"llama3_8b": "llama3_8b_layer", "long": "long_context", "churn": "decode_churn",
+                  "stress_gqa7": "stress_gqa7_lo_off", "stress_gqa8": "stress_gqa8", "tiny": "tiny"}
 PEAK_HBM_GBS = 8000.0
 
 
@@ -212,6 +214,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--workload", default="llama3_8b")
+    ap.add_argument("--batch", type=int, default=0, help="override the workload's batch")
+    ap.add_argument("--context", type=int, default=0, help="override with one fixed context length")
     ap.add_argument("--cpu-requests", type=int, default=8)
     ap.add_argument("--cpu-steps", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -245,7 +249,13 @@ def main():
     dev = torch.device("cuda:0")
     if args.copy_probe_mib > 0:
         copy_probe(args.copy_probe_mib)
-    cfg = synth.config(args.workload)
+    over = {}
+    if args.batch > 0:
+        over["batch"] = args.batch
+    if args.context > 0:
+        over["seq"] = (args.context, args.context)
+        over["max_seq_len"] = args.context + 256
+    cfg = synth.config(args.workload, **over)
     B, H, G, d = cfg["batch"], cfg["num_kv_heads"], cfg["gqa_group"], cfg["head_dim"]
     R = args.replicas
     lens = synth.seq_lens(cfg)
@@ -376,8 +386,12 @@ def main():
         "vs_baseline": None,
         "dtype": "f16-mfma/f32",
         "data": "synthetic",
-        "config": {"workload": "llama3_8b_layer", "q_heads": H * G, "kv_heads": H, "head_dim": d,
-                   "batch": B, "context": int(lens[0]), "score": "zipf(1.1)", "alpha_h": cfg["alpha_h"],
+        "config": {"workload": WORKLOAD_NAMES.get(args.workload, args.workload), "q_heads": H * G,
+                   "kv_heads": H, "head_dim": d, "batch": B,
+                   "context": int(lens[0]) if int(lens.min()) == int(lens.max()) else
+                   [int(lens.min()), int(lens.max())],
+                   "score": "zipf(%g)" % cfg["zipf"][0] if cfg["zipf"][0] == cfg["zipf"][1] else
+                   "zipf(U[%g,%g])" % tuple(cfg["zipf"]), "alpha_h": cfg["alpha_h"],
                    "alpha_l": cfg["alpha_l"], "window": cfg["window"], "replicas": R,
                    "pool_pages": P, "page_bytes": dk.diffkv_page_bytes(cfg),
                    "attn_splits": dk.diffkv_attn_splits(cfg, B)},
@@ -395,7 +409,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS,
                      "traffic": measured_traffic() if args.workload == "llama3_8b" else None,
-                     "kernel": "attn_kernel<128, 1, true, false>", "bytes_per_launch": int(attn_bytes),
+                     "kernel": ("attn_kernel<%d, 1, %s, false>" % (d, "true" if 2 * G <= 16 else "false"))
+                     if dk.diffkv_attn_splits(cfg, B) == 1 else
+                     "attn_kernel<%d, 2, ...> + attn_merge_kernel + score_kernel" % d,
+                     "bytes_per_launch": int(attn_bytes),
                      "stream_read_GBps": stream_read_gbps()},
     }
     if cpu is not None:
