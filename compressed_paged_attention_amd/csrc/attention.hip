@@ -102,16 +102,35 @@ __device__ inline uint32_t crumb2(uint32_t w, int s) {
   return (t & sreg_const<0x03000300u>()) | vreg_const<0x3C003C00u>();
 }
 
+// Splits per unit (grid width) when there are fewer units than compute
+// units: at least one 8-wave workgroup per compute unit, and enough that a
+// unit holding a whole row of pages spreads over workgroups of about
+// kSplitPages pages.  A unit takes pages in chunks of
+// max(ceil(pages / S), kSplitMinPages), so small units use few of the S
+// workgroups and large ones all of them (retention differs widely between
+// heads); the rest exit at once.
+constexpr int kSplitPages = 64;
+constexpr int kMaxSplitsHost = 128;  // the merge kernel's limit
+constexpr int kSplitMinPages = 16;
+
 int attn_splits(const Cfg& c, int batch) {
   const int64_t U = (int64_t)batch * c.H;
-  if (U <= 0) return 1;
-  int64_t S = (256 + U - 1) / U;  // about one 8-wave workgroup per compute unit
+  if (U <= 0 || U >= 256) return 1;
+  int64_t S = (256 + U - 1) / U;
+  const int64_t byrow = (c.L + kSplitPages - 1) / kSplitPages;
+  if (S < byrow) S = byrow;
   int64_t cap = c.L / 16;
   if (cap < 1) cap = 1;
   if (S > cap) S = cap;
-  if (S > 64) S = 64;
+  if (S > kMaxSplitsHost) S = kMaxSplitsHost;
   if (S < 1) S = 1;
   return (int)S;
+}
+
+__host__ __device__ inline int split_pages(int TPg, int S) {
+  if (S <= 1) return TPg;
+  const int q = (TPg + S - 1) / S;
+  return q > kSplitMinPages ? q : kSplitMinPages;
 }
 
 struct AttnWs {
@@ -614,7 +633,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
   };
   const bool sok = state_ok(nh, nl, ph, pl, L);
   const int TPg = sok ? ph + pl : 0;
-  const int pps = (TPg + S - 1) / S;
+  const int pps = split_pages(TPg, S);
   const int p0 = split * pps;
   const int p1 = min(TPg, p0 + pps);
 
@@ -637,6 +656,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
         mp[x * (D + 2) + D] = -INFINITY;
         mp[x * (D + 2) + D + 1] = 0.0f;
       }
+    }
+    return;
+  }
+  if (S > 1 && p0 >= p1) {  // a split past the unit's pages: an empty partial
+    float* mp = part + (((int64_t)u * S + split) * G) * (D + 2);
+    for (int x = tid; x < G; x += blockDim.x) {
+      mp[x * (D + 2) + D] = -INFINITY;
+      mp[x * (D + 2) + D + 1] = 0.0f;
     }
     return;
   }
@@ -1086,7 +1113,12 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
 }
 
 // Split merge (several workgroups per unit): out = sum_s O_s 2^(m_s - M) /
-// sum_s l_s 2^(m_s - M); also the final (M, L) for the score update.
+// sum_s l_s 2^(m_s - M); also the final (M, L) for the score update.  The
+// splits' maxima go to LDS once, each head's weights are formed once, and an
+// output sums only over the splits that attended to pages (in split order).
+// A NaN maximum marks a unit with a bad page id: output 0, (M, L) = (-inf, 0).
+constexpr int kMaxSplits = 128;
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(int H, int G, int S, const int32_t* __restrict__ seq_len,
                                                          const float* __restrict__ part, float* __restrict__ out,
@@ -1096,36 +1128,81 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(int H, int G, int S, co
   if (seq_len[b] <= 0) return;  // the attention kernel already wrote zeros
   const float* up = part + (u * S * G) * (D + 2);
   float* orow = out + ((int64_t)b * H * G + (int64_t)h * G) * D;
-  for (int x = threadIdx.x; x < G * D; x += blockDim.x) {
-    const int g = x / D, dd = x % D;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  __shared__ float sw[kMaxSplits * 16];  // [s][g]: maximum, then weight
+  __shared__ float sLg[16];
+  __shared__ int s_act[kMaxSplits], s_cnt[2], s_bad;
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  for (int x = tid; x < S * G; x += blockDim.x) {
+    const float m = up[x * (D + 2) + D];
+    sw[x] = m;
+    if (m != m) s_bad = 1;
+  }
+  __syncthreads();
+  if (tid < G) {
     float M = -INFINITY;
-    bool bad = false;
+    for (int sp = 0; sp < S; sp++) M = fmaxf(M, sw[sp * G + tid]);
+    if (s_bad) M = -INFINITY;
+    float l = 0.0f;
     for (int sp = 0; sp < S; sp++) {
-      const float ms = up[(sp * G + g) * (D + 2) + D];
-      bad |= ms != ms;
-      M = fmaxf(M, ms);
+      const float m = sw[sp * G + tid];
+      const float w = (M == -INFINITY || m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+      if (w != 0.0f) l += up[(sp * G + tid) * (D + 2) + D + 1] * w;
+      sw[sp * G + tid] = w;
     }
-    float o = 0.0f, l = 0.0f;
-    if (bad) M = -INFINITY;
-    else if (M != -INFINITY)
-      for (int sp = 0; sp < S; sp++) {
-        const float* pp = up + (sp * G + g) * (D + 2);
-        if (pp[D] == -INFINITY) continue;
-        const float f = __builtin_amdgcn_exp2f(pp[D] - M);
-        o += pp[dd] * f;
-        l += pp[D + 1] * f;
+    sLg[tid] = l;
+    if (save) {
+      ml[(u * G + tid) * 2 + 0] = M;
+      ml[(u * G + tid) * 2 + 1] = l;
+    }
+  }
+  __syncthreads();
+  // the splits with a nonzero weight for some head, in order
+  bool act = false;
+  if (tid < S)
+    for (int g = 0; g < G; g++) act |= sw[tid * G + g] != 0.0f;
+  const uint64_t mask = __ballot(act);
+  if (wid < 2 && lane == 0) s_cnt[wid] = __popcll(mask);
+  __syncthreads();
+  if (wid < 2 && act) {
+    const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+    s_act[(wid == 1 ? s_cnt[0] : 0) + below] = tid;
+  }
+  __syncthreads();
+  const int na = s_cnt[0] + (S > 64 ? s_cnt[1] : 0);
+  for (int x = tid; x < G * D; x += blockDim.x) {
+    const int g = x / D, dd = x % D;
+    float o = 0.0f;
+    int k = 0;
+    for (; k + 4 <= na; k += 4) {
+      float v[4], w[4];
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int sp = s_act[k + e];
+        v[e] = up[(sp * G + g) * (D + 2) + dd];
+        w[e] = sw[sp * G + g];
       }
-    orow[x] = l > 0.0f ? o / l : 0.0f;
-    if (save && dd == 0) {
-      ml[(u * G + g) * 2 + 0] = M;
-      ml[(u * G + g) * 2 + 1] = l;
+#pragma unroll
+      for (int e = 0; e < 4; e++) o += v[e] * w[e];
     }
+    for (; k < na; k++) {
+      const int sp = s_act[k];
+      o += up[(sp * G + g) * (D + 2) + dd] * sw[sp * G + g];
+    }
+    const float l = sLg[g];
+    orow[x] = l > 0.0f ? o / l : 0.0f;
   }
 }
 
-// Score update from saved logits (several splits, or a deferred update).
+// Score update from saved logits (several splits, or a deferred update):
+// 16 pages (512 slots) per workgroup.
+// A unit whose merge found a bad page id has (M, L) = (-inf, 0) and is left
+// alone; ids are checked where they are used.
+constexpr int kScorePages = 16;
+
 template <int D>
-__global__ __launch_bounds__(256) void score_kernel(int H, int G, int L, int S, int64_t P, int page_bytes,
+__global__ __launch_bounds__(256) void score_kernel(int H, int G, int L, int64_t P, int page_bytes,
                                                     const int32_t* __restrict__ table,
                                                     const int32_t* __restrict__ state,
                                                     const int32_t* __restrict__ seq_len,
@@ -1140,9 +1217,15 @@ __global__ __launch_bounds__(256) void score_kernel(int H, int G, int L, int S, 
   const int nh = s4[0], nl = s4[1], ph = s4[2], pl = s4[3];
   const int N = seq_len[b];
   if (N <= 0 || nh + nl == 0 || !state_ok(nh, nl, ph, pl, L)) return;
-  if (!unit_ids(ph, pl, L, P, row)) return;
+  const int TPg = ph + pl;
+  const int p0 = split * kScorePages, p1 = min(TPg, p0 + kScorePages);
+  if (p0 >= p1) return;
+  if (ml[u * G * 2 + 1] <= 0.0f) return;  // bad unit (or nothing attended)
   // the unit's scores change here: a plan record no longer applies
-  if (split == 0 && tid == 0 && ph >= 1) *(uint32_t*)(pages + (int64_t)row[0] * page_bytes + plan_rec_off<D>()) = 0u;
+  if (split == 0 && tid == 0 && ph >= 1) {
+    const int32_t id0 = row[0];
+    if (id0 >= 0 && id0 < P) *(uint32_t*)(pages + (int64_t)id0 * page_bytes + plan_rec_off<D>()) = 0u;
+  }
   __shared__ float sM[16], sI[16];
   if (tid < G) {
     sM[tid] = ml[(u * G + tid) * 2 + 0];
@@ -1150,40 +1233,53 @@ __global__ __launch_bounds__(256) void score_kernel(int H, int G, int L, int S, 
     sI[tid] = l > 0.0f ? 1.0f / l : 0.0f;
   }
   __syncthreads();
-  const int TPg = ph + pl;
-  const int pps = (TPg + S - 1) / S;
-  const int p0 = split * pps;
-  const int p1 = min(TPg, p0 + pps);
   const Seg sh = tier_seg(D, true), sl = tier_seg(D, false);
-  for (int x = tid; x < (p1 - p0) * 32; x += blockDim.x) {
-    const int j = p0 + x / 32, t = x % 32;
+  // two slots per thread, the loads of both issued before either is used
+  const int n = (p1 - p0) * 32;
+  int32_t id[2], tx[2];
+  bool ok[2];
+#pragma unroll
+  for (int e = 0; e < 2; e++) {
+    const int x = tid + 256 * e;
+    const int j = p0 + min(x, n - 1) / 32, t = x % 32;
     const bool is_hi = j < ph;
     const int jt = is_hi ? j : j - ph;
     const int nval = is_hi ? min(kHiTokens, nh - kHiTokens * jt) : min(kLoTokens, nl - kLoTokens * jt);
-    if (t >= nval) continue;
-    const int tidx = is_hi ? jt : L - 1 - jt;
-    const uint8_t* pg = pages + (int64_t)row[tidx] * page_bytes;
-    if (*(const int32_t*)(pg + (is_hi ? sh.ps : sl.ps) + 4 * t) >= N) continue;
-    const float* lg = logits + (((int64_t)u * L + tidx) * 32 + t) * G;
-    float mx = 0.0f;
-    for (int g = 0; g < G; g++) mx = fmaxf(mx, __builtin_amdgcn_exp2f(lg[g] - sM[g]) * sI[g]);
-    float* sc = (float*)(pg + (is_hi ? sh.sc : sl.sc) + 4 * t);
-    *sc = *sc + mx;
+    tx[e] = is_hi ? jt : L - 1 - jt;
+    id[e] = row[tx[e]];
+    ok[e] = x < n && t < nval;
   }
+  int32_t pos[2];
+  float old[2], mx[2] = {0.0f, 0.0f};
+  float* sc[2];
+#pragma unroll
+  for (int e = 0; e < 2; e++) {
+    const int x = tid + 256 * e, t = x % 32;
+    const bool is_hi = p0 + min(x, n - 1) / 32 < ph;
+    ok[e] = ok[e] && id[e] >= 0 && id[e] < P;
+    const uint8_t* pg = pages + (int64_t)(ok[e] ? id[e] : 0) * page_bytes;
+    pos[e] = ok[e] ? *(const int32_t*)(pg + (is_hi ? sh.ps : sl.ps) + 4 * t) : N;
+    sc[e] = (float*)(pg + (is_hi ? sh.sc : sl.sc) + 4 * t);
+    old[e] = ok[e] ? *sc[e] : 0.0f;
+    const float* lg = logits + (((int64_t)u * L + tx[e]) * 32 + t) * G;
+    for (int g = 0; g < G; g++) mx[e] = fmaxf(mx[e], __builtin_amdgcn_exp2f(lg[g] - sM[g]) * sI[g]);
+  }
+#pragma unroll
+  for (int e = 0; e < 2; e++)
+    if (ok[e] && pos[e] < N) *sc[e] = old[e] + mx[e];
 }
 
 hipError_t launch_scores(const Cfg& c, const Pool& p, int batch, const int32_t* table, const int32_t* state,
                          const int32_t* seq_len, void* ws, hipStream_t s) {
   const int64_t U = (int64_t)batch * c.H;
   if (U == 0) return hipSuccess;
-  const int S = attn_splits(c, batch);
   AttnWs w = attn_carve(c, batch, true, ws, nullptr);
-  const dim3 grid(S, (unsigned)U), block(256);
+  const dim3 grid((unsigned)((c.L + kScorePages - 1) / kScorePages), (unsigned)U), block(256);
   if (c.d == 128)
-    score_kernel<128><<<grid, block, 0, s>>>(c.H, c.G, c.L, S, p.P, p.page_bytes, table, state, seq_len, w.ml,
+    score_kernel<128><<<grid, block, 0, s>>>(c.H, c.G, c.L, p.P, p.page_bytes, table, state, seq_len, w.ml,
                                              w.logits, p.pages);
   else
-    score_kernel<64><<<grid, block, 0, s>>>(c.H, c.G, c.L, S, p.P, p.page_bytes, table, state, seq_len, w.ml,
+    score_kernel<64><<<grid, block, 0, s>>>(c.H, c.G, c.L, p.P, p.page_bytes, table, state, seq_len, w.ml,
                                             w.logits, p.pages);
   return hipGetLastError();
 }
