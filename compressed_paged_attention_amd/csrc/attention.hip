@@ -133,10 +133,15 @@ __host__ __device__ inline int split_pages(int TPg, int S) {
   return q > kSplitMinPages ? q : kSplitMinPages;
 }
 
+// Score-update chunks (several splits, or a deferred update): 16 pages each.
+constexpr int kScorePages = 16;
+constexpr int kCandWords = 8;  // per chunk: least important high / low candidate, t_c
+
 struct AttnWs {
   float* part;    // [U][S][G][D + 2] split partials (unnormalized O, max, sum)
   float* ml;      // [U][G][2] final (max, sum) in base 2, for the score update
   float* logits;  // [U][L][32][G] base-2 logits of every retained slot
+  int32_t* cand;  // [U][ceil(L/16)][8] score-update candidates per chunk, for the next step's plan
 };
 
 static AttnWs attn_carve(const Cfg& c, int batch, bool scores, void* ws, size_t* bytes) {
@@ -151,6 +156,9 @@ static AttnWs attn_carve(const Cfg& c, int batch, bool scores, void* ws, size_t*
   off = align_up(off + (size_t)U * c.G * 2 * sizeof(float), 256);
   w.logits = (float*)(b + off);
   if (scores) off = align_up(off + (size_t)U * c.L * 32 * c.G * sizeof(float), 256);
+  w.cand = (int32_t*)(b + off);
+  if (scores)
+    off = align_up(off + (size_t)U * ((c.L + kScorePages - 1) / kScorePages) * kCandWords * sizeof(int32_t), 256);
   if (bytes) *bytes = off < 256 ? 256 : off;
   return w;
 }
@@ -1196,18 +1204,22 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(int H, int G, int S, co
 }
 
 // Score update from saved logits (several splits, or a deferred update):
-// 16 pages (512 slots) per workgroup.
-// A unit whose merge found a bad page id has (M, L) = (-inf, 0) and is left
-// alone; ids are checked where they are used.
-constexpr int kScorePages = 16;
+// 16 pages (512 slots) per workgroup.  A unit whose merge found a bad page id
+// has (M, L) = (-inf, 0) and is left alone; ids are checked where they are
+// used.  Each chunk also leaves the candidates the next generation step
+// (length N + 1) needs: the least important non-window high token, the least
+// important low token and the token leaving the window, from the updated
+// sums (the rules of the fused update); score_finish_kernel turns them into
+// the unit's plan record.
 
 template <int D>
-__global__ __launch_bounds__(256) void score_kernel(int H, int G, int L, int64_t P, int page_bytes,
+__global__ __launch_bounds__(256) void score_kernel(int H, int G, int L, int64_t P, int page_bytes, int W,
                                                     const int32_t* __restrict__ table,
                                                     const int32_t* __restrict__ state,
                                                     const int32_t* __restrict__ seq_len,
                                                     const float* __restrict__ ml,
-                                                    const float* __restrict__ logits, uint8_t* pages) {
+                                                    const float* __restrict__ logits, uint8_t* pages,
+                                                    int32_t* __restrict__ cand) {
   const int split = blockIdx.x;
   const int64_t u = blockIdx.y;
   const int b = (int)u / H;
@@ -1227,11 +1239,14 @@ __global__ __launch_bounds__(256) void score_kernel(int H, int G, int L, int64_t
     if (id0 >= 0 && id0 < P) *(uint32_t*)(pages + (int64_t)id0 * page_bytes + plan_rec_off<D>()) = 0u;
   }
   __shared__ float sM[16], sI[16];
+  __shared__ int s_tc;  // slot of the token leaving the window at length N + 1
+  __shared__ float s_tcsum;
   if (tid < G) {
     sM[tid] = ml[(u * G + tid) * 2 + 0];
     const float l = ml[(u * G + tid) * 2 + 1];
     sI[tid] = l > 0.0f ? 1.0f / l : 0.0f;
   }
+  if (tid == 0) s_tc = -1;
   __syncthreads();
   const Seg sh = tier_seg(D, true), sl = tier_seg(D, false);
   // two slots per thread, the loads of both issued before either is used
@@ -1264,9 +1279,107 @@ __global__ __launch_bounds__(256) void score_kernel(int H, int G, int L, int64_t
     const float* lg = logits + (((int64_t)u * L + tx[e]) * 32 + t) * G;
     for (int g = 0; g < G; g++) mx[e] = fmaxf(mx[e], __builtin_amdgcn_exp2f(lg[g] - sM[g]) * sI[g]);
   }
+  const int64_t N1 = (int64_t)N + 1, tc1 = N1 - W;
+  __shared__ Cand cw[2][4];
+  Cand bh{0.0f, kNoPos, 0}, bl{0.0f, kNoPos, 0};
 #pragma unroll
-  for (int e = 0; e < 2; e++)
-    if (ok[e] && pos[e] < N) *sc[e] = old[e] + mx[e];
+  for (int e = 0; e < 2; e++) {
+    const int x = tid + 256 * e, t = x % 32;
+    const int j = p0 + min(x, n - 1) / 32;
+    const bool is_hi = j < ph;
+    const bool upd = ok[e] && pos[e] < N;
+    const float ns = old[e] + mx[e];
+    if (upd) *sc[e] = ns;
+    const int ls = is_hi ? 16 * j + t : 32 * (j - ph) + t;
+    if (upd && is_hi && pos[e] == tc1) {  // positions are unique: one writer
+      s_tc = ls;
+      s_tcsum = ns;
+    }
+    const Cand c{ns, (upd && (!is_hi || pos[e] <= tc1)) ? pos[e] : kNoPos, ls};
+    if (is_hi) bh = min_imp(bh, c, N1);
+    else bl = min_imp(bl, c, N1);
+  }
+  bh = wave_argmin(bh, N1);
+  bl = wave_argmin(bl, N1);
+  const int lane = tid & 63, wid = tid >> 6;
+  if (lane == 0) {
+    cw[0][wid] = bh;
+    cw[1][wid] = bl;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < 4; w++) {
+      bh = min_imp(bh, cw[0][w], N1);
+      bl = min_imp(bl, cw[1][w], N1);
+    }
+    int32_t* cp = cand + ((int64_t)u * gridDim.x + split) * kCandWords;
+    cp[0] = __float_as_int(bh.sum);
+    cp[1] = bh.pos;
+    cp[2] = bh.slot;
+    cp[3] = __float_as_int(bl.sum);
+    cp[4] = bl.pos;
+    cp[5] = bl.slot;
+    cp[6] = s_tc;
+    cp[7] = __float_as_int(s_tcsum);
+  }
+}
+
+// One wave per unit: the chunks' candidates reduced (the order does not
+// matter: the comparison is a strict total order), then the next step's
+// decision written as the unit's plan record, as the fused update does.  The
+// conditions under which score_kernel leaves a unit alone are re-checked
+// here, so candidates of an earlier call are never used.
+template <int D>
+__global__ __launch_bounds__(64) void score_finish_kernel(int H, int G, int L, int64_t P, int page_bytes,
+                                                          PolicyArgs pa, const int32_t* __restrict__ table,
+                                                          const int32_t* __restrict__ state,
+                                                          const int32_t* __restrict__ seq_len,
+                                                          const float* __restrict__ ml,
+                                                          const int32_t* __restrict__ cand, uint8_t* pages) {
+  const int64_t u = blockIdx.x;
+  const int b = (int)u / H;
+  const int lane = threadIdx.x;
+  const int32_t* row = table + u * L;
+  const int32_t* s4 = state + 4 * u;
+  const int nh = s4[0], nl = s4[1], ph = s4[2], pl = s4[3];
+  const int N = seq_len[b];
+  if (N <= 0 || nh + nl == 0 || !state_ok(nh, nl, ph, pl, L) || ph < 1) return;
+  if (ml[u * G * 2 + 1] <= 0.0f) return;
+  const int64_t N1 = (int64_t)N + 1, tc1 = N1 - pa.W;
+  if (nh + nl > N1) return;
+  const int nck = (ph + pl + kScorePages - 1) / kScorePages, ncs = (L + kScorePages - 1) / kScorePages;
+  Cand bh{0.0f, kNoPos, 0}, bl{0.0f, kNoPos, 0};
+  int tcs = -1;
+  float tcsum = 0.0f;
+  for (int k = lane; k < nck; k += 64) {
+    const int32_t* cp = cand + (u * ncs + k) * kCandWords;
+    bh = min_imp(bh, Cand{__int_as_float(cp[0]), cp[1], cp[2]}, N1);
+    bl = min_imp(bl, Cand{__int_as_float(cp[3]), cp[4], cp[5]}, N1);
+    if (cp[6] >= 0) {
+      tcs = cp[6];
+      tcsum = __int_as_float(cp[7]);
+    }
+  }
+  bh = wave_argmin(bh, N1);
+  bl = wave_argmin(bl, N1);
+  const uint64_t has = __ballot(tcs >= 0);
+  if (has) {
+    const int src = (int)__builtin_ctzll(has);
+    tcs = __shfl(tcs, src, 64);
+    tcsum = __shfl(tcsum, src, 64);
+  }
+  if (tc1 >= 0 && tcs < 0) return;  // the plan kernel would not accept the state
+  const int32_t id0 = row[0];
+  if (id0 < 0 || id0 >= P) return;
+  const Plan pn = plan_decide(N1, pa.W, pa.S_max, pa.lo_en, (double)pa.ah, (double)pa.al, nh, nl, ph, pl, L, tcs,
+                              tcsum, bh, bl);
+  uint32_t rw[kRecWords];
+  plan_rec_fill(rw, N1, nh, nl, ph, pl, pn);
+  uint32_t wv = rw[0];
+#pragma unroll
+  for (int k = 1; k < kRecWords; k++) wv = lane == k ? rw[k] : wv;
+  uint32_t* dst = (uint32_t*)(pages + (int64_t)id0 * page_bytes + plan_rec_off<D>());
+  if (lane < kRecWords) dst[lane] = wv;
 }
 
 hipError_t launch_scores(const Cfg& c, const Pool& p, int batch, const int32_t* table, const int32_t* state,
@@ -1275,12 +1388,18 @@ hipError_t launch_scores(const Cfg& c, const Pool& p, int batch, const int32_t* 
   if (U == 0) return hipSuccess;
   AttnWs w = attn_carve(c, batch, true, ws, nullptr);
   const dim3 grid((unsigned)((c.L + kScorePages - 1) / kScorePages), (unsigned)U), block(256);
-  if (c.d == 128)
-    score_kernel<128><<<grid, block, 0, s>>>(c.H, c.G, c.L, p.P, p.page_bytes, table, state, seq_len, w.ml,
-                                             w.logits, p.pages);
-  else
-    score_kernel<64><<<grid, block, 0, s>>>(c.H, c.G, c.L, p.P, p.page_bytes, table, state, seq_len, w.ml,
-                                            w.logits, p.pages);
+  const PolicyArgs pa{c.W, c.S_max, c.lo_en, c.ah, c.al};
+  if (c.d == 128) {
+    score_kernel<128><<<grid, block, 0, s>>>(c.H, c.G, c.L, p.P, p.page_bytes, c.W, table, state, seq_len, w.ml,
+                                             w.logits, p.pages, w.cand);
+    score_finish_kernel<128><<<dim3((unsigned)U), dim3(64), 0, s>>>(c.H, c.G, c.L, p.P, p.page_bytes, pa, table,
+                                                                    state, seq_len, w.ml, w.cand, p.pages);
+  } else {
+    score_kernel<64><<<grid, block, 0, s>>>(c.H, c.G, c.L, p.P, p.page_bytes, c.W, table, state, seq_len, w.ml,
+                                            w.logits, p.pages, w.cand);
+    score_finish_kernel<64><<<dim3((unsigned)U), dim3(64), 0, s>>>(c.H, c.G, c.L, p.P, p.page_bytes, pa, table,
+                                                                   state, seq_len, w.ml, w.cand, p.pages);
+  }
   return hipGetLastError();
 }
 

@@ -538,6 +538,50 @@ def test_plan_record_matches_scan(dk, orc, batch):
 
 
 @pytest.mark.parametrize("d,G,lo", [(128, 4, 1), (64, 5, 1), (128, 7, 0), (64, 16, 1)])
+def test_split_plan_record_matches_scan(dk, orc, d, G, lo):
+    """With several splits per unit the score update runs in 16-page chunks
+    that leave candidates, from which a finishing kernel writes the next
+    step's plan record.  Stepping from those records is byte-identical to
+    stepping with every record erased before each step (the plan kernel then
+    scans), over steps on units of very different sizes, and the records are
+    used."""
+    from tests.parity import first_pages, masked, plan_record_span
+    from workloads import synth
+    cfg = _medium_cfg("llama3_8b", head_dim=d, gqa_group=G, lo_enabled=lo, num_kv_heads=3,
+                      batch=5, max_seq_len=2100, window=64)
+    assert dk.diffkv_attn_splits(cfg, 5) > 1
+    lens = torch.tensor([2000, 37, 900, 1500, 300], dtype=torch.int64)
+    P = int(sum(-(-int(n) // 16) + 2 for n in lens) * 3 * 1.2) + 8
+    b_, c_ = _twin_caches(dk, cfg, 5, lens, P, 2)
+    off, n = plan_record_span(cfg)
+    seq = lens.to(torch.int32).to(dev)
+    used = 0
+    _say(f"split plan records d={d} G={G} lo={lo} splits={dk.diffkv_attn_splits(cfg, 5)}")
+    for step in range(10):
+        dec = synth.make_decode(cfg, step, device=dev)
+        first = c_.page_table[..., 0].reshape(-1)
+        first = first[first >= 0].to(torch.int64)
+        c_.pool.pages.view(P, -1)[first, off:off + n] = 0
+        used += int((_plan_record_words(b_, cfg) != 0).sum())
+        ob = b_.decode_step(dec["q"], seq, dec["k_new"], dec["v_new"], update_scores=1)
+        oc = c_.decode_step(dec["q"], seq, dec["k_new"], dec["v_new"], update_scores=1)
+        torch.cuda.synchronize()
+        assert torch.equal(ob, oc), f"step {step}: outputs differ"
+        for name in ("page_table", "tier_state"):
+            assert torch.equal(getattr(b_, name), getattr(c_, name)), f"step {step}: {name} differs"
+        assert torch.equal(b_.pool.free_list, c_.pool.free_list) and torch.equal(b_.pool.ptr, c_.pool.ptr)
+        pb, pc = np_(b_.pool.pages.view(P, -1)), np_(c_.pool.pages.view(P, -1))
+        fp = first_pages(np_(b_.page_table))
+        for p_ in sorted({int(x) for x in np_(b_.page_table).ravel() if x >= 0}):
+            x, y = (masked(pb[p_], cfg), masked(pc[p_], cfg)) if p_ in fp else (pb[p_], pc[p_])
+            assert np.array_equal(x, y), f"step {step}: page {p_} differs"
+        seq = seq + 1
+    assert used > 0, "no plan record was used"
+    for s_ in (b_, c_):
+        assert int(s_.pool.status.item()) == 0
+
+
+@pytest.mark.parametrize("d,G,lo", [(128, 4, 1), (64, 5, 1), (128, 7, 0), (64, 16, 1)])
 def test_chained_steps_match_plan_kernel(dk, orc, d, G, lo):
     """Chained decode steps (each planned by the previous step's attention)
     against the same steps through the plan kernel, for both head sizes,
