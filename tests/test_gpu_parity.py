@@ -129,6 +129,72 @@ def test_tiny_prompt_and_attention(dk, orc, window):
     _say("tiny attention max err", err)
 
 
+def _edge_rows(rng, n, d, tiers, kv):
+    """fp16 rows that sit on the codec's edges, cycling over the row types:
+    random; constant (zero scale); a range below fp16 resolution (subnormal
+    or zero scale); subnormal values; the full +-65504 range; a large offset
+    with a small range; and rows whose quotients (x - z) / s are exact
+    half-integers for the code width of the token's tier (ties to even).
+    `kv` = 0 for K, 1 for V; tiers: 2 high, 1 low, 0 pruned."""
+    out = np.zeros((n, d), np.float32)
+    for t in range(n):
+        kind = t % 7
+        if kind == 0:
+            r = rng.standard_normal(d)
+        elif kind == 1:
+            r = np.full(d, rng.standard_normal() * 3)
+        elif kind == 2:
+            r = 1.0 + rng.standard_normal(d) * 1e-5
+        elif kind == 3:
+            r = rng.standard_normal(d) * 1e-6
+        elif kind == 4:
+            r = rng.standard_normal(d) * 1000
+            r[rng.integers(0, d)] = 65504.0
+            r[rng.integers(0, d)] = -65504.0
+        elif kind == 5:
+            r = 1000.0 + rng.standard_normal(d) * 0.5
+        else:
+            bits = {(2, 0): 8, (2, 1): 4, (1, 0): 4, (1, 1): 2}.get((int(tiers[t]), kv), 8)
+            q = (1 << bits) - 1
+            r = (rng.integers(0, q, d) + 0.5) * 0.25   # exact half-integer quotients
+            i0, i1 = rng.choice(d, 2, replace=False)
+            r[i0], r[i1] = 0.0, q * 0.25               # min 0, max q s: s = 0.25 exactly
+        out[t] = r
+    return out.astype(np.float16)
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_prompt_codec_edge_rows(dk, orc, d):
+    """Prompt compaction of rows on the codec's edges (constant, sub-resolution
+    and subnormal ranges, +-65504, large offsets, exact half-integer
+    quotients) is byte-identical to the oracle: codes, fp16 scale/zero,
+    scores, positions and every page."""
+    from workloads import synth
+    cfg = synth.config("llama3_8b", head_dim=d, num_kv_heads=2, batch=2, window=0, max_seq_len=512)
+    lens = np.array([200, 77])
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    total, H = int(cu[-1]), 2
+    rng = np.random.default_rng(20261202)
+    # tiers by score (window 0): t % 3 -> high, low, pruned
+    scores = np.zeros((H, total), np.float32)
+    tiers = np.zeros((H, total), np.int64)
+    for b in range(2):
+        N = int(lens[b])
+        for h in range(H):
+            for t in range(N):
+                tiers[h, cu[b] + t] = (2, 1, 0)[(t + h) % 3]
+                scores[h, cu[b] + t] = {2: 2.0, 1: 0.5, 0: 0.05}[tiers[h, cu[b] + t]] / N
+    k = np.zeros((total, H, d), np.float16)
+    v = np.zeros((total, H, d), np.float16)
+    for h in range(H):
+        k[:, h] = _edge_rows(rng, total, d, tiers[h], 0)
+        v[:, h] = _edge_rows(rng, total, d, tiers[h], 1)
+    p = Pair(dk, orc, cfg, 2, 64, total)
+    _say(f"codec edge rows d={d}")
+    p.prompt(cu, k.view(np.int16), v.view(np.int16), scores, what=f"edge rows d={d}")
+    check_pool_invariants(orc, p.o)
+
+
 def _medium_cfg(name, **over):
     from workloads import synth
     c = synth.config(name, **over)
