@@ -207,6 +207,111 @@ def cpu_baseline(cfg, n_req, n_steps, workers):
                 nproc=os.cpu_count())
 
 
+def churn_schedule(args):
+    """Decode churn as the workload defines it: 128 requests with contexts
+    U[1K, 16K] and output budgets U[1, 512]; every step appends one token per
+    request (diffkv_decode_step with the score update); a request that has
+    used its budget is released in the same step and its slot re-admitted
+    with a fresh prompt (U[1K, 16K] tokens, Zipf(1.1) scores): release, then
+    classify + prompt compaction of the admitted requests.  Every input is
+    drawn before the timed region; each step's decode and each admission are
+    bracketed by HIP events on a held stream.  Prints one JSON line."""
+    import numpy as np
+    import torch
+
+    import compressed_paged_attention_amd as dk
+    from workloads import synth
+
+    dev = torch.device("cuda:0")
+    cfg = synth.config("churn")
+    B, H, G, d = cfg["batch"], cfg["num_kv_heads"], cfg["gqa_group"], cfg["head_dim"]
+    S = args.steps
+    rng = np.random.default_rng(synth.SEED_BASE + 4000)
+    lens = synth.seq_lens(cfg)
+    P = synth.pool_pages(cfg, lens, dk.diffkv_page_bytes(cfg))
+    st = dk.DiffKVState(cfg, B, P, max_total_tokens=int(lens.sum()), device=dev)
+    pr = synth.make_prompt(cfg, device=dev, lens=lens)
+    cu = pr["cu_seqlens"].to(dev)
+    tiers, _ = st.classify(cu, pr["scores"])
+    st.compact_prompt(cu, pr["k"], pr["v"], pr["scores"], tiers)
+    torch.cuda.synchronize()
+    del pr, tiers
+    # the schedule, drawn up front
+    lo, hi = cfg["seq"]
+    blo, bhi = cfg["budget"]
+    seq = lens.numpy().astype(np.int64).copy()
+    budget = rng.integers(blo, bhi + 1, B)
+    gen = np.zeros(B, np.int64)
+    steps = []
+    for s_ in range(S):
+        seq_s = seq.astype(np.int32).copy()
+        seq += 1
+        gen += 1
+        done = gen >= budget
+        adm = None
+        if done.any():
+            nl = np.where(done, rng.integers(lo, hi + 1, B), 0)
+            adm = (done.astype(np.uint8), nl)
+            seq[done] = nl[done]
+            gen[done] = 0
+            budget[done] = rng.integers(blo, bhi + 1, int(done.sum()))
+        steps.append((seq_s, adm))
+    dec = [synth.make_decode(cfg, s_, device=dev) for s_ in range(S)]
+    seq_d = [torch.from_numpy(x).to(dev) for x, _ in steps]
+    adm_in = {}
+    for s_, (_, adm) in enumerate(steps):
+        if adm is None:
+            continue
+        mask, nl = adm
+        lens_a = torch.from_numpy(nl.astype(np.int64))
+        pa = synth.make_prompt(cfg, device=dev, salt=1 + s_, lens=lens_a)
+        adm_in[s_] = (torch.from_numpy(mask).to(dev), pa["cu_seqlens"].to(dev), pa["k"], pa["v"], pa["scores"])
+    torch.cuda.synchronize()
+    print(f"[bench] churn: {len(adm_in)} admission events, {sum(int(a[0].sum()) for _, a in steps if a)} "
+          f"requests replaced", file=sys.stderr, flush=True)
+    out = torch.empty(B, H * G, d, dtype=torch.float32, device=dev)
+    # warm the classify outputs' allocations of the first admission
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    e_dec = [(ev(), ev()) for _ in range(S)]
+    e_adm = {s_: (ev(), ev()) for s_ in adm_in}
+    torch.cuda.synchronize()
+    torch.cuda._sleep(args.hold_cycles)
+    for s_ in range(S):
+        e_dec[s_][0].record()
+        st.decode_step(dec[s_]["q"], seq_d[s_], dec[s_]["k_new"], dec[s_]["v_new"], update_scores=1, out=out)
+        e_dec[s_][1].record()
+        if s_ in adm_in:
+            mask, cu_a, k_a, v_a, sc_a = adm_in[s_]
+            e_adm[s_][0].record()
+            st.release(mask)
+            t_a, _ = st.classify(cu_a, sc_a)
+            st.compact_prompt(cu_a, k_a, v_a, sc_a, t_a)
+            e_adm[s_][1].record()
+    torch.cuda.synchronize()
+    status = int(st.pool.status.item())
+    assert status == 0, f"status bits set during the churn run: {status}"
+    dec_us = np.array([a.elapsed_time(b) * 1e3 for a, b in e_dec])
+    adm_us = np.array([e_adm[s_][0].elapsed_time(e_adm[s_][1]) * 1e3 for s_ in sorted(adm_in)])
+    total_us = e_dec[0][0].elapsed_time(e_dec[-1][1]) * 1e3
+    ptr = st.pool.ptr.cpu().numpy().view(np.uint64)
+    res = {
+        "metric": "decode churn: per-step decode time and admissions",
+        "workload": "decode_churn_schedule", "batch": B, "q_heads": H * G, "kv_heads": H, "head_dim": d,
+        "steps": S, "pool_pages": P,
+        "decode_step_us": {"p50": float(np.percentile(dec_us, 50)), "p99": float(np.percentile(dec_us, 99)),
+                           "mean": float(dec_us.mean())},
+        "admission_events": int(len(adm_us)),
+        "requests_replaced": int(sum(int(a[0].sum()) for _, a in steps if a)),
+        "admission_us": {"p50": float(np.percentile(adm_us, 50)) if len(adm_us) else None,
+                         "p99": float(np.percentile(adm_us, 99)) if len(adm_us) else None},
+        "request_tokens_per_s": B * S / (total_us * 1e-6),
+        "timed_region_us": total_us,
+        "pointer_laps": [float(ptr[0]) / P, float(ptr[1]) / P],
+        "data": "synthetic",
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,6 +328,8 @@ def main():
                     help="oracle processes for the all-cores baseline")
     ap.add_argument("--hold-cycles", type=int, default=100_000_000,
                     help="spin-kernel length that holds the stream while a timed segment is enqueued")
+    ap.add_argument("--churn-schedule", action="store_true",
+                    help="run the decode-churn schedule (releases and admissions) instead; one JSON line")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one elementwise copy of this size first (counter calibration)")
     args = ap.parse_args()
@@ -230,6 +337,9 @@ def main():
         print("bench.py: this build measures one GPU only; the path has no cross-GPU exchange "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.churn_schedule:
+        churn_schedule(args)
+        return
 
     import numpy as np
     import torch
