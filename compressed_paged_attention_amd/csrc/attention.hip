@@ -938,7 +938,19 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
       const int64_t N1 = (int64_t)N + 1, tc1 = N1 - pa.W;
       __shared__ Cand cw[2][kWaves];
       Cand bh{0.0f, kNoPos, 0}, bl{0.0f, kNoPos, 0};
-      const int NSL = TPg * 32;  // slots, 32 per page (high pages use 16)
+      const int NSL = TPg * 32;  // slot rows in LDS, 32 per page (high pages use 16)
+      const int NE = 16 * ph + 32 * pl;  // slots the pass visits: 16 per high page
+      // pass index -> (page, in-page slot): high pages first, then low pages
+      auto slot_of = [&](int xe, int& j, int& t) {
+        if (xe < 16 * ph) {
+          j = xe >> 4;
+          t = xe & 15;
+        } else {
+          const int y = xe - 16 * ph;
+          j = ph + (y >> 5);
+          t = y & 31;
+        }
+      };
       // kU slots per thread per round: all loads of a round are issued
       // before any use; GB >= G logits per slot (indices clamped to G - 1:
       // repeats do not change a maximum)
@@ -956,14 +968,15 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
         }
         const float* lgg = logits + (int64_t)u * L * 32 * G;
         // wave-uniform trip count: a wave runs while its first slot is in range
-        for (int x0 = tid; x0 - lane < NSL; x0 += kU * kThreads) {
+        for (int x0 = tid; x0 - lane < NE; x0 += kU * kThreads) {
           float lv[kU][GB], osv[kU];
           int32_t psv[kU];
           uint8_t* pgv[kU];
 #pragma unroll
           for (int e = 0; e < kU; e++) {
-            const int x = min(x0 + e * kThreads, NSL - 1);
-            const int j = x >> 5, t = x & 31;
+            int j, t;
+            slot_of(min(x0 + e * kThreads, NE - 1), j, t);
+            const int x = 32 * j + t;
             const bool hi = j < ph;
             if (kLds) {
 #pragma unroll
@@ -983,10 +996,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
           }
 #pragma unroll
           for (int e = 0; e < kU; e++) {
-            const int x = x0 + e * kThreads;
-            const int j = x >> 5, t = x & 31;
+            const int xe = x0 + e * kThreads;
+            int j, t;
+            slot_of(min(xe, NE - 1), j, t);
             const bool hi = j < ph;
-            const bool ok = x < NSL && t < valid(j) && psv[e] < N;
+            const bool ok = xe < NE && t < valid(j) && psv[e] < N;
             float xm = -INFINITY;
 #pragma unroll
             for (int g = 0; g < GB; g++) xm = fmaxf(xm, lv[e][g] + cg[g]);
