@@ -179,6 +179,18 @@ def _oracle_worker_b(args):
     return _oracle_steps(cfg, n_req, n_steps, _BARRIER)
 
 
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), else the machine type."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(cfg, n_req, n_steps, workers):
     """The oracle timed on this host on a bounded sample of the same workload:
     once on one thread, once as `workers` processes (each n_req / 4 requests
@@ -203,7 +215,7 @@ def cpu_baseline(cfg, n_req, n_steps, workers):
                        f"{cfg['seq'][0]} tokens each) through prompt compaction, then {n_steps} decode "
                        f"steps (step compaction + fp64 attention + score update) started together; "
                        f"value = sum of the processes' request-tokens/s",
-                single_thread=single, cpu=platform.processor() or platform.machine(),
+                single_thread=single, cpu=cpu_model(),
                 nproc=os.cpu_count())
 
 
