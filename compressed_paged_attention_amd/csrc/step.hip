@@ -70,7 +70,7 @@ __global__ __launch_bounds__(kPlanThreads) void step_plan_kernel(int H, int L, i
   __shared__ uint32_t s_bad;
   __shared__ Cand lds[2][kPlanThreads / 64];
   __shared__ int s_rec;
-  // ---- round 1: length, tier state, the table row (every load of a
+  // ---- first round trip: length, tier state, the table row (every load of a
   // thread issued before any is used: one round trip) ----
   const bool cached = L <= kRowCache;
   if (cached) {
