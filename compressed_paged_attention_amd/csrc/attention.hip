@@ -110,7 +110,7 @@ __device__ inline uint32_t crumb2(uint32_t w, int s) {
 // workgroups and large ones all of them (retention differs widely between
 // heads); the rest exit at once.
 constexpr int kSplitPages = 64;
-constexpr int kMaxSplitsHost = 128;  // the merge kernel's limit
+constexpr int kMaxSplits = 128;  // the merge kernel holds one weight per split and head in LDS
 constexpr int kSplitMinPages = 16;
 
 int attn_splits(const Cfg& c, int batch) {
@@ -122,7 +122,7 @@ int attn_splits(const Cfg& c, int batch) {
   int64_t cap = c.L / 16;
   if (cap < 1) cap = 1;
   if (S > cap) S = cap;
-  if (S > kMaxSplitsHost) S = kMaxSplitsHost;
+  if (S > kMaxSplits) S = kMaxSplits;
   if (S < 1) S = 1;
   return (int)S;
 }
@@ -1139,7 +1139,6 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
 // splits' maxima go to LDS once, each head's weights are formed once, and an
 // output sums only over the splits that attended to pages (in split order).
 // A NaN maximum marks a unit with a bad page id: output 0, (M, L) = (-inf, 0).
-constexpr int kMaxSplits = 128;
 
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(int H, int G, int S, const int32_t* __restrict__ seq_len,
