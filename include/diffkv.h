@@ -183,8 +183,11 @@ int diffkv_compact(const diffkv_config* cfg, const diffkv_pool* pool, int32_t mo
  * update_scores: 0 = attention only; 1 = attention, then the score update
  * (each retained token with position < seq_len[b] adds the max over the
  * group's q heads of its softmax weight to its stored score sum; pages are
- * written); 2 = attention that keeps its logits in `workspace` for a later
- * diffkv_update_scores call (needs the DIFFKV_ATTN_SCORES workspace size).
+ * written; the next generation step's plan for length seq_len[b] + 1 is
+ * left in spare bytes of the unit's first high page, where a STEP with that
+ * length and tier state uses it instead of scanning the unit); 2 = attention
+ * that keeps its logits in `workspace` for a later diffkv_update_scores call
+ * (needs the DIFFKV_ATTN_SCORES workspace size).
  * A unit whose tier_state is inconsistent, or whose table row holds a page
  * id outside [0, num_pages), gets output 0, no score update, and sets
  * DIFFKV_ST_BAD_STATE; no load leaves the pool. */
@@ -236,14 +239,19 @@ int diffkv_decode_step(const diffkv_config* cfg, const diffkv_pool* pool, int32_
 /* The score update of a preceding diffkv_decode_attn(update_scores = 2) call
  * with the same arguments and workspace (policy reading of the notes' stored
  * token scores: a running sum of received attention, max over the group's q
- * heads).  Writes the score segment of pool->pages. */
+ * heads).  Writes the score segment of pool->pages and, like update_scores
+ * = 1, the next step's plan record. */
 int diffkv_update_scores(const diffkv_config* cfg, const diffkv_pool* pool, int32_t batch,
                          const int32_t* page_table, const int32_t* tier_state,
                          const int32_t* seq_len, void* workspace, size_t workspace_bytes,
                          void* stream);
 
-/* Number of sequence splits diffkv_decode_attn uses for this config and
- * batch (host-side heuristic; the workspace size depends on it). */
+/* Number of sequence splits (workgroups per unit) diffkv_decode_attn uses
+ * for this config and batch; the workspace size depends on it.  1 when
+ * batch * H >= 256; otherwise max(ceil(256 / (batch * H)), ceil(L / 64)),
+ * at most L / 16 and 128 (L = diffkv_table_len).  A unit then takes its
+ * pages in chunks of max(ceil(pages / splits), 16), so units with many
+ * retained pages use all splits and small ones few. */
 int32_t diffkv_attn_splits(const diffkv_config* cfg, int32_t batch);
 
 #ifdef __cplusplus
