@@ -364,6 +364,25 @@ __device__ inline void codes8(const uint32_t* w, float s, float z, uint32_t* c) 
   }
 }
 
+// The codec's scale and zero (fp16 of range / (2^b - 1), fp16 of the
+// minimum) with the division by the constant 2^b - 1 done as a product with
+// its correctly rounded reciprocal and one fma correction: for every fp32
+// range in [0, 2^17] (ranges of fp16 vectors are at most 131008) the result
+// equals the IEEE quotient bit for bit (checked exhaustively on the CPU for
+// 3, 15 and 255: 0 of 3 x 1.2e9 differ).
+template <int BITS>
+__device__ inline void codec_params_c(float mn, float mx, uint16_t& s16, uint16_t& z16, float& s, float& z) {
+  constexpr float qmax = (float)((1 << BITS) - 1);
+  constexpr float rq = 1.0f / qmax;
+  const float range = __fsub_rn(mx, mn);
+  const float q0 = __fmul_rn(range, rq);
+  const float scale = __builtin_fmaf(__builtin_fmaf(-q0, qmax, range), rq, q0);
+  s16 = f2h_bits(scale);
+  z16 = f2h_bits(mn);
+  s = h2f(s16);
+  z = h2f(z16);
+}
+
 // Where a page comes from (wave-uniform).
 struct PackMeta {
   int32_t id;
@@ -473,8 +492,8 @@ __device__ inline void pack_compute(uint8_t* pg, int lane, int valid, int64_t N,
       }
       uint16_t ks16, kz16, vs16, vz16;
       float ks, kz, vs, vz;
-      codec_params(lo_h(mn), lo_h(mx), sg.kbits, ks16, kz16, ks, kz);
-      codec_params(hi_h(mn), hi_h(mx), sg.vbits, vs16, vz16, vs, vz);
+      codec_params_c<sg.kbits>(lo_h(mn), lo_h(mx), ks16, kz16, ks, kz);
+      codec_params_c<sg.vbits>(hi_h(mn), hi_h(mx), vs16, vz16, vs, vz);
       uint32_t c[8];
       codes8<sg.kbits>(kw, ks, kz, c);
       if (act) {
