@@ -279,19 +279,19 @@ constexpr float kHead = 2.0f;
 constexpr float kLazy = 4.0f;
 
 // One 16-token block in two halves.  block_logits: the block's logits
-// (masked on a partial page).  `s` holds q.c * 2^-24 for tokens
-// first..first+3 of the page; `kmw` the K metadata words of those tokens.
-// sq2 = sum(q) scale_log2 (per head).  K: s = q.c'' with c'' = c 2^-24 (high)
-// or 1 + c/16 (low), so q.c = s * 2^24 or 16 (s - sum q) and
-//   x = ks * s * kmul + (kz - kk ks) sq2,  kmul = 2^24 sl or 16 sl, kk = 0 or 16.
+// (masked on a partial page).  `s` holds q.c'' for tokens first..first+3 of
+// the page; `kmw` the K metadata words of those tokens.  sq2 = sum(q)
+// scale_log2 (per head).  K: c'' = c 2^-24 (high) or 1 + c/16 (low), so
+// q.c = 2^24 s or 16 (s - sum q) and
+//   x = ks (s kmul - cq2) + kz sq2,  kmul = 2^24 sl or 16 sl, cq2 = 0 or 16 sq2.
 __device__ inline void block_logits(const float4_t& s, const uint32_t* kmw, int first, int nval, bool partial,
-                                    float sq2, float kmul, float kk, float* x) {
+                                    float sq2, float kmul, float cq2, float* x) {
 #pragma unroll
   for (int r = 0; r < 4; r++) {
-    // log2e/sqrt(d) (s_k q.c + z_k sum(q)), with s holding q.c * 2^-24
+    // log2e/sqrt(d) (s_k q.c + z_k sum(q))
     const _Float16 ks = __builtin_bit_cast(_Float16, (uint16_t)kmw[r]);
     const _Float16 kz = __builtin_bit_cast(_Float16, (uint16_t)(kmw[r] >> 16));
-    x[r] = (float)ks * (s[r] * kmul) + ((float)kz - kk * (float)ks) * sq2;
+    x[r] = __builtin_fmaf((float)ks, __builtin_fmaf(s[r], kmul, -cq2), (float)kz * sq2);
   }
   if (partial) {
 #pragma unroll
@@ -325,28 +325,30 @@ __device__ inline void ref_check(float lm, Softmax& sm, float4_t* acc) {
 // `vpair(nb)` the fp16 V operand of 16-dim block nb.
 // V: codes c'' = 1 + c/kv (kv = 16 high, 4 low) with operand p s_v kv, so
 //   sum p s_v kv c'' = sum p s_v c + sum p s_v kv, and the z term collects
-//   p (z_v - kv s_v).
+//   p (z_v - kv s_v).  The weights come as pk = p kv = 2^(x - mk) with
+//   mk = m - log2 kv, so pk s_v is the operand, the sums take pk / kv and
+//   the z term pk (z_v / kv - s_v).
 // PACK: column i + G carries the fp16 tail of head i's weights (one matrix
-// instruction per block instead of two); `tail` marks those lanes.
+// instruction per block instead of two); tm is 1 on those lanes, else 0.
 template <int D, bool PACK, typename VOp>
-__device__ inline void block_pv(const float* x, const uint32_t* vmw, float kv, bool tail, Softmax& sm,
+__device__ inline void block_pv(const float* x, const uint32_t* vmw, float mk, float ikv, float tm, Softmax& sm,
                                 float4_t* acc, VOp vpair) {
   constexpr int NB = D / 16;
   _Float16 ph16[4], pl16[4];
 #pragma unroll
   for (int r = 0; r < 4; r++) {
-    const float p = __builtin_amdgcn_exp2f(x[r] - sm.m);
+    const float pk = __builtin_amdgcn_exp2f(x[r] - mk);
     const _Float16 vs = __builtin_bit_cast(_Float16, (uint16_t)vmw[r]);
     const _Float16 vz = __builtin_bit_cast(_Float16, (uint16_t)(vmw[r] >> 16));
-    sm.lsum += p;
-    sm.zsum += p * ((float)vz - kv * (float)vs);
-    const float pp = p * ((float)vs * kv);
+    sm.lsum = __builtin_fmaf(pk, ikv, sm.lsum);
+    sm.zsum = __builtin_fmaf(pk, __builtin_fmaf((float)vz, ikv, -(float)vs), sm.zsum);
+    const float pp = pk * (float)vs;
     ph16[r] = (_Float16)pp;
-    pl16[r] = (_Float16)(pp - (float)ph16[r]);
+    // PACK: the head on head lanes, the tail on tail lanes, without a select
+    pl16[r] = (_Float16)__builtin_fmaf((float)ph16[r], PACK ? -tm : -1.0f, pp);
   }
   if constexpr (PACK) {
-    const half4_t bt = tail ? half4_t{pl16[0], pl16[1], pl16[2], pl16[3]}
-                            : half4_t{ph16[0], ph16[1], ph16[2], ph16[3]};
+    const half4_t bt = {pl16[0], pl16[1], pl16[2], pl16[3]};
 #pragma unroll
     for (int nb = 0; nb < NB; nb++) acc[nb] = mfma16(vpair(nb), bt, acc[nb]);
   } else {
@@ -370,7 +372,7 @@ __device__ inline float max4(const float* x) { return fmaxf(fmaxf(x[0], x[1]), f
 // between their weights).
 template <int D, bool PACK, typename Keep>
 __device__ inline void compute_page(const PageRegs<D>& R, bool hi, int nval, const half8_t* qop, float sq2,
-                                    float sl, bool tail, int qg, Softmax& sm, float4_t* acc, Keep keep) {
+                                    float sl, float tm, int qg, Softmax& sm, float4_t* acc, Keep keep) {
   constexpr int NS = D / 32, KW = PageRegs<D>::KW;
   if (hi) {
     // two accumulators halve the dependent chain of the q.c products
@@ -384,7 +386,7 @@ __device__ inline void compute_page(const PageRegs<D>& R, bool hi, int nval, con
     block_logits(s0 + s1, R.km, 4 * qg, nval, nval < kHiTokens, sq2, kTwo24 * sl, 0.0f, x);
     keep(0, x);
     ref_check<D>(max4(x), sm, acc);
-    block_pv<D, PACK>(x, R.vm, 16.0f, tail, sm, acc, [&](int nb) {
+    block_pv<D, PACK>(x, R.vm, sm.m - 4.0f, 1.0f / 16.0f, tm, sm, acc, [&](int nb) {
       // block nb: pairs 2nb (tokens 0, 1) and 2nb + 1 (tokens 2, 3)
       const uint32_t w = R.v[nb >> 1];
       const int sft = 8 * (nb & 1);
@@ -403,14 +405,14 @@ __device__ inline void compute_page(const PageRegs<D>& R, bool hi, int nval, con
         s0 = mfma32(cat8(cat(nib2(w0, 0), nib2(w0, 4)), cat(nib2(w0, 8), nib2(w0, 12))), qop[ks], s0);
         s1 = mfma32(cat8(cat(nib2(w1, 0), nib2(w1, 4)), cat(nib2(w1, 8), nib2(w1, 12))), qop[ks + 1], s1);
       }
-      block_logits(s0 + s1, R.km + 4 * mb, 16 * mb + 4 * qg, nval, nval < 16 * (mb + 1), sq2, 16.0f * sl, 16.0f,
-                   x[mb]);
+      block_logits(s0 + s1, R.km + 4 * mb, 16 * mb + 4 * qg, nval, nval < 16 * (mb + 1), sq2, 16.0f * sl,
+                   16.0f * sq2, x[mb]);
       keep(mb, x[mb]);
     }
     ref_check<D>(fmaxf(max4(x[0]), max4(x[1])), sm, acc);
 #pragma unroll
     for (int mb = 0; mb < 2; mb++) {
-      block_pv<D, PACK>(x[mb], R.vm + 4 * mb, 4.0f, tail, sm, acc, [&](int nb) {
+      block_pv<D, PACK>(x[mb], R.vm + 4 * mb, sm.m - 2.0f, 0.25f, tm, sm, acc, [&](int nb) {
         // block (nb, mb): pairs P = 2M, 2M + 1 with M = 2nb + mb, in word P / 8
         const int M = 2 * nb + mb;
         const int P0 = 2 * M, P1 = 2 * M + 1;
@@ -766,6 +768,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
     sumq += __shfl_xor(sumq, 32, 64);
   }
   const float sq2 = sumq * scale_log2;
+  const float tm = tail ? 1.0f : 0.0f;
 
   Softmax sm{-INFINITY, 0.0f, 0.0f};
   float4_t acc[NB];
@@ -793,7 +796,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
       }
       // logits: LDS g-major [G][TPg * 32]; workspace [L][32][G] by table slot
       float* lgp = kLds ? lg_s + i * (TPg * 32) + j * 32 : logits + ((int64_t)u * L + table_idx(j)) * 32 * G;
-      compute_page<D, PACK>(R, j < ph, valid(j), qop, sq2, scale_log2, tail, qg, sm, acc, [&](int mb, const float* x) {
+      compute_page<D, PACK>(R, j < ph, valid(j), qop, sq2, scale_log2, tm, qg, sm, acc, [&](int mb, const float* x) {
         if (!SAVE || i >= G) return;
         const int t0 = 16 * mb + 4 * qg;
 #pragma unroll
