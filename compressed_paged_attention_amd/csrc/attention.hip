@@ -35,6 +35,7 @@
 // the score update over the unit's saved logits; with several splits the
 // partials go through a merge kernel.  No device-scope fence is used: on a
 // multi-XCD part those write back and invalidate whole L2 caches.
+#include <atomic>
 #include <type_traits>
 
 #include "dkv_common.hpp"
@@ -142,6 +143,7 @@ struct AttnWs {
   float* ml;      // [U][G][2] final (max, sum) in base 2, for the score update
   float* logits;  // [U][L][32][G] base-2 logits of every retained slot
   int32_t* cand;  // [U][ceil(L/16)][8] score-update candidates per chunk, for the next step's plan
+  int32_t* order; // [U] dispatch order: units by descending page count (more units than compute units)
 };
 
 static AttnWs attn_carve(const Cfg& c, int batch, bool scores, void* ws, size_t* bytes) {
@@ -159,6 +161,8 @@ static AttnWs attn_carve(const Cfg& c, int batch, bool scores, void* ws, size_t*
   w.cand = (int32_t*)(b + off);
   if (scores)
     off = align_up(off + (size_t)U * ((c.L + kScorePages - 1) / kScorePages) * kCandWords * sizeof(int32_t), 256);
+  w.order = (int32_t*)(b + off);
+  off = align_up(off + (size_t)U * sizeof(int32_t), 256);
   if (bytes) *bytes = off < 256 ? 256 : off;
   return w;
 }
@@ -473,13 +477,13 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
                                                         const int32_t* __restrict__ seq_len, uint8_t* pages,
                                                         float* __restrict__ out, float* __restrict__ part,
                                                         float* __restrict__ ml, float* logits, uint32_t* status,
-                                                        StepArgs sa) {
+                                                        StepArgs sa, const int32_t* __restrict__ order) {
   constexpr bool SAVE = MODE != 0;
   constexpr int NB = D / 16;  // 16-dim blocks (N-blocks of PV)
   constexpr int NS = D / 32;  // 32-dim K-steps of QK
   constexpr int QD = D / 4;   // dims per lane group
   const int split = blockIdx.x;
-  const int64_t u = blockIdx.y;
+  const int64_t u = order ? order[blockIdx.y] : blockIdx.y;  // a permutation of the units
   const int b = (int)u / H, h = (int)u % H;  // u < 2^31: 32-bit division
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar loop control
@@ -1419,6 +1423,76 @@ hipError_t launch_scores(const Cfg& c, const Pool& p, int batch, const int32_t* 
   return hipGetLastError();
 }
 
+// Dispatch order when there are more units than compute units (one
+// workgroup per unit, one resident workgroup per compute unit): the
+// hardware starts workgroups in index order as compute units free up, so
+// handing out the units with the most pages first keeps a long unit from
+// starting last (list scheduling, longest first).  A counting sort of the
+// units on ph + pl (capped); the order among equal keys is whatever the LDS
+// atomics give, which changes timing only: every unit still runs in exactly
+// one workgroup and computes the same result.
+constexpr int kOrderKeys = 4096;
+constexpr int kOrderThreads = 1024;
+
+__global__ __launch_bounds__(kOrderThreads) void unit_order_kernel(int64_t U, const int32_t* __restrict__ state,
+                                                                 int32_t* __restrict__ order) {
+  __shared__ int32_t cnt[kOrderKeys];
+  __shared__ int32_t wsum[kOrderThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  // bucket kOrderKeys - 1 - pages: the largest page counts first
+  auto bucket = [&](int64_t u) -> int {
+    const int64_t n = (int64_t)state[4 * u + 2] + state[4 * u + 3];
+    return kOrderKeys - 1 - (int)(n < 0 ? 0 : (n >= kOrderKeys ? kOrderKeys - 1 : n));
+  };
+  for (int k = tid; k < kOrderKeys; k += kOrderThreads) cnt[k] = 0;
+  __syncthreads();
+  for (int64_t u = tid; u < U; u += kOrderThreads) atomicAdd(&cnt[bucket(u)], 1);
+  __syncthreads();
+  // exclusive prefix sum over the buckets, kOrderKeys / kOrderThreads per thread
+  constexpr int KPT = kOrderKeys / kOrderThreads;
+  int v[KPT], sum = 0;
+#pragma unroll
+  for (int e = 0; e < KPT; e++) {
+    v[e] = cnt[KPT * tid + e];
+    sum += v[e];
+  }
+  int x = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wid] = x;
+  __syncthreads();
+  int ex = x - sum;
+  for (int w = 0; w < wid; w++) ex += wsum[w];
+#pragma unroll
+  for (int e = 0; e < KPT; e++) {
+    cnt[KPT * tid + e] = ex;
+    ex += v[e];
+  }
+  __syncthreads();
+  for (int64_t u = tid; u < U; u += kOrderThreads) order[atomicAdd(&cnt[bucket(u)], 1)] = (int32_t)u;
+}
+
+static int device_cus() {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+    cus[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// the order array to pass (and its kernel launched) or null
+static const int32_t* launch_order(int S, int64_t U, const int32_t* state, const AttnWs& w, hipStream_t s) {
+  const int cus = device_cus();
+  if (S != 1 || cus <= 0 || U <= cus) return nullptr;
+  unit_order_kernel<<<dim3(1), dim3(kOrderThreads), 0, s>>>(U, state, w.order);
+  return w.order;
+}
+
 hipError_t launch_attn(const Cfg& c, const Pool& p, int batch, const uint16_t* q, const int32_t* table,
                        const int32_t* state, const int32_t* seq_len, float* out, int mode, void* ws,
                        hipStream_t s) {
@@ -1434,10 +1508,11 @@ hipError_t launch_attn(const Cfg& c, const Pool& p, int batch, const uint16_t* q
   const bool pack = 2 * c.G <= 16;
   const PolicyArgs pa{c.W, c.S_max, c.lo_en, c.ah, c.al};
   const StepArgs none{};
+  const int32_t* order = launch_order(S, U, state, w, s);
 #define DKV_ATTN(D, M, PK)                                                                                 \
   attn_kernel<D, M, PK, false><<<grid, block, 0, s>>>(c.H, c.G, c.L, S, p.P, p.page_bytes, pa, scale_log2, q, \
                                                       table, state, seq_len, p.pages, out, w.part, w.ml,      \
-                                                      w.logits, p.status, none)
+                                                      w.logits, p.status, none, order)
 #define DKV_ATTN_D(D)                                    \
   if (pack) {                                            \
     if (kmode == 0) DKV_ATTN(D, 0, true);                \
@@ -1526,10 +1601,11 @@ hipError_t launch_decode_step(const Cfg& c, const Pool& p, int batch, const int3
                     can_chain ? sn.rec : nullptr,
                     can_chain ? sn.nf : nullptr,
                     can_chain ? sn.cw : nullptr};
+  const int32_t* order = launch_order(1, U, state, w, s);
 #define DKV_STEP(D, M, PK)                                                                                \
   attn_kernel<D, M, PK, true><<<grid, block, 0, s>>>(c.H, c.G, c.L, 1, p.P, p.page_bytes, pa, scale_log2, q, \
                                                      table, state, seq_len, p.pages, out, w.part, w.ml,      \
-                                                     w.logits, p.status, sa)
+                                                     w.logits, p.status, sa, order)
 #define DKV_STEP_D(D)                           \
   if (pack) {                                   \
     if (mode == 0) DKV_STEP(D, 0, true);        \

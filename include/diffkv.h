@@ -190,7 +190,10 @@ int diffkv_compact(const diffkv_config* cfg, const diffkv_pool* pool, int32_t mo
  * (needs the DIFFKV_ATTN_SCORES workspace size).
  * A unit whose tier_state is inconsistent, or whose table row holds a page
  * id outside [0, num_pages), gets output 0, no score update, and sets
- * DIFFKV_ST_BAD_STATE; no load leaves the pool. */
+ * DIFFKV_ST_BAD_STATE; no load leaves the pool.
+ * With more units than the device has compute units (one split per unit),
+ * a small kernel first sorts the units by page count into the workspace so
+ * that the longest start first; results do not depend on that order. */
 int diffkv_decode_attn(const diffkv_config* cfg, const diffkv_pool* pool, int32_t batch,
                        const uint16_t* q, const int32_t* page_table,
                        const int32_t* tier_state, const int32_t* seq_len, float* out,
