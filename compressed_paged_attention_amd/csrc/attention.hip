@@ -1142,54 +1142,49 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
 }
 
 // Split merge (several workgroups per unit): out = sum_s O_s 2^(m_s - M) /
-// sum_s l_s 2^(m_s - M); also the final (M, L) for the score update.  The
-// splits' maxima go to LDS once, each head's weights are formed once, and an
-// output sums only over the splits that attended to pages (in split order).
+// sum_s l_s 2^(m_s - M); also the final (M, L) for the score update.  One
+// workgroup per (head, unit): the splits' maxima and sums come in one pass,
+// every thread derives M and the sum from LDS (same order everywhere), and an
+// output dim is summed by 256 / D threads over interleaved attending splits
+// (loads eight at a time), then added in LDS.
 // A NaN maximum marks a unit with a bad page id: output 0, (M, L) = (-inf, 0).
 
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(int H, int G, int S, const int32_t* __restrict__ seq_len,
                                                          const float* __restrict__ part, float* __restrict__ out,
                                                          float* __restrict__ ml, int save) {
-  const int64_t u = blockIdx.x;
+  constexpr int T = 256 / D;  // threads per output dim
+  const int g = blockIdx.x;
+  const int64_t u = blockIdx.y;
   const int b = (int)u / H, h = (int)u % H;  // u < 2^31: 32-bit division
   if (seq_len[b] <= 0) return;  // the attention kernel already wrote zeros
-  const float* up = part + (u * S * G) * (D + 2);
-  float* orow = out + ((int64_t)b * H * G + (int64_t)h * G) * D;
+  const int64_t stride = (int64_t)G * (D + 2);  // from one split's head g to the next split's
+  const float* up = part + (u * S * G + g) * (D + 2);
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  __shared__ float sw[kMaxSplits * 16];  // [s][g]: maximum, then weight
-  __shared__ float sLg[16];
-  __shared__ int s_act[kMaxSplits], s_cnt[2], s_bad;
-  if (tid == 0) s_bad = 0;
-  __syncthreads();
-  for (int x = tid; x < S * G; x += blockDim.x) {
-    const float m = up[x * (D + 2) + D];
-    sw[x] = m;
-    if (m != m) s_bad = 1;
+  __shared__ float sm[kMaxSplits], sl[kMaxSplits], sw[kMaxSplits];  // maxima, sums, weights
+  __shared__ float so[256];
+  __shared__ int s_act[kMaxSplits], s_cnt[2];
+  if (tid < S) {
+    sm[tid] = up[tid * stride + D];
+    sl[tid] = up[tid * stride + D + 1];
   }
   __syncthreads();
-  if (tid < G) {
-    float M = -INFINITY;
-    for (int sp = 0; sp < S; sp++) M = fmaxf(M, sw[sp * G + tid]);
-    if (s_bad) M = -INFINITY;
-    float l = 0.0f;
-    for (int sp = 0; sp < S; sp++) {
-      const float m = sw[sp * G + tid];
-      const float w = (M == -INFINITY || m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
-      if (w != 0.0f) l += up[(sp * G + tid) * (D + 2) + D + 1] * w;
-      sw[sp * G + tid] = w;
-    }
-    sLg[tid] = l;
-    if (save) {
-      ml[(u * G + tid) * 2 + 0] = M;
-      ml[(u * G + tid) * 2 + 1] = l;
-    }
+  float M = -INFINITY;
+  bool bad = false;
+  for (int sp = 0; sp < S; sp++) {
+    const float m = sm[sp];
+    bad |= m != m;
+    M = fmaxf(M, m);
   }
-  __syncthreads();
-  // the splits with a nonzero weight for some head, in order
+  if (bad) M = -INFINITY;
   bool act = false;
-  if (tid < S)
-    for (int g = 0; g < G; g++) act |= sw[tid * G + g] != 0.0f;
+  if (tid < S) {
+    const float m = sm[tid];
+    const float w = (M == -INFINITY || m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+    sw[tid] = w;
+    act = w != 0.0f;
+  }
+  // the splits with a nonzero weight, in order
   const uint64_t mask = __ballot(act);
   if (wid < 2 && lane == 0) s_cnt[wid] = __popcll(mask);
   __syncthreads();
@@ -1197,29 +1192,42 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(int H, int G, int S, co
     const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
     s_act[(wid == 1 ? s_cnt[0] : 0) + below] = tid;
   }
+  float l = 0.0f;
+  for (int sp = 0; sp < S; sp++) {
+    const float w = sw[sp];
+    if (w != 0.0f) l += sl[sp] * w;
+  }
+  if (save && tid == 0) {
+    ml[(u * G + g) * 2 + 0] = M;
+    ml[(u * G + g) * 2 + 1] = l;
+  }
   __syncthreads();
   const int na = s_cnt[0] + (S > 64 ? s_cnt[1] : 0);
-  for (int x = tid; x < G * D; x += blockDim.x) {
-    const int g = x / D, dd = x % D;
-    float o = 0.0f;
-    int k = 0;
-    for (; k + 4 <= na; k += 4) {
-      float v[4], w[4];
+  const int dd = tid % D;
+  float o = 0.0f;
+  int k = tid / D;
+  for (; k + 7 * T < na; k += 8 * T) {
+    float v[8], w[8];
 #pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const int sp = s_act[k + e];
-        v[e] = up[(sp * G + g) * (D + 2) + dd];
-        w[e] = sw[sp * G + g];
-      }
+    for (int e = 0; e < 8; e++) {
+      const int sp = s_act[k + e * T];
+      v[e] = up[sp * stride + dd];
+      w[e] = sw[sp];
+    }
 #pragma unroll
-      for (int e = 0; e < 4; e++) o += v[e] * w[e];
-    }
-    for (; k < na; k++) {
-      const int sp = s_act[k];
-      o += up[(sp * G + g) * (D + 2) + dd] * sw[sp * G + g];
-    }
-    const float l = sLg[g];
-    orow[x] = l > 0.0f ? o / l : 0.0f;
+    for (int e = 0; e < 8; e++) o += v[e] * w[e];
+  }
+  for (; k < na; k += T) {
+    const int sp = s_act[k];
+    o += up[sp * stride + dd] * sw[sp];
+  }
+  so[tid] = o;
+  __syncthreads();
+  if (tid < D) {
+    float t = so[tid];
+#pragma unroll
+    for (int p = 1; p < T; p++) t += so[p * D + tid];
+    out[(((int64_t)b * H + h) * G + g) * D + tid] = l > 0.0f ? t / l : 0.0f;
   }
 }
 
@@ -1534,10 +1542,10 @@ hipError_t launch_attn(const Cfg& c, const Pool& p, int batch, const uint16_t* q
   if (e != hipSuccess) return e;
   if (S > 1) {
     if (c.d == 128)
-      attn_merge_kernel<128><<<dim3((unsigned)U), dim3(256), 0, s>>>(c.H, c.G, S, seq_len, w.part, out, w.ml,
+      attn_merge_kernel<128><<<dim3((unsigned)c.G, (unsigned)U), dim3(256), 0, s>>>(c.H, c.G, S, seq_len, w.part, out, w.ml,
                                                                      mode != 0);
     else
-      attn_merge_kernel<64><<<dim3((unsigned)U), dim3(256), 0, s>>>(c.H, c.G, S, seq_len, w.part, out, w.ml,
+      attn_merge_kernel<64><<<dim3((unsigned)c.G, (unsigned)U), dim3(256), 0, s>>>(c.H, c.G, S, seq_len, w.part, out, w.ml,
                                                                     mode != 0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
