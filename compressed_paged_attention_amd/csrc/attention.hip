@@ -142,7 +142,7 @@ struct AttnWs {
   float* part;    // [U][S][G][D + 2] split partials (unnormalized O, max, sum)
   float* ml;      // [U][G][2] final (max, sum) in base 2, for the score update
   float* logits;  // [U][L][32][G] base-2 logits of every retained slot
-  int32_t* cand;  // [U][ceil(L/16)][8] score-update candidates per chunk, for the next step's plan
+  int32_t* cand;  // [U][ceil(L/kScorePages)][8] score-update candidates per chunk, for the next step's plan
   int32_t* order; // [U] dispatch order: units by descending page count (more units than compute units)
 };
 
@@ -1232,7 +1232,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(int H, int G, int S, co
 }
 
 // Score update from saved logits (several splits, or a deferred update):
-// 16 pages (512 slots) per workgroup.  A unit whose merge found a bad page id
+// 16 pages (512 slots, 2 per thread) per workgroup.  A unit whose merge found a bad page id
 // has (M, L) = (-inf, 0) and is left alone; ids are checked where they are
 // used.  Each chunk also leaves the candidates the next generation step
 // (length N + 1) needs: the least important non-window high token, the least
@@ -1277,12 +1277,13 @@ __global__ __launch_bounds__(256) void score_kernel(int H, int G, int L, int64_t
   if (tid == 0) s_tc = -1;
   __syncthreads();
   const Seg sh = tier_seg(D, true), sl = tier_seg(D, false);
-  // two slots per thread, the loads of both issued before either is used
+  // SPT slots per thread, the loads of all issued before any is used
+  constexpr int SPT = kScorePages * 32 / 256;
   const int n = (p1 - p0) * 32;
-  int32_t id[2], tx[2];
-  bool ok[2];
+  int32_t id[SPT], tx[SPT];
+  bool ok[SPT];
 #pragma unroll
-  for (int e = 0; e < 2; e++) {
+  for (int e = 0; e < SPT; e++) {
     const int x = tid + 256 * e;
     const int j = p0 + min(x, n - 1) / 32, t = x % 32;
     const bool is_hi = j < ph;
@@ -1292,11 +1293,12 @@ __global__ __launch_bounds__(256) void score_kernel(int H, int G, int L, int64_t
     id[e] = row[tx[e]];
     ok[e] = x < n && t < nval;
   }
-  int32_t pos[2];
-  float old[2], mx[2] = {0.0f, 0.0f};
-  float* sc[2];
+  int32_t pos[SPT];
+  float old[SPT], mx[SPT];
+  float* sc[SPT];
 #pragma unroll
-  for (int e = 0; e < 2; e++) {
+  for (int e = 0; e < SPT; e++) {
+    mx[e] = 0.0f;
     const int x = tid + 256 * e, t = x % 32;
     const bool is_hi = p0 + min(x, n - 1) / 32 < ph;
     ok[e] = ok[e] && id[e] >= 0 && id[e] < P;
@@ -1311,7 +1313,7 @@ __global__ __launch_bounds__(256) void score_kernel(int H, int G, int L, int64_t
   __shared__ Cand cw[2][4];
   Cand bh{0.0f, kNoPos, 0}, bl{0.0f, kNoPos, 0};
 #pragma unroll
-  for (int e = 0; e < 2; e++) {
+  for (int e = 0; e < SPT; e++) {
     const int x = tid + 256 * e, t = x % 32;
     const int j = p0 + min(x, n - 1) / 32;
     const bool is_hi = j < ph;
