@@ -110,7 +110,7 @@ __device__ inline uint32_t crumb2(uint32_t w, int s) {
 // max(ceil(pages / S), kSplitMinPages), so small units use few of the S
 // workgroups and large ones all of them (retention differs widely between
 // heads); the rest exit at once.
-constexpr int kSplitPages = 64;
+constexpr int kSplitPages = 256;
 constexpr int kMaxSplits = 128;  // the merge kernel holds one weight per split and head in LDS
 constexpr int kSplitMinPages = 16;
 
@@ -1433,8 +1433,8 @@ hipError_t launch_scores(const Cfg& c, const Pool& p, int batch, const int32_t* 
   return hipGetLastError();
 }
 
-// Dispatch order when there are more units than compute units (one
-// workgroup per unit, one resident workgroup per compute unit): the
+// Dispatch order when there are more workgroups than compute units (one
+// resident attention workgroup per compute unit): the
 // hardware starts workgroups in index order as compute units free up, so
 // handing out the units with the most pages first keeps a long unit from
 // starting last (list scheduling, longest first).  A counting sort of the
@@ -1495,10 +1495,12 @@ static int device_cus() {
   return n;
 }
 
-// the order array to pass (and its kernel launched) or null
+// the order array to pass (and its kernel launched) or null: with more
+// workgroups than compute units; with several splits the units' workgroups
+// stay adjacent (split index fastest), a long unit's all early
 static const int32_t* launch_order(int S, int64_t U, const int32_t* state, const AttnWs& w, hipStream_t s) {
   const int cus = device_cus();
-  if (S != 1 || cus <= 0 || U <= cus) return nullptr;
+  if (cus <= 0 || U * S <= cus) return nullptr;
   unit_order_kernel<<<dim3(1), dim3(kOrderThreads), 0, s>>>(U, state, w.order);
   return w.order;
 }

@@ -464,6 +464,36 @@ def test_decode_step_entry(dk, orc, batch, H, update):
     check_pool_invariants(orc, p.o)
 
 
+def test_split_units_in_dispatch_order(dk, orc):
+    """Several splits per unit with more workgroups than compute units: the
+    units are dispatched longest first (and their splits side by side);
+    ragged lengths, attention with the score update and decode steps, every
+    unit against the oracle."""
+    from workloads import synth
+    cfg = _medium_cfg("llama3_8b", num_kv_heads=4, batch=12, max_seq_len=1800)
+    S = dk.diffkv_attn_splits(cfg, 12)
+    assert S > 1 and 12 * 4 * S > 256
+    g = torch.Generator().manual_seed(43)
+    lens = torch.randint(100, 1700, (12,), generator=g).to(torch.int64)
+    pr = synth.make_prompt(cfg, lens=lens)
+    cu = pr["cu_seqlens"].numpy()
+    P = int(sum(-(-int(n) // 16) for n in lens) * 4 * 1.1) + 64
+    p = Pair(dk, orc, cfg, 12, P, int(cu[-1]))
+    p.prompt(cu, pr["k"].numpy(), pr["v"].numpy(), pr["scores"].numpy())
+    seq = lens.numpy().astype(np.int32)
+    for step in range(3):
+        dec = synth.make_decode(cfg, step)
+        _say("  split units, step", step)
+        if step == 1:
+            p.decode_step(seq, dec["k_new"].numpy(), dec["v_new"].numpy(), dec["q"].numpy(), True,
+                          f"decode step {step}")
+        else:
+            p.step(seq, dec["k_new"].numpy(), dec["v_new"].numpy(), f"step {step}")
+            p.attend(dec["q"].numpy(), seq, True, f"attn {step}")
+        seq = seq + 1
+    check_pool_invariants(orc, p.o)
+
+
 def test_decode_step_deferred_scores(dk, orc):
     """diffkv_decode_step(update_scores = 2) keeps the logits for a later
     diffkv_update_scores (one split per unit, where the step otherwise runs
