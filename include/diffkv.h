@@ -191,9 +191,10 @@ int diffkv_compact(const diffkv_config* cfg, const diffkv_pool* pool, int32_t mo
  * A unit whose tier_state is inconsistent, or whose table row holds a page
  * id outside [0, num_pages), gets output 0, no score update, and sets
  * DIFFKV_ST_BAD_STATE; no load leaves the pool.
- * With more units than the device has compute units (one split per unit),
- * a small kernel first sorts the units by page count into the workspace so
- * that the longest start first; results do not depend on that order. */
+ * With more workgroups (units times splits) than the device has compute
+ * units, a small kernel first sorts the units by page count into the
+ * workspace so that the longest start first; results do not depend on that
+ * order. */
 int diffkv_decode_attn(const diffkv_config* cfg, const diffkv_pool* pool, int32_t batch,
                        const uint16_t* q, const int32_t* page_table,
                        const int32_t* tier_state, const int32_t* seq_len, float* out,
@@ -251,7 +252,7 @@ int diffkv_update_scores(const diffkv_config* cfg, const diffkv_pool* pool, int3
 
 /* Number of sequence splits (workgroups per unit) diffkv_decode_attn uses
  * for this config and batch; the workspace size depends on it.  1 when
- * batch * H >= 256; otherwise max(ceil(256 / (batch * H)), ceil(L / 64)),
+ * batch * H >= 256; otherwise max(ceil(256 / (batch * H)), ceil(L / 256)),
  * at most L / 16 and 128 (L = diffkv_table_len).  A unit then takes its
  * pages in chunks of max(ceil(pages / splits), 16), so units with many
  * retained pages use all splits and small ones few. */
