@@ -23,6 +23,9 @@ _LIB = os.path.join(_HERE, "libdiffkv_oracle.so")
 
 PRUNE, LO, HI = 0, 1, 2
 ST_POOL_EXHAUSTED, ST_TABLE_OVERFLOW, ST_BAD_STATE = 1, 2, 4
+# generation-step policy cases recorded by State.compact_step(branches=True)
+(BR_INACTIVE, BR_NO_TC, BR_HI_KEEP, BR_HI_DEMOTE, BR_HI_PRUNE, BR_LO_KEEP, BR_LO_PRUNE,
+ BR_PRUNE) = range(8)
 
 
 def build() -> str:
@@ -193,14 +196,19 @@ class State:
                                         ctypes.c_int32(cu.size - 1), _p(cu), _p(k), _p(v), _p(sc),
                                         _p(ti), _p(self.page_table), _p(self.tier_state)))
 
-    def compact_step(self, seq_len, k_new, v_new):
+    def compact_step(self, seq_len, k_new, v_new, branches: bool = False):
+        """One generation step; with branches=True returns int32 [batch, H]:
+        the policy case per unit (BR_*, bits 0-3) and the new page's tier
+        (bits 4-5)."""
         sl = np.ascontiguousarray(seq_len, dtype=np.int32)
         k = np.ascontiguousarray(k_new, dtype=np.uint16)
         v = np.ascontiguousarray(v_new, dtype=np.uint16)
         pool = self._pool()
-        _check(lib().orc_compact_step(ctypes.byref(make_cfg(self.cfg)), ctypes.byref(pool),
-                                      ctypes.c_int32(self.batch), _p(sl), _p(k), _p(v),
-                                      _p(self.page_table), _p(self.tier_state)))
+        br = np.zeros((self.batch, int(self.cfg["num_kv_heads"])), np.int32)
+        _check(lib().orc_compact_step_branches(ctypes.byref(make_cfg(self.cfg)), ctypes.byref(pool),
+                                               ctypes.c_int32(self.batch), _p(sl), _p(k), _p(v),
+                                               _p(self.page_table), _p(self.tier_state), _p(br)))
+        return br if branches else None
 
     def release(self, mask):
         m = np.ascontiguousarray(mask, dtype=np.uint8)

@@ -607,9 +607,12 @@ static uint8_t* slot_page(orc_pool* p, const int32_t* row, int32_t L, int32_t ti
   return page_at(p, row[L - 1 - slot / c->lo_page_tokens]);
 }
 
-int orc_compact_step(const orc_cfg* c, orc_pool* p, int32_t batch,
-                     const int32_t* seq_len, const uint16_t* k_new,
-                     const uint16_t* v_new, int32_t* table, int32_t* state) {
+/* branch (optional, test bookkeeping): per unit the case the plan took,
+ * ORC_BR_* in bits 0-3 and the tier of a new page (0 none) in bits 4-5. */
+static int compact_step_impl(const orc_cfg* c, orc_pool* p, int32_t batch,
+                             const int32_t* seq_len, const uint16_t* k_new,
+                             const uint16_t* v_new, int32_t* table, int32_t* state,
+                             int32_t* branch) {
   if (!cfg_valid(c) || !p || batch < 0 || c->window < 2) return ORC_E_INVALID;
   if (p->page_bytes != orc_page_bytes(c)) return ORC_E_INVALID;
   int32_t H = c->num_kv_heads, d = c->head_dim, L = orc_table_len(c), W = c->window;
@@ -640,6 +643,7 @@ int orc_compact_step(const orc_cfg* c, orc_pool* p, int32_t batch,
     int64_t tc_pos = N - W;
     P->new_hi_slot = n_hi;
     P->hi_append = 1;
+    if (branch) branch[u] = ORC_BR_NO_TC;
     if (tc_pos >= 0) {
       int32_t tc = -1;
       float tc_sum = 0;
@@ -660,6 +664,7 @@ int orc_compact_step(const orc_cfg* c, orc_pool* p, int32_t batch,
           if (v < 0 || less_important(sc, cnt, pos, vs, vc, vp)) { v = s; vs = sc; vp = pos; vc = cnt; }
         }
         int32_t vcls = classify_mean(c, vs, vc, Np);
+        if (branch) branch[u] = vcls == ORC_HI ? ORC_BR_HI_KEEP : (vcls == ORC_LO ? ORC_BR_HI_DEMOTE : ORC_BR_HI_PRUNE);
         if (vcls == ORC_LO) {
           P->lo_src_hi_slot = v;
           P->lo_slot = n_lo;
@@ -685,17 +690,21 @@ int orc_compact_step(const orc_cfg* c, orc_pool* p, int32_t batch,
         if (v >= 0 && classify_mean(c, vs, vc, Np) == ORC_PRUNE) {
           P->lo_slot = v;
           P->lo_append = 0;
+          if (branch) branch[u] = ORC_BR_LO_PRUNE;
         } else {
+          if (branch) branch[u] = ORC_BR_LO_KEEP;
           P->lo_slot = n_lo;
           P->lo_append = 1;
         }
       } else {
         P->new_hi_slot = tc;
         P->hi_append = 0;
+        if (branch) branch[u] = ORC_BR_PRUNE;
       }
     }
     if (P->hi_append && n_hi % Th == 0) P->need_page = ORC_HI;
     if (P->lo_append && n_lo % Tl == 0) P->need_page = ORC_LO;
+    if (branch) branch[u] |= P->need_page << 4;
     if (P->need_page && ph + plo + 1 > L) { st |= ORC_ST_TABLE_OVERFLOW; continue; }
     if (P->need_page) demand++;
   }
@@ -758,6 +767,21 @@ int orc_compact_step(const orc_cfg* c, orc_pool* p, int32_t batch,
   return ORC_OK;
 }
 
+int orc_compact_step(const orc_cfg* c, orc_pool* p, int32_t batch,
+                     const int32_t* seq_len, const uint16_t* k_new,
+                     const uint16_t* v_new, int32_t* table, int32_t* state) {
+  return compact_step_impl(c, p, batch, seq_len, k_new, v_new, table, state, NULL);
+}
+
+int orc_compact_step_branches(const orc_cfg* c, orc_pool* p, int32_t batch,
+                              const int32_t* seq_len, const uint16_t* k_new,
+                              const uint16_t* v_new, int32_t* table, int32_t* state,
+                              int32_t* branch) {
+  if (branch)
+    for (int64_t u = 0; u < (int64_t)batch * (c ? c->num_kv_heads : 0); u++) branch[u] = ORC_BR_INACTIVE;
+  return compact_step_impl(c, p, batch, seq_len, k_new, v_new, table, state, branch);
+}
+
 /* Release ("Memory management", generation workflow: when a request
  * completes, all its pages are reclaimed).  Units of released requests in
  * order; each unit's high pages (table left to right) then low pages (table
@@ -773,6 +797,10 @@ int orc_release(const orc_cfg* c, orc_pool* p, int32_t batch, const uint8_t* mas
     if (!mask[u / H]) continue;
     int32_t ph = state[4 * u + 2], plo = state[4 * u + 3];
     if (ph < 0 || plo < 0 || ph + plo > L) { st |= ORC_ST_BAD_STATE; continue; }
+    /* a page id outside the pool would enter the free list: refuse the call */
+    const int32_t* row = table + u * L;
+    for (int32_t j = 0; j < ph; j++) if (row[j] < 0 || row[j] >= p->num_pages) st |= ORC_ST_BAD_STATE;
+    for (int32_t j = 0; j < plo; j++) if (row[L - 1 - j] < 0 || row[L - 1 - j] >= p->num_pages) st |= ORC_ST_BAD_STATE;
     total += ph + plo;
   }
   if (!st && (int64_t)(p->ptr[1] - p->ptr[0]) + total > p->num_pages) st |= ORC_ST_BAD_STATE;

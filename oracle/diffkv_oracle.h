@@ -103,6 +103,23 @@ int orc_compact_step(const orc_cfg* c, orc_pool* p, int32_t batch,
                      const int32_t* seq_len, const uint16_t* k_new,
                      const uint16_t* v_new, int32_t* page_table,
                      int32_t* tier_state);
+/* The same step, also recording per unit which case of the generation-phase
+ * policy the plan took (bookkeeping for tests): bits 0-3 one of ORC_BR_*,
+ * bits 4-5 the tier of the unit's new page (0: none). */
+enum {
+  ORC_BR_INACTIVE = 0,  /* seq_len <= 0, or the unit was rejected */
+  ORC_BR_NO_TC = 1,     /* no token leaves the window yet (N < W) */
+  ORC_BR_HI_KEEP = 2,   /* t_c high, the least important high token stays */
+  ORC_BR_HI_DEMOTE = 3, /* t_c high, the least important high token moves to low */
+  ORC_BR_HI_PRUNE = 4,  /* t_c high, the least important high token is pruned */
+  ORC_BR_LO_KEEP = 5,   /* t_c low, no low token is pruned */
+  ORC_BR_LO_PRUNE = 6,  /* t_c low, the least important low token is pruned */
+  ORC_BR_PRUNE = 7      /* t_c pruned */
+};
+int orc_compact_step_branches(const orc_cfg* c, orc_pool* p, int32_t batch,
+                              const int32_t* seq_len, const uint16_t* k_new,
+                              const uint16_t* v_new, int32_t* page_table,
+                              int32_t* tier_state, int32_t* branch);
 int orc_release(const orc_cfg* c, orc_pool* p, int32_t batch,
                 const uint8_t* release_mask, int32_t* page_table,
                 int32_t* tier_state);

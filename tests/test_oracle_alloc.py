@@ -214,3 +214,22 @@ def test_random_prompt_release_cycles_wrap(orc):
         check_pool_invariants(orc, st)
     assert int(st.ptr[0]) > 3 * P      # the counters wrapped several times
     assert exhausted > 0
+
+
+@pytest.mark.parametrize("bad_id", [-1, 16])
+def test_release_rejects_page_ids_outside_the_pool(orc, bad_id):
+    # A table entry outside [0, P) in a released unit's used range would put
+    # a foreign id on the free list: the call sets BAD_STATE and commits
+    # nothing (other released units included).
+    cfg, N, tiers, k, v, scores = _fig6_scaled_inputs(orc)
+    st = orc.State(cfg, batch=1, num_pages=16)
+    st.compact_prompt([0, N], k, v, scores, tiers)
+    L = st.page_table.shape[-1]
+    st.page_table[0, 1, L - 1] = bad_id         # head B's first low page
+    before = st.copy()
+    st.release([1])
+    assert st.status[0] == orc.ST_BAD_STATE
+    assert np.array_equal(st.page_table, before.page_table)
+    assert np.array_equal(st.tier_state, before.tier_state)
+    assert np.array_equal(st.free_list, before.free_list)
+    assert np.array_equal(st.ptr, before.ptr)

@@ -172,3 +172,59 @@ def test_importance_from_queries(orc):
     cfg1 = dict(cfg, gqa_group=1)
     sc = orc.importance_from_queries(cfg1, [0, N], k.view(np.uint16), qp[:, :1, :H].view(np.uint16))
     assert np.allclose(sc.sum(1), 1.0, rtol=1e-6)
+
+
+def _gqa_worked_case(orc, d, seq_len_own):
+    """Five high tokens, constant keys (lossless: zero scale, zero = the
+    value): token 2 holds +1 in every dim, the others -1.  Two q heads of one
+    group: head 0 = 3 in every dim, so its logits are +-3 sqrt(d) and token 2
+    takes all its weight (the other weights are below e^-48, far under fp64
+    resolution next to 1); head 1 = 0, so its weights are exactly 1/5.  The
+    group's weight of a token is the max over the heads (DiffKV notes, "KV
+    compression policy": GQA scores combined with max): token 2 gains 1.0,
+    every other token exactly fp32(1/5).  A sum over the heads would give
+    token 2 1.2, a mean 0.6 (and the others 0.1); head 0 alone would give the
+    others 0, head 1 alone token 2 0.2."""
+    n, G = 5, 2
+    xk = np.where(np.arange(n)[:, None] == 2, 1.0, -1.0) * np.ones((n, d))
+    rng = np.random.default_rng(12)
+    xv = np.stack([_grid_token(rng, d, 8, 4)[1] for _ in range(n)])
+    cfg, st = _single_unit_state(orc, d, G, np.full(n, orc.HI, np.uint8), xk.astype(np.float32), xv)
+    q = np.zeros((1, G, d), np.float16)
+    q[0, 0] = 3.0
+    before = {r["pos"]: r["score"] for _, _, r in st.unit_tokens(0, 0)}
+    st.decode_attn(q.view(np.uint16), [seq_len_own], update_scores=True)
+    after = {r["pos"]: r["score"] for _, _, r in st.unit_tokens(0, 0)}
+    return n, before, after, q
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_score_update_max_over_group_worked_case(orc, d):
+    n, before, after, _ = _gqa_worked_case(orc, d, seq_len_own=4)
+    assert all(before[p] == 0.0 for p in range(n))
+    # token 4 is the query's own (position seq_len): unchanged
+    expect = {0: np.float32(0.2), 1: np.float32(0.2), 2: np.float32(1.0), 3: np.float32(0.2), 4: np.float32(0.0)}
+    assert {p: np.float32(after[p]) for p in range(n)} == expect
+
+
+def test_score_update_equals_numpy_max_elementwise(orc):
+    # Random keys, G = 4: each token's increment equals max over the group of
+    # the numpy softmax weights (dequantized keys, fp64), elementwise; the
+    # sum over the group is far from it.
+    rng = np.random.default_rng(8)
+    d, N, G = 64, 60, 4
+    xk = rng.standard_normal((N, d)).astype(np.float16).astype(np.float32)
+    xv = rng.standard_normal((N, d)).astype(np.float16).astype(np.float32)
+    cfg, st = _single_unit_state(orc, d, G, np.full(N, orc.HI, np.uint8), xk, xv)
+    before = {r["pos"]: r["score"] for _, _, r in st.unit_tokens(0, 0)}
+    q = rng.standard_normal((1, G, d)).astype(np.float16)
+    own = N - 1
+    st.decode_attn(q.view(np.uint16), [own], update_scores=True)
+    after = {r["pos"]: r["score"] for _, _, r in st.unit_tokens(0, 0)}
+    delta = np.array([after[p] - before[p] for p in range(N)], np.float64)
+    kh = np.stack([[orc.dequant(*r["kmeta"], int(c)) for c in r["k"]]
+                   for _, _, r in sorted(st.unit_tokens(0, 0), key=lambda e: e[2]["pos"])])
+    ps = np.stack([_np_attention(q[0, g].astype(np.float64), kh.astype(np.float64), np.zeros((N, 1)))[1]
+                   for g in range(G)])
+    assert np.allclose(delta[:own], ps.max(0)[:own], rtol=1e-6, atol=1e-7)
+    assert np.abs(delta[:own] - ps.sum(0)[:own]).max() > 1e-2
