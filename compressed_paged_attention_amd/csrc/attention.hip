@@ -71,6 +71,10 @@ __device__ inline half4_t cat(uint32_t a, uint32_t b) {
 __device__ inline half4_t u8x4(uint32_t w) {
   return cat(__builtin_amdgcn_perm(0u, w, 0x0C010C00u), __builtin_amdgcn_perm(0u, w, 0x0C030C02u));
 }
+// two fp32 values to a packed fp16 pair, rounded toward zero (one instruction)
+__device__ inline half2_t pkrtz(float a, float b) {
+  return __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
 __device__ inline half8_t cat8(half4_t a, half4_t b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
@@ -338,7 +342,7 @@ template <int D, bool PACK, typename VOp>
 __device__ inline void block_pv(const float* x, const uint32_t* vmw, float mk, float ikv, float tm, Softmax& sm,
                                 float4_t* acc, VOp vpair) {
   constexpr int NB = D / 16;
-  _Float16 ph16[4], pl16[4];
+  float pp[4];
 #pragma unroll
   for (int r = 0; r < 4; r++) {
     const float pk = __builtin_amdgcn_exp2f(x[r] - mk);
@@ -346,11 +350,27 @@ __device__ inline void block_pv(const float* x, const uint32_t* vmw, float mk, f
     const _Float16 vz = __builtin_bit_cast(_Float16, (uint16_t)(vmw[r] >> 16));
     sm.lsum = __builtin_fmaf(pk, ikv, sm.lsum);
     sm.zsum = __builtin_fmaf(pk, __builtin_fmaf((float)vz, ikv, -(float)vs), sm.zsum);
-    const float pp = pk * (float)vs;
-    ph16[r] = (_Float16)pp;
-    // PACK: the head on head lanes, the tail on tail lanes, without a select
-    pl16[r] = (_Float16)__builtin_fmaf((float)ph16[r], PACK ? -tm : -1.0f, pp);
+    pp[r] = pk * (float)vs;
+    asm("" : "+v"(pp[r]));
   }
+  // Head and tail of each weight: the head is one conversion of the fp32
+  // value (toward zero), the tail the exact remainder pp - head, converted
+  // again, so head + tail = pp within 2^-21.  The head must be a single
+  // value: when the compiler was free to round the exact product pk vs to
+  // fp16 in one use (a mixed-precision fma) and the fp32 product in another,
+  // the two heads differed by one ulp wherever the product lay within fp32
+  // rounding of an fp16 midpoint, and head + tail missed the weight by that
+  // ulp (measured: 7.5e-4 relative on a token holding 8 % of a sharp
+  // softmax).  The empty asm keeps pp an fp32 value the conversions share.
+  const half2_t h01 = pkrtz(pp[0], pp[1]);
+  const half2_t h23 = pkrtz(pp[2], pp[3]);
+  // PACK: the head on head lanes (tm = 0: pp itself, whose conversion is the
+  // head), the tail on tail lanes (tm = 1), without a select
+  const float tmv = PACK ? tm : 1.0f;
+  const half2_t t01 = pkrtz(__builtin_fmaf((float)h01[0], -tmv, pp[0]), __builtin_fmaf((float)h01[1], -tmv, pp[1]));
+  const half2_t t23 = pkrtz(__builtin_fmaf((float)h23[0], -tmv, pp[2]), __builtin_fmaf((float)h23[1], -tmv, pp[3]));
+  const _Float16 ph16[4] = {h01[0], h01[1], h23[0], h23[1]};
+  const _Float16 pl16[4] = {t01[0], t01[1], t23[0], t23[1]};
   if constexpr (PACK) {
     const half4_t bt = {pl16[0], pl16[1], pl16[2], pl16[3]};
 #pragma unroll

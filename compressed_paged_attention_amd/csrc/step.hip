@@ -349,6 +349,30 @@ size_t release_workspace(const Cfg& c, int batch) {
   return align_up(16 * sizeof(int64_t), 256) + align_up((size_t)batch * c.H * sizeof(int64_t), 256);
 }
 
+// One workgroup per unit: off[u] = 1 when a released unit's row holds a page
+// id outside the pool in its used entries (such an id would enter the free
+// list), else 0.  The plan kernel reads the flag before it overwrites off[u].
+__global__ __launch_bounds__(256) void release_check_kernel(int H, int L, int64_t P,
+                                                            const uint8_t* __restrict__ mask,
+                                                            const int32_t* __restrict__ table,
+                                                            const int32_t* __restrict__ state,
+                                                            int64_t* __restrict__ off) {
+  const int64_t u = blockIdx.x;
+  int bad = 0;
+  if (mask[u / H]) {
+    const int32_t ph = state[4 * u + 2], pl = state[4 * u + 3];
+    if (ph >= 0 && pl >= 0 && ph + pl <= L) {
+      const int32_t* row = table + u * L;
+      for (int j = threadIdx.x; j < ph + pl; j += blockDim.x) {
+        const int32_t id = j < ph ? row[j] : row[L - 1 - (j - ph)];
+        bad |= id < 0 || id >= P;
+      }
+    }
+  }
+  bad = __syncthreads_or(bad);
+  if (threadIdx.x == 0) off[u] = bad ? 1 : 0;
+}
+
 __global__ __launch_bounds__(1024) void release_plan_kernel(int H, int L, int64_t U, int64_t P,
                                                             const uint8_t* __restrict__ mask,
                                                             const int32_t* __restrict__ state,
@@ -364,7 +388,7 @@ __global__ __launch_bounds__(1024) void release_plan_kernel(int H, int L, int64_
     int64_t n = 0;
     if (u < U && mask[u / H]) {
       const int32_t ph = state[4 * u + 2], pl = state[4 * u + 3];
-      if (ph < 0 || pl < 0 || ph + pl > L) atomicOr(&sflags, kStBadState);
+      if (ph < 0 || pl < 0 || ph + pl > L || off[u] != 0) atomicOr(&sflags, kStBadState);
       else n = ph + pl;
     }
     int64_t t;
@@ -413,6 +437,7 @@ hipError_t launch_release(const Cfg& c, const Pool& p, int batch, const uint8_t*
   if (U == 0) return hipSuccess;
   int64_t* hdr = (int64_t*)ws;
   int64_t* off = (int64_t*)((uint8_t*)ws + align_up(16 * sizeof(int64_t), 256));
+  release_check_kernel<<<dim3((unsigned)U), dim3(256), 0, s>>>(c.H, c.L, p.P, mask, table, state, off);
   release_plan_kernel<<<dim3(1), dim3(1024), 0, s>>>(c.H, c.L, U, p.P, mask, state, off, hdr, p.ptr, p.status);
   release_write_kernel<<<dim3((unsigned)U), dim3(256), 0, s>>>(c.H, c.L, p.P, mask, off, hdr, p.list, table,
                                                                state);

@@ -161,7 +161,10 @@ int diffkv_classify(const diffkv_config* cfg, int32_t batch, int64_t total_token
  *   phase).  At most one new page per unit, no reclamation.
  * mode DIFFKV_RELEASE: for requests with release_mask[b] != 0, appends the
  *   unit's high pages (left to right) then low pages (right to left) at the
- *   reclamation pointer, units in order, and resets the rows.
+ *   reclamation pointer, units in order, and resets the rows.  A released
+ *   unit with an inconsistent page count, or whose used table entries hold
+ *   a page id outside [0, num_pages), sets DIFFKV_ST_BAD_STATE and the call
+ *   commits nothing.
  * Unused pointer arguments of a mode may be NULL. */
 int diffkv_compact(const diffkv_config* cfg, const diffkv_pool* pool, int32_t mode,
                    int32_t batch, int64_t total_tokens, const int64_t* cu_seqlens,

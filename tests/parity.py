@@ -107,3 +107,64 @@ def resync_scores(g, st):
     # no longer apply (the next decode step runs the plan kernel)
     g.chain = 0
     torch.cuda.synchronize()
+
+
+def _unit_pages(st):
+    """(high page ids, low page ids, first-page ids) of the oracle state's units."""
+    pt, ts = st.page_table, st.tier_state
+    L = pt.shape[-1]
+    hi, lo, first = [], [], set()
+    for b in range(pt.shape[0]):
+        for h in range(pt.shape[1]):
+            ph, pl = int(ts[b, h, 2]), int(ts[b, h, 3])
+            hi += [int(x) for x in pt[b, h, :ph]]
+            lo += [int(x) for x in pt[b, h, L - pl:]]
+            if ph:
+                first.add(int(pt[b, h, 0]))
+    return np.array(hi, np.int64), np.array(lo, np.int64), first
+
+
+def compare_pages_scores_tol(g, st, what=""):
+    """Every live page byte-identical outside its tier's score segment (and
+    the plan-record span of a unit's first page), score sums within
+    SCORE_ATOL + SCORE_RTOL |ref|.  Vectorized over pages."""
+    from oracle import tier_layout, HI, LO
+    hi, lo, first = _unit_pages(st)
+    pages = g.pool.pages.view(g.pool.num_pages, -1)
+    off, n = plan_record_span(st.cfg)
+    worst = 0.0
+    for ids, tier in ((hi, HI), (lo, LO)):
+        if ids.size == 0:
+            continue
+        _, seg = tier_layout(st.cfg, tier)
+        a = np_(pages.index_select(0, torch.from_numpy(ids).to(pages.device)))
+        b = st.pages[ids]
+        isf = np.array([int(x) in first for x in ids])
+        a[isf, off:off + n] = 0
+        keep = np.ones(a.shape[1], bool)
+        keep[seg[4]:seg[5]] = False
+        bad = np.flatnonzero(~np.all(a[:, keep] == b[:, keep], axis=1))
+        assert bad.size == 0, f"{what}: {bad.size} of {ids.size} pages differ outside the score segment, " \
+                              f"first page ids {ids[bad[:5]].tolist()}"
+        sa = np.ascontiguousarray(a[:, seg[4]:seg[5]]).view(np.float32)
+        sb = np.ascontiguousarray(b[:, seg[4]:seg[5]]).view(np.float32)
+        err = np.abs(sa.astype(np.float64) - sb)
+        tol = SCORE_ATOL + SCORE_RTOL * np.abs(sb.astype(np.float64))
+        assert np.all(err <= tol), f"{what}: score sums differ beyond tolerance (worst ratio {(err / tol).max():.2f})"
+        worst = max(worst, float((err / tol).max()))
+    return worst
+
+
+def sync_scores_to_oracle(g, st):
+    """Copy the device's score segments into the oracle's pages (the other
+    direction of resync_scores): the device's plans for the next step stay
+    valid, and both sides then decide the next step from the same sums."""
+    from oracle import tier_layout, HI, LO
+    hi, lo, _ = _unit_pages(st)
+    pages = g.pool.pages.view(g.pool.num_pages, -1)
+    for ids, tier in ((hi, HI), (lo, LO)):
+        if ids.size == 0:
+            continue
+        _, seg = tier_layout(st.cfg, tier)
+        a = np_(pages.index_select(0, torch.from_numpy(ids).to(pages.device)))
+        st.pages[ids, seg[4]:seg[5]] = a[:, seg[4]:seg[5]]

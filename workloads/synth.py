@@ -143,13 +143,15 @@ def make_prompt(cfg: dict, device="cpu", salt: int = 0, lens: torch.Tensor | Non
     return out
 
 
-def make_decode(cfg: dict, step: int, device="cpu", batch: int | None = None) -> dict:
-    """One decode step's inputs: q [B, H*G, d], k_new / v_new [B, H, d] (fp16 bits)."""
+def make_decode(cfg: dict, step: int, device="cpu", batch: int | None = None, q_scale: float = 1.0) -> dict:
+    """One decode step's inputs: q [B, H*G, d], k_new / v_new [B, H, d] (fp16 bits).
+    q_scale multiplies the query draws (a sharper softmax: a few tokens take
+    most of the weight, the rest lose importance step by step)."""
     B = cfg["batch"] if batch is None else batch
     H, G, d = cfg["num_kv_heads"], cfg["gqa_group"], cfg["head_dim"]
     g = _gen(cfg, 100 + step, device)
     sc = channel_scale(cfg, device)
-    q = _f16_bits(torch.randn(B, H * G, d, generator=g, device=device))
+    q = _f16_bits(torch.randn(B, H * G, d, generator=g, device=device) * q_scale)
     kn = _f16_bits(torch.randn(B, H, d, generator=g, device=device) * sc)
     vn = _f16_bits(torch.randn(B, H, d, generator=g, device=device) * sc)
     return dict(q=q, k_new=kn, v_new=vn)
