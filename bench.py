@@ -1,38 +1,47 @@
 #!/usr/bin/env python3
 """Benchmark of the DiffKV hot path on one MI355X.
 
-Workload: one Llama3-8B-shaped attention layer -- 32 q / 8 KV heads, d = 128,
-batch 32, 4096-token contexts, fp16 K/V ~ N(0,1) with 4 outlier channels x8
-per KV head, importance scores Zipf(1.1) with a per-unit random permutation,
-alpha_h = 1.0, alpha_l = 0.2, W = 64, a pool of 1.25x the conservative need.
+Headline workload (the largest single-GPU configuration): the high-GQA
+stress case -- 64 q / 8 KV heads (GQA 8), d = 128, batch 64, ragged contexts
+U[2000, 64000], fp16 K/V ~ N(0,1) with 4 outlier channels x8 per KV head,
+importance scores Zipf(1.1) with a per-unit random permutation, alpha_h = 1.0,
+alpha_l = 0.2, W = 64, a page pool of 200 GB.  Its working set (~630 MB per
+step) is far beyond the 256 MB Infinity Cache, so one cache replica is used.
+The Llama3-8B-shaped layer (32 q / 8 KV heads, batch 32, 4096 tokens, 8
+replicas so the Infinity Cache cannot hold the working set) is measured in
+the same run and reported under "extra".
 
 A timed step is one decode step of the whole batch on the compacted cache:
 generation-step compaction, then decode attention with the score update, as
-one diffkv_decode_step call: one kernel that commits each unit's step and
-attends over it when every unit is one workgroup.  Each replica's steps are
-chained (a step's score update plans the next one into the workspace; the
-first step of a chain runs a plan kernel first, done in the warmup).  The
-prompt side of the path (classification and prompt compaction) and the
-release are timed in the same run on the same caches and reported beside it.
-Caches rotate over several independent replicas (one per simulated layer) so
-that the 256 MB Infinity Cache cannot hold the working set.
+one diffkv_decode_step call -- with one workgroup per unit, one kernel that
+commits each unit's step and attends over it.  Each replica's steps are
+chained (a step's score update plans the next one into the workspace); every
+replica's chain is started (its first step runs the plan kernel) before the
+warmup steps, so the timed region holds chained steps only.
 
 value = batch * steps / (time of the timed region): request-tokens per second
-of complete decode steps (timed as 8 back-to-back segments; their spread is
-reported as p10/p50/p90 per step).  Three kinds of segments are timed with HIP events on the
-stream the library launches on, each over back-to-back launches while a spin
-kernel issued before the start event holds the stream (so the events measure
-the device, not the host's launch rate): the K complete steps (value), K
-attention launches alone on the final caches (attn_us, roofline), and K more
+of complete decode steps, timed as up to 8 back-to-back segments of
+near-equal length (their spread: p10/p50/p90 per step).  Three kinds of
+segments are timed with HIP events on the stream the library launches on,
+each over back-to-back launches while a spin kernel issued before the start
+event holds the stream (so the events measure the device, not the host's
+launch rate): the K chained steps (value, roofline), K attention launches
+alone on the final caches (attn_us, attention_roofline), and K more
 compaction steps alone through the separate kernels (compaction_us_per_step).
-The compaction's share of a step is (step - attention alone) / step.  The
-roofline object
-describes the attention kernel: algorithmic bytes per launch (codes +
-metadata of every retained token, q, out, table entries, and the 8-byte
-read-modify-write of each retained token's score) over its mean duration;
-stream_read_GBps is the box's achievable read rate (a reduction over 4 GiB),
-the practical ceiling beside the 8 TB/s peak.  The oracle baseline runs first
-(before the process touches the GPU), on one thread and as several processes.
+The compaction's share of a step is (step - attention alone) / step.
+
+roofline describes the dominant kernel, the fused decode step (a chained
+step is one launch of it): algorithmic bytes per launch -- codes + metadata
+of every retained token, q, out, table entries, the 8-byte read-modify-write
+of each retained token's score, and per unit the step's new K/V row, up to
+three high-precision token slots, its tier state and one table entry -- over
+the mean step time.  attention_roofline is the same for the attention
+kernel alone.  traffic is the counters' HBM bytes per launch from the
+committed profile of that workload and kernel, null when the sources changed
+since.  stream_read_GBps is the box's achievable read rate (a reduction over
+4 GiB), the practical ceiling beside the 8 TB/s peak.  The oracle baseline
+runs first (before the process touches the GPU), on one thread and as
+several processes, on a bounded sample of the headline workload.
 """
 from __future__ import annotations
 
@@ -67,7 +76,9 @@ KERNEL_SOURCES = ("compressed_paged_attention_amd/csrc/attention.hip",
                   "compressed_paged_attention_amd/csrc/dkv_common.hpp",
                   "compressed_paged_attention_amd/csrc/dkv_step.hpp",
                   "compressed_paged_attention_amd/csrc/dkv_launch.hpp")
-TRAFFIC_FILE = "profiles/attn_kernel_llama3_8b_traffic.txt"
+
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"attn_kernel_{workload}_traffic.txt")
 
 
 def kernel_source_hash():
@@ -79,22 +90,25 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per attention launch from the committed counter summary
-    (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), or None
-    when the summary is missing or the kernel sources changed since."""
-    path = os.path.join(ROOT, TRAFFIC_FILE)
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    counter summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel
+    calibration), or None when the summary is missing, covers another kernel,
+    or the kernel sources changed since it was taken."""
+    path = traffic_file(workload)
     if not os.path.exists(path):
         return None
     kv = {}
     with open(path) as fh:
         for line in fh:
-            parts = line.split()
-            if len(parts) == 2 and not line.startswith((" ", "#", "|")):
-                kv[parts[0]] = parts[1]
-    if kv.get("source_sha256") != kernel_source_hash() or "traffic_bytes_per_launch" not in kv:
+            if line.startswith(("#", " ", "|")) or ":" not in line:
+                continue
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != kernel_source_hash():
         return None
-    return float(kv["traffic_bytes_per_launch"])
+    key = "traffic_bytes_per_launch " + kernel
+    return float(kv[key]) if key in kv else None
 
 
 def stream_read_gbps(gib=4, reps=10):
@@ -143,6 +157,11 @@ def _oracle_steps(cfg, n_req, n_steps, barrier=None):
     c = dict(cfg, batch=n_req)
     lens = synth.seq_lens(c)
     pr = synth.make_prompt(c, lens=lens)
+    if "pool_bytes" in c:
+        # the workload's 200 GB pool would not fit in host memory: the
+        # sample's own need with the same headroom as the other workloads
+        c.pop("pool_bytes")
+        c["pool_factor"] = 1.25
     P = synth.pool_pages(c, lens, oracle.page_bytes(c))
     st = oracle.State(c, n_req, P)
     cu = pr["cu_seqlens"].numpy()
@@ -161,7 +180,7 @@ def _oracle_steps(cfg, n_req, n_steps, barrier=None):
         st.decode_attn(dec["q"].numpy(), seq, update_scores=True)
         seq += 1
     t_step = (time.perf_counter() - t0) / n_steps
-    return t_prompt, t_step
+    return t_prompt, t_step, int(lens.sum())
 
 
 _BARRIER = None
@@ -193,30 +212,28 @@ def cpu_model():
 
 def cpu_baseline(cfg, n_req, n_steps, workers):
     """The oracle timed on this host on a bounded sample of the same workload:
-    once on one thread, once as `workers` processes (each n_req / 4 requests
-    of its own, steps started together).  Runs before the process touches
-    the GPU (the workers are forked)."""
+    once on one thread, once as `workers` processes (each a sample of its
+    own, steps started together).  Runs before the process touches the GPU
+    (the workers are forked)."""
     import multiprocessing as mp
-    t_prompt, t_step = _oracle_steps(cfg, n_req, n_steps)
+    t_prompt, t_step, ntok = _oracle_steps(cfg, n_req, n_steps)
+    H = cfg["num_kv_heads"]
     single = dict(value=n_req / t_step, cores=1,
-                  sample=f"{n_req} of {cfg['batch']} requests ({n_req * cfg['num_kv_heads']} units, "
-                         f"{cfg['seq'][0]} tokens each): prompt compaction once "
-                         f"({t_prompt:.2f} s, not in value), then {n_steps} decode steps "
-                         f"(step compaction + fp64 attention + score update), "
-                         f"{t_step * 1e3:.1f} ms per step")
-    per = max(1, n_req // 4)
+                  sample=f"{n_req} of {cfg['batch']} requests ({n_req * H} units, {ntok} context tokens in "
+                         f"all): prompt compaction once ({t_prompt:.2f} s, not in value), then {n_steps} decode "
+                         f"steps (step compaction + fp64 attention + score update), {t_step * 1e3:.1f} ms per step")
+    per = max(1, n_req // 2)
     ctx = mp.get_context("fork")
     barrier = ctx.Barrier(workers)
     with ctx.Pool(workers, initializer=_pool_init, initargs=(barrier,)) as pool:
         res = pool.map(_oracle_worker_b, [(cfg, per, n_steps)] * workers)
-    value = sum(per / ts for _, ts in res)
+    value = sum(per / ts for _, ts, _ in res)
     return dict(value=value, unit="request-tokens/s", cores=workers, kind="oracle",
-                sample=f"{workers} processes, each {per} requests ({per * cfg['num_kv_heads']} units, "
-                       f"{cfg['seq'][0]} tokens each) through prompt compaction, then {n_steps} decode "
-                       f"steps (step compaction + fp64 attention + score update) started together; "
-                       f"value = sum of the processes' request-tokens/s",
-                single_thread=single, cpu=cpu_model(),
-                nproc=os.cpu_count())
+                sample=f"{workers} processes, each the first {per} requests of the workload ({per * H} units, "
+                       f"{res[0][2]} context tokens) through prompt compaction, then {n_steps} decode steps "
+                       f"(step compaction + fp64 attention + score update) started together; value = sum of "
+                       f"the processes' request-tokens/s",
+                single_thread=single, cpu=cpu_model(), nproc=os.cpu_count())
 
 
 def churn_schedule(args):
@@ -324,62 +341,32 @@ def churn_schedule(args):
     print(json.dumps(res), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=256)
-    ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--replicas", type=int, default=8)
-    ap.add_argument("--workload", default="llama3_8b")
-    ap.add_argument("--batch", type=int, default=0, help="override the workload's batch")
-    ap.add_argument("--context", type=int, default=0, help="override with one fixed context length")
-    ap.add_argument("--cpu-requests", type=int, default=8)
-    ap.add_argument("--cpu-steps", type=int, default=8)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-workers", type=int, default=min(16, os.cpu_count() or 1),
-                    help="oracle processes for the all-cores baseline")
-    ap.add_argument("--hold-cycles", type=int, default=100_000_000,
-                    help="spin-kernel length that holds the stream while a timed segment is enqueued")
-    ap.add_argument("--churn-schedule", action="store_true",
-                    help="run the decode-churn schedule (releases and admissions) instead; one JSON line")
-    ap.add_argument("--copy-probe-mib", type=int, default=0,
-                    help="run one elementwise copy of this size first (counter calibration)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print("bench.py: this build measures one GPU only; the path has no cross-GPU exchange "
-              "(run with --gpus 1)", file=sys.stderr)
-        sys.exit(2)
-    if args.churn_schedule:
-        churn_schedule(args)
-        return
+def step_extra_bytes(tier_state, H, d):
+    """Bytes a generation step moves per active unit beyond the attention:
+    the new token's fp16 K and V rows (4d), up to three high-precision token
+    slots (the new token written, a demoted token read and its low copy
+    written: 3 (1.5d + 16)), the tier state (16) and one table entry (4)."""
+    U = tier_state.reshape(-1, 4).shape[0]
+    return int(U * (4 * d + 3 * (1.5 * d + 16) + 16 + 4))
 
+
+def measure(args, name, R, steps, warmup, dk):
+    """Prompt side, chained decode steps, attention alone, compaction alone
+    and release of one workload on R cache replicas; returns a dict."""
     import numpy as np
     import torch
 
     from workloads import synth
 
-    # the oracle baseline first: its worker processes fork from a process
-    # that has not touched the GPU
-    cpu = None
-    if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(synth.config(args.workload), args.cpu_requests, args.cpu_steps, args.cpu_workers)
-        print("[bench] cpu baseline done", file=sys.stderr, flush=True)
-
-    import compressed_paged_attention_amd as dk
-
     dev = torch.device("cuda:0")
-    if args.copy_probe_mib > 0:
-        copy_probe(args.copy_probe_mib)
     over = {}
     if args.batch > 0:
         over["batch"] = args.batch
     if args.context > 0:
         over["seq"] = (args.context, args.context)
         over["max_seq_len"] = args.context + 256
-    cfg = synth.config(args.workload, **over)
+    cfg = synth.config(name, **over)
     B, H, G, d = cfg["batch"], cfg["num_kv_heads"], cfg["gqa_group"], cfg["head_dim"]
-    R = args.replicas
     lens = synth.seq_lens(cfg)
     P = synth.pool_pages(cfg, lens, dk.diffkv_page_bytes(cfg))
     total = int(lens.sum())
@@ -388,9 +375,10 @@ def main():
         return torch.cuda.Event(enable_timing=True)
 
     # ---- prompt side on every replica: classify + prompt compaction ----
-    reps, seqs0, prompt_ms = [], [], []
+    reps, prompt_ms = [], []
     for r in range(R):
         pr = synth.make_prompt(cfg, device=dev, salt=r, lens=lens)
+        print(f"[bench] {name} replica {r}: inputs drawn", file=sys.stderr, flush=True)
         st = dk.DiffKVState(cfg, B, P, max_total_tokens=total, device=dev)
         cu = pr["cu_seqlens"].to(dev)
         # classification has no side effects: one untimed call allocates its
@@ -409,22 +397,25 @@ def main():
         assert int(st.pool.status.item()) == 0, "prompt compaction reported a status bit"
         reps.append(st)
         del pr, tiers, counts
-        print(f"[bench] replica {r}: prompt compaction {prompt_ms[-1] * 1e3:.0f} us", file=sys.stderr,
+        print(f"[bench] {name} replica {r}: prompt compaction {prompt_ms[-1] * 1e3:.0f} us", file=sys.stderr,
               flush=True)
     torch.cuda.empty_cache()
 
-    # steps: warmup, the timed full steps, then the compaction-only segment
-    nsteps = args.warmup + 2 * args.steps
-    dec = [synth.make_decode(cfg, s, device=dev) for s in range(nsteps)]
+    # decode inputs for every step: R chain starts, warmup, timed, compaction-only
+    nsteps = R + warmup + 2 * steps
+    dec = [synth.make_decode(cfg, s % 64, device=dev) for s in range(nsteps)]
     seq_per_step = [(lens + s // R).to(torch.int32).to(dev) for s in range(nsteps)]
     out = torch.empty(B, H * G, d, dtype=torch.float32, device=dev)
     ts_before = [st.tier_state.cpu().numpy() for st in reps]
 
+    def full_step(s):
+        # compaction then attention with the score update, one library call
+        # (chained: the replica's previous step planned this one)
+        reps[s % R].decode_step(dec[s]["q"], seq_per_step[s], dec[s]["k_new"], dec[s]["v_new"],
+                                update_scores=1, out=out)
+
     def step_compact(s):
         reps[s % R].compact_step(seq_per_step[s], dec[s]["k_new"], dec[s]["v_new"])
-
-    def step_attn(s):
-        reps[s % R].decode_attn(dec[s]["q"], seq_per_step[s], update_scores=1, out=out)
 
     def timed(fn, first, count):
         """GPU time of `count` back-to-back calls.  The stream is held by a
@@ -440,105 +431,185 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1)
 
-    def full_step(s):
-        # compaction then attention with the score update, one library call
-        # (chained: the replica's previous step planned this one)
-        reps[s % R].decode_step(dec[s]["q"], seq_per_step[s], dec[s]["k_new"], dec[s]["v_new"],
-                                update_scores=1, out=out)
-
-    # warmup: the separate kernels, then one full step per replica (which
-    # starts each replica's chain of planned steps)
-    for s in range(args.warmup):
-        if s < args.warmup - R:
-            step_compact(s)
-            step_attn(s)
-        else:
-            full_step(s)
+    # every replica's chain starts here (its first step runs the plan kernel),
+    # then `warmup` chained steps
+    for s in range(R + warmup):
+        full_step(s)
     torch.cuda.synchronize()
-    print("[bench] warmup done", file=sys.stderr, flush=True)
+    assert all(st.chain > 0 for st in reps)
+    print(f"[bench] {name} warmup done", file=sys.stderr, flush=True)
 
-    # headline: K complete decode steps (compaction + attention with score
-    # update), timed as 8 back-to-back segments (their spread: p10/p50/p90)
-    nseg = 8 if args.steps % 8 == 0 else 1
-    seg_ms = [timed(full_step, args.warmup + k * (args.steps // nseg), args.steps // nseg) for k in range(nseg)]
+    # headline: `steps` chained decode steps, timed as up to 8 back-to-back
+    # segments of near-equal length (their spread: p10/p50/p90 per step)
+    nseg = max(1, min(8, steps))
+    bounds = [R + warmup + (k * steps) // nseg for k in range(nseg + 1)]
+    seg_ms = [timed(full_step, bounds[k], bounds[k + 1] - bounds[k]) for k in range(nseg)]
+    seg_us_per_step = [m * 1e3 / (bounds[k + 1] - bounds[k]) for k, m in enumerate(seg_ms)]
     total_ms = float(sum(seg_ms))
     ts_after = [st.tier_state.cpu().numpy() for st in reps]
-    # attention alone: the same K launches again on the final caches
-    last = args.warmup + args.steps - R
-    attn_ms = timed(lambda s: step_attn(last + (s % R)), 0, args.steps)
-    # compaction alone: K further generation steps
-    comp_ms = timed(step_compact, args.warmup + args.steps, args.steps)
+    # attention alone (with the score update) on the caches the steps left
+    last = R + warmup + steps - R
+    attn_ms = timed(lambda s: reps[(last + s) % R].decode_attn(dec[last + s % R]["q"], seq_per_step[last + s % R],
+                                                               update_scores=1, out=out), 0, steps)
+    # compaction alone through the separate kernels: `steps` further steps
+    comp_ms = timed(step_compact, R + warmup + steps, steps)
     status = [int(st.pool.status.item()) for st in reps]
     assert all(x == 0 for x in status), f"status bits set during the run: {status}"
-    attn = np.array([attn_ms / args.steps])
-    comp = np.array([comp_ms / args.steps])
-    print("[bench] timed steps done", file=sys.stderr, flush=True)
+    print(f"[bench] {name} timed steps done", file=sys.stderr, flush=True)
 
     # ---- release (every replica) ----
     rel_ms = []
     mask = torch.ones(B, dtype=torch.uint8, device=dev)
     for st in reps:
+        torch.cuda.synchronize()
         e0, e1 = ev(), ev()
         e0.record()
         st.release(mask)
         e1.record()
         torch.cuda.synchronize()
         rel_ms.append(e0.elapsed_time(e1))
+    del reps, dec
+    torch.cuda.empty_cache()
 
-    # the attention-only segment runs on the caches as the headline segment left them
     attn_bytes = float(np.mean([algorithmic_attn_bytes(a, B, H, G, d) for a in ts_after]))
-    t_attn_s = float(attn.mean()) * 1e-3
-    achieved = attn_bytes / t_attn_s / 1e9
+    step_bytes = attn_bytes + float(np.mean([step_extra_bytes(a, H, d) for a in ts_after]))
+    step_us = total_ms * 1e3 / steps
+    attn_us = attn_ms * 1e3 / steps
     ts = np.stack(ts_before).reshape(-1, 4).astype(np.int64)
     n_hi, n_lo = int(ts[:, 0].sum()), int(ts[:, 1].sum())
     ctx = R * total * H
-    step_ms = total_ms / args.steps
-    res = {
-        "metric": METRIC,
-        "value": B * args.steps / (total_ms * 1e-3),
-        "unit": "request-tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": step_ms,
-        "step_us_p10_p50_p90": [float(np.percentile(np.array(seg_ms) * 1e3 / (args.steps // nseg), x))
-                                for x in (10, 50, 90)],
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f16-mfma/f32",
-        "data": "synthetic",
-        "config": {"workload": WORKLOAD_NAMES.get(args.workload, args.workload), "q_heads": H * G,
-                   "kv_heads": H, "head_dim": d, "batch": B,
-                   "context": int(lens[0]) if int(lens.min()) == int(lens.max()) else
-                   [int(lens.min()), int(lens.max())],
-                   "score": "zipf(%g)" % cfg["zipf"][0] if cfg["zipf"][0] == cfg["zipf"][1] else
-                   "zipf(U[%g,%g])" % tuple(cfg["zipf"]), "alpha_h": cfg["alpha_h"],
-                   "alpha_l": cfg["alpha_l"], "window": cfg["window"], "replicas": R,
-                   "pool_pages": P, "page_bytes": dk.diffkv_page_bytes(cfg),
-                   "attn_splits": dk.diffkv_attn_splits(cfg, B)},
-        "attn_tokens_per_s": B / t_attn_s,
-        "attn_us": float(attn.mean()) * 1e3,
-        "compaction_us_per_step": float(comp.mean()) * 1e3,
+    one_split = dk.diffkv_attn_splits(cfg, B) == 1
+    pk = "true" if 2 * G <= 16 else "false"
+    step_kernel = "attn_kernel<%d, 1, %s, true>" % (d, pk) if one_split else "step + attention kernels"
+    attn_kernel = ("attn_kernel<%d, 1, %s, false>" % (d, pk)) if one_split else \
+        "attn_kernel<%d, 2, ...> + attn_merge_kernel + score_kernel" % d
+    cfg_out = {"workload": WORKLOAD_NAMES.get(name, name), "q_heads": H * G, "kv_heads": H, "head_dim": d,
+               "batch": B,
+               "context": int(lens[0]) if int(lens.min()) == int(lens.max()) else [int(lens.min()), int(lens.max())],
+               "score": "zipf(%g)" % cfg["zipf"][0] if cfg["zipf"][0] == cfg["zipf"][1] else
+               "zipf(U[%g,%g])" % tuple(cfg["zipf"]), "alpha_h": cfg["alpha_h"], "alpha_l": cfg["alpha_l"],
+               "window": cfg["window"], "lo_enabled": cfg["lo_enabled"], "replicas": R, "pool_pages": P,
+               "page_bytes": dk.diffkv_page_bytes(cfg), "attn_splits": dk.diffkv_attn_splits(cfg, B)}
+    return {
+        "cfg": cfg, "config": cfg_out, "B": B,
+        "value": B * steps / (total_ms * 1e-3),
+        "ms_per_step": step_us * 1e-3,
+        "step_us_p10_p50_p90": [float(np.percentile(seg_us_per_step, x)) for x in (10, 50, 90)],
+        "attn_us": attn_us,
+        "attn_tokens_per_s": B / (attn_us * 1e-6),
+        "compaction_us_per_step": comp_ms * 1e3 / steps,
         # the compaction's cost inside a step: the step minus attention alone
-        "step_minus_attention_us": step_ms * 1e3 - float(attn.mean()) * 1e3,
-        "compaction_share": float((step_ms - attn.mean()) / step_ms),
+        "step_minus_attention_us": step_us - attn_us,
+        "compaction_share": (step_us - attn_us) / step_us,
         "prompt_compaction_us": float(np.mean(prompt_ms)) * 1e3,
         "prompt_input_GBps": (total * H * d * 4 + total * H * 4) / (np.mean(prompt_ms) * 1e-3) / 1e9,
         "release_us": float(np.mean(rel_ms)) * 1e3,
         "retained": {"hi_frac": n_hi / ctx, "lo_frac": n_lo / ctx,
                      "kv_compression_vs_fp16": (ctx * 4 * d) / (n_hi * (1.5 * d + 16) + n_lo * (0.75 * d + 16))},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": measured_traffic() if args.workload == "llama3_8b" else None,
-                     "kernel": ("attn_kernel<%d, 1, %s, false>" % (d, "true" if 2 * G <= 16 else "false"))
-                     if dk.diffkv_attn_splits(cfg, B) == 1 else
-                     "attn_kernel<%d, 2, ...> + attn_merge_kernel + score_kernel" % d,
-                     "bytes_per_launch": int(attn_bytes),
-                     "stream_read_GBps": stream_read_gbps()},
+        "step_kernel": step_kernel, "step_bytes": step_bytes,
+        "attn_kernel": attn_kernel, "attn_bytes": attn_bytes,
     }
+
+
+def roofline(kernel, nbytes, us, workload, stream_gbps):
+    achieved = nbytes / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(workload, kernel),
+            "kernel": kernel, "bytes_per_launch": int(nbytes), "launch_us": us,
+            "stream_read_GBps": stream_gbps}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="stress_gqa8")
+    ap.add_argument("--replicas", type=int, default=0,
+                    help="cache replicas (0: 8, or 1 for the workloads with a 200 GB pool, whose working set "
+                         "is far beyond the 256 MB Infinity Cache)")
+    ap.add_argument("--extra-workload", default="llama3_8b",
+                    help="a second workload measured in the same run and reported as extra keys ('none': skip)")
+    ap.add_argument("--batch", type=int, default=0, help="override the workload's batch")
+    ap.add_argument("--context", type=int, default=0, help="override with one fixed context length")
+    ap.add_argument("--cpu-requests", type=int, default=0, help="oracle sample (0: 8, or 2 with contexts > 4096)")
+    ap.add_argument("--cpu-steps", type=int, default=0, help="oracle decode steps (0: 8, or 4 with contexts > 4096)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-workers", type=int, default=min(16, os.cpu_count() or 1),
+                    help="oracle processes for the all-cores baseline")
+    ap.add_argument("--hold-cycles", type=int, default=100_000_000,
+                    help="spin-kernel length that holds the stream while a timed segment is enqueued")
+    ap.add_argument("--churn-schedule", action="store_true",
+                    help="run the decode-churn schedule (releases and admissions) instead; one JSON line")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one elementwise copy of this size first (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only; the path has no cross-GPU exchange "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if args.churn_schedule:
+        churn_schedule(args)
+        return
+
+    from workloads import synth
+
+    def replicas_for(name):
+        if args.replicas > 0:
+            return args.replicas
+        return 1 if "pool_bytes" in synth.config(name) else 8
+
+    # the oracle baseline first: its worker processes fork from a process
+    # that has not touched the GPU
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        c0 = synth.config(args.workload)
+        short = c0["seq"][1] <= 4096
+        nreq = args.cpu_requests or (8 if short else 2)
+        cpu = cpu_baseline(c0, nreq, args.cpu_steps or (8 if short else 4), args.cpu_workers)
+        print("[bench] cpu baseline done", file=sys.stderr, flush=True)
+
+    import compressed_paged_attention_amd as dk
+
+    if args.copy_probe_mib > 0:
+        copy_probe(args.copy_probe_mib)
+    m = measure(args, args.workload, replicas_for(args.workload), args.steps, args.warmup, dk)
+    stream = stream_read_gbps()
+    res = {
+        "metric": METRIC,
+        "value": m["value"],
+        "unit": "request-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": m["ms_per_step"],
+        "step_us_p10_p50_p90": m["step_us_p10_p50_p90"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16-mfma/f32",
+        "data": "synthetic",
+        "config": m["config"],
+    }
+    for k in ("attn_tokens_per_s", "attn_us", "compaction_us_per_step", "step_minus_attention_us",
+              "compaction_share", "prompt_compaction_us", "prompt_input_GBps", "release_us", "retained"):
+        res[k] = m[k]
+    # the dominant kernel: the fused decode step (one launch per chained step)
+    res["roofline"] = roofline(m["step_kernel"], m["step_bytes"], m["ms_per_step"] * 1e3, args.workload, stream)
+    res["attention_roofline"] = roofline(m["attn_kernel"], m["attn_bytes"], m["attn_us"], args.workload, stream)
     if cpu is not None:
         res["cpu_baseline"] = cpu
+    if args.extra_workload and args.extra_workload != "none" and args.extra_workload != args.workload:
+        e = measure(args, args.extra_workload, replicas_for(args.extra_workload), args.steps, args.warmup, dk)
+        ex = {k: e[k] for k in ("value", "ms_per_step", "step_us_p10_p50_p90", "attn_us", "attn_tokens_per_s",
+                                "compaction_us_per_step", "step_minus_attention_us", "compaction_share",
+                                "prompt_compaction_us", "release_us", "retained", "config")}
+        ex["roofline"] = roofline(e["step_kernel"], e["step_bytes"], e["ms_per_step"] * 1e3, args.extra_workload,
+                                  stream)
+        ex["attention_roofline"] = roofline(e["attn_kernel"], e["attn_bytes"], e["attn_us"], args.extra_workload,
+                                            stream)
+        res["extra"] = {WORKLOAD_NAMES.get(args.extra_workload, args.extra_workload): ex}
     print(json.dumps(res), flush=True)
 
 

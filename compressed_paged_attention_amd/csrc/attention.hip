@@ -503,7 +503,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
   constexpr int NS = D / 32;  // 32-dim K-steps of QK
   constexpr int QD = D / 4;   // dims per lane group
   const int split = blockIdx.x;
-  const int64_t u = order ? order[blockIdx.y] : blockIdx.y;  // a permutation of the units
+  // a permutation of the units (clamped: a workspace overwritten between
+  // chained calls cannot send a load outside the tables)
+  const int64_t u = order ? min(max(order[blockIdx.y], 0), (int32_t)gridDim.y - 1) : blockIdx.y;
   const int b = (int)u / H, h = (int)u % H;  // u < 2^31: 32-bit division
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar loop control
@@ -1517,13 +1519,20 @@ static int device_cus() {
 
 // the order array to pass (and its kernel launched) or null: with more
 // workgroups than compute units; with several splits the units' workgroups
-// stay adjacent (split index fastest), a long unit's all early
-static const int32_t* launch_order(int S, int64_t U, const int32_t* state, const AttnWs& w, hipStream_t s) {
+// stay adjacent (split index fastest), a long unit's all early.  reuse: the
+// workspace already holds an order for these units (a chained decode step:
+// the previous call of the chain wrote it; page counts move by at most one
+// page per unit and step, and the order only affects timing).
+static const int32_t* launch_order(int S, int64_t U, const int32_t* state, const AttnWs& w, hipStream_t s,
+                                   bool reuse = false) {
   const int cus = device_cus();
   if (cus <= 0 || U * S <= cus) return nullptr;
-  unit_order_kernel<<<dim3(1), dim3(kOrderThreads), 0, s>>>(U, state, w.order);
+  if (!reuse) unit_order_kernel<<<dim3(1), dim3(kOrderThreads), 0, s>>>(U, state, w.order);
   return w.order;
 }
+
+// a chain recomputes the dispatch order at its start and every this many steps
+constexpr int kOrderRefresh = 16;
 
 hipError_t launch_attn(const Cfg& c, const Pool& p, int batch, const uint16_t* q, const int32_t* table,
                        const int32_t* state, const int32_t* seq_len, float* out, int mode, void* ws,
@@ -1633,7 +1642,7 @@ hipError_t launch_decode_step(const Cfg& c, const Pool& p, int batch, const int3
                     can_chain ? sn.rec : nullptr,
                     can_chain ? sn.nf : nullptr,
                     can_chain ? sn.cw : nullptr};
-  const int32_t* order = launch_order(1, U, state, w, s);
+  const int32_t* order = launch_order(1, U, state, w, s, chained && chain % kOrderRefresh != 0);
 #define DKV_STEP(D, M, PK)                                                                                \
   attn_kernel<D, M, PK, true><<<grid, block, 0, s>>>(c.H, c.G, c.L, 1, p.P, p.page_bytes, pa, scale_log2, q, \
                                                      table, state, seq_len, p.pages, out, w.part, w.ml,      \
