@@ -74,8 +74,10 @@ def lib() -> ctypes.CDLL:
         L.diffkv_decode_attn.argtypes = [cfgp, poolp, i32, vp, vp, vp, vp, vp, i32, vp, sz, vp]
         L.diffkv_update_scores.argtypes = [cfgp, poolp, i32, vp, vp, vp, vp, sz, vp]
         L.diffkv_decode_step.argtypes = [cfgp, poolp, i32, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, sz, vp]
+        L.diffkv_decode_attn_noalloc.argtypes = [cfgp, poolp, i32, vp, vp, vp, vp, vp, i32, vp]
         for f in ("diffkv_pool_init", "diffkv_state_init", "diffkv_classify", "diffkv_compact",
-                  "diffkv_decode_attn", "diffkv_update_scores", "diffkv_decode_step"):
+                  "diffkv_decode_attn", "diffkv_update_scores", "diffkv_decode_step",
+                  "diffkv_decode_attn_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -177,6 +179,18 @@ def diffkv_decode_attn(cfg: dict, pool: Pool, batch: int, q, page_table, tier_st
                                     int(update_scores), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(stream)),
            "diffkv_decode_attn")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def diffkv_decode_attn_noalloc(cfg: dict, pool: Pool, batch: int, q, page_table, tier_state, seq_len, out,
+                               update_scores: int, stream=None) -> int:
+    """Returns the library's code (DIFFKV_OK or an error) instead of raising,
+    so callers can see the size limit's DIFFKV_E_WORKSPACE."""
+    return lib().diffkv_decode_attn_noalloc(ctypes.byref(make_config(cfg)), ctypes.byref(pool.struct()), batch,
+                                            _ptr(q), _ptr(page_table), _ptr(tier_state), _ptr(seq_len), _ptr(out),
+                                            int(update_scores), _stream(stream))
 
 
 def diffkv_update_scores(cfg: dict, pool: Pool, batch: int, page_table, tier_state, seq_len, workspace,

@@ -10,8 +10,11 @@
  *
  * Conventions (all entry points)
  *  - Every pointer argument is DEVICE memory unless marked "host".  The
- *    caller allocates and owns every buffer; the library allocates nothing
- *    and keeps no global state, so distinct pools can be used concurrently.
+ *    caller allocates and owns every buffer; the library allocates nothing.
+ *    Its only global state is a per-device cache of the compute-unit count
+ *    (read once with hipDeviceGetAttribute) and, for
+ *    diffkv_decode_attn_noalloc, one fixed device array per GPU; distinct
+ *    pools can be used concurrently.
  *  - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
  *    kernels on it and return without synchronizing.
  *  - fp16 tensors travel as raw IEEE binary16 bits (uint16_t).
@@ -256,6 +259,26 @@ int diffkv_update_scores(const diffkv_config* cfg, const diffkv_pool* pool, int3
                          const int32_t* page_table, const int32_t* tier_state,
                          const int32_t* seq_len, void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/* Decode attention without a workspace argument, for callers that cannot
+ * allocate (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Arguments, results and errors are those of
+ * diffkv_decode_attn with update_scores 0 or 1; the scratch the call needs
+ * is a fixed array of DIFFKV_NOALLOC_SCRATCH_BYTES inside the library (one
+ * per GPU, held until the process ends; its device address is looked up
+ * once per device, on the first call with that device current).
+ *  - update_scores = 2 (logits kept for a later call) -> DIFFKV_E_INVALID.
+ *  - A call whose workspace (diffkv_workspace_bytes(DIFFKV_ATTN or
+ *    DIFFKV_ATTN_SCORES, batch)) exceeds the array -> DIFFKV_E_WORKSPACE,
+ *    nothing enqueued.
+ *  - Calls the library makes: no hipMalloc, hipFree or other allocation.
+ *  - Every call on one GPU uses the same array and leaves its contents
+ *    there: calls that overlap on one GPU (other streams, other threads)
+ *    race and must be serialized by the caller. */
+#define DIFFKV_NOALLOC_SCRATCH_BYTES (64u << 20)
+int diffkv_decode_attn_noalloc(const diffkv_config* cfg, const diffkv_pool* pool, int32_t batch,
+                               const uint16_t* q, const int32_t* page_table, const int32_t* tier_state,
+                               const int32_t* seq_len, float* out, int32_t update_scores, void* stream);
 
 /* Number of sequence splits (workgroups per unit) diffkv_decode_attn uses
  * for this config and batch; the workspace size depends on it.  1 when
