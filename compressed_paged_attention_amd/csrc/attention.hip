@@ -145,10 +145,14 @@ constexpr int kCandWords = 8;  // per chunk: least important high / low candidat
 struct AttnWs {
   float* part;    // [U][S][G][D + 2] split partials (unnormalized O, max, sum)
   float* ml;      // [U][G][2] final (max, sum) in base 2, for the score update
-  float* logits;  // [U][L][32][G] base-2 logits of every retained slot
+  float* logits;  // [U][L][32][logit_stride(G)] base-2 logits of every retained slot
   int32_t* cand;  // [U][ceil(L/kScorePages)][8] score-update candidates per chunk, for the next step's plan
   int32_t* order; // [U] dispatch order: units by descending page count (more units than compute units)
 };
+
+// Logits of one slot in the workspace: G of them, padded to a power of two
+// (4, 8 or 16 floats: one slot is one or more aligned 16-byte loads).
+__host__ __device__ constexpr int logit_stride(int G) { return G <= 4 ? 4 : (G <= 8 ? 8 : 16); }
 
 static AttnWs attn_carve(const Cfg& c, int batch, bool scores, void* ws, size_t* bytes) {
   const int64_t U = (int64_t)batch * c.H;
@@ -161,7 +165,7 @@ static AttnWs attn_carve(const Cfg& c, int batch, bool scores, void* ws, size_t*
   w.ml = (float*)(b + off);
   off = align_up(off + (size_t)U * c.G * 2 * sizeof(float), 256);
   w.logits = (float*)(b + off);
-  if (scores) off = align_up(off + (size_t)U * c.L * 32 * c.G * sizeof(float), 256);
+  if (scores) off = align_up(off + (size_t)U * c.L * 32 * logit_stride(c.G) * sizeof(float), 256);
   w.cand = (int32_t*)(b + off);
   if (scores)
     off = align_up(off + (size_t)U * ((c.L + kScorePages - 1) / kScorePages) * kCandWords * sizeof(int32_t), 256);
@@ -804,6 +808,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
   // logits go to LDS when the whole unit's fit (fused score update), else to
   // the workspace (indexed by table slot)
   const bool lg_lds = MODE == 1 && TPg * 32 * (G + 2) + TPg <= kLdsWords;
+  const bool ids_lds = MODE == 1 && !lg_lds && TPg <= kLdsWords;  // workspace logits, page ids in LDS
+  const int GS = logit_stride(G);
   float* lg_s = (float*)lds_w;
   float* osc_s = (float*)lds_w + TPg * 32 * G;
   int32_t* pos_s = (int32_t*)lds_w + TPg * 32 * (G + 1);
@@ -818,17 +824,21 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
       if (kLds) {
         if (lane < 32) osc_s[j * 32 + lane] = __uint_as_float(R.sp);
         else pos_s[j * 32 + lane - 32] = (int32_t)R.sp;
-        if (lane == 0) id_s[j] = R.id;
       }
-      // logits: LDS g-major [G][TPg * 32]; workspace [L][32][G] by table slot
-      float* lgp = kLds ? lg_s + i * (TPg * 32) + j * 32 : logits + ((int64_t)u * L + table_idx(j)) * 32 * G;
+      // the page ids the score pass visits (workspace logits: the LDS area
+      // holds only the ids)
+      if (MODE == 1 && lane == 0 && (kLds || ids_lds)) (kLds ? id_s : (int32_t*)lds_w)[j] = R.id;
+      // logits: LDS g-major [G][TPg * 32]; workspace [L][32][GS] by table
+      // slot, every lane below GS storing (lanes G..GS-1 hold finite values
+      // the score pass masks), so a slot is read with 16-byte loads
+      float* lgp = kLds ? lg_s + i * (TPg * 32) + j * 32 : logits + ((int64_t)u * L + table_idx(j)) * 32 * GS;
       compute_page<D, PACK>(R, j < ph, valid(j), qop, sq2, scale_log2, tm, qg, sm, acc, [&](int mb, const float* x) {
-        if (!SAVE || i >= G) return;
+        if (!SAVE || i >= (kLds ? G : GS)) return;
         const int t0 = 16 * mb + 4 * qg;
 #pragma unroll
         for (int r = 0; r < 4; r++) {
           if (kLds) lgp[t0 + r] = x[r];
-          else lgp[(t0 + r) * G + i] = x[r];
+          else lgp[(t0 + r) * GS + i] = x[r];
         }
       });
     };
@@ -981,21 +991,22 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
         }
       };
       // kU slots per thread per round: all loads of a round are issued
-      // before any use; GB >= G logits per slot (indices clamped to G - 1:
-      // repeats do not change a maximum)
+      // before any use; GB >= G logits per slot (LDS: indices clamped to
+      // G - 1, repeats do not change a maximum; workspace: GB = GS floats
+      // per slot, heads G..GB-1 masked by c = -inf)
       auto pass = [&](auto lds_tag, auto gb_tag) {
         constexpr bool kLds = decltype(lds_tag)::value;
         constexpr int GB = decltype(gb_tag)::value;
-        constexpr int kU = kLds ? 1 : 4;  // LDS reads need no batching
+        constexpr int kU = kLds ? 1 : 8;  // LDS reads need no batching
         // max_g 2^(x_g - M_g) / L_g = 2^(max_g (x_g + c_g)), c_g = -M_g - log2 L_g:
         // one exponential per slot
         float cg[GB];
 #pragma unroll
         for (int g = 0; g < GB; g++) {
           const float M = sM[min(g, G - 1)], I = sI[min(g, G - 1)];
-          cg[g] = (M == -INFINITY || I == 0.0f) ? -INFINITY : __builtin_amdgcn_logf(I) - M;
+          cg[g] = (M == -INFINITY || I == 0.0f || (!kLds && g >= G)) ? -INFINITY : __builtin_amdgcn_logf(I) - M;
         }
-        const float* lgg = logits + (int64_t)u * L * 32 * G;
+        const float* lgg = logits + (int64_t)u * L * 32 * GB;
         // wave-uniform trip count: a wave runs while its first slot is in range
         for (int x0 = tid; x0 - lane < NE; x0 += kU * kThreads) {
           float lv[kU][GB], osv[kU];
@@ -1015,9 +1026,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
               pgv[e] = pages + (int64_t)id_s[j] * page_bytes;
             } else {
               const int tx = table_idx(j);
+              const float4_t* src = (const float4_t*)(lgg + (tx * 32 + t) * GB);
 #pragma unroll
-              for (int g = 0; g < GB; g++) lv[e][g] = lgg[(tx * 32 + t) * G + min(g, G - 1)];
-              pgv[e] = pages + (int64_t)id_tix(tx) * page_bytes;
+              for (int c = 0; c < GB / 4; c++) {
+                const float4_t v4 = src[c];
+#pragma unroll
+                for (int k = 0; k < 4; k++) lv[e][4 * c + k] = v4[k];
+              }
+              pgv[e] = pages + (int64_t)(ids_lds ? ((const int32_t*)lds_w)[j] : id_tix(tx)) * page_bytes;
               const int tt = min(t, hi ? kHiTokens - 1 : kLoTokens - 1);
               osv[e] = *(const float*)(pgv[e] + (hi ? sh.sc : sl.sc) + 4 * tt);
               psv[e] = *(const int32_t*)(pgv[e] + (hi ? sh.ps : sl.ps) + 4 * tt);
@@ -1328,7 +1344,7 @@ __global__ __launch_bounds__(256) void score_kernel(int H, int G, int L, int64_t
     pos[e] = ok[e] ? *(const int32_t*)(pg + (is_hi ? sh.ps : sl.ps) + 4 * t) : N;
     sc[e] = (float*)(pg + (is_hi ? sh.sc : sl.sc) + 4 * t);
     old[e] = ok[e] ? *sc[e] : 0.0f;
-    const float* lg = logits + (((int64_t)u * L + tx[e]) * 32 + t) * G;
+    const float* lg = logits + (((int64_t)u * L + tx[e]) * 32 + t) * logit_stride(G);
     for (int g = 0; g < G; g++) mx[e] = fmaxf(mx[e], __builtin_amdgcn_exp2f(lg[g] - sM[g]) * sI[g]);
   }
   const int64_t N1 = (int64_t)N + 1, tc1 = N1 - W;
