@@ -299,3 +299,16 @@ def importance_from_queries(cfg: dict, cu_seqlens, k, qprobe) -> np.ndarray:
     _check(lib().orc_importance_from_queries(ctypes.byref(make_cfg(cfg)), ctypes.c_int32(cu.size - 1),
                                              _p(cu), _p(kk), ctypes.c_int32(nq), _p(qp), _p(scores)))
     return scores
+
+
+def importance_causal(cfg: dict, cu_seqlens, q, k) -> np.ndarray:
+    """Per-token mean attention received from the later tokens of its prompt
+    (causal softmax, max over the group's q heads): fp32 [H, total]."""
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+    qq = np.ascontiguousarray(q, dtype=np.uint16)
+    kk = np.ascontiguousarray(k, dtype=np.uint16)
+    H = int(cfg["num_kv_heads"])
+    scores = np.zeros((H, int(cu[-1])), np.float32)
+    _check(lib().orc_importance_causal(ctypes.byref(make_cfg(cfg)), ctypes.c_int32(cu.size - 1), _p(cu),
+                                       _p(qq), _p(kk), _p(scores)))
+    return scores

@@ -1020,3 +1020,59 @@ int orc_importance_from_queries(const orc_cfg* c, int32_t batch, const int64_t* 
   }
   return ORC_OK;
 }
+
+/* Prompt importance from the prompt's own queries ("KV compression policy",
+ * prompt phase: the importance of token i is the average of the attention
+ * scores it receives from the tokens after it; for GQA the scores of the q
+ * heads sharing the KV head are combined with max).  Causal attention: query
+ * j attends to keys 0..j, softmax over them (fp64, scale 1/sqrt(d)).  For
+ * every later query j > i the group's weight of key i is the max over the G
+ * heads of a_{j,i}; the importance is the mean over those N-1-i queries
+ * (the query's own weight a_{i,i} is excluded: the count of token i is the
+ * number of tokens after it), rounded to fp32 once; the last token (no later
+ * query) gets 0.  q: [total, H*G, d] fp16, k: [total, H, d] fp16, scores:
+ * [H, total] fp32. */
+int orc_importance_causal(const orc_cfg* c, int32_t batch, const int64_t* cu,
+                          const uint16_t* q, const uint16_t* k, float* scores) {
+  if (!cfg_valid(c) || !cu_valid(batch, cu)) return ORC_E_INVALID;
+  int32_t H = c->num_kv_heads, G = c->gqa_group, d = c->head_dim;
+  int64_t total = cu[batch];
+  double scale = 1.0 / sqrt((double)d);
+  for (int32_t r = 0; r < batch; r++) {
+    int64_t N = cu[r + 1] - cu[r];
+    if (N <= 0) continue;
+    double* acc = (double*)malloc(sizeof(double) * (size_t)N);
+    double* mx = (double*)malloc(sizeof(double) * (size_t)N);
+    double* x = (double*)malloc(sizeof(double) * (size_t)N);
+    for (int32_t h = 0; h < H; h++) {
+      for (int64_t i = 0; i < N; i++) acc[i] = 0.0;
+      for (int64_t j = 1; j < N; j++) {
+        for (int64_t i = 0; i < j; i++) mx[i] = 0.0;
+        for (int32_t g = 0; g < G; g++) {
+          const uint16_t* qr = q + ((cu[r] + j) * H * G + (int64_t)h * G + g) * d;
+          double m = -INFINITY, z = 0.0;
+          for (int64_t i = 0; i <= j; i++) {
+            const uint16_t* kr = k + ((cu[r] + i) * H + h) * d;
+            double a = 0.0;
+            for (int32_t e = 0; e < d; e++)
+              a += (double)orc_f16_to_f32(qr[e]) * (double)orc_f16_to_f32(kr[e]);
+            x[i] = a * scale;
+            if (x[i] > m) m = x[i];
+          }
+          for (int64_t i = 0; i <= j; i++) z += exp(x[i] - m);
+          for (int64_t i = 0; i < j; i++) {
+            double p = exp(x[i] - m) / z;
+            if (p > mx[i]) mx[i] = p;
+          }
+        }
+        for (int64_t i = 0; i < j; i++) acc[i] += mx[i];
+      }
+      for (int64_t i = 0; i < N; i++) {
+        int64_t cnt = N - 1 - i;
+        scores[(int64_t)h * total + cu[r] + i] = cnt > 0 ? (float)(acc[i] / (double)cnt) : 0.0f;
+      }
+    }
+    free(acc); free(mx); free(x);
+  }
+  return ORC_OK;
+}

@@ -138,6 +138,12 @@ void orc_attention_unit_vectors(const double* q, const double* k,
                                 double* out);
 /* Prompt importance from nq probe queries: per token, mean over queries of
  * the max over the G q heads of a KV head of the softmax weight. */
+/* Prompt importance from the prompt's own queries under causal attention:
+ * per token the mean over the later tokens' queries of the max over the
+ * KV head's q heads of the weight it receives.  q [total, H*G, d], k
+ * [total, H, d] fp16; scores [H, total] fp32. */
+int orc_importance_causal(const orc_cfg* c, int32_t batch, const int64_t* cu_seqlens,
+                          const uint16_t* q, const uint16_t* k, float* scores);
 int orc_importance_from_queries(const orc_cfg* c, int32_t batch,
                                 const int64_t* cu_seqlens, const uint16_t* k,
                                 int32_t nq, const uint16_t* qprobe,
