@@ -22,7 +22,8 @@ LIB_PATH = os.path.join(_HERE, "libdiffkv.so")
 
 DIFFKV_OK, DIFFKV_E_INVALID, DIFFKV_E_WORKSPACE, DIFFKV_E_HIP = 0, 1, 2, 3
 ST_POOL_EXHAUSTED, ST_TABLE_OVERFLOW, ST_BAD_STATE, ST_STALE_CHAIN = 1, 2, 4, 8
-PROMPT, STEP, RELEASE, ATTN, ATTN_SCORES, DECODE_STEP, DECODE_STEP_SCORES = 0, 1, 2, 3, 4, 5, 6
+PROMPT, STEP, RELEASE, ATTN, ATTN_SCORES, DECODE_STEP, DECODE_STEP_SCORES, IMPORTANCE = 0, 1, 2, 3, 4, 5, 6, 7
+IMP_CAUSAL, IMP_PROBE = 0, 1
 PRUNE, LO, HI = 0, 1, 2
 
 
@@ -75,9 +76,10 @@ def lib() -> ctypes.CDLL:
         L.diffkv_update_scores.argtypes = [cfgp, poolp, i32, vp, vp, vp, vp, sz, vp]
         L.diffkv_decode_step.argtypes = [cfgp, poolp, i32, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, sz, vp]
         L.diffkv_decode_attn_noalloc.argtypes = [cfgp, poolp, i32, vp, vp, vp, vp, vp, i32, vp]
+        L.diffkv_importance.argtypes = [cfgp, i32, i32, i64, vp, i32, vp, vp, vp, vp, sz, vp]
         for f in ("diffkv_pool_init", "diffkv_state_init", "diffkv_classify", "diffkv_compact",
                   "diffkv_decode_attn", "diffkv_update_scores", "diffkv_decode_step",
-                  "diffkv_decode_attn_noalloc"):
+                  "diffkv_decode_attn_noalloc", "diffkv_importance"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -179,6 +181,32 @@ def diffkv_decode_attn(cfg: dict, pool: Pool, batch: int, q, page_table, tier_st
                                     int(update_scores), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(stream)),
            "diffkv_decode_attn")
+
+
+def diffkv_importance(cfg: dict, mode: int, cu_seqlens, q, k, scores, workspace, nq: int = 0, stream=None):
+    """Prompt-phase importance (mean received attention, max over the group)
+    into scores [H, total]; q: [total, H*G, d] (IMP_CAUSAL) or
+    [batch, nq, H*G, d] (IMP_PROBE), k: [total, H, d] fp16 bits."""
+    batch = cu_seqlens.numel() - 1
+    total = int(k.shape[0])
+    _check(lib().diffkv_importance(ctypes.byref(make_config(cfg)), int(mode), batch, total, _ptr(cu_seqlens),
+                                   int(nq), _ptr(q), _ptr(k), _ptr(scores), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)),
+           "diffkv_importance")
+
+
+def importance(cfg: dict, cu_seqlens, q, k, nq: int = 0):
+    """Allocates the outputs and workspace (torch) and calls diffkv_importance:
+    causal from the prompt's own queries, or from probes when nq > 0."""
+    total = int(k.shape[0])
+    H = int(cfg["num_kv_heads"])
+    batch = cu_seqlens.numel() - 1
+    mode = IMP_PROBE if nq > 0 else IMP_CAUSAL
+    n = batch * nq if nq > 0 else total
+    ws = torch.empty(max(diffkv_workspace_bytes(cfg, IMPORTANCE, batch, n), 256), dtype=torch.uint8, device=k.device)
+    scores = torch.empty(H, total, dtype=torch.float32, device=k.device)
+    diffkv_importance(cfg, mode, cu_seqlens, q, k, scores, ws, nq=nq)
+    return scores
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20

@@ -84,6 +84,7 @@ size_t diffkv_workspace_bytes(const diffkv_config* cfg, int32_t op, int32_t batc
     case DIFFKV_DECODE_STEP_SCORES:
       return align_up(step_workspace(c, batch), 256) + align_up(attn_workspace(c, batch, true), 256) +
              step_workspace(c, batch);
+    case DIFFKV_IMPORTANCE: return importance_workspace(c, total_tokens);
     default: return 0;
   }
 }
@@ -179,6 +180,24 @@ int diffkv_decode_step(const diffkv_config* cfg, const diffkv_pool* pool, int32_
   uint8_t* w = (uint8_t*)workspace;
   return rc(launch_decode_step(c, to_pool(pool), batch, seq_len, k_new, v_new, q, page_table, tier_state, out,
                                update_scores, chain, w, w + ws_step, w + ws_step + ws_attn, (hipStream_t)stream));
+}
+
+int diffkv_importance(const diffkv_config* cfg, int32_t mode, int32_t batch, int64_t total_tokens,
+                      const int64_t* cu_seqlens, int32_t nq, const uint16_t* q, const uint16_t* k, float* scores,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (!cfg_ok(cfg) || batch < 0 || batch > 65535 || total_tokens < 0) return DIFFKV_E_INVALID;
+  if (mode != DIFFKV_IMP_CAUSAL && mode != DIFFKV_IMP_PROBE) return DIFFKV_E_INVALID;
+  if ((int64_t)cfg->num_kv_heads * cfg->gqa_group > 65535) return DIFFKV_E_INVALID;
+  if (batch > 0 && !cu_seqlens) return DIFFKV_E_INVALID;
+  if (mode == DIFFKV_IMP_PROBE && (nq < 1 || nq > 65536)) return DIFFKV_E_INVALID;
+  if (total_tokens > 0 && (!q || !k || !scores)) return DIFFKV_E_INVALID;
+  // rows are read with 16-byte loads
+  if (((uintptr_t)q | (uintptr_t)k) & 15u) return DIFFKV_E_INVALID;
+  const Cfg c = to_cfg(cfg);
+  const int64_t nqtot = mode == DIFFKV_IMP_PROBE ? (int64_t)batch * nq : total_tokens;
+  if (!ws_ok(workspace) || workspace_bytes < importance_workspace(c, nqtot)) return DIFFKV_E_WORKSPACE;
+  return rc(launch_importance(c, batch, total_tokens, cu_seqlens, mode == DIFFKV_IMP_PROBE ? 1 : 0, nq, q, k,
+                              scores, workspace, (hipStream_t)stream));
 }
 
 int diffkv_update_scores(const diffkv_config* cfg, const diffkv_pool* pool, int32_t batch, const int32_t* page_table,

@@ -68,6 +68,11 @@ hipError_t launch_decode_step(const Cfg& c, const Pool& p, int batch, const int3
                               int32_t* state, float* out, int mode, int chain, void* ws_step, void* ws_attn,
                               void* ws_next, hipStream_t s);
 
+// prompt-phase importance (nqtot: queries in all: total tokens, or batch * nq probes)
+size_t importance_workspace(const Cfg& c, int64_t nqtot);
+hipError_t launch_importance(const Cfg& c, int batch, int64_t total, const int64_t* cu, int probe, int nq,
+                             const uint16_t* q, const uint16_t* k, float* scores, void* ws, hipStream_t s);
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace dkv

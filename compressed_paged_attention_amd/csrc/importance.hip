@@ -1,0 +1,232 @@
+// importance.hip -- prompt-phase token importance on the GPU: the input of
+// classification, computed from the prompt's own queries.
+//
+// What is computed (DiffKV notes, "KV compression policy", prompt phase): the
+// importance of token i is the mean of the attention weights it receives from
+// the tokens after it; the weights of the q heads that share a KV head are
+// combined with max.  Causal attention: query j attends to keys 0..j with
+// softmax(q_j . k / sqrt(d)).  For each later query j > i the group's weight
+// of key i is max_g a^g_{j,i}; the importance is their mean over the N-1-i
+// later queries (the token's own query excluded; the last token gets 0).
+// A probe mode takes nq extra queries per request that see every token
+// (count nq) -- the recipe of the tiny workload.
+//
+// MI355X mapping.  A dense contraction (every query against every earlier
+// key), so the QK products run on the matrix units
+// (v_mfma_f32_16x16x32_f16: A = 16 queries x 32 dims, B = 32 dims x 16 keys,
+// lane l holds query rows 4(l/16)..+3 of key column l mod 16):
+//   imp_stats_kernel: per (16-query block, q head) the softmax reference and
+//     sum over the query's keys, lane-local online (each lane sees one key
+//     column per block, 64 keys per step) merged over the 16 lanes of a row
+//     once; stores c = -(max + log2 sum) in base 2, so a weight is 2^(x + c);
+//   imp_sum_kernel: per (16-key block, KV head) the keys stay in registers
+//     while the wave walks the later query blocks and the group's heads:
+//     2^(x + c) masked to later queries, max over heads, summed per key;
+//     the mean is written to scores[h][token].
+// Both kernels loop over their blocks with a grid stride, so every length is
+// covered whatever the grid.
+#include "dkv_common.hpp"
+#include "dkv_launch.hpp"
+
+namespace dkv {
+
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kImpWaves = 4;  // waves per workgroup, each one 16-row block
+constexpr float kL2e = 1.4426950408889634f;
+
+__device__ inline float4_t mfma32(half8_t a, half8_t b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// 8 fp16 of a row (16 bytes; rows are 16-byte aligned: d is a multiple of 8
+// and the tensors start 16-byte aligned), or zeros for a row out of range
+__device__ inline half8_t load8(const uint16_t* p, bool ok) {
+  if (!ok) return half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+  return __builtin_bit_cast(half8_t, *(const uint4*)p);
+}
+
+// query row pointer of query j of request r, head qh
+struct QRows {
+  const uint16_t* q;
+  int64_t base;     // causal: cu[r]; probe: r * nq
+  int64_t stride;   // H * G * D
+  __device__ const uint16_t* row(int64_t j, int qh, int D) const {
+    return q + (base + j) * stride + (int64_t)qh * D;
+  }
+};
+
+}  // namespace
+
+// stats[qh][qtok] = -(M + log2 L) in base 2 over the keys query qtok sees.
+template <int D>
+__global__ __launch_bounds__(64 * kImpWaves) void imp_stats_kernel(int H, int G, int probe, int nq,
+                                                                   const int64_t* __restrict__ cu,
+                                                                   const uint16_t* __restrict__ q,
+                                                                   const uint16_t* __restrict__ k,
+                                                                   float* __restrict__ stats, int64_t nqtot,
+                                                                   int64_t total, float scale_log2) {
+  constexpr int NS = D / 32;
+  const int r = blockIdx.z, qh = blockIdx.y, h = qh / G;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int col = lane & 15, rg = lane >> 4;
+  const int64_t c0 = cu[r];
+  const int N = (int)(cu[r + 1] - c0);
+  const int NQ = probe ? nq : N;
+  if (N <= 0 || c0 < 0 || c0 + N > total) return;  // (a malformed cu_seqlens entry: nothing read)
+  const QRows Q{q, probe ? (int64_t)r * nq : c0, (int64_t)H * G * D};
+  for (int jb = (blockIdx.x * kImpWaves + wid) * 16; jb < NQ; jb += gridDim.x * kImpWaves * 16) {
+    // A operand: query jb + col, dims 8 rg + 32 s
+    half8_t a[NS];
+    const int jq = jb + col;
+#pragma unroll
+    for (int s = 0; s < NS; s++) a[s] = load8(Q.row(min(jq, NQ - 1), qh, D) + 8 * rg + 32 * s, jq < NQ);
+    float m[4], l[4];
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+      m[t] = -INFINITY;
+      l[t] = 0.0f;
+    }
+    // keys the block's last query sees
+    const int kend = probe ? N : min(N, jb + 16);
+    for (int ib = 0; ib < kend; ib += 64) {
+      float x[4][4];  // [key block][row]
+#pragma unroll
+      for (int kb = 0; kb < 4; kb++) {
+        const int ik = ib + 16 * kb + col;
+        float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (ib + 16 * kb < kend) {
+#pragma unroll
+          for (int s = 0; s < NS; s++)
+            acc = mfma32(a[s], load8(k + ((c0 + min(ik, N - 1)) * H + h) * D + 8 * rg + 32 * s, ik < N), acc);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+          const int j = jb + 4 * rg + t;  // this lane's query rows
+          const bool ok = ik < kend && (probe || ik <= j);
+          x[kb][t] = ok ? acc[t] * scale_log2 : -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 4; t++) {
+        const float bm = fmaxf(fmaxf(x[0][t], x[1][t]), fmaxf(x[2][t], x[3][t]));
+        const float mn = fmaxf(m[t], bm);
+        if (mn != -INFINITY) {
+          float s = l[t] * __builtin_amdgcn_exp2f(m[t] - mn);
+#pragma unroll
+          for (int kb = 0; kb < 4; kb++) s += __builtin_amdgcn_exp2f(x[kb][t] - mn);
+          l[t] = s;
+          m[t] = mn;
+        }
+      }
+    }
+    // merge over the 16 key columns of a row group (lanes of one DPP row)
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+      const float M = group_reduce<16>(m[t], [](float a_, float b_) { return fmaxf(a_, b_); });
+      const float part = M == -INFINITY ? 0.0f : l[t] * __builtin_amdgcn_exp2f(m[t] - M);
+      const float L = group_reduce<16>(part, [](float a_, float b_) { return a_ + b_; });
+      const int j = jb + 4 * rg + t;
+      if (col == 0 && j < NQ)
+        stats[(int64_t)qh * nqtot + (probe ? (int64_t)r * nq : c0) + j] =
+            L > 0.0f ? -(M + __builtin_amdgcn_logf(L)) : -INFINITY;
+    }
+  }
+}
+
+// scores[h][c0 + i] = mean over the queries that count for key i of the max
+// over the group's heads of 2^(x + c).
+template <int D>
+__global__ __launch_bounds__(64 * kImpWaves) void imp_sum_kernel(int H, int G, int probe, int nq,
+                                                                 const int64_t* __restrict__ cu,
+                                                                 const uint16_t* __restrict__ q,
+                                                                 const uint16_t* __restrict__ k,
+                                                                 const float* __restrict__ stats, int64_t nqtot,
+                                                                 int64_t total, float scale_log2,
+                                                                 float* __restrict__ scores) {
+  constexpr int NS = D / 32;
+  const int r = blockIdx.z, h = blockIdx.y;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int col = lane & 15, rg = lane >> 4;
+  const int64_t c0 = cu[r];
+  const int N = (int)(cu[r + 1] - c0);
+  const int NQ = probe ? nq : N;
+  if (N <= 0 || c0 < 0 || c0 + N > total) return;  // (a malformed cu_seqlens entry: nothing read)
+  const QRows Q{q, probe ? (int64_t)r * nq : c0, (int64_t)H * G * D};
+  const int64_t sbase = probe ? (int64_t)r * nq : c0;
+  for (int ib = (blockIdx.x * kImpWaves + wid) * 16; ib < N; ib += gridDim.x * kImpWaves * 16) {
+    // B operand: key ib + col, dims 8 rg + 32 s (kept for the whole walk)
+    const int ik = ib + col;
+    half8_t kb[NS];
+#pragma unroll
+    for (int s = 0; s < NS; s++) kb[s] = load8(k + ((c0 + min(ik, N - 1)) * H + h) * D + 8 * rg + 32 * s, ik < N);
+    float sum = 0.0f;
+    // queries that can count for this block's keys: causal j > i >= ib
+    for (int jb = probe ? 0 : ib; jb < NQ; jb += 16) {
+      float pm[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      const int jq = jb + col;  // the A operand's query row for this lane
+      for (int g = 0; g < G; g++) {
+        const int qh = h * G + g;
+        float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < NS; s++)
+          acc = mfma32(load8(Q.row(min(jq, NQ - 1), qh, D) + 8 * rg + 32 * s, jq < NQ), kb[s], acc);
+        // the references of this lane's four query rows
+        const int j0 = jb + 4 * rg;
+        const float* sp = stats + (int64_t)qh * nqtot + sbase;
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+          const int j = j0 + t;
+          const bool ok = j < NQ && ik < N && (probe || j > ik);
+          const float cv = sp[min(j, NQ - 1)];  // in bounds whatever ok is
+          const float c = ok ? cv : -INFINITY;
+          pm[t] = fmaxf(pm[t], ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(acc[t], scale_log2, c)) : 0.0f);
+        }
+      }
+      sum += (pm[0] + pm[1]) + (pm[2] + pm[3]);
+    }
+    // the four row groups of a key column: lanes col, col + 16, col + 32, col + 48
+    sum += lane_xchg_t<4>(sum);
+    sum += lane_xchg_t<5>(sum);
+    if (rg == 0 && ik < N) {
+      const int cnt = probe ? nq : N - 1 - ik;
+      scores[(int64_t)h * total + c0 + ik] = cnt > 0 ? sum / (float)cnt : 0.0f;
+    }
+  }
+}
+
+size_t importance_workspace(const Cfg& c, int64_t nqtot) {
+  return align_up((size_t)c.H * c.G * (size_t)(nqtot > 0 ? nqtot : 1) * sizeof(float), 256);
+}
+
+hipError_t launch_importance(const Cfg& c, int batch, int64_t total, const int64_t* cu, int probe, int nq,
+                             const uint16_t* q, const uint16_t* k, float* scores, void* ws, hipStream_t s) {
+  if (batch == 0 || total == 0) return hipSuccess;
+  const int64_t nqtot = probe ? (int64_t)batch * nq : total;
+  float* stats = (float*)ws;
+  const float scale_log2 = (1.0f / sqrtf((float)c.d)) * kL2e;
+  // blocks of 64 rows per workgroup; lengths up to max_seq_len in one pass
+  // (longer ones by the kernels' grid-stride loops)
+  const int64_t rows = probe ? nq : (c.S_max < total ? c.S_max : total);
+  const unsigned gx = (unsigned)((rows + 16 * kImpWaves - 1) / (16 * kImpWaves));
+  const int64_t keys = c.S_max < total ? c.S_max : total;
+  const unsigned kx = (unsigned)((keys + 16 * kImpWaves - 1) / (16 * kImpWaves));
+  const dim3 block(64 * kImpWaves);
+  if (c.d == 128) {
+    imp_stats_kernel<128><<<dim3(gx, c.H * c.G, batch), block, 0, s>>>(c.H, c.G, probe, nq, cu, q, k, stats, nqtot,
+                                                                      total, scale_log2);
+    imp_sum_kernel<128><<<dim3(kx, c.H, batch), block, 0, s>>>(c.H, c.G, probe, nq, cu, q, k, stats, nqtot, total,
+                                                               scale_log2, scores);
+  } else {
+    imp_stats_kernel<64><<<dim3(gx, c.H * c.G, batch), block, 0, s>>>(c.H, c.G, probe, nq, cu, q, k, stats, nqtot,
+                                                                     total, scale_log2);
+    imp_sum_kernel<64><<<dim3(kx, c.H, batch), block, 0, s>>>(c.H, c.G, probe, nq, cu, q, k, stats, nqtot, total,
+                                                              scale_log2, scores);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dkv

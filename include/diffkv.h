@@ -92,8 +92,10 @@ enum {
   DIFFKV_ATTN = 3,
   DIFFKV_ATTN_SCORES = 4,
   DIFFKV_DECODE_STEP = 5,        /* diffkv_decode_step, update_scores = 0 */
-  DIFFKV_DECODE_STEP_SCORES = 6  /* diffkv_decode_step, update_scores = 1 or 2 */
+  DIFFKV_DECODE_STEP_SCORES = 6, /* diffkv_decode_step, update_scores = 1 or 2 */
+  DIFFKV_IMPORTANCE = 7          /* diffkv_importance; total_tokens = queries in all (see there) */
 };
+enum { DIFFKV_IMP_CAUSAL = 0, DIFFKV_IMP_PROBE = 1 };
 
 /* Bytes of one unified page (six segments, "Memory management"): 3584 at
  * d = 128, 2048 at d = 64; -1 for an invalid config. */
@@ -120,6 +122,32 @@ int diffkv_pool_init(const diffkv_config* cfg, const diffkv_pool* pool, void* st
  * tier_state [batch, H, 4] = 0. */
 int diffkv_state_init(const diffkv_config* cfg, int32_t batch, int32_t* page_table,
                       int32_t* tier_state, void* stream);
+
+/* Prompt-phase token importance, the input of diffkv_classify ("KV
+ * compression policy", prompt phase: a token's importance is the mean of the
+ * attention weights it receives from the tokens after it; the weights of the
+ * q heads sharing a KV head are combined with max).
+ *  mode DIFFKV_IMP_CAUSAL: q fp16 [total_tokens, H*G, d] holds the prompt's
+ *    own queries (token-major, as a prefill produces them).  Query j of a
+ *    request attends causally to its keys 0..j (softmax of q.k/sqrt(d));
+ *    token i's importance is the mean over the N-1-i later queries j > i of
+ *    max over the group of its weight; the last token gets 0.
+ *  mode DIFFKV_IMP_PROBE: q fp16 [batch, nq, H*G, d] holds nq probe queries
+ *    per request that attend to all N tokens; importance = the mean over the
+ *    nq probes of max over the group of the weight.
+ *  cu_seqlens int64 [batch+1] (device), k fp16 [total_tokens, H, d]; q and k
+ *    16-byte aligned, else DIFFKV_E_INVALID.
+ *  scores fp32 [H, total_tokens] out: the mean per token, as diffkv_classify
+ *    and diffkv_compact(PROMPT) take it.
+ *  workspace: diffkv_workspace_bytes(cfg, DIFFKV_IMPORTANCE, batch, n) with
+ *    n = total_tokens (causal) or batch * nq (probe): one fp32 softmax
+ *    reference per query and q head.
+ * Work is quadratic in the prompt length (causal); computed in fp32 on the
+ * matrix units from the fp16 inputs (within 1e-4 relative of the fp64
+ * definition on the tested inputs). */
+int diffkv_importance(const diffkv_config* cfg, int32_t mode, int32_t batch, int64_t total_tokens,
+                      const int64_t* cu_seqlens, int32_t nq, const uint16_t* q, const uint16_t* k,
+                      float* scores, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Token classification ("Approach"; "KV compression policy", prompt phase).
  *  cu_seqlens  int64 [batch+1], cu[0] = 0, non-decreasing; N_r = cu[r+1]-cu[r]

@@ -301,14 +301,15 @@ def importance_from_queries(cfg: dict, cu_seqlens, k, qprobe) -> np.ndarray:
     return scores
 
 
-def importance_causal(cfg: dict, cu_seqlens, q, k) -> np.ndarray:
+def importance_causal(cfg: dict, cu_seqlens, q, k, tail: int = 0) -> np.ndarray:
     """Per-token mean attention received from the later tokens of its prompt
-    (causal softmax, max over the group's q heads): fp32 [H, total]."""
+    (causal softmax, max over the group's q heads): fp32 [H, total].  tail > 0:
+    only the last `tail` tokens of each request (the others stay 0)."""
     cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
     qq = np.ascontiguousarray(q, dtype=np.uint16)
     kk = np.ascontiguousarray(k, dtype=np.uint16)
     H = int(cfg["num_kv_heads"])
     scores = np.zeros((H, int(cu[-1])), np.float32)
-    _check(lib().orc_importance_causal(ctypes.byref(make_cfg(cfg)), ctypes.c_int32(cu.size - 1), _p(cu),
-                                       _p(qq), _p(kk), _p(scores)))
+    _check(lib().orc_importance_causal_tail(ctypes.byref(make_cfg(cfg)), ctypes.c_int32(cu.size - 1), _p(cu),
+                                            _p(qq), _p(kk), ctypes.c_int64(tail), _p(scores)))
     return scores

@@ -1032,47 +1032,67 @@ int orc_importance_from_queries(const orc_cfg* c, int32_t batch, const int64_t* 
  * number of tokens after it), rounded to fp32 once; the last token (no later
  * query) gets 0.  q: [total, H*G, d] fp16, k: [total, H, d] fp16, scores:
  * [H, total] fp32. */
-int orc_importance_causal(const orc_cfg* c, int32_t batch, const int64_t* cu,
-                          const uint16_t* q, const uint16_t* k, float* scores) {
-  if (!cfg_valid(c) || !cu_valid(batch, cu)) return ORC_E_INVALID;
+/* tail > 0: only the last `tail` tokens of each request get a value (the
+ * sampled outputs of a long prompt: they need only the queries after them);
+ * the other scores are left as they are. */
+static int importance_causal_impl(const orc_cfg* c, int32_t batch, const int64_t* cu,
+                                  const uint16_t* q, const uint16_t* k, int64_t tail, float* scores) {
+  if (!cfg_valid(c) || !cu_valid(batch, cu) || tail < 0) return ORC_E_INVALID;
   int32_t H = c->num_kv_heads, G = c->gqa_group, d = c->head_dim;
   int64_t total = cu[batch];
   double scale = 1.0 / sqrt((double)d);
+  double qd[128];
   for (int32_t r = 0; r < batch; r++) {
     int64_t N = cu[r + 1] - cu[r];
     if (N <= 0) continue;
+    int64_t first = (tail > 0 && tail < N) ? N - tail : 0; /* tokens first..N-1 get a value */
     double* acc = (double*)malloc(sizeof(double) * (size_t)N);
     double* mx = (double*)malloc(sizeof(double) * (size_t)N);
     double* x = (double*)malloc(sizeof(double) * (size_t)N);
+    double* kd = (double*)malloc(sizeof(double) * (size_t)N * d);
     for (int32_t h = 0; h < H; h++) {
-      for (int64_t i = 0; i < N; i++) acc[i] = 0.0;
-      for (int64_t j = 1; j < N; j++) {
-        for (int64_t i = 0; i < j; i++) mx[i] = 0.0;
+      for (int64_t i = 0; i < N; i++) {
+        acc[i] = 0.0;
+        const uint16_t* kr = k + ((cu[r] + i) * H + h) * d;
+        for (int32_t e = 0; e < d; e++) kd[i * d + e] = (double)orc_f16_to_f32(kr[e]);
+      }
+      /* only the queries after a token count for it */
+      for (int64_t j = first + 1; j < N; j++) {
+        for (int64_t i = first; i < j; i++) mx[i] = 0.0;
         for (int32_t g = 0; g < G; g++) {
           const uint16_t* qr = q + ((cu[r] + j) * H * G + (int64_t)h * G + g) * d;
+          for (int32_t e = 0; e < d; e++) qd[e] = (double)orc_f16_to_f32(qr[e]);
           double m = -INFINITY, z = 0.0;
           for (int64_t i = 0; i <= j; i++) {
-            const uint16_t* kr = k + ((cu[r] + i) * H + h) * d;
             double a = 0.0;
-            for (int32_t e = 0; e < d; e++)
-              a += (double)orc_f16_to_f32(qr[e]) * (double)orc_f16_to_f32(kr[e]);
+            for (int32_t e = 0; e < d; e++) a += qd[e] * kd[i * d + e];
             x[i] = a * scale;
             if (x[i] > m) m = x[i];
           }
           for (int64_t i = 0; i <= j; i++) z += exp(x[i] - m);
-          for (int64_t i = 0; i < j; i++) {
+          for (int64_t i = first; i < j; i++) {
             double p = exp(x[i] - m) / z;
             if (p > mx[i]) mx[i] = p;
           }
         }
-        for (int64_t i = 0; i < j; i++) acc[i] += mx[i];
+        for (int64_t i = first; i < j; i++) acc[i] += mx[i];
       }
-      for (int64_t i = 0; i < N; i++) {
+      for (int64_t i = first; i < N; i++) {
         int64_t cnt = N - 1 - i;
         scores[(int64_t)h * total + cu[r] + i] = cnt > 0 ? (float)(acc[i] / (double)cnt) : 0.0f;
       }
     }
-    free(acc); free(mx); free(x);
+    free(acc); free(mx); free(x); free(kd);
   }
   return ORC_OK;
+}
+
+int orc_importance_causal(const orc_cfg* c, int32_t batch, const int64_t* cu,
+                          const uint16_t* q, const uint16_t* k, float* scores) {
+  return importance_causal_impl(c, batch, cu, q, k, 0, scores);
+}
+
+int orc_importance_causal_tail(const orc_cfg* c, int32_t batch, const int64_t* cu,
+                               const uint16_t* q, const uint16_t* k, int64_t tail, float* scores) {
+  return importance_causal_impl(c, batch, cu, q, k, tail, scores);
 }

@@ -144,6 +144,10 @@ void orc_attention_unit_vectors(const double* q, const double* k,
  * [total, H, d] fp16; scores [H, total] fp32. */
 int orc_importance_causal(const orc_cfg* c, int32_t batch, const int64_t* cu_seqlens,
                           const uint16_t* q, const uint16_t* k, float* scores);
+/* The same for the last `tail` tokens of each request only (the others'
+ * scores are left as they are): sampled outputs of long prompts. */
+int orc_importance_causal_tail(const orc_cfg* c, int32_t batch, const int64_t* cu_seqlens,
+                               const uint16_t* q, const uint16_t* k, int64_t tail, float* scores);
 int orc_importance_from_queries(const orc_cfg* c, int32_t batch,
                                 const int64_t* cu_seqlens, const uint16_t* k,
                                 int32_t nq, const uint16_t* qprobe,

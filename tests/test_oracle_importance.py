@@ -109,3 +109,21 @@ def test_equals_decode_score_updates_over_growing_prefixes(orc):
             got[rec["pos"]] += rec["score"]
     cnt = N - 1 - np.arange(N)
     assert np.allclose(got[:-1], imp[:-1].astype(np.float64) * cnt[:-1], rtol=2e-6)
+
+
+def test_tail_equals_full_on_the_tail(orc):
+    # the sampled variant gives the last tokens exactly the full values
+    rng = np.random.default_rng(4)
+    d, H, G = 64, 2, 2
+    lens = [50, 9, 33]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q = rng.standard_normal((cu[-1], H * G, d)).astype(np.float16).view(np.uint16)
+    k = rng.standard_normal((cu[-1], H, d)).astype(np.float16).view(np.uint16)
+    cfg = _cfg(d, H, G, 64)
+    full = orc.importance_causal(cfg, cu, q, k)
+    part = orc.importance_causal(cfg, cu, q, k, tail=12)
+    for r, n in enumerate(lens):
+        a, b = cu[r], cu[r + 1]
+        t = min(12, n)
+        assert np.array_equal(part[:, b - t:b], full[:, b - t:b])
+        assert np.all(part[:, a:b - t] == 0.0)
