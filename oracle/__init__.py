@@ -313,3 +313,14 @@ def importance_causal(cfg: dict, cu_seqlens, q, k, tail: int = 0) -> np.ndarray:
     _check(lib().orc_importance_causal_tail(ctypes.byref(make_cfg(cfg)), ctypes.c_int32(cu.size - 1), _p(cu),
                                             _p(qq), _p(kk), ctypes.c_int64(tail), _p(scores)))
     return scores
+
+
+def keydiff_scores(cfg: dict, cu_seqlens, k, anchor_raw: bool = False) -> np.ndarray:
+    """Query-free importance from the keys alone (anchor cosine): fp32 [H, total]."""
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+    kk = np.ascontiguousarray(k, dtype=np.uint16)
+    H = int(cfg["num_kv_heads"])
+    scores = np.zeros((H, int(cu[-1])), np.float32)
+    _check(lib().orc_keydiff_scores(ctypes.byref(make_cfg(cfg)), ctypes.c_int32(cu.size - 1), _p(cu), _p(kk),
+                                    ctypes.c_int32(1 if anchor_raw else 0), _p(scores)))
+    return scores

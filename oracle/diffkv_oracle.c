@@ -1096,3 +1096,63 @@ int orc_importance_causal_tail(const orc_cfg* c, int32_t batch, const int64_t* c
                                const uint16_t* q, const uint16_t* k, int64_t tail, float* scores) {
   return importance_causal_impl(c, batch, cu, q, k, tail, scores);
 }
+
+/* Query-free importance, KeyDiff page ("方法细节", efficient variant): the
+ * anchor is the mean of the unit's keys, normalized to unit length
+ * (anchor_raw = 0, the method's anchor) or as they are (anchor_raw = 1, the
+ * page's reported simplification); a key's eviction score is its cosine
+ * similarity to the anchor, the least similar keys being the ones to keep.
+ * Reading taken to feed the alpha/N classification: importance
+ * w_i = 1 - cos(anchor, k_i) normalized over the unit's tokens,
+ * s_i = w_i / sum_j w_j (a distribution over the tokens like the mean
+ * attention, uniform 1/N when every key is parallel to the anchor); a zero
+ * key or a zero anchor has cosine 0.  fp64, rounded to fp32 once.
+ * k [total, H, d] fp16; scores [H, total] fp32. */
+int orc_keydiff_scores(const orc_cfg* c, int32_t batch, const int64_t* cu, const uint16_t* k,
+                       int32_t anchor_raw, float* scores) {
+  if (!cfg_valid(c) || !cu_valid(batch, cu)) return ORC_E_INVALID;
+  int32_t H = c->num_kv_heads, d = c->head_dim;
+  int64_t total = cu[batch];
+  double mu[128], x[128];
+  for (int32_t r = 0; r < batch; r++) {
+    int64_t N = cu[r + 1] - cu[r];
+    if (N <= 0) continue;
+    double* w = (double*)malloc(sizeof(double) * (size_t)N);
+    for (int32_t h = 0; h < H; h++) {
+      for (int32_t e = 0; e < d; e++) mu[e] = 0.0;
+      for (int64_t i = 0; i < N; i++) {
+        const uint16_t* kr = k + ((cu[r] + i) * H + h) * d;
+        double nn = 0.0;
+        for (int32_t e = 0; e < d; e++) {
+          x[e] = (double)orc_f16_to_f32(kr[e]);
+          nn += x[e] * x[e];
+        }
+        double inv = anchor_raw ? 1.0 : (nn > 0.0 ? 1.0 / sqrt(nn) : 0.0);
+        for (int32_t e = 0; e < d; e++) mu[e] += x[e] * inv;
+      }
+      double mn = 0.0;
+      for (int32_t e = 0; e < d; e++) {
+        mu[e] /= (double)N;
+        mn += mu[e] * mu[e];
+      }
+      mn = sqrt(mn);
+      double sw = 0.0;
+      for (int64_t i = 0; i < N; i++) {
+        const uint16_t* kr = k + ((cu[r] + i) * H + h) * d;
+        double dot = 0.0, nn = 0.0;
+        for (int32_t e = 0; e < d; e++) {
+          double v = (double)orc_f16_to_f32(kr[e]);
+          dot += v * mu[e];
+          nn += v * v;
+        }
+        double cs = (nn > 0.0 && mn > 0.0) ? dot / (sqrt(nn) * mn) : 0.0;
+        w[i] = 1.0 - cs;
+        sw += w[i];
+      }
+      for (int64_t i = 0; i < N; i++)
+        scores[(int64_t)h * total + cu[r] + i] = (float)(sw > 0.0 ? w[i] / sw : 1.0 / (double)N);
+    }
+    free(w);
+  }
+  return ORC_OK;
+}

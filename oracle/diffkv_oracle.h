@@ -148,6 +148,11 @@ int orc_importance_causal(const orc_cfg* c, int32_t batch, const int64_t* cu_seq
  * scores are left as they are): sampled outputs of long prompts. */
 int orc_importance_causal_tail(const orc_cfg* c, int32_t batch, const int64_t* cu_seqlens,
                                const uint16_t* q, const uint16_t* k, int64_t tail, float* scores);
+/* Query-free importance (KeyDiff anchor cosine): w_i = 1 - cos(anchor, k_i),
+ * the anchor the mean of the unit's normalized keys (anchor_raw = 0) or raw
+ * keys (1); scores = w normalized over the unit's tokens. */
+int orc_keydiff_scores(const orc_cfg* c, int32_t batch, const int64_t* cu_seqlens,
+                       const uint16_t* k, int32_t anchor_raw, float* scores);
 int orc_importance_from_queries(const orc_cfg* c, int32_t batch,
                                 const int64_t* cu_seqlens, const uint16_t* k,
                                 int32_t nq, const uint16_t* qprobe,
