@@ -511,6 +511,52 @@ def measure(args, name, R, steps, warmup, dk):
     }
 
 
+PEAK_FP16_MFMA_TFLOPS = 2500.0
+
+
+def importance_timing(args, name, dk):
+    """Prompt-side importance (diffkv_importance, causal: every prompt query
+    against its earlier keys, twice -- softmax statistics, then the column
+    means) on the workload's prompt shape with seeded N(0,1) queries; one
+    warmup call, then one call timed with HIP events on a held stream.
+    Algorithmic flops: 2 passes x 2d per (query, key <= query) pair and q
+    head; bound by the fp16 matrix peak."""
+    import torch
+
+    from workloads import synth
+    dev = torch.device("cuda:0")
+    cfg = synth.config(name)
+    H, G, d = cfg["num_kv_heads"], cfg["gqa_group"], cfg["head_dim"]
+    lens = synth.seq_lens(cfg)
+    pr = synth.make_prompt(cfg, device=dev, lens=lens)
+    gq = torch.Generator(device=dev)
+    gq.manual_seed(synth.SEED_BASE + 999)
+    q = torch.randn(int(lens.sum()), H * G, d, generator=gq, device=dev).to(torch.float16).view(torch.int16)
+    cu = pr["cu_seqlens"].to(dev)
+    total = int(lens.sum())
+    ws = torch.empty(dk.diffkv_workspace_bytes(cfg, dk.IMPORTANCE, cfg["batch"], total), dtype=torch.uint8,
+                     device=dev)
+    scores = torch.empty(H, total, dtype=torch.float32, device=dev)
+    dk.diffkv_importance(cfg, dk.IMP_CAUSAL, cu, q, pr["k"], scores, ws)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(args.hold_cycles)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    dk.diffkv_importance(cfg, dk.IMP_CAUSAL, cu, q, pr["k"], scores, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3
+    pairs = sum(int(n) * (int(n) + 1) // 2 for n in lens.tolist())
+    flops = 2 * 2 * d * pairs * H * G
+    del pr, q, ws, scores
+    torch.cuda.empty_cache()
+    tf = flops / (us * 1e-6) / 1e12
+    return {"workload": WORKLOAD_NAMES.get(name, name), "us": us, "tokens": total,
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tf / PEAK_FP16_MFMA_TFLOPS, "flops_per_launch": flops,
+                         "kernel": "imp_stats_kernel + imp_sum_kernel"}}
+
+
 def roofline(kernel, nbytes, us, workload, stream_gbps):
     achieved = nbytes / (us * 1e-6) / 1e9
     return {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -610,6 +656,7 @@ def main():
         ex["attention_roofline"] = roofline(e["attn_kernel"], e["attn_bytes"], e["attn_us"], args.extra_workload,
                                             stream)
         res["extra"] = {WORKLOAD_NAMES.get(args.extra_workload, args.extra_workload): ex}
+        res["extra"]["prompt_importance"] = importance_timing(args, args.extra_workload, dk)
     print(json.dumps(res), flush=True)
 
 

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libdiffkv.so")
 
 DIFFKV_OK, DIFFKV_E_INVALID, DIFFKV_E_WORKSPACE, DIFFKV_E_HIP = 0, 1, 2, 3
 ST_POOL_EXHAUSTED, ST_TABLE_OVERFLOW, ST_BAD_STATE, ST_STALE_CHAIN = 1, 2, 4, 8
-PROMPT, STEP, RELEASE, ATTN, ATTN_SCORES, DECODE_STEP, DECODE_STEP_SCORES, IMPORTANCE = 0, 1, 2, 3, 4, 5, 6, 7
+PROMPT, STEP, RELEASE, ATTN, ATTN_SCORES, DECODE_STEP, DECODE_STEP_SCORES, IMPORTANCE, KEYDIFF = range(9)
 IMP_CAUSAL, IMP_PROBE = 0, 1
 PRUNE, LO, HI = 0, 1, 2
 
@@ -77,9 +77,10 @@ def lib() -> ctypes.CDLL:
         L.diffkv_decode_step.argtypes = [cfgp, poolp, i32, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, sz, vp]
         L.diffkv_decode_attn_noalloc.argtypes = [cfgp, poolp, i32, vp, vp, vp, vp, vp, i32, vp]
         L.diffkv_importance.argtypes = [cfgp, i32, i32, i64, vp, i32, vp, vp, vp, vp, sz, vp]
+        L.diffkv_keydiff_scores.argtypes = [cfgp, i32, i64, vp, vp, i32, vp, vp, sz, vp]
         for f in ("diffkv_pool_init", "diffkv_state_init", "diffkv_classify", "diffkv_compact",
                   "diffkv_decode_attn", "diffkv_update_scores", "diffkv_decode_step",
-                  "diffkv_decode_attn_noalloc", "diffkv_importance"):
+                  "diffkv_decode_attn_noalloc", "diffkv_importance", "diffkv_keydiff_scores"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -206,6 +207,19 @@ def importance(cfg: dict, cu_seqlens, q, k, nq: int = 0):
     ws = torch.empty(max(diffkv_workspace_bytes(cfg, IMPORTANCE, batch, n), 256), dtype=torch.uint8, device=k.device)
     scores = torch.empty(H, total, dtype=torch.float32, device=k.device)
     diffkv_importance(cfg, mode, cu_seqlens, q, k, scores, ws, nq=nq)
+    return scores
+
+
+def keydiff_scores(cfg: dict, cu_seqlens, k, anchor_raw: bool = False):
+    """Query-free importance from the keys (diffkv_keydiff_scores): allocates
+    the outputs and workspace (torch); fp32 [H, total]."""
+    total = int(k.shape[0])
+    batch = cu_seqlens.numel() - 1
+    ws = torch.empty(diffkv_workspace_bytes(cfg, KEYDIFF, batch, total), dtype=torch.uint8, device=k.device)
+    scores = torch.empty(int(cfg["num_kv_heads"]), total, dtype=torch.float32, device=k.device)
+    _check(lib().diffkv_keydiff_scores(ctypes.byref(make_config(cfg)), batch, total, _ptr(cu_seqlens), _ptr(k),
+                                       1 if anchor_raw else 0, _ptr(scores), _ptr(ws),
+                                       ws.numel() * ws.element_size(), _stream(None)), "diffkv_keydiff_scores")
     return scores
 
 

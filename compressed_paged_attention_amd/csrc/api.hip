@@ -85,6 +85,7 @@ size_t diffkv_workspace_bytes(const diffkv_config* cfg, int32_t op, int32_t batc
       return align_up(step_workspace(c, batch), 256) + align_up(attn_workspace(c, batch, true), 256) +
              step_workspace(c, batch);
     case DIFFKV_IMPORTANCE: return importance_workspace(c, total_tokens);
+    case DIFFKV_KEYDIFF: return keydiff_workspace(c, batch, total_tokens);
     default: return 0;
   }
 }
@@ -198,6 +199,20 @@ int diffkv_importance(const diffkv_config* cfg, int32_t mode, int32_t batch, int
   if (!ws_ok(workspace) || workspace_bytes < importance_workspace(c, nqtot)) return DIFFKV_E_WORKSPACE;
   return rc(launch_importance(c, batch, total_tokens, cu_seqlens, mode == DIFFKV_IMP_PROBE ? 1 : 0, nq, q, k,
                               scores, workspace, (hipStream_t)stream));
+}
+
+int diffkv_keydiff_scores(const diffkv_config* cfg, int32_t batch, int64_t total_tokens, const int64_t* cu_seqlens,
+                          const uint16_t* k, int32_t anchor_raw, float* scores, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!cfg_ok(cfg) || batch < 0 || batch > 65535 || total_tokens < 0) return DIFFKV_E_INVALID;
+  if (cfg->num_kv_heads > 65535 || (anchor_raw != 0 && anchor_raw != 1)) return DIFFKV_E_INVALID;
+  if (batch > 0 && !cu_seqlens) return DIFFKV_E_INVALID;
+  if (total_tokens > 0 && (!k || !scores)) return DIFFKV_E_INVALID;
+  if ((uintptr_t)k & 15u) return DIFFKV_E_INVALID;  // rows are read with 16-byte loads
+  const Cfg c = to_cfg(cfg);
+  if (!ws_ok(workspace) || workspace_bytes < keydiff_workspace(c, batch, total_tokens)) return DIFFKV_E_WORKSPACE;
+  return rc(launch_keydiff(c, batch, total_tokens, cu_seqlens, k, anchor_raw, scores, workspace,
+                           (hipStream_t)stream));
 }
 
 int diffkv_update_scores(const diffkv_config* cfg, const diffkv_pool* pool, int32_t batch, const int32_t* page_table,

@@ -73,6 +73,11 @@ size_t importance_workspace(const Cfg& c, int64_t nqtot);
 hipError_t launch_importance(const Cfg& c, int batch, int64_t total, const int64_t* cu, int probe, int nq,
                              const uint16_t* q, const uint16_t* k, float* scores, void* ws, hipStream_t s);
 
+// query-free importance from the keys (anchor cosine); raw: anchor of raw keys
+size_t keydiff_workspace(const Cfg& c, int batch, int64_t total);
+hipError_t launch_keydiff(const Cfg& c, int batch, int64_t total, const int64_t* cu, const uint16_t* k, int raw,
+                          float* scores, void* ws, hipStream_t s);
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace dkv

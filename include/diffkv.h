@@ -93,7 +93,8 @@ enum {
   DIFFKV_ATTN_SCORES = 4,
   DIFFKV_DECODE_STEP = 5,        /* diffkv_decode_step, update_scores = 0 */
   DIFFKV_DECODE_STEP_SCORES = 6, /* diffkv_decode_step, update_scores = 1 or 2 */
-  DIFFKV_IMPORTANCE = 7          /* diffkv_importance; total_tokens = queries in all (see there) */
+  DIFFKV_IMPORTANCE = 7,         /* diffkv_importance; total_tokens = queries in all (see there) */
+  DIFFKV_KEYDIFF = 8             /* diffkv_keydiff_scores */
 };
 enum { DIFFKV_IMP_CAUSAL = 0, DIFFKV_IMP_PROBE = 1 };
 
@@ -148,6 +149,23 @@ int diffkv_state_init(const diffkv_config* cfg, int32_t batch, int32_t* page_tab
 int diffkv_importance(const diffkv_config* cfg, int32_t mode, int32_t batch, int64_t total_tokens,
                       const int64_t* cu_seqlens, int32_t nq, const uint16_t* q, const uint16_t* k,
                       float* scores, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Query-free token importance from the keys alone, an alternative input of
+ * diffkv_classify (KeyDiff page, method details: the anchor is the mean of
+ * the unit's normalized keys -- anchor_raw = 1: of the raw keys, the page's
+ * simplification -- and a key's eviction score is its cosine to the anchor,
+ * the least similar keys being kept).  Per unit, importance
+ * w_i = 1 - cos(anchor, k_i) normalized over the unit's tokens
+ * (scores[h][token] sum to 1 per unit, like the mean attention; 1/N each
+ * when every key is parallel to the anchor; a zero key or anchor has
+ * cosine 0), so the alpha/N thresholds apply unchanged.
+ *  cu_seqlens int64 [batch+1] (device), k fp16 [total_tokens, H, d]
+ *  (16-byte aligned), scores fp32 [H, total_tokens] out.
+ *  workspace: diffkv_workspace_bytes(cfg, DIFFKV_KEYDIFF, batch, total_tokens).
+ * Every sum runs in a fixed order: the scores are deterministic. */
+int diffkv_keydiff_scores(const diffkv_config* cfg, int32_t batch, int64_t total_tokens,
+                          const int64_t* cu_seqlens, const uint16_t* k, int32_t anchor_raw, float* scores,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Token classification ("Approach"; "KV compression policy", prompt phase).
  *  cu_seqlens  int64 [batch+1], cu[0] = 0, non-decreasing; N_r = cu[r+1]-cu[r]
