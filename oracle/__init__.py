@@ -229,6 +229,27 @@ class State:
                                      ctypes.c_int32(1 if update_scores else 0)))
         return out
 
+    def page_bounds(self) -> np.ndarray:
+        """fp32 [num_pages, 2, d]: per-dimension min / max of every live
+        page's dequantized keys (other pages NaN)."""
+        d = int(self.cfg["head_dim"])
+        b = np.full((self.num_pages, 2, d), np.nan, np.float32)
+        pool = self._pool()
+        _check(lib().orc_page_bounds(ctypes.byref(make_cfg(self.cfg)), ctypes.byref(pool),
+                                     ctypes.c_int32(self.batch), _p(self.page_table), _p(self.tier_state), _p(b)))
+        return b
+
+    def page_scores(self, q, seq_len, bounds) -> np.ndarray:
+        """fp32 [batch, H, L] page scores in table order from `bounds`."""
+        qq = np.ascontiguousarray(q, dtype=np.uint16)
+        sl = np.ascontiguousarray(seq_len, dtype=np.int32)
+        bb = np.ascontiguousarray(bounds, dtype=np.float32)
+        out = np.zeros(self.page_table.shape, np.float32)
+        _check(lib().orc_page_scores(ctypes.byref(make_cfg(self.cfg)), ctypes.c_int32(self.batch), _p(qq),
+                                     _p(self.page_table), _p(self.tier_state), _p(sl), _p(bb),
+                                     ctypes.c_int64(self.num_pages), _p(out)))
+        return out
+
     # -- inspection -------------------------------------------------------
     def read_slot(self, page_id: int, tier: int, slot: int):
         d = int(self.cfg["head_dim"])

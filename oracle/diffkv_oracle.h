@@ -148,6 +148,15 @@ int orc_importance_causal(const orc_cfg* c, int32_t batch, const int64_t* cu_seq
  * scores are left as they are): sampled outputs of long prompts. */
 int orc_importance_causal_tail(const orc_cfg* c, int32_t batch, const int64_t* cu_seqlens,
                                const uint16_t* q, const uint16_t* k, int64_t tail, float* scores);
+/* Per-page key bounds: bounds [num_pages][2][d] fp32 (min row, max row)
+ * over the dequantized keys of each live page's retained slots. */
+int orc_page_bounds(const orc_cfg* c, orc_pool* p, int32_t batch, const int32_t* page_table,
+                    const int32_t* tier_state, float* bounds);
+/* Page scores in table order [batch, H, L]: max over the group's q heads of
+ * sum_i max(q_i kmin_i, q_i kmax_i); -inf at empty entries. */
+int orc_page_scores(const orc_cfg* c, int32_t batch, const uint16_t* q, const int32_t* page_table,
+                    const int32_t* tier_state, const int32_t* seq_len, const float* bounds,
+                    int64_t num_pages, float* scores);
 /* Query-free importance (KeyDiff anchor cosine): w_i = 1 - cos(anchor, k_i),
  * the anchor the mean of the unit's normalized keys (anchor_raw = 0) or raw
  * keys (1); scores = w normalized over the unit's tokens. */
