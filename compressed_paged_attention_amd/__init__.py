@@ -78,9 +78,12 @@ def lib() -> ctypes.CDLL:
         L.diffkv_decode_attn_noalloc.argtypes = [cfgp, poolp, i32, vp, vp, vp, vp, vp, i32, vp]
         L.diffkv_importance.argtypes = [cfgp, i32, i32, i64, vp, i32, vp, vp, vp, vp, sz, vp]
         L.diffkv_keydiff_scores.argtypes = [cfgp, i32, i64, vp, vp, i32, vp, vp, sz, vp]
+        L.diffkv_page_bounds.argtypes = [cfgp, poolp, i32, vp, vp, vp, vp]
+        L.diffkv_page_scores.argtypes = [cfgp, poolp, i32, vp, vp, vp, vp, vp, vp, vp]
         for f in ("diffkv_pool_init", "diffkv_state_init", "diffkv_classify", "diffkv_compact",
                   "diffkv_decode_attn", "diffkv_update_scores", "diffkv_decode_step",
-                  "diffkv_decode_attn_noalloc", "diffkv_importance", "diffkv_keydiff_scores"):
+                  "diffkv_decode_attn_noalloc", "diffkv_importance", "diffkv_keydiff_scores",
+                  "diffkv_page_bounds", "diffkv_page_scores"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -329,6 +332,26 @@ class DiffKVState:
                            chain=c if update_scores == 1 else 0)
         if update_scores == 1:
             self.chain = c + 1
+        return out
+
+    def page_bounds(self, bounds=None):
+        """Per-page key bounds [num_pages, 2, d] fp32 (min row, max row) of
+        every live page (diffkv_page_bounds); other rows as they were."""
+        if bounds is None:
+            bounds = torch.full((self.pool.num_pages, 2, self.d), float("nan"), dtype=torch.float32,
+                                device=self.page_table.device)
+        _check(lib().diffkv_page_bounds(ctypes.byref(make_config(self.cfg)), ctypes.byref(self.pool.struct()),
+                                        self.batch, _ptr(self.page_table), _ptr(self.tier_state), _ptr(bounds),
+                                        _stream(None)), "diffkv_page_bounds")
+        return bounds
+
+    def page_scores(self, q, seq_len, bounds):
+        """Page scores [batch, H, L] in table order (diffkv_page_scores)."""
+        out = torch.empty(self.batch, self.H, self.L, dtype=torch.float32, device=q.device)
+        _check(lib().diffkv_page_scores(ctypes.byref(make_config(self.cfg)), ctypes.byref(self.pool.struct()),
+                                        self.batch, _ptr(q), _ptr(self.page_table), _ptr(self.tier_state),
+                                        _ptr(seq_len), _ptr(bounds), _ptr(out), _stream(None)),
+               "diffkv_page_scores")
         return out
 
     def update_scores(self, seq_len):

@@ -78,6 +78,13 @@ size_t keydiff_workspace(const Cfg& c, int batch, int64_t total);
 hipError_t launch_keydiff(const Cfg& c, int batch, int64_t total, const int64_t* cu, const uint16_t* k, int raw,
                           float* scores, void* ws, hipStream_t s);
 
+// per-page key bounds [P][2][d] and page scores [batch][H][L]
+hipError_t launch_page_bounds(const Cfg& c, const Pool& p, int batch, const int32_t* table, const int32_t* state,
+                              float* bounds, hipStream_t s);
+hipError_t launch_page_scores(const Cfg& c, int64_t P, int batch, const uint16_t* q, const int32_t* table,
+                              const int32_t* state, const int32_t* seq_len, const float* bounds, float* scores,
+                              hipStream_t s);
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace dkv

@@ -167,6 +167,30 @@ int diffkv_keydiff_scores(const diffkv_config* cfg, int32_t batch, int64_t total
                           const int64_t* cu_seqlens, const uint16_t* k, int32_t anchor_raw, float* scores,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* Per-page key bounds (FlexiCache page, "3.2 KV page scoring", after
+ * Quest: each KV page keeps the per-dimension minimum and maximum of its
+ * keys).  For every live page of the batch's units (table entries in the
+ * unit's high prefix / low suffix), over the dequantized keys of its
+ * retained slots (the keys the attention reads):
+ *  bounds fp32 [pool->num_pages][2][d] out: row 0 the minima, row 1 the
+ *  maxima (exact fp32 values); other pages' rows untouched.  Kept apart from
+ *  the pages, as the page keeps its min-max vectors in a cache of their own;
+ *  call again after compaction to refresh them.  Units with an inconsistent
+ *  tier state and page ids outside the pool are skipped. */
+int diffkv_page_bounds(const diffkv_config* cfg, const diffkv_pool* pool, int32_t batch,
+                       const int32_t* page_table, const int32_t* tier_state, float* bounds, void* stream);
+
+/* Page scores from the bounds: for a query, the largest dot product it
+ * could have with any key of the page, sum_i max(q_i kmin_i, q_i kmax_i),
+ * combined over the KV head's q heads with max (the aggregation used for
+ * token scores); a decode step can skip the pages whose score is low.
+ *  q fp16 [batch, H*G, d]; seq_len int32 [batch] (<= 0: inactive);
+ *  scores fp32 [batch, H, L] out in table order, -inf at empty entries and
+ *  for inactive requests.  fp32 with fixed-order sums. */
+int diffkv_page_scores(const diffkv_config* cfg, const diffkv_pool* pool, int32_t batch, const uint16_t* q,
+                       const int32_t* page_table, const int32_t* tier_state, const int32_t* seq_len,
+                       const float* bounds, float* scores, void* stream);
+
 /* Token classification ("Approach"; "KV compression policy", prompt phase).
  *  cu_seqlens  int64 [batch+1], cu[0] = 0, non-decreasing; N_r = cu[r+1]-cu[r]
  *  scores      fp32 [H, cu[batch]]: per token its mean received attention
