@@ -42,7 +42,12 @@ class Cfg(ctypes.Structure):
                 ("gqa_group", ctypes.c_int32), ("hi_page_tokens", ctypes.c_int32),
                 ("lo_page_tokens", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("lo_enabled", ctypes.c_int32),
-                ("alpha_h", ctypes.c_float), ("alpha_l", ctypes.c_float)]
+                ("alpha_h", ctypes.c_float), ("alpha_l", ctypes.c_float),
+                ("prompt_rule", ctypes.c_int32), ("alpha_h_head", ctypes.c_void_p),
+                ("alpha_l_head", ctypes.c_void_p)]
+
+
+RULE_ALPHA_N, RULE_ALPHA_I = 0, 1
 
 
 class _Pool(ctypes.Structure):
@@ -73,10 +78,24 @@ def lib() -> ctypes.CDLL:
 
 
 def make_cfg(c: dict) -> Cfg:
-    return Cfg(int(c["head_dim"]), int(c["num_kv_heads"]), int(c["gqa_group"]),
-               int(c.get("hi_page_tokens", 16)), int(c.get("lo_page_tokens", 32)),
-               int(c["max_seq_len"]), int(c["window"]), int(c.get("lo_enabled", 1)),
-               float(c["alpha_h"]), float(c["alpha_l"]))
+    """Config dict -> orc_cfg.  Optional keys: prompt_rule (RULE_ALPHA_N or
+    RULE_ALPHA_I), alpha_h_head / alpha_l_head (H thresholds each)."""
+    r = Cfg(int(c["head_dim"]), int(c["num_kv_heads"]), int(c["gqa_group"]),
+            int(c.get("hi_page_tokens", 16)), int(c.get("lo_page_tokens", 32)),
+            int(c["max_seq_len"]), int(c["window"]), int(c.get("lo_enabled", 1)),
+            float(c["alpha_h"]), float(c["alpha_l"]), int(c.get("prompt_rule", RULE_ALPHA_N)))
+    keep = []
+    for key in ("alpha_h_head", "alpha_l_head"):
+        v = c.get(key)
+        if v is None:
+            continue
+        a = np.ascontiguousarray(np.asarray(v, np.float32).reshape(-1))
+        if a.size != r.num_kv_heads:
+            raise ValueError(f"{key} needs {r.num_kv_heads} values")
+        keep.append(a)
+        setattr(r, key, a.ctypes.data)
+    r._keep = keep  # the arrays live as long as the struct
+    return r
 
 
 def _p(a: np.ndarray):

@@ -42,7 +42,26 @@ static int cfg_valid(const orc_cfg* c) {
   if (c->max_seq_len < 1 || c->max_seq_len >= (1 << 29) || c->window < 0) return 0;
   if (!(c->alpha_l >= 0.0f) || !(c->alpha_h >= 0.0f)) return 0;
   if (c->lo_enabled && c->alpha_l > c->alpha_h) return 0;
+  if (c->prompt_rule != ORC_RULE_ALPHA_N && c->prompt_rule != ORC_RULE_ALPHA_I) return 0;
+  if ((c->alpha_h_head == NULL) != (c->alpha_l_head == NULL)) return 0;
+  if (c->alpha_h_head) {
+    for (int32_t h = 0; h < c->num_kv_heads; h++) {
+      float ah = c->alpha_h_head[h], al = c->alpha_l_head[h];
+      if (!(al >= 0.0f) || !(ah >= 0.0f)) return 0;
+      if (c->lo_enabled && al > ah) return 0;
+    }
+  }
   return 1;
+}
+
+/* Thresholds of KV head h: the head's own pair when the config carries
+ * per-head arrays ("KV compression policy", the extensibility paragraph: one
+ * shared pair by default, tuned per head as an option), else the shared pair. */
+static double alpha_hi(const orc_cfg* c, int32_t h) {
+  return (double)(c->alpha_h_head ? c->alpha_h_head[h] : c->alpha_h);
+}
+static double alpha_lo(const orc_cfg* c, int32_t h) {
+  return (double)(c->alpha_l_head ? c->alpha_l_head[h] : c->alpha_l);
 }
 
 int32_t orc_table_len(const orc_cfg* c) {
@@ -303,21 +322,25 @@ float orc_dequant(uint16_t s16, uint16_t z16, int32_t code) {
  * the last W tokens are always high precision; otherwise a token whose mean
  * score exceeds alpha_h/N is high, one in [alpha_l/N, alpha_h/N] is low, and
  * one below alpha_l/N is pruned.  N is the request's length (the approach
- * summary and the generation-phase algorithm use N; the prompt passage's
- * 1/i variant is not taken).  Comparisons are made without division, as
- * s*N against alpha in fp64, which is exact for N < 2^29.  With the low tier
- * closed, a token is high iff s*N >= alpha_l and pruned otherwise.        */
+ * summary and the generation-phase algorithm use N).  The prompt passage
+ * compares the i-th token against alpha/i instead, a threshold that adapts
+ * along the sequence; prompt_rule = ORC_RULE_ALPHA_I takes that reading,
+ * with i = position + 1 (tokens counted from 1).  Comparisons are made
+ * without division, as s*N (or s*i) against alpha in fp64, which is exact
+ * for N < 2^29.  With the low tier closed, a token is high iff
+ * s*N >= alpha_l and pruned otherwise.                                     */
 /* ------------------------------------------------------------------------ */
 
-static int32_t classify_prompt(const orc_cfg* c, float s, int64_t N, int64_t p) {
+static int32_t classify_prompt(const orc_cfg* c, int32_t h, float s, int64_t N, int64_t p) {
   if (c->window > 0 && p >= N - c->window) return ORC_HI;
-  double x = (double)s * (double)N;
+  int64_t denom = c->prompt_rule == ORC_RULE_ALPHA_I ? p + 1 : N;
+  double x = (double)s * (double)denom;
   if (c->lo_enabled) {
-    if (x > (double)c->alpha_h) return ORC_HI;
-    if (x >= (double)c->alpha_l) return ORC_LO;
+    if (x > alpha_hi(c, h)) return ORC_HI;
+    if (x >= alpha_lo(c, h)) return ORC_LO;
     return ORC_PRUNE;
   }
-  return x >= (double)c->alpha_l ? ORC_HI : ORC_PRUNE;
+  return x >= alpha_lo(c, h) ? ORC_HI : ORC_PRUNE;
 }
 
 static int cu_valid(int32_t batch, const int64_t* cu) {
@@ -338,7 +361,7 @@ int orc_classify(const orc_cfg* c, int32_t batch, const int64_t* cu,
       int32_t nh = 0, nl = 0;
       for (int64_t p = 0; p < N; p++) {
         int64_t idx = (int64_t)h * total + cu[r] + p;
-        int32_t t = classify_prompt(c, scores[idx], N, p);
+        int32_t t = classify_prompt(c, h, scores[idx], N, p);
         tiers[idx] = (uint8_t)t;
         if (t == ORC_HI) nh++;
         if (t == ORC_LO) nl++;
@@ -583,9 +606,9 @@ typedef struct {
   int32_t page_id;
 } step_plan;
 
-static int32_t classify_mean(const orc_cfg* c, float sum, int64_t cnt, int64_t Np) {
+static int32_t classify_mean(const orc_cfg* c, int32_t h, float sum, int64_t cnt, int64_t Np) {
   double x = (double)sum * (double)Np;
-  double ch = (double)c->alpha_h * (double)cnt, cl = (double)c->alpha_l * (double)cnt;
+  double ch = alpha_hi(c, h) * (double)cnt, cl = alpha_lo(c, h) * (double)cnt;
   if (c->lo_enabled) {
     if (x > ch) return ORC_HI;
     if (x >= cl) return ORC_LO;
@@ -641,6 +664,7 @@ static int compact_step_impl(const orc_cfg* c, orc_pool* p, int32_t batch,
     if (bad_id) { st |= ORC_ST_BAD_STATE; continue; }
     int64_t Np = N + 1;
     int64_t tc_pos = N - W;
+    int32_t hh = (int32_t)(u % H);
     P->new_hi_slot = n_hi;
     P->hi_append = 1;
     if (branch) branch[u] = ORC_BR_NO_TC;
@@ -653,7 +677,7 @@ static int compact_step_impl(const orc_cfg* c, orc_pool* p, int32_t batch,
         if (pos == tc_pos) { tc = s; tc_sum = sc; }
       }
       if (tc < 0) { st |= ORC_ST_BAD_STATE; continue; }
-      int32_t cls = classify_mean(c, tc_sum, W - 1, Np);
+      int32_t cls = classify_mean(c, hh, tc_sum, W - 1, Np);
       if (cls == ORC_HI) {
         int32_t v = -1; float vs = 0; int32_t vp = 0; int64_t vc = 0;
         for (int32_t s = 0; s < n_hi; s++) {
@@ -663,7 +687,7 @@ static int compact_step_impl(const orc_cfg* c, orc_pool* p, int32_t batch,
           int64_t cnt = N - 1 - pos;
           if (v < 0 || less_important(sc, cnt, pos, vs, vc, vp)) { v = s; vs = sc; vp = pos; vc = cnt; }
         }
-        int32_t vcls = classify_mean(c, vs, vc, Np);
+        int32_t vcls = classify_mean(c, hh, vs, vc, Np);
         if (branch) branch[u] = vcls == ORC_HI ? ORC_BR_HI_KEEP : (vcls == ORC_LO ? ORC_BR_HI_DEMOTE : ORC_BR_HI_PRUNE);
         if (vcls == ORC_LO) {
           P->lo_src_hi_slot = v;
@@ -687,7 +711,7 @@ static int compact_step_impl(const orc_cfg* c, orc_pool* p, int32_t batch,
           int64_t cnt = N - 1 - pos;
           if (less_important(sc, cnt, pos, vs, vc, vp)) { v = s; vs = sc; vp = pos; vc = cnt; }
         }
-        if (v >= 0 && classify_mean(c, vs, vc, Np) == ORC_PRUNE) {
+        if (v >= 0 && classify_mean(c, hh, vs, vc, Np) == ORC_PRUNE) {
           P->lo_slot = v;
           P->lo_append = 0;
           if (branch) branch[u] = ORC_BR_LO_PRUNE;

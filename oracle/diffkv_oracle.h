@@ -38,7 +38,13 @@ typedef struct {
   int32_t window;         /* W: most recent tokens always high precision */
   int32_t lo_enabled;     /* 0: high / prune only */
   float alpha_h, alpha_l; /* thresholds are alpha/N */
+  int32_t prompt_rule;    /* ORC_RULE_ALPHA_N: prompt tokens against alpha/N;
+                             ORC_RULE_ALPHA_I: the i-th prompt token against alpha/i */
+  const float* alpha_h_head; /* host arrays of H per-KV-head thresholds, or both NULL */
+  const float* alpha_l_head;
 } orc_cfg;
+
+enum { ORC_RULE_ALPHA_N = 0, ORC_RULE_ALPHA_I = 1 };
 
 typedef struct {
   uint8_t* pages;     /* [num_pages * page_bytes] */

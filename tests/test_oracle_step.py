@@ -78,12 +78,19 @@ def _sets(st, b, h, orc):
     return hi, lo, sums
 
 
-@pytest.mark.parametrize("lo_enabled", [1, 0])
-def test_step_matches_set_model(orc, lo_enabled):
-    rng = np.random.default_rng(100 + lo_enabled)
+@pytest.mark.parametrize("lo_enabled,per_head", [(1, False), (0, False), (1, True)])
+def test_step_matches_set_model(orc, lo_enabled, per_head):
+    # per_head: each KV head classifies against its own (alpha_h, alpha_l)
+    # ("KV compression policy", extensibility paragraph); the set model runs
+    # one policy per head with that head's pair
+    rng = np.random.default_rng(100 + lo_enabled + 7 * per_head)
     d, H, G, B, W = 64, 2, 2, 2, 6
     cfg = dict(head_dim=d, num_kv_heads=H, gqa_group=G, max_seq_len=700, window=W,
                alpha_h=1.0, alpha_l=0.3, lo_enabled=lo_enabled)
+    ah, al = [1.0] * H, [0.3] * H
+    if per_head:
+        ah, al = [1.0, 2.5], [0.3, 0.6]
+        cfg.update(alpha_h_head=ah, alpha_l_head=al, alpha_h=9.0, alpha_l=9.0)
     lens = np.array([40, 3])         # the second prompt is shorter than the window
     cu = np.concatenate([[0], np.cumsum(lens)])
     total = int(cu[-1])
@@ -96,7 +103,7 @@ def test_step_matches_set_model(orc, lo_enabled):
     tiers, _ = orc.classify(cfg, cu, sc)
     st = orc.State(cfg, batch=B, num_pages=200)
     st.compact_prompt(cu, k, v, sc, tiers)
-    model = SetModel(W, cfg["alpha_h"], cfg["alpha_l"], lo_enabled)
+    models = [SetModel(W, ah[h], al[h], lo_enabled) for h in range(H)]
     seq = lens.astype(np.int32).copy()
     gone = [[set() for _ in range(H)] for _ in range(B)]
     cases = {}
@@ -105,7 +112,7 @@ def test_step_matches_set_model(orc, lo_enabled):
         for b in range(B):
             for h in range(H):
                 hi, lo, sums = _sets(st, b, h, orc)
-                expect[b, h] = model.step(hi, lo, sums, int(seq[b]))
+                expect[b, h] = models[h].step(hi, lo, sums, int(seq[b]))
         state0 = st.tier_state.copy()
         end0 = int(st.ptr[1])
         kn = (rng.standard_normal((B, H, d)) * scale).astype(np.float16).view(np.uint16)
