@@ -36,7 +36,12 @@ class diffkv_config(ctypes.Structure):
                 ("gqa_group", ctypes.c_int32), ("hi_page_tokens", ctypes.c_int32),
                 ("lo_page_tokens", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("lo_enabled", ctypes.c_int32),
-                ("alpha_h", ctypes.c_float), ("alpha_l", ctypes.c_float)]
+                ("alpha_h", ctypes.c_float), ("alpha_l", ctypes.c_float),
+                ("prompt_rule", ctypes.c_int32), ("alpha_h_head", ctypes.c_void_p),
+                ("alpha_l_head", ctypes.c_void_p)]
+
+
+RULE_ALPHA_N, RULE_ALPHA_I = 0, 1
 
 
 class diffkv_pool(ctypes.Structure):
@@ -89,11 +94,42 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
+_head_alpha_cache: dict = {}
+
+
+def _head_alphas(v, H: int):
+    """Per-head thresholds as a device float32 tensor of H (cached by value,
+    so a config reused across calls uploads them once)."""
+    if isinstance(v, torch.Tensor):
+        if not v.is_cuda or v.dtype != torch.float32 or not v.is_contiguous() or v.numel() != H:
+            raise DiffKVError("per-head thresholds: contiguous float32 device tensor of H expected")
+        return v
+    key = (tuple(float(x) for x in v), torch.cuda.current_device())
+    t = _head_alpha_cache.get(key)
+    if t is None:
+        if len(key[0]) != H:
+            raise DiffKVError(f"per-head thresholds: {H} values expected")
+        t = torch.tensor(key[0], dtype=torch.float32, device="cuda")
+        _head_alpha_cache[key] = t
+    return t
+
+
 def make_config(c: dict) -> diffkv_config:
-    return diffkv_config(int(c["head_dim"]), int(c["num_kv_heads"]), int(c["gqa_group"]),
-                         int(c.get("hi_page_tokens", 16)), int(c.get("lo_page_tokens", 32)),
-                         int(c["max_seq_len"]), int(c["window"]), int(c.get("lo_enabled", 1)),
-                         float(c["alpha_h"]), float(c["alpha_l"]))
+    """Config dict -> diffkv_config.  Optional keys: prompt_rule
+    (RULE_ALPHA_N / RULE_ALPHA_I) and alpha_h_head / alpha_l_head (H values
+    each: a sequence, or a float32 device tensor)."""
+    r = diffkv_config(int(c["head_dim"]), int(c["num_kv_heads"]), int(c["gqa_group"]),
+                      int(c.get("hi_page_tokens", 16)), int(c.get("lo_page_tokens", 32)),
+                      int(c["max_seq_len"]), int(c["window"]), int(c.get("lo_enabled", 1)),
+                      float(c["alpha_h"]), float(c["alpha_l"]), int(c.get("prompt_rule", RULE_ALPHA_N)))
+    keep = []
+    for key in ("alpha_h_head", "alpha_l_head"):
+        if c.get(key) is not None:
+            t = _head_alphas(c[key], r.num_kv_heads)
+            keep.append(t)
+            setattr(r, key, t.data_ptr())
+    r._keep = keep  # the device arrays live as long as the struct
+    return r
 
 
 def _ptr(t) -> ctypes.c_void_p:

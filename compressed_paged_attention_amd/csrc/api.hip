@@ -22,6 +22,8 @@ bool cfg_ok(const diffkv_config* c) {
   if (c->max_seq_len < 1 || c->max_seq_len >= (1 << 29) || c->window < 0) return false;
   if (!(c->alpha_l >= 0.0f) || !(c->alpha_h >= 0.0f)) return false;
   if (c->lo_enabled && c->alpha_l > c->alpha_h) return false;
+  if (c->prompt_rule != DIFFKV_RULE_ALPHA_N && c->prompt_rule != DIFFKV_RULE_ALPHA_I) return false;
+  if ((c->alpha_h_head == nullptr) != (c->alpha_l_head == nullptr)) return false;
   return true;
 }
 
@@ -36,6 +38,9 @@ Cfg to_cfg(const diffkv_config* c) {
   r.S_max = c->max_seq_len;
   r.ah = c->alpha_h;
   r.al = c->alpha_l;
+  r.ah_head = c->alpha_h_head;
+  r.al_head = c->alpha_l_head;
+  r.prompt_rule = c->prompt_rule;
   return r;
 }
 

@@ -460,7 +460,11 @@ constexpr int kLdsWords = 16384;
 struct PolicyArgs {
   int W, S_max, lo_en;
   float ah, al;
+  const float* ah_head;  // per-KV-head thresholds (null: ah, al)
+  const float* al_head;
 };
+__device__ inline double pa_ah(const PolicyArgs& pa, int h) { return (double)(pa.ah_head ? pa.ah_head[h] : pa.ah); }
+__device__ inline double pa_al(const PolicyArgs& pa, int h) { return (double)(pa.al_head ? pa.al_head[h] : pa.al); }
 
 // The generation step's commit, run in front of the attention (STEP): the
 // step workspace made by the plan kernel, the new tokens and the pool lists.
@@ -1088,7 +1092,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
       const float tcsum = s_tcsum;
       int cls = -1;
       if (tc1 >= 0 && tcs >= 0)
-        cls = classify_mean(tcsum, pa.W - 1, N1 + 1, pa.lo_en, (double)pa.ah, (double)pa.al);
+        cls = classify_mean(tcsum, pa.W - 1, N1 + 1, pa.lo_en, pa_ah(pa, h), pa_al(pa, h));
       const bool needH = cls == kTierHi, needL = cls == kTierLo;
       // the needed candidate: wave butterflies, then the waves' results in
       // lanes 0..7 of wave 0
@@ -1119,7 +1123,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
         // record, one round of id lookups).
         const bool rec_ok = ph >= 1 && nh + nl <= N1 && !(tc1 >= 0 && tcs < 0);
         if (rec_ok) {
-          const Plan pn = plan_decide(N1, pa.W, pa.S_max, pa.lo_en, (double)pa.ah, (double)pa.al, nh, nl, ph, pl,
+          const Plan pn = plan_decide(N1, pa.W, pa.S_max, pa.lo_en, pa_ah(pa, h), pa_al(pa, h), nh, nl, ph, pl,
                                       L, tcs, tcsum, bh, bl);
           uint32_t rw[kRecWords];
           plan_rec_fill(rw, N1, nh, nl, ph, pl, pn);
@@ -1439,7 +1443,8 @@ __global__ __launch_bounds__(64) void score_finish_kernel(int H, int G, int L, i
   if (tc1 >= 0 && tcs < 0) return;  // the plan kernel would not accept the state
   const int32_t id0 = row[0];
   if (id0 < 0 || id0 >= P) return;
-  const Plan pn = plan_decide(N1, pa.W, pa.S_max, pa.lo_en, (double)pa.ah, (double)pa.al, nh, nl, ph, pl, L, tcs,
+  const Plan pn = plan_decide(N1, pa.W, pa.S_max, pa.lo_en, pa_ah(pa, (int)(u % H)), pa_al(pa, (int)(u % H)), nh, nl,
+                              ph, pl, L, tcs,
                               tcsum, bh, bl);
   uint32_t rw[kRecWords];
   plan_rec_fill(rw, N1, nh, nl, ph, pl, pn);
@@ -1456,7 +1461,7 @@ hipError_t launch_scores(const Cfg& c, const Pool& p, int batch, const int32_t* 
   if (U == 0) return hipSuccess;
   AttnWs w = attn_carve(c, batch, true, ws, nullptr);
   const dim3 grid((unsigned)((c.L + kScorePages - 1) / kScorePages), (unsigned)U), block(256);
-  const PolicyArgs pa{c.W, c.S_max, c.lo_en, c.ah, c.al};
+  const PolicyArgs pa{c.W, c.S_max, c.lo_en, c.ah, c.al, c.ah_head, c.al_head};
   if (c.d == 128) {
     score_kernel<128><<<grid, block, 0, s>>>(c.H, c.G, c.L, p.P, p.page_bytes, c.W, table, state, seq_len, w.ml,
                                              w.logits, p.pages, w.cand);
@@ -1563,7 +1568,7 @@ hipError_t launch_attn(const Cfg& c, const Pool& p, int batch, const uint16_t* q
   const int kmode = mode == 1 && S > 1 ? 2 : mode;
   // head and tail of the weights share one matrix instruction when 2G <= 16
   const bool pack = 2 * c.G <= 16;
-  const PolicyArgs pa{c.W, c.S_max, c.lo_en, c.ah, c.al};
+  const PolicyArgs pa{c.W, c.S_max, c.lo_en, c.ah, c.al, c.ah_head, c.al_head};
   const StepArgs none{};
   const int32_t* order = launch_order(S, U, state, w, s);
 #define DKV_ATTN(D, M, PK)                                                                                 \
@@ -1640,7 +1645,7 @@ hipError_t launch_decode_step(const Cfg& c, const Pool& p, int batch, const int3
   const float scale_log2 = (1.0f / sqrtf((float)c.d)) * kLog2e;
   const dim3 grid(1, (unsigned)U), block(kThreads);
   const bool pack = 2 * c.G <= 16;
-  const PolicyArgs pa{c.W, c.S_max, c.lo_en, c.ah, c.al};
+  const PolicyArgs pa{c.W, c.S_max, c.lo_en, c.ah, c.al, c.ah_head, c.al_head};
   const StepArgs sa{k,
                     v,
                     sw.hdr,

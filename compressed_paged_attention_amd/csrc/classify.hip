@@ -41,9 +41,11 @@ hipError_t launch_state_init(const Cfg& c, int batch, int32_t* table, int32_t* s
   return hipGetLastError();
 }
 
-__device__ inline int tier_of(float s, int64_t N, int64_t p, int W, int lo_en, double ah, double al) {
+// rule 0: s N against alpha (threshold alpha/N); rule 1: s (p + 1) against
+// alpha (threshold alpha/i for the i-th token, i = p + 1)
+__device__ inline int tier_of(float s, int64_t N, int64_t p, int W, int lo_en, double ah, double al, int rule) {
   if (W > 0 && p >= N - W) return kTierHi;
-  const double x = (double)s * (double)N;
+  const double x = (double)s * (double)(rule ? p + 1 : N);
   if (lo_en) {
     if (x > ah) return kTierHi;
     return x >= al ? kTierLo : kTierPrune;
@@ -54,6 +56,8 @@ __device__ inline int tier_of(float s, int64_t N, int64_t p, int W, int lo_en, d
 // grid (H, batch); one workgroup per unit walks its tokens and reduces the
 // two counts.
 __global__ __launch_bounds__(1024) void classify_kernel(int H, int W, int lo_en, float ah, float al,
+                                                        const float* __restrict__ ah_head,
+                                                        const float* __restrict__ al_head, int rule,
                                                         int64_t total, const int64_t* __restrict__ cu,
                                                         const float* __restrict__ scores,
                                                         uint8_t* __restrict__ tiers,
@@ -69,10 +73,10 @@ __global__ __launch_bounds__(1024) void classify_kernel(int H, int W, int lo_en,
   }
   const float* s = scores + (int64_t)h * total + b0;
   uint8_t* t = tiers + (int64_t)h * total + b0;
-  const double dah = (double)ah, dal = (double)al;
+  const double dah = (double)(ah_head ? ah_head[h] : ah), dal = (double)(al_head ? al_head[h] : al);
   int nh = 0, nl = 0;
   for (int64_t p = threadIdx.x; p < N; p += blockDim.x) {
-    const int ti = tier_of(s[p], N, p, W, lo_en, dah, dal);
+    const int ti = tier_of(s[p], N, p, W, lo_en, dah, dal, rule);
     t[p] = (uint8_t)ti;
     nh += ti == kTierHi;
     nl += ti == kTierLo;
@@ -100,7 +104,8 @@ __global__ __launch_bounds__(1024) void classify_kernel(int H, int W, int lo_en,
 hipError_t launch_classify(const Cfg& c, int batch, int64_t total, const int64_t* cu,
                            const float* scores, uint8_t* tiers, int32_t* counts, hipStream_t s) {
   if (batch == 0) return hipSuccess;
-  classify_kernel<<<dim3(c.H, batch), dim3(1024), 0, s>>>(c.H, c.W, c.lo_en, c.ah, c.al, total, cu,
+  classify_kernel<<<dim3(c.H, batch), dim3(1024), 0, s>>>(c.H, c.W, c.lo_en, c.ah, c.al, c.ah_head, c.al_head,
+                                                          c.prompt_rule, total, cu,
                                                           scores, tiers, counts);
   return hipGetLastError();
 }

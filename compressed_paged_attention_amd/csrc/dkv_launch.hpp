@@ -11,6 +11,10 @@ namespace dkv {
 struct Cfg {
   int d, H, G, L, W, lo_en, S_max;
   float ah, al;
+  // per-KV-head thresholds (device arrays of H, or null: ah, al for every head)
+  const float* ah_head;
+  const float* al_head;
+  int prompt_rule;  // 0: prompt tokens against alpha/N; 1: against alpha/i (i = position + 1)
 };
 
 struct Pool {

@@ -52,7 +52,9 @@ constexpr int kRowCache = 4096;   // table rows up to this long are read once in
 // token (wave butterflies, then the four waves' candidates in one quad).
 template <int D>
 __global__ __launch_bounds__(kPlanThreads) void step_plan_kernel(int H, int L, int W, int S_max, int lo_en, float ah,
-                                                                 float al, int64_t P, int page_bytes,
+                                                                 float al, const float* __restrict__ ah_head,
+                                                                 const float* __restrict__ al_head, int64_t P,
+                                                                 int page_bytes,
                                                                  const int32_t* __restrict__ seq_len,
                                                                  const int32_t* __restrict__ table,
                                                                  const int32_t* __restrict__ state,
@@ -141,7 +143,7 @@ __global__ __launch_bounds__(kPlanThreads) void step_plan_kernel(int H, int L, i
   if (s_rec) return;
   const Seg sh = tier_seg(D, true), sl = tier_seg(D, false);
   const int64_t tc_pos = N - W;
-  const double dah = (double)ah, dal = (double)al;
+  const double dah = (double)(ah_head ? ah_head[u % H] : ah), dal = (double)(al_head ? al_head[u % H] : al);
   const Cand none{0.0f, kNoPos, 0};
   Cand bh = none, bl = none;
   if (tc_pos >= 0) {
@@ -297,7 +299,8 @@ hipError_t launch_step_plan(const Cfg& c, const Pool& p, int batch, const int32_
   const StepWs w = step_carve(c, batch, ws);
 #define DKV_PLAN(D)                                                                                       \
   step_plan_kernel<D><<<dim3((unsigned)U), dim3(kPlanThreads), 0, s>>>(c.H, c.L, c.W, c.S_max, c.lo_en, c.ah, \
-                                                                       c.al, p.P, p.page_bytes, seq_len, table, \
+                                                                       c.al, c.ah_head, c.al_head, p.P,        \
+                                                                       p.page_bytes, seq_len, table,           \
                                                                        state, p.pages, p.ptr, w.hdr, w.rec, w.nf)
   if (c.d == 128) DKV_PLAN(128);
   else DKV_PLAN(64);

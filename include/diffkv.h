@@ -48,10 +48,20 @@ extern "C" {
 /* Host struct.  Thresholds: high if mean score > alpha_h/N, low if in
  * [alpha_l/N, alpha_h/N], pruned below alpha_l/N ("Approach"; "KV
  * compression policy").  With lo_enabled = 0: high iff >= alpha_l/N.
+ * Policy variants ("KV compression policy"):
+ *  - prompt_rule = DIFFKV_RULE_ALPHA_I compares the i-th prompt token
+ *    (i = position + 1) against alpha/i, as the prompt-phase paragraph
+ *    states; the generation step always uses alpha/N (N = the new length).
+ *  - alpha_h_head / alpha_l_head (DEVICE arrays of num_kv_heads floats, both
+ *    or neither) give each KV head its own pair, the extensibility
+ *    paragraph's option; NULL = the shared pair for every head.  The library
+ *    cannot read them on the host: the caller guarantees
+ *    0 <= alpha_l_head[h] <= alpha_h_head[h] when lo_enabled (other values
+ *    are used as given in the same comparisons).
  * Valid: head_dim in {64,128}; 1 <= gqa_group <= 16; hi_page_tokens = 16;
  * 1 <= max_seq_len < 2^29 (score sums times token counts stay exact in fp64);
  * lo_page_tokens = 32; window >= 0 (>= 2 for STEP);
- * 0 <= alpha_l <= alpha_h when lo_enabled. */
+ * 0 <= alpha_l <= alpha_h when lo_enabled; prompt_rule in {0, 1}. */
 typedef struct {
   int32_t head_dim;       /* d */
   int32_t num_kv_heads;   /* H */
@@ -62,7 +72,12 @@ typedef struct {
   int32_t window;         /* W: the most recent W tokens stay high precision */
   int32_t lo_enabled;     /* 0: high / prune only */
   float alpha_h, alpha_l;
+  int32_t prompt_rule;        /* DIFFKV_RULE_ALPHA_N (0) or DIFFKV_RULE_ALPHA_I (1) */
+  const float* alpha_h_head;  /* [num_kv_heads] device, or NULL */
+  const float* alpha_l_head;  /* [num_kv_heads] device, or NULL */
 } diffkv_config;
+
+enum { DIFFKV_RULE_ALPHA_N = 0, DIFFKV_RULE_ALPHA_I = 1 };
 
 /* Host struct describing caller-owned device buffers of one page pool
  * ("Memory management": unified pages, circular free page list). */
