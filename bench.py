@@ -557,6 +557,70 @@ def importance_timing(args, name, dk):
                          "kernel": "imp_stats_kernel + imp_sum_kernel"}}
 
 
+def side_timings(args, name, dk):
+    """Query-free importance (diffkv_keydiff_scores) on the workload's prompt
+    keys, and per-page key bounds (diffkv_page_bounds) and page scores
+    (diffkv_page_scores) over its compacted cache; each a warmup call, then
+    8 calls timed with HIP events on a held stream.  Algorithmic bytes:
+    KeyDiff reads each key once and writes one fp32 score (2d + 4 per token
+    and head); the bounds read the K codes and metadata of every retained
+    token (d + 4 high, d/2 + 4 low) and write 2d fp32 per live page; the page
+    scores read the bounds and the queries and write one fp32 per table
+    entry."""
+    import torch
+
+    from workloads import synth
+    dev = torch.device("cuda:0")
+    cfg = synth.config(name)
+    B, H, G, d = cfg["batch"], cfg["num_kv_heads"], cfg["gqa_group"], cfg["head_dim"]
+    lens = synth.seq_lens(cfg)
+    P = synth.pool_pages(cfg, lens, dk.diffkv_page_bytes(cfg))
+    total = int(lens.sum())
+    pr = synth.make_prompt(cfg, device=dev, lens=lens)
+    st = dk.DiffKVState(cfg, B, P, max_total_tokens=total, device=dev)
+    cu = pr["cu_seqlens"].to(dev)
+    t, _ = st.classify(cu, pr["scores"])
+    st.compact_prompt(cu, pr["k"], pr["v"], pr["scores"], t)
+    q = synth.make_decode(cfg, 0, device=dev)["q"]
+    seq = lens.to(torch.int32).to(dev)
+    n = 8
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        torch.cuda._sleep(args.hold_cycles)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    def line(kernel, nbytes, us):
+        gbs = nbytes / (us * 1e-6) / 1e9
+        return {"us": us, "bytes_per_launch": int(nbytes),
+                "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": gbs / PEAK_HBM_GBS, "kernel": kernel}}
+
+    k = pr["k"]
+    us_kd = timed(lambda: dk.keydiff_scores(cfg, cu, k))
+    bounds = torch.zeros(P, 2, d, dtype=torch.float32, device=dev)
+    us_pb = timed(lambda: st.page_bounds(bounds))
+    us_ps = timed(lambda: st.page_scores(q, seq, bounds))
+    ts = st.tier_state.view(-1, 4).to(torch.int64).sum(0).tolist()
+    n_hi, n_lo, p_hi, p_lo = ts
+    out = {"workload": WORKLOAD_NAMES.get(name, name),
+           "keydiff_scores": line("kd_partial/anchor/score/norm kernels", total * H * (2 * d + 4), us_kd),
+           "page_bounds": line("page_bounds_kernel",
+                               n_hi * (d + 4) + n_lo * (d // 2 + 4) + (p_hi + p_lo) * 8 * d, us_pb),
+           "page_scores": line("page_scores_kernel",
+                               (p_hi + p_lo) * 8 * d + B * H * G * d * 2 + B * H * st.L * 4, us_ps)}
+    del pr, st, bounds
+    torch.cuda.empty_cache()
+    return out
+
+
 def roofline(kernel, nbytes, us, workload, stream_gbps):
     achieved = nbytes / (us * 1e-6) / 1e9
     return {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -657,6 +721,7 @@ def main():
                                             stream)
         res["extra"] = {WORKLOAD_NAMES.get(args.extra_workload, args.extra_workload): ex}
         res["extra"]["prompt_importance"] = importance_timing(args, args.extra_workload, dk)
+        res["extra"]["key_bounds_and_keydiff"] = side_timings(args, args.extra_workload, dk)
     print(json.dumps(res), flush=True)
 
 
