@@ -210,8 +210,10 @@ int diffkv_page_scores(const diffkv_config* cfg, const diffkv_pool* pool, int32_
  *  cu_seqlens  int64 [batch+1], cu[0] = 0, non-decreasing; N_r = cu[r+1]-cu[r]
  *  scores      fp32 [H, cu[batch]]: per token its mean received attention
  *  tiers       uint8 [H, cu[batch]] out: 2 high, 1 low, 0 pruned.  The last
- *              W tokens of each request are high; otherwise s*N_r is compared
- *              with alpha_h and alpha_l exactly (fp64, no division).
+ *              W tokens of each request are high; otherwise s*N_r (with
+ *              prompt_rule = DIFFKV_RULE_ALPHA_I: s*(p+1) for position p) is
+ *              compared with the KV head's alpha_h and alpha_l exactly (fp64,
+ *              no division).
  *  tier_counts int32 [batch, H, 2] out: (high count, low count). */
 int diffkv_classify(const diffkv_config* cfg, int32_t batch, int64_t total_tokens,
                     const int64_t* cu_seqlens, const float* scores, uint8_t* tiers,
