@@ -235,6 +235,8 @@ int diffkv_page_scores(const diffkv_config* cfg, const diffkv_pool* pool, int32_
   if (!cfg_ok(cfg) || !pool_ok(cfg, pool) || batch < 0) return DIFFKV_E_INVALID;
   if (batch > 0 && (!q || !page_table || !tier_state || !seq_len || !bounds || !scores)) return DIFFKV_E_INVALID;
   if ((int64_t)batch * cfg->num_kv_heads > 65535) return DIFFKV_E_INVALID;
+  // pairs of dimensions per lane: 4-byte query words, 8-byte bound pairs
+  if (((uintptr_t)q & 3) != 0 || ((uintptr_t)bounds & 7) != 0) return DIFFKV_E_INVALID;
   return rc(launch_page_scores(to_cfg(cfg), pool->num_pages, batch, q, page_table, tier_state, seq_len, bounds,
                                scores, (hipStream_t)stream));
 }

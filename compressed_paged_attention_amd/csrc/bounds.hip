@@ -7,12 +7,16 @@
 // The bounds live in a table of their own indexed by page id (as FlexiCache
 // keeps its min-max vectors apart from the KV pages), fp32, over the
 // dequantized keys of each page's retained slots -- the keys the attention
-// reads -- so they are exact.  One thread per (page, dimension):
-//   page_bounds_kernel: walks the page's valid slots (codes and scale/zero),
-//     min and max per dimension;
-//   page_scores_kernel: per q head of the group the block sum of
-//     max(q kmin, q kmax) in a fixed order, max over the group, written in
+// reads -- so they are exact.
+//   page_bounds_kernel: one thread per (page, dimension); every slot's code
+//     byte and scale/zero word of the page are loaded before any is used (one
+//     round trip per page, not one per slot), then min and max per dimension;
+//   page_scores_kernel: one wave per table entry, each lane D/64 dimensions;
+//     per q head of the group the lane's max(q kmin, q kmax) terms, a wave
+//     sum in a fixed butterfly order, then the max over the group, written in
 //     table order (-inf at empty entries).
+// Both grids give each unit a fixed number of workgroups that stride over its
+// table, so empty entries cost no launches.
 // HBM-bound: a refresh reads the K codes and metadata of every live page
 // (~2.1 KB per page at d = 128) and writes 2d fp32; scoring reads the bounds.
 #include "dkv_common.hpp"
@@ -30,6 +34,33 @@ __device__ inline bool state_valid(int nh, int nl, int ph, int pl, int L) {
 
 }  // namespace
 
+// min and max over the first nv of a page's T slots for dimension dim:
+// every slot's code and metadata loaded first (all in the page), then used
+template <int D, bool HI>
+__device__ inline void page_dim_bounds(const uint8_t* pg, int nv, int dim, float& mn, float& mx) {
+  constexpr int T = HI ? kHiTokens : kLoTokens;
+  constexpr Seg sg = tier_seg(D, HI);
+  uint32_t cb[T], m[T];
+#pragma unroll
+  for (int t = 0; t < T; t++) {
+    int byte, shift;
+    k_field(D, HI, t, dim, byte, shift);
+    cb[t] = (uint32_t)pg[sg.kc + byte] >> shift;
+    m[t] = *(const uint32_t*)(pg + sg.km + 4 * t);
+  }
+  mn = INFINITY;
+  mx = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < T; t++) {
+    if (t >= nv) continue;
+    const float x = dequant(h2f((uint16_t)m[t]), h2f((uint16_t)(m[t] >> 16)), cb[t] & (HI ? 0xFFu : 0xFu));
+    mn = fminf(mn, x);
+    mx = fmaxf(mx, x);
+  }
+}
+
+constexpr int kBoundsWgPerUnit = 8;  // workgroups per unit (grid x), striding over its pages
+
 // bounds [P][2][D]: row 0 minima, row 1 maxima
 template <int D>
 __global__ __launch_bounds__(kBThreads) void page_bounds_kernel(int L, int64_t P, int page_bytes,
@@ -37,32 +68,26 @@ __global__ __launch_bounds__(kBThreads) void page_bounds_kernel(int L, int64_t P
                                                                const int32_t* __restrict__ state,
                                                                const uint8_t* __restrict__ pages,
                                                                float* __restrict__ bounds) {
-  constexpr int PPB = kBThreads / D;  // pages per workgroup
+  constexpr int PPB = kBThreads / D;  // pages per workgroup and round
   const int64_t u = blockIdx.y;
-  const int pj = blockIdx.x * PPB + threadIdx.x / D, dim = threadIdx.x % D;
+  const int dim = threadIdx.x % D;
   const int32_t* s4 = state + 4 * u;
   const int nh = s4[0], nl = s4[1], ph = s4[2], pl = s4[3];
-  if (!state_valid(nh, nl, ph, pl, L) || pj >= ph + pl) return;
-  const bool hi = pj < ph;
-  const int jt = hi ? pj : pj - ph;
-  const int32_t id = table[u * L + (hi ? jt : L - 1 - jt)];
-  if (id < 0 || id >= P) return;
-  const int nv = hi ? min(kHiTokens, nh - kHiTokens * jt) : min(kLoTokens, nl - kLoTokens * jt);
-  const Seg sg = tier_seg(D, hi);
-  const uint8_t* pg = pages + (int64_t)id * page_bytes;
-  float mn = INFINITY, mx = -INFINITY;
-  for (int t = 0; t < nv; t++) {
-    int byte, shift;
-    k_field(D, hi, t, dim, byte, shift);
-    const uint32_t code = (uint32_t)(pg[sg.kc + byte] >> shift) & (hi ? 0xFFu : 0xFu);
-    const uint32_t m = *(const uint32_t*)(pg + sg.km + 4 * t);
-    const float x = dequant(h2f((uint16_t)m), h2f((uint16_t)(m >> 16)), code);
-    mn = fminf(mn, x);
-    mx = fmaxf(mx, x);
+  if (!state_valid(nh, nl, ph, pl, L)) return;
+  for (int pj = blockIdx.x * PPB + threadIdx.x / D; pj < ph + pl; pj += gridDim.x * PPB) {
+    const bool hi = pj < ph;  // uniform over the page's D threads (whole waves)
+    const int jt = hi ? pj : pj - ph;
+    const int32_t id = table[u * L + (hi ? jt : L - 1 - jt)];
+    if (id < 0 || id >= P) continue;
+    const int nv = hi ? min(kHiTokens, nh - kHiTokens * jt) : min(kLoTokens, nl - kLoTokens * jt);
+    const uint8_t* pg = pages + (int64_t)id * page_bytes;
+    float mn, mx;
+    if (hi) page_dim_bounds<D, true>(pg, nv, dim, mn, mx);
+    else page_dim_bounds<D, false>(pg, nv, dim, mn, mx);
+    float* bo = bounds + (int64_t)id * 2 * D;
+    bo[dim] = mn;
+    bo[D + dim] = mx;
   }
-  float* b = bounds + (int64_t)id * 2 * D;
-  b[dim] = mn;
-  b[D + dim] = mx;
 }
 
 // scores [U][L] in table order
@@ -74,35 +99,60 @@ __global__ __launch_bounds__(kBThreads) void page_scores_kernel(int H, int G, in
                                                                const int32_t* __restrict__ seq_len,
                                                                const float* __restrict__ bounds,
                                                                float* __restrict__ scores) {
-  constexpr int PPB = kBThreads / D;
-  constexpr int WPP = D / 64;  // waves per page
+  constexpr int WPB = kBThreads / 64;  // waves (table entries) per workgroup and round
+  constexpr int DPL = D / 64;          // dimensions per lane: 2l, 2l + 1 (d = 128) or l (d = 64)
   const int64_t u = blockIdx.y;
   const int b = (int)(u / H), h = (int)(u % H);
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int pp = tid / D, dim = tid % D;
-  const int tix = blockIdx.x * PPB + pp;  // table index of this thread's page
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int32_t* s4 = state + 4 * u;
   const int nh = s4[0], nl = s4[1], ph = s4[2], pl = s4[3];
-  const bool live = seq_len[b] > 0 && state_valid(nh, nl, ph, pl, L) && tix < L && (tix < ph || tix >= L - pl);
-  const int32_t id = live ? table[u * L + tix] : -1;
-  const bool ok = live && id >= 0 && id < P;
-  const float* bp = bounds + (int64_t)(ok ? id : 0) * 2 * D;
-  const float mn = ok ? bp[dim] : 0.0f, mx = ok ? bp[D + dim] : 0.0f;
-  __shared__ float part[kBThreads / 64];
-  float best = -INFINITY;
-  for (int g = 0; g < G; g++) {
-    const float qe = h2f(q[((int64_t)b * H * G + (int64_t)h * G + g) * D + dim]);
-    float v = fmaxf(qe * mn, qe * mx);
-    v = wave_sum(v);  // the 64 dims of this wave, fixed butterfly order
-    __syncthreads();
-    if (lane == 0) part[wid] = v;
-    __syncthreads();
-    float s = 0.0f;
+  const bool unit_ok = seq_len[b] > 0 && state_valid(nh, nl, ph, pl, L);
+  // the group's query elements of this lane's dimensions (fp16 bits)
+  uint32_t qw[16];
+  const uint16_t* qb = q + ((int64_t)b * H * G + (int64_t)h * G) * D;
 #pragma unroll
-    for (int w = 0; w < WPP; w++) s += part[pp * WPP + w];
-    best = fmaxf(best, s);
+  for (int g = 0; g < 16; g++) {
+    if (g >= G || !unit_ok) {
+      qw[g] = 0u;
+    } else if constexpr (DPL == 2) {
+      qw[g] = *(const uint32_t*)(qb + (int64_t)g * D + 2 * lane);
+    } else {
+      qw[g] = qb[(int64_t)g * D + lane];
+    }
   }
-  if (dim == 0 && tix < L) scores[u * L + tix] = ok ? best : -INFINITY;
+  for (int tix = blockIdx.x * WPB + wid; tix < L; tix += gridDim.x * WPB) {
+    const bool live = unit_ok && (tix < ph || tix >= L - pl);
+    const int32_t id = live ? table[u * L + tix] : -1;
+    const bool ok = live && id >= 0 && id < P;  // uniform over the wave
+    float best = -INFINITY;
+    if (ok) {
+      const float* bp = bounds + (int64_t)id * 2 * D;
+      float mn[DPL], mx[DPL];
+      if constexpr (DPL == 2) {
+        const float2 a = *(const float2*)(bp + 2 * lane), c = *(const float2*)(bp + D + 2 * lane);
+        mn[0] = a.x;
+        mn[1] = a.y;
+        mx[0] = c.x;
+        mx[1] = c.y;
+      } else {
+        mn[0] = bp[lane];
+        mx[0] = bp[D + lane];
+      }
+#pragma unroll
+      for (int g = 0; g < 16; g++) {
+        if (g < G) {  // (G is uniform)
+          float v = 0.0f;
+#pragma unroll
+          for (int e = 0; e < DPL; e++) {
+            const float qe = h2f((uint16_t)(qw[g] >> (16 * e)));
+            v += fmaxf(qe * mn[e], qe * mx[e]);
+          }
+          best = fmaxf(best, wave_sum(v));  // fixed butterfly order
+        }
+      }
+    }
+    if (lane == 0) scores[u * L + tix] = best;
+  }
 }
 
 hipError_t launch_page_bounds(const Cfg& c, const Pool& p, int batch, const int32_t* table, const int32_t* state,
@@ -110,7 +160,8 @@ hipError_t launch_page_bounds(const Cfg& c, const Pool& p, int batch, const int3
   const int64_t U = (int64_t)batch * c.H;
   if (U == 0) return hipSuccess;
   const int ppb = kBThreads / c.d;
-  const dim3 grid((unsigned)((c.L + ppb - 1) / ppb), (unsigned)U), block(kBThreads);
+  const int gx = min((c.L + ppb - 1) / ppb, kBoundsWgPerUnit);
+  const dim3 grid((unsigned)gx, (unsigned)U), block(kBThreads);
   if (c.d == 128)
     page_bounds_kernel<128><<<grid, block, 0, s>>>(c.L, p.P, p.page_bytes, table, state, p.pages, bounds);
   else
@@ -123,8 +174,9 @@ hipError_t launch_page_scores(const Cfg& c, int64_t P, int batch, const uint16_t
                               hipStream_t s) {
   const int64_t U = (int64_t)batch * c.H;
   if (U == 0) return hipSuccess;
-  const int ppb = kBThreads / c.d;
-  const dim3 grid((unsigned)((c.L + ppb - 1) / ppb), (unsigned)U), block(kBThreads);
+  constexpr int wpb = kBThreads / 64;
+  const int gx = min((c.L + wpb - 1) / wpb, kBoundsWgPerUnit);
+  const dim3 grid((unsigned)gx, (unsigned)U), block(kBThreads);
   if (c.d == 128)
     page_scores_kernel<128><<<grid, block, 0, s>>>(c.H, c.G, c.L, P, q, table, state, seq_len, bounds, scores);
   else

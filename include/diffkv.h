@@ -199,9 +199,11 @@ int diffkv_page_bounds(const diffkv_config* cfg, const diffkv_pool* pool, int32_
  * could have with any key of the page, sum_i max(q_i kmin_i, q_i kmax_i),
  * combined over the KV head's q heads with max (the aggregation used for
  * token scores); a decode step can skip the pages whose score is low.
- *  q fp16 [batch, H*G, d]; seq_len int32 [batch] (<= 0: inactive);
+ *  q fp16 [batch, H*G, d] (4-byte aligned); seq_len int32 [batch] (<= 0:
+ *  inactive); bounds as diffkv_page_bounds wrote them (8-byte aligned);
  *  scores fp32 [batch, H, L] out in table order, -inf at empty entries and
- *  for inactive requests.  fp32 with fixed-order sums. */
+ *  for inactive requests.  fp32 with fixed-order sums.  DIFFKV_E_INVALID on
+ *  a misaligned q or bounds. */
 int diffkv_page_scores(const diffkv_config* cfg, const diffkv_pool* pool, int32_t batch, const uint16_t* q,
                        const int32_t* page_table, const int32_t* tier_state, const int32_t* seq_len,
                        const float* bounds, float* scores, void* stream);

@@ -78,3 +78,28 @@ def test_decode_step_host_validation():
         att = dk.diffkv_workspace_bytes(c, dk.ATTN_SCORES, b)
         r = lambda x: -(-x // 256) * 256
         assert dk.diffkv_workspace_bytes(c, dk.DECODE_STEP_SCORES, b) == r(step) + r(att) + step
+
+
+def test_policy_and_bounds_host_validation():
+    """The policy fields are checked with the config (prompt_rule 0 or 1;
+    both per-head arrays or neither), and diffkv_page_scores refuses a query
+    or bounds pointer its paired loads cannot use (batch 0: nothing would
+    run either way)."""
+    import compressed_paged_attention_amd as dk
+    from workloads import synth
+    c = synth.config("llama3_8b")
+    L = dk.lib()
+    assert dk.diffkv_page_bytes(dict(c, prompt_rule=1)) == 3584
+    assert dk.diffkv_page_bytes(dict(c, prompt_rule=2)) == -1
+    fake = 1 << 20  # never dereferenced on the host
+    one = dk.make_config(c)
+    one.alpha_h_head = fake
+    assert L.diffkv_page_bytes(ctypes.byref(one)) == -1
+    one.alpha_l_head = fake
+    assert L.diffkv_page_bytes(ctypes.byref(one)) == 3584
+    cfg = dk.make_config(c)
+    pool = dk.diffkv_pool(fake, fake, fake, fake, 10, 3584)
+    ok = [fake] * 6  # q, page_table, tier_state, seq_len, bounds, scores
+    assert L.diffkv_page_scores(ctypes.byref(cfg), ctypes.byref(pool), 0, *ok, None) == dk.DIFFKV_OK
+    for bad in ([fake + 2] + [fake] * 5, [fake] * 4 + [fake + 4, fake]):
+        assert L.diffkv_page_scores(ctypes.byref(cfg), ctypes.byref(pool), 0, *bad, None) == dk.DIFFKV_E_INVALID
