@@ -138,8 +138,8 @@ __host__ __device__ inline int split_pages(int TPg, int S) {
   return q > kSplitMinPages ? q : kSplitMinPages;
 }
 
-// Score-update chunks (several splits, or a deferred update): 16 pages each.
-constexpr int kScorePages = 16;
+// Score-update chunks (several splits, or a deferred update): 64 pages each.
+constexpr int kScorePages = 64;
 constexpr int kCandWords = 8;  // per chunk: least important high / low candidate, t_c
 
 struct AttnWs {
@@ -1274,15 +1274,19 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(int H, int G, int S, co
 }
 
 // Score update from saved logits (several splits, or a deferred update):
-// 16 pages (512 slots, 2 per thread) per workgroup.  A unit whose merge found a bad page id
-// has (M, L) = (-inf, 0) and is left alone; ids are checked where they are
-// used.  Each chunk also leaves the candidates the next generation step
-// (length N + 1) needs: the least important non-window high token, the least
-// important low token and the token leaving the window, from the updated
-// sums (the rules of the fused update); score_finish_kernel turns them into
-// the unit's plan record.
+// 64 pages per workgroup, their slots enumerated as the fused pass does (16
+// per high page, 32 per low page: at most 2048, 8 per thread); every load of a
+// thread's slots (table entries, GB-float logit rows as 16-byte loads, then
+// positions and old sums) is issued before any is used, and each slot takes
+// one exponential: max_g p_g = 2^(max_g (x_g + c_g)), c_g = -M_g - log2 L_g.
+// A unit whose merge found a bad page id has (M, L) = (-inf, 0) and is left
+// alone; ids are checked where they are used.  Each chunk also leaves the
+// candidates the next generation step (length N + 1) needs: the least
+// important non-window high token, the least important low token and the
+// token leaving the window, from the updated sums (the rules of the fused
+// update); score_finish_kernel turns them into the unit's plan record.
 
-template <int D>
+template <int D, int GB>
 __global__ __launch_bounds__(256) void score_kernel(int H, int G, int L, int64_t P, int page_bytes, int W,
                                                     const int32_t* __restrict__ table,
                                                     const int32_t* __restrict__ state,
@@ -1308,59 +1312,82 @@ __global__ __launch_bounds__(256) void score_kernel(int H, int G, int L, int64_t
     const int32_t id0 = row[0];
     if (id0 >= 0 && id0 < P) *(uint32_t*)(pages + (int64_t)id0 * page_bytes + plan_rec_off<D>()) = 0u;
   }
-  __shared__ float sM[16], sI[16];
-  __shared__ int s_tc;  // slot of the token leaving the window at length N + 1
+  __shared__ float sC[16];  // c_g = -M_g - log2 L_g (-inf: no weight)
+  __shared__ int s_tc;      // slot of the token leaving the window at length N + 1
   __shared__ float s_tcsum;
-  if (tid < G) {
-    sM[tid] = ml[(u * G + tid) * 2 + 0];
-    const float l = ml[(u * G + tid) * 2 + 1];
-    sI[tid] = l > 0.0f ? 1.0f / l : 0.0f;
+  if (tid < GB) {
+    const float M = tid < G ? ml[(u * G + tid) * 2 + 0] : -INFINITY;
+    const float l = tid < G ? ml[(u * G + tid) * 2 + 1] : 0.0f;
+    sC[tid] = (M == -INFINITY || !(l > 0.0f)) ? -INFINITY : __builtin_amdgcn_logf(1.0f / l) - M;
   }
   if (tid == 0) s_tc = -1;
-  __syncthreads();
+  // the chunk's slots: high pages (16 slots) first, then low pages (32)
+  const int nhp = max(0, min(ph, p1) - p0);
+  const int NE = 16 * nhp + 32 * (p1 - p0 - nhp);
+  auto slot_of = [&](int xe, int& j, int& t) {
+    if (xe < 16 * nhp) {
+      j = p0 + (xe >> 4);
+      t = xe & 15;
+    } else {
+      const int y = xe - 16 * nhp;
+      j = p0 + nhp + (y >> 5);
+      t = y & 31;
+    }
+  };
   const Seg sh = tier_seg(D, true), sl = tier_seg(D, false);
-  // SPT slots per thread, the loads of all issued before any is used
   constexpr int SPT = kScorePages * 32 / 256;
-  const int n = (p1 - p0) * 32;
-  int32_t id[SPT], tx[SPT];
+  int32_t id[SPT], jx[SPT], tt[SPT];
   bool ok[SPT];
+  float lv[SPT][GB];
 #pragma unroll
   for (int e = 0; e < SPT; e++) {
-    const int x = tid + 256 * e;
-    const int j = p0 + min(x, n - 1) / 32, t = x % 32;
+    const int xe = tid + 256 * e;
+    int j, t;
+    slot_of(min(xe, NE - 1), j, t);
     const bool is_hi = j < ph;
     const int jt = is_hi ? j : j - ph;
     const int nval = is_hi ? min(kHiTokens, nh - kHiTokens * jt) : min(kLoTokens, nl - kLoTokens * jt);
-    tx[e] = is_hi ? jt : L - 1 - jt;
-    id[e] = row[tx[e]];
-    ok[e] = x < n && t < nval;
+    const int tx = is_hi ? jt : L - 1 - jt;
+    jx[e] = j;
+    tt[e] = t;
+    id[e] = row[tx];
+    ok[e] = xe < NE && t < nval;
+    const float4_t* src = (const float4_t*)(logits + (((int64_t)u * L + tx) * 32 + t) * GB);
+#pragma unroll
+    for (int c4 = 0; c4 < GB / 4; c4++) {
+      const float4_t v4 = src[c4];
+#pragma unroll
+      for (int k = 0; k < 4; k++) lv[e][4 * c4 + k] = v4[k];
+    }
   }
   int32_t pos[SPT];
-  float old[SPT], mx[SPT];
+  float old[SPT];
   float* sc[SPT];
 #pragma unroll
   for (int e = 0; e < SPT; e++) {
-    mx[e] = 0.0f;
-    const int x = tid + 256 * e, t = x % 32;
-    const bool is_hi = p0 + min(x, n - 1) / 32 < ph;
+    const bool is_hi = jx[e] < ph;
     ok[e] = ok[e] && id[e] >= 0 && id[e] < P;
     const uint8_t* pg = pages + (int64_t)(ok[e] ? id[e] : 0) * page_bytes;
-    pos[e] = ok[e] ? *(const int32_t*)(pg + (is_hi ? sh.ps : sl.ps) + 4 * t) : N;
-    sc[e] = (float*)(pg + (is_hi ? sh.sc : sl.sc) + 4 * t);
+    pos[e] = ok[e] ? *(const int32_t*)(pg + (is_hi ? sh.ps : sl.ps) + 4 * tt[e]) : N;
+    sc[e] = (float*)(pg + (is_hi ? sh.sc : sl.sc) + 4 * tt[e]);
     old[e] = ok[e] ? *sc[e] : 0.0f;
-    const float* lg = logits + (((int64_t)u * L + tx[e]) * 32 + t) * logit_stride(G);
-    for (int g = 0; g < G; g++) mx[e] = fmaxf(mx[e], __builtin_amdgcn_exp2f(lg[g] - sM[g]) * sI[g]);
   }
+  __syncthreads();  // sC, s_tc
+  float cg[GB];
+#pragma unroll
+  for (int g = 0; g < GB; g++) cg[g] = sC[g];
   const int64_t N1 = (int64_t)N + 1, tc1 = N1 - W;
   __shared__ Cand cw[2][4];
   Cand bh{0.0f, kNoPos, 0}, bl{0.0f, kNoPos, 0};
 #pragma unroll
   for (int e = 0; e < SPT; e++) {
-    const int x = tid + 256 * e, t = x % 32;
-    const int j = p0 + min(x, n - 1) / 32;
+    const int j = jx[e], t = tt[e];
     const bool is_hi = j < ph;
     const bool upd = ok[e] && pos[e] < N;
-    const float ns = old[e] + mx[e];
+    float xm = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < GB; g++) xm = fmaxf(xm, lv[e][g] + cg[g]);
+    const float ns = old[e] + __builtin_amdgcn_exp2f(xm);
     if (upd) *sc[e] = ns;
     const int ls = is_hi ? 16 * j + t : 32 * (j - ph) + t;
     if (upd && is_hi && pos[e] == tc1) {  // positions are unique: one writer
@@ -1462,17 +1489,25 @@ hipError_t launch_scores(const Cfg& c, const Pool& p, int batch, const int32_t* 
   AttnWs w = attn_carve(c, batch, true, ws, nullptr);
   const dim3 grid((unsigned)((c.L + kScorePages - 1) / kScorePages), (unsigned)U), block(256);
   const PolicyArgs pa{c.W, c.S_max, c.lo_en, c.ah, c.al, c.ah_head, c.al_head};
+  const int GS = logit_stride(c.G);
+#define DKV_SCORE(D, GB)                                                                                 \
+  score_kernel<D, GB><<<grid, block, 0, s>>>(c.H, c.G, c.L, p.P, p.page_bytes, c.W, table, state, seq_len, \
+                                             w.ml, w.logits, p.pages, w.cand)
+#define DKV_SCORE_D(D)                  \
+  if (GS == 4) DKV_SCORE(D, 4);         \
+  else if (GS == 8) DKV_SCORE(D, 8);    \
+  else DKV_SCORE(D, 16);
   if (c.d == 128) {
-    score_kernel<128><<<grid, block, 0, s>>>(c.H, c.G, c.L, p.P, p.page_bytes, c.W, table, state, seq_len, w.ml,
-                                             w.logits, p.pages, w.cand);
+    DKV_SCORE_D(128)
     score_finish_kernel<128><<<dim3((unsigned)U), dim3(64), 0, s>>>(c.H, c.G, c.L, p.P, p.page_bytes, pa, table,
                                                                     state, seq_len, w.ml, w.cand, p.pages);
   } else {
-    score_kernel<64><<<grid, block, 0, s>>>(c.H, c.G, c.L, p.P, p.page_bytes, c.W, table, state, seq_len, w.ml,
-                                            w.logits, p.pages, w.cand);
+    DKV_SCORE_D(64)
     score_finish_kernel<64><<<dim3((unsigned)U), dim3(64), 0, s>>>(c.H, c.G, c.L, p.P, p.page_bytes, pa, table,
                                                                    state, seq_len, w.ml, w.cand, p.pages);
   }
+#undef DKV_SCORE_D
+#undef DKV_SCORE
   return hipGetLastError();
 }
 
