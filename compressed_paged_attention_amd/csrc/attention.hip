@@ -832,17 +832,19 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
       // the page ids the score pass visits (workspace logits: the LDS area
       // holds only the ids)
       if (MODE == 1 && lane == 0 && (kLds || ids_lds)) (kLds ? id_s : (int32_t*)lds_w)[j] = R.id;
-      // logits: LDS g-major [G][TPg * 32]; workspace [L][32][GS] by table
-      // slot, every lane below GS storing (lanes G..GS-1 hold finite values
-      // the score pass masks), so a slot is read with 16-byte loads
+      // logits: LDS g-major [G][TPg * 32]; workspace by table slot in the
+      // lanes' own order, [L][32/4][GS][4]: the four consecutive tokens a
+      // lane holds for one head are one 16-byte store, every lane below GS
+      // storing (lanes G..GS-1 hold finite values the score pass masks)
       float* lgp = kLds ? lg_s + i * (TPg * 32) + j * 32 : logits + ((int64_t)u * L + table_idx(j)) * 32 * GS;
       compute_page<D, PACK>(R, j < ph, valid(j), qop, sq2, scale_log2, tm, qg, sm, acc, [&](int mb, const float* x) {
         if (!SAVE || i >= (kLds ? G : GS)) return;
         const int t0 = 16 * mb + 4 * qg;
+        if (kLds) {
 #pragma unroll
-        for (int r = 0; r < 4; r++) {
-          if (kLds) lgp[t0 + r] = x[r];
-          else lgp[(t0 + r) * GS + i] = x[r];
+          for (int r = 0; r < 4; r++) lgp[t0 + r] = x[r];
+        } else {
+          *(float4_t*)(lgp + ((t0 >> 2) * GS + i) * 4) = float4_t{x[0], x[1], x[2], x[3]};
         }
       });
     };
@@ -994,80 +996,112 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
           t = y & 31;
         }
       };
-      // kU slots per thread per round: all loads of a round are issued
-      // before any use; GB >= G logits per slot (LDS: indices clamped to
-      // G - 1, repeats do not change a maximum; workspace: GB = GS floats
-      // per slot, heads G..GB-1 masked by c = -inf)
-      auto pass = [&](auto lds_tag, auto gb_tag) {
-        constexpr bool kLds = decltype(lds_tag)::value;
-        constexpr int GB = decltype(gb_tag)::value;
-        constexpr int kU = kLds ? 1 : 8;  // LDS reads need no batching
-        // max_g 2^(x_g - M_g) / L_g = 2^(max_g (x_g + c_g)), c_g = -M_g - log2 L_g:
-        // one exponential per slot
-        float cg[GB];
-#pragma unroll
+      // c_g with max_g 2^(x_g - M_g) / L_g = 2^(max_g (x_g + c_g)),
+      // c_g = -M_g - log2 L_g: one exponential per slot.  GB >= G heads per
+      // slot (LDS: indices clamped to G - 1, repeats do not change a maximum;
+      // workspace: GB = GS, heads G..GB-1 masked by c = -inf)
+      auto cvec = [&](float* cg, int GB, bool lds) {
         for (int g = 0; g < GB; g++) {
           const float M = sM[min(g, G - 1)], I = sI[min(g, G - 1)];
-          cg[g] = (M == -INFINITY || I == 0.0f || (!kLds && g >= G)) ? -INFINITY : __builtin_amdgcn_logf(I) - M;
+          cg[g] = (M == -INFINITY || I == 0.0f || (!lds && g >= G)) ? -INFINITY : __builtin_amdgcn_logf(I) - M;
         }
-        const float* lgg = logits + (int64_t)u * L * 32 * GB;
+      };
+      // one slot's new sum: t_c's sum published, the tier's running
+      // candidate updated with one comparison
+      auto visit = [&](bool ok, bool hi, int j, int t, float ns, int32_t pos) {
+        const int ls = hi ? 16 * j + t : 32 * (j - ph) + t;
+        if (ok && hi && pos == tc1) {  // positions are unique: one writer
+          s_tc = ls;
+          s_tcsum = ns;
+        }
+        const Cand c{ns, (ok && (!hi || pos <= tc1)) ? pos : kNoPos, ls};
+        const Cand a{hi ? bh.sum : bl.sum, hi ? bh.pos : bl.pos, hi ? bh.slot : bl.slot};
+        const bool win = less_imp(c, a, N1);
+        if (win && hi) bh = c;
+        if (win && !hi) bl = c;
+      };
+      // logits in LDS: one slot per thread and round
+      auto pass_lds = [&](auto gb_tag) {
+        constexpr int GB = decltype(gb_tag)::value;
+        float cg[GB];
+#pragma unroll
+        for (int g = 0; g < GB; g++) cg[g] = 0.0f;
+        cvec(cg, GB, true);
         // wave-uniform trip count: a wave runs while its first slot is in range
-        for (int x0 = tid; x0 - lane < NE; x0 += kU * kThreads) {
-          float lv[kU][GB], osv[kU];
-          int32_t psv[kU];
-          uint8_t* pgv[kU];
+        for (int xe = tid; xe - lane < NE; xe += kThreads) {
+          int j, t;
+          slot_of(min(xe, NE - 1), j, t);
+          const int x = 32 * j + t;
+          const bool hi = j < ph;
+          float xm = -INFINITY;
 #pragma unroll
-          for (int e = 0; e < kU; e++) {
+          for (int g = 0; g < GB; g++) xm = fmaxf(xm, lg_s[min(g, G - 1) * NSL + x] + cg[g]);
+          const int32_t pos = pos_s[x];
+          const bool ok = xe < NE && t < valid(j) && pos < N;
+          const float ns = osc_s[x] + __builtin_amdgcn_exp2f(xm);
+          uint8_t* pg = pages + (int64_t)id_s[j] * page_bytes;
+          // non-temporal: these words are read again only by a later
+          // step, and the launch then ends with fewer dirty lines to write back
+          if (ok) __builtin_nontemporal_store(ns, (float*)(pg + (hi ? sh.sc : sl.sc) + 4 * t));
+          visit(ok, hi, j, t, ns, pos);
+        }
+      };
+      // logits in the workspace, [L][32/4][GB][4] per unit: four consecutive
+      // slots of a page per thread (pages hold 16 or 32 slots, so a group
+      // never straddles two), kUG groups per round with every load issued
+      // before any use; a group's sums are stored as one 16-byte word (slots
+      // that do not change are stored back unchanged)
+      auto pass_ws = [&](auto gb_tag) {
+        constexpr int GB = decltype(gb_tag)::value;
+        constexpr int kUG = 2;
+        float cg[GB];
+#pragma unroll
+        for (int g = 0; g < GB; g++) cg[g] = 0.0f;
+        cvec(cg, GB, false);
+        const float* lgg = logits + (int64_t)u * L * 32 * GB;
+        const int NG = NE >> 2;  // NE is a multiple of 16
+        for (int x0 = tid; x0 - lane < NG; x0 += kUG * kThreads) {
+          float lv[kUG][GB][4];
+          float4_t osv[kUG];
+          int4 psv[kUG];
+          uint8_t* pgv[kUG];
+#pragma unroll
+          for (int e = 0; e < kUG; e++) {
             int j, t;
-            slot_of(min(x0 + e * kThreads, NE - 1), j, t);
-            const int x = 32 * j + t;
+            slot_of(4 * min(x0 + e * kThreads, NG - 1), j, t);
             const bool hi = j < ph;
-            if (kLds) {
+            const int tx = table_idx(j);
+            const float4_t* src = (const float4_t*)(lgg + ((int64_t)tx * 32 + t) * GB);
 #pragma unroll
-              for (int g = 0; g < GB; g++) lv[e][g] = lg_s[min(g, G - 1) * NSL + x];
-              osv[e] = osc_s[x];
-              psv[e] = pos_s[x];
-              pgv[e] = pages + (int64_t)id_s[j] * page_bytes;
-            } else {
-              const int tx = table_idx(j);
-              const float4_t* src = (const float4_t*)(lgg + (tx * 32 + t) * GB);
+            for (int g = 0; g < GB; g++) {
+              const float4_t v4 = src[g];
 #pragma unroll
-              for (int c = 0; c < GB / 4; c++) {
-                const float4_t v4 = src[c];
-#pragma unroll
-                for (int k = 0; k < 4; k++) lv[e][4 * c + k] = v4[k];
-              }
-              pgv[e] = pages + (int64_t)(ids_lds ? ((const int32_t*)lds_w)[j] : id_tix(tx)) * page_bytes;
-              const int tt = min(t, hi ? kHiTokens - 1 : kLoTokens - 1);
-              osv[e] = *(const float*)(pgv[e] + (hi ? sh.sc : sl.sc) + 4 * tt);
-              psv[e] = *(const int32_t*)(pgv[e] + (hi ? sh.ps : sl.ps) + 4 * tt);
+              for (int r = 0; r < 4; r++) lv[e][g][r] = v4[r];
             }
+            pgv[e] = pages + (int64_t)(ids_lds ? ((const int32_t*)lds_w)[j] : id_tix(tx)) * page_bytes;
+            osv[e] = *(const float4_t*)(pgv[e] + (hi ? sh.sc : sl.sc) + 4 * t);
+            psv[e] = *(const int4*)(pgv[e] + (hi ? sh.ps : sl.ps) + 4 * t);
           }
 #pragma unroll
-          for (int e = 0; e < kU; e++) {
-            const int xe = x0 + e * kThreads;
+          for (int e = 0; e < kUG; e++) {
+            const int xg = x0 + e * kThreads;
             int j, t;
-            slot_of(min(xe, NE - 1), j, t);
+            slot_of(4 * min(xg, NG - 1), j, t);
             const bool hi = j < ph;
-            const bool ok = xe < NE && t < valid(j) && psv[e] < N;
-            float xm = -INFINITY;
+            const int nv = valid(j);
+            const int32_t pv[4] = {psv[e].x, psv[e].y, psv[e].z, psv[e].w};
+            float4_t nsv;
 #pragma unroll
-            for (int g = 0; g < GB; g++) xm = fmaxf(xm, lv[e][g] + cg[g]);
-            const float ns = osv[e] + __builtin_amdgcn_exp2f(xm);
-            const int ls = hi ? 16 * j + t : 32 * (j - ph) + t;
-            // non-temporal: these words are read again only by a later
-            // step, and the launch then ends with fewer dirty lines to write back
-            if (ok) __builtin_nontemporal_store(ns, (float*)(pgv[e] + (hi ? sh.sc : sl.sc) + 4 * t));
-            if (ok && hi && psv[e] == tc1) {  // positions are unique: one writer
-              s_tc = ls;
-              s_tcsum = ns;
+            for (int r = 0; r < 4; r++) {
+              const bool ok = xg < NG && t + r < nv && pv[r] < N;
+              float xm = -INFINITY;
+#pragma unroll
+              for (int g = 0; g < GB; g++) xm = fmaxf(xm, lv[e][g][r] + cg[g]);
+              const float ns = osv[e][r] + __builtin_amdgcn_exp2f(xm);
+              nsv[r] = ok ? ns : osv[e][r];
+              visit(ok, hi, j, t + r, ns, pv[r]);
             }
-            // one comparison per slot, against the running candidate of its tier
-            const Cand c{ns, (ok && (!hi || psv[e] <= tc1)) ? psv[e] : kNoPos, ls};
-            const Cand a{hi ? bh.sum : bl.sum, hi ? bh.pos : bl.pos, hi ? bh.slot : bl.slot};
-            const bool win = less_imp(c, a, N1);
-            if (win && hi) bh = c;
-            if (win && !hi) bl = c;
+            if (xg < NG) __builtin_nontemporal_store(nsv, (float4_t*)(pgv[e] + (hi ? sh.sc : sl.sc) + 4 * t));
           }
         }
       };
@@ -1075,13 +1109,13 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
       using I8 = std::integral_constant<int, 8>;
       using I16 = std::integral_constant<int, 16>;
       if (lg_lds) {
-        if (G <= 4) pass(std::true_type{}, I4{});
-        else if (G <= 8) pass(std::true_type{}, I8{});
-        else pass(std::true_type{}, I16{});
+        if (G <= 4) pass_lds(I4{});
+        else if (G <= 8) pass_lds(I8{});
+        else pass_lds(I16{});
       } else {
-        if (G <= 4) pass(std::false_type{}, I4{});
-        else if (G <= 8) pass(std::false_type{}, I8{});
-        else pass(std::false_type{}, I16{});
+        if (G <= 4) pass_ws(I4{});
+        else if (G <= 8) pass_ws(I8{});
+        else pass_ws(I16{});
       }
       // The next step's plan needs at most one of the two candidates: the
       // class of the token leaving the window decides (high: the least
@@ -1275,10 +1309,12 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(int H, int G, int S, co
 
 // Score update from saved logits (several splits, or a deferred update):
 // 64 pages per workgroup, their slots enumerated as the fused pass does (16
-// per high page, 32 per low page: at most 2048, 8 per thread); every load of a
-// thread's slots (table entries, GB-float logit rows as 16-byte loads, then
-// positions and old sums) is issued before any is used, and each slot takes
-// one exponential: max_g p_g = 2^(max_g (x_g + c_g)), c_g = -M_g - log2 L_g.
+// per high page, 32 per low page: at most 2048, in groups of four
+// consecutive slots, two groups per thread); every load of a thread's groups
+// (table entries, the group's logits as GB 16-byte loads, then positions and
+// old sums) is issued before any is used, each slot takes one exponential:
+// max_g p_g = 2^(max_g (x_g + c_g)), c_g = -M_g - log2 L_g, and a group's new
+// sums are stored as one 16-byte word.
 // A unit whose merge found a bad page id has (M, L) = (-inf, 0) and is left
 // alone; ids are checked where they are used.  Each chunk also leaves the
 // candidates the next generation step (length N + 1) needs: the least
@@ -1335,42 +1371,43 @@ __global__ __launch_bounds__(256) void score_kernel(int H, int G, int L, int64_t
     }
   };
   const Seg sh = tier_seg(D, true), sl = tier_seg(D, false);
-  constexpr int SPT = kScorePages * 32 / 256;
-  int32_t id[SPT], jx[SPT], tt[SPT];
-  bool ok[SPT];
-  float lv[SPT][GB];
+  // groups of four consecutive slots of a page (logits [L][32/4][GB][4] per
+  // unit, as the attention stores them)
+  constexpr int GPT = kScorePages * 32 / 4 / 256;  // groups per thread
+  const int NG = NE >> 2;
+  int32_t id[GPT], jx[GPT], tt[GPT];
+  float lv[GPT][GB][4];
 #pragma unroll
-  for (int e = 0; e < SPT; e++) {
-    const int xe = tid + 256 * e;
+  for (int e = 0; e < GPT; e++) {
+    const int xg = tid + 256 * e;
     int j, t;
-    slot_of(min(xe, NE - 1), j, t);
+    slot_of(4 * min(xg, NG - 1), j, t);
     const bool is_hi = j < ph;
     const int jt = is_hi ? j : j - ph;
-    const int nval = is_hi ? min(kHiTokens, nh - kHiTokens * jt) : min(kLoTokens, nl - kLoTokens * jt);
     const int tx = is_hi ? jt : L - 1 - jt;
     jx[e] = j;
     tt[e] = t;
     id[e] = row[tx];
-    ok[e] = xe < NE && t < nval;
     const float4_t* src = (const float4_t*)(logits + (((int64_t)u * L + tx) * 32 + t) * GB);
 #pragma unroll
-    for (int c4 = 0; c4 < GB / 4; c4++) {
-      const float4_t v4 = src[c4];
+    for (int g = 0; g < GB; g++) {
+      const float4_t v4 = src[g];
 #pragma unroll
-      for (int k = 0; k < 4; k++) lv[e][4 * c4 + k] = v4[k];
+      for (int r = 0; r < 4; r++) lv[e][g][r] = v4[r];
     }
   }
-  int32_t pos[SPT];
-  float old[SPT];
-  float* sc[SPT];
+  int4 pos[GPT];
+  float4_t old[GPT];
+  uint8_t* pgs[GPT];
+  bool okp[GPT];
 #pragma unroll
-  for (int e = 0; e < SPT; e++) {
+  for (int e = 0; e < GPT; e++) {
     const bool is_hi = jx[e] < ph;
-    ok[e] = ok[e] && id[e] >= 0 && id[e] < P;
-    const uint8_t* pg = pages + (int64_t)(ok[e] ? id[e] : 0) * page_bytes;
-    pos[e] = ok[e] ? *(const int32_t*)(pg + (is_hi ? sh.ps : sl.ps) + 4 * tt[e]) : N;
-    sc[e] = (float*)(pg + (is_hi ? sh.sc : sl.sc) + 4 * tt[e]);
-    old[e] = ok[e] ? *sc[e] : 0.0f;
+    okp[e] = tid + 256 * e < NG && id[e] >= 0 && id[e] < P;
+    const uint8_t* pg = pages + (int64_t)(okp[e] ? id[e] : 0) * page_bytes;
+    pgs[e] = (uint8_t*)pg + (is_hi ? sh.sc : sl.sc) + 4 * tt[e];
+    pos[e] = *(const int4*)(pg + (is_hi ? sh.ps : sl.ps) + 4 * tt[e]);
+    old[e] = *(const float4_t*)pgs[e];
   }
   __syncthreads();  // sC, s_tc
   float cg[GB];
@@ -1380,23 +1417,33 @@ __global__ __launch_bounds__(256) void score_kernel(int H, int G, int L, int64_t
   __shared__ Cand cw[2][4];
   Cand bh{0.0f, kNoPos, 0}, bl{0.0f, kNoPos, 0};
 #pragma unroll
-  for (int e = 0; e < SPT; e++) {
-    const int j = jx[e], t = tt[e];
+  for (int e = 0; e < GPT; e++) {
+    const int j = jx[e];
     const bool is_hi = j < ph;
-    const bool upd = ok[e] && pos[e] < N;
-    float xm = -INFINITY;
+    const int jt = is_hi ? j : j - ph;
+    const int nval = is_hi ? min(kHiTokens, nh - kHiTokens * jt) : min(kLoTokens, nl - kLoTokens * jt);
+    const int32_t pv[4] = {pos[e].x, pos[e].y, pos[e].z, pos[e].w};
+    float4_t nsv;
 #pragma unroll
-    for (int g = 0; g < GB; g++) xm = fmaxf(xm, lv[e][g] + cg[g]);
-    const float ns = old[e] + __builtin_amdgcn_exp2f(xm);
-    if (upd) *sc[e] = ns;
-    const int ls = is_hi ? 16 * j + t : 32 * (j - ph) + t;
-    if (upd && is_hi && pos[e] == tc1) {  // positions are unique: one writer
-      s_tc = ls;
-      s_tcsum = ns;
+    for (int r = 0; r < 4; r++) {
+      const int t = tt[e] + r;
+      const bool upd = okp[e] && t < nval && pv[r] < N;
+      float xm = -INFINITY;
+#pragma unroll
+      for (int g = 0; g < GB; g++) xm = fmaxf(xm, lv[e][g][r] + cg[g]);
+      const float ns = old[e][r] + __builtin_amdgcn_exp2f(xm);
+      nsv[r] = upd ? ns : old[e][r];
+      const int ls = is_hi ? 16 * j + t : 32 * (j - ph) + t;
+      if (upd && is_hi && pv[r] == tc1) {  // positions are unique: one writer
+        s_tc = ls;
+        s_tcsum = ns;
+      }
+      const Cand c{ns, (upd && (!is_hi || pv[r] <= tc1)) ? pv[r] : kNoPos, ls};
+      if (is_hi) bh = min_imp(bh, c, N1);
+      else bl = min_imp(bl, c, N1);
     }
-    const Cand c{ns, (upd && (!is_hi || pos[e] <= tc1)) ? pos[e] : kNoPos, ls};
-    if (is_hi) bh = min_imp(bh, c, N1);
-    else bl = min_imp(bl, c, N1);
+    // the group's sums as one word (unchanged slots stored back as they were)
+    if (okp[e]) *(float4_t*)pgs[e] = nsv;
   }
   bh = wave_argmin(bh, N1);
   bl = wave_argmin(bl, N1);
