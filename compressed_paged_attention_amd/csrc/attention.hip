@@ -552,7 +552,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
   // step leaves alone; it then takes a smaller share of those, and the
   // written pages from their images.
   constexpr int kCW = kWaves - 1;     // the committing wave
-  constexpr int kCommitPages = 6;     // its commit, in page computes (share)
+  constexpr int kCommitPages = 10;    // its commit, in page computes (share)
   static_assert(sizeof(buf) >= 2 * page_bytes_for(D), "two page images in the merge buffer");
   __shared__ int s_vd[3 * kWaves];
   __shared__ int32_t s_idt[2];        // ids of the written high and low pages
@@ -716,8 +716,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
   // w + 4) do not progress alike: the hardware prefers the older one, and
   // waves 0-3 end a like share of pages about 15 % sooner (35 % without the
   // score update).  So the pages are cut in two ranges, each taken
-  // round-robin: waves 0-3 the first kShareA/256 of them, the others the
-  // rest.  With a step, the commit wave takes the pages from `cut` up and
+  // round-robin: waves 0-3 the first 150/256 of them (170/256 without the
+  // score update; 170/256 of the pages below `cut` with a step, against
+  // three waves), the others the rest; the shares were measured to end the
+  // waves of a pair together at the 200 GB stress workload.  With a step, the commit wave takes the pages from `cut` up and
   // then the written pages, which everyone else skips; waves 0-3 and 4-6
   // share the pages below `cut`.  The order is static: results do not depend
   // on timing.
@@ -725,13 +727,13 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
   const int cut = TPg - n_cw;
   int lo, hi, stride, off;  // this wave's pages: lo + off, lo + off + stride, ... below hi
   if (!go) {
-    const int nA = ((p1 - p0) * (MODE == 1 ? 137 : 147)) >> 8;
+    const int nA = ((p1 - p0) * (MODE == 1 ? 150 : 170)) >> 8;
     lo = wid < 4 ? p0 : p0 + nA;
     hi = wid < 4 ? p0 + nA : p1;
     stride = 4;
     off = wid & 3;
   } else if (wid < kCW) {
-    const int nA = (cut * 155) >> 8;  // 4 waves against 3
+    const int nA = (cut * 170) >> 8;  // 4 waves against 3
     lo = wid < 4 ? 0 : nA;
     hi = wid < 4 ? nA : cut;
     stride = wid < 4 ? 4 : kCW - 4;
