@@ -14,16 +14,22 @@
 // MI355X mapping.  A dense contraction (every query against every earlier
 // key), so the QK products run on the matrix units
 // (v_mfma_f32_16x16x32_f16: A = 16 queries x 32 dims, B = 32 dims x 16 keys,
-// lane l holds query rows 4(l/16)..+3 of key column l mod 16):
-//   imp_stats_kernel: per (16-query block, q head) the softmax reference and
+// lane l holds query rows 4(l/16)..+3 of key column l mod 16).  A workgroup
+// of 4 waves owns a tile of 64 rows (16 per wave, kept in registers) and
+// walks the other operand in 64-row tiles staged once per workgroup in LDS
+// (rows padded by 16 bytes so the 16 rows a wave reads per instruction fall
+// in different banks), the next tile's global loads in flight during each
+// tile's products:
+//   imp_stats_kernel: per (64-query tile, q head) the softmax reference and
 //     sum over the query's keys, lane-local online (each lane sees one key
-//     column per block, 64 keys per step) merged over the 16 lanes of a row
-//     once; stores c = -(max + log2 sum) in base 2, so a weight is 2^(x + c);
-//   imp_sum_kernel: per (16-key block, KV head) the keys stay in registers
-//     while the wave walks the later query blocks and the group's heads:
+//     column per block) merged over the 16 lanes of a row once; stores
+//     c = -(max + log2 sum) in base 2, so a weight is 2^(x + c);
+//   imp_sum_kernel: per (64-key tile, KV head) the keys stay in registers
+//     while the workgroup walks the later query tiles and, per tile, the
+//     group's heads (each head's query tile and references staged in LDS):
 //     2^(x + c) masked to later queries, max over heads, summed per key;
 //     the mean is written to scores[h][token].
-// Both kernels loop over their blocks with a grid stride, so every length is
+// Both kernels loop over their tiles with a grid stride, so every length is
 // covered whatever the grid.
 #include "dkv_common.hpp"
 #include "dkv_launch.hpp"
@@ -61,6 +67,41 @@ struct QRows {
 
 }  // namespace
 
+constexpr int kTile = 64;  // rows per workgroup tile (16 per wave)
+
+// A 64-row tile of fp16 rows of D, moved by the workgroup's 256 threads in
+// 16-byte chunks: fetch (global -> registers, rows past `n` zero), then put
+// (registers -> LDS rows of D + 8 halfs).
+template <int D>
+struct Tile {
+  static constexpr int CPT = D / 32;  // chunks per thread: 64 rows x D/8 chunks / 256 threads
+  static constexpr int LR = D + 8;    // LDS row, in halfs
+  uint4 v[CPT];
+  template <typename RowPtr>
+  __device__ inline void fetch(int tid, int n0, int n, RowPtr row) {
+#pragma unroll
+    for (int e = 0; e < CPT; e++) {
+      const int c = tid + 256 * e, rr = c / (D / 8), cc = c % (D / 8);
+      const int x = n0 + rr;
+      v[e] = x < n ? *(const uint4*)(row(x) + 8 * cc) : uint4{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ inline void put(int tid, uint16_t* lds) const {
+#pragma unroll
+    for (int e = 0; e < CPT; e++) {
+      const int c = tid + 256 * e, rr = c / (D / 8), cc = c % (D / 8);
+      *(uint4*)(lds + rr * LR + 8 * cc) = v[e];
+    }
+  }
+};
+
+// the B / A operand slice a lane reads from an LDS tile: row 16 blk + col,
+// dims 32 s + 8 rg .. + 7
+template <int D>
+__device__ inline half8_t lds8(const uint16_t* lds, int row, int s, int rg) {
+  return __builtin_bit_cast(half8_t, *(const uint4*)(lds + row * Tile<D>::LR + 32 * s + 8 * rg));
+}
+
 // stats[qh][qtok] = -(M + log2 L) in base 2 over the keys query qtok sees.
 template <int D>
 __global__ __launch_bounds__(64 * kImpWaves) void imp_stats_kernel(int H, int G, int probe, int nq,
@@ -70,16 +111,19 @@ __global__ __launch_bounds__(64 * kImpWaves) void imp_stats_kernel(int H, int G,
                                                                    float* __restrict__ stats, int64_t nqtot,
                                                                    int64_t total, float scale_log2) {
   constexpr int NS = D / 32;
+  __shared__ __align__(16) uint16_t ks[kTile * Tile<D>::LR];
   const int r = blockIdx.z, qh = blockIdx.y, h = qh / G;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int col = lane & 15, rg = lane >> 4;
   const int64_t c0 = cu[r];
   const int N = (int)(cu[r + 1] - c0);
   const int NQ = probe ? nq : N;
   if (N <= 0 || c0 < 0 || c0 + N > total) return;  // (a malformed cu_seqlens entry: nothing read)
   const QRows Q{q, probe ? (int64_t)r * nq : c0, (int64_t)H * G * D};
-  for (int jb = (blockIdx.x * kImpWaves + wid) * 16; jb < NQ; jb += gridDim.x * kImpWaves * 16) {
+  auto krow = [&](int x) { return k + ((c0 + x) * H + h) * D; };
+  for (int jt = blockIdx.x * kTile; jt < NQ; jt += gridDim.x * kTile) {
     // A operand: query jb + col, dims 8 rg + 32 s
+    const int jb = jt + 16 * wid;
     half8_t a[NS];
     const int jq = jb + col;
 #pragma unroll
@@ -90,18 +134,24 @@ __global__ __launch_bounds__(64 * kImpWaves) void imp_stats_kernel(int H, int G,
       m[t] = -INFINITY;
       l[t] = 0.0f;
     }
-    // keys the block's last query sees
-    const int kend = probe ? N : min(N, jb + 16);
-    for (int ib = 0; ib < kend; ib += 64) {
+    // keys the tile's last query sees (workgroup-uniform)
+    const int kend = probe ? N : min(N, jt + kTile);
+    Tile<D> tl;
+    tl.fetch(tid, 0, N, krow);
+    for (int kt = 0; kt < kend; kt += kTile) {
+      __syncthreads();  // the previous tile's reads are done
+      tl.put(tid, ks);
+      __syncthreads();
+      if (kt + kTile < kend) tl.fetch(tid, kt + kTile, N, krow);  // in flight during the products
+      if (!probe && kt > jb + 15) continue;  // (wave-uniform) every key after this wave's queries
       float x[4][4];  // [key block][row]
 #pragma unroll
       for (int kb = 0; kb < 4; kb++) {
-        const int ik = ib + 16 * kb + col;
+        const int ik = kt + 16 * kb + col;
         float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (ib + 16 * kb < kend) {
+        if (kt + 16 * kb < kend && (probe || kt + 16 * kb <= jb + 15)) {
 #pragma unroll
-          for (int s = 0; s < NS; s++)
-            acc = mfma32(a[s], load8(k + ((c0 + min(ik, N - 1)) * H + h) * D + 8 * rg + 32 * s, ik < N), acc);
+          for (int s = 0; s < NS; s++) acc = mfma32(a[s], lds8<D>(ks, 16 * kb + col, s, rg), acc);
         }
 #pragma unroll
         for (int t = 0; t < 4; t++) {
@@ -115,10 +165,10 @@ __global__ __launch_bounds__(64 * kImpWaves) void imp_stats_kernel(int H, int G,
         const float bm = fmaxf(fmaxf(x[0][t], x[1][t]), fmaxf(x[2][t], x[3][t]));
         const float mn = fmaxf(m[t], bm);
         if (mn != -INFINITY) {
-          float s = l[t] * __builtin_amdgcn_exp2f(m[t] - mn);
+          float sacc = l[t] * __builtin_amdgcn_exp2f(m[t] - mn);
 #pragma unroll
-          for (int kb = 0; kb < 4; kb++) s += __builtin_amdgcn_exp2f(x[kb][t] - mn);
-          l[t] = s;
+          for (int kb = 0; kb < 4; kb++) sacc += __builtin_amdgcn_exp2f(x[kb][t] - mn);
+          l[t] = sacc;
           m[t] = mn;
         }
       }
@@ -148,8 +198,10 @@ __global__ __launch_bounds__(64 * kImpWaves) void imp_sum_kernel(int H, int G, i
                                                                  int64_t total, float scale_log2,
                                                                  float* __restrict__ scores) {
   constexpr int NS = D / 32;
+  __shared__ __align__(16) uint16_t qs[kTile * Tile<D>::LR];
+  __shared__ float cs[kTile];
   const int r = blockIdx.z, h = blockIdx.y;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int col = lane & 15, rg = lane >> 4;
   const int64_t c0 = cu[r];
   const int N = (int)(cu[r + 1] - c0);
@@ -157,36 +209,57 @@ __global__ __launch_bounds__(64 * kImpWaves) void imp_sum_kernel(int H, int G, i
   if (N <= 0 || c0 < 0 || c0 + N > total) return;  // (a malformed cu_seqlens entry: nothing read)
   const QRows Q{q, probe ? (int64_t)r * nq : c0, (int64_t)H * G * D};
   const int64_t sbase = probe ? (int64_t)r * nq : c0;
-  for (int ib = (blockIdx.x * kImpWaves + wid) * 16; ib < N; ib += gridDim.x * kImpWaves * 16) {
+  for (int it = blockIdx.x * kTile; it < N; it += gridDim.x * kTile) {
     // B operand: key ib + col, dims 8 rg + 32 s (kept for the whole walk)
+    const int ib = it + 16 * wid;
     const int ik = ib + col;
     half8_t kb[NS];
 #pragma unroll
     for (int s = 0; s < NS; s++) kb[s] = load8(k + ((c0 + min(ik, N - 1)) * H + h) * D + 8 * rg + 32 * s, ik < N);
     float sum = 0.0f;
-    // queries that can count for this block's keys: causal j > i >= ib
-    for (int jb = probe ? 0 : ib; jb < NQ; jb += 16) {
-      float pm[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      const int jq = jb + col;  // the A operand's query row for this lane
+    // query tiles that can count for this tile's keys (causal: j > i >= it),
+    // and per tile the group's heads; the (tile, head) pairs in that order,
+    // the next pair's rows and references in flight during each pair's products
+    const int jt0 = probe ? 0 : it;
+    Tile<D> tl;
+    float cpre = 0.0f;
+    auto fetch = [&](int jt, int g) {
+      const int qh = h * G + g;
+      tl.fetch(tid, jt, NQ, [&](int x) { return Q.row(x, qh, D); });
+      if (tid < kTile) cpre = stats[(int64_t)qh * nqtot + sbase + min(jt + tid, NQ - 1)];
+    };
+    if (jt0 < NQ) fetch(jt0, 0);
+    for (int jt = jt0; jt < NQ; jt += kTile) {
+      float pm[4][4];  // [query block][row]: max over the heads so far
+#pragma unroll
+      for (int qb = 0; qb < 4; qb++)
+#pragma unroll
+        for (int t = 0; t < 4; t++) pm[qb][t] = 0.0f;
       for (int g = 0; g < G; g++) {
-        const int qh = h * G + g;
-        float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        __syncthreads();  // the previous pair's reads are done
+        tl.put(tid, qs);
+        if (tid < kTile) cs[tid] = cpre;
+        __syncthreads();
+        if (g + 1 < G) fetch(jt, g + 1);
+        else if (jt + kTile < NQ) fetch(jt + kTile, 0);
+        if (!probe && jt + kTile - 1 <= ib) continue;  // (wave-uniform) no query after this wave's keys
 #pragma unroll
-        for (int s = 0; s < NS; s++)
-          acc = mfma32(load8(Q.row(min(jq, NQ - 1), qh, D) + 8 * rg + 32 * s, jq < NQ), kb[s], acc);
-        // the references of this lane's four query rows
-        const int j0 = jb + 4 * rg;
-        const float* sp = stats + (int64_t)qh * nqtot + sbase;
+        for (int qb = 0; qb < 4; qb++) {
+          if (!probe && jt + 16 * qb + 15 <= ib) continue;  // (wave-uniform)
+          float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int t = 0; t < 4; t++) {
-          const int j = j0 + t;
-          const bool ok = j < NQ && ik < N && (probe || j > ik);
-          const float cv = sp[min(j, NQ - 1)];  // in bounds whatever ok is
-          const float c = ok ? cv : -INFINITY;
-          pm[t] = fmaxf(pm[t], ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(acc[t], scale_log2, c)) : 0.0f);
+          for (int s = 0; s < NS; s++) acc = mfma32(lds8<D>(qs, 16 * qb + col, s, rg), kb[s], acc);
+#pragma unroll
+          for (int t = 0; t < 4; t++) {
+            const int jr = 16 * qb + 4 * rg + t, j = jt + jr;
+            const bool ok = j < NQ && ik < N && (probe || j > ik);
+            const float c = ok ? cs[jr] : -INFINITY;
+            pm[qb][t] = fmaxf(pm[qb][t], ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(acc[t], scale_log2, c)) : 0.0f);
+          }
         }
       }
-      sum += (pm[0] + pm[1]) + (pm[2] + pm[3]);
+#pragma unroll
+      for (int qb = 0; qb < 4; qb++) sum += (pm[qb][0] + pm[qb][1]) + (pm[qb][2] + pm[qb][3]);
     }
     // the four row groups of a key column: lanes col, col + 16, col + 32, col + 48
     sum += lane_xchg_t<4>(sum);
