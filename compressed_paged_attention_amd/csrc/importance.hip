@@ -144,6 +144,31 @@ __global__ __launch_bounds__(64 * kImpWaves) void imp_stats_kernel(int H, int G,
       __syncthreads();
       if (kt + kTile < kend) tl.fetch(tid, kt + kTile, N, krow);  // in flight during the products
       if (!probe && kt > jb + 15) continue;  // (wave-uniform) every key after this wave's queries
+      // a full tile (every key in range and before every query of the wave)
+      // needs no mask; the rows' maxima move only when a tile exceeds them
+      const bool full = kt + kTile <= N && (probe || kt + kTile - 1 <= jb);
+      if (full) {
+        float4_t acc[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; kb++) {
+          acc[kb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int s = 0; s < NS; s++) acc[kb] = mfma32(a[s], lds8<D>(ks, 16 * kb + col, s, rg), acc[kb]);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+          const float bm = fmaxf(fmaxf(acc[0][t], acc[1][t]), fmaxf(acc[2][t], acc[3][t])) * scale_log2;
+          if (bm > m[t]) {
+            l[t] *= __builtin_amdgcn_exp2f(m[t] - bm);  // (0 from an empty row: m = -inf)
+            m[t] = bm;
+          }
+          float sacc = l[t];
+#pragma unroll
+          for (int kb = 0; kb < 4; kb++) sacc += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[kb][t], scale_log2, -m[t]));
+          l[t] = sacc;
+        }
+        continue;
+      }
       float x[4][4];  // [key block][row]
 #pragma unroll
       for (int kb = 0; kb < 4; kb++) {
@@ -199,7 +224,7 @@ __global__ __launch_bounds__(64 * kImpWaves) void imp_sum_kernel(int H, int G, i
                                                                  float* __restrict__ scores) {
   constexpr int NS = D / 32;
   __shared__ __align__(16) uint16_t qs[kTile * Tile<D>::LR];
-  __shared__ float cs[kTile];
+  __shared__ __align__(16) float cs[kTile];
   const int r = blockIdx.z, h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int col = lane & 15, rg = lane >> 4;
@@ -243,18 +268,28 @@ __global__ __launch_bounds__(64 * kImpWaves) void imp_sum_kernel(int H, int G, i
         if (g + 1 < G) fetch(jt, g + 1);
         else if (jt + kTile < NQ) fetch(jt + kTile, 0);
         if (!probe && jt + kTile - 1 <= ib) continue;  // (wave-uniform) no query after this wave's keys
+        // a full tile (every query in range and after every key of the wave,
+        // the wave's keys in range) needs no mask
+        const bool full = jt + kTile <= NQ && ib + 16 <= N && (probe || jt >= ib + 16);
 #pragma unroll
         for (int qb = 0; qb < 4; qb++) {
           if (!probe && jt + 16 * qb + 15 <= ib) continue;  // (wave-uniform)
           float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
           for (int s = 0; s < NS; s++) acc = mfma32(lds8<D>(qs, 16 * qb + col, s, rg), kb[s], acc);
+          const float4_t c4 = *(const float4_t*)(cs + 16 * qb + 4 * rg);  // the lane's four query rows
+          if (full) {
 #pragma unroll
-          for (int t = 0; t < 4; t++) {
-            const int jr = 16 * qb + 4 * rg + t, j = jt + jr;
-            const bool ok = j < NQ && ik < N && (probe || j > ik);
-            const float c = ok ? cs[jr] : -INFINITY;
-            pm[qb][t] = fmaxf(pm[qb][t], ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(acc[t], scale_log2, c)) : 0.0f);
+            for (int t = 0; t < 4; t++)
+              pm[qb][t] = fmaxf(pm[qb][t], __builtin_amdgcn_exp2f(__builtin_fmaf(acc[t], scale_log2, c4[t])));
+          } else {
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+              const int j = jt + 16 * qb + 4 * rg + t;
+              const bool ok = j < NQ && ik < N && (probe || j > ik);
+              const float c = ok ? c4[t] : -INFINITY;
+              pm[qb][t] = fmaxf(pm[qb][t], ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(acc[t], scale_log2, c)) : 0.0f);
+            }
           }
         }
       }
