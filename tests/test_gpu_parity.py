@@ -472,7 +472,9 @@ def test_split_units_in_dispatch_order(dk, orc):
     from workloads import synth
     cfg = _medium_cfg("llama3_8b", num_kv_heads=4, batch=12, max_seq_len=1800)
     S = dk.diffkv_attn_splits(cfg, 12)
-    assert S > 1 and 12 * 4 * S > 256
+    U = 12 * 4
+    # more workgroups than this device's compute units: the ordering kernel runs
+    assert S > 1 and U * S > torch.cuda.get_device_properties(0).multi_processor_count
     g = torch.Generator().manual_seed(43)
     lens = torch.randint(100, 1700, (12,), generator=g).to(torch.int64)
     pr = synth.make_prompt(cfg, lens=lens)
@@ -489,7 +491,18 @@ def test_split_units_in_dispatch_order(dk, orc):
                           f"decode step {step}")
         else:
             p.step(seq, dec["k_new"].numpy(), dec["v_new"].numpy(), f"step {step}")
+            p.g.ws_attn.fill_(0xFF)  # no permutation of 0..U-1 left from earlier calls
             p.attend(dec["q"].numpy(), seq, True, f"attn {step}")
+            # the dispatch order the attention used: a permutation of the
+            # units, longest (most pages) first, somewhere in its workspace
+            # (every workspace array starts 256-byte aligned)
+            ws = p.g.ws_attn.view(torch.int32).cpu().numpy()
+            order = next((ws[o:o + U] for o in range(0, ws.size - U + 1, 64)
+                          if np.array_equal(np.sort(ws[o:o + U]), np.arange(U))), None)
+            assert order is not None, "no dispatch order in the attention workspace"
+            st = np_(p.g.tier_state).reshape(-1, 4)
+            pages = (st[:, 2] + st[:, 3])[order]
+            assert np.all(np.diff(pages) <= 0), pages
         seq = seq + 1
     check_pool_invariants(orc, p.o)
 
