@@ -44,7 +44,9 @@ class Cfg(ctypes.Structure):
                 ("window", ctypes.c_int32), ("lo_enabled", ctypes.c_int32),
                 ("alpha_h", ctypes.c_float), ("alpha_l", ctypes.c_float),
                 ("prompt_rule", ctypes.c_int32), ("alpha_h_head", ctypes.c_void_p),
-                ("alpha_l_head", ctypes.c_void_p)]
+                ("alpha_l_head", ctypes.c_void_p),
+                ("hi_k_bits", ctypes.c_int32), ("hi_v_bits", ctypes.c_int32),
+                ("lo_k_bits", ctypes.c_int32), ("lo_v_bits", ctypes.c_int32)]
 
 
 RULE_ALPHA_N, RULE_ALPHA_I = 0, 1
@@ -79,7 +81,8 @@ def lib() -> ctypes.CDLL:
 
 def make_cfg(c: dict) -> Cfg:
     """Config dict -> orc_cfg.  Optional keys: prompt_rule (RULE_ALPHA_N or
-    RULE_ALPHA_I), alpha_h_head / alpha_l_head (H thresholds each)."""
+    RULE_ALPHA_I), alpha_h_head / alpha_l_head (H thresholds each),
+    hi_k_bits / hi_v_bits / lo_k_bits / lo_v_bits (tier codecs)."""
     r = Cfg(int(c["head_dim"]), int(c["num_kv_heads"]), int(c["gqa_group"]),
             int(c.get("hi_page_tokens", 16)), int(c.get("lo_page_tokens", 32)),
             int(c["max_seq_len"]), int(c["window"]), int(c.get("lo_enabled", 1)),
@@ -95,6 +98,9 @@ def make_cfg(c: dict) -> Cfg:
         keep.append(a)
         setattr(r, key, a.ctypes.data)
     r._keep = keep  # the arrays live as long as the struct
+    # tier codecs (bits of K and V codes per tier; absent: K8V4 / K4V2)
+    for key in ("hi_k_bits", "hi_v_bits", "lo_k_bits", "lo_v_bits"):
+        setattr(r, key, int(c.get(key, 0)))
     return r
 
 

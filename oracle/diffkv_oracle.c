@@ -33,8 +33,36 @@
 static int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 static int32_t round16(int32_t x) { return (x + 15) / 16 * 16; }
 
+/* Tier codecs ("Results": the bit-split ablation compares K and V code
+ * widths such as K8V4, K4V8, K4V2, K2V4, K8V2, K4V1).  All four widths 0
+ * select the default pair, high K8V4 and low K4V2, with the page layout
+ * below; any other choice uses the plain layout (codec_plain). */
+static void tier_bits(const orc_cfg* c, int32_t tier, int32_t* kb, int32_t* vb) {
+  int dflt = c->hi_k_bits == 0 && c->hi_v_bits == 0 && c->lo_k_bits == 0 && c->lo_v_bits == 0;
+  if (tier == ORC_HI) {
+    *kb = dflt ? 8 : c->hi_k_bits;
+    *vb = dflt ? 4 : c->hi_v_bits;
+  } else {
+    *kb = dflt ? 4 : c->lo_k_bits;
+    *vb = dflt ? 2 : c->lo_v_bits;
+  }
+}
+
+/* The plain layout: any widths other than the default pair, or the default
+ * pair given explicitly (it is not the default layout then).  Codes are
+ * token-major and packed from bit 0: code (t, j) at bit (t d + j) b of its
+ * segment. */
+static int codec_plain(const orc_cfg* c) {
+  return c->hi_k_bits != 0 || c->hi_v_bits != 0 || c->lo_k_bits != 0 || c->lo_v_bits != 0;
+}
+
+static int bits_ok(int32_t b) { return b == 1 || b == 2 || b == 4 || b == 8; }
+
 static int cfg_valid(const orc_cfg* c) {
   if (!c) return 0;
+  if (codec_plain(c) && !(bits_ok(c->hi_k_bits) && bits_ok(c->hi_v_bits) && bits_ok(c->lo_k_bits) &&
+                          bits_ok(c->lo_v_bits)))
+    return 0;
   if (c->head_dim != 64 && c->head_dim != 128) return 0;
   if (c->num_kv_heads < 1 || c->gqa_group < 1 || c->gqa_group > 16) return 0;
   if (c->hi_page_tokens != 16 || c->lo_page_tokens != 2 * c->hi_page_tokens) return 0;
@@ -80,8 +108,8 @@ int32_t orc_table_len(const orc_cfg* c) {
 int32_t orc_tier_layout(const orc_cfg* c, int32_t tier, int32_t seg[7]) {
   int32_t d = c->head_dim;
   int32_t T = (tier == ORC_HI) ? c->hi_page_tokens : c->lo_page_tokens;
-  int32_t kbits = (tier == ORC_HI) ? 8 : 4;
-  int32_t vbits = (tier == ORC_HI) ? 4 : 2;
+  int32_t kbits, vbits;
+  tier_bits(c, tier, &kbits, &vbits);
   int32_t size[6];
   size[0] = T * d * kbits / 8; /* K codes */
   size[1] = 4 * T;             /* K scale + zero, fp16 each */
@@ -115,6 +143,14 @@ void orc_k_code_addr(const orc_cfg* c, int32_t tier, int32_t tok, int32_t j,
   int32_t seg[7];
   orc_tier_layout(c, tier, seg);
   int32_t d = c->head_dim;
+  if (codec_plain(c)) {
+    int32_t kb, vb;
+    tier_bits(c, tier, &kb, &vb);
+    int64_t bit = ((int64_t)tok * d + j) * kb;
+    *byte = seg[0] + (int32_t)(bit / 8);
+    *shift = (int32_t)(bit % 8);
+    return;
+  }
   if (tier == ORC_HI) {
     *byte = seg[0] + tok * d + j;
     *shift = 0;
@@ -141,6 +177,14 @@ void orc_v_code_addr(const orc_cfg* c, int32_t tier, int32_t tok, int32_t j,
                      int32_t* byte, int32_t* shift) {
   int32_t seg[7];
   orc_tier_layout(c, tier, seg);
+  if (codec_plain(c)) {
+    int32_t kb, vb;
+    tier_bits(c, tier, &kb, &vb);
+    int64_t bit = ((int64_t)tok * c->head_dim + j) * vb;
+    *byte = seg[2] + (int32_t)(bit / 8);
+    *shift = (int32_t)(bit % 8);
+    return;
+  }
   int32_t chunk = c->head_dim / 8;
   int32_t i = j % 16, nb = j / 16, r = tok % 4;
   int32_t q, M, w, bit;
@@ -189,7 +233,8 @@ static void write_slot(const orc_cfg* c, uint8_t* page, int32_t tier, int32_t sl
                        const uint16_t vm[2], float score, int32_t pos) {
   int32_t seg[7];
   orc_tier_layout(c, tier, seg);
-  int32_t kbits = tier == ORC_HI ? 8 : 4, vbits = tier == ORC_HI ? 4 : 2;
+  int32_t kbits, vbits;
+  tier_bits(c, tier, &kbits, &vbits);
   for (int32_t j = 0; j < c->head_dim; j++) {
     int32_t byte, shift;
     orc_k_code_addr(c, tier, slot, j, &byte, &shift);
@@ -210,7 +255,8 @@ void orc_read_slot(const orc_cfg* c, const uint8_t* page, int32_t tier, int32_t 
                    float* score, int32_t* pos) {
   int32_t seg[7];
   orc_tier_layout(c, tier, seg);
-  int32_t kbits = tier == ORC_HI ? 8 : 4, vbits = tier == ORC_HI ? 4 : 2;
+  int32_t kbits, vbits;
+  tier_bits(c, tier, &kbits, &vbits);
   for (int32_t j = 0; j < c->head_dim; j++) {
     int32_t byte, shift;
     if (kc) {
@@ -497,8 +543,10 @@ static void store_token(const orc_cfg* c, uint8_t* page, int32_t tier, int32_t s
   int32_t d = c->head_dim;
   uint8_t kc[128], vc[128];
   uint16_t km[2], vm[2];
-  orc_quantize(xk, d, tier == ORC_HI ? 8 : 4, &km[0], &km[1], kc);
-  orc_quantize(xv, d, tier == ORC_HI ? 4 : 2, &vm[0], &vm[1], vc);
+  int32_t kb, vb;
+  tier_bits(c, tier, &kb, &vb);
+  orc_quantize(xk, d, kb, &km[0], &km[1], kc);
+  orc_quantize(xv, d, vb, &vm[0], &vm[1], vc);
   write_slot(c, page, tier, slot, kc, vc, km, vm, score, pos);
 }
 

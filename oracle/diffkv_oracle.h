@@ -42,6 +42,9 @@ typedef struct {
                              ORC_RULE_ALPHA_I: the i-th prompt token against alpha/i */
   const float* alpha_h_head; /* host arrays of H per-KV-head thresholds, or both NULL */
   const float* alpha_l_head;
+  /* tier codecs: bits of K and V codes per tier, each in {1, 2, 4, 8};
+   * all four 0 = the default K8V4 (high) / K4V2 (low) */
+  int32_t hi_k_bits, hi_v_bits, lo_k_bits, lo_v_bits;
 } orc_cfg;
 
 enum { ORC_RULE_ALPHA_N = 0, ORC_RULE_ALPHA_I = 1 };

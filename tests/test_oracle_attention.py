@@ -45,10 +45,12 @@ def _grid_token(rng, d, kbits, vbits):
     return one(kbits, 2.0 ** -4, -8.0), one(vbits, 0.5, -3.0)
 
 
-def _single_unit_state(orc, d, G, tiers_row, xk, xv, window=0):
+def _single_unit_state(orc, d, G, tiers_row, xk, xv, window=0, codec=None):
     N = tiers_row.size
     cfg = dict(head_dim=d, num_kv_heads=1, gqa_group=G, max_seq_len=N + 8, window=window,
                alpha_h=1.0, alpha_l=0.2)
+    if codec is not None:
+        cfg.update(hi_k_bits=codec[0], hi_v_bits=codec[1], lo_k_bits=codec[2], lo_v_bits=codec[3])
     st = orc.State(cfg, batch=1, num_pages=2 * N // 16 + 8)
     k = xk.astype(np.float16).view(np.uint16)[:, None, :]
     v = xv.astype(np.float16).view(np.uint16)[:, None, :]
@@ -57,17 +59,19 @@ def _single_unit_state(orc, d, G, tiers_row, xk, xv, window=0):
     return cfg, st
 
 
-@pytest.mark.parametrize("d", [64, 128])
-def test_lossless_cache_equals_textbook_attention(orc, d):
-    rng = np.random.default_rng(d)
+@pytest.mark.parametrize("d,codec", [(64, None), (128, None), (64, (4, 8, 2, 4)), (128, (8, 2, 4, 1))])
+def test_lossless_cache_equals_textbook_attention(orc, d, codec):
+    # codec: the tier widths (K high, V high, K low, V low); None: K8V4 / K4V2
+    rng = np.random.default_rng(d + (sum(codec) if codec else 0))
     N, G = 90, 3
     tiers = rng.choice([orc.PRUNE, orc.LO, orc.HI], N).astype(np.uint8)
     xk = np.zeros((N, d), np.float32)
     xv = np.zeros((N, d), np.float32)
+    w = codec or (8, 4, 4, 2)
     for t in range(N):
-        kb, vb = (8, 4) if tiers[t] == orc.HI else (4, 2)
+        kb, vb = (w[0], w[1]) if tiers[t] == orc.HI else (w[2], w[3])
         xk[t], xv[t] = _grid_token(rng, d, kb, vb)
-    cfg, st = _single_unit_state(orc, d, G, tiers, xk, xv)
+    cfg, st = _single_unit_state(orc, d, G, tiers, xk, xv, codec=codec)
     q = rng.standard_normal((1, G, d)).astype(np.float16)
     out = st.decode_attn(q.view(np.uint16), [N])
     keep = tiers != orc.PRUNE

@@ -38,7 +38,7 @@ def test_f16_nan(orc):
     assert np.isnan(orc.f16_to_f32(orc.f32_to_f16(np.array([np.nan], np.float32))))[0]
 
 
-@pytest.mark.parametrize("bits", [8, 4, 2])
+@pytest.mark.parametrize("bits", [8, 4, 2, 1])
 def test_codec_roundtrip_bound(orc, bits):
     rng = np.random.default_rng(bits)
     qmax = (1 << bits) - 1
@@ -79,7 +79,7 @@ def test_codec_worked_values(orc):
     assert np.array_equal(np.array([orc.dequant(s, z, int(k)) for k in c], np.float32), x)
 
 
-@pytest.mark.parametrize("bits", [8, 4, 2])
+@pytest.mark.parametrize("bits", [8, 4, 2, 1])
 def test_codec_constant_vector(orc, bits):
     x = np.full(64, 1.375, np.float32)
     s, z, c = orc.quantize(x, bits)
@@ -160,3 +160,89 @@ def test_table_length_reading(orc):
     # derived size check: int32 rows of S_max/T_h = 4096/16 entries for
     # 32 layers x 8 KV heads x 128 requests total 32 MiB
     assert 32 * 8 * 128 * (4096 // 16) * 4 == 32 * 2**20
+
+
+# --- tier codec variants ("Results": the bit-split ablation, K4V8, K2V4,
+# K8V2, K4V1 against K8V4 / K4V2): the plain layout, token-major codes
+# packed from bit 0
+
+VARIANTS = [(4, 8, 2, 4), (8, 2, 4, 1), (8, 4, 4, 2), (2, 1, 1, 2)]
+
+
+def _vcfg(d, codec):
+    hk, hv, lk, lv = codec
+    return dict(head_dim=d, num_kv_heads=1, gqa_group=1, max_seq_len=64, window=0, alpha_h=1.0,
+                alpha_l=0.2, hi_k_bits=hk, hi_v_bits=hv, lo_k_bits=lk, lo_v_bits=lv)
+
+
+@pytest.mark.parametrize("codec", VARIANTS)
+def test_variant_layout_sizes(orc, codec):
+    # segments of T d b / 8 bytes for the codes (16-byte aligned), the page
+    # the larger tier; e.g. K4V8 at d = 128: 16 x 64 + 16 x 128 code bytes
+    for d in (64, 128):
+        c = _vcfg(d, codec)
+        pages = []
+        for tier, T, kb, vb in ((orc.HI, 16, codec[0], codec[1]), (orc.LO, 32, codec[2], codec[3])):
+            T_, seg = orc.tier_layout(c, tier)
+            assert T_ == T
+            r16 = lambda x: -(-x // 16) * 16
+            assert np.diff(seg).tolist() == [r16(T * d * kb // 8), 4 * T, r16(T * d * vb // 8), 4 * T, 4 * T, 4 * T]
+            pages.append(seg[6])
+        assert orc.page_bytes(c) == max(pages)
+    # K4V8 high (1024 + 2048 code bytes + 256) against K2V4 low (32 tokens:
+    # 1024 + 2048 + 512): the low tier sets the page
+    assert orc.page_bytes(_vcfg(128, (4, 8, 2, 4))) == 32 * 32 + 32 * 64 + 4 * 4 * 32
+    for bad in ((3, 4, 4, 2), (8, 4, 4, 0), (16, 4, 4, 2)):
+        assert orc.page_bytes(_vcfg(128, bad)) == -1
+
+
+@pytest.mark.parametrize("codec", VARIANTS)
+def test_variant_fields_tile_segments(orc, codec):
+    # every (token, dim) code of a tier has its own bits, token-major from
+    # bit 0: code (t, j) at bit (t d + j) b of its segment
+    d = 64
+    c = _vcfg(d, codec)
+    for tier, T, kb, vb in ((orc.HI, 16, codec[0], codec[1]), (orc.LO, 32, codec[2], codec[3])):
+        _, seg = orc.tier_layout(c, tier)
+        for fn, bits, lo in ((orc.k_code_addr, kb, seg[0]), (orc.v_code_addr, vb, seg[2])):
+            seen = set()
+            for t in range(T):
+                for j in range(d):
+                    b, sh = fn(c, tier, t, j)
+                    assert (b - lo) * 8 + sh == (t * d + j) * bits
+                    seen.update((b, x) for x in range(sh, sh + bits))
+            assert len(seen) == T * d * bits
+
+
+@pytest.mark.parametrize("codec", VARIANTS)
+def test_variant_prompt_codes_within_half_a_step(orc, codec):
+    # a prompt compacted with a variant codec: every retained token's K and V
+    # read back from its page lie within half a quantization step (plus the
+    # fp16 rounding of the scale) of the input, at the tier's width
+    rng = np.random.default_rng(sum(codec))
+    d, H, N = 64, 2, 100
+    c = dict(_vcfg(d, codec), num_kv_heads=H, max_seq_len=256, window=8)
+    cu = np.array([0, N])
+    k = rng.standard_normal((N, H, d)).astype(np.float16)
+    v = rng.standard_normal((N, H, d)).astype(np.float16)
+    sc = (rng.random((H, N)) ** 3 / 20).astype(np.float32)
+    tiers, counts = orc.classify(c, cu, sc)
+    st = orc.State(c, batch=1, num_pages=64)
+    st.compact_prompt(cu, k.view(np.uint16), v.view(np.uint16), sc, tiers)
+    widths = {orc.HI: (codec[0], codec[1]), orc.LO: (codec[2], codec[3])}
+    seen = {orc.HI: 0, orc.LO: 0}
+    for h in range(H):
+        for tier, slot, rec in st.unit_tokens(0, h):
+            p = rec["pos"]
+            seen[tier] += 1
+            for name, x, bits in (("k", k, widths[tier][0]), ("v", v, widths[tier][1])):
+                xs = x[p, h].astype(np.float32)
+                s16, z16 = (int(x) for x in rec[name + "meta"])
+                step = float(np.uint16(s16).view(np.float16))
+                codes = rec[name]
+                assert codes.max() <= (1 << bits) - 1
+                xh = np.array([orc.dequant(s16, z16, int(q)) for q in codes])
+                rng_ = float(xs.max() - xs.min())
+                bound = step / 2 * (1 + 1e-6) + ((1 << bits) - 1) * abs(step - rng_ / ((1 << bits) - 1)) + 1e-6
+                assert np.all(np.abs(xh - xs) <= bound), (tier, name, np.abs(xh - xs).max(), bound)
+    assert seen[orc.HI] > 0 and seen[orc.LO] > 0

@@ -78,15 +78,18 @@ def _sets(st, b, h, orc):
     return hi, lo, sums
 
 
-@pytest.mark.parametrize("lo_enabled,per_head", [(1, False), (0, False), (1, True)])
-def test_step_matches_set_model(orc, lo_enabled, per_head):
+@pytest.mark.parametrize("lo_enabled,per_head,codec", [(1, False, None), (0, False, None), (1, True, None),
+                                                      (1, False, (4, 8, 2, 4)), (1, False, (8, 2, 4, 1))])
+def test_step_matches_set_model(orc, lo_enabled, per_head, codec):
     # per_head: each KV head classifies against its own (alpha_h, alpha_l)
     # ("KV compression policy", extensibility paragraph); the set model runs
     # one policy per head with that head's pair
-    rng = np.random.default_rng(100 + lo_enabled + 7 * per_head)
+    rng = np.random.default_rng(100 + lo_enabled + 7 * per_head + (sum(codec) if codec else 0))
     d, H, G, B, W = 64, 2, 2, 2, 6
     cfg = dict(head_dim=d, num_kv_heads=H, gqa_group=G, max_seq_len=700, window=W,
                alpha_h=1.0, alpha_l=0.3, lo_enabled=lo_enabled)
+    if codec is not None:  # tier codec variant (the policy does not depend on it)
+        cfg.update(hi_k_bits=codec[0], hi_v_bits=codec[1], lo_k_bits=codec[2], lo_v_bits=codec[3])
     ah, al = [1.0] * H, [0.3] * H
     if per_head:
         ah, al = [1.0, 2.5], [0.3, 0.6]
