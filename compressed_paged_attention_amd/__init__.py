@@ -38,7 +38,9 @@ class diffkv_config(ctypes.Structure):
                 ("window", ctypes.c_int32), ("lo_enabled", ctypes.c_int32),
                 ("alpha_h", ctypes.c_float), ("alpha_l", ctypes.c_float),
                 ("prompt_rule", ctypes.c_int32), ("alpha_h_head", ctypes.c_void_p),
-                ("alpha_l_head", ctypes.c_void_p)]
+                ("alpha_l_head", ctypes.c_void_p),
+                ("hi_k_bits", ctypes.c_int32), ("hi_v_bits", ctypes.c_int32),
+                ("lo_k_bits", ctypes.c_int32), ("lo_v_bits", ctypes.c_int32)]
 
 
 RULE_ALPHA_N, RULE_ALPHA_I = 0, 1
@@ -116,8 +118,9 @@ def _head_alphas(v, H: int):
 
 def make_config(c: dict) -> diffkv_config:
     """Config dict -> diffkv_config.  Optional keys: prompt_rule
-    (RULE_ALPHA_N / RULE_ALPHA_I) and alpha_h_head / alpha_l_head (H values
-    each: a sequence, or a float32 device tensor)."""
+    (RULE_ALPHA_N / RULE_ALPHA_I), alpha_h_head / alpha_l_head (H values
+    each: a sequence, or a float32 device tensor) and hi_k_bits / hi_v_bits /
+    lo_k_bits / lo_v_bits (tier codecs)."""
     r = diffkv_config(int(c["head_dim"]), int(c["num_kv_heads"]), int(c["gqa_group"]),
                       int(c.get("hi_page_tokens", 16)), int(c.get("lo_page_tokens", 32)),
                       int(c["max_seq_len"]), int(c["window"]), int(c.get("lo_enabled", 1)),
@@ -129,6 +132,8 @@ def make_config(c: dict) -> diffkv_config:
             keep.append(t)
             setattr(r, key, t.data_ptr())
     r._keep = keep  # the device arrays live as long as the struct
+    for key in ("hi_k_bits", "hi_v_bits", "lo_k_bits", "lo_v_bits"):  # tier codecs (absent: K8V4 / K4V2)
+        setattr(r, key, int(c.get(key, 0)))
     return r
 
 

@@ -24,6 +24,10 @@ bool cfg_ok(const diffkv_config* c) {
   if (c->lo_enabled && c->alpha_l > c->alpha_h) return false;
   if (c->prompt_rule != DIFFKV_RULE_ALPHA_N && c->prompt_rule != DIFFKV_RULE_ALPHA_I) return false;
   if ((c->alpha_h_head == nullptr) != (c->alpha_l_head == nullptr)) return false;
+  const bool plain = c->hi_k_bits || c->hi_v_bits || c->lo_k_bits || c->lo_v_bits;
+  auto bits_ok = [](int32_t b) { return b == 1 || b == 2 || b == 4 || b == 8; };
+  if (plain && !(bits_ok(c->hi_k_bits) && bits_ok(c->hi_v_bits) && bits_ok(c->lo_k_bits) && bits_ok(c->lo_v_bits)))
+    return false;
   return true;
 }
 
@@ -41,12 +45,15 @@ Cfg to_cfg(const diffkv_config* c) {
   r.ah_head = c->alpha_h_head;
   r.al_head = c->alpha_l_head;
   r.prompt_rule = c->prompt_rule;
+  r.plain = c->hi_k_bits || c->hi_v_bits || c->lo_k_bits || c->lo_v_bits;
+  r.codec = r.plain ? Codec{c->hi_k_bits, c->hi_v_bits, c->lo_k_bits, c->lo_v_bits} : Codec{8, 4, 4, 2};
+  r.page_bytes = r.plain ? plain_page_bytes(r.d, r.codec) : page_bytes_for(r.d);
   return r;
 }
 
 bool pool_ok(const diffkv_config* c, const diffkv_pool* p) {
   return p && p->pages && p->free_list && p->ptr && p->status && p->num_pages >= 1 &&
-         p->num_pages < (int64_t(1) << 31) && p->page_bytes == page_bytes_for(c->head_dim);
+         p->num_pages < (int64_t(1) << 31) && p->page_bytes == to_cfg(c).page_bytes;
 }
 
 Pool to_pool(const diffkv_pool* p) {
@@ -61,7 +68,7 @@ extern "C" {
 
 int32_t diffkv_page_bytes(const diffkv_config* cfg) {
   if (!cfg_ok(cfg)) return -1;
-  return page_bytes_for(cfg->head_dim);
+  return to_cfg(cfg).page_bytes;
 }
 
 int32_t diffkv_table_len(const diffkv_config* cfg) {

@@ -116,7 +116,6 @@ __device__ inline uint32_t crumb2(uint32_t w, int s) {
 // heads); the rest exit at once.
 constexpr int kSplitPages = 256;
 constexpr int kMaxSplits = 128;  // the merge kernel holds one weight per split and head in LDS
-constexpr int kSplitMinPages = 16;
 
 int attn_splits(const Cfg& c, int batch) {
   const int64_t U = (int64_t)batch * c.H;
@@ -132,11 +131,6 @@ int attn_splits(const Cfg& c, int batch) {
   return (int)S;
 }
 
-__host__ __device__ inline int split_pages(int TPg, int S) {
-  if (S <= 1) return TPg;
-  const int q = (TPg + S - 1) / S;
-  return q > kSplitMinPages ? q : kSplitMinPages;
-}
 
 // Score-update chunks (several splits, or a deferred update): 64 pages each.
 constexpr int kScorePages = 64;
@@ -176,6 +170,7 @@ static AttnWs attn_carve(const Cfg& c, int batch, bool scores, void* ws, size_t*
 }
 
 size_t attn_workspace(const Cfg& c, int batch, bool scores) {
+  if (c.plain) return plain_attn_workspace(c, batch, scores);
   size_t n = 0;
   attn_carve(c, batch, scores, nullptr, &n);
   return n;
@@ -1544,6 +1539,7 @@ __global__ __launch_bounds__(64) void score_finish_kernel(int H, int G, int L, i
 
 hipError_t launch_scores(const Cfg& c, const Pool& p, int batch, const int32_t* table, const int32_t* state,
                          const int32_t* seq_len, void* ws, hipStream_t s) {
+  if (c.plain) return launch_scores_plain(c, p, batch, table, state, seq_len, ws, s);
   const int64_t U = (int64_t)batch * c.H;
   if (U == 0) return hipSuccess;
   AttnWs w = attn_carve(c, batch, true, ws, nullptr);
@@ -1653,6 +1649,7 @@ constexpr int kOrderRefresh = 16;
 hipError_t launch_attn(const Cfg& c, const Pool& p, int batch, const uint16_t* q, const int32_t* table,
                        const int32_t* state, const int32_t* seq_len, float* out, int mode, void* ws,
                        hipStream_t s) {
+  if (c.plain) return launch_attn_plain(c, p, batch, q, table, state, seq_len, out, mode, ws, s);
   const int64_t U = (int64_t)batch * c.H;
   if (U == 0) return hipSuccess;
   const int S = attn_splits(c, batch);
@@ -1690,17 +1687,23 @@ hipError_t launch_attn(const Cfg& c, const Pool& p, int batch, const uint16_t* q
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (S > 1) {
-    if (c.d == 128)
-      attn_merge_kernel<128><<<dim3((unsigned)c.G, (unsigned)U), dim3(256), 0, s>>>(c.H, c.G, S, seq_len, w.part, out, w.ml,
-                                                                     mode != 0);
-    else
-      attn_merge_kernel<64><<<dim3((unsigned)c.G, (unsigned)U), dim3(256), 0, s>>>(c.H, c.G, S, seq_len, w.part, out, w.ml,
-                                                                    mode != 0);
-    e = hipGetLastError();
+    e = launch_attn_merge(c, batch, S, seq_len, w.part, out, w.ml, mode != 0, s);
     if (e != hipSuccess) return e;
     if (mode == 1) return launch_scores(c, p, batch, table, state, seq_len, ws, s);
   }
   return hipSuccess;
+}
+
+hipError_t launch_attn_merge(const Cfg& c, int batch, int S, const int32_t* seq_len, const float* part, float* out,
+                             float* ml, bool save, hipStream_t s) {
+  const int64_t U = (int64_t)batch * c.H;
+  if (U == 0) return hipSuccess;
+  const dim3 grid((unsigned)c.G, (unsigned)U), block(256);
+  if (c.d == 128)
+    attn_merge_kernel<128><<<grid, block, 0, s>>>(c.H, c.G, S, seq_len, part, out, ml, save ? 1 : 0);
+  else
+    attn_merge_kernel<64><<<grid, block, 0, s>>>(c.H, c.G, S, seq_len, part, out, ml, save ? 1 : 0);
+  return hipGetLastError();
 }
 
 // With one split per unit the step's commit runs inside the attention
@@ -1713,7 +1716,7 @@ hipError_t launch_decode_step(const Cfg& c, const Pool& p, int batch, const int3
   const int64_t U = (int64_t)batch * c.H;
   if (U == 0) return hipSuccess;
   const int S = attn_splits(c, batch);
-  if (S != 1 || mode == 2) {
+  if (S != 1 || mode == 2 || c.plain) {
     hipError_t e = launch_step(c, p, batch, seq_len, k, v, table, state, ws_step, s);
     if (e != hipSuccess) return e;
     return launch_attn(c, p, batch, q, table, state, seq_len, out, mode, ws_attn, s);

@@ -1,0 +1,403 @@
+// attention_plain.hip -- decode attention and score update over pages of a
+// tier codec variant (DiffKV notes, "Results": the bit-split ablation of K
+// and V code widths; plain page layout, widths in {1, 2, 4, 8}).
+//
+// What is computed is that of the default kernels ("Background": the softmax
+// of q.k/sqrt(d) weighting v over the unit's retained tokens, K and V
+// dequantized per token as s*c + z; "Implementation": high pages before low
+// pages, sequence splits merged at the end), for any pair of widths per tier:
+//
+//   plain_attn_kernel   (split, unit) workgroups of 4 waves; wave w takes the
+//                       split's pages w, w+4, ...  Per page:
+//     QK: lane = (token t, part of d): the token's codes of that part in
+//         16-code blocks (2b bytes each), dequantized in fp32 and dotted with
+//         the group's q heads (fp32 in LDS, padded with zero rows to GB);
+//         the parts are summed with two (high page) or one (low page) lane
+//         exchanges in a fixed order;
+//     online softmax per head in base 2 (fp32);
+//     PV: lane = d/64 consecutive dims; per token the lane's codes (one byte,
+//         or two for 8-bit codes at d = 128), dequantized, times the token's
+//         weights (broadcast LDS reads);
+//   then the waves are merged in LDS in a fixed order into one partial
+//   (unnormalized O, max, sum) per split and head, and the split merge of the
+//   default path normalizes them (it also keeps (max, sum) for the score
+//   update).
+//   plain_score_kernel  the score update from the logits the attention kept:
+//     each retained token with position < seq_len adds max_g of its softmax
+//     weight to its score word.
+//
+// A bad page id makes its split's partial NaN: the merge then writes zeros
+// for the unit and (max, sum) = (-inf, 0), so the score update skips it.
+#include "dkv_common.hpp"
+#include "dkv_launch.hpp"
+
+namespace dkv {
+
+namespace {
+
+constexpr int kPWaves = 4;
+constexpr int kPThreads = 64 * kPWaves;
+constexpr float kLog2eP = 1.4426950408889634f;
+
+struct PlainWs {
+  float* part;    // [U][S][G][D + 2]
+  float* ml;      // [U][G][2] base-2 (max, sum) after the merge
+  float* logits;  // [U][G][32 L] base-2 logits by slot (high slots, then low)
+};
+
+PlainWs plain_carve(const Cfg& c, int batch, bool scores, void* ws, size_t* bytes) {
+  const int64_t U = (int64_t)batch * c.H;
+  const int S = attn_splits(c, batch);
+  uint8_t* b = (uint8_t*)ws;
+  size_t off = 0;
+  PlainWs w;
+  w.part = (float*)(b + off);
+  off = align_up(off + (size_t)U * S * c.G * (c.d + 2) * sizeof(float), 256);
+  w.ml = (float*)(b + off);
+  off = align_up(off + (size_t)U * c.G * 2 * sizeof(float), 256);
+  w.logits = (float*)(b + off);
+  if (scores) off = align_up(off + (size_t)U * c.G * 32 * c.L * sizeof(float), 256);
+  if (bytes) *bytes = off < 256 ? 256 : off;
+  return w;
+}
+
+__device__ inline bool plain_state_ok(int nh, int nl, int ph, int pl, int L) {
+  return nh >= 0 && nl >= 0 && ph == (int)cdiv(nh, kHiTokens) && pl == (int)cdiv(nl, kLoTokens) && ph + pl <= L;
+}
+
+// 16 codes of width B from a 2B-byte block (aligned to 2B bytes); code e at
+// bit e B, little-endian.
+template <int B>
+__device__ inline void load16(const uint8_t* p, uint32_t (&w)[4]) {
+  w[1] = w[2] = w[3] = 0u;
+  if constexpr (B == 8) {
+    const uint4 x = *(const uint4*)p;
+    w[0] = x.x;
+    w[1] = x.y;
+    w[2] = x.z;
+    w[3] = x.w;
+  } else if constexpr (B == 4) {
+    const uint2 x = *(const uint2*)p;
+    w[0] = x.x;
+    w[1] = x.y;
+  } else if constexpr (B == 2) {
+    w[0] = *(const uint32_t*)p;
+  } else {
+    w[0] = *(const uint16_t*)p;
+  }
+}
+
+template <int B>
+__device__ inline uint32_t code_at(const uint32_t (&w)[4], int e) {
+  return (w[(e * B) >> 5] >> ((e * B) & 31)) & ((1u << B) - 1u);
+}
+
+// q . k^ for the lane's token and part of d, every head of the padded group.
+template <int D, int T, int KB, int GB>
+__device__ inline void plain_qk(const uint8_t* pg, const Seg& sg, int lane, const float* qs, float (&acc)[GB]) {
+  constexpr int PARTS = 64 / T, DP = D / PARTS;
+  const int t = lane % T, part = lane / T;
+  const uint32_t mw = *(const uint32_t*)(pg + sg.km + 4 * t);
+  const float s = h2f((uint16_t)(mw & 0xFFFFu)), z = h2f((uint16_t)(mw >> 16));
+#pragma unroll
+  for (int g = 0; g < GB; g++) acc[g] = 0.0f;
+#pragma unroll
+  for (int blk = 0; blk < DP / 16; blk++) {
+    const int j0 = part * DP + 16 * blk;
+    uint32_t w[4];
+    load16<KB>(pg + sg.kc + (t * D + j0) * KB / 8, w);
+#pragma unroll
+    for (int e = 0; e < 16; e++) {
+      const float x = dequant(s, z, code_at<KB>(w, e));
+#pragma unroll
+      for (int g = 0; g < GB; g++) acc[g] = __builtin_fmaf(qs[g * D + j0 + e], x, acc[g]);
+    }
+  }
+  // the parts of d (lanes t + T k), summed in the same order in every lane
+#pragma unroll
+  for (int g = 0; g < GB; g++) {
+    if constexpr (PARTS == 4) acc[g] += __shfl_xor(acc[g], 16, 64);
+    acc[g] += __shfl_xor(acc[g], 32, 64);
+  }
+}
+
+template <int D, int T, int GB>
+__device__ inline void plain_qk_any(int kb, const uint8_t* pg, const Seg& sg, int lane, const float* qs,
+                                    float (&acc)[GB]) {
+  if (kb == 8) plain_qk<D, T, 8, GB>(pg, sg, lane, qs, acc);
+  else if (kb == 4) plain_qk<D, T, 4, GB>(pg, sg, lane, qs, acc);
+  else if (kb == 2) plain_qk<D, T, 2, GB>(pg, sg, lane, qs, acc);
+  else plain_qk<D, T, 1, GB>(pg, sg, lane, qs, acc);
+}
+
+// o[g][e] += p[t][g] v^[t][lane dims] over the page's nv tokens; pw holds the
+// weights [32][16] of this wave.
+template <int D, int VB, int GB>
+__device__ inline void plain_pv(const uint8_t* pg, const Seg& sg, int lane, int nv, const float* pw,
+                                float (&o)[GB][D / 64]) {
+  constexpr int DL = D / 64;
+  const int jd = lane * DL;
+  const uint32_t vmw = lane < sg.T ? *(const uint32_t*)(pg + sg.vm + 4 * lane) : 0u;
+  for (int t0 = 0; t0 < nv; t0 += 8) {
+    uint32_t cw[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      const int t = min(t0 + k, nv - 1);
+      const int bit = (t * D + jd) * VB;
+      if constexpr (DL * VB <= 8) cw[k] = (uint32_t)pg[sg.vc + (bit >> 3)] >> (bit & 7);
+      else cw[k] = *(const uint16_t*)(pg + sg.vc + (bit >> 3));  // two 8-bit codes, 2-byte aligned
+    }
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      const int t = t0 + k;
+      if (t < nv) {  // uniform
+        const uint32_t m = __builtin_amdgcn_readlane(vmw, t);
+        const float s = h2f((uint16_t)(m & 0xFFFFu)), z = h2f((uint16_t)(m >> 16));
+        float v[DL];
+#pragma unroll
+        for (int e = 0; e < DL; e++) v[e] = dequant(s, z, (cw[k] >> (e * VB)) & ((1u << VB) - 1u));
+#pragma unroll
+        for (int g = 0; g < GB; g++) {
+          const float p = pw[t * 16 + g];
+#pragma unroll
+          for (int e = 0; e < DL; e++) o[g][e] = __builtin_fmaf(p, v[e], o[g][e]);
+        }
+      }
+    }
+  }
+}
+
+template <int D, int GB>
+__device__ inline void plain_pv_any(int vb, const uint8_t* pg, const Seg& sg, int lane, int nv, const float* pw,
+                                    float (&o)[GB][D / 64]) {
+  if (vb == 8) plain_pv<D, 8, GB>(pg, sg, lane, nv, pw, o);
+  else if (vb == 4) plain_pv<D, 4, GB>(pg, sg, lane, nv, pw, o);
+  else if (vb == 2) plain_pv<D, 2, GB>(pg, sg, lane, nv, pw, o);
+  else plain_pv<D, 1, GB>(pg, sg, lane, nv, pw, o);
+}
+
+// LDS operations of one wave complete in program order; this keeps the
+// compiler from moving them across the point
+__device__ inline void wave_lds_order() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+}  // namespace
+
+template <int D, int GB>
+__global__ __launch_bounds__(kPThreads) void plain_attn_kernel(int H, int G, int L, int S, int64_t P, int page_bytes,
+                                                               Lay lay, float scale_log2, int keep_logits,
+                                                               const uint16_t* __restrict__ q,
+                                                               const int32_t* __restrict__ table,
+                                                               const int32_t* __restrict__ state,
+                                                               const int32_t* __restrict__ seq_len,
+                                                               const uint8_t* __restrict__ pages,
+                                                               float* __restrict__ out, float* __restrict__ part,
+                                                               float* __restrict__ logits, uint32_t* status) {
+  constexpr int DL = D / 64;
+  const int split = blockIdx.x;
+  const int64_t u = blockIdx.y;
+  const int b = (int)u / H, h = (int)u % H;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  __shared__ float qs[GB * D];
+  __shared__ float ps[kPWaves][32 * 16];
+  __shared__ float sml[kPWaves][GB][2];
+  __shared__ float ob[kPWaves][GB * D];
+  const int N = seq_len[b];
+  if (N <= 0) {
+    if (split == 0)
+      for (int x = tid; x < G * D; x += kPThreads) out[((int64_t)b * H * G + (int64_t)h * G) * D + x] = 0.0f;
+    return;
+  }
+  const int32_t* s4 = state + 4 * u;
+  const int nh = s4[0], nl = s4[1], ph = s4[2], pl = s4[3];
+  const bool sok = plain_state_ok(nh, nl, ph, pl, L);
+  if (!sok && split == 0 && tid == 0) atomicOr(status, kStBadState);
+  const int TPg = sok ? ph + pl : 0;
+  const int pps = split_pages(TPg, S);
+  const int p0 = split * pps, p1 = min(TPg, p0 + pps);
+  // the group's q heads (fp32; rows G..GB-1 zero)
+  const uint16_t* qb = q + ((int64_t)b * H * G + (int64_t)h * G) * D;
+  for (int x = tid; x < GB * D; x += kPThreads) qs[x] = x < G * D ? h2f(qb[x]) : 0.0f;
+  __syncthreads();
+  float m[GB], l[GB], o[GB][DL];
+#pragma unroll
+  for (int g = 0; g < GB; g++) {
+    m[g] = -INFINITY;
+    l[g] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < DL; e++) o[g][e] = 0.0f;
+  }
+  bool bad = false;
+  float* pw = ps[wid];
+  const int64_t LS = (int64_t)32 * L;
+  for (int j = p0 + wid; j < p1; j += kPWaves) {
+    const bool hi = j < ph;
+    const int jt = hi ? j : j - ph;
+    const int32_t id = table[u * L + (hi ? jt : L - 1 - jt)];
+    if (id < 0 || id >= P) {
+      bad = true;
+      continue;
+    }
+    const uint8_t* pg = pages + (int64_t)id * page_bytes;
+    const Seg& sg = lay.seg(hi);
+    const int T = sg.T;
+    const int nv = hi ? min(kHiTokens, nh - kHiTokens * jt) : min(kLoTokens, nl - kLoTokens * jt);
+    const int slot0 = hi ? kHiTokens * jt : nh + kLoTokens * jt;
+    float x[GB];
+    if (hi) plain_qk_any<D, kHiTokens, GB>(sg.kbits, pg, sg, lane, qs, x);
+    else plain_qk_any<D, kLoTokens, GB>(sg.kbits, pg, sg, lane, qs, x);
+    const int t = lane % T;
+    const bool first = lane < T, live = t < nv;
+#pragma unroll
+    for (int g = 0; g < GB; g++) x[g] = live ? x[g] * scale_log2 : -INFINITY;
+    if (keep_logits && first && live)
+      for (int g = 0; g < G; g++) logits[(u * G + g) * LS + slot0 + t] = x[g];
+    wave_lds_order();  // the previous page's weights have been read
+#pragma unroll
+    for (int g = 0; g < GB; g++) {
+      const float mn = fmaxf(m[g], wave_max(x[g]));  // finite: nv >= 1
+      const float al = __builtin_amdgcn_exp2f(m[g] - mn);
+      const float p = live ? __builtin_amdgcn_exp2f(x[g] - mn) : 0.0f;
+      l[g] = l[g] * al + wave_sum(first ? p : 0.0f);
+#pragma unroll
+      for (int e = 0; e < DL; e++) o[g][e] *= al;
+      m[g] = mn;
+      if (first) pw[t * 16 + g] = p;
+    }
+    wave_lds_order();
+    plain_pv_any<D, GB>(sg.vbits, pg, sg, lane, nv, pw, o);
+  }
+  // the waves' partials, merged in a fixed order
+  if (lane == 0)
+#pragma unroll
+    for (int g = 0; g < GB; g++) {
+      sml[wid][g][0] = m[g];
+      sml[wid][g][1] = l[g];
+    }
+#pragma unroll
+  for (int g = 0; g < GB; g++)
+#pragma unroll
+    for (int e = 0; e < DL; e++) ob[wid][g * D + lane * DL + e] = o[g][e];
+  bad = __syncthreads_or(bad);
+  if (bad && tid == 0) atomicOr(status, kStBadState);
+  float* up = part + ((u * S + split) * G) * (D + 2);
+  for (int x = tid; x < G * D; x += kPThreads) {
+    const int g = x / D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kPWaves; w++) M = fmaxf(M, sml[w][g][0]);
+    float acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kPWaves; w++) {
+      const float mw = sml[w][g][0];
+      const float wt = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+      acc += ob[w][x] * wt;
+    }
+    up[g * (D + 2) + (x % D)] = acc;
+  }
+  if (tid < G) {
+    const int g = tid;
+    float M = -INFINITY, Lsum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kPWaves; w++) M = fmaxf(M, sml[w][g][0]);
+#pragma unroll
+    for (int w = 0; w < kPWaves; w++) {
+      const float mw = sml[w][g][0];
+      if (mw != -INFINITY) Lsum += sml[w][g][1] * __builtin_amdgcn_exp2f(mw - M);
+    }
+    up[g * (D + 2) + D] = bad ? __builtin_nanf("") : M;
+    up[g * (D + 2) + D + 1] = Lsum;
+  }
+}
+
+// One thread per retained slot of the unit (grid x: blocks of 256 slots).
+__global__ __launch_bounds__(256) void plain_score_kernel(int H, int G, int L, int64_t P, int page_bytes, Lay lay,
+                                                          const int32_t* __restrict__ table,
+                                                          const int32_t* __restrict__ state,
+                                                          const int32_t* __restrict__ seq_len,
+                                                          const float* __restrict__ ml,
+                                                          const float* __restrict__ logits, uint8_t* pages) {
+  const int64_t u = blockIdx.y;
+  const int b = (int)u / H;
+  const int N = seq_len[b];
+  if (N <= 0) return;
+  const int32_t* s4 = state + 4 * u;
+  const int nh = s4[0], nl = s4[1], ph = s4[2], pl = s4[3];
+  if (!plain_state_ok(nh, nl, ph, pl, L)) return;
+  const int s = blockIdx.x * 256 + threadIdx.x;
+  if (s >= nh + nl) return;
+  if (!(ml[u * G * 2 + 1] > 0.0f)) return;  // bad unit
+  const bool hi = s < nh;
+  const int ls = hi ? s : s - nh;
+  const int jt = hi ? ls / kHiTokens : ls / kLoTokens, idx = hi ? ls % kHiTokens : ls % kLoTokens;
+  const int32_t id = table[u * L + (hi ? jt : L - 1 - jt)];
+  if (id < 0 || id >= P) return;
+  const int64_t LS = (int64_t)32 * L;
+  float pmax = 0.0f;
+  for (int g = 0; g < G; g++) {
+    const float M = ml[(u * G + g) * 2 + 0], Ls = ml[(u * G + g) * 2 + 1];
+    const float p = __builtin_amdgcn_exp2f(logits[(u * G + g) * LS + s] - M) / Ls;
+    pmax = fmaxf(pmax, p);
+  }
+  const Seg& sg = lay.seg(hi);
+  uint8_t* pg = pages + (int64_t)id * page_bytes;
+  const int32_t pos = *(const int32_t*)(pg + sg.ps + 4 * idx);
+  if (pos >= N) return;
+  float* sc = (float*)(pg + sg.sc + 4 * idx);
+  *sc = *sc + pmax;
+}
+
+size_t plain_attn_workspace(const Cfg& c, int batch, bool scores) {
+  size_t n = 0;
+  plain_carve(c, batch, scores, nullptr, &n);
+  return n;
+}
+
+hipError_t launch_scores_plain(const Cfg& c, const Pool& p, int batch, const int32_t* table, const int32_t* state,
+                               const int32_t* seq_len, void* ws, hipStream_t s) {
+  const int64_t U = (int64_t)batch * c.H;
+  if (U == 0) return hipSuccess;
+  const PlainWs w = plain_carve(c, batch, true, ws, nullptr);
+  const dim3 grid((unsigned)((32 * (int64_t)c.L + 255) / 256), (unsigned)U), block(256);
+  plain_score_kernel<<<grid, block, 0, s>>>(c.H, c.G, c.L, p.P, p.page_bytes, Lay(c.d, true, c.codec), table, state,
+                                            seq_len, w.ml, w.logits, p.pages);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_plain(const Cfg& c, const Pool& p, int batch, const uint16_t* q, const int32_t* table,
+                             const int32_t* state, const int32_t* seq_len, float* out, int mode, void* ws,
+                             hipStream_t s) {
+  const int64_t U = (int64_t)batch * c.H;
+  if (U == 0) return hipSuccess;
+  const int S = attn_splits(c, batch);
+  const PlainWs w = plain_carve(c, batch, mode != 0, ws, nullptr);
+  const float scale_log2 = (1.0f / sqrtf((float)c.d)) * kLog2eP;
+  const dim3 grid((unsigned)S, (unsigned)U), block(kPThreads);
+  const Lay lay(c.d, true, c.codec);
+  const int GB = c.G <= 4 ? 4 : (c.G <= 8 ? 8 : 16);
+#define DKV_PATTN(D, GB_)                                                                                      \
+  plain_attn_kernel<D, GB_><<<grid, block, 0, s>>>(c.H, c.G, c.L, S, p.P, p.page_bytes, lay, scale_log2,       \
+                                                   mode != 0, q, table, state, seq_len, p.pages, out, w.part,  \
+                                                   w.logits, p.status)
+#define DKV_PATTN_D(D)              \
+  if (GB == 4) DKV_PATTN(D, 4);     \
+  else if (GB == 8) DKV_PATTN(D, 8); \
+  else DKV_PATTN(D, 16);
+  if (c.d == 128) {
+    DKV_PATTN_D(128)
+  } else {
+    DKV_PATTN_D(64)
+  }
+#undef DKV_PATTN_D
+#undef DKV_PATTN
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_attn_merge(c, batch, S, seq_len, w.part, out, w.ml, mode != 0, s);
+  if (e != hipSuccess) return e;
+  if (mode == 1) return launch_scores_plain(c, p, batch, table, state, seq_len, ws, s);
+  return hipSuccess;
+}
+
+}  // namespace dkv

@@ -59,11 +59,37 @@ __device__ inline void page_dim_bounds(const uint8_t* pg, int nv, int dim, float
   }
 }
 
+// The same for the plain layout of a tier codec variant (segment offsets and
+// K width from sg; a code never spans two bytes).
+template <int D, bool HI>
+__device__ inline void page_dim_bounds_plain(const uint8_t* pg, int nv, int dim, const Seg& sg, float& mn,
+                                             float& mx) {
+  constexpr int T = HI ? kHiTokens : kLoTokens;
+  const uint32_t mask = (1u << sg.kbits) - 1u;
+  uint32_t cb[T], m[T];
+#pragma unroll
+  for (int t = 0; t < T; t++) {
+    int byte, shift;
+    plain_field(sg.kc, D, sg.kbits, t, dim, byte, shift);
+    cb[t] = (uint32_t)pg[byte] >> shift;
+    m[t] = *(const uint32_t*)(pg + sg.km + 4 * t);
+  }
+  mn = INFINITY;
+  mx = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < T; t++) {
+    if (t >= nv) continue;
+    const float x = dequant(h2f((uint16_t)m[t]), h2f((uint16_t)(m[t] >> 16)), cb[t] & mask);
+    mn = fminf(mn, x);
+    mx = fmaxf(mx, x);
+  }
+}
+
 constexpr int kBoundsWgPerUnit = 8;  // workgroups per unit (grid x), striding over its pages
 
 // bounds [P][2][D]: row 0 minima, row 1 maxima
-template <int D>
-__global__ __launch_bounds__(kBThreads) void page_bounds_kernel(int L, int64_t P, int page_bytes,
+template <int D, bool PLAIN>
+__global__ __launch_bounds__(kBThreads) void page_bounds_kernel(int L, int64_t P, int page_bytes, Seg shp, Seg slp,
                                                                const int32_t* __restrict__ table,
                                                                const int32_t* __restrict__ state,
                                                                const uint8_t* __restrict__ pages,
@@ -82,8 +108,13 @@ __global__ __launch_bounds__(kBThreads) void page_bounds_kernel(int L, int64_t P
     const int nv = hi ? min(kHiTokens, nh - kHiTokens * jt) : min(kLoTokens, nl - kLoTokens * jt);
     const uint8_t* pg = pages + (int64_t)id * page_bytes;
     float mn, mx;
-    if (hi) page_dim_bounds<D, true>(pg, nv, dim, mn, mx);
-    else page_dim_bounds<D, false>(pg, nv, dim, mn, mx);
+    if constexpr (PLAIN) {
+      if (hi) page_dim_bounds_plain<D, true>(pg, nv, dim, shp, mn, mx);
+      else page_dim_bounds_plain<D, false>(pg, nv, dim, slp, mn, mx);
+    } else {
+      if (hi) page_dim_bounds<D, true>(pg, nv, dim, mn, mx);
+      else page_dim_bounds<D, false>(pg, nv, dim, mn, mx);
+    }
     float* bo = bounds + (int64_t)id * 2 * D;
     bo[dim] = mn;
     bo[D + dim] = mx;
@@ -162,10 +193,18 @@ hipError_t launch_page_bounds(const Cfg& c, const Pool& p, int batch, const int3
   const int ppb = kBThreads / c.d;
   const int gx = min((c.L + ppb - 1) / ppb, kBoundsWgPerUnit);
   const dim3 grid((unsigned)gx, (unsigned)U), block(kBThreads);
-  if (c.d == 128)
-    page_bounds_kernel<128><<<grid, block, 0, s>>>(c.L, p.P, p.page_bytes, table, state, p.pages, bounds);
-  else
-    page_bounds_kernel<64><<<grid, block, 0, s>>>(c.L, p.P, p.page_bytes, table, state, p.pages, bounds);
+  const Lay lay(c.d, c.plain, c.codec);
+#define DKV_BOUNDS(D, PL)                                                                                 \
+  page_bounds_kernel<D, PL><<<grid, block, 0, s>>>(c.L, p.P, p.page_bytes, lay.seg(true), lay.seg(false), \
+                                                   table, state, p.pages, bounds)
+  if (c.d == 128) {
+    if (c.plain) DKV_BOUNDS(128, true);
+    else DKV_BOUNDS(128, false);
+  } else {
+    if (c.plain) DKV_BOUNDS(64, true);
+    else DKV_BOUNDS(64, false);
+  }
+#undef DKV_BOUNDS
   return hipGetLastError();
 }
 

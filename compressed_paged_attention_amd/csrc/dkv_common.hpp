@@ -94,6 +94,66 @@ __host__ __device__ inline void k_field(int d, bool hi, int tok, int j, int& byt
 }
 
 // ---------------------------------------------------------------------------
+// Tier codec variants ("Results": the bit-split ablation compares K and V
+// code widths such as K8V4, K4V8, K4V2, K2V4, K8V2, K4V1).  Widths other
+// than the default pair (or the default pair given explicitly) use the plain
+// layout: the same six segments and token counts, K and V codes token-major
+// and packed from bit 0 -- code (t, j) at bit (t d + j) b of its segment --
+// so a width in {1, 2, 4, 8} never splits a code across bytes.
+// ---------------------------------------------------------------------------
+struct Codec {
+  int kb_hi, vb_hi, kb_lo, vb_lo;
+};
+
+__host__ __device__ inline Seg plain_seg(int d, bool hi, const Codec& c) {
+  const int T = hi ? kHiTokens : kLoTokens;
+  const int kb = hi ? c.kb_hi : c.kb_lo, vb = hi ? c.vb_hi : c.vb_lo;
+  const int kc = 0;
+  const int km = kc + r16(T * d * kb / 8);
+  const int vc = km + r16(4 * T);
+  const int vm = vc + r16(T * d * vb / 8);
+  const int sc = vm + r16(4 * T);
+  const int ps = sc + r16(4 * T);
+  const int end = ps + r16(4 * T);
+  return Seg{T, kb, vb, kc, km, vc, vm, sc, ps, end};
+}
+
+__host__ __device__ inline int plain_page_bytes(int d, const Codec& c) {
+  const int a = plain_seg(d, true, c).bytes, b = plain_seg(d, false, c).bytes;
+  return a > b ? a : b;
+}
+
+// the largest plain page: 8-bit K and V in both tiers
+__host__ __device__ constexpr int plain_page_max(int d) { return 32 * d * 2 + 4 * 4 * 32; }
+
+__host__ __device__ inline void plain_field(int seg_off, int d, int bits, int tok, int j, int& byte, int& shift) {
+  const int bit = (tok * d + j) * bits;
+  byte = seg_off + (bit >> 3);
+  shift = bit & 7;
+}
+
+// The page layout as seen by the kernels that serve either kind (commit,
+// plan, bounds): the default layout above, or the plain layout of a codec.
+struct Lay {
+  int d;
+  bool plain;
+  Seg s[2];  // [low, high]
+  __host__ __device__ Lay(int d_, bool plain_, const Codec& c) : d(d_), plain(plain_) {
+    s[0] = plain_ ? plain_seg(d_, false, c) : tier_seg(d_, false);
+    s[1] = plain_ ? plain_seg(d_, true, c) : tier_seg(d_, true);
+  }
+  __host__ __device__ const Seg& seg(bool hi) const { return s[hi ? 1 : 0]; }
+  __host__ __device__ void kf(bool hi, int tok, int j, int& byte, int& shift) const {
+    if (plain) plain_field(s[hi ? 1 : 0].kc, d, s[hi ? 1 : 0].kbits, tok, j, byte, shift);
+    else k_field(d, hi, tok, j, byte, shift);
+  }
+  __host__ __device__ void vf(bool hi, int tok, int j, int& byte, int& shift) const {
+    if (plain) plain_field(s[hi ? 1 : 0].vc, d, s[hi ? 1 : 0].vbits, tok, j, byte, shift);
+    else v_field(d, hi, tok, j, byte, shift);
+  }
+};
+
+// ---------------------------------------------------------------------------
 // fp16 helpers (IEEE binary16, round to nearest even via v_cvt_f16_f32).
 // ---------------------------------------------------------------------------
 __device__ inline uint16_t f2h_bits(float x) {

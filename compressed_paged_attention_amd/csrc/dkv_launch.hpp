@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "dkv_common.hpp"
+
 namespace dkv {
 
 struct Cfg {
@@ -15,6 +17,9 @@ struct Cfg {
   const float* ah_head;
   const float* al_head;
   int prompt_rule;  // 0: prompt tokens against alpha/N; 1: against alpha/i (i = position + 1)
+  bool plain;       // a tier codec variant: the plain layout (else the default K8V4 / K4V2 layout)
+  Codec codec;      // its widths (the default pair when !plain)
+  int page_bytes;   // bytes of one unified page under this codec
 };
 
 struct Pool {
@@ -58,6 +63,14 @@ hipError_t launch_release(const Cfg& c, const Pool& p, int batch, const uint8_t*
 
 // decode attention
 int attn_splits(const Cfg& c, int batch);
+// pages per split: a unit with TPg pages takes them in chunks of
+// max(ceil(TPg / S), kSplitMinPages)
+constexpr int kSplitMinPages = 16;
+__host__ __device__ inline int split_pages(int TPg, int S) {
+  if (S <= 1) return TPg;
+  const int q = (TPg + S - 1) / S;
+  return q > kSplitMinPages ? q : kSplitMinPages;
+}
 size_t attn_workspace(const Cfg& c, int batch, bool scores);
 // mode 0: attention; 1: attention + score update; 2: attention keeping logits
 hipError_t launch_attn(const Cfg& c, const Pool& p, int batch, const uint16_t* q,
@@ -65,6 +78,16 @@ hipError_t launch_attn(const Cfg& c, const Pool& p, int batch, const uint16_t* q
                        float* out, int mode, void* ws, hipStream_t s);
 hipError_t launch_scores(const Cfg& c, const Pool& p, int batch, const int32_t* table,
                          const int32_t* state, const int32_t* seq_len, void* ws, hipStream_t s);
+// the split merge: partials [U][S][G][d + 2] -> out; (max, sum) to ml when save
+hipError_t launch_attn_merge(const Cfg& c, int batch, int S, const int32_t* seq_len, const float* part,
+                             float* out, float* ml, bool save, hipStream_t s);
+// tier codec variants (plain layout): attention, score update, workspace
+size_t plain_attn_workspace(const Cfg& c, int batch, bool scores);
+hipError_t launch_attn_plain(const Cfg& c, const Pool& p, int batch, const uint16_t* q,
+                             const int32_t* table, const int32_t* state, const int32_t* seq_len,
+                             float* out, int mode, void* ws, hipStream_t s);
+hipError_t launch_scores_plain(const Cfg& c, const Pool& p, int batch, const int32_t* table,
+                               const int32_t* state, const int32_t* seq_len, void* ws, hipStream_t s);
 // generation step then attention for the same step; ws_step and ws_next are
 // the two step slots (chain: consecutive chained calls before this one)
 hipError_t launch_decode_step(const Cfg& c, const Pool& p, int batch, const int32_t* seq_len,

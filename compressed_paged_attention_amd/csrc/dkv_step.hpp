@@ -145,6 +145,64 @@ __device__ void img_store(const uint32_t* img, const TokWrite& t, uint8_t* pages
   }
 }
 
+// The same three phases for the plain layout of a tier codec variant: a
+// token's K and V codes are whole, 8-byte aligned byte ranges of their own
+// (t d b / 8 bytes in, d b / 8 long), so an existing page needs no load:
+// the token's ranges are zeroed in the image, edited and stored with its
+// four words.
+__device__ inline void img_load_plain(uint32_t* img, const TokWrite& t, const Lay& lay, int page_bytes) {
+  if (!t.on) return;
+  const Seg& sg = lay.seg(t.hi);
+  if (t.fresh) {
+    for (int w = threadIdx.x; w < page_bytes / 4; w += blockDim.x) img[w] = 0u;
+  } else {
+    const int kw = lay.d * sg.kbits / 32, vw = lay.d * sg.vbits / 32;  // words per token
+    for (int w = threadIdx.x; w < kw + vw; w += blockDim.x)
+      img[w < kw ? (sg.kc / 4 + t.idx * kw + w) : (sg.vc / 4 + t.idx * vw + (w - kw))] = 0u;
+  }
+}
+
+__device__ inline void img_token_plain(uint32_t* img, const TokWrite& t, const Lay& lay, uint32_t ck, uint32_t cv,
+                                       uint32_t kmeta, uint32_t vmeta, float score, int32_t pos) {
+  if (!t.on) return;
+  const Seg& sg = lay.seg(t.hi);
+  if (threadIdx.x < lay.d) {
+    int byte, shift;
+    lay.kf(t.hi, t.idx, threadIdx.x, byte, shift);
+    lds_put(img, byte, shift, sg.kbits, ck);
+    lay.vf(t.hi, t.idx, threadIdx.x, byte, shift);
+    lds_put(img, byte, shift, sg.vbits, cv);
+  }
+  if (threadIdx.x == 0) {
+    img[sg.km / 4 + t.idx] = kmeta;
+    img[sg.vm / 4 + t.idx] = vmeta;
+    img[sg.sc / 4 + t.idx] = __float_as_uint(score);
+    img[sg.ps / 4 + t.idx] = (uint32_t)pos;
+  }
+}
+
+__device__ inline void img_store_plain(const uint32_t* img, const TokWrite& t, const Lay& lay, uint8_t* pages,
+                                       int page_bytes) {
+  if (!t.on) return;
+  const Seg& sg = lay.seg(t.hi);
+  uint8_t* pg = pages + (int64_t)t.id * page_bytes;
+  if (t.fresh) {
+    for (int c = threadIdx.x; c < page_bytes / 16; c += blockDim.x) ((uint4*)pg)[c] = ((const uint4*)img)[c];
+    return;
+  }
+  const int kw = lay.d * sg.kbits / 32, vw = lay.d * sg.vbits / 32;
+  for (int w = threadIdx.x; w < kw + vw + 4; w += blockDim.x) {
+    int off;  // word index
+    if (w < kw) off = sg.kc / 4 + t.idx * kw + w;
+    else if (w < kw + vw) off = sg.vc / 4 + t.idx * vw + (w - kw);
+    else {
+      const int seg = w - kw - vw;
+      off = (seg == 0 ? sg.km : seg == 1 ? sg.vm : seg == 2 ? sg.sc : sg.ps) / 4 + t.idx;
+    }
+    ((uint32_t*)pg)[off] = img[off];
+  }
+}
+
 // min and max of the D values held by threads 0..D-1, for n vectors at once
 template <int D, int NV>
 __device__ void block_minmax(float (&mn)[NV], float (&mx)[NV], float* red) {
@@ -353,9 +411,9 @@ __device__ inline bool plan_rec_check(const uint32_t* w, int64_t seq, int nh, in
 }
 
 // LDS scratch of commit_unit, in 32-bit words: two page images plus misc.
-template <int D>
+template <int D, bool PLAIN = false>
 constexpr int commit_lds_words() {
-  return 2 * (page_bytes_for(D) / 4) + 64;
+  return 2 * ((PLAIN ? plain_page_max(D) : page_bytes_for(D)) / 4) + 64;
 }
 
 // Result of commit_unit: whether this unit's step was committed, and its
@@ -372,16 +430,18 @@ struct UnitState {
 // demand words (all-or-nothing check included) and workgroup 0 advances the
 // allocation pointer; otherwise the coordination kernel's result is read.
 // `sm` is LDS scratch of commit_lds_words<D>() words, 16-byte aligned.
-template <int D, bool DIRECT>
+// PLAIN: the plain layout of a tier codec variant, described by `lay`
+// (ignored otherwise); `sm` then holds commit_lds_words<D, true>() words.
+template <int D, bool DIRECT, bool PLAIN = false>
 __device__ UnitState commit_unit(int64_t u, int H, int L, int64_t U, int64_t P, int page_bytes,
                                  const int32_t* __restrict__ seq_len, const uint16_t* __restrict__ k_new,
                                  const uint16_t* __restrict__ v_new, const int64_t* __restrict__ hdr,
                                  const int32_t* __restrict__ rec, const int32_t* __restrict__ nf,
                                  const int32_t* __restrict__ list, int32_t* __restrict__ table,
                                  int32_t* __restrict__ state, uint8_t* pages, uint64_t* ptr, uint32_t* status,
-                                 uint32_t* sm) {
-  constexpr Seg sh = tier_seg(D, true);
-  constexpr int kPageWords = page_bytes_for(D) / 4;
+                                 uint32_t* sm, const Lay& lay = Lay(D, false, Codec{8, 4, 4, 2})) {
+  const Seg sh = PLAIN ? lay.seg(true) : tier_seg(D, true);
+  constexpr int kPageWords = (PLAIN ? plain_page_max(D) : page_bytes_for(D)) / 4;
   const int tid = threadIdx.x;
   const int b = (int)u / H, h = (int)u % H;  // u < 2^31: 32-bit division
   const int32_t* s4c = state + 4 * u;
@@ -408,7 +468,7 @@ __device__ UnitState commit_unit(int64_t u, int H, int L, int64_t U, int64_t P, 
   }
   int32_t page = -1;
   if constexpr (DIRECT) {
-    int* lds = (int*)(sm + 2 * (page_bytes_for(D) / 4));  // 16 ints
+    int* lds = (int*)(sm + 2 * kPageWords);  // 16 ints
     int64_t& s_off = *(int64_t*)(lds + 16);
     uint32_t& s_fl = *(uint32_t*)(lds + 18);
     if (tid == 0) s_fl = 0;
@@ -449,8 +509,13 @@ __device__ UnitState commit_unit(int64_t u, int H, int L, int64_t U, int64_t P, 
   uint32_t* img_h = sm;
   uint32_t* img_l = sm + kPageWords;
   float* red = (float*)(sm + 2 * kPageWords + 20);  // 16 floats
-  img_load<D>(img_h, th, pages, page_bytes);
-  img_load<D>(img_l, tl, pages, page_bytes);
+  if constexpr (PLAIN) {
+    img_load_plain(img_h, th, lay, page_bytes);
+    img_load_plain(img_l, tl, lay, page_bytes);
+  } else {
+    img_load<D>(img_h, th, pages, page_bytes);
+    img_load<D>(img_l, tl, pages, page_bytes);
+  }
   // the requantized token's dequantized values (read before anything is
   // written: its high slot may be the new token's)
   float xk_rq = 0.0f, xv_rq = 0.0f, sc_rq = 0.0f;
@@ -464,10 +529,19 @@ __device__ UnitState commit_unit(int64_t u, int H, int L, int64_t U, int64_t P, 
     pos_rq = *(const int32_t*)(src + sh.ps + 4 * si);
     if (tid < D) {
       int byte, shift;
-      k_field(D, true, si, tid, byte, shift);
-      xk_rq = dequant(h2f((uint16_t)km), h2f((uint16_t)(km >> 16)), ((uint32_t)src[byte] >> shift) & 0xFFu);
-      v_field(D, true, si, tid, byte, shift);
-      xv_rq = dequant(h2f((uint16_t)vm), h2f((uint16_t)(vm >> 16)), ((uint32_t)src[byte] >> shift) & 0xFu);
+      if constexpr (PLAIN) {
+        lay.kf(true, si, tid, byte, shift);
+        xk_rq = dequant(h2f((uint16_t)km), h2f((uint16_t)(km >> 16)),
+                        ((uint32_t)src[byte] >> shift) & ((1u << sh.kbits) - 1u));
+        lay.vf(true, si, tid, byte, shift);
+        xv_rq = dequant(h2f((uint16_t)vm), h2f((uint16_t)(vm >> 16)),
+                        ((uint32_t)src[byte] >> shift) & ((1u << sh.vbits) - 1u));
+      } else {
+        k_field(D, true, si, tid, byte, shift);
+        xk_rq = dequant(h2f((uint16_t)km), h2f((uint16_t)(km >> 16)), ((uint32_t)src[byte] >> shift) & 0xFFu);
+        v_field(D, true, si, tid, byte, shift);
+        xv_rq = dequant(h2f((uint16_t)vm), h2f((uint16_t)(vm >> 16)), ((uint32_t)src[byte] >> shift) & 0xFu);
+      }
     }
   }
   const int32_t N = seq_len[b];
@@ -475,32 +549,31 @@ __device__ UnitState commit_unit(int64_t u, int H, int L, int64_t U, int64_t P, 
   // ---- phase 2: quantize, edit the images ----
   float mn[4] = {xk_new, xv_new, xk_rq, xv_rq}, mx[4] = {xk_new, xv_new, xk_rq, xv_rq};
   block_minmax<D, 4>(mn, mx, red);
-  {
-    const Seg sg = tier_seg(D, true);
+  auto token = [&](uint32_t* img, const TokWrite& t, float xk, float xv, int v, float score, int32_t pos) {
+    const Seg sg = PLAIN ? lay.seg(t.hi) : tier_seg(D, t.hi);
     uint16_t ks16, kz16, vs16, vz16;
     float ks, kz, vs, vz;
-    codec_params(mn[0], mx[0], sg.kbits, ks16, kz16, ks, kz);
-    codec_params(mn[1], mx[1], sg.vbits, vs16, vz16, vs, vz);
-    img_token<D>(img_h, th, codec_code(xk_new, ks, kz, sg.kbits), codec_code(xv_new, vs, vz, sg.vbits),
-                 (uint32_t)ks16 | ((uint32_t)kz16 << 16), (uint32_t)vs16 | ((uint32_t)vz16 << 16), 0.0f, N);
-  }
-  if (tl.on) {
-    const Seg sg = tier_seg(D, false);
-    uint16_t ks16, kz16, vs16, vz16;
-    float ks, kz, vs, vz;
-    codec_params(mn[2], mx[2], sg.kbits, ks16, kz16, ks, kz);
-    codec_params(mn[3], mx[3], sg.vbits, vs16, vz16, vs, vz);
-    img_token<D>(img_l, tl, codec_code(xk_rq, ks, kz, sg.kbits), codec_code(xv_rq, vs, vz, sg.vbits),
-                 (uint32_t)ks16 | ((uint32_t)kz16 << 16), (uint32_t)vs16 | ((uint32_t)vz16 << 16), sc_rq,
-                 pos_rq);
-  }
+    codec_params(mn[v], mx[v], sg.kbits, ks16, kz16, ks, kz);
+    codec_params(mn[v + 1], mx[v + 1], sg.vbits, vs16, vz16, vs, vz);
+    const uint32_t ck = codec_code(xk, ks, kz, sg.kbits), cv = codec_code(xv, vs, vz, sg.vbits);
+    const uint32_t kmeta = (uint32_t)ks16 | ((uint32_t)kz16 << 16), vmeta = (uint32_t)vs16 | ((uint32_t)vz16 << 16);
+    if constexpr (PLAIN) img_token_plain(img, t, lay, ck, cv, kmeta, vmeta, score, pos);
+    else img_token<D>(img, t, ck, cv, kmeta, vmeta, score, pos);
+  };
+  token(img_h, th, xk_new, xv_new, 0, 0.0f, N);
+  if (tl.on) token(img_l, tl, xk_rq, xv_rq, 2, sc_rq, pos_rq);
   __syncthreads();
   // ---- phase 3: stores ----
-  img_store<D>(img_h, th, pages, page_bytes);
-  img_store<D>(img_l, tl, pages, page_bytes);
-  // the unit changed: its plan record (first high page) no longer applies
-  if (tid == 0 && ph >= 1 && id_first >= 0 && id_first < P)
-    *(uint32_t*)(pages + (int64_t)id_first * page_bytes + plan_rec_off<D>()) = 0u;
+  if constexpr (PLAIN) {
+    img_store_plain(img_h, th, lay, pages, page_bytes);
+    img_store_plain(img_l, tl, lay, pages, page_bytes);
+  } else {
+    img_store<D>(img_h, th, pages, page_bytes);
+    img_store<D>(img_l, tl, pages, page_bytes);
+    // the unit changed: its plan record (first high page) no longer applies
+    if (tid == 0 && ph >= 1 && id_first >= 0 && id_first < P)
+      *(uint32_t*)(pages + (int64_t)id_first * page_bytes + plan_rec_off<D>()) = 0u;
+  }
   res = UnitState{true, nh + hi_app, nl + lo_app, ph + (need == kTierHi), pl + (need == kTierLo),
                   need == kTierHi ? ph : (need == kTierLo ? L - 1 - pl : -1), page};
   if (tid == 0) {

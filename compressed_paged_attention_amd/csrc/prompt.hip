@@ -369,7 +369,7 @@ __device__ inline void codes8(const uint32_t* w, float s, float z, uint32_t* c) 
 // its correctly rounded reciprocal and one fma correction: for every fp32
 // range in [0, 2^17] (ranges of fp16 vectors are at most 131008) the result
 // equals the IEEE quotient bit for bit (checked exhaustively on the CPU for
-// 3, 15 and 255: 0 of 3 x 1.2e9 differ).
+// 1, 3, 15 and 255: none of 4 x 1.2e9 differ).
 template <int BITS>
 __device__ inline void codec_params_c(float mn, float mx, uint16_t& s16, uint16_t& z16, float& s, float& z) {
   constexpr float qmax = (float)((1 << BITS) - 1);
@@ -424,6 +424,29 @@ __device__ inline void pack_pos(const PackMeta& m, int g, bool act, const int32_
     }
 }
 
+// Per token: the (K, V) minima and maxima over the group's NA lanes as fp16
+// pairs (K in the low half, V in the high half) from the lane's 8 K and 8 V
+// values (per-lane pair minima / maxima, then a reduction over the group).
+template <int NA>
+__device__ inline void tok_minmax(const uint32_t (&kw)[4], const uint32_t (&vw)[4], uint32_t& mn, uint32_t& mx) {
+  const uint32_t kn = pmin(pmin(kw[0], kw[1]), pmin(kw[2], kw[3]));
+  const uint32_t kx = pmax(pmax(kw[0], kw[1]), pmax(kw[2], kw[3]));
+  const uint32_t vn = pmin(pmin(vw[0], vw[1]), pmin(vw[2], vw[3]));
+  const uint32_t vx = pmax(pmax(vw[0], vw[1]), pmax(vw[2], vw[3]));
+  mn = pmin(__builtin_amdgcn_perm(vn, kn, 0x05040100u), __builtin_amdgcn_perm(vn, kn, 0x07060302u));
+  mx = pmax(__builtin_amdgcn_perm(vx, kx, 0x05040100u), __builtin_amdgcn_perm(vx, kx, 0x07060302u));
+  mn = pmin(mn, lane_xchg<0>(mn));
+  mx = pmax(mx, lane_xchg<0>(mx));
+  mn = pmin(mn, lane_xchg<1>(mn));
+  mx = pmax(mx, lane_xchg<1>(mx));
+  mn = pmin(mn, lane_xchg<2>(mn));
+  mx = pmax(mx, lane_xchg<2>(mx));
+  if constexpr (NA > 8) {
+    mn = pmin(mn, lane_xchg<3>(mn));
+    mx = pmax(mx, lane_xchg<3>(mx));
+  }
+}
+
 // Page packing ("Memory management": a unified page holds its tokens'
 // quantized K and V with their metadata, score and position).  One wave per
 // page, no LDS: lane (g, a), a = lane mod d/8, holds dims 8a..8a+7 of the
@@ -473,23 +496,8 @@ __device__ inline void pack_compute(uint8_t* pg, int lane, int valid, int64_t N,
       const int t = 16 * th + 4 * g + r;
       const uint32_t kw[4] = {kr[th][r][0], kr[th][r][1], kr[th][r][2], kr[th][r][3]};
       const uint32_t vwr[4] = {vr[th][r][0], vr[th][r][1], vr[th][r][2], vr[th][r][3]};
-      // per-lane pair minima / maxima, then (K, V) words reduced over the group
-      const uint32_t kn = pmin(pmin(kw[0], kw[1]), pmin(kw[2], kw[3]));
-      const uint32_t kx = pmax(pmax(kw[0], kw[1]), pmax(kw[2], kw[3]));
-      const uint32_t vn = pmin(pmin(vwr[0], vwr[1]), pmin(vwr[2], vwr[3]));
-      const uint32_t vx = pmax(pmax(vwr[0], vwr[1]), pmax(vwr[2], vwr[3]));
-      uint32_t mn = pmin(__builtin_amdgcn_perm(vn, kn, 0x05040100u), __builtin_amdgcn_perm(vn, kn, 0x07060302u));
-      uint32_t mx = pmax(__builtin_amdgcn_perm(vx, kx, 0x05040100u), __builtin_amdgcn_perm(vx, kx, 0x07060302u));
-      mn = pmin(mn, lane_xchg<0>(mn));
-      mx = pmax(mx, lane_xchg<0>(mx));
-      mn = pmin(mn, lane_xchg<1>(mn));
-      mx = pmax(mx, lane_xchg<1>(mx));
-      mn = pmin(mn, lane_xchg<2>(mn));
-      mx = pmax(mx, lane_xchg<2>(mx));
-      if constexpr (NA > 8) {
-        mn = pmin(mn, lane_xchg<3>(mn));
-        mx = pmax(mx, lane_xchg<3>(mx));
-      }
+      uint32_t mn, mx;
+      tok_minmax<NA>(kw, vwr, mn, mx);
       uint16_t ks16, kz16, vs16, vz16;
       float ks, kz, vs, vz;
       codec_params_c<sg.kbits>(lo_h(mn), lo_h(mx), ks16, kz16, ks, kz);
@@ -540,13 +548,124 @@ __device__ inline void pack_compute(uint8_t* pg, int lane, int valid, int64_t N,
     *(uint4*)(pg + off) = make_uint4(0u, 0u, 0u, 0u);
 }
 
+// codes8 and codec_params_c for a width known at run time (wave-uniform):
+// the same operations with 2^b - 1 and its correctly rounded reciprocal
+// (an IEEE division, as the constant one is) in registers, so the results are
+// those of the constant-width helpers.
+__device__ inline void codes8_var(int bits, const uint32_t* w, float s, float z, uint32_t* c) {
+  const float qmax = (float)((1 << bits) - 1);
+  const float rs = s == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(s);
+  float dmax = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; e++) {
+    const float d = (e & 1) ? sub_h<1>(w[e >> 1], z) : sub_h<0>(w[e >> 1], z);
+    const float t = __fmul_rn(d, rs);
+    const float rt = __builtin_rintf(t);
+    dmax = fmaxf(dmax, __builtin_fabsf(t - rt));
+    c[e] = (uint32_t)__builtin_amdgcn_fmed3f(rt, 0.0f, qmax);
+  }
+  if (!(dmax < 0.5f - 0x1p-13f)) {
+#pragma unroll
+    for (int e = 0; e < 8; e++) c[e] = codec_code((e & 1) ? hi_h(w[e >> 1]) : lo_h(w[e >> 1]), s, z, bits);
+  }
+}
+
+__device__ inline void codec_params_var(int bits, float mn, float mx, uint16_t& s16, uint16_t& z16, float& s,
+                                        float& z) {
+  const float qmax = (float)((1 << bits) - 1);
+  const float rq = __fdiv_rn(1.0f, qmax);
+  const float range = __fsub_rn(mx, mn);
+  const float q0 = __fmul_rn(range, rq);
+  const float scale = __builtin_fmaf(__builtin_fmaf(-q0, qmax, range), rq, q0);
+  s16 = f2h_bits(scale);
+  z16 = f2h_bits(mn);
+  s = h2f(s16);
+  z = h2f(z16);
+}
+
+// The 8 codes of dims 8a..8a+7 of token t in the plain layout: 8b bits at
+// bit (t d + 8a) b of the segment, i.e. b whole bytes at byte (t d/8 + a) b,
+// code e at bit e b (little-endian).
+template <int D>
+__device__ inline void put_codes8(uint8_t* seg, int bits, int t, int a, const uint32_t* c) {
+  uint32_t w0 = 0u, w1 = 0u;
+#pragma unroll
+  for (int e = 0; e < 8; e++) {
+    const int bit = e * bits;  // < 64
+    if (bit < 32) w0 |= c[e] << bit;
+    else w1 |= c[e] << (bit - 32);
+  }
+  uint8_t* dst = seg + (t * (D / 8) + a) * bits;
+  if (bits == 8) *(uint2*)dst = make_uint2(w0, w1);
+  else if (bits == 4) *(uint32_t*)dst = w0;
+  else if (bits == 2) *(uint16_t*)dst = (uint16_t)w0;
+  else *dst = (uint8_t)w0;
+}
+
+// Page packing for a tier codec variant (plain layout, widths in sg): the
+// lane and token mapping, minima / maxima and the score and position words
+// of pack_compute; the codes of a lane's 8 dims leave as whole bytes.
+template <int D, bool HI>
+__device__ inline void pack_compute_plain(uint8_t* pg, int lane, int valid, int64_t N, const int32_t (&pos)[2][4],
+                                          u32x4 (&kr)[2][4], u32x4 (&vr)[2][4], const float (&mean)[2][4],
+                                          const Seg& sg, int page_bytes) {
+  constexpr int NA = D / 8;
+  constexpr int NT = HI ? 1 : 2;
+  const int a = lane % NA, g = lane / NA;
+  const bool act = g < 4;
+#pragma unroll
+  for (int th = 0; th < NT; th++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int t = 16 * th + 4 * g + r;
+      const bool ok = act && t < valid;
+      if (!ok) {
+        kr[th][r] = u32x4{0u, 0u, 0u, 0u};
+        vr[th][r] = u32x4{0u, 0u, 0u, 0u};
+      }
+      if (act && (a == 2 || a == 3)) {
+        uint32_t wd = 0u;
+        if (ok)
+          wd = a == 3 ? (uint32_t)pos[th][r] : __float_as_uint(__fmul_rn(mean[th][r], (float)(N - 1 - pos[th][r])));
+        *(uint32_t*)(pg + (a == 2 ? sg.sc : sg.ps) + 4 * t) = wd;
+      }
+    }
+#pragma unroll
+  for (int th = 0; th < NT; th++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int t = 16 * th + 4 * g + r;
+      const uint32_t kw[4] = {kr[th][r][0], kr[th][r][1], kr[th][r][2], kr[th][r][3]};
+      const uint32_t vwr[4] = {vr[th][r][0], vr[th][r][1], vr[th][r][2], vr[th][r][3]};
+      uint32_t mn, mx;
+      tok_minmax<NA>(kw, vwr, mn, mx);
+      uint16_t ks16, kz16, vs16, vz16;
+      float ks, kz, vs, vz;
+      codec_params_var(sg.kbits, lo_h(mn), lo_h(mx), ks16, kz16, ks, kz);
+      codec_params_var(sg.vbits, hi_h(mn), hi_h(mx), vs16, vz16, vs, vz);
+      uint32_t c[8];
+      codes8_var(sg.kbits, kw, ks, kz, c);
+      if (act) put_codes8<D>(pg + sg.kc, sg.kbits, t, a, c);
+      codes8_var(sg.vbits, vwr, vs, vz, c);
+      if (act) {
+        put_codes8<D>(pg + sg.vc, sg.vbits, t, a, c);
+        if (a < 2)
+          *(uint32_t*)(pg + (a == 0 ? sg.km : sg.vm) + 4 * t) =
+              a == 0 ? ((uint32_t)ks16 | ((uint32_t)kz16 << 16)) : ((uint32_t)vs16 | ((uint32_t)vz16 << 16));
+      }
+    }
+  for (int off = sg.bytes + 16 * lane; off < page_bytes; off += 16 * 64)
+    *(uint4*)(pg + off) = make_uint4(0u, 0u, 0u, 0u);
+}
+
 // Persistent: each wave packs a contiguous range of the call's TP pages
 // (items in unit order, each unit's high pages then its low pages; the
 // owner of an item comes from the page map the list kernel wrote).  While a
 // page's rows are in flight the wave looks up the next page and loads its
 // positions, so a page waits for one round trip.
-template <int D>
+template <int D, bool PLAIN>
 __global__ __launch_bounds__(256) void prompt_pack_kernel(int H, int L, int64_t total, int64_t P, int page_bytes,
+                                                          Seg sgh, Seg sgl,
                                                           const int64_t* __restrict__ hdr,
                                                           const int64_t* __restrict__ rec,
                                                           const int32_t* __restrict__ pmap,
@@ -597,8 +716,13 @@ __global__ __launch_bounds__(256) void prompt_pack_kernel(int H, int L, int64_t 
       if (lane == 0) atomicOr(status, kStBadState);
     } else {
       uint8_t* pg = pages + (int64_t)m.id * page_bytes;
-      if (m.hi) pack_compute<D, true>(pg, lane, m.valid, m.N, pos, kr, vr, mean);
-      else pack_compute<D, false>(pg, lane, m.valid, m.N, pos, kr, vr, mean);
+      if constexpr (PLAIN) {
+        if (m.hi) pack_compute_plain<D, true>(pg, lane, m.valid, m.N, pos, kr, vr, mean, sgh, page_bytes);
+        else pack_compute_plain<D, false>(pg, lane, m.valid, m.N, pos, kr, vr, mean, sgl, page_bytes);
+      } else {
+        if (m.hi) pack_compute<D, true>(pg, lane, m.valid, m.N, pos, kr, vr, mean);
+        else pack_compute<D, false>(pg, lane, m.valid, m.N, pos, kr, vr, mean);
+      }
     }
     m = mn;
 #pragma unroll
@@ -628,17 +752,24 @@ hipError_t launch_prompt(const Cfg& c, const Pool& p, int batch, int64_t total, 
   int dev = 0, cus = 0, per_cu = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e == hipSuccess)
-    e = c.d == 128 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prompt_pack_kernel<128>, 256, 0)
-                   : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prompt_pack_kernel<64>, 256, 0);
-  if (e != hipSuccess) return e;
-  int64_t grid = (int64_t)(cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
-  if (c.d == 128)
-    prompt_pack_kernel<128><<<dim3((unsigned)grid), dim3(256), 0, s>>>(
-        c.H, c.L, total, p.P, p.page_bytes, w.hdr, w.rec, w.pmap, w.pos, table, k, v, scores, p.pages, p.status);
-  else
-    prompt_pack_kernel<64><<<dim3((unsigned)grid), dim3(256), 0, s>>>(
-        c.H, c.L, total, p.P, p.page_bytes, w.hdr, w.rec, w.pmap, w.pos, table, k, v, scores, p.pages, p.status);
+  const Lay lay(c.d, c.plain, c.codec);
+#define DKV_PACK(D, PL)                                                                                            \
+  do {                                                                                                             \
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prompt_pack_kernel<D, PL>, 256, 0); \
+    if (e != hipSuccess) return e;                                                                                 \
+    const int64_t grid = (int64_t)(cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);                                 \
+    prompt_pack_kernel<D, PL><<<dim3((unsigned)grid), dim3(256), 0, s>>>(                                          \
+        c.H, c.L, total, p.P, p.page_bytes, lay.seg(true), lay.seg(false), w.hdr, w.rec, w.pmap, w.pos, table, k,  \
+        v, scores, p.pages, p.status);                                                                             \
+  } while (0)
+  if (c.d == 128) {
+    if (c.plain) DKV_PACK(128, true);
+    else DKV_PACK(128, false);
+  } else {
+    if (c.plain) DKV_PACK(64, true);
+    else DKV_PACK(64, false);
+  }
+#undef DKV_PACK
   return hipGetLastError();
 }
 

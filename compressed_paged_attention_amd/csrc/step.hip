@@ -50,11 +50,13 @@ constexpr int kRowCache = 4096;   // table rows up to this long are read once in
 // in one round; then one pass over both tiers' score and position words finds
 // t_c, the least important non-window high token and the least important low
 // token (wave butterflies, then the four waves' candidates in one quad).
-template <int D>
+// PLAIN (a tier codec variant): score and position words at the offsets of
+// sh / sl, and no plan records (their spare bytes are not reserved there).
+template <int D, bool PLAIN>
 __global__ __launch_bounds__(kPlanThreads) void step_plan_kernel(int H, int L, int W, int S_max, int lo_en, float ah,
                                                                  float al, const float* __restrict__ ah_head,
                                                                  const float* __restrict__ al_head, int64_t P,
-                                                                 int page_bytes,
+                                                                 int page_bytes, Seg shp, Seg slp,
                                                                  const int32_t* __restrict__ seq_len,
                                                                  const int32_t* __restrict__ table,
                                                                  const int32_t* __restrict__ state,
@@ -94,7 +96,7 @@ __global__ __launch_bounds__(kPlanThreads) void step_plan_kernel(int H, int L, i
   // unit's first high page)
   const int32_t first_id = row[0];
   uint32_t rw[kRecWords];
-  if (tid == 0) {
+  if (!PLAIN && tid == 0) {
     const uint32_t* w = (const uint32_t*)(pages + (int64_t)min(max(first_id, 0), (int32_t)(P - 1)) * page_bytes +
                                           plan_rec_off<D>());
 #pragma unroll
@@ -128,7 +130,7 @@ __global__ __launch_bounds__(kPlanThreads) void step_plan_kernel(int H, int L, i
   }
   auto page_of = [&](int tix) { return cached ? row_s[tix] : row[tix]; };
   // ---- a plan record left by the previous attention: no scan needed ----
-  if (tid == 0) {
+  if (!PLAIN && tid == 0) {
     s_rec = 0;
     const int32_t p0 = ph >= 1 ? first_id : -1;
     if (p0 >= 0 && p0 < P) {
@@ -139,9 +141,10 @@ __global__ __launch_bounds__(kPlanThreads) void step_plan_kernel(int H, int L, i
       }
     }
   }
+  if (PLAIN && tid == 0) s_rec = 0;
   __syncthreads();
   if (s_rec) return;
-  const Seg sh = tier_seg(D, true), sl = tier_seg(D, false);
+  const Seg sh = PLAIN ? shp : tier_seg(D, true), sl = PLAIN ? slp : tier_seg(D, false);
   const int64_t tc_pos = N - W;
   const double dah = (double)(ah_head ? ah_head[u % H] : ah), dal = (double)(al_head ? al_head[u % H] : al);
   const Cand none{0.0f, kNoPos, 0};
@@ -292,18 +295,41 @@ __global__ __launch_bounds__(256) void step_commit_kernel(int H, int L, int64_t 
                          state, pages, ptr, status, sm);
 }
 
+// The same for the plain layout of a tier codec variant.
+template <int D, bool DIRECT>
+__global__ __launch_bounds__(256) void step_commit_plain_kernel(int H, int L, int64_t U, int64_t P, int page_bytes,
+                                                                Lay lay, const int32_t* __restrict__ seq_len,
+                                                                const uint16_t* __restrict__ k_new,
+                                                                const uint16_t* __restrict__ v_new,
+                                                                const int64_t* __restrict__ hdr,
+                                                                const int32_t* __restrict__ rec,
+                                                                const int32_t* __restrict__ nf,
+                                                                const int32_t* __restrict__ list,
+                                                                int32_t* __restrict__ table,
+                                                                int32_t* __restrict__ state, uint8_t* pages,
+                                                                uint64_t* ptr, uint32_t* status) {
+  __shared__ __align__(16) uint32_t sm[commit_lds_words<D, true>()];
+  commit_unit<D, DIRECT, true>(blockIdx.x, H, L, U, P, page_bytes, seq_len, k_new, v_new, hdr, rec, nf, list,
+                               table, state, pages, ptr, status, sm, lay);
+}
+
 hipError_t launch_step_plan(const Cfg& c, const Pool& p, int batch, const int32_t* seq_len, const int32_t* table,
                             const int32_t* state, void* ws, hipStream_t s) {
   const int64_t U = (int64_t)batch * c.H;
   if (U == 0) return hipSuccess;
   const StepWs w = step_carve(c, batch, ws);
-#define DKV_PLAN(D)                                                                                       \
-  step_plan_kernel<D><<<dim3((unsigned)U), dim3(kPlanThreads), 0, s>>>(c.H, c.L, c.W, c.S_max, c.lo_en, c.ah, \
-                                                                       c.al, c.ah_head, c.al_head, p.P,        \
-                                                                       p.page_bytes, seq_len, table,           \
-                                                                       state, p.pages, p.ptr, w.hdr, w.rec, w.nf)
-  if (c.d == 128) DKV_PLAN(128);
-  else DKV_PLAN(64);
+  const Lay lay(c.d, c.plain, c.codec);
+#define DKV_PLAN(D, PL)                                                                                    \
+  step_plan_kernel<D, PL><<<dim3((unsigned)U), dim3(kPlanThreads), 0, s>>>(                                 \
+      c.H, c.L, c.W, c.S_max, c.lo_en, c.ah, c.al, c.ah_head, c.al_head, p.P, p.page_bytes, lay.seg(true),  \
+      lay.seg(false), seq_len, table, state, p.pages, p.ptr, w.hdr, w.rec, w.nf)
+  if (c.d == 128) {
+    if (c.plain) DKV_PLAN(128, true);
+    else DKV_PLAN(128, false);
+  } else {
+    if (c.plain) DKV_PLAN(64, true);
+    else DKV_PLAN(64, false);
+  }
 #undef DKV_PLAN
   return hipGetLastError();
 }
@@ -326,14 +352,30 @@ hipError_t launch_step_commit(const Cfg& c, const Pool& p, int batch, const int3
   step_commit_kernel<D, DIR><<<grid, block, 0, s>>>(c.H, c.L, U, p.P, p.page_bytes, seq_len, k, v, w.hdr, \
                                                     w.rec, w.nf, p.list, table, state, p.pages, p.ptr,  \
                                                     p.status)
-  if (U <= kDirectUnits) {
+#define DKV_COMMIT_PLAIN(D, DIR)                                                                         \
+  step_commit_plain_kernel<D, DIR><<<grid, block, 0, s>>>(c.H, c.L, U, p.P, p.page_bytes,                 \
+                                                          Lay(c.d, true, c.codec), seq_len, k, v, w.hdr,  \
+                                                          w.rec, w.nf, p.list, table, state, p.pages,     \
+                                                          p.ptr, p.status)
+  const bool direct = U <= kDirectUnits;
+  if (!direct)
+    step_coord_kernel<<<dim3(1), dim3(1024), 0, s>>>(U, p.P, w.nf, w.rec, p.list, w.hdr, p.ptr, p.status);
+  if (c.plain) {
+    if (c.d == 128) {
+      if (direct) DKV_COMMIT_PLAIN(128, true);
+      else DKV_COMMIT_PLAIN(128, false);
+    } else {
+      if (direct) DKV_COMMIT_PLAIN(64, true);
+      else DKV_COMMIT_PLAIN(64, false);
+    }
+  } else if (direct) {
     if (c.d == 128) DKV_COMMIT(128, true);
     else DKV_COMMIT(64, true);
   } else {
-    step_coord_kernel<<<dim3(1), dim3(1024), 0, s>>>(U, p.P, w.nf, w.rec, p.list, w.hdr, p.ptr, p.status);
     if (c.d == 128) DKV_COMMIT(128, false);
     else DKV_COMMIT(64, false);
   }
+#undef DKV_COMMIT_PLAIN
 #undef DKV_COMMIT
   return hipGetLastError();
 }

@@ -75,6 +75,18 @@ typedef struct {
   int32_t prompt_rule;        /* DIFFKV_RULE_ALPHA_N (0) or DIFFKV_RULE_ALPHA_I (1) */
   const float* alpha_h_head;  /* [num_kv_heads] device, or NULL */
   const float* alpha_l_head;  /* [num_kv_heads] device, or NULL */
+  /* Tier codecs ("Results": the bit-split ablation, e.g. K4V8, K2V4, K8V2,
+   * K4V1 against K8V4 / K4V2): code widths of K and V in the high and the
+   * low tier, each in {1, 2, 4, 8}; all four 0 = the default K8V4 / K4V2.
+   * A variant (or the default pair given explicitly) uses the plain page
+   * layout: the same six segments and 16 / 32 tokens per page, codes
+   * token-major and packed from bit 0 (code (t, j) at bit (t d + j) b of its
+   * segment); diffkv_page_bytes gives its page size.  Every entry point
+   * takes variants, with the same results and status rules; they run on
+   * general kernels (codes dequantized in fp32 on the vector units): a
+   * decode step is the STEP followed by the attention (chain is ignored) and
+   * no next-step plan records are kept (a STEP always scans the unit). */
+  int32_t hi_k_bits, hi_v_bits, lo_k_bits, lo_v_bits;
 } diffkv_config;
 
 enum { DIFFKV_RULE_ALPHA_N = 0, DIFFKV_RULE_ALPHA_I = 1 };

@@ -23,9 +23,12 @@ def live_pages(page_table: np.ndarray) -> list:
 
 def plan_record_span(cfg) -> tuple:
     """Bytes after the last segment of a high page that the library uses for
-    its private plan record (the oracle leaves them zero)."""
+    its private plan record (the oracle leaves them zero); none for a tier
+    codec variant, which keeps no plan records."""
     from oracle import HI, tier_layout
     _, seg = tier_layout(cfg, HI)
+    if any(cfg.get(k, 0) for k in ("hi_k_bits", "hi_v_bits", "lo_k_bits", "lo_v_bits")):
+        return int(seg[6]), 0
     return int(seg[6]), 64
 
 

@@ -103,3 +103,29 @@ def test_policy_and_bounds_host_validation():
     assert L.diffkv_page_scores(ctypes.byref(cfg), ctypes.byref(pool), 0, *ok, None) == dk.DIFFKV_OK
     for bad in ([fake + 2] + [fake] * 5, [fake] * 4 + [fake + 4, fake]):
         assert L.diffkv_page_scores(ctypes.byref(cfg), ctypes.byref(pool), 0, *bad, None) == dk.DIFFKV_E_INVALID
+
+
+def test_codec_variant_page_bytes_and_validation():
+    """Tier codec variants: the library's page size is the plain layout's
+    (the larger tier: six 16-byte aligned segments, codes T d b / 8 bytes),
+    the same as the oracle's for every width pair; widths outside
+    {1, 2, 4, 8}, or some but not all four set, are refused; all four zero
+    is the default layout."""
+    import itertools
+
+    import compressed_paged_attention_amd as dk
+    import oracle
+    from workloads import synth
+    c = synth.config("llama3_8b")
+    r16 = lambda x: -(-x // 16) * 16
+    for d in (64, 128):
+        for hk, hv, lk, lv in itertools.product((1, 2, 4, 8), repeat=4):
+            v = dict(c, head_dim=d, hi_k_bits=hk, hi_v_bits=hv, lo_k_bits=lk, lo_v_bits=lv)
+            want = max(r16(T * d * kb // 8) + r16(T * d * vb // 8) + 16 * T
+                       for T, kb, vb in ((16, hk, hv), (32, lk, lv)))
+            assert dk.diffkv_page_bytes(v) == want == oracle.page_bytes(v), (d, hk, hv, lk, lv)
+            for op in (dk.ATTN, dk.ATTN_SCORES, dk.DECODE_STEP_SCORES):
+                assert dk.diffkv_workspace_bytes(v, op, 4, 0) > 0
+    assert dk.diffkv_page_bytes(dict(c, hi_k_bits=3, hi_v_bits=4, lo_k_bits=4, lo_v_bits=2)) == -1
+    assert dk.diffkv_page_bytes(dict(c, hi_k_bits=8)) == -1
+    assert dk.diffkv_page_bytes(dict(c, hi_k_bits=0, hi_v_bits=0, lo_k_bits=0, lo_v_bits=0)) == 3584
