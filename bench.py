@@ -621,6 +621,73 @@ def side_timings(args, name, dk):
     return out
 
 
+CODEC_VARIANTS = ((4, 8, 2, 4), (8, 2, 4, 1))  # (K, V) high, (K, V) low: the ablation's K4V8/K2V4 and K8V2/K4V1
+
+
+def codec_timings(args, name, dk):
+    """Tier codec variants (plain layout) at the workload's shape: decode
+    attention with the score update (diffkv_decode_attn) and the generation
+    step (diffkv_compact STEP) on the compacted cache; each a warmup call,
+    then 8 calls timed with HIP events on a held stream (the steps advance
+    the cache).  Algorithmic bytes of the attention: per retained token its
+    K and V codes (d (b_K + b_V) / 8) and scale/zero words (8), 8 for the
+    score read-modify-write, 4 per page-table entry, q (fp16) and out (fp32)
+    rows."""
+    import torch
+
+    from workloads import synth
+    dev = torch.device("cuda:0")
+    out = {"workload": WORKLOAD_NAMES.get(name, name)}
+    for codec in CODEC_VARIANTS:
+        hk, hv, lk, lv = codec
+        cfg = dict(synth.config(name), hi_k_bits=hk, hi_v_bits=hv, lo_k_bits=lk, lo_v_bits=lv)
+        B, H, G, d = cfg["batch"], cfg["num_kv_heads"], cfg["gqa_group"], cfg["head_dim"]
+        lens = synth.seq_lens(cfg)
+        P = synth.pool_pages(cfg, lens, dk.diffkv_page_bytes(cfg))
+        total = int(lens.sum())
+        pr = synth.make_prompt(cfg, device=dev, lens=lens)
+        st = dk.DiffKVState(cfg, B, P, max_total_tokens=total, device=dev)
+        cu = pr["cu_seqlens"].to(dev)
+        t, _ = st.classify(cu, pr["scores"])
+        st.compact_prompt(cu, pr["k"], pr["v"], pr["scores"], t)
+        del pr
+        dec = synth.make_decode(cfg, 0, device=dev)
+        seq = lens.to(torch.int32).to(dev)
+        n = 8
+
+        def timed(fn):
+            fn()
+            torch.cuda.synchronize()
+            torch.cuda._sleep(args.hold_cycles)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(n):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / n
+
+        ts = st.tier_state.view(-1, 4).to(torch.int64).sum(0).tolist()
+        n_hi, n_lo, p_hi, p_lo = ts
+        nbytes = (n_hi * (d * (hk + hv) // 8 + 8) + n_lo * (d * (lk + lv) // 8 + 8) + 8 * (n_hi + n_lo)
+                  + 4 * (p_hi + p_lo) + B * H * G * d * (2 + 4))
+        us_attn = timed(lambda: st.decode_attn(dec["q"], seq, update_scores=1))
+        seqs = [seq + i for i in range(n + 1)]  # each step one token further
+        it = iter(seqs)
+        us_step = timed(lambda: st.compact_step(next(it), dec["k_new"], dec["v_new"]))
+        assert int(st.pool.status[0]) == 0, "codec variant step status"
+        gbs = nbytes / (us_attn * 1e-6) / 1e9
+        out[f"K{hk}V{hv}_K{lk}V{lv}"] = {
+            "attn_us": us_attn, "step_us": us_step, "page_bytes": dk.diffkv_page_bytes(cfg),
+            "retained_hi_lo_tokens": [n_hi, n_lo],
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS, "kernel": "plain_attn_kernel + merge + plain_score_kernel",
+                         "bytes_per_launch": int(nbytes)}}
+        del st
+        torch.cuda.empty_cache()
+    return out
+
+
 def roofline(kernel, nbytes, us, workload, stream_gbps):
     achieved = nbytes / (us * 1e-6) / 1e9
     return {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -722,6 +789,7 @@ def main():
         res["extra"] = {WORKLOAD_NAMES.get(args.extra_workload, args.extra_workload): ex}
         res["extra"]["prompt_importance"] = importance_timing(args, args.extra_workload, dk)
         res["extra"]["key_bounds_and_keydiff"] = side_timings(args, args.extra_workload, dk)
+        res["extra"]["codec_variants"] = codec_timings(args, args.extra_workload, dk)
     print(json.dumps(res), flush=True)
 
 

@@ -7,8 +7,9 @@
 // dequantized per token as s*c + z; "Implementation": high pages before low
 // pages, sequence splits merged at the end), for any pair of widths per tier:
 //
-//   plain_attn_kernel   (split, unit) workgroups of 4 waves; wave w takes the
-//                       split's pages w, w+4, ...  Per page:
+//   plain_attn_kernel   (split, unit) workgroups of 8 waves; wave w takes the
+//                       split's pages w, w+8, ...  Per page (every load of
+//                       the page issued first):
 //     QK: lane = (token t, part of d): the token's codes of that part in
 //         16-code blocks (2b bytes each), dequantized in fp32 and dotted with
 //         the group's q heads (fp32 in LDS, padded with zero rows to GB);
@@ -35,7 +36,7 @@ namespace dkv {
 
 namespace {
 
-constexpr int kPWaves = 4;
+constexpr int kPWaves = 8;
 constexpr int kPThreads = 64 * kPWaves;
 constexpr float kLog2eP = 1.4426950408889634f;
 
@@ -92,25 +93,78 @@ __device__ inline uint32_t code_at(const uint32_t (&w)[4], int e) {
   return (w[(e * B) >> 5] >> ((e * B) & 31)) & ((1u << B) - 1u);
 }
 
-// q . k^ for the lane's token and part of d, every head of the padded group.
-template <int D, int T, int KB, int GB>
-__device__ inline void plain_qk(const uint8_t* pg, const Seg& sg, int lane, const float* qs, float (&acc)[GB]) {
-  constexpr int PARTS = 64 / T, DP = D / PARTS;
+// Everything one lane loads for one page: the K code blocks of its token and
+// part of d (QK mapping), its token's K scale/zero word, the V scale/zero
+// word of slot `lane`, and the bytes holding its V codes of every slot (d/64
+// consecutive dims: one byte, or two for 8-bit codes at d = 128).  High
+// pages use the first half of kw and cw.
+template <int D>
+struct PageLd {
+  uint32_t kw[D / 32][4];
+  uint32_t cw[kLoTokens];
+  uint32_t kmw, vmw;
+};
+
+template <int D, int T, int KB>
+__device__ inline void plain_load_k(const uint8_t* pg, const Seg& sg, int lane, int nv, PageLd<D>& r) {
+  constexpr int PARTS = 64 / T, DP = D / PARTS, DL = D / 64;
   const int t = lane % T, part = lane / T;
-  const uint32_t mw = *(const uint32_t*)(pg + sg.km + 4 * t);
-  const float s = h2f((uint16_t)(mw & 0xFFFFu)), z = h2f((uint16_t)(mw >> 16));
+  r.kmw = *(const uint32_t*)(pg + sg.km + 4 * t);
+  r.vmw = lane < T ? *(const uint32_t*)(pg + sg.vm + 4 * lane) : 0u;
+#pragma unroll
+  for (int blk = 0; blk < DP / 16; blk++) load16<KB>(pg + sg.kc + (t * D + part * DP + 16 * blk) * KB / 8, r.kw[blk]);
+  // V: slot k's codes of the lane's dims start at bit (k d + jd) b; k d b is
+  // a whole number of bytes, so the shift (jd b mod 8) is the lane's own and
+  // is applied where the codes are used.  Slots past nv are read too (they
+  // are inside the page) and never used.
+  const int vb = sg.vbits;
+  const uint8_t* vbase = pg + sg.vc + ((lane * DL * vb) >> 3);
+  const int stride = D * vb / 8;
+  if (DL * vb <= 8) {
+#pragma unroll
+    for (int k = 0; k < T; k++) r.cw[k] = vbase[k * stride];
+  } else {  // two 8-bit codes, 2-byte aligned
+#pragma unroll
+    for (int k = 0; k < T; k++) r.cw[k] = *(const uint16_t*)(vbase + k * stride);
+  }
+  (void)nv;
+}
+
+template <int D, int T>
+__device__ inline void plain_load(const uint8_t* pg, const Seg& sg, int lane, int nv, PageLd<D>& r) {
+  if (sg.kbits == 8) plain_load_k<D, T, 8>(pg, sg, lane, nv, r);
+  else if (sg.kbits == 4) plain_load_k<D, T, 4>(pg, sg, lane, nv, r);
+  else if (sg.kbits == 2) plain_load_k<D, T, 2>(pg, sg, lane, nv, r);
+  else plain_load_k<D, T, 1>(pg, sg, lane, nv, r);
+}
+
+// q . k^ for the lane's token and part of d, every head of the padded group,
+// from the codes: q . k^ = s (q . c) + z sum(q) (the parts of d summed
+// first).  qs holds q as [d][GB] (one 16-byte read gives four heads of a
+// dim), qsum the heads' sums.
+template <int D, int T, int KB, int GB>
+__device__ inline void plain_qk(const uint32_t (&w)[D / 32][4], uint32_t mw, int lane, const float* qs,
+                                const float* qsum, float (&x)[GB]) {
+  constexpr int PARTS = 64 / T, DP = D / PARTS;
+  const int part = lane / T;
+  float acc[GB];
 #pragma unroll
   for (int g = 0; g < GB; g++) acc[g] = 0.0f;
 #pragma unroll
   for (int blk = 0; blk < DP / 16; blk++) {
     const int j0 = part * DP + 16 * blk;
-    uint32_t w[4];
-    load16<KB>(pg + sg.kc + (t * D + j0) * KB / 8, w);
 #pragma unroll
     for (int e = 0; e < 16; e++) {
-      const float x = dequant(s, z, code_at<KB>(w, e));
+      const float c = (float)code_at<KB>(w[blk], e);
+      const float4* qv = (const float4*)(qs + (j0 + e) * GB);
 #pragma unroll
-      for (int g = 0; g < GB; g++) acc[g] = __builtin_fmaf(qs[g * D + j0 + e], x, acc[g]);
+      for (int g4 = 0; g4 < GB / 4; g4++) {
+        const float4 q4 = qv[g4];
+        acc[4 * g4 + 0] = __builtin_fmaf(q4.x, c, acc[4 * g4 + 0]);
+        acc[4 * g4 + 1] = __builtin_fmaf(q4.y, c, acc[4 * g4 + 1]);
+        acc[4 * g4 + 2] = __builtin_fmaf(q4.z, c, acc[4 * g4 + 2]);
+        acc[4 * g4 + 3] = __builtin_fmaf(q4.w, c, acc[4 * g4 + 3]);
+      }
     }
   }
   // the parts of d (lanes t + T k), summed in the same order in every lane
@@ -119,61 +173,49 @@ __device__ inline void plain_qk(const uint8_t* pg, const Seg& sg, int lane, cons
     if constexpr (PARTS == 4) acc[g] += __shfl_xor(acc[g], 16, 64);
     acc[g] += __shfl_xor(acc[g], 32, 64);
   }
+  const float s = h2f((uint16_t)(mw & 0xFFFFu)), z = h2f((uint16_t)(mw >> 16));
+#pragma unroll
+  for (int g = 0; g < GB; g++) x[g] = __builtin_fmaf(s, acc[g], z * qsum[g]);
 }
 
 template <int D, int T, int GB>
-__device__ inline void plain_qk_any(int kb, const uint8_t* pg, const Seg& sg, int lane, const float* qs,
-                                    float (&acc)[GB]) {
-  if (kb == 8) plain_qk<D, T, 8, GB>(pg, sg, lane, qs, acc);
-  else if (kb == 4) plain_qk<D, T, 4, GB>(pg, sg, lane, qs, acc);
-  else if (kb == 2) plain_qk<D, T, 2, GB>(pg, sg, lane, qs, acc);
-  else plain_qk<D, T, 1, GB>(pg, sg, lane, qs, acc);
+__device__ inline void plain_qk_any(int kb, const PageLd<D>& r, int lane, const float* qs, const float* qsum,
+                                    float (&x)[GB]) {
+  if (kb == 8) plain_qk<D, T, 8, GB>(r.kw, r.kmw, lane, qs, qsum, x);
+  else if (kb == 4) plain_qk<D, T, 4, GB>(r.kw, r.kmw, lane, qs, qsum, x);
+  else if (kb == 2) plain_qk<D, T, 2, GB>(r.kw, r.kmw, lane, qs, qsum, x);
+  else plain_qk<D, T, 1, GB>(r.kw, r.kmw, lane, qs, qsum, x);
 }
 
-// o[g][e] += p[t][g] v^[t][lane dims] over the page's nv tokens; pw holds the
-// weights [32][16] of this wave.
-template <int D, int VB, int GB>
-__device__ inline void plain_pv(const uint8_t* pg, const Seg& sg, int lane, int nv, const float* pw,
+// o[g][e] += p'[t][g] c[t][lane dims] over the page's nv slots, pw holding
+// this wave's p' = p s_v as [32][16] (the z_v part is summed separately:
+// sum_t p v^ = sum_t (p s_v) c + sum_t p z_v).
+template <int D, int T, int GB>
+__device__ inline void plain_pv(int vb, const uint32_t (&cw)[kLoTokens], int nv, int lane, const float* pw,
                                 float (&o)[GB][D / 64]) {
   constexpr int DL = D / 64;
-  const int jd = lane * DL;
-  const uint32_t vmw = lane < sg.T ? *(const uint32_t*)(pg + sg.vm + 4 * lane) : 0u;
-  for (int t0 = 0; t0 < nv; t0 += 8) {
-    uint32_t cw[8];
+  const uint32_t mask = (1u << vb) - 1u;
+  const int sh = (lane * DL * vb) & 7;  // the lane's first code within its byte
 #pragma unroll
-    for (int k = 0; k < 8; k++) {
-      const int t = min(t0 + k, nv - 1);
-      const int bit = (t * D + jd) * VB;
-      if constexpr (DL * VB <= 8) cw[k] = (uint32_t)pg[sg.vc + (bit >> 3)] >> (bit & 7);
-      else cw[k] = *(const uint16_t*)(pg + sg.vc + (bit >> 3));  // two 8-bit codes, 2-byte aligned
-    }
+  for (int t = 0; t < T; t++) {
+    if (t < nv) {  // uniform
+      float c[DL];
 #pragma unroll
-    for (int k = 0; k < 8; k++) {
-      const int t = t0 + k;
-      if (t < nv) {  // uniform
-        const uint32_t m = __builtin_amdgcn_readlane(vmw, t);
-        const float s = h2f((uint16_t)(m & 0xFFFFu)), z = h2f((uint16_t)(m >> 16));
-        float v[DL];
+      for (int e = 0; e < DL; e++) c[e] = (float)((cw[t] >> (sh + e * vb)) & mask);
+      const float4* pv = (const float4*)(pw + t * 16);
 #pragma unroll
-        for (int e = 0; e < DL; e++) v[e] = dequant(s, z, (cw[k] >> (e * VB)) & ((1u << VB) - 1u));
+      for (int g4 = 0; g4 < GB / 4; g4++) {
+        const float4 p4 = pv[g4];
 #pragma unroll
-        for (int g = 0; g < GB; g++) {
-          const float p = pw[t * 16 + g];
-#pragma unroll
-          for (int e = 0; e < DL; e++) o[g][e] = __builtin_fmaf(p, v[e], o[g][e]);
+        for (int e = 0; e < DL; e++) {
+          o[4 * g4 + 0][e] = __builtin_fmaf(p4.x, c[e], o[4 * g4 + 0][e]);
+          o[4 * g4 + 1][e] = __builtin_fmaf(p4.y, c[e], o[4 * g4 + 1][e]);
+          o[4 * g4 + 2][e] = __builtin_fmaf(p4.z, c[e], o[4 * g4 + 2][e]);
+          o[4 * g4 + 3][e] = __builtin_fmaf(p4.w, c[e], o[4 * g4 + 3][e]);
         }
       }
     }
   }
-}
-
-template <int D, int GB>
-__device__ inline void plain_pv_any(int vb, const uint8_t* pg, const Seg& sg, int lane, int nv, const float* pw,
-                                    float (&o)[GB][D / 64]) {
-  if (vb == 8) plain_pv<D, 8, GB>(pg, sg, lane, nv, pw, o);
-  else if (vb == 4) plain_pv<D, 4, GB>(pg, sg, lane, nv, pw, o);
-  else if (vb == 2) plain_pv<D, 2, GB>(pg, sg, lane, nv, pw, o);
-  else plain_pv<D, 1, GB>(pg, sg, lane, nv, pw, o);
 }
 
 // LDS operations of one wave complete in program order; this keeps the
@@ -184,6 +226,41 @@ __device__ inline void wave_lds_order() {
 }
 
 }  // namespace
+
+// One page of one wave from its loaded words: QK, the online softmax update
+// of (m, l, o, zs) and PV.  lg: where the page's logits go (slot t of head g
+// at lg[g LS + t]), or null.  zs: this lane's share of sum_t p z_v per head
+// (lanes below T).
+template <int D, int T, int GB>
+__device__ inline void plain_page(const PageLd<D>& r, const Seg& sg, int lane, int nv, int G, int64_t LS, float* lg,
+                                  const float* qs, const float* qsum, float scale_log2, float* pw, float (&m)[GB],
+                                  float (&l)[GB], float (&o)[GB][D / 64], float (&zs)[GB]) {
+  constexpr int DL = D / 64;
+  float x[GB];
+  plain_qk_any<D, T, GB>(sg.kbits, r, lane, qs, qsum, x);
+  const int t = lane % T;
+  const bool first = lane < T, live = t < nv;
+  const float sv = h2f((uint16_t)(r.vmw & 0xFFFFu)), zv = h2f((uint16_t)(r.vmw >> 16));
+#pragma unroll
+  for (int g = 0; g < GB; g++) x[g] = live ? x[g] * scale_log2 : -INFINITY;
+  if (lg && first && live)
+    for (int g = 0; g < G; g++) lg[g * LS + t] = x[g];
+  wave_lds_order();  // the previous page's weights have been read
+#pragma unroll
+  for (int g = 0; g < GB; g++) {
+    const float mn = fmaxf(m[g], wave_max(x[g]));  // finite: nv >= 1
+    const float al = __builtin_amdgcn_exp2f(m[g] - mn);
+    const float p = (first && live) ? __builtin_amdgcn_exp2f(x[g] - mn) : 0.0f;
+    l[g] = l[g] * al + wave_sum(p);
+#pragma unroll
+    for (int e = 0; e < DL; e++) o[g][e] *= al;
+    zs[g] = __builtin_fmaf(p, zv, zs[g] * al);
+    m[g] = mn;
+    if (first) pw[t * 16 + g] = p * sv;
+  }
+  wave_lds_order();
+  plain_pv<D, T, GB>(sg.vbits, r.cw, nv, lane, pw, o);
+}
 
 template <int D, int GB>
 __global__ __launch_bounds__(kPThreads) void plain_attn_kernel(int H, int G, int L, int S, int64_t P, int page_bytes,
@@ -199,9 +276,11 @@ __global__ __launch_bounds__(kPThreads) void plain_attn_kernel(int H, int G, int
   const int split = blockIdx.x;
   const int64_t u = blockIdx.y;
   const int b = (int)u / H, h = (int)u % H;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  __shared__ float qs[GB * D];
-  __shared__ float ps[kPWaves][32 * 16];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: page choice and loads in scalar registers
+  __shared__ __align__(16) float qs[D * GB];  // [d][GB]
+  __shared__ float qsum[GB];
+  __shared__ __align__(16) float ps[kPWaves][32 * 16];
   __shared__ float sml[kPWaves][GB][2];
   __shared__ float ob[kPWaves][GB * D];
   const int N = seq_len[b];
@@ -217,57 +296,79 @@ __global__ __launch_bounds__(kPThreads) void plain_attn_kernel(int H, int G, int
   const int TPg = sok ? ph + pl : 0;
   const int pps = split_pages(TPg, S);
   const int p0 = split * pps, p1 = min(TPg, p0 + pps);
-  // the group's q heads (fp32; rows G..GB-1 zero)
+  // the group's q heads (fp32, [d][GB]; heads G..GB-1 zero) and their sums
   const uint16_t* qb = q + ((int64_t)b * H * G + (int64_t)h * G) * D;
-  for (int x = tid; x < GB * D; x += kPThreads) qs[x] = x < G * D ? h2f(qb[x]) : 0.0f;
+  for (int x = tid; x < GB * D; x += kPThreads) {
+    const int g = x / D, j = x % D;
+    qs[j * GB + g] = g < G ? h2f(qb[x]) : 0.0f;
+  }
   __syncthreads();
-  float m[GB], l[GB], o[GB][DL];
+  if (tid < GB) {
+    float a = 0.0f;
+    for (int j = 0; j < D; j++) a += qs[j * GB + tid];
+    qsum[tid] = a;
+  }
+  __syncthreads();
+  float m[GB], l[GB], o[GB][DL], zs[GB];
 #pragma unroll
   for (int g = 0; g < GB; g++) {
     m[g] = -INFINITY;
     l[g] = 0.0f;
+    zs[g] = 0.0f;
 #pragma unroll
     for (int e = 0; e < DL; e++) o[g][e] = 0.0f;
   }
   bool bad = false;
   float* pw = ps[wid];
   const int64_t LS = (int64_t)32 * L;
-  for (int j = p0 + wid; j < p1; j += kPWaves) {
-    const bool hi = j < ph;
-    const int jt = hi ? j : j - ph;
-    const int32_t id = table[u * L + (hi ? jt : L - 1 - jt)];
-    if (id < 0 || id >= P) {
-      bad = true;
-      continue;
-    }
-    const uint8_t* pg = pages + (int64_t)id * page_bytes;
-    const Seg& sg = lay.seg(hi);
-    const int T = sg.T;
+  // The wave's pages j = p0 + wid + 8k.  Software pipeline: the table id two
+  // pages ahead and every load of the next page are issued before the
+  // current page is computed.
+  auto id_of = [&](int jj) {
+    const bool hi = jj < ph;
+    const int jt = hi ? jj : jj - ph;
+    return table[u * L + (hi ? jt : L - 1 - jt)];
+  };
+  auto ok_id = [&](int32_t id) { return id >= 0 && id < P; };
+  auto load = [&](int jj, int32_t id, PageLd<D>& r) {
+    const bool hi = jj < ph;
+    const int jt = hi ? jj : jj - ph;
     const int nv = hi ? min(kHiTokens, nh - kHiTokens * jt) : min(kLoTokens, nl - kLoTokens * jt);
-    const int slot0 = hi ? kHiTokens * jt : nh + kLoTokens * jt;
-    float x[GB];
-    if (hi) plain_qk_any<D, kHiTokens, GB>(sg.kbits, pg, sg, lane, qs, x);
-    else plain_qk_any<D, kLoTokens, GB>(sg.kbits, pg, sg, lane, qs, x);
-    const int t = lane % T;
-    const bool first = lane < T, live = t < nv;
-#pragma unroll
-    for (int g = 0; g < GB; g++) x[g] = live ? x[g] * scale_log2 : -INFINITY;
-    if (keep_logits && first && live)
-      for (int g = 0; g < G; g++) logits[(u * G + g) * LS + slot0 + t] = x[g];
-    wave_lds_order();  // the previous page's weights have been read
-#pragma unroll
-    for (int g = 0; g < GB; g++) {
-      const float mn = fmaxf(m[g], wave_max(x[g]));  // finite: nv >= 1
-      const float al = __builtin_amdgcn_exp2f(m[g] - mn);
-      const float p = live ? __builtin_amdgcn_exp2f(x[g] - mn) : 0.0f;
-      l[g] = l[g] * al + wave_sum(first ? p : 0.0f);
-#pragma unroll
-      for (int e = 0; e < DL; e++) o[g][e] *= al;
-      m[g] = mn;
-      if (first) pw[t * 16 + g] = p;
+    const uint8_t* pg = pages + (int64_t)id * page_bytes;
+    if (hi) plain_load<D, kHiTokens>(pg, lay.seg(true), lane, nv, r);
+    else plain_load<D, kLoTokens>(pg, lay.seg(false), lane, nv, r);
+  };
+  int j = p0 + wid;
+  int32_t id_cur = j < p1 ? id_of(j) : -1;
+  int32_t id_nx = j + kPWaves < p1 ? id_of(j + kPWaves) : -1;
+  PageLd<D> cur;
+  if (j < p1 && ok_id(id_cur)) load(j, id_cur, cur);
+  for (; j < p1; j += kPWaves) {
+    const int jn = j + kPWaves;
+    const int32_t id_n = id_nx;
+    id_nx = jn + kPWaves < p1 ? id_of(jn + kPWaves) : -1;
+    PageLd<D> nxt;
+    if (jn < p1 && ok_id(id_n)) load(jn, id_n, nxt);
+    if (!ok_id(id_cur)) {
+      bad = true;
+    } else {
+      const bool hi = j < ph;
+      const int jt = hi ? j : j - ph;
+      const int nv = hi ? min(kHiTokens, nh - kHiTokens * jt) : min(kLoTokens, nl - kLoTokens * jt);
+      const int slot0 = hi ? kHiTokens * jt : nh + kLoTokens * jt;
+      float* lg = keep_logits ? logits + u * G * LS + slot0 : nullptr;
+      if (hi) plain_page<D, kHiTokens, GB>(cur, lay.seg(true), lane, nv, G, LS, lg, qs, qsum, scale_log2, pw, m, l, o, zs);
+      else plain_page<D, kLoTokens, GB>(cur, lay.seg(false), lane, nv, G, LS, lg, qs, qsum, scale_log2, pw, m, l, o, zs);
     }
-    wave_lds_order();
-    plain_pv_any<D, GB>(sg.vbits, pg, sg, lane, nv, pw, o);
+    cur = nxt;
+    id_cur = id_n;
+  }
+  // the z_v part of every dim: the wave's sum of p z_v
+#pragma unroll
+  for (int g = 0; g < GB; g++) {
+    const float zt = wave_sum(zs[g]);
+#pragma unroll
+    for (int e = 0; e < DL; e++) o[g][e] += zt;
   }
   // the waves' partials, merged in a fixed order
   if (lane == 0)
