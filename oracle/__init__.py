@@ -46,7 +46,9 @@ class Cfg(ctypes.Structure):
                 ("prompt_rule", ctypes.c_int32), ("alpha_h_head", ctypes.c_void_p),
                 ("alpha_l_head", ctypes.c_void_p),
                 ("hi_k_bits", ctypes.c_int32), ("hi_v_bits", ctypes.c_int32),
-                ("lo_k_bits", ctypes.c_int32), ("lo_v_bits", ctypes.c_int32)]
+                ("lo_k_bits", ctypes.c_int32), ("lo_v_bits", ctypes.c_int32),
+                ("num_levels", ctypes.c_int32), ("alpha_mid", ctypes.c_float * 2),
+                ("mid_k_bits", ctypes.c_int32 * 2), ("mid_v_bits", ctypes.c_int32 * 2)]
 
 
 RULE_ALPHA_N, RULE_ALPHA_I = 0, 1
@@ -76,13 +78,18 @@ def lib() -> ctypes.CDLL:
         _lib.orc_page_bytes.restype = ctypes.c_int32
         _lib.orc_table_len.restype = ctypes.c_int32
         _lib.orc_tier_layout.restype = ctypes.c_int32
+        _lib.orc_level_layout.restype = ctypes.c_int32
+        _lib.orc_num_levels.restype = ctypes.c_int32
+        _lib.orc_state_words.restype = ctypes.c_int32
     return _lib
 
 
 def make_cfg(c: dict) -> Cfg:
     """Config dict -> orc_cfg.  Optional keys: prompt_rule (RULE_ALPHA_N or
     RULE_ALPHA_I), alpha_h_head / alpha_l_head (H thresholds each),
-    hi_k_bits / hi_v_bits / lo_k_bits / lo_v_bits (tier codecs)."""
+    hi_k_bits / hi_v_bits / lo_k_bits / lo_v_bits (tier codecs), num_levels
+    (3 or 4 precision levels) with alpha_mid / mid_k_bits / mid_v_bits (one
+    value per middle level)."""
     r = Cfg(int(c["head_dim"]), int(c["num_kv_heads"]), int(c["gqa_group"]),
             int(c.get("hi_page_tokens", 16)), int(c.get("lo_page_tokens", 32)),
             int(c["max_seq_len"]), int(c["window"]), int(c.get("lo_enabled", 1)),
@@ -101,6 +108,12 @@ def make_cfg(c: dict) -> Cfg:
     # tier codecs (bits of K and V codes per tier; absent: K8V4 / K4V2)
     for key in ("hi_k_bits", "hi_v_bits", "lo_k_bits", "lo_v_bits"):
         setattr(r, key, int(c.get(key, 0)))
+    r.num_levels = int(c.get("num_levels", 0))
+    for key, conv in (("alpha_mid", float), ("mid_k_bits", int), ("mid_v_bits", int)):
+        vals = list(c.get(key, ()))
+        arr = getattr(r, key)
+        for i in range(2):
+            arr[i] = conv(vals[i]) if i < len(vals) else conv(0)
     return r
 
 
@@ -120,6 +133,20 @@ def page_bytes(cfg: dict) -> int:
 
 def table_len(cfg: dict) -> int:
     return lib().orc_table_len(ctypes.byref(make_cfg(cfg)))
+
+
+def num_levels(cfg: dict) -> int:
+    return lib().orc_num_levels(ctypes.byref(make_cfg(cfg)))
+
+
+def state_words(cfg: dict) -> int:
+    return lib().orc_state_words(ctypes.byref(make_cfg(cfg)))
+
+
+def level_layout(cfg: dict, level: int):
+    seg = np.zeros(7, np.int32)
+    T = lib().orc_level_layout(ctypes.byref(make_cfg(cfg)), level, _p(seg))
+    return T, seg
 
 
 def tier_layout(cfg: dict, tier: int):
@@ -167,15 +194,18 @@ def dequant(s16: int, z16: int, code: int) -> float:
     return lib().orc_dequant(s16, z16, code)
 
 
-def classify(cfg: dict, cu_seqlens, scores):
+def classify(cfg: dict, cu_seqlens, scores, levels_impl: bool = False):
+    """Tier codes [H, total] (K - level, 0 pruned; two tiers: HI, LO, PRUNE)
+    and counts [batch, H, K].  levels_impl: the K-level implementation even
+    for two tiers."""
     cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
     sc = np.ascontiguousarray(scores, dtype=np.float32)
     B = cu.size - 1
     H = int(cfg["num_kv_heads"])
     tiers = np.zeros(sc.shape, np.uint8)
-    counts = np.zeros((B, H, 2), np.int32)
-    _check(lib().orc_classify(ctypes.byref(make_cfg(cfg)), ctypes.c_int32(B), _p(cu), _p(sc),
-                              _p(tiers), _p(counts)))
+    counts = np.zeros((B, H, max(num_levels(cfg), 2)), np.int32)
+    fn = lib().orc_levels_classify if levels_impl else lib().orc_classify
+    _check(fn(ctypes.byref(make_cfg(cfg)), ctypes.c_int32(B), _p(cu), _p(sc), _p(tiers), _p(counts)))
     return tiers, counts
 
 
@@ -193,8 +223,9 @@ class State:
         self.free_list = np.zeros(self.num_pages, np.int32)
         self.ptr = np.zeros(2, np.uint64)
         self.status = np.zeros(1, np.uint32)
+        self.K = max(num_levels(cfg), 2)
         self.page_table = np.full((batch, H, self.L), -1, np.int32)
-        self.tier_state = np.zeros((batch, H, 4), np.int32)
+        self.tier_state = np.zeros((batch, H, 2 * self.K), np.int32)
         if init_pages:
             _check(lib().orc_pool_init(ctypes.byref(self._pool())))
 
@@ -210,48 +241,57 @@ class State:
         return s
 
     # -- operations -----------------------------------------------------
-    def compact_prompt(self, cu_seqlens, k, v, scores, tiers):
+    # levels_impl=True runs the K-level implementation even for two tiers
+    # (the two must agree there).
+    def compact_prompt(self, cu_seqlens, k, v, scores, tiers, levels_impl: bool = False):
         cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
         k = np.ascontiguousarray(k, dtype=np.uint16)
         v = np.ascontiguousarray(v, dtype=np.uint16)
         sc = np.ascontiguousarray(scores, dtype=np.float32)
         ti = np.ascontiguousarray(tiers, dtype=np.uint8)
         pool = self._pool()
-        _check(lib().orc_compact_prompt(ctypes.byref(make_cfg(self.cfg)), ctypes.byref(pool),
-                                        ctypes.c_int32(cu.size - 1), _p(cu), _p(k), _p(v), _p(sc),
-                                        _p(ti), _p(self.page_table), _p(self.tier_state)))
+        fn = lib().orc_levels_compact_prompt if levels_impl else lib().orc_compact_prompt
+        _check(fn(ctypes.byref(make_cfg(self.cfg)), ctypes.byref(pool), ctypes.c_int32(cu.size - 1), _p(cu),
+                  _p(k), _p(v), _p(sc), _p(ti), _p(self.page_table), _p(self.tier_state)))
 
-    def compact_step(self, seq_len, k_new, v_new, branches: bool = False):
+    def compact_step(self, seq_len, k_new, v_new, branches: bool = False, levels_impl: bool = False):
         """One generation step; with branches=True returns int32 [batch, H]:
-        the policy case per unit (BR_*, bits 0-3) and the new page's tier
-        (bits 4-5)."""
+        two tiers, the policy case per unit (BR_*, bits 0-3) and the new
+        page's tier (bits 4-5); K levels (or levels_impl), t_c's class in
+        bits 0-3 (level, 14 pruned, 15 none), the victim's in bits 4-7 and
+        the new page's level + 1 in bits 8-11 (-1 inactive)."""
         sl = np.ascontiguousarray(seq_len, dtype=np.int32)
         k = np.ascontiguousarray(k_new, dtype=np.uint16)
         v = np.ascontiguousarray(v_new, dtype=np.uint16)
         pool = self._pool()
         br = np.zeros((self.batch, int(self.cfg["num_kv_heads"])), np.int32)
-        _check(lib().orc_compact_step_branches(ctypes.byref(make_cfg(self.cfg)), ctypes.byref(pool),
-                                               ctypes.c_int32(self.batch), _p(sl), _p(k), _p(v),
-                                               _p(self.page_table), _p(self.tier_state), _p(br)))
+        if levels_impl:
+            _check(lib().orc_levels_compact_step(ctypes.byref(make_cfg(self.cfg)), ctypes.byref(pool),
+                                                 ctypes.c_int32(self.batch), _p(sl), _p(k), _p(v),
+                                                 _p(self.page_table), _p(self.tier_state), _p(br)))
+        else:
+            _check(lib().orc_compact_step_branches(ctypes.byref(make_cfg(self.cfg)), ctypes.byref(pool),
+                                                   ctypes.c_int32(self.batch), _p(sl), _p(k), _p(v),
+                                                   _p(self.page_table), _p(self.tier_state), _p(br)))
         return br if branches else None
 
-    def release(self, mask):
+    def release(self, mask, levels_impl: bool = False):
         m = np.ascontiguousarray(mask, dtype=np.uint8)
         pool = self._pool()
-        _check(lib().orc_release(ctypes.byref(make_cfg(self.cfg)), ctypes.byref(pool),
-                                 ctypes.c_int32(self.batch), _p(m), _p(self.page_table),
-                                 _p(self.tier_state)))
+        fn = lib().orc_levels_release if levels_impl else lib().orc_release
+        _check(fn(ctypes.byref(make_cfg(self.cfg)), ctypes.byref(pool), ctypes.c_int32(self.batch), _p(m),
+                  _p(self.page_table), _p(self.tier_state)))
 
-    def decode_attn(self, q, seq_len, update_scores: bool = False) -> np.ndarray:
+    def decode_attn(self, q, seq_len, update_scores: bool = False, levels_impl: bool = False) -> np.ndarray:
         qq = np.ascontiguousarray(q, dtype=np.uint16)
         sl = np.ascontiguousarray(seq_len, dtype=np.int32)
         H, G, d = int(self.cfg["num_kv_heads"]), int(self.cfg["gqa_group"]), int(self.cfg["head_dim"])
         out = np.zeros((self.batch, H * G, d), np.float32)
         pool = self._pool()
-        _check(lib().orc_decode_attn(ctypes.byref(make_cfg(self.cfg)), ctypes.byref(pool),
-                                     ctypes.c_int32(self.batch), _p(qq), _p(self.page_table),
-                                     _p(self.tier_state), _p(sl), _p(out),
-                                     ctypes.c_int32(1 if update_scores else 0)))
+        fn = lib().orc_levels_decode_attn if levels_impl else lib().orc_decode_attn
+        _check(fn(ctypes.byref(make_cfg(self.cfg)), ctypes.byref(pool), ctypes.c_int32(self.batch), _p(qq),
+                  _p(self.page_table), _p(self.tier_state), _p(sl), _p(out),
+                  ctypes.c_int32(1 if update_scores else 0)))
         return out
 
     def page_bounds(self) -> np.ndarray:
@@ -290,8 +330,37 @@ class State:
                             ctypes.byref(sc), ctypes.byref(pos))
         return dict(k=kc, v=vc, kmeta=km, vmeta=vm, score=sc.value, pos=pos.value)
 
+    def read_level_slot(self, page_id: int, level: int, slot: int):
+        d = int(self.cfg["head_dim"])
+        kc = np.zeros(d, np.uint8)
+        vc = np.zeros(d, np.uint8)
+        km = np.zeros(2, np.uint16)
+        vm = np.zeros(2, np.uint16)
+        sc = ctypes.c_float()
+        pos = ctypes.c_int32()
+        page = np.ascontiguousarray(self.pages[page_id])
+        lib().orc_read_level_slot(ctypes.byref(make_cfg(self.cfg)), _p(page), ctypes.c_int32(level),
+                                  ctypes.c_int32(slot), _p(kc), _p(vc), _p(km), _p(vm),
+                                  ctypes.byref(sc), ctypes.byref(pos))
+        return dict(k=kc, v=vc, kmeta=km, vmeta=vm, score=sc.value, pos=pos.value)
+
+    def level_page(self, b: int, h: int, level: int, j: int) -> int:
+        """Page id of page j of a level (row level // 2: even levels from the
+        left, odd levels from the right)."""
+        Lr = self.L // ((self.K + 1) // 2)
+        col = j if level % 2 == 0 else Lr - 1 - j
+        return int(self.page_table[b, h, (level // 2) * Lr + col])
+
     def unit_tokens(self, b: int, h: int):
-        """List of (tier, slot, slot-record) of one unit's retained tokens."""
+        """List of (tier, slot, slot-record) of one unit's retained tokens
+        (K levels: (level, slot, record))."""
+        if self.K >= 3:
+            out = []
+            for lv in range(self.K):
+                T = 16 if lv == 0 else 32
+                for s in range(int(self.tier_state[b, h, lv])):
+                    out.append((lv, s, self.read_level_slot(self.level_page(b, h, lv, s // T), lv, s % T)))
+            return out
         n_hi, n_lo, ph, pl = (int(x) for x in self.tier_state[b, h])
         row = self.page_table[b, h]
         out = []

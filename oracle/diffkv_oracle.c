@@ -58,8 +58,11 @@ static int codec_plain(const orc_cfg* c) {
 
 static int bits_ok(int32_t b) { return b == 1 || b == 2 || b == 4 || b == 8; }
 
+static int levels_valid(const orc_cfg* c);
+
 static int cfg_valid(const orc_cfg* c) {
   if (!c) return 0;
+  if (!levels_valid(c)) return 0;
   if (codec_plain(c) && !(bits_ok(c->hi_k_bits) && bits_ok(c->hi_v_bits) && bits_ok(c->lo_k_bits) &&
                           bits_ok(c->lo_v_bits)))
     return 0;
@@ -92,10 +95,19 @@ static double alpha_lo(const orc_cfg* c, int32_t h) {
   return (double)(c->alpha_l_head ? c->alpha_l_head[h] : c->alpha_l);
 }
 
-int32_t orc_table_len(const orc_cfg* c) {
+/* Entries of one table row ("Memory management": the row length is the
+ * maximum sequence length over the high tier's tokens per page). */
+static int32_t row_len(const orc_cfg* c) {
   /* The page says a row of S_max / T_h entries cannot overflow; one more is
    * needed (hi and lo pages together can exceed ceil(N/T_h) by one). */
   return (int32_t)cdiv64(c->max_seq_len, c->hi_page_tokens) + 1;
+}
+
+static int32_t num_levels(const orc_cfg* c) { return c->num_levels >= 3 ? c->num_levels : 2; }
+
+int32_t orc_table_len(const orc_cfg* c) {
+  /* one row per pair of levels (two tiers: one row) */
+  return (num_levels(c) + 1) / 2 * row_len(c);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -128,6 +140,14 @@ int32_t orc_tier_layout(const orc_cfg* c, int32_t tier, int32_t seg[7]) {
 
 int32_t orc_page_bytes(const orc_cfg* c) {
   if (!cfg_valid(c)) return -1;
+  if (num_levels(c) >= 3) {
+    int32_t best = 0, seg[7];
+    for (int32_t l = 0; l < num_levels(c); l++) {
+      orc_level_layout(c, l, seg);
+      if (seg[6] > best) best = seg[6];
+    }
+    return best;
+  }
   int32_t a[7], b[7];
   orc_tier_layout(c, ORC_HI, a);
   orc_tier_layout(c, ORC_LO, b);
@@ -399,6 +419,7 @@ static int cu_valid(int32_t batch, const int64_t* cu) {
 int orc_classify(const orc_cfg* c, int32_t batch, const int64_t* cu,
                  const float* scores, uint8_t* tiers, int32_t* counts) {
   if (!cfg_valid(c) || !cu_valid(batch, cu)) return ORC_E_INVALID;
+  if (num_levels(c) >= 3) return orc_levels_classify(c, batch, cu, scores, tiers, counts);
   int32_t H = c->num_kv_heads;
   int64_t total = cu[batch];
   for (int32_t r = 0; r < batch; r++) {
@@ -564,6 +585,7 @@ int orc_compact_prompt(const orc_cfg* c, orc_pool* p, int32_t batch,
                        int32_t* table, int32_t* state) {
   if (!cfg_valid(c) || !p || !cu_valid(batch, cu)) return ORC_E_INVALID;
   if (p->page_bytes != orc_page_bytes(c)) return ORC_E_INVALID;
+  if (num_levels(c) >= 3) return orc_levels_compact_prompt(c, p, batch, cu, k, v, scores, tiers, table, state);
   int32_t H = c->num_kv_heads, d = c->head_dim, L = orc_table_len(c);
   int32_t Th = c->hi_page_tokens, Tl = c->lo_page_tokens;
   int64_t total = cu[batch];
@@ -842,6 +864,7 @@ static int compact_step_impl(const orc_cfg* c, orc_pool* p, int32_t batch,
 int orc_compact_step(const orc_cfg* c, orc_pool* p, int32_t batch,
                      const int32_t* seq_len, const uint16_t* k_new,
                      const uint16_t* v_new, int32_t* table, int32_t* state) {
+  if (c && num_levels(c) >= 3) return orc_levels_compact_step(c, p, batch, seq_len, k_new, v_new, table, state, NULL);
   return compact_step_impl(c, p, batch, seq_len, k_new, v_new, table, state, NULL);
 }
 
@@ -849,6 +872,7 @@ int orc_compact_step_branches(const orc_cfg* c, orc_pool* p, int32_t batch,
                               const int32_t* seq_len, const uint16_t* k_new,
                               const uint16_t* v_new, int32_t* table, int32_t* state,
                               int32_t* branch) {
+  if (c && num_levels(c) >= 3) return orc_levels_compact_step(c, p, batch, seq_len, k_new, v_new, table, state, branch);
   if (branch)
     for (int64_t u = 0; u < (int64_t)batch * (c ? c->num_kv_heads : 0); u++) branch[u] = ORC_BR_INACTIVE;
   return compact_step_impl(c, p, batch, seq_len, k_new, v_new, table, state, branch);
@@ -862,6 +886,7 @@ int orc_compact_step_branches(const orc_cfg* c, orc_pool* p, int32_t batch,
 int orc_release(const orc_cfg* c, orc_pool* p, int32_t batch, const uint8_t* mask,
                 int32_t* table, int32_t* state) {
   if (!cfg_valid(c) || !p || batch < 0) return ORC_E_INVALID;
+  if (num_levels(c) >= 3) return orc_levels_release(c, p, batch, mask, table, state);
   int32_t H = c->num_kv_heads, L = orc_table_len(c);
   int64_t U = (int64_t)batch * H, total = 0;
   uint32_t st = 0;
@@ -959,6 +984,7 @@ int orc_decode_attn(const orc_cfg* c, orc_pool* p, int32_t batch, const uint16_t
                     float* out, int32_t update_scores) {
   if (!cfg_valid(c) || !p || batch < 0) return ORC_E_INVALID;
   if (p->page_bytes != orc_page_bytes(c)) return ORC_E_INVALID;
+  if (num_levels(c) >= 3) return orc_levels_decode_attn(c, p, batch, q, table, state, seq_len, out, update_scores);
   int32_t H = c->num_kv_heads, G = c->gqa_group, d = c->head_dim, L = orc_table_len(c);
   int32_t Th = c->hi_page_tokens, Tl = c->lo_page_tokens;
   memset(out, 0, sizeof(float) * (size_t)batch * H * G * d);
@@ -1239,7 +1265,7 @@ int orc_keydiff_scores(const orc_cfg* c, int32_t batch, const int64_t* cu, const
  * (other pages untouched). */
 int orc_page_bounds(const orc_cfg* c, orc_pool* p, int32_t batch, const int32_t* table,
                     const int32_t* state, float* bounds) {
-  if (!cfg_valid(c) || !p || batch < 0) return ORC_E_INVALID;
+  if (!cfg_valid(c) || !p || batch < 0 || num_levels(c) >= 3) return ORC_E_INVALID;
   int32_t H = c->num_kv_heads, d = c->head_dim, L = orc_table_len(c);
   int32_t Th = c->hi_page_tokens, Tl = c->lo_page_tokens;
   for (int64_t u = 0; u < (int64_t)batch * H; u++) {
@@ -1280,7 +1306,7 @@ int orc_page_bounds(const orc_cfg* c, orc_pool* p, int32_t batch, const int32_t*
 int orc_page_scores(const orc_cfg* c, int32_t batch, const uint16_t* q, const int32_t* table,
                     const int32_t* state, const int32_t* seq_len, const float* bounds,
                     int64_t num_pages, float* scores) {
-  if (!cfg_valid(c) || batch < 0) return ORC_E_INVALID;
+  if (!cfg_valid(c) || batch < 0 || num_levels(c) >= 3) return ORC_E_INVALID;
   int32_t H = c->num_kv_heads, G = c->gqa_group, d = c->head_dim, L = orc_table_len(c);
   for (int64_t u = 0; u < (int64_t)batch * H; u++) {
     int32_t b = (int32_t)(u / H), h = (int32_t)(u % H);
@@ -1309,5 +1335,704 @@ int orc_page_scores(const orc_cfg* c, int32_t batch, const uint16_t* q, const in
       out[t] = (float)best;
     }
   }
+  return ORC_OK;
+}
+
+/* ======================================================================== */
+/* More than two precision levels ("KV compression policy", extensibility
+ * paragraph: the policy allows more than two quantization levels; "Memory
+ * management", generation workflow: extra levels are supported by combining
+ * unidirectional or bidirectional page tables).                           */
+/*                                                                          */
+/* Readings (the pages name the extension but do not spell it out):         */
+/*  - K levels 0 (most precise) .. K-1; thresholds alpha_0 = alpha_h >=     */
+/*    alpha_1 >= .. >= alpha_{K-1} = alpha_l; a token is in the first level */
+/*    l < K-1 with mean * N > alpha_l, else in level K-1 if mean * N >=     */
+/*    alpha_{K-1}, else pruned (K = 2: the two-tier rule).  The window is   */
+/*    level 0.                                                               */
+/*  - level 0 holds T_h tokens per page, the others T_l;                     */
+/*  - table row r holds level 2r from the left and level 2r+1 from the       */
+/*    right (a bidirectional row; with K = 3 row 1 holds level 2 alone, a   */
+/*    unidirectional row); every row has the two-tier row length;            */
+/*  - prompt allocation generalizes Fig 6: the conservative block of         */
+/*    ceil(N/T_h) pages feeds levels 0, 2, 3 (in that order) from its left  */
+/*    end and level 1 from its right end; the middle returns to the list;   */
+/*    pages the block lacks come after the frees, in the order levels 0, 2, */
+/*    3, then level 1 innermost first (two tiers: the extra low page);      */
+/*  - generation step: t_c's level l_c; l_c = 0: the least important        */
+/*    non-window level-0 token (t_c included) moves to its own class's      */
+/*    level or is pruned; l_c >= 1: t_c moves to level l_c and the least    */
+/*    important token of level l_c (t_c included) moves down to its class's */
+/*    level or is pruned when its class is below l_c; a removal and an      */
+/*    insertion in one level share the slot, otherwise the insertion        */
+/*    appends (one new page at most, never a free);                        */
+/*  - release: row by row, the left level's pages left to right, then the   */
+/*    right level's pages right to left.                                    */
+/* ======================================================================== */
+
+static int levels_valid(const orc_cfg* c) {
+  if (c->num_levels == 0 || c->num_levels == 2) return 1;
+  if (c->num_levels != 3 && c->num_levels != 4) return 0;
+  int32_t K = c->num_levels;
+  if (!c->lo_enabled) return 0;
+  if (!(bits_ok(c->hi_k_bits) && bits_ok(c->hi_v_bits) && bits_ok(c->lo_k_bits) && bits_ok(c->lo_v_bits)))
+    return 0;
+  for (int32_t m = 0; m < K - 2; m++) {
+    if (!bits_ok(c->mid_k_bits[m]) || !bits_ok(c->mid_v_bits[m])) return 0;
+    if (!(c->alpha_mid[m] >= 0.0f)) return 0;
+  }
+  /* thresholds descend with the level, for the shared pair and every head */
+  for (int32_t h = -1; h < (c->alpha_h_head ? c->num_kv_heads : 0); h++) {
+    float prev = h < 0 ? c->alpha_h : c->alpha_h_head[h];
+    for (int32_t m = 0; m < K - 2; m++) {
+      if (c->alpha_mid[m] > prev) return 0;
+      prev = c->alpha_mid[m];
+    }
+    if ((h < 0 ? c->alpha_l : c->alpha_l_head[h]) > prev) return 0;
+  }
+  return 1;
+}
+
+int32_t orc_num_levels(const orc_cfg* c) { return cfg_valid(c) ? num_levels(c) : -1; }
+int32_t orc_state_words(const orc_cfg* c) { return cfg_valid(c) ? 2 * num_levels(c) : -1; }
+
+static int32_t level_tokens(const orc_cfg* c, int32_t l) { return l == 0 ? c->hi_page_tokens : c->lo_page_tokens; }
+
+static void level_bits(const orc_cfg* c, int32_t l, int32_t* kb, int32_t* vb) {
+  int32_t K = num_levels(c);
+  if (K == 2) {
+    tier_bits(c, l == 0 ? ORC_HI : ORC_LO, kb, vb);
+  } else if (l == 0) {
+    *kb = c->hi_k_bits;
+    *vb = c->hi_v_bits;
+  } else if (l == K - 1) {
+    *kb = c->lo_k_bits;
+    *vb = c->lo_v_bits;
+  } else {
+    *kb = c->mid_k_bits[l - 1];
+    *vb = c->mid_v_bits[l - 1];
+  }
+}
+
+static double level_alpha(const orc_cfg* c, int32_t h, int32_t l) {
+  int32_t K = num_levels(c);
+  if (l == 0) return alpha_hi(c, h);
+  if (l == K - 1) return alpha_lo(c, h);
+  return (double)c->alpha_mid[l - 1];
+}
+
+int32_t orc_level_layout(const orc_cfg* c, int32_t l, int32_t seg[7]) {
+  if (num_levels(c) == 2) return orc_tier_layout(c, l == 0 ? ORC_HI : ORC_LO, seg);
+  int32_t d = c->head_dim, T = level_tokens(c, l), kb, vb;
+  level_bits(c, l, &kb, &vb);
+  int32_t size[6] = {T * d * kb / 8, 4 * T, T * d * vb / 8, 4 * T, 4 * T, 4 * T};
+  int32_t off = 0;
+  for (int i = 0; i < 6; i++) {
+    seg[i] = off;
+    off += round16(size[i]);
+  }
+  seg[6] = off;
+  return T;
+}
+
+/* code (tok, j) of level l: the two tiers' own layouts, else plain */
+static void level_code_addr(const orc_cfg* c, int32_t l, int is_v, int32_t tok, int32_t j, int32_t* byte,
+                            int32_t* shift) {
+  if (num_levels(c) == 2) {
+    if (is_v) orc_v_code_addr(c, l == 0 ? ORC_HI : ORC_LO, tok, j, byte, shift);
+    else orc_k_code_addr(c, l == 0 ? ORC_HI : ORC_LO, tok, j, byte, shift);
+    return;
+  }
+  int32_t seg[7], kb, vb;
+  orc_level_layout(c, l, seg);
+  level_bits(c, l, &kb, &vb);
+  int64_t bit = ((int64_t)tok * c->head_dim + j) * (is_v ? vb : kb);
+  *byte = seg[is_v ? 2 : 0] + (int32_t)(bit / 8);
+  *shift = (int32_t)(bit % 8);
+}
+
+void orc_read_level_slot(const orc_cfg* c, const uint8_t* page, int32_t l, int32_t slot, uint8_t* kc,
+                         uint8_t* vc, uint16_t* km, uint16_t* vm, float* score, int32_t* pos) {
+  int32_t seg[7], kb, vb;
+  orc_level_layout(c, l, seg);
+  level_bits(c, l, &kb, &vb);
+  for (int32_t j = 0; j < c->head_dim; j++) {
+    int32_t byte, shift;
+    if (kc) {
+      level_code_addr(c, l, 0, slot, j, &byte, &shift);
+      kc[j] = (uint8_t)get_field(page, byte, shift, kb);
+    }
+    if (vc) {
+      level_code_addr(c, l, 1, slot, j, &byte, &shift);
+      vc[j] = (uint8_t)get_field(page, byte, shift, vb);
+    }
+  }
+  if (km) { km[0] = get_u16(page + seg[1] + 4 * slot); km[1] = get_u16(page + seg[1] + 4 * slot + 2); }
+  if (vm) { vm[0] = get_u16(page + seg[3] + 4 * slot); vm[1] = get_u16(page + seg[3] + 4 * slot + 2); }
+  if (score) *score = bits_f32(get_u32(page + seg[4] + 4 * slot));
+  if (pos) *pos = (int32_t)get_u32(page + seg[5] + 4 * slot);
+}
+
+/* Quantize one token (fp32 K and V) with level l's codec into its slot. */
+static void store_level_token(const orc_cfg* c, uint8_t* page, int32_t l, int32_t slot, const float* xk,
+                              const float* xv, float score, int32_t pos) {
+  int32_t seg[7], kb, vb;
+  orc_level_layout(c, l, seg);
+  level_bits(c, l, &kb, &vb);
+  uint8_t kc[128], vc[128];
+  uint16_t km[2], vm[2];
+  orc_quantize(xk, c->head_dim, kb, &km[0], &km[1], kc);
+  orc_quantize(xv, c->head_dim, vb, &vm[0], &vm[1], vc);
+  for (int32_t j = 0; j < c->head_dim; j++) {
+    int32_t byte, shift;
+    level_code_addr(c, l, 0, slot, j, &byte, &shift);
+    put_field(page, byte, shift, kb, kc[j]);
+    level_code_addr(c, l, 1, slot, j, &byte, &shift);
+    put_field(page, byte, shift, vb, vc[j]);
+  }
+  put_u16(page + seg[1] + 4 * slot, km[0]);
+  put_u16(page + seg[1] + 4 * slot + 2, km[1]);
+  put_u16(page + seg[3] + 4 * slot, vm[0]);
+  put_u16(page + seg[3] + 4 * slot + 2, vm[1]);
+  put_u32(page + seg[4] + 4 * slot, f32_bits(score));
+  put_u32(page + seg[5] + 4 * slot, (uint32_t)pos);
+}
+
+/* Table entry (index within the unit's R rows) of page j of level l. */
+static int64_t level_entry(const orc_cfg* c, int32_t l, int32_t j) {
+  int32_t Lr = row_len(c);
+  return (int64_t)(l / 2) * Lr + (l % 2 == 0 ? j : Lr - 1 - j);
+}
+
+static uint8_t* level_slot_page(orc_pool* p, const int32_t* row, const orc_cfg* c, int32_t l, int32_t slot) {
+  return page_at(p, row[level_entry(c, l, slot / level_tokens(c, l))]);
+}
+
+/* Class of a value x = mean * N (or mean * i) against the levels'
+ * thresholds times `scale` (1, or a count): level, or -1 pruned. */
+static int32_t level_class(const orc_cfg* c, int32_t h, double x, double scale) {
+  int32_t K = num_levels(c);
+  if (K == 2 && !c->lo_enabled) return x >= alpha_lo(c, h) * scale ? 0 : -1; /* two tiers, low tier closed */
+  for (int32_t l = 0; l < K - 1; l++)
+    if (x > level_alpha(c, h, l) * scale) return l;
+  return x >= level_alpha(c, h, K - 1) * scale ? K - 1 : -1;
+}
+
+/* Prompt classification: tier code K - l for level l, 0 pruned; counts
+ * [batch][H][K] per level. */
+int orc_levels_classify(const orc_cfg* c, int32_t batch, const int64_t* cu, const float* scores, uint8_t* tiers,
+                        int32_t* counts) {
+  if (!cfg_valid(c) || !cu_valid(batch, cu)) return ORC_E_INVALID;
+  int32_t H = c->num_kv_heads, K = num_levels(c);
+  int64_t total = cu[batch];
+  for (int32_t r = 0; r < batch; r++) {
+    int64_t N = cu[r + 1] - cu[r];
+    for (int32_t h = 0; h < H; h++) {
+      int32_t* cnt = counts + ((int64_t)r * H + h) * K;
+      for (int32_t l = 0; l < K; l++) cnt[l] = 0;
+      for (int64_t p = 0; p < N; p++) {
+        int64_t idx = (int64_t)h * total + cu[r] + p;
+        int32_t l;
+        if (c->window > 0 && p >= N - c->window) {
+          l = 0;
+        } else {
+          int64_t denom = c->prompt_rule == ORC_RULE_ALPHA_I ? p + 1 : N;
+          l = level_class(c, h, (double)scores[idx] * (double)denom, 1.0);
+        }
+        tiers[idx] = (uint8_t)(l < 0 ? 0 : K - l);
+        if (l >= 0) cnt[l]++;
+      }
+    }
+  }
+  return ORC_OK;
+}
+
+/* Which block page or extra page each of a unit's pages takes (readings
+ * above).  Q order: levels 0, 2, 3 (index order), then level 1 innermost
+ * first.  For every Q position: block index >= 0, or -1 - (extra number). */
+static void level_block_map(const orc_cfg* c, int64_t k, const int64_t* np, int64_t* map, int64_t* freed_lo,
+                            int64_t* freed_hi, int64_t* extras) {
+  int32_t K = num_levels(c);
+  int64_t A = 0;
+  for (int32_t l = 0; l < K; l++)
+    if (l != 1) A += np[l];
+  int64_t p1 = np[1];
+  int64_t Ain = A < k ? A : k;
+  int64_t Rin = p1 < k - Ain ? p1 : k - Ain;
+  int64_t e = 0;
+  for (int64_t i = 0; i < A; i++) map[i] = i < Ain ? i : -1 - (e++);
+  for (int64_t m = 0; m < p1; m++) map[A + m] = m < p1 - Rin ? -1 - (e++) : k - p1 + m;
+  *freed_lo = Ain;
+  *freed_hi = k - Rin; /* freed block pages [Ain, k - Rin) */
+  *extras = e;
+}
+
+/* (level, page index) of Q position i */
+static void level_q_page(const orc_cfg* c, const int64_t* np, int64_t i, int32_t* l, int64_t* j) {
+  int32_t K = num_levels(c);
+  for (int32_t x = 0; x < K; x++) {
+    if (x == 1) continue;
+    if (i < np[x]) {
+      *l = x;
+      *j = i;
+      return;
+    }
+    i -= np[x];
+  }
+  *l = 1;
+  *j = np[1] - 1 - i; /* level 1 innermost first */
+}
+
+int orc_levels_compact_prompt(const orc_cfg* c, orc_pool* p, int32_t batch, const int64_t* cu, const uint16_t* k,
+                              const uint16_t* v, const float* scores, const uint8_t* tiers, int32_t* table,
+                              int32_t* state) {
+  if (!cfg_valid(c) || !p || !cu_valid(batch, cu)) return ORC_E_INVALID;
+  if (p->page_bytes != orc_page_bytes(c)) return ORC_E_INVALID;
+  int32_t H = c->num_kv_heads, d = c->head_dim, K = num_levels(c), Lr = row_len(c), LT = orc_table_len(c);
+  int32_t SW = 2 * K;
+  int64_t total = cu[batch], U = (int64_t)batch * H;
+  int64_t* cnt = (int64_t*)calloc((size_t)(U > 0 ? U : 1) * K, sizeof(int64_t));
+  for (int64_t u = 0; u < U; u++) {
+    int32_t r = (int32_t)(u / H), h = (int32_t)(u % H);
+    for (int64_t t = 0; t < cu[r + 1] - cu[r]; t++) {
+      uint8_t ti = tiers[(int64_t)h * total + cu[r] + t];
+      if (ti >= 1 && ti <= K) cnt[u * K + (K - ti)]++;
+    }
+  }
+  /* plan: per-unit block, pages, frees, extras; validity and capacity */
+  uint32_t st = 0;
+  int64_t Ktot = 0, F = 0, E = 0;
+  for (int64_t u = 0; u < U; u++) {
+    int64_t N = cu[u / H + 1] - cu[u / H];
+    if (N <= 0) continue;
+    for (int32_t w = 0; w < SW; w++)
+      if (state[u * SW + w]) st |= ORC_ST_BAD_STATE;
+    if (N > c->max_seq_len) st |= ORC_ST_TABLE_OVERFLOW;
+    int64_t np[4] = {0, 0, 0, 0}, sum_n = 0;
+    for (int32_t l = 0; l < K; l++) {
+      np[l] = cdiv64(cnt[u * K + l], level_tokens(c, l));
+      sum_n += cnt[u * K + l];
+    }
+    if (sum_n > N) st |= ORC_ST_BAD_STATE;
+    int64_t kk = cdiv64(N, c->hi_page_tokens);
+    if (kk > Lr) st |= ORC_ST_TABLE_OVERFLOW;
+    for (int32_t r = 0; r < (K + 1) / 2; r++)
+      if (np[2 * r] + (2 * r + 1 < K ? np[2 * r + 1] : 0) > Lr) st |= ORC_ST_TABLE_OVERFLOW;
+    int64_t flo, fhi, e;
+    int64_t* map = (int64_t*)malloc(sizeof(int64_t) * (size_t)(np[0] + np[1] + np[2] + np[3] + 1));
+    level_block_map(c, kk, np, map, &flo, &fhi, &e);
+    free(map);
+    Ktot += kk;
+    F += fhi - flo;
+    E += e;
+  }
+  int64_t free0 = (int64_t)(p->ptr[1] - p->ptr[0]);
+  if (!st && (Ktot > free0 || Ktot - F + E > free0)) st |= ORC_ST_POOL_EXHAUSTED;
+  if (st) {
+    p->status[0] |= st;
+    free(cnt);
+    return ORC_OK;
+  }
+  /* coordination (as in the two-tier Fig 6 workflow): every unit's block in
+   * unit order from the allocation pointer, placed into the table; the
+   * unused block pages appended at the reclamation pointer (units in order);
+   * then the extra pages, units in order, each unit's in Q order. */
+  uint64_t start = p->ptr[0], end = p->ptr[1];
+  int32_t* freed = (int32_t*)malloc(sizeof(int32_t) * (size_t)(F > 0 ? F : 1));
+  int64_t nf = 0;
+  for (int64_t u = 0; u < U; u++) {
+    int64_t N = cu[u / H + 1] - cu[u / H];
+    if (N <= 0) continue;
+    int64_t kk = cdiv64(N, c->hi_page_tokens);
+    int64_t np[4] = {0, 0, 0, 0}, flo, fhi, e;
+    for (int32_t l = 0; l < K; l++) np[l] = cdiv64(cnt[u * K + l], level_tokens(c, l));
+    int64_t nq = np[0] + np[1] + np[2] + np[3];
+    int64_t* map = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nq + 1));
+    level_block_map(c, kk, np, map, &flo, &fhi, &e);
+    int32_t* row = table + u * LT;
+    for (int64_t i = 0; i < nq; i++) {
+      if (map[i] < 0) continue;
+      int32_t l;
+      int64_t j;
+      level_q_page(c, np, i, &l, &j);
+      row[level_entry(c, l, (int32_t)j)] = p->free_list[(start + (uint64_t)map[i]) % (uint64_t)p->num_pages];
+    }
+    for (int64_t i = flo; i < fhi; i++) freed[nf++] = p->free_list[(start + (uint64_t)i) % (uint64_t)p->num_pages];
+    start += (uint64_t)kk;
+    free(map);
+  }
+  for (int64_t i = 0; i < nf; i++) p->free_list[(end + (uint64_t)i) % (uint64_t)p->num_pages] = freed[i];
+  end += (uint64_t)nf;
+  for (int64_t u = 0; u < U; u++) {
+    int64_t N = cu[u / H + 1] - cu[u / H];
+    if (N <= 0) continue;
+    int64_t np[4] = {0, 0, 0, 0}, flo, fhi, e;
+    for (int32_t l = 0; l < K; l++) np[l] = cdiv64(cnt[u * K + l], level_tokens(c, l));
+    int64_t nq = np[0] + np[1] + np[2] + np[3];
+    int64_t* map = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nq + 1));
+    level_block_map(c, cdiv64(N, c->hi_page_tokens), np, map, &flo, &fhi, &e);
+    int32_t* row = table + u * LT;
+    for (int64_t i = 0; i < nq; i++) {
+      if (map[i] >= 0) continue;
+      int32_t l;
+      int64_t j;
+      level_q_page(c, np, i, &l, &j);
+      row[level_entry(c, l, (int32_t)j)] = p->free_list[(start + (uint64_t)(-1 - map[i])) % (uint64_t)p->num_pages];
+    }
+    start += (uint64_t)e;
+    free(map);
+    for (int32_t l = 0; l < K; l++) {
+      state[u * SW + l] = (int32_t)cnt[u * K + l];
+      state[u * SW + K + l] = (int32_t)np[l];
+    }
+  }
+  p->ptr[0] = start;
+  p->ptr[1] = end;
+  free(freed);
+  /* packing: zeroed pages, tokens in position order into their level */
+  float xk[128], xv[128];
+  for (int64_t u = 0; u < U; u++) {
+    int32_t r = (int32_t)(u / H), h = (int32_t)(u % H);
+    int64_t N = cu[r + 1] - cu[r];
+    if (N <= 0) continue;
+    int32_t* row = table + u * LT;
+    for (int32_t l = 0; l < K; l++)
+      for (int32_t j = 0; j < state[u * SW + K + l]; j++)
+        memset(page_at(p, row[level_entry(c, l, j)]), 0, (size_t)p->page_bytes);
+    int32_t next[4] = {0, 0, 0, 0};
+    for (int64_t t = 0; t < N; t++) {
+      int64_t idx = (int64_t)h * total + cu[r] + t;
+      uint8_t ti = tiers[idx];
+      if (ti < 1 || ti > K) continue;
+      int32_t l = K - ti, s = next[l]++;
+      const uint16_t* kr = k + ((cu[r] + t) * H + h) * d;
+      const uint16_t* vr = v + ((cu[r] + t) * H + h) * d;
+      for (int32_t j = 0; j < d; j++) {
+        xk[j] = orc_f16_to_f32(kr[j]);
+        xv[j] = orc_f16_to_f32(vr[j]);
+      }
+      float sum = scores[idx] * (float)(N - 1 - t);
+      store_level_token(c, level_slot_page(p, row, c, l, s), l, s % level_tokens(c, l), xk, xv, sum, (int32_t)t);
+    }
+  }
+  free(cnt);
+  return ORC_OK;
+}
+
+/* One token move of a step: from (level, slot) to (level, slot). */
+typedef struct {
+  int32_t on, src_l, src_s, dst_l, dst_s;
+} lv_move;
+
+typedef struct {
+  int32_t active;
+  int32_t new_slot;         /* level-0 slot of the new token */
+  lv_move mv[2];            /* mv[0] leaves level 0 (t_c or the level-0 victim); mv[1] the level-l_c victim */
+  int32_t append[4];        /* tokens each level gains */
+  int32_t need_level;       /* level of the new page, -1 none */
+  int32_t page_id;
+} lv_plan;
+
+int orc_levels_compact_step(const orc_cfg* c, orc_pool* p, int32_t batch, const int32_t* seq_len,
+                            const uint16_t* k_new, const uint16_t* v_new, int32_t* table, int32_t* state,
+                            int32_t* branch) {
+  if (!cfg_valid(c) || !p || batch < 0 || c->window < 2) return ORC_E_INVALID;
+  if (p->page_bytes != orc_page_bytes(c)) return ORC_E_INVALID;
+  int32_t H = c->num_kv_heads, d = c->head_dim, K = num_levels(c), W = c->window, LT = orc_table_len(c);
+  int32_t SW = 2 * K, Lr = row_len(c);
+  int64_t U = (int64_t)batch * H;
+  lv_plan* pl = (lv_plan*)calloc((size_t)(U > 0 ? U : 1), sizeof(lv_plan));
+  if (branch)
+    for (int64_t u = 0; u < U; u++) branch[u] = -1;
+  uint32_t st = 0;
+  int64_t demand = 0;
+  for (int64_t u = 0; u < U; u++) {
+    lv_plan* P = &pl[u];
+    P->need_level = -1;
+    int64_t N = seq_len[u / H];
+    if (N <= 0) continue;
+    P->active = 1;
+    const int32_t* s = state + u * SW;
+    const int32_t* row = table + u * LT;
+    if (N + 1 > c->max_seq_len) { st |= ORC_ST_TABLE_OVERFLOW; continue; }
+    int bad = 0;
+    int64_t sum_n = 0;
+    for (int32_t l = 0; l < K; l++) {
+      if (s[l] < 0 || s[K + l] != cdiv64(s[l], level_tokens(c, l))) bad = 1;
+      sum_n += s[l];
+    }
+    for (int32_t r = 0; r < (K + 1) / 2; r++)
+      if (s[K + 2 * r] + (2 * r + 1 < K ? s[K + 2 * r + 1] : 0) > Lr) bad = 1;
+    if (sum_n > N) bad = 1;
+    if (!bad)
+      for (int32_t l = 0; l < K; l++)
+        for (int32_t j = 0; j < s[K + l]; j++) {
+          int32_t id = row[level_entry(c, l, j)];
+          if (id < 0 || id >= p->num_pages) bad = 1;
+        }
+    if (bad) { st |= ORC_ST_BAD_STATE; continue; }
+    int64_t Np = N + 1, tc_pos = N - W;
+    int32_t hh = (int32_t)(u % H);
+    P->new_slot = s[0];
+    P->append[0] = 1;
+    int32_t br_tc = 15, br_v = 15;
+    if (tc_pos >= 0) {
+      int32_t tc = -1;
+      float tc_sum = 0;
+      for (int32_t x = 0; x < s[0]; x++) {
+        float sc; int32_t pos;
+        orc_read_level_slot(c, level_slot_page(p, row, c, 0, x), 0, x % level_tokens(c, 0), 0, 0, 0, 0, &sc, &pos);
+        if (pos == tc_pos) { tc = x; tc_sum = sc; }
+      }
+      if (tc < 0) { st |= ORC_ST_BAD_STATE; continue; }
+      int32_t lc = level_class(c, hh, (double)tc_sum * (double)Np, (double)(W - 1));
+      br_tc = lc < 0 ? 14 : lc;
+      if (lc == 0) {
+        /* the least important non-window level-0 token (t_c included) */
+        int32_t v = -1; float vs = 0; int32_t vp = 0; int64_t vcn = 0;
+        for (int32_t x = 0; x < s[0]; x++) {
+          float sc; int32_t pos;
+          orc_read_level_slot(c, level_slot_page(p, row, c, 0, x), 0, x % level_tokens(c, 0), 0, 0, 0, 0, &sc, &pos);
+          if (pos > tc_pos) continue;
+          int64_t cn = N - 1 - pos;
+          if (v < 0 || less_important(sc, cn, pos, vs, vcn, vp)) { v = x; vs = sc; vp = pos; vcn = cn; }
+        }
+        int32_t lv = level_class(c, hh, (double)vs * (double)Np, (double)vcn);
+        br_v = lv < 0 ? 14 : lv;
+        if (lv != 0) {
+          P->new_slot = v;
+          P->append[0] = 0;
+          if (lv > 0) {
+            P->mv[0] = (lv_move){1, 0, v, lv, s[lv]};
+            P->append[lv] = 1;
+          }
+        }
+      } else if (lc > 0) {
+        /* t_c leaves level 0; the least important of level l_c and t_c */
+        P->new_slot = tc;
+        P->append[0] = 0;
+        int32_t v = -1; float vs = tc_sum; int32_t vp = (int32_t)tc_pos; int64_t vcn = W - 1;
+        for (int32_t x = 0; x < s[lc]; x++) {
+          float sc; int32_t pos;
+          orc_read_level_slot(c, level_slot_page(p, row, c, lc, x), lc, x % level_tokens(c, lc), 0, 0, 0, 0, &sc,
+                              &pos);
+          int64_t cn = N - 1 - pos;
+          if (less_important(sc, cn, pos, vs, vcn, vp)) { v = x; vs = sc; vp = pos; vcn = cn; }
+        }
+        int32_t lv = v >= 0 ? level_class(c, hh, (double)vs * (double)Np, (double)vcn) : lc;
+        br_v = v < 0 ? 15 : (lv < 0 ? 14 : lv);
+        if (v >= 0 && lv != lc) {
+          /* the victim moves down (or is pruned); t_c takes its slot */
+          P->mv[0] = (lv_move){1, 0, tc, lc, v};
+          if (lv > 0) {
+            P->mv[1] = (lv_move){1, lc, v, lv, s[lv]};
+            P->append[lv] = 1;
+          }
+        } else {
+          P->mv[0] = (lv_move){1, 0, tc, lc, s[lc]};
+          P->append[lc] = 1;
+        }
+      } else {
+        P->new_slot = tc;
+        P->append[0] = 0;
+      }
+    }
+    for (int32_t l = 0; l < K; l++)
+      if (P->append[l] && s[l] % level_tokens(c, l) == 0) P->need_level = l;
+    if (branch) branch[u] = br_tc | (br_v << 4) | ((P->need_level + 1) << 8);
+    if (P->need_level >= 0) {
+      int32_t l = P->need_level, r = l / 2;
+      if (s[K + 2 * r] + (2 * r + 1 < K ? s[K + 2 * r + 1] : 0) + 1 > Lr) { st |= ORC_ST_TABLE_OVERFLOW; continue; }
+      demand++;
+    }
+  }
+  if (!st && demand > (int64_t)(p->ptr[1] - p->ptr[0])) st |= ORC_ST_POOL_EXHAUSTED;
+  if (st) {
+    p->status[0] |= st;
+    free(pl);
+    return ORC_OK;
+  }
+  uint64_t start = p->ptr[0];
+  for (int64_t u = 0; u < U; u++)
+    if (pl[u].active && pl[u].need_level >= 0) pl[u].page_id = p->free_list[(start++) % (uint64_t)p->num_pages];
+  p->ptr[0] = start;
+  /* commit: the new page, the moves (sources read before any write), the new token */
+  float xk[128], xv[128];
+  for (int64_t u = 0; u < U; u++) {
+    lv_plan* P = &pl[u];
+    if (!P->active) continue;
+    int32_t b = (int32_t)(u / H);
+    int32_t* row = table + u * LT;
+    int32_t* s = state + u * SW;
+    if (P->need_level >= 0) {
+      int32_t l = P->need_level;
+      row[level_entry(c, l, s[K + l])] = P->page_id;
+      s[K + l]++;
+      memset(page_at(p, P->page_id), 0, (size_t)p->page_bytes);
+    }
+    float mk[2][128], mvv[2][128], msc[2];
+    int32_t mpos[2];
+    for (int m = 0; m < 2; m++) {
+      if (!P->mv[m].on) continue;
+      uint8_t kc[128], vc[128];
+      uint16_t km[2], vm[2];
+      int32_t l = P->mv[m].src_l, x = P->mv[m].src_s;
+      orc_read_level_slot(c, level_slot_page(p, row, c, l, x), l, x % level_tokens(c, l), kc, vc, km, vm, &msc[m],
+                          &mpos[m]);
+      for (int32_t j = 0; j < d; j++) {
+        mk[m][j] = orc_dequant(km[0], km[1], kc[j]);
+        mvv[m][j] = orc_dequant(vm[0], vm[1], vc[j]);
+      }
+    }
+    for (int m = 0; m < 2; m++) {
+      if (!P->mv[m].on) continue;
+      int32_t l = P->mv[m].dst_l, x = P->mv[m].dst_s;
+      store_level_token(c, level_slot_page(p, row, c, l, x), l, x % level_tokens(c, l), mk[m], mvv[m], msc[m],
+                        mpos[m]);
+    }
+    for (int32_t l = 1; l < K; l++) s[l] += P->append[l];
+    const uint16_t* kr = k_new + ((int64_t)b * H + (u % H)) * d;
+    const uint16_t* vr = v_new + ((int64_t)b * H + (u % H)) * d;
+    for (int32_t j = 0; j < d; j++) {
+      xk[j] = orc_f16_to_f32(kr[j]);
+      xv[j] = orc_f16_to_f32(vr[j]);
+    }
+    store_level_token(c, level_slot_page(p, row, c, 0, P->new_slot), 0, P->new_slot % level_tokens(c, 0), xk, xv,
+                      0.0f, seq_len[b]);
+    s[0] += P->append[0];
+  }
+  free(pl);
+  return ORC_OK;
+}
+
+int orc_levels_release(const orc_cfg* c, orc_pool* p, int32_t batch, const uint8_t* mask, int32_t* table,
+                       int32_t* state) {
+  if (!cfg_valid(c) || !p || batch < 0) return ORC_E_INVALID;
+  int32_t H = c->num_kv_heads, K = num_levels(c), SW = 2 * K, Lr = row_len(c), LT = orc_table_len(c);
+  int64_t U = (int64_t)batch * H, total = 0;
+  uint32_t st = 0;
+  for (int64_t u = 0; u < U; u++) {
+    if (!mask[u / H]) continue;
+    const int32_t* s = state + u * SW;
+    const int32_t* row = table + u * LT;
+    for (int32_t r = 0; r < (K + 1) / 2; r++) {
+      int32_t a = s[K + 2 * r], bb = 2 * r + 1 < K ? s[K + 2 * r + 1] : 0;
+      if (a < 0 || bb < 0 || a + bb > Lr) { st |= ORC_ST_BAD_STATE; break; }
+    }
+    if (st) continue;
+    for (int32_t l = 0; l < K; l++)
+      for (int32_t j = 0; j < s[K + l]; j++) {
+        int32_t id = row[level_entry(c, l, j)];
+        if (id < 0 || id >= p->num_pages) st |= ORC_ST_BAD_STATE;
+      }
+    for (int32_t l = 0; l < K; l++) total += s[K + l];
+  }
+  if (!st && (int64_t)(p->ptr[1] - p->ptr[0]) + total > p->num_pages) st |= ORC_ST_BAD_STATE;
+  if (st) {
+    p->status[0] |= st;
+    return ORC_OK;
+  }
+  uint64_t end = p->ptr[1];
+  for (int64_t u = 0; u < U; u++) {
+    if (!mask[u / H]) continue;
+    int32_t* row = table + u * LT;
+    int32_t* s = state + u * SW;
+    for (int32_t l = 0; l < K; l++) /* levels in order: left levels left to right, right levels right to left */
+      for (int32_t j = 0; j < s[K + l]; j++) p->free_list[(end++) % (uint64_t)p->num_pages] = row[level_entry(c, l, j)];
+    for (int32_t j = 0; j < LT; j++) row[j] = -1;
+    for (int32_t w = 0; w < SW; w++) s[w] = 0;
+  }
+  p->ptr[1] = end;
+  return ORC_OK;
+}
+
+int orc_levels_decode_attn(const orc_cfg* c, orc_pool* p, int32_t batch, const uint16_t* q, const int32_t* table,
+                           const int32_t* state, const int32_t* seq_len, float* out, int32_t update_scores) {
+  if (!cfg_valid(c) || !p || batch < 0) return ORC_E_INVALID;
+  if (p->page_bytes != orc_page_bytes(c)) return ORC_E_INVALID;
+  int32_t H = c->num_kv_heads, G = c->gqa_group, d = c->head_dim, K = num_levels(c), SW = 2 * K;
+  int32_t Lr = row_len(c), LT = orc_table_len(c);
+  memset(out, 0, sizeof(float) * (size_t)batch * H * G * d);
+  uint32_t st = 0;
+  for (int64_t u = 0; u < (int64_t)batch * H; u++) {
+    int32_t b = (int32_t)(u / H), h = (int32_t)(u % H);
+    if (seq_len[b] <= 0) continue;
+    const int32_t* s = state + u * SW;
+    const int32_t* row = table + u * LT;
+    int bad = 0;
+    int32_t n = 0;
+    for (int32_t l = 0; l < K; l++) {
+      if (s[l] < 0 || s[K + l] != cdiv64(s[l], level_tokens(c, l))) bad = 1;
+      n += s[l];
+    }
+    for (int32_t r = 0; r < (K + 1) / 2; r++)
+      if (s[K + 2 * r] + (2 * r + 1 < K ? s[K + 2 * r + 1] : 0) > Lr) bad = 1;
+    if (!bad)
+      for (int32_t l = 0; l < K; l++)
+        for (int32_t j = 0; j < s[K + l]; j++) {
+          int32_t id = row[level_entry(c, l, j)];
+          if (id < 0 || id >= p->num_pages) bad = 1;
+        }
+    if (bad) { st |= ORC_ST_BAD_STATE; continue; }
+    if (n == 0) continue;
+    double* kh = (double*)malloc(sizeof(double) * (size_t)n * d);
+    double* vh = (double*)malloc(sizeof(double) * (size_t)n * d);
+    int32_t* lev = (int32_t*)malloc(sizeof(int32_t) * (size_t)n);
+    int32_t* slot = (int32_t*)malloc(sizeof(int32_t) * (size_t)n);
+    int32_t* pos = (int32_t*)malloc(sizeof(int32_t) * (size_t)n);
+    double* pmax = (double*)calloc((size_t)n, sizeof(double));
+    double* x = (double*)malloc(sizeof(double) * (size_t)n);
+    int32_t t = 0;
+    for (int32_t l = 0; l < K; l++)
+      for (int32_t sl = 0; sl < s[l]; sl++, t++) {
+        uint8_t kc[128], vc[128];
+        uint16_t km[2], vm[2];
+        float sc;
+        orc_read_level_slot(c, level_slot_page(p, row, c, l, sl), l, sl % level_tokens(c, l), kc, vc, km, vm, &sc,
+                            &pos[t]);
+        lev[t] = l;
+        slot[t] = sl;
+        for (int32_t i = 0; i < d; i++) {
+          kh[(int64_t)t * d + i] = (double)orc_dequant(km[0], km[1], kc[i]);
+          vh[(int64_t)t * d + i] = (double)orc_dequant(vm[0], vm[1], vc[i]);
+        }
+      }
+    double scale = 1.0 / sqrt((double)d);
+    for (int32_t g = 0; g < G; g++) {
+      int32_t jh = h * G + g;
+      const uint16_t* qr = q + ((int64_t)b * H * G + jh) * d;
+      double qd[128];
+      for (int32_t i = 0; i < d; i++) qd[i] = (double)orc_f16_to_f32(qr[i]);
+      double m = -INFINITY, z = 0.0;
+      for (int32_t a = 0; a < n; a++) {
+        double acc = 0.0;
+        for (int32_t i = 0; i < d; i++) acc += qd[i] * kh[(int64_t)a * d + i];
+        x[a] = acc * scale;
+        if (x[a] > m) m = x[a];
+      }
+      for (int32_t a = 0; a < n; a++) z += exp(x[a] - m);
+      float* o = out + ((int64_t)b * H * G + jh) * d;
+      for (int32_t i = 0; i < d; i++) {
+        double acc = 0.0;
+        for (int32_t a = 0; a < n; a++) acc += exp(x[a] - m) / z * vh[(int64_t)a * d + i];
+        o[i] = (float)acc;
+      }
+      for (int32_t a = 0; a < n; a++) {
+        double pr = exp(x[a] - m) / z;
+        if (pr > pmax[a]) pmax[a] = pr;
+      }
+    }
+    if (update_scores) {
+      for (int32_t a = 0; a < n; a++) {
+        if (pos[a] >= seq_len[b]) continue;
+        int32_t seg[7];
+        orc_level_layout(c, lev[a], seg);
+        uint8_t* sp = level_slot_page(p, row, c, lev[a], slot[a]) + seg[4] + 4 * (slot[a] % level_tokens(c, lev[a]));
+        put_u32(sp, f32_bits((float)((double)bits_f32(get_u32(sp)) + pmax[a])));
+      }
+    }
+    free(kh); free(vh); free(lev); free(slot); free(pos); free(pmax); free(x);
+  }
+  p->status[0] |= st;
   return ORC_OK;
 }

@@ -45,6 +45,15 @@ typedef struct {
   /* tier codecs: bits of K and V codes per tier, each in {1, 2, 4, 8};
    * all four 0 = the default K8V4 (high) / K4V2 (low) */
   int32_t hi_k_bits, hi_v_bits, lo_k_bits, lo_v_bits;
+  /* More than two precision levels: num_levels K = 0 or 2 keeps the two
+   * tiers above; K = 3 or 4 gives levels 0 (high: alpha_h, hi bits, T_h
+   * tokens per page) .. K-1 (low: alpha_l, lo bits, T_l tokens), the middle
+   * levels l = 1..K-2 with alpha_mid[l-1] and mid_k_bits / mid_v_bits[l-1]
+   * (T_l tokens).  Codecs must be given (plain layout); table rows: level
+   * 2r from the left and level 2r+1 from the right of row r. */
+  int32_t num_levels;
+  float alpha_mid[2];
+  int32_t mid_k_bits[2], mid_v_bits[2];
 } orc_cfg;
 
 enum { ORC_RULE_ALPHA_N = 0, ORC_RULE_ALPHA_I = 1 };
@@ -77,6 +86,41 @@ void orc_v_code_addr(const orc_cfg* c, int32_t tier, int32_t tok, int32_t j,
 void orc_read_slot(const orc_cfg* c, const uint8_t* page, int32_t tier, int32_t slot,
                    uint8_t* kc, uint8_t* vc, uint16_t* kmeta /*[2]*/,
                    uint16_t* vmeta /*[2]*/, float* score, int32_t* pos);
+
+/* Levels (K >= 3, or K = 2 as the two tiers: level 0 = high, 1 = low):
+ * number of levels, int32 words of tier state per unit (n_0..n_{K-1},
+ * p_0..p_{K-1}), and the layout of one level's pages (as orc_tier_layout). */
+int32_t orc_num_levels(const orc_cfg* c);
+int32_t orc_state_words(const orc_cfg* c);
+int32_t orc_level_layout(const orc_cfg* c, int32_t level, int32_t seg[7]);
+/* Unpack one slot of a level's page (as orc_read_slot). */
+void orc_read_level_slot(const orc_cfg* c, const uint8_t* page, int32_t level, int32_t slot,
+                         uint8_t* kc, uint8_t* vc, uint16_t* kmeta, uint16_t* vmeta,
+                         float* score, int32_t* pos);
+/* The generation step over K levels (any K, also 2), recording per unit:
+ * bits 0-3 the class of t_c (level, 14 = pruned, 15 = no t_c), bits 4-7 the
+ * class of the victim (level, 14 = pruned, 15 = no victim considered),
+ * bits 8-11 the level of the new page + 1 (0: none); -1 inactive. */
+int orc_levels_compact_step(const orc_cfg* c, orc_pool* p, int32_t batch,
+                            const int32_t* seq_len, const uint16_t* k_new,
+                            const uint16_t* v_new, int32_t* page_table,
+                            int32_t* tier_state, int32_t* branch);
+/* Level versions of classify, prompt compaction, release and attention
+ * (any K; the two-tier entry points call them when K >= 3). */
+int orc_levels_classify(const orc_cfg* c, int32_t batch, const int64_t* cu_seqlens,
+                        const float* scores, uint8_t* tiers, int32_t* tier_counts);
+int orc_levels_compact_prompt(const orc_cfg* c, orc_pool* p, int32_t batch,
+                              const int64_t* cu_seqlens, const uint16_t* k,
+                              const uint16_t* v, const float* scores,
+                              const uint8_t* tiers, int32_t* page_table,
+                              int32_t* tier_state);
+int orc_levels_release(const orc_cfg* c, orc_pool* p, int32_t batch,
+                       const uint8_t* release_mask, int32_t* page_table,
+                       int32_t* tier_state);
+int orc_levels_decode_attn(const orc_cfg* c, orc_pool* p, int32_t batch,
+                           const uint16_t* q, const int32_t* page_table,
+                           const int32_t* tier_state, const int32_t* seq_len,
+                           float* out, int32_t update_scores);
 
 /* ---- fp16 and codec ---------------------------------------------------- */
 uint16_t orc_f32_to_f16(float f);
