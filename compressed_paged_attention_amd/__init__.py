@@ -40,7 +40,9 @@ class diffkv_config(ctypes.Structure):
                 ("prompt_rule", ctypes.c_int32), ("alpha_h_head", ctypes.c_void_p),
                 ("alpha_l_head", ctypes.c_void_p),
                 ("hi_k_bits", ctypes.c_int32), ("hi_v_bits", ctypes.c_int32),
-                ("lo_k_bits", ctypes.c_int32), ("lo_v_bits", ctypes.c_int32)]
+                ("lo_k_bits", ctypes.c_int32), ("lo_v_bits", ctypes.c_int32),
+                ("num_levels", ctypes.c_int32), ("alpha_mid", ctypes.c_float * 2),
+                ("mid_k_bits", ctypes.c_int32 * 2), ("mid_v_bits", ctypes.c_int32 * 2)]
 
 
 RULE_ALPHA_N, RULE_ALPHA_I = 0, 1
@@ -70,6 +72,8 @@ def lib() -> ctypes.CDLL:
         L.diffkv_page_bytes.restype = i32
         L.diffkv_table_len.argtypes = [cfgp]
         L.diffkv_table_len.restype = i32
+        L.diffkv_state_words.argtypes = [cfgp]
+        L.diffkv_state_words.restype = i32
         L.diffkv_attn_splits.argtypes = [cfgp, i32]
         L.diffkv_attn_splits.restype = i32
         L.diffkv_workspace_bytes.argtypes = [cfgp, i32, i32, i64]
@@ -120,7 +124,8 @@ def make_config(c: dict) -> diffkv_config:
     """Config dict -> diffkv_config.  Optional keys: prompt_rule
     (RULE_ALPHA_N / RULE_ALPHA_I), alpha_h_head / alpha_l_head (H values
     each: a sequence, or a float32 device tensor) and hi_k_bits / hi_v_bits /
-    lo_k_bits / lo_v_bits (tier codecs)."""
+    lo_k_bits / lo_v_bits (tier codecs), num_levels (3 or 4 precision levels)
+    with alpha_mid / mid_k_bits / mid_v_bits (one value per middle level)."""
     r = diffkv_config(int(c["head_dim"]), int(c["num_kv_heads"]), int(c["gqa_group"]),
                       int(c.get("hi_page_tokens", 16)), int(c.get("lo_page_tokens", 32)),
                       int(c["max_seq_len"]), int(c["window"]), int(c.get("lo_enabled", 1)),
@@ -134,6 +139,12 @@ def make_config(c: dict) -> diffkv_config:
     r._keep = keep  # the device arrays live as long as the struct
     for key in ("hi_k_bits", "hi_v_bits", "lo_k_bits", "lo_v_bits"):  # tier codecs (absent: K8V4 / K4V2)
         setattr(r, key, int(c.get(key, 0)))
+    r.num_levels = int(c.get("num_levels", 0))  # 3 or 4 precision levels (absent: two tiers)
+    for key, conv in (("alpha_mid", float), ("mid_k_bits", int), ("mid_v_bits", int)):
+        vals = list(c.get(key, ()))
+        arr = getattr(r, key)
+        for i in range(2):
+            arr[i] = conv(vals[i]) if i < len(vals) else conv(0)
     return r
 
 
@@ -163,6 +174,10 @@ def diffkv_page_bytes(cfg: dict) -> int:
 
 def diffkv_table_len(cfg: dict) -> int:
     return lib().diffkv_table_len(ctypes.byref(make_config(cfg)))
+
+
+def diffkv_state_words(cfg: dict) -> int:
+    return lib().diffkv_state_words(ctypes.byref(make_config(cfg)))
 
 
 def diffkv_attn_splits(cfg: dict, batch: int) -> int:
@@ -308,7 +323,8 @@ class DiffKVState:
         self.L = diffkv_table_len(cfg)
         self.pool = Pool(cfg, num_pages, device)
         self.page_table = torch.empty(batch, self.H, self.L, dtype=torch.int32, device=device)
-        self.tier_state = torch.empty(batch, self.H, 4, dtype=torch.int32, device=device)
+        self.K = diffkv_state_words(cfg) // 2  # precision levels
+        self.tier_state = torch.empty(batch, self.H, 2 * self.K, dtype=torch.int32, device=device)
         cws = max(diffkv_workspace_bytes(cfg, PROMPT, batch, max_total_tokens),
                   diffkv_workspace_bytes(cfg, STEP, batch), diffkv_workspace_bytes(cfg, RELEASE, batch))
         self.ws_compact = torch.empty(cws, dtype=torch.uint8, device=device)
@@ -326,7 +342,7 @@ class DiffKVState:
     def classify(self, cu_seqlens, scores):
         total = int(scores.shape[1])
         tiers = torch.empty(self.H, total, dtype=torch.uint8, device=scores.device)
-        counts = torch.empty(cu_seqlens.numel() - 1, self.H, 2, dtype=torch.int32, device=scores.device)
+        counts = torch.empty(cu_seqlens.numel() - 1, self.H, self.K, dtype=torch.int32, device=scores.device)
         diffkv_classify(self.cfg, cu_seqlens, scores, tiers, counts, total)
         return tiers, counts
 

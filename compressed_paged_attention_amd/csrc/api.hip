@@ -28,6 +28,22 @@ bool cfg_ok(const diffkv_config* c) {
   auto bits_ok = [](int32_t b) { return b == 1 || b == 2 || b == 4 || b == 8; };
   if (plain && !(bits_ok(c->hi_k_bits) && bits_ok(c->hi_v_bits) && bits_ok(c->lo_k_bits) && bits_ok(c->lo_v_bits)))
     return false;
+  if (c->num_levels != 0 && c->num_levels != 2) {
+    // K = 3 or 4 levels: every width given, the low level on, thresholds
+    // descending (the per-head arrays live on the device: the caller keeps
+    // alpha_h_head[h] >= alpha_mid[0] and alpha_mid[K-3] >= alpha_l_head[h])
+    const int K = c->num_levels;
+    if (K != 3 && K != 4) return false;
+    if (!plain || !c->lo_enabled) return false;
+    float prev = c->alpha_h;
+    for (int m = 0; m < K - 2; m++) {
+      if (!bits_ok(c->mid_k_bits[m]) || !bits_ok(c->mid_v_bits[m])) return false;
+      if (!(c->alpha_mid[m] >= 0.0f)) return false;
+      if (c->alpha_h_head == nullptr && c->alpha_mid[m] > prev) return false;
+      prev = c->alpha_mid[m];
+    }
+    if (c->alpha_h_head == nullptr && c->alpha_l > prev) return false;
+  }
   return true;
 }
 
@@ -48,6 +64,25 @@ Cfg to_cfg(const diffkv_config* c) {
   r.plain = c->hi_k_bits || c->hi_v_bits || c->lo_k_bits || c->lo_v_bits;
   r.codec = r.plain ? Codec{c->hi_k_bits, c->hi_v_bits, c->lo_k_bits, c->lo_v_bits} : Codec{8, 4, 4, 2};
   r.page_bytes = r.plain ? plain_page_bytes(r.d, r.codec) : page_bytes_for(r.d);
+  r.K = c->num_levels >= 3 ? c->num_levels : 2;
+  r.R = (r.K + 1) / 2;
+  r.LT = r.R * r.L;
+  r.amid[0] = c->alpha_mid[0];
+  r.amid[1] = c->alpha_mid[1];
+  if (r.K == 2) {
+    r.lv[0] = r.plain ? plain_seg(r.d, true, r.codec) : tier_seg(r.d, true);
+    r.lv[1] = r.plain ? plain_seg(r.d, false, r.codec) : tier_seg(r.d, false);
+    r.lv[2] = r.lv[3] = r.lv[1];
+  } else {
+    r.page_bytes = 0;
+    for (int l = 0; l < 4; l++) {
+      const int ll = l < r.K ? l : r.K - 1;
+      const int kb = ll == 0 ? c->hi_k_bits : (ll == r.K - 1 ? c->lo_k_bits : c->mid_k_bits[ll - 1]);
+      const int vb = ll == 0 ? c->hi_v_bits : (ll == r.K - 1 ? c->lo_v_bits : c->mid_v_bits[ll - 1]);
+      r.lv[l] = level_seg(r.d, ll == 0 ? kHiTokens : kLoTokens, kb, vb);
+      if (r.lv[l].bytes > r.page_bytes) r.page_bytes = r.lv[l].bytes;
+    }
+  }
   return r;
 }
 
@@ -73,7 +108,12 @@ int32_t diffkv_page_bytes(const diffkv_config* cfg) {
 
 int32_t diffkv_table_len(const diffkv_config* cfg) {
   if (!cfg_ok(cfg)) return -1;
-  return to_cfg(cfg).L;
+  return to_cfg(cfg).LT;
+}
+
+int32_t diffkv_state_words(const diffkv_config* cfg) {
+  if (!cfg_ok(cfg)) return -1;
+  return 2 * to_cfg(cfg).K;
 }
 
 int32_t diffkv_attn_splits(const diffkv_config* cfg, int32_t batch) {
@@ -229,7 +269,7 @@ int diffkv_keydiff_scores(const diffkv_config* cfg, int32_t batch, int64_t total
 
 int diffkv_page_bounds(const diffkv_config* cfg, const diffkv_pool* pool, int32_t batch, const int32_t* page_table,
                        const int32_t* tier_state, float* bounds, void* stream) {
-  if (!cfg_ok(cfg) || !pool_ok(cfg, pool) || batch < 0) return DIFFKV_E_INVALID;
+  if (!cfg_ok(cfg) || !pool_ok(cfg, pool) || batch < 0 || cfg->num_levels >= 3) return DIFFKV_E_INVALID;
   if (batch > 0 && (!page_table || !tier_state || !bounds)) return DIFFKV_E_INVALID;
   if ((int64_t)batch * cfg->num_kv_heads > 65535) return DIFFKV_E_INVALID;
   return rc(launch_page_bounds(to_cfg(cfg), to_pool(pool), batch, page_table, tier_state, bounds,
@@ -239,7 +279,7 @@ int diffkv_page_bounds(const diffkv_config* cfg, const diffkv_pool* pool, int32_
 int diffkv_page_scores(const diffkv_config* cfg, const diffkv_pool* pool, int32_t batch, const uint16_t* q,
                        const int32_t* page_table, const int32_t* tier_state, const int32_t* seq_len,
                        const float* bounds, float* scores, void* stream) {
-  if (!cfg_ok(cfg) || !pool_ok(cfg, pool) || batch < 0) return DIFFKV_E_INVALID;
+  if (!cfg_ok(cfg) || !pool_ok(cfg, pool) || batch < 0 || cfg->num_levels >= 3) return DIFFKV_E_INVALID;
   if (batch > 0 && (!q || !page_table || !tier_state || !seq_len || !bounds || !scores)) return DIFFKV_E_INVALID;
   if ((int64_t)batch * cfg->num_kv_heads > 65535) return DIFFKV_E_INVALID;
   // pairs of dimensions per lane: 4-byte query words, 8-byte bound pairs

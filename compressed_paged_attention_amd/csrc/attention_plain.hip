@@ -57,13 +57,40 @@ PlainWs plain_carve(const Cfg& c, int batch, bool scores, void* ws, size_t* byte
   w.ml = (float*)(b + off);
   off = align_up(off + (size_t)U * c.G * 2 * sizeof(float), 256);
   w.logits = (float*)(b + off);
-  if (scores) off = align_up(off + (size_t)U * c.G * 32 * c.L * sizeof(float), 256);
+  if (scores) off = align_up(off + (size_t)U * c.G * 32 * c.LT * sizeof(float), 256);
   if (bytes) *bytes = off < 256 ? 256 : off;
   return w;
 }
 
-__device__ inline bool plain_state_ok(int nh, int nl, int ph, int pl, int L) {
-  return nh >= 0 && nl >= 0 && ph == (int)cdiv(nh, kHiTokens) && pl == (int)cdiv(nl, kLoTokens) && ph + pl <= L;
+// A unit's levels: token counts n[l], page counts p[l] (state words l and
+// K + l), and their prefix sums (pages and slots of the levels before l).
+struct UnitLv {
+  int n[4], p[4], pp[5], np[5];
+  bool ok;
+};
+
+__device__ inline UnitLv unit_levels(const int32_t* s, const Levels& lv) {
+  UnitLv x;
+  x.ok = true;
+  x.pp[0] = x.np[0] = 0;
+  for (int l = 0; l < 4; l++) {
+    x.n[l] = l < lv.K ? s[l] : 0;
+    x.p[l] = l < lv.K ? s[lv.K + l] : 0;
+    x.ok &= x.n[l] >= 0 && x.p[l] == (int)cdiv(x.n[l], lv.T(l));
+    x.pp[l + 1] = x.pp[l] + x.p[l];
+    x.np[l + 1] = x.np[l] + x.n[l];
+  }
+  x.ok &= x.p[0] + x.p[1] <= lv.L && x.p[2] + x.p[3] <= lv.L;
+  return x;
+}
+
+// level of the unit's page j (pages in level order)
+__device__ inline int level_of_page(const UnitLv& x, int j) {
+  return j < x.pp[1] ? 0 : j < x.pp[2] ? 1 : j < x.pp[3] ? 2 : 3;
+}
+// level of the unit's slot s (slots in level order)
+__device__ inline int level_of_slot(const UnitLv& x, int s) {
+  return s < x.np[1] ? 0 : s < x.np[2] ? 1 : s < x.np[3] ? 2 : 3;
 }
 
 // 16 codes of width B from a 2B-byte block (aligned to 2B bytes); code e at
@@ -264,7 +291,8 @@ __device__ inline void plain_page(const PageLd<D>& r, const Seg& sg, int lane, i
 
 template <int D, int GB>
 __global__ __launch_bounds__(kPThreads) void plain_attn_kernel(int H, int G, int L, int S, int64_t P, int page_bytes,
-                                                               Lay lay, float scale_log2, int keep_logits,
+                                                               int LT, Levels lv, float scale_log2,
+                                                               int keep_logits,
                                                                const uint16_t* __restrict__ q,
                                                                const int32_t* __restrict__ table,
                                                                const int32_t* __restrict__ state,
@@ -289,11 +317,10 @@ __global__ __launch_bounds__(kPThreads) void plain_attn_kernel(int H, int G, int
       for (int x = tid; x < G * D; x += kPThreads) out[((int64_t)b * H * G + (int64_t)h * G) * D + x] = 0.0f;
     return;
   }
-  const int32_t* s4 = state + 4 * u;
-  const int nh = s4[0], nl = s4[1], ph = s4[2], pl = s4[3];
-  const bool sok = plain_state_ok(nh, nl, ph, pl, L);
+  const UnitLv ux = unit_levels(state + 2 * lv.K * u, lv);
+  const bool sok = ux.ok;
   if (!sok && split == 0 && tid == 0) atomicOr(status, kStBadState);
-  const int TPg = sok ? ph + pl : 0;
+  const int TPg = sok ? ux.pp[4] : 0;
   const int pps = split_pages(TPg, S);
   const int p0 = split * pps, p1 = min(TPg, p0 + pps);
   // the group's q heads (fp32, [d][GB]; heads G..GB-1 zero) and their sums
@@ -320,23 +347,22 @@ __global__ __launch_bounds__(kPThreads) void plain_attn_kernel(int H, int G, int
   }
   bool bad = false;
   float* pw = ps[wid];
-  const int64_t LS = (int64_t)32 * L;
+  const int64_t LS = (int64_t)32 * LT;
   // The wave's pages j = p0 + wid + 8k.  Software pipeline: the table id two
   // pages ahead and every load of the next page are issued before the
   // current page is computed.
   auto id_of = [&](int jj) {
-    const bool hi = jj < ph;
-    const int jt = hi ? jj : jj - ph;
-    return table[u * L + (hi ? jt : L - 1 - jt)];
+    const int l = level_of_page(ux, jj);
+    return table[u * LT + lv.entry(l, jj - ux.pp[l])];
   };
   auto ok_id = [&](int32_t id) { return id >= 0 && id < P; };
+  auto nv_of = [&](int l, int jt) { return min(lv.T(l), ux.n[l] - lv.T(l) * jt); };
   auto load = [&](int jj, int32_t id, PageLd<D>& r) {
-    const bool hi = jj < ph;
-    const int jt = hi ? jj : jj - ph;
-    const int nv = hi ? min(kHiTokens, nh - kHiTokens * jt) : min(kLoTokens, nl - kLoTokens * jt);
+    const int l = level_of_page(ux, jj);
+    const int jt = jj - ux.pp[l];
     const uint8_t* pg = pages + (int64_t)id * page_bytes;
-    if (hi) plain_load<D, kHiTokens>(pg, lay.seg(true), lane, nv, r);
-    else plain_load<D, kLoTokens>(pg, lay.seg(false), lane, nv, r);
+    if (l == 0) plain_load<D, kHiTokens>(pg, lv.s[0], lane, nv_of(0, jt), r);
+    else plain_load<D, kLoTokens>(pg, lv.s[l], lane, nv_of(l, jt), r);
   };
   int j = p0 + wid;
   int32_t id_cur = j < p1 ? id_of(j) : -1;
@@ -352,13 +378,13 @@ __global__ __launch_bounds__(kPThreads) void plain_attn_kernel(int H, int G, int
     if (!ok_id(id_cur)) {
       bad = true;
     } else {
-      const bool hi = j < ph;
-      const int jt = hi ? j : j - ph;
-      const int nv = hi ? min(kHiTokens, nh - kHiTokens * jt) : min(kLoTokens, nl - kLoTokens * jt);
-      const int slot0 = hi ? kHiTokens * jt : nh + kLoTokens * jt;
+      const int lev = level_of_page(ux, j);
+      const int jt = j - ux.pp[lev];
+      const int nv = nv_of(lev, jt);
+      const int slot0 = ux.np[lev] + lv.T(lev) * jt;
       float* lg = keep_logits ? logits + u * G * LS + slot0 : nullptr;
-      if (hi) plain_page<D, kHiTokens, GB>(cur, lay.seg(true), lane, nv, G, LS, lg, qs, qsum, scale_log2, pw, m, l, o, zs);
-      else plain_page<D, kLoTokens, GB>(cur, lay.seg(false), lane, nv, G, LS, lg, qs, qsum, scale_log2, pw, m, l, o, zs);
+      if (lev == 0) plain_page<D, kHiTokens, GB>(cur, lv.s[0], lane, nv, G, LS, lg, qs, qsum, scale_log2, pw, m, l, o, zs);
+      else plain_page<D, kLoTokens, GB>(cur, lv.s[lev], lane, nv, G, LS, lg, qs, qsum, scale_log2, pw, m, l, o, zs);
     }
     cur = nxt;
     id_cur = id_n;
@@ -414,7 +440,7 @@ __global__ __launch_bounds__(kPThreads) void plain_attn_kernel(int H, int G, int
 }
 
 // One thread per retained slot of the unit (grid x: blocks of 256 slots).
-__global__ __launch_bounds__(256) void plain_score_kernel(int H, int G, int L, int64_t P, int page_bytes, Lay lay,
+__global__ __launch_bounds__(256) void plain_score_kernel(int H, int G, int LT, int64_t P, int page_bytes, Levels lv,
                                                           const int32_t* __restrict__ table,
                                                           const int32_t* __restrict__ state,
                                                           const int32_t* __restrict__ seq_len,
@@ -424,25 +450,24 @@ __global__ __launch_bounds__(256) void plain_score_kernel(int H, int G, int L, i
   const int b = (int)u / H;
   const int N = seq_len[b];
   if (N <= 0) return;
-  const int32_t* s4 = state + 4 * u;
-  const int nh = s4[0], nl = s4[1], ph = s4[2], pl = s4[3];
-  if (!plain_state_ok(nh, nl, ph, pl, L)) return;
+  const UnitLv ux = unit_levels(state + 2 * lv.K * u, lv);
+  if (!ux.ok) return;
   const int s = blockIdx.x * 256 + threadIdx.x;
-  if (s >= nh + nl) return;
+  if (s >= ux.np[4]) return;
   if (!(ml[u * G * 2 + 1] > 0.0f)) return;  // bad unit
-  const bool hi = s < nh;
-  const int ls = hi ? s : s - nh;
-  const int jt = hi ? ls / kHiTokens : ls / kLoTokens, idx = hi ? ls % kHiTokens : ls % kLoTokens;
-  const int32_t id = table[u * L + (hi ? jt : L - 1 - jt)];
+  const int lev = level_of_slot(ux, s);
+  const int ls = s - ux.np[lev], T = lv.T(lev);
+  const int jt = ls / T, idx = ls % T;
+  const int32_t id = table[u * LT + lv.entry(lev, jt)];
   if (id < 0 || id >= P) return;
-  const int64_t LS = (int64_t)32 * L;
+  const int64_t LS = (int64_t)32 * LT;
   float pmax = 0.0f;
   for (int g = 0; g < G; g++) {
     const float M = ml[(u * G + g) * 2 + 0], Ls = ml[(u * G + g) * 2 + 1];
     const float p = __builtin_amdgcn_exp2f(logits[(u * G + g) * LS + s] - M) / Ls;
     pmax = fmaxf(pmax, p);
   }
-  const Seg& sg = lay.seg(hi);
+  const Seg& sg = lv.s[lev];
   uint8_t* pg = pages + (int64_t)id * page_bytes;
   const int32_t pos = *(const int32_t*)(pg + sg.ps + 4 * idx);
   if (pos >= N) return;
@@ -461,9 +486,9 @@ hipError_t launch_scores_plain(const Cfg& c, const Pool& p, int batch, const int
   const int64_t U = (int64_t)batch * c.H;
   if (U == 0) return hipSuccess;
   const PlainWs w = plain_carve(c, batch, true, ws, nullptr);
-  const dim3 grid((unsigned)((32 * (int64_t)c.L + 255) / 256), (unsigned)U), block(256);
-  plain_score_kernel<<<grid, block, 0, s>>>(c.H, c.G, c.L, p.P, p.page_bytes, Lay(c.d, true, c.codec), table, state,
-                                            seq_len, w.ml, w.logits, p.pages);
+  const dim3 grid((unsigned)((32 * (int64_t)c.LT + 255) / 256), (unsigned)U), block(256);
+  plain_score_kernel<<<grid, block, 0, s>>>(c.H, c.G, c.LT, p.P, p.page_bytes, levels_of(c), table, state, seq_len,
+                                            w.ml, w.logits, p.pages);
   return hipGetLastError();
 }
 
@@ -476,10 +501,10 @@ hipError_t launch_attn_plain(const Cfg& c, const Pool& p, int batch, const uint1
   const PlainWs w = plain_carve(c, batch, mode != 0, ws, nullptr);
   const float scale_log2 = (1.0f / sqrtf((float)c.d)) * kLog2eP;
   const dim3 grid((unsigned)S, (unsigned)U), block(kPThreads);
-  const Lay lay(c.d, true, c.codec);
+  const Levels lv = levels_of(c);
   const int GB = c.G <= 4 ? 4 : (c.G <= 8 ? 8 : 16);
 #define DKV_PATTN(D, GB_)                                                                                      \
-  plain_attn_kernel<D, GB_><<<grid, block, 0, s>>>(c.H, c.G, c.L, S, p.P, p.page_bytes, lay, scale_log2,       \
+  plain_attn_kernel<D, GB_><<<grid, block, 0, s>>>(c.H, c.G, c.L, S, p.P, p.page_bytes, c.LT, lv, scale_log2,  \
                                                    mode != 0, q, table, state, seq_len, p.pages, out, w.part,  \
                                                    w.logits, p.status)
 #define DKV_PATTN_D(D)              \

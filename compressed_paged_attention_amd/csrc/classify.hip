@@ -34,7 +34,7 @@ hipError_t launch_pool_init(const Pool& p, hipStream_t s) {
 }
 
 hipError_t launch_state_init(const Cfg& c, int batch, int32_t* table, int32_t* state, hipStream_t s) {
-  const int64_t nt = (int64_t)batch * c.H * c.L, ns = (int64_t)batch * c.H * 4;
+  const int64_t nt = (int64_t)batch * c.H * c.LT, ns = (int64_t)batch * c.H * 2 * c.K;
   const int64_t n = nt > ns ? nt : ns;
   if (n == 0) return hipSuccess;
   state_init_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(table, nt, state, ns);
@@ -101,9 +101,67 @@ __global__ __launch_bounds__(1024) void classify_kernel(int H, int W, int lo_en,
   }
 }
 
+// K precision levels: the first level l < K-1 with x > alpha_l, else level
+// K-1 if x >= alpha_{K-1}, else pruned; code K - l (0 pruned).
+// (a0: level 0's threshold, a1 and a2 the middle levels', aL the last's)
+__device__ inline int level_code(float s, int64_t N, int64_t p, int W, int K, double a0, double a1, double a2,
+                                 double aL, int rule) {
+  if (W > 0 && p >= N - W) return K;
+  const double x = (double)s * (double)(rule ? p + 1 : N);
+  if (x > a0) return K;
+  if (x > a1) return K - 1;
+  if (K == 4 && x > a2) return 2;
+  return x >= aL ? 1 : 0;
+}
+
+// grid (H, batch); one workgroup per unit, K counts per unit
+__global__ __launch_bounds__(1024) void classify_levels_kernel(int H, int W, int K, float ah, float al, float am0,
+                                                               float am1, const float* __restrict__ ah_head,
+                                                               const float* __restrict__ al_head, int rule,
+                                                               int64_t total, const int64_t* __restrict__ cu,
+                                                               const float* __restrict__ scores,
+                                                               uint8_t* __restrict__ tiers,
+                                                               int32_t* __restrict__ counts) {
+  const int h = blockIdx.x, r = blockIdx.y;
+  const int64_t b0 = cu[r], N = cu[r + 1] - b0;
+  int32_t* cnt = counts + ((int64_t)r * H + h) * K;
+  const bool ok = !(b0 < 0 || N < 0 || cu[r + 1] > total);  // inconsistent offsets: nothing is read
+  const double a0 = (double)(ah_head ? ah_head[h] : ah), aL = (double)(al_head ? al_head[h] : al);
+  int n[4] = {0, 0, 0, 0};
+  if (ok) {
+    const float* s = scores + (int64_t)h * total + b0;
+    uint8_t* t = tiers + (int64_t)h * total + b0;
+    for (int64_t p = threadIdx.x; p < N; p += blockDim.x) {
+      const int code = level_code(s[p], N, p, W, K, a0, (double)am0, (double)am1, aL, rule);
+      t[p] = (uint8_t)code;
+#pragma unroll
+      for (int l = 0; l < 4; l++) n[l] += l < K && code == K - l;
+    }
+  }
+  __shared__ int red[4][16];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+  for (int l = 0; l < 4; l++) {
+    n[l] = wave_sum(n[l]);
+    if (lane == 0) red[l][wid] = n[l];
+  }
+  __syncthreads();
+  if (threadIdx.x < K) {
+    int x = 0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); w++) x += red[threadIdx.x][w];
+    cnt[threadIdx.x] = x;
+  }
+}
+
 hipError_t launch_classify(const Cfg& c, int batch, int64_t total, const int64_t* cu,
                            const float* scores, uint8_t* tiers, int32_t* counts, hipStream_t s) {
   if (batch == 0) return hipSuccess;
+  if (c.K >= 3) {
+    classify_levels_kernel<<<dim3(c.H, batch), dim3(1024), 0, s>>>(c.H, c.W, c.K, c.ah, c.al, c.amid[0], c.amid[1],
+                                                                   c.ah_head, c.al_head, c.prompt_rule, total, cu,
+                                                                   scores, tiers, counts);
+    return hipGetLastError();
+  }
   classify_kernel<<<dim3(c.H, batch), dim3(1024), 0, s>>>(c.H, c.W, c.lo_en, c.ah, c.al, c.ah_head, c.al_head,
                                                           c.prompt_rule, total, cu,
                                                           scores, tiers, counts);

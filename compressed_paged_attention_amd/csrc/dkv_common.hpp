@@ -105,6 +105,18 @@ struct Codec {
   int kb_hi, vb_hi, kb_lo, vb_lo;
 };
 
+// The plain layout of T tokens with K and V code widths kb, vb.
+__host__ __device__ inline Seg level_seg(int d, int T, int kb, int vb) {
+  const int kc = 0;
+  const int km = kc + r16(T * d * kb / 8);
+  const int vc = km + r16(4 * T);
+  const int vm = vc + r16(T * d * vb / 8);
+  const int sc = vm + r16(4 * T);
+  const int ps = sc + r16(4 * T);
+  const int end = ps + r16(4 * T);
+  return Seg{T, kb, vb, kc, km, vc, vm, sc, ps, end};
+}
+
 __host__ __device__ inline Seg plain_seg(int d, bool hi, const Codec& c) {
   const int T = hi ? kHiTokens : kLoTokens;
   const int kb = hi ? c.kb_hi : c.kb_lo, vb = hi ? c.vb_hi : c.vb_lo;

@@ -20,7 +20,30 @@ struct Cfg {
   bool plain;       // a tier codec variant: the plain layout (else the default K8V4 / K4V2 layout)
   Codec codec;      // its widths (the default pair when !plain)
   int page_bytes;   // bytes of one unified page under this codec
+  // precision levels: K = 2 (the two tiers) or 3, 4 (level 0 high .. K-1
+  // low, plain layout); table rows R = ceil(K/2) of L entries (row r: level
+  // 2r from the left, 2r+1 from the right); tier state 2K words per unit
+  int K, R, LT;     // LT = R * L entries per unit
+  float amid[2];    // thresholds of levels 1 .. K-2
+  Seg lv[4];        // page layout of each level
 };
+
+// The levels as the general kernels see them (passed by value).
+struct Levels {
+  int K, R, L;      // levels, table rows, row length
+  Seg s[4];
+  __host__ __device__ int entry(int l, int j) const { return (l >> 1) * L + ((l & 1) ? L - 1 - j : j); }
+  __host__ __device__ int T(int l) const { return l == 0 ? kHiTokens : kLoTokens; }
+};
+
+inline Levels levels_of(const Cfg& c) {
+  Levels v;
+  v.K = c.K;
+  v.R = c.R;
+  v.L = c.L;
+  for (int l = 0; l < 4; l++) v.s[l] = c.lv[l];
+  return v;
+}
 
 struct Pool {
   uint8_t* pages;

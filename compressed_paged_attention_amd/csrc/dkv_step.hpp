@@ -18,6 +18,15 @@ namespace dkv {
 // lo_src, the first high page), so the commit needs no table lookup.
 constexpr int kSRec = 12;
 enum { S_NEWHI = 0, S_HIAPP, S_LOSRC, S_LOSLOT, S_LOAPP, S_PAGE, S_IDH, S_IDL, S_IDS, S_IDF };
+// K precision levels: the level-0 slot of the new token, the appends per
+// level (bit l), the level of a new page (-1 none), the page (S_PAGE, as in
+// the two-tier record) and two token moves {on, source level, slot,
+// destination level, slot}: t_c or a level-0 victim leaving level 0, and a
+// victim of t_c's level moving further down.
+constexpr int kLRec = 16;
+enum { LS_NEW = 0, LS_APP, LS_NEED, LS_MV0 = 6, LS_MV1 = 11 };
+static_assert(S_PAGE == 5, "the level record keeps the page where the coordination kernel writes it");
+inline int rec_words(const Cfg& c) { return c.K >= 3 ? kLRec : kSRec; }
 enum { SH_COMMIT = 0, SH_START, SH_END, SH_D };
 constexpr int32_t kActive = 4;
 // Up to this many units every commit workgroup redoes the unit-order prefix
@@ -40,7 +49,7 @@ inline StepWs step_carve(const Cfg& c, int batch, void* ws) {
   w.hdr = (int64_t*)p;
   p += align_up(16 * sizeof(int64_t), 256);
   w.rec = (int32_t*)p;
-  p += align_up(U * kSRec * sizeof(int32_t), 256);
+  p += align_up(U * rec_words(c) * sizeof(int32_t), 256);
   w.nf = (int32_t*)p;
   p += align_up(U * sizeof(int32_t), 256);
   w.cw = (int32_t*)p;

@@ -67,9 +67,45 @@ static PromptWs carve(const Cfg& c, int batch, int64_t total, void* ws, size_t* 
   return w;
 }
 
+constexpr int kLRecP = 24;  // int64 fields per unit record (levels)
+enum { LP_K = 0, LP_KOFF, LP_FOFF, LP_EOFF, LP_POFF, LP_N, LP_BASE, LP_FLAGS, LP_A, LP_AIN, LP_RIN, LP_E,
+       LP_NL0, LP_NP0 = LP_NL0 + 4, LP_OFF0 = LP_NP0 + 4 };  // + per-level counts, pages, token offsets
+
+struct PromptLvWs {
+  int64_t* hdr;
+  int64_t* rec;
+  int32_t* chunks;  // [U][C][4] counts, then chunk offsets
+  int32_t* pos;     // [H][total]
+  int32_t* freed;   // [U * L]
+  int32_t* pmap;    // [U * LT]
+};
+
+static PromptLvWs carve_levels(const Cfg& c, int batch, int64_t total, void* ws, size_t* bytes) {
+  const int64_t U = (int64_t)batch * c.H;
+  const int C = num_chunks(c);
+  size_t off = 0;
+  PromptLvWs w;
+  uint8_t* b = (uint8_t*)ws;
+  w.hdr = (int64_t*)(b + off);
+  off = align_up(off + 16 * sizeof(int64_t), 256);
+  w.rec = (int64_t*)(b + off);
+  off = align_up(off + (size_t)U * kLRecP * sizeof(int64_t), 256);
+  w.chunks = (int32_t*)(b + off);
+  off = align_up(off + (size_t)U * C * 4 * sizeof(int32_t), 256);
+  w.pos = (int32_t*)(b + off);
+  off = align_up(off + (size_t)c.H * total * sizeof(int32_t), 256);
+  w.freed = (int32_t*)(b + off);
+  off = align_up(off + (size_t)U * c.L * sizeof(int32_t), 256);
+  w.pmap = (int32_t*)(b + off);
+  off = align_up(off + (size_t)U * c.LT * sizeof(int32_t), 256);
+  if (bytes) *bytes = off;
+  return w;
+}
+
 size_t prompt_workspace(const Cfg& c, int batch, int64_t total) {
   size_t n = 0;
-  carve(c, batch, total, nullptr, &n);
+  if (c.K >= 3) carve_levels(c, batch, total, nullptr, &n);
+  else carve(c, batch, total, nullptr, &n);
   return n;
 }
 
@@ -732,12 +768,394 @@ __global__ __launch_bounds__(256) void prompt_pack_kernel(int H, int L, int64_t 
   }
 }
 
+
+// ===========================================================================
+// K precision levels (DiffKV notes, "KV compression policy", extensibility;
+// "Memory management", generation workflow: extra levels by combining
+// unidirectional or bidirectional page tables).  The same five phases over
+// K = 3 or 4 levels:
+//   count   per-chunk counts of every level;
+//   plan    per unit: pages per level, the conservative block of ceil(N/16)
+//           pages, its use (levels 0, 2, 3 from the left end in that order,
+//           level 1 from the right end, the middle freed) and the pages it
+//           lacks (extras); scans over units; capacity; pointers;
+//   scatter slot -> position lists (levels contiguous in the unit's token
+//           range, each in position order) and the block's table entries;
+//   list    frees at the old reclamation pointer, extras after them, the
+//           page map;
+//   pack    one wave per page (persistent), as the plain packer.
+// A unit's pages in "Q order": level 0, 2, 3 pages (index order), then
+// level 1's innermost first; block page i serves Q position i (i < A'),
+// the right end serves level 1, positions between take extras.
+// ===========================================================================
+__global__ __launch_bounds__(256) void prompt_count_levels_kernel(int H, int K, int64_t total, int C,
+                                                                  const int64_t* __restrict__ cu,
+                                                                  const uint8_t* __restrict__ tiers,
+                                                                  int32_t* __restrict__ chunks) {
+  const int c = blockIdx.x;
+  const int64_t u = blockIdx.y;
+  const int r = (int)(u / H), h = (int)(u % H);
+  const int64_t b0 = cu[r], N = cu[r + 1] - b0;
+  const int64_t t0 = (int64_t)c * kChunk;
+  const int64_t t1 = N < t0 + kChunk ? N : t0 + kChunk;
+  int n[4] = {0, 0, 0, 0};
+  if (b0 >= 0 && N > 0 && cu[r + 1] <= total) {
+    const uint8_t* t = tiers + (int64_t)h * total + b0;
+    for (int64_t p = t0 + threadIdx.x; p < t1; p += blockDim.x) {
+      const int code = t[p];
+#pragma unroll
+      for (int l = 0; l < 4; l++) n[l] += l < K && code == K - l;  // (code 0: pruned)
+    }
+  }
+  __shared__ int red[4][4];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+  for (int l = 0; l < 4; l++) {
+    n[l] = wave_sum(n[l]);
+    if (lane == 0) red[l][wid] = n[l];
+  }
+  __syncthreads();
+  if (threadIdx.x < 4) chunks[(u * C + c) * 4 + threadIdx.x] = red[threadIdx.x][0] + red[threadIdx.x][1] +
+                                                                 red[threadIdx.x][2] + red[threadIdx.x][3];
+}
+
+__global__ __launch_bounds__(1024) void prompt_plan_levels_kernel(int H, int K, int L, int S_max, int batch, int C,
+                                                                  int64_t total, const int64_t* __restrict__ cu,
+                                                                  const int32_t* __restrict__ state,
+                                                                  int32_t* __restrict__ chunks,
+                                                                  int64_t* __restrict__ rec,
+                                                                  int64_t* __restrict__ hdr, uint64_t* ptr,
+                                                                  uint32_t* status) {
+  __shared__ int64_t lds[20];
+  __shared__ uint32_t sflags;
+  if (threadIdx.x == 0) sflags = 0;
+  __syncthreads();
+  const int64_t U = (int64_t)batch * H;
+  int64_t carry[4] = {0, 0, 0, 0};  // K, F, E, pages
+  for (int64_t base = 0; base < U; base += blockDim.x) {
+    const int64_t u = base + threadIdx.x;
+    int64_t k = 0, f = 0, e = 0, nq = 0, N = 0, b0 = 0, A = 0, Ain = 0, Rin = 0;
+    int64_t n[4] = {0, 0, 0, 0}, np[4] = {0, 0, 0, 0};
+    uint32_t flags = 0;
+    if (u < U) {
+      const int r = (int)(u / H);
+      b0 = cu[r];
+      const int64_t b1 = cu[r + 1];
+      N = b1 - b0;
+      if (b0 < 0 || N < 0 || b1 > total || (r == 0 && b0 != 0)) {
+        flags |= kStBadState;
+        N = 0;
+      } else if (N > 0) {
+        for (int w = 0; w < 2 * K; w++)
+          if (state[u * 2 * K + w]) flags |= kStBadState;
+        if (N > S_max) {
+          flags |= kStOverflow;
+        } else {
+          for (int c = 0; c < C; c++) {
+            int32_t* ch = chunks + (u * C + c) * 4;
+#pragma unroll
+            for (int l = 0; l < 4; l++) {
+              const int32_t a = ch[l];
+              ch[l] = (int32_t)n[l];
+              n[l] += a;
+            }
+          }
+          int64_t sum = 0;
+#pragma unroll
+          for (int l = 0; l < 4; l++) {
+            np[l] = cdiv(n[l], l == 0 ? kHiTokens : kLoTokens);
+            sum += n[l];
+          }
+          k = cdiv(N, kHiTokens);
+          if (sum > N) flags |= kStBadState;
+          if (k > L || np[0] + np[1] > L || np[2] + np[3] > L) flags |= kStOverflow;
+          A = np[0] + np[2] + np[3];
+          Ain = A < k ? A : k;
+          Rin = np[1] < k - Ain ? np[1] : k - Ain;
+          f = k - Ain - Rin;
+          e = (A - Ain) + (np[1] - Rin);
+          nq = A + np[1];
+        }
+      }
+    }
+    if (flags) atomicOr(&sflags, flags);
+    int64_t tot[4];
+    const int64_t ok = block_excl_scan(k, lds, tot[0]);
+    const int64_t of = block_excl_scan(f, lds, tot[1]);
+    const int64_t oe = block_excl_scan(e, lds, tot[2]);
+    const int64_t op = block_excl_scan(nq, lds, tot[3]);
+    if (u < U) {
+      int64_t* R = rec + u * kLRecP;
+      R[LP_K] = k;
+      R[LP_KOFF] = carry[0] + ok;
+      R[LP_FOFF] = carry[1] + of;
+      R[LP_EOFF] = carry[2] + oe;
+      R[LP_POFF] = carry[3] + op;
+      R[LP_N] = N;
+      R[LP_BASE] = b0;
+      R[LP_FLAGS] = flags;
+      R[LP_A] = A;
+      R[LP_AIN] = Ain;
+      R[LP_RIN] = Rin;
+      R[LP_E] = e;
+      int64_t o = 0;
+      for (int l = 0; l < 4; l++) {
+        R[LP_NL0 + l] = n[l];
+        R[LP_NP0 + l] = np[l];
+        R[LP_OFF0 + l] = o;
+        o += n[l];
+      }
+    }
+    for (int i = 0; i < 4; i++) carry[i] += tot[i];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint64_t start = ptr[0], end = ptr[1];
+    const int64_t free0 = (int64_t)(end - start);
+    uint32_t st = sflags;
+    const int64_t Kt = carry[0], F = carry[1], E = carry[2];
+    if (!st && (Kt > free0 || Kt - F + E > free0)) st |= kStExhausted;
+    hdr[H_K] = Kt;
+    hdr[H_F] = F;
+    hdr[H_E] = E;
+    hdr[H_START] = (int64_t)start;
+    hdr[H_END] = (int64_t)end;
+    hdr[H_PAGES] = carry[3];
+    hdr[H_COMMIT] = st == 0;
+    if (st) {
+      atomicOr(status, st);
+    } else {
+      ptr[0] = start + (uint64_t)(Kt + E);
+      ptr[1] = end + (uint64_t)F;
+    }
+  }
+}
+
+// (level, page index) of Q position i of a unit (record R)
+__device__ inline void lv_q_page(const int64_t* R, int64_t i, int& l, int64_t& j) {
+  const int64_t p0 = R[LP_NP0], p1 = R[LP_NP0 + 1], p2 = R[LP_NP0 + 2], p3 = R[LP_NP0 + 3];
+  if (i < p0) { l = 0; j = i; return; }
+  i -= p0;
+  if (i < p2) { l = 2; j = i; return; }
+  i -= p2;
+  if (i < p3) { l = 3; j = i; return; }
+  i -= p3;
+  l = 1;
+  j = p1 - 1 - i;  // level 1 innermost first
+}
+
+__global__ __launch_bounds__(256) void prompt_scatter_levels_kernel(int H, int K, int L, int LT, int C,
+                                                                    int64_t total, int64_t P,
+                                                                    const uint8_t* __restrict__ tiers,
+                                                                    const int64_t* __restrict__ hdr,
+                                                                    const int64_t* __restrict__ rec,
+                                                                    const int32_t* __restrict__ chunks,
+                                                                    const int32_t* __restrict__ list,
+                                                                    int32_t* __restrict__ pos_list,
+                                                                    int32_t* __restrict__ freed,
+                                                                    int32_t* __restrict__ table,
+                                                                    int32_t* __restrict__ state) {
+  if (!hdr[H_COMMIT]) return;
+  const int c = blockIdx.x;
+  const int64_t u = blockIdx.y;
+  const int h = (int)(u % H);
+  const int64_t* R = rec + u * kLRecP;
+  const int64_t N = R[LP_N], b0 = R[LP_BASE];
+  if (N <= 0) return;
+  const int64_t t0 = (int64_t)c * kChunk;
+  if (t0 < N) {
+    const uint8_t* t = tiers + (int64_t)h * total + b0;
+    constexpr int kPer = kChunk / 256;
+    const int64_t p0 = t0 + (int64_t)threadIdx.x * kPer;
+    uint8_t v[kPer];
+    int cnt[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < kPer; i++) {
+      const int64_t p = p0 + i;
+      v[i] = p < N ? t[p] : (uint8_t)0;
+#pragma unroll
+      for (int l = 0; l < 4; l++) cnt[l] += l < K && v[i] == K - l;  // (code 0: pruned)
+    }
+    __shared__ int lds[20];
+    int base[4];
+#pragma unroll
+    for (int l = 0; l < 4; l++) {
+      int tl;
+      base[l] = block_excl_scan(cnt[l], lds, tl) + chunks[(u * C + c) * 4 + l] + (int)R[LP_OFF0 + l];
+    }
+    int32_t* pl = pos_list + (int64_t)h * total + b0;
+#pragma unroll
+    for (int i = 0; i < kPer; i++) {
+      const int code = v[i];
+      if (code >= 1 && code <= K) {
+        // (a bitwise select keeps base[] in registers)
+        const int l = K - code;
+        const int s = l == 0 ? base[0]++ : l == 1 ? base[1]++ : l == 2 ? base[2]++ : base[3]++;
+        pl[s] = (int32_t)(p0 + i);
+      }
+    }
+  }
+  if (c == 0) {
+    const int64_t k = R[LP_K], Ain = R[LP_AIN], Rin = R[LP_RIN], A = R[LP_A], p1 = R[LP_NP0 + 1];
+    const uint64_t start = (uint64_t)hdr[H_START] + (uint64_t)R[LP_KOFF];
+    int32_t* row = table + u * LT;
+    for (int64_t i = threadIdx.x; i < k; i += blockDim.x) {
+      const int32_t id = list[(start + (uint64_t)i) % (uint64_t)P];
+      int64_t q = -1;
+      if (i < Ain) q = i;                              // left end
+      else if (i >= k - Rin) q = A + (i - (k - p1));   // right end: level 1
+      if (q >= 0) {
+        int l;
+        int64_t j;
+        lv_q_page(R, q, l, j);
+        row[(l >> 1) * L + ((l & 1) ? L - 1 - j : j)] = id;
+      } else {
+        freed[R[LP_FOFF] + (i - Ain)] = id;
+      }
+    }
+    if (threadIdx.x < 2 * K) {
+      const int w = threadIdx.x;
+      state[u * 2 * K + w] = (int32_t)(w < K ? R[LP_NL0 + w] : R[LP_NP0 + (w - K)]);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void prompt_list_levels_kernel(int L, int LT, int64_t P,
+                                                                 const int64_t* __restrict__ hdr,
+                                                                 const int64_t* __restrict__ rec,
+                                                                 const int32_t* __restrict__ freed, int32_t* list,
+                                                                 int32_t* __restrict__ table,
+                                                                 int32_t* __restrict__ pmap) {
+  if (!hdr[H_COMMIT]) return;
+  const int64_t u = blockIdx.x;
+  const int64_t* R = rec + u * kLRecP;
+  if (R[LP_N] <= 0) return;
+  const int64_t k = R[LP_K], Ain = R[LP_AIN], Rin = R[LP_RIN], A = R[LP_A], e = R[LP_E];
+  const int64_t nq = A + R[LP_NP0 + 1];
+  for (int64_t i = threadIdx.x; i < nq; i += blockDim.x) pmap[R[LP_POFF] + i] = (int32_t)u;
+  const int64_t f = k - Ain - Rin;
+  const uint64_t end0 = (uint64_t)hdr[H_END];
+  for (int64_t i = threadIdx.x; i < f; i += blockDim.x)
+    list[(end0 + (uint64_t)(R[LP_FOFF] + i)) % (uint64_t)P] = freed[R[LP_FOFF] + i];
+  // extras after the frees: the left part's first, then level 1's (the
+  // frees being appended now are read from their own array)
+  for (int64_t x = threadIdx.x; x < e; x += blockDim.x) {
+    const uint64_t li = (uint64_t)hdr[H_START] + (uint64_t)hdr[H_K] + (uint64_t)(R[LP_EOFF] + x);
+    const int32_t id = li < end0 ? list[li % (uint64_t)P] : freed[li - end0];
+    const int64_t q = x < A - Ain ? Ain + x : A + (x - (A - Ain));
+    int l;
+    int64_t j;
+    lv_q_page(R, q, l, j);
+    table[u * LT + (l >> 1) * L + ((l & 1) ? L - 1 - j : j)] = id;
+  }
+}
+
+// Persistent: each wave packs pages item = w, w + nw, ... (the call's TP
+// pages in unit order, each unit's in Q order).
+template <int D>
+__global__ __launch_bounds__(256) void prompt_pack_levels_kernel(int H, int L, int LT, int64_t total, int64_t P,
+                                                                 int page_bytes, Levels lv,
+                                                                 const int64_t* __restrict__ hdr,
+                                                                 const int64_t* __restrict__ rec,
+                                                                 const int32_t* __restrict__ pmap,
+                                                                 const int32_t* __restrict__ pos_list,
+                                                                 const int32_t* __restrict__ table,
+                                                                 const uint16_t* __restrict__ k,
+                                                                 const uint16_t* __restrict__ v,
+                                                                 const float* __restrict__ scores,
+                                                                 uint8_t* __restrict__ pages, uint32_t* status) {
+  if (!hdr[H_COMMIT]) return;
+  const int64_t TP = hdr[H_PAGES];
+  constexpr int NA = D / 8;
+  const int lane = threadIdx.x & 63;
+  const int a = lane % NA, g = lane / NA;
+  const bool act = g < 4;
+  const int64_t nw = (int64_t)gridDim.x * (blockDim.x >> 6);
+  const int64_t w = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  for (int64_t item = w; item < TP; item += nw) {
+    const int u = __builtin_amdgcn_readfirstlane(pmap[item]);
+    const int64_t* R = rec + (int64_t)u * kLRecP;
+    const int h = u % H;
+    int l;
+    int64_t j;
+    lv_q_page(R, item - R[LP_POFF], l, j);
+    const int T = l == 0 ? kHiTokens : kLoTokens;
+    const int64_t n_l = R[LP_NL0 + l], slot0 = j * T;
+    const int valid = (int)(n_l - slot0 < T ? n_l - slot0 : T);
+    const int64_t N = R[LP_N], b0 = R[LP_BASE];
+    const int32_t id = table[(int64_t)u * LT + (l >> 1) * L + ((l & 1) ? L - 1 - j : j)];
+    const int32_t* pl = pos_list + (int64_t)h * total + b0 + R[LP_OFF0 + l];
+    int32_t pos[2][4];
+#pragma unroll
+    for (int th = 0; th < 2; th++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const int t = 16 * th + 4 * g + r;
+        pos[th][r] = pl[slot0 + ((act && t < valid) ? t : 0)];
+      }
+    u32x4 kr[2][4], vr[2][4];
+    float mean[2][4];
+    const float* sc = scores + (int64_t)h * total + b0;
+#pragma unroll
+    for (int th = 0; th < 2; th++) {
+      if (th == 1 && l == 0) break;
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const int64_t row = ((b0 + pos[th][r]) * H + h) * D + 8 * a;
+        kr[th][r] = __builtin_nontemporal_load((const u32x4*)(k + row));
+        vr[th][r] = __builtin_nontemporal_load((const u32x4*)(v + row));
+        mean[th][r] = sc[pos[th][r]];
+      }
+    }
+    if (id < 0 || id >= P) {
+      if (lane == 0) atomicOr(status, kStBadState);
+      continue;
+    }
+    uint8_t* pg = pages + (int64_t)id * page_bytes;
+    if (l == 0) pack_compute_plain<D, true>(pg, lane, valid, N, pos, kr, vr, mean, lv.s[0], page_bytes);
+    else pack_compute_plain<D, false>(pg, lane, valid, N, pos, kr, vr, mean, lv.s[l], page_bytes);
+  }
+}
+
+static hipError_t launch_prompt_levels(const Cfg& c, const Pool& p, int batch, int64_t total, const int64_t* cu,
+                                       const uint16_t* k, const uint16_t* v, const float* scores,
+                                       const uint8_t* tiers, int32_t* table, int32_t* state, void* ws,
+                                       hipStream_t s) {
+  const int64_t U = (int64_t)batch * c.H;
+  PromptLvWs w = carve_levels(c, batch, total, ws, nullptr);
+  const int C = num_chunks(c);
+  prompt_count_levels_kernel<<<dim3(C, (unsigned)U), dim3(256), 0, s>>>(c.H, c.K, total, C, cu, tiers, w.chunks);
+  prompt_plan_levels_kernel<<<dim3(1), dim3(1024), 0, s>>>(c.H, c.K, c.L, c.S_max, batch, C, total, cu, state,
+                                                           w.chunks, w.rec, w.hdr, p.ptr, p.status);
+  prompt_scatter_levels_kernel<<<dim3(C, (unsigned)U), dim3(256), 0, s>>>(c.H, c.K, c.L, c.LT, C, total, p.P,
+                                                                          tiers, w.hdr, w.rec, w.chunks, p.list,
+                                                                          w.pos, w.freed, table, state);
+  prompt_list_levels_kernel<<<dim3((unsigned)U), dim3(256), 0, s>>>(c.L, c.LT, p.P, w.hdr, w.rec, w.freed, p.list,
+                                                                    table, w.pmap);
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)(4 * (cus > 0 ? cus : 1)));
+  const Levels lv = levels_of(c);
+  if (c.d == 128)
+    prompt_pack_levels_kernel<128><<<grid, dim3(256), 0, s>>>(c.H, c.L, c.LT, total, p.P, p.page_bytes, lv, w.hdr,
+                                                              w.rec, w.pmap, w.pos, table, k, v, scores, p.pages,
+                                                              p.status);
+  else
+    prompt_pack_levels_kernel<64><<<grid, dim3(256), 0, s>>>(c.H, c.L, c.LT, total, p.P, p.page_bytes, lv, w.hdr,
+                                                             w.rec, w.pmap, w.pos, table, k, v, scores, p.pages,
+                                                             p.status);
+  return hipGetLastError();
+}
+
 hipError_t launch_prompt(const Cfg& c, const Pool& p, int batch, int64_t total, const int64_t* cu,
                          const uint16_t* k, const uint16_t* v, const float* scores,
                          const uint8_t* tiers, int32_t* table, int32_t* state, void* ws,
                          hipStream_t s) {
   const int64_t U = (int64_t)batch * c.H;
   if (U == 0) return hipSuccess;
+  if (c.K >= 3) return launch_prompt_levels(c, p, batch, total, cu, k, v, scores, tiers, table, state, ws, s);
   PromptWs w = carve(c, batch, total, ws, nullptr);
   const int C = num_chunks(c);
   prompt_count_kernel<<<dim3(C, (unsigned)U), dim3(256), 0, s>>>(c.H, total, C, cu, tiers, w.chunks);

@@ -87,6 +87,28 @@ typedef struct {
    * decode step is the STEP followed by the attention (chain is ignored) and
    * no next-step plan records are kept (a STEP always scans the unit). */
   int32_t hi_k_bits, hi_v_bits, lo_k_bits, lo_v_bits;
+  /* More than two precision levels ("KV compression policy", extensibility
+   * paragraph; "Memory management", generation workflow: extra levels by
+   * combining unidirectional or bidirectional page tables).  num_levels K:
+   * 0 or 2 = the two tiers above; 3 or 4 = levels 0 (most precise) .. K-1:
+   *   level 0: alpha_h, hi bits, 16 tokens per page;
+   *   levels 1 .. K-2: alpha_mid[l-1], mid_k_bits / mid_v_bits[l-1], 32 tokens;
+   *   level K-1: alpha_l, lo bits, 32 tokens.
+   * All of the used widths must be given (plain layout), lo_enabled = 1, and
+   * alpha_h >= alpha_mid[0] (>= alpha_mid[1]) >= alpha_l (per-head arrays
+   * replace alpha_h and alpha_l per head and must keep that order; the
+   * middle thresholds are shared).  A token is in the first level l < K-1
+   * with mean * N > alpha_l, else in level K-1 if mean * N >= alpha_{K-1},
+   * else pruned; the window is level 0.  The page table has R = ceil(K/2)
+   * rows per unit (row r: level 2r from the left, level 2r+1 from the
+   * right); the tier state has 2K words per unit (token counts n_0..n_{K-1},
+   * then page counts); the prompt's block feeds levels 0, 2, 3 from its left
+   * end and level 1 from its right end; a generation step moves at most t_c
+   * and one victim down (see diffkv_compact).  Per-page key bounds and page
+   * scores refuse K >= 3 (DIFFKV_E_INVALID). */
+  int32_t num_levels;
+  float alpha_mid[2];
+  int32_t mid_k_bits[2], mid_v_bits[2];
 } diffkv_config;
 
 enum { DIFFKV_RULE_ALPHA_N = 0, DIFFKV_RULE_ALPHA_I = 1 };
@@ -129,8 +151,13 @@ enum { DIFFKV_IMP_CAUSAL = 0, DIFFKV_IMP_PROBE = 1 };
  * d = 128, 2048 at d = 64; -1 for an invalid config. */
 int32_t diffkv_page_bytes(const diffkv_config* cfg);
 
-/* Entries per page-table row, ceil(max_seq_len / 16) + 1; -1 if invalid. */
+/* Page-table entries per unit: R rows of ceil(max_seq_len / 16) + 1 (R = 1
+ * for the two tiers, ceil(K / 2) with K precision levels); -1 if invalid. */
 int32_t diffkv_table_len(const diffkv_config* cfg);
+
+/* int32 words of tier state per unit: 2K (4 for the two tiers); -1 if
+ * invalid. */
+int32_t diffkv_state_words(const diffkv_config* cfg);
 
 /* Device scratch needed by one call of `op` (DIFFKV_PROMPT / STEP / RELEASE
  * for diffkv_compact, DIFFKV_ATTN or DIFFKV_ATTN_SCORES for
@@ -146,8 +173,8 @@ size_t diffkv_workspace_bytes(const diffkv_config* cfg, int32_t op, int32_t batc
 /* Fills free_list with 0..num_pages-1, ptr = {0, num_pages}, status = 0. */
 int diffkv_pool_init(const diffkv_config* cfg, const diffkv_pool* pool, void* stream);
 
-/* Resets `batch` requests to empty: page_table [batch, H, L] = -1,
- * tier_state [batch, H, 4] = 0. */
+/* Resets `batch` requests to empty: page_table [batch, H, table_len] = -1,
+ * tier_state [batch, H, state_words] = 0. */
 int diffkv_state_init(const diffkv_config* cfg, int32_t batch, int32_t* page_table,
                       int32_t* tier_state, void* stream);
 
@@ -223,12 +250,14 @@ int diffkv_page_scores(const diffkv_config* cfg, const diffkv_pool* pool, int32_
 /* Token classification ("Approach"; "KV compression policy", prompt phase).
  *  cu_seqlens  int64 [batch+1], cu[0] = 0, non-decreasing; N_r = cu[r+1]-cu[r]
  *  scores      fp32 [H, cu[batch]]: per token its mean received attention
- *  tiers       uint8 [H, cu[batch]] out: 2 high, 1 low, 0 pruned.  The last
+ *  tiers       uint8 [H, cu[batch]] out: 2 high, 1 low, 0 pruned (K levels:
+ *              K - level, 0 pruned).  The last
  *              W tokens of each request are high; otherwise s*N_r (with
  *              prompt_rule = DIFFKV_RULE_ALPHA_I: s*(p+1) for position p) is
  *              compared with the KV head's alpha_h and alpha_l exactly (fp64,
  *              no division).
- *  tier_counts int32 [batch, H, 2] out: (high count, low count). */
+ *  tier_counts int32 [batch, H, 2] out: (high count, low count) (K levels:
+ *              [batch, H, K], one count per level). */
 int diffkv_classify(const diffkv_config* cfg, int32_t batch, int64_t total_tokens,
                     const int64_t* cu_seqlens, const float* scores, uint8_t* tiers,
                     int32_t* tier_counts, void* stream);
@@ -269,6 +298,20 @@ int diffkv_classify(const diffkv_config* cfg, int32_t batch, int64_t total_token
  *   unit with an inconsistent page count, or whose used table entries hold
  *   a page id outside [0, num_pages), sets DIFFKV_ST_BAD_STATE and the call
  *   commits nothing.
+ * K precision levels (num_levels 3 or 4): page_table [batch, H, R * L] (row
+ *   r = level 2r from the left, level 2r+1 from the right), tier_state
+ *   [batch, H, 2K] (n_0..n_{K-1}, p_0..p_{K-1}); level l's slot s lives in
+ *   page s / T_l of that level (T_0 = 16, else 32).  PROMPT: the block of
+ *   ceil(N/16) pages feeds levels 0, 2, 3 (in that order) from its left end
+ *   and level 1 from its right end, the middle is reclaimed, pages the block
+ *   lacks are taken after the frees (levels 0, 2, 3, then level 1 innermost
+ *   first).  STEP: t_c's level l_c; l_c = 0: the least important non-window
+ *   level-0 token (t_c included) moves to its class's level or is pruned;
+ *   l_c >= 1: t_c moves to level l_c and the least important token of level
+ *   l_c (t_c included) moves down to its class's level or is pruned when
+ *   its class is below l_c; a removal and an insertion in one level share
+ *   the slot, otherwise the insertion appends.  RELEASE: row by row, the
+ *   left level's pages left to right, then the right level's right to left.
  * Unused pointer arguments of a mode may be NULL. */
 int diffkv_compact(const diffkv_config* cfg, const diffkv_pool* pool, int32_t mode,
                    int32_t batch, int64_t total_tokens, const int64_t* cu_seqlens,
@@ -384,7 +427,8 @@ int diffkv_decode_attn_noalloc(const diffkv_config* cfg, const diffkv_pool* pool
 /* Number of sequence splits (workgroups per unit) diffkv_decode_attn uses
  * for this config and batch; the workspace size depends on it.  1 when
  * batch * H >= 256; otherwise max(ceil(256 / (batch * H)), ceil(L / 256)),
- * at most L / 16 and 128 (L = diffkv_table_len).  A unit then takes its
+ * at most L / 16 and 128 (L = one table row: ceil(max_seq_len / 16) + 1).
+ * A unit then takes its
  * pages in chunks of max(ceil(pages / splits), 16), so units with many
  * retained pages use all splits and small ones few. */
 int32_t diffkv_attn_splits(const diffkv_config* cfg, int32_t batch);

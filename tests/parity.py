@@ -75,7 +75,7 @@ def assert_scores_close(g, st, what=""):
     """Score sums of every live slot within tolerance; everything else bit-exact."""
     gp = gpu_pages(g)
     live = live_pages(st.page_table)
-    from oracle import tier_layout, HI, LO
+    from oracle import level_layout, num_levels
     cfg = st.cfg
     first = first_pages(st.page_table)
     for p in live:
@@ -84,8 +84,8 @@ def assert_scores_close(g, st, what=""):
             a = masked(a, cfg)
         if np.array_equal(a, b):
             continue
-        for t in (HI, LO):
-            _, seg = tier_layout(cfg, t)
+        for lv in range(max(num_levels(cfg), 2)):  # the page's level: the one whose score segment explains it
+            _, seg = level_layout(cfg, lv)
             sa = a[seg[4]:seg[5]].view(np.float32)
             sb = b[seg[4]:seg[5]].view(np.float32)
             a2, b2 = a.copy(), b.copy()
