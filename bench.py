@@ -621,13 +621,17 @@ def side_timings(args, name, dk):
     return out
 
 
-CODEC_VARIANTS = ((4, 8, 2, 4), (8, 2, 4, 1))  # (K, V) high, (K, V) low: the ablation's K4V8/K2V4 and K8V2/K4V1
+# (K, V) high, (K, V) low: the ablation's K4V8/K2V4 and K8V2/K4V1; then three
+# precision levels K8V8 / K8V4 / K4V2 (thresholds alpha_h, 0.5, alpha_l)
+CODEC_VARIANTS = (((4, 8, 2, 4), {}), ((8, 2, 4, 1), {}),
+                  ((8, 8, 4, 2), dict(num_levels=3, alpha_mid=[0.5], mid_k_bits=[8], mid_v_bits=[4])))
 
 
 def codec_timings(args, name, dk):
-    """Tier codec variants (plain layout) at the workload's shape: decode
-    attention with the score update (diffkv_decode_attn) and the generation
-    step (diffkv_compact STEP) on the compacted cache; each a warmup call,
+    """Tier codec variants and three precision levels (plain layout) at the
+    workload's shape: decode attention with the score update
+    (diffkv_decode_attn) and the generation step (diffkv_compact STEP) on
+    the compacted cache; each a warmup call,
     then 8 calls timed with HIP events on a held stream (the steps advance
     the cache).  Algorithmic bytes of the attention: per retained token its
     K and V codes (d (b_K + b_V) / 8) and scale/zero words (8), 8 for the
@@ -638,9 +642,12 @@ def codec_timings(args, name, dk):
     from workloads import synth
     dev = torch.device("cuda:0")
     out = {"workload": WORKLOAD_NAMES.get(name, name)}
-    for codec in CODEC_VARIANTS:
+    for codec, extra in CODEC_VARIANTS:
         hk, hv, lk, lv = codec
-        cfg = dict(synth.config(name), hi_k_bits=hk, hi_v_bits=hv, lo_k_bits=lk, lo_v_bits=lv)
+        cfg = dict(synth.config(name), hi_k_bits=hk, hi_v_bits=hv, lo_k_bits=lk, lo_v_bits=lv, **extra)
+        K = int(extra.get("num_levels", 2))
+        bits = [(hk, hv)] + [(a, b) for a, b in zip(extra.get("mid_k_bits", []), extra.get("mid_v_bits", []))]
+        bits += [(lk, lv)]
         B, H, G, d = cfg["batch"], cfg["num_kv_heads"], cfg["gqa_group"], cfg["head_dim"]
         lens = synth.seq_lens(cfg)
         P = synth.pool_pages(cfg, lens, dk.diffkv_page_bytes(cfg))
@@ -667,19 +674,19 @@ def codec_timings(args, name, dk):
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) * 1e3 / n
 
-        ts = st.tier_state.view(-1, 4).to(torch.int64).sum(0).tolist()
-        n_hi, n_lo, p_hi, p_lo = ts
-        nbytes = (n_hi * (d * (hk + hv) // 8 + 8) + n_lo * (d * (lk + lv) // 8 + 8) + 8 * (n_hi + n_lo)
-                  + 4 * (p_hi + p_lo) + B * H * G * d * (2 + 4))
+        ts = st.tier_state.view(-1, 2 * K).to(torch.int64).sum(0).tolist()
+        ntok, npg = ts[:K], ts[K:]
+        nbytes = (sum(ntok[l] * (d * (bits[l][0] + bits[l][1]) // 8 + 8 + 8) for l in range(K)) + 4 * sum(npg)
+                  + B * H * G * d * (2 + 4))
         us_attn = timed(lambda: st.decode_attn(dec["q"], seq, update_scores=1))
         seqs = [seq + i for i in range(n + 1)]  # each step one token further
         it = iter(seqs)
         us_step = timed(lambda: st.compact_step(next(it), dec["k_new"], dec["v_new"]))
         assert int(st.pool.status[0]) == 0, "codec variant step status"
         gbs = nbytes / (us_attn * 1e-6) / 1e9
-        out[f"K{hk}V{hv}_K{lk}V{lv}"] = {
+        out["_".join(f"K{a}V{b}" for a, b in bits)] = {
             "attn_us": us_attn, "step_us": us_step, "page_bytes": dk.diffkv_page_bytes(cfg),
-            "retained_hi_lo_tokens": [n_hi, n_lo],
+            "retained_tokens_per_level": ntok,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": gbs / PEAK_HBM_GBS, "kernel": "plain_attn_kernel + merge + plain_score_kernel",
                          "bytes_per_launch": int(nbytes)}}

@@ -62,35 +62,48 @@ PlainWs plain_carve(const Cfg& c, int batch, bool scores, void* ws, size_t* byte
   return w;
 }
 
-// A unit's levels: token counts n[l], page counts p[l] (state words l and
-// K + l), and their prefix sums (pages and slots of the levels before l).
+// A unit's levels: token counts n_l, page counts p_l (state words l and
+// K + l), and the prefix sums pp_l (pages) and np_l (slots) of the levels
+// before l, as scalars: looked up by a run-time level through selects (an
+// array indexed at run time would live in scratch memory).
 struct UnitLv {
-  int n[4], p[4], pp[5], np[5];
+  int n0, n1, n2, n3, pp1, pp2, pp3, pp4, np1, np2, np3, np4;
   bool ok;
+  __device__ int n(int l) const { return l == 0 ? n0 : l == 1 ? n1 : l == 2 ? n2 : n3; }
+  __device__ int pp(int l) const { return l == 0 ? 0 : l == 1 ? pp1 : l == 2 ? pp2 : l == 3 ? pp3 : pp4; }
+  __device__ int np(int l) const { return l == 0 ? 0 : l == 1 ? np1 : l == 2 ? np2 : l == 3 ? np3 : np4; }
 };
 
 __device__ inline UnitLv unit_levels(const int32_t* s, const Levels& lv) {
+  const int K = lv.K;
+  const int n0 = s[0], n1 = s[1], n2 = K > 2 ? s[2] : 0, n3 = K > 3 ? s[3] : 0;
+  const int p0 = s[K], p1 = s[K + 1], p2 = K > 2 ? s[K + 2] : 0, p3 = K > 3 ? s[K + 3] : 0;
   UnitLv x;
-  x.ok = true;
-  x.pp[0] = x.np[0] = 0;
-  for (int l = 0; l < 4; l++) {
-    x.n[l] = l < lv.K ? s[l] : 0;
-    x.p[l] = l < lv.K ? s[lv.K + l] : 0;
-    x.ok &= x.n[l] >= 0 && x.p[l] == (int)cdiv(x.n[l], lv.T(l));
-    x.pp[l + 1] = x.pp[l] + x.p[l];
-    x.np[l + 1] = x.np[l] + x.n[l];
-  }
-  x.ok &= x.p[0] + x.p[1] <= lv.L && x.p[2] + x.p[3] <= lv.L;
+  x.n0 = n0;
+  x.n1 = n1;
+  x.n2 = n2;
+  x.n3 = n3;
+  x.pp1 = p0;
+  x.pp2 = p0 + p1;
+  x.pp3 = p0 + p1 + p2;
+  x.pp4 = p0 + p1 + p2 + p3;
+  x.np1 = n0;
+  x.np2 = n0 + n1;
+  x.np3 = n0 + n1 + n2;
+  x.np4 = n0 + n1 + n2 + n3;
+  x.ok = n0 >= 0 && n1 >= 0 && n2 >= 0 && n3 >= 0 && p0 == (int)cdiv(n0, kHiTokens) &&
+         p1 == (int)cdiv(n1, kLoTokens) && p2 == (int)cdiv(n2, kLoTokens) && p3 == (int)cdiv(n3, kLoTokens) &&
+         p0 + p1 <= lv.L && p2 + p3 <= lv.L;
   return x;
 }
 
 // level of the unit's page j (pages in level order)
 __device__ inline int level_of_page(const UnitLv& x, int j) {
-  return j < x.pp[1] ? 0 : j < x.pp[2] ? 1 : j < x.pp[3] ? 2 : 3;
+  return j < x.pp1 ? 0 : j < x.pp2 ? 1 : j < x.pp3 ? 2 : 3;
 }
 // level of the unit's slot s (slots in level order)
 __device__ inline int level_of_slot(const UnitLv& x, int s) {
-  return s < x.np[1] ? 0 : s < x.np[2] ? 1 : s < x.np[3] ? 2 : 3;
+  return s < x.np1 ? 0 : s < x.np2 ? 1 : s < x.np3 ? 2 : 3;
 }
 
 // 16 codes of width B from a 2B-byte block (aligned to 2B bytes); code e at
@@ -320,7 +333,7 @@ __global__ __launch_bounds__(kPThreads) void plain_attn_kernel(int H, int G, int
   const UnitLv ux = unit_levels(state + 2 * lv.K * u, lv);
   const bool sok = ux.ok;
   if (!sok && split == 0 && tid == 0) atomicOr(status, kStBadState);
-  const int TPg = sok ? ux.pp[4] : 0;
+  const int TPg = sok ? ux.pp4 : 0;
   const int pps = split_pages(TPg, S);
   const int p0 = split * pps, p1 = min(TPg, p0 + pps);
   // the group's q heads (fp32, [d][GB]; heads G..GB-1 zero) and their sums
@@ -353,13 +366,13 @@ __global__ __launch_bounds__(kPThreads) void plain_attn_kernel(int H, int G, int
   // current page is computed.
   auto id_of = [&](int jj) {
     const int l = level_of_page(ux, jj);
-    return table[u * LT + lv.entry(l, jj - ux.pp[l])];
+    return table[u * LT + lv.entry(l, jj - ux.pp(l))];
   };
   auto ok_id = [&](int32_t id) { return id >= 0 && id < P; };
-  auto nv_of = [&](int l, int jt) { return min(lv.T(l), ux.n[l] - lv.T(l) * jt); };
+  auto nv_of = [&](int l, int jt) { return min(lv.T(l), ux.n(l) - lv.T(l) * jt); };
   auto load = [&](int jj, int32_t id, PageLd<D>& r) {
     const int l = level_of_page(ux, jj);
-    const int jt = jj - ux.pp[l];
+    const int jt = jj - ux.pp(l);
     const uint8_t* pg = pages + (int64_t)id * page_bytes;
     if (l == 0) plain_load<D, kHiTokens>(pg, lv.s[0], lane, nv_of(0, jt), r);
     else plain_load<D, kLoTokens>(pg, lv.s[l], lane, nv_of(l, jt), r);
@@ -379,9 +392,9 @@ __global__ __launch_bounds__(kPThreads) void plain_attn_kernel(int H, int G, int
       bad = true;
     } else {
       const int lev = level_of_page(ux, j);
-      const int jt = j - ux.pp[lev];
+      const int jt = j - ux.pp(lev);
       const int nv = nv_of(lev, jt);
-      const int slot0 = ux.np[lev] + lv.T(lev) * jt;
+      const int slot0 = ux.np(lev) + lv.T(lev) * jt;
       float* lg = keep_logits ? logits + u * G * LS + slot0 : nullptr;
       if (lev == 0) plain_page<D, kHiTokens, GB>(cur, lv.s[0], lane, nv, G, LS, lg, qs, qsum, scale_log2, pw, m, l, o, zs);
       else plain_page<D, kLoTokens, GB>(cur, lv.s[lev], lane, nv, G, LS, lg, qs, qsum, scale_log2, pw, m, l, o, zs);
@@ -453,10 +466,10 @@ __global__ __launch_bounds__(256) void plain_score_kernel(int H, int G, int LT, 
   const UnitLv ux = unit_levels(state + 2 * lv.K * u, lv);
   if (!ux.ok) return;
   const int s = blockIdx.x * 256 + threadIdx.x;
-  if (s >= ux.np[4]) return;
+  if (s >= ux.np4) return;
   if (!(ml[u * G * 2 + 1] > 0.0f)) return;  // bad unit
   const int lev = level_of_slot(ux, s);
-  const int ls = s - ux.np[lev], T = lv.T(lev);
+  const int ls = s - ux.np(lev), T = lv.T(lev);
   const int jt = ls / T, idx = ls % T;
   const int32_t id = table[u * LT + lv.entry(lev, jt)];
   if (id < 0 || id >= P) return;
