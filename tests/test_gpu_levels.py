@@ -213,3 +213,52 @@ def test_levels_refused_by_page_bounds(dk, orc):
     st = dk.DiffKVState(cfg, 1, 8, device=dev)
     with pytest.raises(dk.DiffKVError):
         st.page_bounds()
+
+
+@pytest.mark.parametrize("rule", [0, 1])
+def test_levels_per_head_thresholds_and_rule(dk, orc, rule):
+    """Three levels with per-KV-head outer thresholds (alpha_h and alpha_l
+    per head, the middle one shared) and both prompt rules (alpha/N, and
+    alpha/i for the i-th token): classification, prompt compaction and 12
+    steps with score updates, bit-exact."""
+    from workloads import synth
+    cfg = _levels_cfg(3, num_kv_heads=3, batch=4, max_seq_len=2500, window=16, prompt_rule=rule,
+                      alpha_h_head=[1.0, 1.2, 0.9], alpha_l_head=[0.75, 0.6, 0.8], alpha_h=9.0, alpha_l=0.0)
+    lens = torch.tensor([1200, 40, 900, 333], dtype=torch.int64)
+    pr = synth.make_prompt(cfg, lens=lens)
+    cu = pr["cu_seqlens"].numpy()
+    P = int(sum(-(-int(n) // 16) for n in lens) * 3 * 1.2) + 64
+    p = Pair(dk, orc, cfg, 4, P, int(cu[-1]))
+    _say(f"levels per head, rule {rule}: prompt")
+    p.prompt(cu, pr["k"].numpy(), pr["v"].numpy(), pr["scores"].numpy())
+    seq = lens.numpy().astype(np.int32)
+    for step in range(12):
+        dec = synth.make_decode(cfg, step)
+        p.step(seq, dec["k_new"].numpy(), dec["v_new"].numpy(), f"step {step}")
+        p.attend(dec["q"].numpy(), seq, True, f"attn {step}")
+        seq = seq + 1
+    check_pool_invariants(orc, p.o)
+
+
+def test_levels_noalloc_entry(dk, orc):
+    """The allocation-free decode attention on a three-level cache equals the
+    workspace entry point byte for byte (output and updated pages)."""
+    from workloads import synth
+    cfg = _levels_cfg(3, num_kv_heads=2, batch=3, max_seq_len=1200)
+    lens = torch.tensor([900, 130, 511], dtype=torch.int64)
+    pr = synth.make_prompt(cfg, lens=lens)
+    cu = pr["cu_seqlens"].numpy()
+    P = int(sum(-(-int(n) // 16) for n in lens) * 2 * 1.2) + 32
+    p = Pair(dk, orc, cfg, 3, P, int(cu[-1]))
+    p.prompt(cu, pr["k"].numpy(), pr["v"].numpy(), pr["scores"].numpy())
+    seq_d = torch.from_numpy(lens.numpy().astype(np.int32)).to(dev)
+    q = torch.from_numpy(synth.make_decode(cfg, 0)["q"].numpy()).to(dev)
+    pages0 = p.g.pool.pages.clone()
+    out_a = p.g.decode_attn(q, seq_d, update_scores=1)
+    pages_a = p.g.pool.pages.clone()
+    p.g.pool.pages.copy_(pages0)
+    out_b = torch.empty_like(out_a)
+    rc = dk.diffkv_decode_attn_noalloc(cfg, p.g.pool, 3, q, p.g.page_table, p.g.tier_state, seq_d, out_b, 1)
+    assert rc == dk.DIFFKV_OK
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_b) and torch.equal(pages_a, p.g.pool.pages)
