@@ -574,7 +574,6 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
     if (MODE == 1) load_page_sp<D>(R, pg, jj >= ph, lane);
   };
   PageRegs<D> A, B;
-  bool spec = false;  // A already holds page wid (loads issued before the verdict)
   WaveCommit<D> wc;
   if constexpr (STEP) {
     // with at most kWaveVerdictUnits units the committing wave takes the
@@ -603,10 +602,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
     id_src = R[S_IDS];
     id_first = R[S_IDF];
     need = wu & 3;
-    // the first page of waves 0-3 is page wid whatever the verdict, unless
-    // the step writes it: its loads need not wait for the verdict
-    spec = wid < 4 && wid < ph && wid != (new_hi >> 4) && state_ok(nh, nl, ph, pl, L);
-    if (spec) fetch_id(A, wid, id_guess, true);
+    // (no page load goes out before the verdict: issuing the first pages of
+    // waves 0-3 speculatively made the verdict's own loads wait behind them,
+    // 2 % slower steps)
     // the committing wave's loads, before the verdict (its unit asks for a
     // commit; the verdict may still refuse it)
     if (wid == kCW && (wu & kActive) && ((uint32_t)wu >> 8) == 0)
@@ -754,7 +752,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
   auto in_seq = [&](int x) { return x >= lo + off && x < hi && (x - lo - off) % stride == 0; };
   int n_w = lo + off < hi ? (hi - 1 - lo - off) / stride + 1 : 0;
   if (go) n_w -= (int)in_seq(jh) + (int)(jl >= 0 && in_seq(jl));
-  if (ja0 >= 0 && !committer && !(spec && ja0 == wid))
+  if (ja0 >= 0 && !committer)
     fetch_id(A, ja0, (ja0 == wid && ja0 < ph0) ? id_guess : row[table_idx(ja0)], true);
   if constexpr (STEP) {
     if (committer) {
