@@ -295,10 +295,12 @@ __device__ inline void block_logits(const float4_t& s, const uint32_t* kmw, int 
                                     float sq2, float kmul, float cq2, float* x) {
 #pragma unroll
   for (int r = 0; r < 4; r++) {
-    // log2e/sqrt(d) (s_k q.c + z_k sum(q))
+    // log2e/sqrt(d) (s_k q.c + z_k sum(q)); both fp16 factors enter
+    // mixed-precision fmas straight from the metadata word (z_k sq2 as an
+    // fma with a zero addend: one instruction, no conversion)
     const _Float16 ks = __builtin_bit_cast(_Float16, (uint16_t)kmw[r]);
     const _Float16 kz = __builtin_bit_cast(_Float16, (uint16_t)(kmw[r] >> 16));
-    x[r] = __builtin_fmaf((float)ks, __builtin_fmaf(s[r], kmul, -cq2), (float)kz * sq2);
+    x[r] = __builtin_fmaf((float)ks, __builtin_fmaf(s[r], kmul, -cq2), __builtin_fmaf((float)kz, sq2, 0.0f));
   }
   if (partial) {
 #pragma unroll
@@ -309,13 +311,15 @@ __device__ inline void block_logits(const float4_t& s, const uint32_t* kmw, int 
 
 // The reference check, once per page: lm is the lane's largest logit of the
 // page.  A column's maximum breaks the bound exactly when one of its lanes'
-// does, so the common case needs no cross-lane step; when some column breaks
-// it (rare), every column's reference moves to its maximum + kHead + kLazy
-// if that is higher, and the sums are rescaled.
+// does, so the common case needs no cross-lane step (ref_breaks); when some
+// column breaks it (rare), every column's reference moves to its maximum +
+// kHead + kLazy if that is higher, and the sums are rescaled (ref_move).
 template <int D>
-__device__ inline void ref_check(float lm, Softmax& sm, float4_t* acc) {
+__device__ inline bool ref_breaks(float lm, const Softmax& sm) { return __any(lm + kHead > sm.m); }
+template <int D>
+__device__ inline void ref_move(float lm, Softmax& sm, float4_t* acc) {
   constexpr int NB = D / 16;
-  if (__any(lm + kHead > sm.m)) {
+  {
     const float pm = rows_max(lm) + kHead;
     const float mn = pm > sm.m ? pm + kLazy : sm.m;
     const float alpha = __builtin_amdgcn_exp2f(sm.m - mn);
@@ -349,7 +353,7 @@ __device__ inline void block_pv(const float* x, const uint32_t* vmw, float mk, f
     const _Float16 vz = __builtin_bit_cast(_Float16, (uint16_t)(vmw[r] >> 16));
     sm.lsum = __builtin_fmaf(pk, ikv, sm.lsum);
     sm.zsum = __builtin_fmaf(pk, __builtin_fmaf((float)vz, ikv, -(float)vs), sm.zsum);
-    pp[r] = pk * (float)vs;
+    pp[r] = __builtin_fmaf(pk, (float)vs, 0.0f);  // a mixed-precision fma: no conversion of s_v
     asm("" : "+v"(pp[r]));
   }
   // Head and tail of each weight: the head is one conversion of the fp32
@@ -398,49 +402,64 @@ __device__ inline void compute_page(const PageRegs<D>& R, bool hi, int nval, con
                                     float sl, float tm, int qg, Softmax& sm, float4_t* acc, Keep keep) {
   constexpr int NS = D / 32, KW = PageRegs<D>::KW;
   if (hi) {
-    // two accumulators halve the dependent chain of the q.c products
-    float4_t s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = s0;
+    // one accumulator: dependent matrix instructions of one shape issue
+    // back to back (the chain costs no vector instructions)
+    float4_t s0 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int ks = 0; ks < NS; ks += 2) {
-      s0 = mfma32(cat8(u8x4(R.k[2 * ks]), u8x4(R.k[2 * ks + 1])), qop[ks], s0);
-      s1 = mfma32(cat8(u8x4(R.k[2 * ks + 2]), u8x4(R.k[2 * ks + 3])), qop[ks + 1], s1);
-    }
+    for (int ks = 0; ks < NS; ks++) s0 = mfma32(cat8(u8x4(R.k[2 * ks]), u8x4(R.k[2 * ks + 1])), qop[ks], s0);
     float x[4];
-    block_logits(s0 + s1, R.km, 4 * qg, nval, nval < kHiTokens, sq2, kTwo24 * sl, 0.0f, x);
+    block_logits(s0, R.km, 4 * qg, nval, nval < kHiTokens, sq2, kTwo24 * sl, 0.0f, x);
     keep(0, x);
-    ref_check<D>(max4(x), sm, acc);
-    block_pv<D, PACK>(x, R.vm, sm.m - 4.0f, 1.0f / 16.0f, tm, sm, acc, [&](int nb) {
-      // block nb: pairs 2nb (tokens 0, 1) and 2nb + 1 (tokens 2, 3)
-      const uint32_t w = R.v[nb >> 1];
-      const int sft = 8 * (nb & 1);
-      return cat(nib2(w, sft), nib2(w, sft + 4));
-    });
+    auto pv = [&]() {
+      block_pv<D, PACK>(x, R.vm, sm.m - 4.0f, 1.0f / 16.0f, tm, sm, acc, [&](int nb) {
+        // block nb: pairs 2nb (tokens 0, 1) and 2nb + 1 (tokens 2, 3)
+        const uint32_t w = R.v[nb >> 1];
+        const int sft = 8 * (nb & 1);
+        return cat(nib2(w, sft), nib2(w, sft + 4));
+      });
+    };
+    // each outcome of the reference check has its own products, so the
+    // accumulators are not copied to join the two paths
+    const float lm = max4(x);
+    if (ref_breaks<D>(lm, sm)) {
+      ref_move<D>(lm, sm, acc);
+      pv();
+    } else {
+      pv();
+    }
   } else {
     // both blocks' q.c products and logits first, then one reference check
     float x[2][4];
 #pragma unroll
     for (int mb = 0; mb < 2; mb++) {
-      float4_t s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = s0;
+      float4_t s0 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int ks = 0; ks < NS; ks += 2) {
+      for (int ks = 0; ks < NS; ks++) {
         // word w: dims 8w .. 8w + 7 as nibble pairs (0, 4), (1, 5), (2, 6), (3, 7)
-        const uint32_t w0 = R.k[KW * mb + ks], w1 = R.k[KW * mb + ks + 1];
+        const uint32_t w0 = R.k[KW * mb + ks];
         s0 = mfma32(cat8(cat(nib2(w0, 0), nib2(w0, 4)), cat(nib2(w0, 8), nib2(w0, 12))), qop[ks], s0);
-        s1 = mfma32(cat8(cat(nib2(w1, 0), nib2(w1, 4)), cat(nib2(w1, 8), nib2(w1, 12))), qop[ks + 1], s1);
       }
-      block_logits(s0 + s1, R.km + 4 * mb, 16 * mb + 4 * qg, nval, nval < 16 * (mb + 1), sq2, 16.0f * sl,
-                   16.0f * sq2, x[mb]);
+      block_logits(s0, R.km + 4 * mb, 16 * mb + 4 * qg, nval, nval < 16 * (mb + 1), sq2, 16.0f * sl, 16.0f * sq2,
+                   x[mb]);
       keep(mb, x[mb]);
     }
-    ref_check<D>(fmaxf(max4(x[0]), max4(x[1])), sm, acc);
+    auto pv = [&]() {
 #pragma unroll
-    for (int mb = 0; mb < 2; mb++) {
-      block_pv<D, PACK>(x[mb], R.vm + 4 * mb, sm.m - 2.0f, 0.25f, tm, sm, acc, [&](int nb) {
-        // block (nb, mb): pairs P = 2M, 2M + 1 with M = 2nb + mb, in word P / 8
-        const int M = 2 * nb + mb;
-        const int P0 = 2 * M, P1 = 2 * M + 1;
-        return cat(crumb2(R.v[P0 >> 3], 2 * (P0 & 7)), crumb2(R.v[P1 >> 3], 2 * (P1 & 7)));
-      });
+      for (int mb = 0; mb < 2; mb++) {
+        block_pv<D, PACK>(x[mb], R.vm + 4 * mb, sm.m - 2.0f, 0.25f, tm, sm, acc, [&](int nb) {
+          // block (nb, mb): pairs P = 2M, 2M + 1 with M = 2nb + mb, in word P / 8
+          const int M = 2 * nb + mb;
+          const int P0 = 2 * M, P1 = 2 * M + 1;
+          return cat(crumb2(R.v[P0 >> 3], 2 * (P0 & 7)), crumb2(R.v[P1 >> 3], 2 * (P1 & 7)));
+        });
+      }
+    };
+    const float lm = fmaxf(max4(x[0]), max4(x[1]));
+    if (ref_breaks<D>(lm, sm)) {
+      ref_move<D>(lm, sm, acc);
+      pv();
+    } else {
+      pv();
     }
   }
 }
