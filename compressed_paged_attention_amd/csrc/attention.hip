@@ -48,6 +48,7 @@ typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 8;              // waves per attention workgroup
 constexpr int kThreads = 64 * kWaves;
@@ -194,12 +195,13 @@ __device__ inline bool unit_ids(int ph, int pl, int L, int64_t P, const int32_t*
 // Registers of one page for one lane.  A page is read with the same loads
 // whatever its tier (tier offsets are scalar selects, not branches), so the
 // compiler keeps the following pages' loads in flight during a compute.
-template <int D>
+// E = the lane's tokens per 16-token block in the softmax layout (below).
+template <int D, int E>
 struct PageRegs {
   static constexpr int KW = D / 32;  // dwords per K load
   uint32_t k[2 * KW];  // high: 2*KW dwords of token i; low: KW of token i, KW of i+16
-  uint32_t km[8];      // K (scale, zero) words: tokens 4qg.. (low: and 16+4qg..)
-  uint32_t vm[8];      // V (scale, zero) words
+  uint32_t km[2 * E];  // K (scale, zero) words of the lane's softmax tokens (low: both blocks)
+  uint32_t vm[2 * E];  // V (scale, zero) words
   uint32_t v[KW];      // the lane's V chunk
   uint32_t sp;         // fused score update: lane < 32 score slot lane, else position slot lane - 32
   int32_t id;          // page id (wave-uniform)
@@ -214,36 +216,39 @@ __device__ inline void ldw(uint32_t* r, const uint8_t* p) {
   if constexpr (N == 4) {
     const u32x4_t a = __builtin_nontemporal_load((const u32x4_t*)p);
     r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
-  } else {
+  } else if constexpr (N == 2) {
     const u32x2_t a = __builtin_nontemporal_load((const u32x2_t*)p);
     r[0] = a[0]; r[1] = a[1];
+  } else {
+    r[0] = __builtin_nontemporal_load((const uint32_t*)p);
   }
 }
 
 // kb: lane K offset of the high tier (token i, dims qg*D/4); the low tier's
-// is kb/2 (token i) and kb/2 + 16*D/2 (token i + 16).  mq = 16 qg, vl = lane
-// chunk offset.  Metadata segments start at the same offset in both tiers.
-template <int D>
-__device__ inline void load_page(PageRegs<D>& R, const uint8_t* pg, bool lo, int kb, int mq, int vl) {
-  constexpr int KW = PageRegs<D>::KW;
+// is kb/2 (token i) and kb/2 + 16*D/2 (token i + 16).  mt = 4 x the lane's
+// first softmax token, vl = lane chunk offset.  Metadata segments start at
+// the same offset in both tiers.
+template <int D, int E>
+__device__ inline void load_page(PageRegs<D, E>& R, const uint8_t* pg, bool lo, int kb, int mt, int vl) {
+  constexpr int KW = PageRegs<D, E>::KW;
   constexpr Seg sh = tier_seg(D, true), sl = tier_seg(D, false);
   static_assert(sh.km == sl.km, "K metadata offsets differ between tiers");
   const int k0 = lo ? (kb >> 1) : kb;
   const int k1 = lo ? (kb >> 1) + 16 * (D / 2) : kb + 4 * KW;
   ldw<KW>(R.k, pg + k0);
   ldw<KW>(R.k + KW, pg + k1);
-  ldw<4>(R.km, pg + sh.km + mq);
-  ldw<4>(R.km + 4, pg + sh.km + mq + (lo ? 64 : 0));
+  ldw<E>(R.km, pg + sh.km + mt);
+  ldw<E>(R.km + E, pg + sh.km + mt + (lo ? 64 : 0));
   const int vm = lo ? sl.vm : sh.vm;
-  ldw<4>(R.vm, pg + vm + mq);
-  ldw<4>(R.vm + 4, pg + vm + mq + (lo ? 64 : 0));
+  ldw<E>(R.vm, pg + vm + mt);
+  ldw<E>(R.vm + E, pg + vm + mt + (lo ? 64 : 0));
   ldw<KW>(R.v, pg + (lo ? sl.vc : sh.vc) + vl);
 }
 
 // Score and position words of the page's 32 slots (high pages: slots 16..31
 // are other in-page bytes, never used).
-template <int D>
-__device__ inline void load_page_sp(PageRegs<D>& R, const uint8_t* pg, bool lo, int lane) {
+template <int D, int E>
+__device__ inline void load_page_sp(PageRegs<D, E>& R, const uint8_t* pg, bool lo, int lane) {
   constexpr Seg sh = tier_seg(D, true), sl = tier_seg(D, false);
   const int off = lane < 32 ? (lo ? sl.sc : sh.sc) + 4 * lane : (lo ? sl.ps : sh.ps) + 4 * (lane - 32);
   R.sp = __builtin_nontemporal_load((const uint32_t*)(pg + off));
@@ -273,6 +278,71 @@ __device__ inline float rows_sum(float v) {
   return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
+// The softmax layout.  The QK product leaves lane (i, qg) the logits of
+// tokens 4qg .. 4qg+3 of column i; with G <= 8 most of the 16 columns repeat
+// or carry nothing, so the per-element work (logit, weight, sums) would run
+// on 4 values per lane of which G/16 matter.  With GP = G rounded up to a
+// power of two (4, 8 or 16) and E = GP / 4, lane (i, qg) instead takes E
+// elements: head i & (GP-1), tokens 4qg + E (i / GP) + e.  The moves are DPP
+// row shifts restricted to the banks (groups of 4 lanes of a row) that
+// receive (`bank` mask); the weights go back to the matrix operand layout
+// (head columns 0..GP-1, their fp16 tails in columns GP..2GP-1) the same way.
+// E = 4 is the identity.
+constexpr int kRowShl = 0x100, kRowShr = 0x110;
+template <int CTRL, int BANK>
+__device__ inline float dpp_mov(float old, float src) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), CTRL, 0xF, BANK, false));
+}
+// lane i of a row takes element e from register E (i / GP) + e of lane i & (GP-1)
+template <int E>
+__device__ inline void spread(const float4_t& s, float* v) {
+  if constexpr (E == 4) {
+#pragma unroll
+    for (int r = 0; r < 4; r++) v[r] = s[r];
+  } else if constexpr (E == 2) {
+    v[0] = dpp_mov<kRowShr + 8, 0xC>(s[0], s[2]);
+    v[1] = dpp_mov<kRowShr + 8, 0xC>(s[1], s[3]);
+  } else {
+    float t = dpp_mov<kRowShr + 4, 0x2>(s[0], s[1]);
+    t = dpp_mov<kRowShr + 8, 0x4>(t, s[2]);
+    v[0] = dpp_mov<kRowShr + 12, 0x8>(t, s[3]);
+  }
+}
+// back to the operand layout: lane i (head column i < GP, or the tail column
+// of head i - GP) takes token r of its head from lane (i & (GP-1)) + GP (r / E),
+// element r % E (lanes of columns >= 2GP keep finite values of their own)
+template <int E>
+__device__ inline void gather(const float* pp, float* g) {
+  if constexpr (E == 4) {
+#pragma unroll
+    for (int r = 0; r < 4; r++) g[r] = pp[r];
+  } else if constexpr (E == 2) {
+    g[0] = dpp_mov<kRowShr + 8, 0xC>(pp[0], pp[0]);
+    g[1] = dpp_mov<kRowShr + 8, 0xC>(pp[1], pp[1]);
+    g[2] = dpp_mov<kRowShl + 8, 0x3>(pp[0], pp[0]);
+    g[3] = dpp_mov<kRowShl + 8, 0x3>(pp[1], pp[1]);
+  } else {
+    g[0] = dpp_mov<kRowShr + 4, 0x2>(pp[0], pp[0]);
+    g[1] = dpp_mov<kRowShl + 4, 0x1>(pp[0], pp[0]);
+    g[2] = dpp_mov<kRowShl + 4, 0x2>(dpp_mov<kRowShl + 8, 0x1>(pp[0], pp[0]), pp[0]);
+    g[3] = dpp_mov<kRowShl + 8, 0x2>(dpp_mov<kRowShl + 12, 0x1>(pp[0], pp[0]), pp[0]);
+  }
+}
+// a per-head value over the lanes of one row that hold the same head
+template <int E>
+__device__ inline float heads_max(float v) {
+  if constexpr (E <= 2) v = fmaxf(v, __shfl_xor(v, 8, 64));
+  if constexpr (E == 1) v = fmaxf(v, __shfl_xor(v, 4, 64));
+  return v;
+}
+template <int E>
+__device__ inline float heads_sum(float v) {
+  if constexpr (E <= 2) v += __shfl_xor(v, 8, 64);
+  if constexpr (E == 1) v += __shfl_xor(v, 4, 64);
+  return v;
+}
+
 // Reference of the online softmax.  Weights are p = 2^(x - m) for a
 // reference m the wave chooses; every sum (weights, the z term, the PV
 // accumulator) carries the same 2^-m, which the normalization removes, so m
@@ -280,82 +350,86 @@ __device__ inline float rows_sum(float v) {
 // p <= 1/4 and the fp16 operand p s_v kv stays below 4 s_v (high, kv = 16)
 // or s_v (low, kv = 4): finite for the scale of any vector of fp16 values
 // (range <= 131008, so s_v <= 8734 high, 43670 low).  It moves (to the page's
-// column max + kHead + kLazy) only when a page breaks that bound, so the
-// accumulators are rescaled rarely.
+// head max + kHead + kLazy) only when a page breaks that bound, so the
+// accumulators are rescaled rarely.  Every lane of a head holds its reference.
 constexpr float kHead = 2.0f;
 constexpr float kLazy = 4.0f;
 
-// One 16-token block in two halves.  block_logits: the block's logits
-// (masked on a partial page).  `s` holds q.c'' for tokens first..first+3 of
-// the page; `kmw` the K metadata words of those tokens.  sq2 = sum(q)
-// scale_log2 (per head).  K: c'' = c 2^-24 (high) or 1 + c/16 (low), so
-// q.c = 2^24 s or 16 (s - sum q) and
+// One 16-token block.  block_logits: the lane's E logits of the block
+// (masked on a partial page).  `v` holds q.c'' for in-page tokens
+// first..first+E-1 of the lane's head; `kmw` the K metadata words of those
+// tokens.  sq2 = sum(q) scale_log2 (of that head).  K: c'' = c 2^-24 (high)
+// or 1 + c/16 (low), so q.c = 2^24 s or 16 (s - sum q) and
 //   x = ks (s kmul - cq2) + kz sq2,  kmul = 2^24 sl or 16 sl, cq2 = 0 or 16 sq2.
-__device__ inline void block_logits(const float4_t& s, const uint32_t* kmw, int first, int nval, bool partial,
+template <int E>
+__device__ inline void block_logits(const float* v, const uint32_t* kmw, int first, int nval, bool partial,
                                     float sq2, float kmul, float cq2, float* x) {
 #pragma unroll
-  for (int r = 0; r < 4; r++) {
+  for (int e = 0; e < E; e++) {
     // log2e/sqrt(d) (s_k q.c + z_k sum(q)); both fp16 factors enter
     // mixed-precision fmas straight from the metadata word (z_k sq2 as an
     // fma with a zero addend: one instruction, no conversion)
-    const _Float16 ks = __builtin_bit_cast(_Float16, (uint16_t)kmw[r]);
-    const _Float16 kz = __builtin_bit_cast(_Float16, (uint16_t)(kmw[r] >> 16));
-    x[r] = __builtin_fmaf((float)ks, __builtin_fmaf(s[r], kmul, -cq2), __builtin_fmaf((float)kz, sq2, 0.0f));
+    const _Float16 ks = __builtin_bit_cast(_Float16, (uint16_t)kmw[e]);
+    const _Float16 kz = __builtin_bit_cast(_Float16, (uint16_t)(kmw[e] >> 16));
+    x[e] = __builtin_fmaf((float)ks, __builtin_fmaf(v[e], kmul, -cq2), __builtin_fmaf((float)kz, sq2, 0.0f));
   }
   if (partial) {
 #pragma unroll
-    for (int r = 0; r < 4; r++)
-      if (first + r >= nval) x[r] = -INFINITY;
+    for (int e = 0; e < E; e++)
+      if (first + e >= nval) x[e] = -INFINITY;
   }
 }
 
 // The reference check, once per page: lm is the lane's largest logit of the
-// page.  A column's maximum breaks the bound exactly when one of its lanes'
+// page.  A head's maximum breaks the bound exactly when one of its lanes'
 // does, so the common case needs no cross-lane step (ref_breaks); when some
-// column breaks it (rare), every column's reference moves to its maximum +
+// head breaks it (rare), every head's reference moves to its maximum +
 // kHead + kLazy if that is higher, and the sums are rescaled (ref_move).
-template <int D>
+// The accumulator columns of lane i belong to head i & (GP-1), the lane's
+// own softmax head, so its reference scales them.
 __device__ inline bool ref_breaks(float lm, const Softmax& sm) { return __any(lm + kHead > sm.m); }
-template <int D>
+template <int D, int E>
 __device__ inline void ref_move(float lm, Softmax& sm, float4_t* acc) {
   constexpr int NB = D / 16;
-  {
-    const float pm = rows_max(lm) + kHead;
-    const float mn = pm > sm.m ? pm + kLazy : sm.m;
-    const float alpha = __builtin_amdgcn_exp2f(sm.m - mn);
-    sm.lsum *= alpha;
-    sm.zsum *= alpha;
+  const float pm = heads_max<E>(rows_max(lm)) + kHead;
+  const float mn = pm > sm.m ? pm + kLazy : sm.m;
+  const float alpha = __builtin_amdgcn_exp2f(sm.m - mn);
+  sm.lsum *= alpha;
+  sm.zsum *= alpha;
 #pragma unroll
-    for (int nb = 0; nb < NB; nb++) acc[nb] *= alpha;
-    sm.m = mn;
-  }
+  for (int nb = 0; nb < NB; nb++) acc[nb] *= alpha;
+  sm.m = mn;
 }
 
-// block_pv: weights of the block's logits under the reference, their sums,
-// and the PV products.  `vmw` the V metadata words of the lane's tokens;
+// block_pv: weights of the lane's E logits under the reference, their sums,
+// and the PV products.  `vmw` the V metadata words of those tokens;
 // `vpair(nb)` the fp16 V operand of 16-dim block nb.
 // V: codes c'' = 1 + c/kv (kv = 16 high, 4 low) with operand p s_v kv, so
 //   sum p s_v kv c'' = sum p s_v c + sum p s_v kv, and the z term collects
 //   p (z_v - kv s_v).  The weights come as pk = p kv = 2^(x - mk) with
 //   mk = m - log2 kv, so pk s_v is the operand, the sums take pk / kv and
 //   the z term pk (z_v / kv - s_v).
-// PACK: column i + G carries the fp16 tail of head i's weights (one matrix
+// PACK: column GP + h carries the fp16 tail of head h's weights (one matrix
 // instruction per block instead of two); tm is 1 on those lanes, else 0.
-template <int D, bool PACK, typename VOp>
+template <int D, int E, bool PACK, typename VOp>
 __device__ inline void block_pv(const float* x, const uint32_t* vmw, float mk, float ikv, float tm, Softmax& sm,
                                 float4_t* acc, VOp vpair) {
   constexpr int NB = D / 16;
-  float pp[4];
+  float pe[E];
 #pragma unroll
-  for (int r = 0; r < 4; r++) {
-    const float pk = __builtin_amdgcn_exp2f(x[r] - mk);
-    const _Float16 vs = __builtin_bit_cast(_Float16, (uint16_t)vmw[r]);
-    const _Float16 vz = __builtin_bit_cast(_Float16, (uint16_t)(vmw[r] >> 16));
+  for (int e = 0; e < E; e++) {
+    const float pk = __builtin_amdgcn_exp2f(x[e] - mk);
+    const _Float16 vs = __builtin_bit_cast(_Float16, (uint16_t)vmw[e]);
+    const _Float16 vz = __builtin_bit_cast(_Float16, (uint16_t)(vmw[e] >> 16));
     sm.lsum = __builtin_fmaf(pk, ikv, sm.lsum);
     sm.zsum = __builtin_fmaf(pk, __builtin_fmaf((float)vz, ikv, -(float)vs), sm.zsum);
-    pp[r] = __builtin_fmaf(pk, (float)vs, 0.0f);  // a mixed-precision fma: no conversion of s_v
-    asm("" : "+v"(pp[r]));
+    pe[e] = __builtin_fmaf(pk, (float)vs, 0.0f);  // a mixed-precision fma: no conversion of s_v
+    asm("" : "+v"(pe[e]));
   }
+  float pp[4];
+  gather<E>(pe, pp);
+#pragma unroll
+  for (int r = 0; r < 4; r++) asm("" : "+v"(pp[r]));
   // Head and tail of each weight: the head is one conversion of the fp32
   // value (toward zero), the tail the exact remainder pp - head, converted
   // again, so head + tail = pp within 2^-21.  The head must be a single
@@ -390,28 +464,35 @@ __device__ inline void block_pv(const float* x, const uint32_t* vmw, float mk, f
   }
 }
 
-__device__ inline float max4(const float* x) { return fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])); }
+template <int E>
+__device__ inline float maxe(const float* x) {
+  float m = x[0];
+#pragma unroll
+  for (int e = 1; e < E; e++) m = fmaxf(m, x[e]);
+  return m;
+}
 
-// keep(mb, x): stores the 4 logits of 16-token block mb of the page.  The
-// q.c products use the K = 32 instruction: lane (i, qg) holds 8 dims of
+// keep(mb, x): stores the lane's E logits of 16-token block mb of the page.
+// The q.c products use the K = 32 instruction: lane (i, qg) holds 8 dims of
 // token i per step, the same 8 dims of q as its Q operand.  One reference
 // check per page (a low page's two blocks share it, so nothing branches
-// between their weights).
-template <int D, bool PACK, typename Keep>
-__device__ inline void compute_page(const PageRegs<D>& R, bool hi, int nval, const half8_t* qop, float sq2,
-                                    float sl, float tm, int qg, Softmax& sm, float4_t* acc, Keep keep) {
-  constexpr int NS = D / 32, KW = PageRegs<D>::KW;
+// between their weights).  ts = the lane's first softmax token in a block.
+template <int D, int E, bool PACK, typename Keep>
+__device__ inline void compute_page(const PageRegs<D, E>& R, bool hi, int nval, const half8_t* qop, float sq2,
+                                    float sl, float tm, int ts, Softmax& sm, float4_t* acc, Keep keep) {
+  constexpr int NS = D / 32, KW = PageRegs<D, E>::KW;
   if (hi) {
     // one accumulator: dependent matrix instructions of one shape issue
     // back to back (the chain costs no vector instructions)
     float4_t s0 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int ks = 0; ks < NS; ks++) s0 = mfma32(cat8(u8x4(R.k[2 * ks]), u8x4(R.k[2 * ks + 1])), qop[ks], s0);
-    float x[4];
-    block_logits(s0, R.km, 4 * qg, nval, nval < kHiTokens, sq2, kTwo24 * sl, 0.0f, x);
+    float v[E], x[E];
+    spread<E>(s0, v);
+    block_logits<E>(v, R.km, ts, nval, nval < kHiTokens, sq2, kTwo24 * sl, 0.0f, x);
     keep(0, x);
     auto pv = [&]() {
-      block_pv<D, PACK>(x, R.vm, sm.m - 4.0f, 1.0f / 16.0f, tm, sm, acc, [&](int nb) {
+      block_pv<D, E, PACK>(x, R.vm, sm.m - 4.0f, 1.0f / 16.0f, tm, sm, acc, [&](int nb) {
         // block nb: pairs 2nb (tokens 0, 1) and 2nb + 1 (tokens 2, 3)
         const uint32_t w = R.v[nb >> 1];
         const int sft = 8 * (nb & 1);
@@ -420,16 +501,16 @@ __device__ inline void compute_page(const PageRegs<D>& R, bool hi, int nval, con
     };
     // each outcome of the reference check has its own products, so the
     // accumulators are not copied to join the two paths
-    const float lm = max4(x);
-    if (ref_breaks<D>(lm, sm)) {
-      ref_move<D>(lm, sm, acc);
+    const float lm = maxe<E>(x);
+    if (ref_breaks(lm, sm)) {
+      ref_move<D, E>(lm, sm, acc);
       pv();
     } else {
       pv();
     }
   } else {
     // both blocks' q.c products and logits first, then one reference check
-    float x[2][4];
+    float x[2][E];
 #pragma unroll
     for (int mb = 0; mb < 2; mb++) {
       float4_t s0 = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -439,14 +520,16 @@ __device__ inline void compute_page(const PageRegs<D>& R, bool hi, int nval, con
         const uint32_t w0 = R.k[KW * mb + ks];
         s0 = mfma32(cat8(cat(nib2(w0, 0), nib2(w0, 4)), cat(nib2(w0, 8), nib2(w0, 12))), qop[ks], s0);
       }
-      block_logits(s0, R.km + 4 * mb, 16 * mb + 4 * qg, nval, nval < 16 * (mb + 1), sq2, 16.0f * sl, 16.0f * sq2,
-                   x[mb]);
+      float v[E];
+      spread<E>(s0, v);
+      block_logits<E>(v, R.km + E * mb, 16 * mb + ts, nval, nval < 16 * (mb + 1), sq2, 16.0f * sl, 16.0f * sq2,
+                      x[mb]);
       keep(mb, x[mb]);
     }
     auto pv = [&]() {
 #pragma unroll
       for (int mb = 0; mb < 2; mb++) {
-        block_pv<D, PACK>(x[mb], R.vm + 4 * mb, sm.m - 2.0f, 0.25f, tm, sm, acc, [&](int nb) {
+        block_pv<D, E, PACK>(x[mb], R.vm + E * mb, sm.m - 2.0f, 0.25f, tm, sm, acc, [&](int nb) {
           // block (nb, mb): pairs P = 2M, 2M + 1 with M = 2nb + mb, in word P / 8
           const int M = 2 * nb + mb;
           const int P0 = 2 * M, P1 = 2 * M + 1;
@@ -454,9 +537,9 @@ __device__ inline void compute_page(const PageRegs<D>& R, bool hi, int nval, con
         });
       }
     };
-    const float lm = fmaxf(max4(x[0]), max4(x[1]));
-    if (ref_breaks<D>(lm, sm)) {
-      ref_move<D>(lm, sm, acc);
+    const float lm = fmaxf(maxe<E>(x[0]), maxe<E>(x[1]));
+    if (ref_breaks(lm, sm)) {
+      ref_move<D, E>(lm, sm, acc);
       pv();
     } else {
       pv();
@@ -511,7 +594,7 @@ struct StepArgs {
   int32_t* cw_n;
 };
 
-template <int D, int MODE, bool PACK, bool STEP>
+template <int D, int MODE, int GP, bool STEP>
 __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int S, int64_t P, int page_bytes,
                                                         PolicyArgs pa, float scale_log2, const uint16_t* __restrict__ q,
                                                         const int32_t* __restrict__ table,
@@ -521,6 +604,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
                                                         float* __restrict__ ml, float* logits, uint32_t* status,
                                                         StepArgs sa, const int32_t* __restrict__ order) {
   constexpr bool SAVE = MODE != 0;
+  // GP: G rounded up to 4, 8 or 16; with GP <= 8 the heads' fp16 tails ride
+  // in columns GP .. 2GP-1 of the PV product (PACK), and the softmax runs on
+  // E = GP / 4 elements per lane
+  constexpr bool PACK = GP <= 8;
+  constexpr int E = GP / 4;
   constexpr int NB = D / 16;  // 16-dim blocks (N-blocks of PV)
   constexpr int NS = D / 32;  // 32-dim K-steps of QK
   constexpr int QD = D / 4;   // dims per lane group
@@ -536,7 +624,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
   // the query and the table entry of this wave's first page (a guess that
   // holds when the unit has more than wid high pages) go out first: neither
   // waits for the unit's state
-  const int qhead = i < G ? i : (PACK && i < 2 * G ? i - G : -1);
+  const int hs = i & (GP - 1);  // the lane's softmax head (and its columns' head)
+  const int qhead = (i < 2 * GP && hs < G && (PACK || i < GP)) ? hs : -1;
   uint4 qraw[QD / 8];
   {
     const uint4* src =
@@ -579,20 +668,23 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
   int need = 0, new_hi = 0, hi_app = 0, lo_src = -1, lo_slot = 0, lo_app = 0, rank = 0;
   int32_t id_hrow = 0, id_lrow = 0, id_src = 0, id_first = 0;
   int64_t start = 0;
-  const int kbase = i * D + qg * (D / 4), mq = 16 * qg, vl = lane * (D / 8);
+  // ts: the lane's first softmax token of a 16-token block (4 x it: its
+  // metadata words' offset)
+  const int ts = 4 * qg + E * (i / GP);
+  const int kbase = i * D + qg * (D / 4), mt = 4 * ts, vl = lane * (D / 8);
   uint32_t badid = 0;
   // page ids are checked where they are used (check: the id names a page of
   // the unit); a bad id is clamped into the pool (the load stays in bounds)
   // and zeroes the unit's result
-  auto fetch_id = [&](PageRegs<D>& R, int jj, int32_t id, bool check) {
+  auto fetch_id = [&](PageRegs<D, E>& R, int jj, int32_t id, bool check) {
     badid |= (uint32_t)(check && (id < 0 || id >= P));
     id = min(max(id, 0), (int32_t)(P - 1));
     R.id = id;
     const uint8_t* pg = pages + (int64_t)id * page_bytes;
-    load_page<D>(R, pg, jj >= ph, kbase, mq, vl);
-    if (MODE == 1) load_page_sp<D>(R, pg, jj >= ph, lane);
+    load_page<D, E>(R, pg, jj >= ph, kbase, mt, vl);
+    if (MODE == 1) load_page_sp<D, E>(R, pg, jj >= ph, lane);
   };
-  PageRegs<D> A, B;
+  PageRegs<D, E> A, B;
   WaveCommit<D> wc;
   if constexpr (STEP) {
     // with at most kWaveVerdictUnits units the committing wave takes the
@@ -762,7 +854,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
       while (j < hi && (j == jh || j == jl)) j += stride;
     return j < hi ? j : -1;
   };
-  auto fetch = [&](PageRegs<D>& R, int jj) {
+  auto fetch = [&](PageRegs<D, E>& R, int jj) {
     fetch_id(R, jj, row[table_idx(max(jj, 0))], true);  // uniform index: scalar load
   };
   const int ja0 = nextj(-1);
@@ -800,8 +892,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
   }
 
   // ---- Q operand: lane (i, qg) holds column i's head, dims qg*QD .. +QD-1;
-  // with PACK, columns G .. 2G-1 repeat heads 0 .. G-1 (their tails) ----
-  const bool tail = PACK && i >= G;
+  // with PACK, columns GP .. GP+G-1 repeat heads 0 .. G-1 (their tails) ----
+  const bool tail = PACK && i >= GP;
   half8_t qop[NS];
   float sumq = 0.0f;
   {
@@ -826,7 +918,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
     sumq += __shfl_xor(sumq, 16, 64);
     sumq += __shfl_xor(sumq, 32, 64);
   }
-  const float sq2 = sumq * scale_log2;
+  // sum(q) of the lane's softmax head (lanes of columns >= 2GP hold no q)
+  const float sq2c = sumq * scale_log2;
+  const float sq2 = PACK ? __shfl(sq2c, (lane & 48) | hs, 64) : sq2c;
   const float tm = tail ? 1.0f : 0.0f;
 
   Softmax sm{-INFINITY, 0.0f, 0.0f};
@@ -849,7 +943,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
   // per-block stores need no branch.
   auto page_loop = [&](auto lds_tag) {
     constexpr bool kLds = decltype(lds_tag)::value;
-    auto run = [&](PageRegs<D>& R, int j) {
+    auto run = [&](PageRegs<D, E>& R, int j) {
       if (kLds) {
         if (lane < 32) osc_s[j * 32 + lane] = __uint_as_float(R.sp);
         else pos_s[j * 32 + lane - 32] = (int32_t)R.sp;
@@ -858,18 +952,21 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
       // holds only the ids)
       if (MODE == 1 && lane == 0 && (kLds || ids_lds)) (kLds ? id_s : (int32_t*)lds_w)[j] = R.id;
       // logits: LDS g-major [G][TPg * 32]; workspace by table slot in the
-      // lanes' own order, [L][32/4][GS][4]: the four consecutive tokens a
-      // lane holds for one head are one 16-byte store, every lane below GS
-      // storing (lanes G..GS-1 hold finite values the score pass masks)
-      float* lgp = kLds ? lg_s + i * (TPg * 32) + j * 32 : logits + ((int64_t)u * L + table_idx(j)) * 32 * GS;
-      compute_page<D, PACK>(R, j < ph, valid(j), qop, sq2, scale_log2, tm, qg, sm, acc, [&](int mb, const float* x) {
-        if (!SAVE || i >= (kLds ? G : GS)) return;
-        const int t0 = 16 * mb + 4 * qg;
+      // lanes' own order, [L][32/4][GS][4] (GS = GP): the E consecutive
+      // tokens a lane holds for its head are one store, every lane storing
+      // (heads G..GS-1 hold finite values the score pass masks)
+      float* lgp = kLds ? lg_s + hs * (TPg * 32) + j * 32 : logits + ((int64_t)u * L + table_idx(j)) * 32 * GS;
+      compute_page<D, E, PACK>(R, j < ph, valid(j), qop, sq2, scale_log2, tm, ts, sm, acc, [&](int mb, const float* x) {
+        if (!SAVE || hs >= (kLds ? G : GS)) return;
+        const int t0 = 16 * mb + ts;
         if (kLds) {
 #pragma unroll
-          for (int r = 0; r < 4; r++) lgp[t0 + r] = x[r];
+          for (int e = 0; e < E; e++) lgp[t0 + e] = x[e];
         } else {
-          *(float4_t*)(lgp + ((t0 >> 2) * GS + i) * 4) = float4_t{x[0], x[1], x[2], x[3]};
+          float* dst = lgp + ((t0 >> 2) * GS + hs) * 4 + (t0 & 3);
+          if constexpr (E == 4) *(float4_t*)dst = float4_t{x[0], x[1], x[2], x[3]};
+          else if constexpr (E == 2) *(float2_t*)dst = float2_t{x[0], x[1]};
+          else *dst = x[0];
         }
       });
     };
@@ -906,8 +1003,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
           const int j = t == 0 ? jh : jl;
           if (j < 0) continue;
           const uint8_t* img = (const uint8_t*)(t == 0 ? img_h : img_l);
-          load_page<D>(A, img, j >= ph, kbase, mq, vl);
-          if (MODE == 1) load_page_sp<D>(A, img, j >= ph, lane);
+          load_page<D, E>(A, img, j >= ph, kbase, mt, vl);
+          if (MODE == 1) load_page_sp<D, E>(A, img, j >= ph, lane);
           A.id = s_idt[t];
           run(A, j);
         }
@@ -926,8 +1023,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
   // ---- merge the waves: maxima, rescale, fixed-order sums in LDS ----
   // Two barriers: after the first every lane derives its column's maximum
   // and sum from the waves' values itself (same order in every lane).
-  sm.lsum = rows_sum(sm.lsum);
-  sm.zsum = rows_sum(sm.zsum);
+  sm.lsum = heads_sum<E>(rows_sum(sm.lsum));
+  sm.zsum = heads_sum<E>(rows_sum(sm.zsum));
   __shared__ uint32_t wbad[kWaves];
   __shared__ int s_tc;
   __shared__ float s_tcsum;
@@ -955,7 +1052,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
       sL[i] = l;
       sI[i] = l > 0.0f ? 1.0f / l : 0.0f;
     }
-    const int ncol = PACK ? 2 * G : G;  // columns that carry data
+    const int ncol = PACK ? 2 * GP : G;  // columns that carry data
     if (i < ncol) {
       // O = acc + sum p (z_v - kv s_v) (the z term once per head: not in tail columns)
       const float f = (M == -INFINITY || sm.m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sm.m - M);
@@ -971,7 +1068,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
   const float* ob = (const float*)&buf[0][0];
   auto ocol = [&](int g, int dim) {  // sum over waves (fixed order) of column g (+ its tail)
     const int o0 = (g * (D / 4) + ((dim >> 2) ^ (g & 15))) * 4 + (dim & 3);
-    const int o1 = ((g + G) * (D / 4) + ((dim >> 2) ^ ((g + G) & 15))) * 4 + (dim & 3);
+    const int o1 = ((g + GP) * (D / 4) + ((dim >> 2) ^ ((g + GP) & 15))) * 4 + (dim & 3);
     float o = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWaves; w++) {
@@ -1675,24 +1772,26 @@ hipError_t launch_attn(const Cfg& c, const Pool& p, int batch, const uint16_t* q
   const dim3 grid(S, (unsigned)U), block(kThreads);
   // a single split runs the score update inside the attention workgroup
   const int kmode = mode == 1 && S > 1 ? 2 : mode;
-  // head and tail of the weights share one matrix instruction when 2G <= 16
-  const bool pack = 2 * c.G <= 16;
+  // G rounded up to 4, 8 or 16 (the kernel's softmax layout)
+  const int gp = c.G <= 4 ? 4 : (c.G <= 8 ? 8 : 16);
   const PolicyArgs pa{c.W, c.S_max, c.lo_en, c.ah, c.al, c.ah_head, c.al_head};
   const StepArgs none{};
   const int32_t* order = launch_order(S, U, state, w, s);
-#define DKV_ATTN(D, M, PK)                                                                                 \
-  attn_kernel<D, M, PK, false><<<grid, block, 0, s>>>(c.H, c.G, c.L, S, p.P, p.page_bytes, pa, scale_log2, q, \
+#define DKV_ATTN(D, M, GPV)                                                                                \
+  attn_kernel<D, M, GPV, false><<<grid, block, 0, s>>>(c.H, c.G, c.L, S, p.P, p.page_bytes, pa, scale_log2, q, \
                                                       table, state, seq_len, p.pages, out, w.part, w.ml,      \
                                                       w.logits, p.status, none, order)
-#define DKV_ATTN_D(D)                                    \
-  if (pack) {                                            \
-    if (kmode == 0) DKV_ATTN(D, 0, true);                \
-    else if (kmode == 1) DKV_ATTN(D, 1, true);           \
-    else DKV_ATTN(D, 2, true);                           \
-  } else {                                               \
-    if (kmode == 0) DKV_ATTN(D, 0, false);               \
-    else if (kmode == 1) DKV_ATTN(D, 1, false);          \
-    else DKV_ATTN(D, 2, false);                          \
+#define DKV_ATTN_G(D, GPV)                     \
+  if (kmode == 0) DKV_ATTN(D, 0, GPV);         \
+  else if (kmode == 1) DKV_ATTN(D, 1, GPV);    \
+  else DKV_ATTN(D, 2, GPV);
+#define DKV_ATTN_D(D)                          \
+  if (gp == 4) {                               \
+    DKV_ATTN_G(D, 4)                           \
+  } else if (gp == 8) {                        \
+    DKV_ATTN_G(D, 8)                           \
+  } else {                                     \
+    DKV_ATTN_G(D, 16)                          \
   }
   if (c.d == 128) {
     DKV_ATTN_D(128)
@@ -1700,6 +1799,7 @@ hipError_t launch_attn(const Cfg& c, const Pool& p, int batch, const uint16_t* q
     DKV_ATTN_D(64)
   }
 #undef DKV_ATTN_D
+#undef DKV_ATTN_G
 #undef DKV_ATTN
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1759,7 +1859,7 @@ hipError_t launch_decode_step(const Cfg& c, const Pool& p, int batch, const int3
   AttnWs w = attn_carve(c, batch, mode != 0, ws_attn, nullptr);
   const float scale_log2 = (1.0f / sqrtf((float)c.d)) * kLog2e;
   const dim3 grid(1, (unsigned)U), block(kThreads);
-  const bool pack = 2 * c.G <= 16;
+  const int gp = c.G <= 4 ? 4 : (c.G <= 8 ? 8 : 16);
   const PolicyArgs pa{c.W, c.S_max, c.lo_en, c.ah, c.al, c.ah_head, c.al_head};
   const StepArgs sa{k,
                     v,
@@ -1779,17 +1879,20 @@ hipError_t launch_decode_step(const Cfg& c, const Pool& p, int batch, const int3
                     can_chain ? sn.nf : nullptr,
                     can_chain ? sn.cw : nullptr};
   const int32_t* order = launch_order(1, U, state, w, s, chained && chain % kOrderRefresh != 0);
-#define DKV_STEP(D, M, PK)                                                                                \
-  attn_kernel<D, M, PK, true><<<grid, block, 0, s>>>(c.H, c.G, c.L, 1, p.P, p.page_bytes, pa, scale_log2, q, \
+#define DKV_STEP(D, M, GPV)                                                                               \
+  attn_kernel<D, M, GPV, true><<<grid, block, 0, s>>>(c.H, c.G, c.L, 1, p.P, p.page_bytes, pa, scale_log2, q, \
                                                      table, state, seq_len, p.pages, out, w.part, w.ml,      \
                                                      w.logits, p.status, sa, order)
+#define DKV_STEP_G(D, GPV)                      \
+  if (mode == 0) DKV_STEP(D, 0, GPV);           \
+  else DKV_STEP(D, 1, GPV);
 #define DKV_STEP_D(D)                           \
-  if (pack) {                                   \
-    if (mode == 0) DKV_STEP(D, 0, true);        \
-    else DKV_STEP(D, 1, true);                  \
+  if (gp == 4) {                                \
+    DKV_STEP_G(D, 4)                            \
+  } else if (gp == 8) {                         \
+    DKV_STEP_G(D, 8)                            \
   } else {                                      \
-    if (mode == 0) DKV_STEP(D, 0, false);       \
-    else DKV_STEP(D, 1, false);                 \
+    DKV_STEP_G(D, 16)                           \
   }
   if (c.d == 128) {
     DKV_STEP_D(128)
@@ -1797,6 +1900,7 @@ hipError_t launch_decode_step(const Cfg& c, const Pool& p, int batch, const int3
     DKV_STEP_D(64)
   }
 #undef DKV_STEP_D
+#undef DKV_STEP_G
 #undef DKV_STEP
   return hipGetLastError();
 }
