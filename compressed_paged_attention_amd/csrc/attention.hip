@@ -655,7 +655,6 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
   // step leaves alone; it then takes a smaller share of those, and the
   // written pages from their images.
   constexpr int kCW = kWaves - 1;     // the committing wave
-  constexpr int kCommitPages = 10;    // its commit, in page computes (share)
   static_assert(sizeof(buf) >= 2 * page_bytes_for(D), "two page images in the merge buffer");
   __shared__ int s_vd[3 * kWaves];
   __shared__ int32_t s_idt[2];        // ids of the written high and low pages
@@ -817,27 +816,33 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
   }
 
   // ---- page order (wave-uniform).  The two waves that share a SIMD (w and
-  // w + 4) do not progress alike: the hardware prefers the older one, and
-  // waves 0-3 end a like share of pages about 15 % sooner (35 % without the
-  // score update).  So the pages are cut in two ranges, each taken
-  // round-robin: waves 0-3 the first 150/256 of them (170/256 without the
-  // score update; 170/256 of the pages below `cut` with a step, against
-  // three waves), the others the rest; the shares were measured to end the
-  // waves of a pair together at the 200 GB stress workload.  With a step, the commit wave takes the pages from `cut` up and
-  // then the written pages, which everyone else skips; waves 0-3 and 4-6
-  // share the pages below `cut`.  The order is static: results do not depend
-  // on timing.
-  const int n_cw = go ? max(0, (TPg - kCommitPages * kCW) / kWaves) : 0;
+  // w + 4) do not progress alike: the hardware prefers the older one, whose
+  // pages take 1.2-2x less time, by how much depending on the softmax layout
+  // and the mode.  So the pages are cut in two ranges, each taken
+  // round-robin: waves 0-3 the first kShare/256 of them, the others the
+  // rest.  With a step, the commit wave takes the n_cw pages from `cut` up
+  // (a linear fit in the page count: its share of the unit less its commit)
+  // and then the written pages, which everyone else skips; waves 0-3 and 4-6
+  // share the pages below `cut`.  The shares were measured (per-workgroup
+  // timestamps) to end the waves together: G <= 4 on the Llama3-8B layer,
+  // 4 < G <= 8 on the 200 GB stress workload.  The order is static: results
+  // do not depend on timing.
+  constexpr int kShare0 = E == 1 ? 171 : (E == 2 ? 165 : 170);  // attention alone
+  constexpr int kShare1 = E == 1 ? 158 : (E == 2 ? 142 : 150);  // with the score update
+  constexpr int kShareS = E == 1 ? 176 : (E == 2 ? 161 : 170);  // with a step: 4 waves against 3
+  constexpr int kCwMul = E == 1 ? 24 : (E == 2 ? 28 : 32);       // n_cw = (TPg kCwMul - kCwSub) / 256
+  constexpr int kCwSub = E == 1 ? 1137 : (E == 2 ? 640 : 2240);
+  const int n_cw = go ? max(0, (TPg * kCwMul - kCwSub) >> 8) : 0;
   const int cut = TPg - n_cw;
   int lo, hi, stride, off;  // this wave's pages: lo + off, lo + off + stride, ... below hi
   if (!go) {
-    const int nA = ((p1 - p0) * (MODE == 1 ? 150 : 170)) >> 8;
+    const int nA = ((p1 - p0) * (MODE == 1 ? kShare1 : kShare0)) >> 8;
     lo = wid < 4 ? p0 : p0 + nA;
     hi = wid < 4 ? p0 + nA : p1;
     stride = 4;
     off = wid & 3;
   } else if (wid < kCW) {
-    const int nA = (cut * 170) >> 8;  // 4 waves against 3
+    const int nA = (cut * kShareS) >> 8;  // 4 waves against 3
     lo = wid < 4 ? 0 : nA;
     hi = wid < 4 ? nA : cut;
     stride = wid < 4 ? 4 : kCW - 4;
@@ -1286,7 +1291,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
           uint32_t wv = rw[0];
 #pragma unroll
           for (int k = 1; k < kRecWords; k++) wv = lane == k ? rw[k] : wv;
-          uint32_t* dst = (uint32_t*)(pages + (int64_t)id_tix(0) * page_bytes + plan_rec_off<D>());
+          // the unit's first high page (page-loop index 0: its id in LDS when the ids are there)
+          const int32_t id0 = lg_lds ? id_s[0] : (ids_lds ? ((const int32_t*)lds_w)[0] : id_tix(0));
+          uint32_t* dst = (uint32_t*)(pages + (int64_t)id0 * page_bytes + plan_rec_off<D>());
           if (lane < kRecWords) dst[lane] = wv;
           if constexpr (STEP) {
             if (sa.cw_n) {
@@ -1301,9 +1308,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(int H, int G, int L, int
                               : lane == S_IDS ? cl(pn.lo_src >> 4)
                                               : 0;
               int32_t id;
-              if (lg_lds) {
+              if (lg_lds || ids_lds) {
+                const int32_t* ids = lg_lds ? id_s : (const int32_t*)lds_w;
                 const int j = tix < ph ? tix : ph + (L - 1 - tix);
-                id = id_s[min(j, TPg - 1)];
+                id = ids[min(j, TPg - 1)];
                 id = j < TPg ? id : -1;
               } else {
                 id = id_tix(tix);
