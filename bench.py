@@ -479,9 +479,9 @@ def measure(args, name, R, steps, warmup, dk):
     n_hi, n_lo = int(ts[:, 0].sum()), int(ts[:, 1].sum())
     ctx = R * total * H
     one_split = dk.diffkv_attn_splits(cfg, B) == 1
-    pk = "true" if 2 * G <= 16 else "false"
-    step_kernel = "attn_kernel<%d, 1, %s, true>" % (d, pk) if one_split else "step + attention kernels"
-    attn_kernel = ("attn_kernel<%d, 1, %s, false>" % (d, pk)) if one_split else \
+    gp = 4 if G <= 4 else (8 if G <= 8 else 16)  # the kernel's softmax layout (G rounded up)
+    step_kernel = "attn_kernel<%d, 1, %d, true>" % (d, gp) if one_split else "step + attention kernels"
+    attn_kernel = ("attn_kernel<%d, 1, %d, false>" % (d, gp)) if one_split else \
         "attn_kernel<%d, 2, ...> + attn_merge_kernel + score_kernel" % d
     cfg_out = {"workload": WORKLOAD_NAMES.get(name, name), "q_heads": H * G, "kv_heads": H, "head_dim": d,
                "batch": B,
