@@ -1770,7 +1770,7 @@ constexpr int kOrderRefresh = 16;
 
 hipError_t launch_attn(const Cfg& c, const Pool& p, int batch, const uint16_t* q, const int32_t* table,
                        const int32_t* state, const int32_t* seq_len, float* out, int mode, void* ws,
-                       hipStream_t s) {
+                       hipStream_t s, bool reuse_order) {
   if (c.plain) return launch_attn_plain(c, p, batch, q, table, state, seq_len, out, mode, ws, s);
   const int64_t U = (int64_t)batch * c.H;
   if (U == 0) return hipSuccess;
@@ -1784,7 +1784,7 @@ hipError_t launch_attn(const Cfg& c, const Pool& p, int batch, const uint16_t* q
   const int gp = c.G <= 4 ? 4 : (c.G <= 8 ? 8 : 16);
   const PolicyArgs pa{c.W, c.S_max, c.lo_en, c.ah, c.al, c.ah_head, c.al_head};
   const StepArgs none{};
-  const int32_t* order = launch_order(S, U, state, w, s);
+  const int32_t* order = launch_order(S, U, state, w, s, reuse_order);
 #define DKV_ATTN(D, M, GPV)                                                                                \
   attn_kernel<D, M, GPV, false><<<grid, block, 0, s>>>(c.H, c.G, c.L, S, p.P, p.page_bytes, pa, scale_log2, q, \
                                                       table, state, seq_len, p.pages, out, w.part, w.ml,      \
@@ -1844,7 +1844,10 @@ hipError_t launch_decode_step(const Cfg& c, const Pool& p, int batch, const int3
   if (S != 1 || mode == 2 || c.plain) {
     hipError_t e = launch_step(c, p, batch, seq_len, k, v, table, state, ws_step, s);
     if (e != hipSuccess) return e;
-    return launch_attn(c, p, batch, q, table, state, seq_len, out, mode, ws_attn, s);
+    // a chained call (same workspace, nothing else writing it) keeps the
+    // chain's dispatch order, recomputed every kOrderRefresh calls
+    return launch_attn(c, p, batch, q, table, state, seq_len, out, mode, ws_attn, s,
+                       !c.plain && chain > 0 && chain % kOrderRefresh != 0);
   }
   const bool direct = U <= kDirectUnits;
   // chained steps: the attention with the score update plans the next step

@@ -95,10 +95,12 @@ __host__ __device__ inline int split_pages(int TPg, int S) {
   return q > kSplitMinPages ? q : kSplitMinPages;
 }
 size_t attn_workspace(const Cfg& c, int batch, bool scores);
-// mode 0: attention; 1: attention + score update; 2: attention keeping logits
+// mode 0: attention; 1: attention + score update; 2: attention keeping logits.
+// reuse_order: the dispatch order a previous call left in ws stands (it
+// changes timing only)
 hipError_t launch_attn(const Cfg& c, const Pool& p, int batch, const uint16_t* q,
                        const int32_t* table, const int32_t* state, const int32_t* seq_len,
-                       float* out, int mode, void* ws, hipStream_t s);
+                       float* out, int mode, void* ws, hipStream_t s, bool reuse_order = false);
 hipError_t launch_scores(const Cfg& c, const Pool& p, int batch, const int32_t* table,
                          const int32_t* state, const int32_t* seq_len, void* ws, hipStream_t s);
 // the split merge: partials [U][S][G][d + 2] -> out; (max, sum) to ml when save

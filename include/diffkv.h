@@ -379,10 +379,11 @@ int diffkv_decode_attn(const diffkv_config* cfg, const diffkv_pool* pool, int32_
  *           previous step's: on any mismatch the whole step is aborted
  *           (nothing committed, DIFFKV_ST_STALE_CHAIN set; repeat it with
  *           chain = 0).  Ignored where a chained call does not apply.
- *           With more units than compute units a chained call also reuses
- *           the dispatch order (units by page count) the chain's first call
- *           left in the workspace, recomputing it every 16 calls; the order
- *           changes timing only, never results.
+ *           With more units (or unit splits) than compute units any call
+ *           with chain > 0 also reuses the dispatch order (units by page
+ *           count) the chain's first call left in the workspace,
+ *           recomputing it every 16 calls; the order changes timing only,
+ *           never results.
  *  workspace: diffkv_workspace_bytes(DIFFKV_DECODE_STEP[_SCORES]); it
  *           carries the plans from one chained call to the next; with
  *           update_scores = 2 it carries the logits to diffkv_update_scores

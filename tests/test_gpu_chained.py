@@ -232,3 +232,47 @@ def test_release_rejects_page_ids_outside_the_pool(dk, orc, bad_id):
     assert int(p.o.status[0]) == orc.ST_BAD_STATE
     assert np.array_equal(p.o.page_table, before.page_table)
     assert np.array_equal(p.o.free_list, before.free_list) and np.array_equal(p.o.ptr, before.ptr)
+
+
+def test_split_chain_reuses_dispatch_order(dk):
+    """Several splits per unit and more (unit, split) pairs than compute
+    units: a chained diffkv_decode_step keeps the dispatch order (units by
+    page count) the chain's first call left in the workspace and recomputes
+    it every 16 calls.  The order changes timing only, so 20 chained steps
+    and the same 20 steps each with chain = 0 (order recomputed every time)
+    must leave byte-identical outputs, tables, tier state, pool and pages."""
+    from workloads import synth
+    cfg = synth.config("llama3_8b", num_kv_heads=8, batch=3, max_seq_len=4200, window=64)
+    cfg.pop("pool_factor", None)
+    B, H = 3, 8
+    S = dk.diffkv_attn_splits(cfg, B)
+    assert S > 1 and B * H * S > 256, (S, B * H)
+    lens = torch.tensor([3500, 1200, 2700], dtype=torch.int64)
+    pr = synth.make_prompt(cfg, device=dev, lens=lens)
+    P = int(sum(-(-int(n) // 16) for n in lens) * H * 1.2) + 64
+    cu = pr["cu_seqlens"].to(dev)
+    a = dk.DiffKVState(cfg, B, P, max_total_tokens=int(lens.sum()), device=dev)
+    t, _ = a.classify(cu, pr["scores"])
+    a.compact_prompt(cu, pr["k"], pr["v"], pr["scores"], t)
+    # the second cache: a byte copy of the first (pages never written included)
+    b = dk.DiffKVState(cfg, B, P, max_total_tokens=int(lens.sum()), device=dev)
+    for name in ("page_table", "tier_state"):
+        getattr(b, name).copy_(getattr(a, name))
+    for name in ("pages", "free_list", "ptr", "status"):
+        getattr(b.pool, name).copy_(getattr(a.pool, name))
+    torch.cuda.synchronize()
+    seq = lens.to(torch.int32).to(dev)
+    for step in range(20):
+        dec = synth.make_decode(cfg, step, device=dev)
+        oa = a.decode_step(dec["q"], seq, dec["k_new"], dec["v_new"], update_scores=1)
+        ob = b.decode_step(dec["q"], seq, dec["k_new"], dec["v_new"], update_scores=1, chain=0)
+        torch.cuda.synchronize()
+        what = f"split chain step {step} (chain {a.chain})"
+        assert torch.equal(oa, ob), f"{what}: outputs differ"
+        for name in ("page_table", "tier_state"):
+            assert torch.equal(getattr(a, name), getattr(b, name)), f"{what}: {name} differs"
+        assert torch.equal(a.pool.free_list, b.pool.free_list) and torch.equal(a.pool.ptr, b.pool.ptr), what
+        assert torch.equal(a.pool.pages, b.pool.pages), f"{what}: pages differ"
+        seq = seq + 1
+    assert a.chain == 20 and int(a.pool.status.item()) == 0 and int(b.pool.status.item()) == 0
+    _say(f"split chain: S={S}, 20 chained steps identical to unchained ones")
