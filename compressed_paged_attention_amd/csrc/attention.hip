@@ -1451,15 +1451,20 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(int H, int G, int S, co
 // important non-window high token, the least important low token and the
 // token leaving the window, from the updated sums (the rules of the fused
 // update); score_finish_kernel turns them into the unit's plan record.
+// MERGE (the update in the same call as the attention): every workgroup takes
+// its unit's (M, L) from the S split partials itself, and the unit's first
+// chunk also writes the merged output and (M, L) -- the split merge as
+// attn_merge_kernel does it, one kernel launch fewer.
 
-template <int D, int GB>
+template <int D, int GB, bool MERGE>
 __global__ __launch_bounds__(256) void score_kernel(int H, int G, int L, int64_t P, int page_bytes, int W,
                                                     const int32_t* __restrict__ table,
                                                     const int32_t* __restrict__ state,
                                                     const int32_t* __restrict__ seq_len,
-                                                    const float* __restrict__ ml,
+                                                    float* __restrict__ ml,
                                                     const float* __restrict__ logits, uint8_t* pages,
-                                                    int32_t* __restrict__ cand) {
+                                                    int32_t* __restrict__ cand, int S,
+                                                    const float* __restrict__ part, float* __restrict__ out) {
   const int split = blockIdx.x;
   const int64_t u = blockIdx.y;
   const int b = (int)u / H;
@@ -1472,20 +1477,85 @@ __global__ __launch_bounds__(256) void score_kernel(int H, int G, int L, int64_t
   const int TPg = ph + pl;
   const int p0 = split * kScorePages, p1 = min(TPg, p0 + kScorePages);
   if (p0 >= p1) return;
-  if (ml[u * G * 2 + 1] <= 0.0f) return;  // bad unit (or nothing attended)
+  __shared__ float sC[16];  // c_g = -M_g - log2 L_g (-inf: no weight)
+  if constexpr (MERGE) {
+    // every split's (m, l) per head into LDS in one round of loads; per head
+    // M = max over the splits (a NaN marks a bad unit: M = -inf), the splits'
+    // weights 2^(m_s - M) and L, in split order
+    __shared__ float sW[16][kMaxSplits];
+    __shared__ float sMS[kMaxSplits * 16], sLS[kMaxSplits * 16];
+    __shared__ float sML[16][2];
+    const float* up = part + (u * S) * G * (D + 2);
+    for (int x = tid; x < S * G; x += 256) {
+      sMS[x] = up[x * (D + 2) + D];
+      sLS[x] = up[x * (D + 2) + D + 1];
+    }
+    __syncthreads();
+    if (tid < G) {
+      float M = -INFINITY;
+      bool badp = false;
+      for (int sp = 0; sp < S; sp++) {
+        const float m = sMS[sp * G + tid];
+        badp |= m != m;
+        M = fmaxf(M, m);
+      }
+      if (badp) M = -INFINITY;
+      float l = 0.0f;
+      for (int sp = 0; sp < S; sp++) {
+        const float m = sMS[sp * G + tid];
+        const float w = (M == -INFINITY || m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+        sW[tid][sp] = w;
+        if (w != 0.0f) l += sLS[sp * G + tid] * w;
+      }
+      sML[tid][0] = M;
+      sML[tid][1] = l;
+    }
+    __syncthreads();
+    if (split == 0) {
+      // the merged output: eight splits' values of an output loaded at once
+      const int hh = (int)(u % H);
+      for (int x = tid; x < G * D; x += 256) {
+        const int g = x / D, dd = x % D;
+        float o = 0.0f;
+        for (int sp0 = 0; sp0 < S; sp0 += 8) {
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; e++) v[e] = sp0 + e < S ? up[((sp0 + e) * G + g) * (D + 2) + dd] : 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; e++) {
+            const float w = sp0 + e < S ? sW[g][sp0 + e] : 0.0f;
+            if (w != 0.0f) o += v[e] * w;
+          }
+        }
+        const float l = sML[g][1];
+        out[(((int64_t)b * H + hh) * G + g) * D + dd] = l > 0.0f ? o / l : 0.0f;
+      }
+      if (tid < G) {
+        ml[(u * G + tid) * 2 + 0] = sML[tid][0];
+        ml[(u * G + tid) * 2 + 1] = sML[tid][1];
+      }
+    }
+    if (!(sML[0][1] > 0.0f)) return;  // bad unit (or nothing attended)
+    if (tid < GB) {
+      const float M = tid < G ? sML[tid][0] : -INFINITY;
+      const float l = tid < G ? sML[tid][1] : 0.0f;
+      sC[tid] = (M == -INFINITY || !(l > 0.0f)) ? -INFINITY : __builtin_amdgcn_logf(1.0f / l) - M;
+    }
+  } else {
+    if (ml[u * G * 2 + 1] <= 0.0f) return;  // bad unit (or nothing attended)
+    if (tid < GB) {
+      const float M = tid < G ? ml[(u * G + tid) * 2 + 0] : -INFINITY;
+      const float l = tid < G ? ml[(u * G + tid) * 2 + 1] : 0.0f;
+      sC[tid] = (M == -INFINITY || !(l > 0.0f)) ? -INFINITY : __builtin_amdgcn_logf(1.0f / l) - M;
+    }
+  }
   // the unit's scores change here: a plan record no longer applies
   if (split == 0 && tid == 0 && ph >= 1) {
     const int32_t id0 = row[0];
     if (id0 >= 0 && id0 < P) *(uint32_t*)(pages + (int64_t)id0 * page_bytes + plan_rec_off<D>()) = 0u;
   }
-  __shared__ float sC[16];  // c_g = -M_g - log2 L_g (-inf: no weight)
   __shared__ int s_tc;      // slot of the token leaving the window at length N + 1
   __shared__ float s_tcsum;
-  if (tid < GB) {
-    const float M = tid < G ? ml[(u * G + tid) * 2 + 0] : -INFINITY;
-    const float l = tid < G ? ml[(u * G + tid) * 2 + 1] : 0.0f;
-    sC[tid] = (M == -INFINITY || !(l > 0.0f)) ? -INFINITY : __builtin_amdgcn_logf(1.0f / l) - M;
-  }
   if (tid == 0) s_tc = -1;
   // the chunk's slots: high pages (16 slots) first, then low pages (32)
   const int nhp = max(0, min(ph, p1) - p0);
@@ -1661,6 +1731,13 @@ __global__ __launch_bounds__(64) void score_finish_kernel(int H, int G, int L, i
 
 hipError_t launch_scores(const Cfg& c, const Pool& p, int batch, const int32_t* table, const int32_t* state,
                          const int32_t* seq_len, void* ws, hipStream_t s) {
+  return launch_scores_merge(c, p, batch, table, state, seq_len, ws, s, 0, nullptr);
+}
+
+// merge_S > 0: the split partials of the attention just run (S = merge_S)
+// are merged into out by the score kernel itself
+hipError_t launch_scores_merge(const Cfg& c, const Pool& p, int batch, const int32_t* table, const int32_t* state,
+                               const int32_t* seq_len, void* ws, hipStream_t s, int merge_S, float* out) {
   if (c.plain) return launch_scores_plain(c, p, batch, table, state, seq_len, ws, s);
   const int64_t U = (int64_t)batch * c.H;
   if (U == 0) return hipSuccess;
@@ -1668,9 +1745,15 @@ hipError_t launch_scores(const Cfg& c, const Pool& p, int batch, const int32_t* 
   const dim3 grid((unsigned)((c.L + kScorePages - 1) / kScorePages), (unsigned)U), block(256);
   const PolicyArgs pa{c.W, c.S_max, c.lo_en, c.ah, c.al, c.ah_head, c.al_head};
   const int GS = logit_stride(c.G);
-#define DKV_SCORE(D, GB)                                                                                 \
-  score_kernel<D, GB><<<grid, block, 0, s>>>(c.H, c.G, c.L, p.P, p.page_bytes, c.W, table, state, seq_len, \
-                                             w.ml, w.logits, p.pages, w.cand)
+  const bool merge = merge_S > 0;
+#define DKV_SCORE(D, GB)                                                                                          \
+  if (merge)                                                                                                      \
+    score_kernel<D, GB, true><<<grid, block, 0, s>>>(c.H, c.G, c.L, p.P, p.page_bytes, c.W, table, state, seq_len, \
+                                                     w.ml, w.logits, p.pages, w.cand, merge_S, w.part, out);     \
+  else                                                                                                            \
+    score_kernel<D, GB, false><<<grid, block, 0, s>>>(c.H, c.G, c.L, p.P, p.page_bytes, c.W, table, state,        \
+                                                      seq_len, w.ml, w.logits, p.pages, w.cand, 0, nullptr,     \
+                                                      nullptr)
 #define DKV_SCORE_D(D)                  \
   if (GS == 4) DKV_SCORE(D, 4);         \
   else if (GS == 8) DKV_SCORE(D, 8);    \
@@ -1812,9 +1895,9 @@ hipError_t launch_attn(const Cfg& c, const Pool& p, int batch, const uint16_t* q
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (S > 1) {
-    e = launch_attn_merge(c, batch, S, seq_len, w.part, out, w.ml, mode != 0, s);
-    if (e != hipSuccess) return e;
-    if (mode == 1) return launch_scores(c, p, batch, table, state, seq_len, ws, s);
+    // with the score update the score kernel merges the splits itself
+    if (mode == 1) return launch_scores_merge(c, p, batch, table, state, seq_len, ws, s, S, out);
+    return launch_attn_merge(c, batch, S, seq_len, w.part, out, w.ml, mode != 0, s);
   }
   return hipSuccess;
 }

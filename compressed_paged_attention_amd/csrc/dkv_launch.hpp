@@ -103,6 +103,9 @@ hipError_t launch_attn(const Cfg& c, const Pool& p, int batch, const uint16_t* q
                        float* out, int mode, void* ws, hipStream_t s, bool reuse_order = false);
 hipError_t launch_scores(const Cfg& c, const Pool& p, int batch, const int32_t* table,
                          const int32_t* state, const int32_t* seq_len, void* ws, hipStream_t s);
+hipError_t launch_scores_merge(const Cfg& c, const Pool& p, int batch, const int32_t* table,
+                               const int32_t* state, const int32_t* seq_len, void* ws, hipStream_t s,
+                               int merge_S, float* out);
 // the split merge: partials [U][S][G][d + 2] -> out; (max, sum) to ml when save
 hipError_t launch_attn_merge(const Cfg& c, int batch, int S, const int32_t* seq_len, const float* part,
                              float* out, float* ml, bool save, hipStream_t s);
