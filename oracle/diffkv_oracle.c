@@ -1262,30 +1262,31 @@ int orc_keydiff_scores(const orc_cfg* c, int32_t batch, const int64_t* cu, const
  * Here a page's keys are the dequantized keys of its retained slots (what
  * the attention reads).  bounds [num_pages][2][d] fp32: row 0 the minima,
  * row 1 the maxima, written for every live page of the batch's units
- * (other pages untouched). */
+ * (other pages untouched).  With K precision levels every level's pages
+ * count (level l: p_l pages of the unit's rows, its own codec and page
+ * size); two levels are the high and low tiers. */
+static int32_t level_tokens(const orc_cfg* c, int32_t l);
+static int64_t level_entry(const orc_cfg* c, int32_t l, int32_t j);
 int orc_page_bounds(const orc_cfg* c, orc_pool* p, int32_t batch, const int32_t* table,
                     const int32_t* state, float* bounds) {
-  if (!cfg_valid(c) || !p || batch < 0 || num_levels(c) >= 3) return ORC_E_INVALID;
-  int32_t H = c->num_kv_heads, d = c->head_dim, L = orc_table_len(c);
-  int32_t Th = c->hi_page_tokens, Tl = c->lo_page_tokens;
+  if (!cfg_valid(c) || !p || batch < 0) return ORC_E_INVALID;
+  int32_t H = c->num_kv_heads, d = c->head_dim, LT = orc_table_len(c), K = num_levels(c);
   for (int64_t u = 0; u < (int64_t)batch * H; u++) {
-    const int32_t* s4 = state + 4 * u;
-    const int32_t* row = table + u * L;
-    for (int32_t tier = ORC_LO; tier <= ORC_HI; tier++) {
-      int32_t n = tier == ORC_HI ? s4[0] : s4[1], T = tier == ORC_HI ? Th : Tl;
-      int32_t np = tier == ORC_HI ? s4[2] : s4[3];
+    const int32_t* s = state + (int64_t)2 * K * u;
+    const int32_t* row = table + u * LT;
+    for (int32_t l = 0; l < K; l++) {
+      int32_t n = s[l], np = s[K + l], T = level_tokens(c, l);
       for (int32_t j = 0; j < np; j++) {
-        int32_t id = tier == ORC_HI ? row[j] : row[L - 1 - j];
+        int32_t id = row[level_entry(c, l, j)];
         if (id < 0 || id >= p->num_pages) continue;
         float* mn = bounds + (int64_t)id * 2 * d;
         float* mx = mn + d;
         for (int32_t e = 0; e < d; e++) { mn[e] = INFINITY; mx[e] = -INFINITY; }
         int32_t nv = n - T * j < T ? n - T * j : T;
         for (int32_t t = 0; t < nv; t++) {
-          uint8_t kc[128], vc[128];
-          uint16_t km[2], vm[2];
-          float sc; int32_t pos;
-          orc_read_slot(c, page_at(p, id), tier, t, kc, vc, km, vm, &sc, &pos);
+          uint8_t kc[128];
+          uint16_t km[2];
+          orc_read_level_slot(c, page_at(p, id), l, t, kc, NULL, km, NULL, NULL, NULL);
           for (int32_t e = 0; e < d; e++) {
             float x = orc_dequant(km[0], km[1], kc[e]);
             if (x < mn[e]) mn[e] = x;
@@ -1301,38 +1302,40 @@ int orc_page_bounds(const orc_cfg* c, orc_pool* p, int32_t batch, const int32_t*
 /* Page scores from the bounds: for every page of every unit, in table order,
  * the max over the KV head's q heads (the group's combination, as for the
  * token scores) of sum_i max(q_i kmin_i, q_i kmax_i), fp64 rounded to fp32;
- * q [batch, H*G, d] fp16; scores [batch, H, L] fp32, -inf at empty entries
- * and for inactive requests (seq_len <= 0). */
+ * q [batch, H*G, d] fp16; scores [batch, H, table_len] fp32, -inf at empty
+ * entries and for inactive requests (seq_len <= 0). */
 int orc_page_scores(const orc_cfg* c, int32_t batch, const uint16_t* q, const int32_t* table,
                     const int32_t* state, const int32_t* seq_len, const float* bounds,
                     int64_t num_pages, float* scores) {
-  if (!cfg_valid(c) || batch < 0 || num_levels(c) >= 3) return ORC_E_INVALID;
-  int32_t H = c->num_kv_heads, G = c->gqa_group, d = c->head_dim, L = orc_table_len(c);
+  if (!cfg_valid(c) || batch < 0) return ORC_E_INVALID;
+  int32_t H = c->num_kv_heads, G = c->gqa_group, d = c->head_dim, LT = orc_table_len(c), K = num_levels(c);
   for (int64_t u = 0; u < (int64_t)batch * H; u++) {
     int32_t b = (int32_t)(u / H), h = (int32_t)(u % H);
-    const int32_t* s4 = state + 4 * u;
-    const int32_t* row = table + u * L;
-    float* out = scores + u * L;
-    for (int32_t t = 0; t < L; t++) out[t] = -INFINITY;
+    const int32_t* s = state + (int64_t)2 * K * u;
+    const int32_t* row = table + u * LT;
+    float* out = scores + u * LT;
+    for (int32_t t = 0; t < LT; t++) out[t] = -INFINITY;
     if (seq_len[b] <= 0) continue;
-    for (int32_t t = 0; t < L; t++) {
-      int live = t < s4[2] || t >= L - s4[3];
-      int32_t id = row[t];
-      if (!live || id < 0 || id >= num_pages) continue;
-      const float* mn = bounds + (int64_t)id * 2 * d;
-      const float* mx = mn + d;
-      double best = -INFINITY;
-      for (int32_t g = 0; g < G; g++) {
-        const uint16_t* qr = q + ((int64_t)b * H * G + (int64_t)h * G + g) * d;
-        double s = 0.0;
-        for (int32_t e = 0; e < d; e++) {
-          double qe = (double)orc_f16_to_f32(qr[e]);
-          double a = qe * mn[e], bb = qe * mx[e];
-          s += a > bb ? a : bb;
+    for (int32_t l = 0; l < K; l++) {
+      for (int32_t j = 0; j < s[K + l]; j++) {
+        int64_t t = level_entry(c, l, j);
+        int32_t id = row[t];
+        if (id < 0 || id >= num_pages) continue;
+        const float* mn = bounds + (int64_t)id * 2 * d;
+        const float* mx = mn + d;
+        double best = -INFINITY;
+        for (int32_t g = 0; g < G; g++) {
+          const uint16_t* qr = q + ((int64_t)b * H * G + (int64_t)h * G + g) * d;
+          double sum = 0.0;
+          for (int32_t e = 0; e < d; e++) {
+            double qe = (double)orc_f16_to_f32(qr[e]);
+            double x0 = qe * mn[e], x1 = qe * mx[e];
+            sum += x0 > x1 ? x0 : x1;
+          }
+          if (sum > best) best = sum;
         }
-        if (s > best) best = s;
+        out[t] = (float)best;
       }
-      out[t] = (float)best;
     }
   }
   return ORC_OK;
