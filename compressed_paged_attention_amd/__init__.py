@@ -403,7 +403,7 @@ class DiffKVState:
         return bounds
 
     def page_scores(self, q, seq_len, bounds):
-        """Page scores [batch, H, L] in table order (diffkv_page_scores)."""
+        """Page scores [batch, H, table_len] in table order (diffkv_page_scores)."""
         out = torch.empty(self.batch, self.H, self.L, dtype=torch.float32, device=q.device)
         _check(lib().diffkv_page_scores(ctypes.byref(make_config(self.cfg)), ctypes.byref(self.pool.struct()),
                                         self.batch, _ptr(q), _ptr(self.page_table), _ptr(self.tier_state),

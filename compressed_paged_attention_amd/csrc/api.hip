@@ -269,7 +269,7 @@ int diffkv_keydiff_scores(const diffkv_config* cfg, int32_t batch, int64_t total
 
 int diffkv_page_bounds(const diffkv_config* cfg, const diffkv_pool* pool, int32_t batch, const int32_t* page_table,
                        const int32_t* tier_state, float* bounds, void* stream) {
-  if (!cfg_ok(cfg) || !pool_ok(cfg, pool) || batch < 0 || cfg->num_levels >= 3) return DIFFKV_E_INVALID;
+  if (!cfg_ok(cfg) || !pool_ok(cfg, pool) || batch < 0) return DIFFKV_E_INVALID;
   if (batch > 0 && (!page_table || !tier_state || !bounds)) return DIFFKV_E_INVALID;
   if ((int64_t)batch * cfg->num_kv_heads > 65535) return DIFFKV_E_INVALID;
   return rc(launch_page_bounds(to_cfg(cfg), to_pool(pool), batch, page_table, tier_state, bounds,
@@ -279,7 +279,7 @@ int diffkv_page_bounds(const diffkv_config* cfg, const diffkv_pool* pool, int32_
 int diffkv_page_scores(const diffkv_config* cfg, const diffkv_pool* pool, int32_t batch, const uint16_t* q,
                        const int32_t* page_table, const int32_t* tier_state, const int32_t* seq_len,
                        const float* bounds, float* scores, void* stream) {
-  if (!cfg_ok(cfg) || !pool_ok(cfg, pool) || batch < 0 || cfg->num_levels >= 3) return DIFFKV_E_INVALID;
+  if (!cfg_ok(cfg) || !pool_ok(cfg, pool) || batch < 0) return DIFFKV_E_INVALID;
   if (batch > 0 && (!q || !page_table || !tier_state || !seq_len || !bounds || !scores)) return DIFFKV_E_INVALID;
   if ((int64_t)batch * cfg->num_kv_heads > 65535) return DIFFKV_E_INVALID;
   // pairs of dimensions per lane: 4-byte query words, 8-byte bound pairs

@@ -11,6 +11,9 @@
 //   page_bounds_kernel: one thread per (page, dimension); every slot's code
 //     byte and scale/zero word of the page are loaded before any is used (one
 //     round trip per page, not one per slot), then min and max per dimension;
+//     with K precision levels (DiffKV notes, "KV compression policy",
+//     extensibility paragraph) every level's pages, each with its own codec
+//     and page size;
 //   page_scores_kernel: one wave per table entry, each lane D/64 dimensions;
 //     per q head of the group the lane's max(q kmin, q kmax) terms, a wave
 //     sum in a fixed butterfly order, then the max over the group, written in
@@ -28,8 +31,19 @@ namespace {
 
 constexpr int kBThreads = 256;
 
-__device__ inline bool state_valid(int nh, int nl, int ph, int pl, int L) {
-  return nh >= 0 && nl >= 0 && ph == (int)cdiv(nh, kHiTokens) && pl == (int)cdiv(nl, kLoTokens) && ph + pl <= L;
+// A unit's level state is consistent: n_l >= 0 tokens in p_l = ceil(n_l / T_l)
+// pages per level, and the two levels that share a table row fit in it.
+__device__ inline bool levels_valid(const int32_t* s, const Levels& lv) {
+  bool ok = true;
+#pragma unroll
+  for (int l = 0; l < 4; l++) {
+    if (l < lv.K) ok = ok && s[l] >= 0 && s[lv.K + l] == (int)cdiv(s[l], lv.T(l));
+  }
+#pragma unroll
+  for (int r = 0; r < 2; r++) {
+    if (r < lv.R) ok = ok && s[lv.K + 2 * r] + (2 * r + 1 < lv.K ? s[lv.K + 2 * r + 1] : 0) <= lv.L;
+  }
+  return ok;
 }
 
 }  // namespace
@@ -87,9 +101,11 @@ __device__ inline void page_dim_bounds_plain(const uint8_t* pg, int nv, int dim,
 
 constexpr int kBoundsWgPerUnit = 8;  // workgroups per unit (grid x), striding over its pages
 
-// bounds [P][2][D]: row 0 minima, row 1 maxima
+// bounds [P][2][D]: row 0 minima, row 1 maxima.  Levels in turn (the level
+// is uniform over the grid, so the page size and codec are too); within a
+// level the unit's workgroups stride over its pages.
 template <int D, bool PLAIN>
-__global__ __launch_bounds__(kBThreads) void page_bounds_kernel(int L, int64_t P, int page_bytes, Seg shp, Seg slp,
+__global__ __launch_bounds__(kBThreads) void page_bounds_kernel(Levels lv, int64_t P, int page_bytes,
                                                                const int32_t* __restrict__ table,
                                                                const int32_t* __restrict__ state,
                                                                const uint8_t* __restrict__ pages,
@@ -97,33 +113,40 @@ __global__ __launch_bounds__(kBThreads) void page_bounds_kernel(int L, int64_t P
   constexpr int PPB = kBThreads / D;  // pages per workgroup and round
   const int64_t u = blockIdx.y;
   const int dim = threadIdx.x % D;
-  const int32_t* s4 = state + 4 * u;
-  const int nh = s4[0], nl = s4[1], ph = s4[2], pl = s4[3];
-  if (!state_valid(nh, nl, ph, pl, L)) return;
-  for (int pj = blockIdx.x * PPB + threadIdx.x / D; pj < ph + pl; pj += gridDim.x * PPB) {
-    const bool hi = pj < ph;  // uniform over the page's D threads (whole waves)
-    const int jt = hi ? pj : pj - ph;
-    const int32_t id = table[u * L + (hi ? jt : L - 1 - jt)];
-    if (id < 0 || id >= P) continue;
-    const int nv = hi ? min(kHiTokens, nh - kHiTokens * jt) : min(kLoTokens, nl - kLoTokens * jt);
-    const uint8_t* pg = pages + (int64_t)id * page_bytes;
-    float mn, mx;
-    if constexpr (PLAIN) {
-      if (hi) page_dim_bounds_plain<D, true>(pg, nv, dim, shp, mn, mx);
-      else page_dim_bounds_plain<D, false>(pg, nv, dim, slp, mn, mx);
-    } else {
-      if (hi) page_dim_bounds<D, true>(pg, nv, dim, mn, mx);
-      else page_dim_bounds<D, false>(pg, nv, dim, mn, mx);
+  const int K = lv.K;
+  const int64_t LT = (int64_t)lv.R * lv.L;
+  const int32_t* s = state + 2 * K * u;
+  if (!levels_valid(s, lv)) return;
+  for (int l = 0; l < K; l++) {
+    const int n = s[l], np = s[K + l];
+    // the level's layout by selects (a run-time index into the argument
+    // would go through scratch memory)
+    const Seg sg = l == 0 ? lv.s[0] : l == 1 ? lv.s[1] : l == 2 ? lv.s[2] : lv.s[3];
+    for (int j = blockIdx.x * PPB + threadIdx.x / D; j < np; j += gridDim.x * PPB) {
+      const int32_t id = table[u * LT + lv.entry(l, j)];
+      if (id < 0 || id >= P) continue;
+      const uint8_t* pg = pages + (int64_t)id * page_bytes;
+      float mn, mx;
+      if (l == 0) {
+        const int nv = min(kHiTokens, n - kHiTokens * j);
+        if constexpr (PLAIN) page_dim_bounds_plain<D, true>(pg, nv, dim, sg, mn, mx);
+        else page_dim_bounds<D, true>(pg, nv, dim, mn, mx);
+      } else {
+        const int nv = min(kLoTokens, n - kLoTokens * j);
+        if constexpr (PLAIN) page_dim_bounds_plain<D, false>(pg, nv, dim, sg, mn, mx);
+        else page_dim_bounds<D, false>(pg, nv, dim, mn, mx);
+      }
+      float* bo = bounds + (int64_t)id * 2 * D;
+      bo[dim] = mn;
+      bo[D + dim] = mx;
     }
-    float* bo = bounds + (int64_t)id * 2 * D;
-    bo[dim] = mn;
-    bo[D + dim] = mx;
   }
 }
 
-// scores [U][L] in table order
+// scores [U][R L] in table order (row r: level 2r from the left, 2r + 1
+// from the right)
 template <int D>
-__global__ __launch_bounds__(kBThreads) void page_scores_kernel(int H, int G, int L, int64_t P,
+__global__ __launch_bounds__(kBThreads) void page_scores_kernel(int H, int G, Levels lv, int64_t P,
                                                                const uint16_t* __restrict__ q,
                                                                const int32_t* __restrict__ table,
                                                                const int32_t* __restrict__ state,
@@ -135,9 +158,10 @@ __global__ __launch_bounds__(kBThreads) void page_scores_kernel(int H, int G, in
   const int64_t u = blockIdx.y;
   const int b = (int)(u / H), h = (int)(u % H);
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int32_t* s4 = state + 4 * u;
-  const int nh = s4[0], nl = s4[1], ph = s4[2], pl = s4[3];
-  const bool unit_ok = seq_len[b] > 0 && state_valid(nh, nl, ph, pl, L);
+  const int K = lv.K, L = lv.L, LT = lv.R * lv.L;
+  const int32_t* s = state + 2 * K * u;
+  const bool unit_ok = seq_len[b] > 0 && levels_valid(s, lv);
+  const int p0 = s[K], p1 = s[K + 1], p2 = K > 2 ? s[K + 2] : 0, p3 = K > 3 ? s[K + 3] : 0;
   // the group's query elements of this lane's dimensions (fp16 bits)
   uint32_t qw[16];
   const uint16_t* qb = q + ((int64_t)b * H * G + (int64_t)h * G) * D;
@@ -151,9 +175,11 @@ __global__ __launch_bounds__(kBThreads) void page_scores_kernel(int H, int G, in
       qw[g] = qb[(int64_t)g * D + lane];
     }
   }
-  for (int tix = blockIdx.x * WPB + wid; tix < L; tix += gridDim.x * WPB) {
-    const bool live = unit_ok && (tix < ph || tix >= L - pl);
-    const int32_t id = live ? table[u * L + tix] : -1;
+  for (int tix = blockIdx.x * WPB + wid; tix < LT; tix += gridDim.x * WPB) {
+    const bool r1 = tix >= L;
+    const int col = r1 ? tix - L : tix, pa = r1 ? p2 : p0, pb = r1 ? p3 : p1;
+    const bool live = unit_ok && (col < pa || col >= L - pb);
+    const int32_t id = live ? table[u * LT + tix] : -1;
     const bool ok = live && id >= 0 && id < P;  // uniform over the wave
     float best = -INFINITY;
     if (ok) {
@@ -182,7 +208,7 @@ __global__ __launch_bounds__(kBThreads) void page_scores_kernel(int H, int G, in
         }
       }
     }
-    if (lane == 0) scores[u * L + tix] = best;
+    if (lane == 0) scores[u * LT + tix] = best;
   }
 }
 
@@ -193,10 +219,9 @@ hipError_t launch_page_bounds(const Cfg& c, const Pool& p, int batch, const int3
   const int ppb = kBThreads / c.d;
   const int gx = min((c.L + ppb - 1) / ppb, kBoundsWgPerUnit);
   const dim3 grid((unsigned)gx, (unsigned)U), block(kBThreads);
-  const Lay lay(c.d, c.plain, c.codec);
-#define DKV_BOUNDS(D, PL)                                                                                 \
-  page_bounds_kernel<D, PL><<<grid, block, 0, s>>>(c.L, p.P, p.page_bytes, lay.seg(true), lay.seg(false), \
-                                                   table, state, p.pages, bounds)
+  const Levels lv = levels_of(c);
+#define DKV_BOUNDS(D, PL) \
+  page_bounds_kernel<D, PL><<<grid, block, 0, s>>>(lv, p.P, p.page_bytes, table, state, p.pages, bounds)
   if (c.d == 128) {
     if (c.plain) DKV_BOUNDS(128, true);
     else DKV_BOUNDS(128, false);
@@ -214,12 +239,13 @@ hipError_t launch_page_scores(const Cfg& c, int64_t P, int batch, const uint16_t
   const int64_t U = (int64_t)batch * c.H;
   if (U == 0) return hipSuccess;
   constexpr int wpb = kBThreads / 64;
-  const int gx = min((c.L + wpb - 1) / wpb, kBoundsWgPerUnit);
+  const int gx = min((c.LT + wpb - 1) / wpb, kBoundsWgPerUnit);
   const dim3 grid((unsigned)gx, (unsigned)U), block(kBThreads);
+  const Levels lv = levels_of(c);
   if (c.d == 128)
-    page_scores_kernel<128><<<grid, block, 0, s>>>(c.H, c.G, c.L, P, q, table, state, seq_len, bounds, scores);
+    page_scores_kernel<128><<<grid, block, 0, s>>>(c.H, c.G, lv, P, q, table, state, seq_len, bounds, scores);
   else
-    page_scores_kernel<64><<<grid, block, 0, s>>>(c.H, c.G, c.L, P, q, table, state, seq_len, bounds, scores);
+    page_scores_kernel<64><<<grid, block, 0, s>>>(c.H, c.G, lv, P, q, table, state, seq_len, bounds, scores);
   return hipGetLastError();
 }
 

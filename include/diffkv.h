@@ -224,8 +224,9 @@ int diffkv_keydiff_scores(const diffkv_config* cfg, int32_t batch, int64_t total
 /* Per-page key bounds (FlexiCache page, "3.2 KV page scoring", after
  * Quest: each KV page keeps the per-dimension minimum and maximum of its
  * keys).  For every live page of the batch's units (table entries in the
- * unit's high prefix / low suffix), over the dequantized keys of its
- * retained slots (the keys the attention reads):
+ * unit's high prefix / low suffix; with K levels the p_l pages of every
+ * level, each with its own codec and page size), over the dequantized keys
+ * of its retained slots (the keys the attention reads):
  *  bounds fp32 [pool->num_pages][2][d] out: row 0 the minima, row 1 the
  *  maxima (exact fp32 values); other pages' rows untouched.  Kept apart from
  *  the pages, as the page keeps its min-max vectors in a cache of their own;
@@ -240,8 +241,8 @@ int diffkv_page_bounds(const diffkv_config* cfg, const diffkv_pool* pool, int32_
  * token scores); a decode step can skip the pages whose score is low.
  *  q fp16 [batch, H*G, d] (4-byte aligned); seq_len int32 [batch] (<= 0:
  *  inactive); bounds as diffkv_page_bounds wrote them (8-byte aligned);
- *  scores fp32 [batch, H, L] out in table order, -inf at empty entries and
- *  for inactive requests.  fp32 with fixed-order sums.  DIFFKV_E_INVALID on
+ *  scores fp32 [batch, H, table_len] out in table order (diffkv_table_len
+ *  entries per unit), -inf at empty entries and for inactive requests.  fp32 with fixed-order sums.  DIFFKV_E_INVALID on
  *  a misaligned q or bounds. */
 int diffkv_page_scores(const diffkv_config* cfg, const diffkv_pool* pool, int32_t batch, const uint16_t* q,
                        const int32_t* page_table, const int32_t* tier_state, const int32_t* seq_len,

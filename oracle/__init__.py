@@ -305,7 +305,7 @@ class State:
         return b
 
     def page_scores(self, q, seq_len, bounds) -> np.ndarray:
-        """fp32 [batch, H, L] page scores in table order from `bounds`."""
+        """fp32 [batch, H, table_len] page scores in table order from `bounds`."""
         qq = np.ascontiguousarray(q, dtype=np.uint16)
         sl = np.ascontiguousarray(seq_len, dtype=np.int32)
         bb = np.ascontiguousarray(bounds, dtype=np.float32)

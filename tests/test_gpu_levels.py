@@ -208,11 +208,35 @@ def test_levels_decode_step_entry(dk, orc, update):
     check_pool_invariants(orc, p.o)
 
 
-def test_levels_refused_by_page_bounds(dk, orc):
-    cfg = _levels_cfg(3, num_kv_heads=1, batch=1, max_seq_len=64)
-    st = dk.DiffKVState(cfg, 1, 8, device=dev)
-    with pytest.raises(dk.DiffKVError):
-        st.page_bounds()
+@pytest.mark.parametrize("K,d,G", [(3, 128, 4), (4, 64, 5), (4, 128, 8)])
+def test_levels_page_bounds_and_scores(dk, orc, K, d, G):
+    """Per-page key bounds and page scores over K levels (every level's
+    pages with its own codec and page size; scores over both table rows):
+    bounds bit-exact, scores to the fixed-order fp32 bound, after prompt
+    compaction (an inactive request) and again after 6 generation steps."""
+    from tests.test_gpu_page_bounds import _compare
+    from workloads import synth
+    cfg = _levels_cfg(K, head_dim=d, gqa_group=G, num_kv_heads=3, batch=4, max_seq_len=2400, window=16)
+    lens = torch.tensor([1300, 40, 777, 2000], dtype=torch.int64)
+    pr = synth.make_prompt(cfg, lens=lens)
+    cu = pr["cu_seqlens"].numpy()
+    P = int(sum(-(-int(n) // 16) for n in lens) * 3 * 1.2) + 64
+    p = Pair(dk, orc, cfg, 4, P, int(cu[-1]))
+    _say(f"levels bounds K={K} d={d} G={G}: prompt")
+    p.prompt(cu, pr["k"].numpy(), pr["v"].numpy(), pr["scores"].numpy())
+    seq = lens.numpy().astype(np.int32)
+    seq[1] = 0                                   # an inactive request
+    q = synth.make_decode(cfg, 0)["q"].numpy().view(np.uint16)
+    n = _compare(p, orc, cfg, q, seq, f"K={K} d={d} G={G}")
+    levels = {int(l) for b in (0, 2, 3) for h in range(3) for l, _, _ in p.o.unit_tokens(b, h)}
+    assert levels == set(range(K)), levels      # pages of every level took part
+    seq = lens.numpy().astype(np.int32)
+    for step in range(6):
+        dec = synth.make_decode(cfg, step)
+        p.step(seq, dec["k_new"].numpy(), dec["v_new"].numpy(), f"step {step}")
+        seq = seq + 1
+    _compare(p, orc, cfg, q, seq, f"K={K} d={d} G={G} after steps")
+    _say(f"  {n} live pages")
 
 
 @pytest.mark.parametrize("rule", [0, 1])
