@@ -14,12 +14,14 @@
 //     with K precision levels (DiffKV notes, "KV compression policy",
 //     extensibility paragraph) every level's pages, each with its own codec
 //     and page size;
-//   page_scores_kernel: one wave per table entry, each lane D/64 dimensions;
-//     per q head of the group the lane's max(q kmin, q kmax) terms, a wave
-//     sum in a fixed butterfly order, then the max over the group, written in
-//     table order (-inf at empty entries).
+//   page_scores_kernel: a wave per table entry, each lane D/64 dimensions,
+//     the live entries enumerated densely, eight per wave and round (their
+//     table ids, then their bounds, loaded before any is used); per q head
+//     of the group the lane's max(q kmin, q kmax) terms, a wave sum in a
+//     fixed butterfly order, then the max over the group, written in table
+//     order (-inf at empty entries, filled in one coalesced pass).
 // Both grids give each unit a fixed number of workgroups that stride over its
-// table, so empty entries cost no launches.
+// live pages.
 // HBM-bound: a refresh reads the K codes and metadata of every live page
 // (~2.1 KB per page at d = 128) and writes 2d fp32; scoring reads the bounds.
 #include "dkv_common.hpp"
@@ -99,7 +101,12 @@ __device__ inline void page_dim_bounds_plain(const uint8_t* pg, int nv, int dim,
   }
 }
 
-constexpr int kBoundsWgPerUnit = 8;  // workgroups per unit (grid x), striding over its pages
+constexpr int kBoundsWgPerUnit = 8;  // bounds: workgroups per unit (grid x), striding over its pages
+// page scores: workgroups of 16 waves, at most 8 per unit, each wave kNB
+// live table entries per round
+constexpr int kSThreads = 1024;
+constexpr int kScoreWgPerUnit = 8;
+constexpr int kNB = 8;
 
 // bounds [P][2][D]: row 0 minima, row 1 maxima.  Levels in turn (the level
 // is uniform over the grid, so the page size and codec are too); within a
@@ -144,16 +151,17 @@ __global__ __launch_bounds__(kBThreads) void page_bounds_kernel(Levels lv, int64
 }
 
 // scores [U][R L] in table order (row r: level 2r from the left, 2r + 1
-// from the right)
+// from the right).  The empty entries get -inf in one coalesced pass; the
+// live ones are enumerated densely (level by level) over the unit's waves.
 template <int D>
-__global__ __launch_bounds__(kBThreads) void page_scores_kernel(int H, int G, Levels lv, int64_t P,
+__global__ __launch_bounds__(kSThreads) void page_scores_kernel(int H, int G, Levels lv, int64_t P,
                                                                const uint16_t* __restrict__ q,
                                                                const int32_t* __restrict__ table,
                                                                const int32_t* __restrict__ state,
                                                                const int32_t* __restrict__ seq_len,
                                                                const float* __restrict__ bounds,
                                                                float* __restrict__ scores) {
-  constexpr int WPB = kBThreads / 64;  // waves (table entries) per workgroup and round
+  constexpr int WPB = kSThreads / 64;  // waves per workgroup
   constexpr int DPL = D / 64;          // dimensions per lane: 2l, 2l + 1 (d = 128) or l (d = 64)
   const int64_t u = blockIdx.y;
   const int b = (int)(u / H), h = (int)(u % H);
@@ -161,13 +169,22 @@ __global__ __launch_bounds__(kBThreads) void page_scores_kernel(int H, int G, Le
   const int K = lv.K, L = lv.L, LT = lv.R * lv.L;
   const int32_t* s = state + 2 * K * u;
   const bool unit_ok = seq_len[b] > 0 && levels_valid(s, lv);
-  const int p0 = s[K], p1 = s[K + 1], p2 = K > 2 ? s[K + 2] : 0, p3 = K > 3 ? s[K + 3] : 0;
+  const int p0 = unit_ok ? s[K] : 0, p1 = unit_ok ? s[K + 1] : 0;
+  const int p2 = unit_ok && K > 2 ? s[K + 2] : 0, p3 = unit_ok && K > 3 ? s[K + 3] : 0;
+  float* out = scores + u * LT;
+  for (int tix = blockIdx.x * kSThreads + threadIdx.x; tix < LT; tix += gridDim.x * kSThreads) {
+    const bool r1 = tix >= L;
+    const int col = r1 ? tix - L : tix, pa = r1 ? p2 : p0, pb = r1 ? p3 : p1;
+    if (!(col < pa || col >= L - pb)) out[tix] = -INFINITY;
+  }
+  const int nlive = p0 + p1 + p2 + p3;
+  if (nlive == 0) return;
   // the group's query elements of this lane's dimensions (fp16 bits)
   uint32_t qw[16];
   const uint16_t* qb = q + ((int64_t)b * H * G + (int64_t)h * G) * D;
 #pragma unroll
   for (int g = 0; g < 16; g++) {
-    if (g >= G || !unit_ok) {
+    if (g >= G) {
       qw[g] = 0u;
     } else if constexpr (DPL == 2) {
       qw[g] = *(const uint32_t*)(qb + (int64_t)g * D + 2 * lane);
@@ -175,40 +192,63 @@ __global__ __launch_bounds__(kBThreads) void page_scores_kernel(int H, int G, Le
       qw[g] = qb[(int64_t)g * D + lane];
     }
   }
-  for (int tix = blockIdx.x * WPB + wid; tix < LT; tix += gridDim.x * WPB) {
-    const bool r1 = tix >= L;
-    const int col = r1 ? tix - L : tix, pa = r1 ? p2 : p0, pb = r1 ? p3 : p1;
-    const bool live = unit_ok && (col < pa || col >= L - pb);
-    const int32_t id = live ? table[u * LT + tix] : -1;
-    const bool ok = live && id >= 0 && id < P;  // uniform over the wave
-    float best = -INFINITY;
-    if (ok) {
-      const float* bp = bounds + (int64_t)id * 2 * D;
-      float mn[DPL], mx[DPL];
+  // live entry v -> table entry: level 0 from the left of row 0, level 1
+  // from its right, levels 2 and 3 likewise in row 1
+  auto entry_of = [&](int v) {
+    return v < p0 ? v
+                  : v < p0 + p1 ? L - 1 - (v - p0)
+                                : v < p0 + p1 + p2 ? L + (v - p0 - p1) : 2 * L - 1 - (v - p0 - p1 - p2);
+  };
+  const int nw = gridDim.x * WPB;
+  for (int v0 = blockIdx.x * WPB + wid; v0 < nlive; v0 += kNB * nw) {
+    // kNB entries: their table ids, then their bounds, loaded before any is used
+    int32_t id[kNB];
+#pragma unroll
+    for (int k = 0; k < kNB; k++) {
+      const int v = v0 + k * nw;
+      id[k] = v < nlive ? table[u * LT + entry_of(v)] : -1;
+    }
+    float mn[kNB][DPL], mx[kNB][DPL];
+#pragma unroll
+    for (int k = 0; k < kNB; k++) {
+      const bool ok = id[k] >= 0 && id[k] < P;  // uniform over the wave
+      const float* bp = bounds + (int64_t)(ok ? id[k] : 0) * 2 * D;
       if constexpr (DPL == 2) {
-        const float2 a = *(const float2*)(bp + 2 * lane), c = *(const float2*)(bp + D + 2 * lane);
-        mn[0] = a.x;
-        mn[1] = a.y;
-        mx[0] = c.x;
-        mx[1] = c.y;
-      } else {
-        mn[0] = bp[lane];
-        mx[0] = bp[D + lane];
-      }
-#pragma unroll
-      for (int g = 0; g < 16; g++) {
-        if (g < G) {  // (G is uniform)
-          float v = 0.0f;
-#pragma unroll
-          for (int e = 0; e < DPL; e++) {
-            const float qe = h2f((uint16_t)(qw[g] >> (16 * e)));
-            v += fmaxf(qe * mn[e], qe * mx[e]);
-          }
-          best = fmaxf(best, wave_sum(v));  // fixed butterfly order
+        float2 x0 = {0.0f, 0.0f}, x1 = {0.0f, 0.0f};
+        if (ok) {
+          x0 = *(const float2*)(bp + 2 * lane);
+          x1 = *(const float2*)(bp + D + 2 * lane);
         }
+        mn[k][0] = x0.x;
+        mn[k][1] = x0.y;
+        mx[k][0] = x1.x;
+        mx[k][1] = x1.y;
+      } else {
+        mn[k][0] = ok ? bp[lane] : 0.0f;
+        mx[k][0] = ok ? bp[D + lane] : 0.0f;
       }
     }
-    if (lane == 0) scores[u * LT + tix] = best;
+#pragma unroll
+    for (int k = 0; k < kNB; k++) {
+      const int v = v0 + k * nw;
+      if (v >= nlive) continue;  // (uniform)
+      float best = -INFINITY;
+      if (id[k] >= 0 && id[k] < P) {
+#pragma unroll
+        for (int g = 0; g < 16; g++) {
+          if (g < G) {  // (G is uniform)
+            float x = 0.0f;
+#pragma unroll
+            for (int e = 0; e < DPL; e++) {
+              const float qe = h2f((uint16_t)(qw[g] >> (16 * e)));
+              x += fmaxf(qe * mn[k][e], qe * mx[k][e]);
+            }
+            best = fmaxf(best, wave_sum(x));  // fixed butterfly order
+          }
+        }
+      }
+      if (lane == 0) out[entry_of(v)] = best;
+    }
   }
 }
 
@@ -238,9 +278,8 @@ hipError_t launch_page_scores(const Cfg& c, int64_t P, int batch, const uint16_t
                               hipStream_t s) {
   const int64_t U = (int64_t)batch * c.H;
   if (U == 0) return hipSuccess;
-  constexpr int wpb = kBThreads / 64;
-  const int gx = min((c.LT + wpb - 1) / wpb, kBoundsWgPerUnit);
-  const dim3 grid((unsigned)gx, (unsigned)U), block(kBThreads);
+  const int gx = min((c.LT + 511) / 512, kScoreWgPerUnit);
+  const dim3 grid((unsigned)gx, (unsigned)U), block(kSThreads);
   const Levels lv = levels_of(c);
   if (c.d == 128)
     page_scores_kernel<128><<<grid, block, 0, s>>>(c.H, c.G, lv, P, q, table, state, seq_len, bounds, scores);

@@ -147,20 +147,25 @@ __global__ __launch_bounds__(kChunk) void kd_score_kernel(int H, const int64_t* 
                                                          float* __restrict__ scores, float* __restrict__ wsum) {
   constexpr int LPT = D / 8;
   constexpr int TPW = 64 / LPT;
-  const int r = blockIdx.z, h = blockIdx.y;
+  // the blocks take the chunks in the reverse of kd_partial_kernel's order,
+  // so the keys read last there are read first here, while the memory-side
+  // cache may still hold them
+  const int r = gridDim.z - 1 - blockIdx.z, h = gridDim.y - 1 - blockIdx.y;
   int64_t c0;
   int N;
   if (!unit_range(cu, r, total, c0, N)) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int sl = lane % LPT, tw = lane / LPT;
   const int64_t base = c0 / kChunk + r;
+  const int nch = (N + kChunk - 1) / kChunk;
   const float* m = mu + ((int64_t)r * H + h) * (D + 1);
   float mv[8];
 #pragma unroll
   for (int e = 0; e < 8; e++) mv[e] = m[8 * sl + e];
   const float mn = m[D];
   __shared__ float wl[kChunk];
-  for (int ch = blockIdx.x; ch * kChunk < N; ch += gridDim.x) {
+  for (int cx = blockIdx.x; cx < nch; cx += gridDim.x) {
+    const int ch = nch - 1 - cx;
     for (int t0 = wid * 64; t0 < wid * 64 + 64; t0 += TPW) {
       const int tt = t0 + tw, i = ch * kChunk + tt;
       if (i >= N) {

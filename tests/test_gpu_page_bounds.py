@@ -92,3 +92,30 @@ def test_page_bounds_llama3_full_batch():
     q = synth.make_decode(cfg, 0)["q"].numpy().view(np.uint16)
     n = _compare(p, oracle, cfg, q, seq, "llama3_8b")
     print(f"page bounds llama3_8b: {n} live pages", flush=True)
+
+
+def test_page_bounds_long_units():
+    """Long units (32768- and 20000-token prompts, low thresholds: 560 to
+    880 live pages per unit out of 2065 entries): the entries spread over
+    several workgroups of a unit and several rounds of each wave; then
+    one generation step and a refresh."""
+    import compressed_paged_attention_amd as dk
+    import oracle
+    from workloads import synth
+    cfg = synth.config("long", batch=2, num_kv_heads=2, alpha_h=0.1, alpha_l=0.005)
+    cfg.pop("pool_factor")
+    lens = torch.tensor([32768, 20000], dtype=torch.int64)
+    pr = synth.make_prompt(cfg, lens=lens)
+    cu = pr["cu_seqlens"].numpy()
+    P = int(sum(-(-int(n) // 16) for n in lens) * 2 * 1.1) + 8
+    p = Pair(dk, oracle, cfg, 2, P, int(cu[-1]))
+    p.prompt(cu, pr["k"].numpy(), pr["v"].numpy(), pr["scores"].numpy())
+    ts = p.o.tier_state.reshape(-1, 4)
+    assert (ts[:, 2] + ts[:, 3]).max() > 800
+    seq = lens.numpy().astype(np.int32)
+    q = synth.make_decode(cfg, 0)["q"].numpy().view(np.uint16)
+    n = _compare(p, oracle, cfg, q, seq, "long units")
+    print(f"page bounds long units: {n} live pages", flush=True)
+    dec = synth.make_decode(cfg, 1)
+    p.step(seq, dec["k_new"].numpy(), dec["v_new"].numpy(), "step")
+    _compare(p, oracle, cfg, q, seq + 1, "long units after a step")
