@@ -31,7 +31,6 @@ namespace dkv {
 
 namespace {
 
-constexpr int kBThreads = 256;
 
 // A unit's level state is consistent: n_l >= 0 tokens in p_l = ceil(n_l / T_l)
 // pages per level, and the two levels that share a table row fit in it.
@@ -101,7 +100,12 @@ __device__ inline void page_dim_bounds_plain(const uint8_t* pg, int nv, int dim,
   }
 }
 
-constexpr int kBoundsWgPerUnit = 8;  // bounds: workgroups per unit (grid x), striding over its pages
+// bounds: threads per workgroup (the plain layouts' kernels hold more
+// registers per thread), and one workgroup per this many entries of a
+// unit's table row
+template <bool PLAIN>
+constexpr int bnd_threads() { return PLAIN ? 512 : 1024; }
+constexpr int kBndRowEntries = 512;
 // page scores: workgroups of 16 waves, at most 8 per unit, each wave kNB
 // live table entries per round
 constexpr int kSThreads = 1024;
@@ -112,12 +116,12 @@ constexpr int kNB = 8;
 // is uniform over the grid, so the page size and codec are too); within a
 // level the unit's workgroups stride over its pages.
 template <int D, bool PLAIN>
-__global__ __launch_bounds__(kBThreads) void page_bounds_kernel(Levels lv, int64_t P, int page_bytes,
+__global__ __launch_bounds__(bnd_threads<PLAIN>()) void page_bounds_kernel(Levels lv, int64_t P, int page_bytes,
                                                                const int32_t* __restrict__ table,
                                                                const int32_t* __restrict__ state,
                                                                const uint8_t* __restrict__ pages,
                                                                float* __restrict__ bounds) {
-  constexpr int PPB = kBThreads / D;  // pages per workgroup and round
+  constexpr int PPB = bnd_threads<PLAIN>() / D;  // pages per workgroup and round
   const int64_t u = blockIdx.y;
   const int dim = threadIdx.x % D;
   const int K = lv.K;
@@ -256,9 +260,8 @@ hipError_t launch_page_bounds(const Cfg& c, const Pool& p, int batch, const int3
                               float* bounds, hipStream_t s) {
   const int64_t U = (int64_t)batch * c.H;
   if (U == 0) return hipSuccess;
-  const int ppb = kBThreads / c.d;
-  const int gx = min((c.L + ppb - 1) / ppb, kBoundsWgPerUnit);
-  const dim3 grid((unsigned)gx, (unsigned)U), block(kBThreads);
+  const int gx = (c.L + kBndRowEntries - 1) / kBndRowEntries;
+  const dim3 grid((unsigned)gx, (unsigned)U), block(c.plain ? bnd_threads<true>() : bnd_threads<false>());
   const Levels lv = levels_of(c);
 #define DKV_BOUNDS(D, PL) \
   page_bounds_kernel<D, PL><<<grid, block, 0, s>>>(lv, p.P, p.page_bytes, table, state, p.pages, bounds)
