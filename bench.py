@@ -482,7 +482,7 @@ def measure(args, name, R, steps, warmup, dk):
     gp = 4 if G <= 4 else (8 if G <= 8 else 16)  # the kernel's softmax layout (G rounded up)
     step_kernel = "attn_kernel<%d, 1, %d, true>" % (d, gp) if one_split else "step + attention kernels"
     attn_kernel = ("attn_kernel<%d, 1, %d, false>" % (d, gp)) if one_split else \
-        "attn_kernel<%d, 2, ...> + attn_merge_kernel + score_kernel" % d
+        "attn_kernel<%d, 2, ...> + score_kernel (merging the splits) + score_finish_kernel" % d
     cfg_out = {"workload": WORKLOAD_NAMES.get(name, name), "q_heads": H * G, "kv_heads": H, "head_dim": d,
                "batch": B,
                "context": int(lens[0]) if int(lens.min()) == int(lens.max()) else [int(lens.min()), int(lens.max())],
