@@ -28,7 +28,8 @@
 //   imp_sum_kernel: per (64-key tile, KV head) the keys stay in registers
 //     while the workgroup walks the later query tiles and, per tile, the
 //     group's heads (each head's query tile and references staged in LDS):
-//     2^(x + c) masked to later queries, max over heads, summed per key;
+//     x + c masked to later queries, max over heads, then 2^ of it summed
+//     per key;
 //     the mean is written to scores[h][token].
 // Both kernels loop over their tiles with a grid stride, so every length is
 // covered whatever the grid.
@@ -256,11 +257,14 @@ __global__ __launch_bounds__(64 * kImpWaves) void imp_sum_kernel(int H, int G, i
     };
     if (jt0 < NQ) fetch(jt0, 0);
     for (int jt = jt0; jt < NQ; jt += kTile) {
-      float pm[4][4];  // [query block][row]: max over the heads so far
+      // [query block][row]: max over the heads so far of the exponent x + c
+      // (2^ is increasing, so the max of the weights is 2^ of this max: one
+      // exponential per (query, key) instead of one per head)
+      float pm[4][4];
 #pragma unroll
       for (int qb = 0; qb < 4; qb++)
 #pragma unroll
-        for (int t = 0; t < 4; t++) pm[qb][t] = 0.0f;
+        for (int t = 0; t < 4; t++) pm[qb][t] = -INFINITY;
       for (int g = 0; g < G; g++) {
         __syncthreads();  // the previous pair's reads are done
         tl.put(tid, qs);
@@ -281,21 +285,22 @@ __global__ __launch_bounds__(64 * kImpWaves) void imp_sum_kernel(int H, int G, i
           const float4_t c4 = *(const float4_t*)(cs + 16 * qb + 4 * rg);  // the lane's four query rows
           if (full) {
 #pragma unroll
-            for (int t = 0; t < 4; t++)
-              pm[qb][t] = fmaxf(pm[qb][t], __builtin_amdgcn_exp2f(__builtin_fmaf(acc[t], scale_log2, c4[t])));
+            for (int t = 0; t < 4; t++) pm[qb][t] = fmaxf(pm[qb][t], __builtin_fmaf(acc[t], scale_log2, c4[t]));
           } else {
 #pragma unroll
             for (int t = 0; t < 4; t++) {
               const int j = jt + 16 * qb + 4 * rg + t;
               const bool ok = j < NQ && ik < N && (probe || j > ik);
-              const float c = ok ? c4[t] : -INFINITY;
-              pm[qb][t] = fmaxf(pm[qb][t], ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(acc[t], scale_log2, c)) : 0.0f);
+              pm[qb][t] = fmaxf(pm[qb][t], ok ? __builtin_fmaf(acc[t], scale_log2, c4[t]) : -INFINITY);
             }
           }
         }
       }
+      // (2^-inf = 0: masked pairs, and queries whose references are -inf)
 #pragma unroll
-      for (int qb = 0; qb < 4; qb++) sum += (pm[qb][0] + pm[qb][1]) + (pm[qb][2] + pm[qb][3]);
+      for (int qb = 0; qb < 4; qb++)
+        sum += (__builtin_amdgcn_exp2f(pm[qb][0]) + __builtin_amdgcn_exp2f(pm[qb][1])) +
+               (__builtin_amdgcn_exp2f(pm[qb][2]) + __builtin_amdgcn_exp2f(pm[qb][3]));
     }
     // the four row groups of a key column: lanes col, col + 16, col + 32, col + 48
     sum += lane_xchg_t<4>(sum);
