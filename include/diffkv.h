@@ -105,7 +105,7 @@ typedef struct {
    * then page counts); the prompt's block feeds levels 0, 2, 3 from its left
    * end and level 1 from its right end; a generation step moves at most t_c
    * and one victim down (see diffkv_compact).  Per-page key bounds and page
-   * scores refuse K >= 3 (DIFFKV_E_INVALID). */
+   * scores cover every level (scores over all R rows of the table). */
   int32_t num_levels;
   float alpha_mid[2];
   int32_t mid_k_bits[2], mid_v_bits[2];
